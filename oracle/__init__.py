@@ -1,0 +1,33 @@
+"""CPU float64 oracle for decode attention over a compressed KV cache.
+
+TEST INFRASTRUCTURE ONLY: tests/, the package's smoke check and the CPU
+baseline leg of bench.py are the only code that may import it.  It shares no
+code with the HIP library and never calls it.
+
+Parity status of each function (what pins it is in tests/test_oracle_*.py):
+  share_map       pinned (exhaustive enumeration, page's memory figures)
+  attention       pinned (closed forms, brute force, invariants)
+  decode_attention pinned (GQA grouping, all-leaders reduction)
+  value_range     pinned (hand values, invariances, torch float32 rounding)
+  window_score    pinned (closed-form causal case, row sums, brute force)
+  philox4         pinned (64-bit instance equals numpy's Philox4x64-10)
+  exp_variate     pinned (end points, exponential law)
+  select          pinned (invariants, top-K reduction, exact 8-token law)
+  compact         pinned (gather identity, restricted attention)
+  run_decode      pinned through the functions above and the schedule count
+End-to-end model quality (does the eviction keep accuracy?) is parity
+unpinned: it needs trained weights and datasets that are not available.
+"""
+from .philox import philox4, philox4x32_10, seed_key, mulhilo
+from .kvc_oracle import (
+    share_map, append_row, attention, decode_attention, value_range,
+    window_score, philox_word0, exp_variate, select, select_detail, compact,
+    eviction_due, run_decode,
+)
+
+__all__ = [
+    "philox4", "philox4x32_10", "seed_key", "mulhilo", "share_map",
+    "append_row", "attention", "decode_attention", "value_range",
+    "window_score", "philox_word0", "exp_variate", "select", "select_detail",
+    "compact", "eviction_due", "run_decode",
+]
