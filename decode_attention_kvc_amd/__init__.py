@@ -1,0 +1,15 @@
+"""libkvc: decode attention over a compressed KV cache on AMD MI355X.
+
+The compute runs in libkvc.so (hand-written HIP for gfx950); this package
+holds the library sources (csrc/), its build script and the ctypes binding.
+Importing the package loads the library and fails if it is not built.
+"""
+from ._lib import (  # noqa: F401
+    Cache, KvcError, EXPORTS, HEAD_DIM, T_ALIGN, KVC_F32, KVC_BF16, KVC_OK, KVC_EINVAL,
+    KVC_EDTYPE, KVC_EALIGN, KVC_EWORKSPACE, KVC_EALIAS, KVC_EHIP, lib, strerror,
+    kvc_version, kvc_strerror, kvc_share_map, kvc_append, kvc_decode_attn_ws_bytes,
+    kvc_decode_attn, kvc_value_range, kvc_score_ws_bytes, kvc_score, kvc_select_ws_bytes,
+    kvc_select, kvc_compact, kvc_philox_words,
+)
+
+lib()

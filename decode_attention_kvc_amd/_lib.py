@@ -1,0 +1,269 @@
+"""ctypes binding of libkvc.so.
+
+Argument marshalling only: every function here has the name of the C export
+it calls, converts torch tensors to device pointers (and the current HIP
+stream), and raises KvcError on a non-zero status.  All computation runs in
+the library's HIP kernels; there is no fallback path.
+"""
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvc.so")
+
+KVC_OK, KVC_EINVAL, KVC_EDTYPE, KVC_EALIGN, KVC_EWORKSPACE, KVC_EALIAS, KVC_EHIP = 0, -1, -2, -3, -4, -5, -6
+KVC_F32, KVC_BF16 = 0, 1
+HEAD_DIM = 128
+T_ALIGN = 64
+
+EXPORTS = (
+    "kvc_version", "kvc_strerror", "kvc_share_map", "kvc_append",
+    "kvc_decode_attn_ws_bytes", "kvc_decode_attn", "kvc_value_range",
+    "kvc_score_ws_bytes", "kvc_score", "kvc_select_ws_bytes", "kvc_select",
+    "kvc_compact", "kvc_philox_words",
+)
+
+
+class KvcError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({strerror(status)})")
+
+
+class kvc_cache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("n_slots", ctypes.c_int32), ("nb", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("t_len", ctypes.c_int32), ("t_cap", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m decode_attention_kvc_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz, f32 = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                 ctypes.c_size_t, ctypes.c_float)
+        cp = ctypes.POINTER(kvc_cache)
+        ip = ctypes.POINTER(ctypes.c_int32)
+        szp = ctypes.POINTER(ctypes.c_size_t)
+        sig = {
+            "kvc_version": ([], i32),
+            "kvc_strerror": ([i32], ctypes.c_char_p),
+            "kvc_share_map": ([i32, ip, i32, ip, ip], i32),
+            "kvc_append": ([cp, i32, vp, vp, vp], i32),
+            "kvc_decode_attn_ws_bytes": ([cp, i32, i32, szp], i32),
+            "kvc_decode_attn": ([cp, vp, i64, i32, ip, i32, f32, vp, vp, i32, vp, i64, vp, i64,
+                                 vp, sz, vp], i32),
+            "kvc_value_range": ([cp, i32, vp, vp], i32),
+            "kvc_score_ws_bytes": ([cp, i32, i32, szp], i32),
+            "kvc_score": ([cp, i32, vp, i32, i32, f32, vp, vp, vp, vp, sz, vp], i32),
+            "kvc_select_ws_bytes": ([i32, i32, i32, szp], i32),
+            "kvc_select": ([vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_uint64, i32, vp, vp,
+                            sz, vp], i32),
+            "kvc_compact": ([cp, i32, vp, i32, cp, vp], i32),
+            "kvc_philox_words": ([i64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                                  ctypes.c_uint64, vp, vp], i32),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def strerror(status):
+    return lib().kvc_strerror(int(status)).decode()
+
+
+def _check(status, where):
+    if status != KVC_OK:
+        raise KvcError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    if torch.cuda.is_available():
+        return torch.cuda.current_stream().cuda_stream
+    return None
+
+
+def _dtype_code(dt):
+    if dt == torch.float32:
+        return KVC_F32
+    if dt == torch.bfloat16:
+        return KVC_BF16
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+@dataclass
+class Cache:
+    """A leader-slot KV cache in libkvc's layout (see include/kvc.h).
+
+    k: [n_slots][nb][n_kv_heads][t_cap][128]; v: [n_slots][nb][n_kv_heads]
+    [128][t_cap] (token-minor)."""
+    k: torch.Tensor
+    v: torch.Tensor
+    t_len: int
+
+    @staticmethod
+    def empty(n_slots, nb, n_kv_heads, t_cap, dtype=torch.bfloat16, device="cuda", t_len=0):
+        t_cap = int(math.ceil(t_cap / T_ALIGN) * T_ALIGN)
+        k = torch.empty((n_slots, nb, n_kv_heads, t_cap, HEAD_DIM), dtype=dtype, device=device)
+        v = torch.empty((n_slots, nb, n_kv_heads, HEAD_DIM, t_cap), dtype=dtype, device=device)
+        return Cache(k, v, t_len)
+
+    @property
+    def n_slots(self):
+        return self.k.shape[0]
+
+    @property
+    def nb(self):
+        return self.k.shape[1]
+
+    @property
+    def n_kv_heads(self):
+        return self.k.shape[2]
+
+    @property
+    def t_cap(self):
+        return self.k.shape[3]
+
+    @property
+    def dtype(self):
+        return self.k.dtype
+
+    def desc(self):
+        return kvc_cache(self.k.data_ptr(), self.v.data_ptr(), _dtype_code(self.k.dtype),
+                         self.n_slots, self.nb, self.n_kv_heads, HEAD_DIM, int(self.t_len),
+                         self.t_cap)
+
+    # views in logical [..][t][d] form (plumbing for tests and data setup)
+    def k_rows(self, slot):
+        return self.k[slot, :, :, : self.t_len, :]
+
+    def v_rows(self, slot):
+        return self.v[slot, :, :, :, : self.t_len].transpose(-1, -2)
+
+    def fill(self, slot, k_rows, v_rows):
+        """Write logical rows [nb][hkv][T][d] into a slot and set t_len = T."""
+        T = k_rows.shape[2]
+        self.k[slot, :, :, :T, :].copy_(k_rows)
+        self.v[slot, :, :, :, :T].copy_(v_rows.transpose(-1, -2))
+        self.t_len = T
+
+
+# ---------------------------------------------------------------------------
+# exports
+# ---------------------------------------------------------------------------
+def kvc_version():
+    return lib().kvc_version()
+
+
+def kvc_strerror(status):
+    return strerror(status)
+
+
+def kvc_share_map(n_layers, leaders):
+    """Returns (src_layer, src_slot) as lists."""
+    arr = (ctypes.c_int32 * max(1, len(leaders)))(*leaders)
+    src = (ctypes.c_int32 * n_layers)()
+    slot = (ctypes.c_int32 * n_layers)()
+    _check(lib().kvc_share_map(n_layers, arr, len(leaders), src, slot), "kvc_share_map")
+    return list(src), list(slot)
+
+
+def kvc_append(cache, slot, k_new, v_new, stream=None):
+    c = cache.desc()
+    _check(lib().kvc_append(ctypes.byref(c), slot, _ptr(k_new), _ptr(v_new), _stream(stream)),
+           "kvc_append")
+
+
+def kvc_decode_attn_ws_bytes(cache, n_q_layers, n_q_heads):
+    c = cache.desc()
+    out = ctypes.c_size_t()
+    _check(lib().kvc_decode_attn_ws_bytes(ctypes.byref(c), n_q_layers, n_q_heads,
+                                          ctypes.byref(out)), "kvc_decode_attn_ws_bytes")
+    return out.value
+
+
+def kvc_decode_attn(cache, q, q_slot, out, lse=None, ws=None, scale=0.0, k_new=None,
+                    v_new=None, append_slot=-1, q_layer_stride=0, out_layer_stride=0,
+                    lse_layer_stride=0, n_q_layers=None, n_q_heads=None, stream=None):
+    """q: [nq][nb][Hq][d] (or strided views given explicit strides)."""
+    c = cache.desc()
+    nq = len(q_slot) if n_q_layers is None else n_q_layers
+    hq = q.shape[-2] if n_q_heads is None else n_q_heads
+    slots = (ctypes.c_int32 * max(1, nq))(*[int(s) for s in q_slot])
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().kvc_decode_attn(ctypes.byref(c), _ptr(q), q_layer_stride, nq, slots, hq,
+                                 float(scale), _ptr(k_new), _ptr(v_new), append_slot, _ptr(out),
+                                 out_layer_stride, _ptr(lse), lse_layer_stride, _ptr(ws),
+                                 ws_bytes, _stream(stream)), "kvc_decode_attn")
+
+
+def kvc_value_range(cache, slot, rng, stream=None):
+    c = cache.desc()
+    _check(lib().kvc_value_range(ctypes.byref(c), slot, _ptr(rng), _stream(stream)),
+           "kvc_value_range")
+
+
+def kvc_score_ws_bytes(cache, n_q_heads, w):
+    c = cache.desc()
+    out = ctypes.c_size_t()
+    _check(lib().kvc_score_ws_bytes(ctypes.byref(c), n_q_heads, w, ctypes.byref(out)),
+           "kvc_score_ws_bytes")
+    return out.value
+
+
+def kvc_score(cache, slot, q_obs, score, rng=None, lse_obs=None, ws=None, scale=0.0,
+              stream=None):
+    """q_obs: [w][nb][Hq][d]."""
+    c = cache.desc()
+    w, hq = q_obs.shape[0], q_obs.shape[2]
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().kvc_score(ctypes.byref(c), slot, _ptr(q_obs), hq, w, float(scale),
+                           _ptr(lse_obs), _ptr(score), _ptr(rng), _ptr(ws), ws_bytes,
+                           _stream(stream)), "kvc_score")
+
+
+def kvc_select_ws_bytes(nb, n_kv_heads, t_len):
+    out = ctypes.c_size_t()
+    _check(lib().kvc_select_ws_bytes(nb, n_kv_heads, t_len, ctypes.byref(out)),
+           "kvc_select_ws_bytes")
+    return out.value
+
+
+def kvc_select(score, rng, nb, n_kv_heads, t_len, budget_k, recent_b, n_v, seed, layer_id,
+               kept, ws=None, stream=None):
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().kvc_select(_ptr(score), _ptr(rng), nb, n_kv_heads, t_len, budget_k, recent_b,
+                            n_v, int(seed) & (2**64 - 1), layer_id, _ptr(kept), _ptr(ws),
+                            ws_bytes, _stream(stream)), "kvc_select")
+
+
+def kvc_compact(src, slot, kept, n_keep, dst, stream=None):
+    cs, cd = src.desc(), dst.desc()
+    _check(lib().kvc_compact(ctypes.byref(cs), slot, _ptr(kept), n_keep, ctypes.byref(cd),
+                             _stream(stream)), "kvc_compact")
+
+
+def kvc_philox_words(n, c1, c2, c3, seed, out, stream=None):
+    _check(lib().kvc_philox_words(n, c1, c2, c3, int(seed) & (2**64 - 1), _ptr(out),
+                                  _stream(stream)), "kvc_philox_words")

@@ -1,0 +1,481 @@
+// libkvc C ABI: argument validation, launch planning and error mapping.
+// Every entry point checks all of its arguments on the host before it
+// enqueues anything; on an error it returns a negative kvc_status and
+// leaves every output untouched.
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "../../include/kvc.h"
+#include "kvc_internal.h"
+
+using namespace kvc;
+
+namespace {
+
+constexpr int VERSION = 10000;   // 1.0.0
+
+bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+size_t elem_size(int dtype) { return dtype == KVC_F32 ? 4 : 2; }
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int check_cache(const kvc_cache* c) {
+    if (!c) return KVC_EALIGN;
+    if (c->dtype != KVC_F32 && c->dtype != KVC_BF16) return KVC_EDTYPE;
+    if (c->head_dim != KVC_HEAD_DIM) return KVC_EINVAL;
+    if (c->n_slots < 1 || c->nb < 0 || c->n_kv_heads < 1) return KVC_EINVAL;
+    if (c->t_cap < 0 || c->t_len < 0 || c->t_len > c->t_cap) return KVC_EINVAL;
+    if (c->t_cap % KVC_T_ALIGN) return KVC_EINVAL;
+    if (!aligned16(c->k) || !aligned16(c->v)) return KVC_EALIGN;
+    return KVC_OK;
+}
+
+size_t slot_elems(const kvc_cache* c) {
+    return (size_t)c->nb * c->n_kv_heads * c->t_cap * KVC_HEAD_DIM;
+}
+const char* slot_k(const kvc_cache* c, int slot) {
+    return static_cast<const char*>(c->k) + (size_t)slot * slot_elems(c) * elem_size(c->dtype);
+}
+const char* slot_v(const kvc_cache* c, int slot) {
+    return static_cast<const char*>(c->v) + (size_t)slot * slot_elems(c) * elem_size(c->dtype);
+}
+
+int hip_status() { return hipGetLastError() == hipSuccess ? KVC_OK : KVC_EHIP; }
+
+// Tuning knob for experiments: workgroups an attention launch aims for.
+int attn_target_wgs() {
+    static int v = [] {
+        const char* e = getenv("KVC_ATTN_TARGET_WGS");
+        const int x = e ? atoi(e) : 0;
+        return x > 0 ? x : 1024;
+    }();
+    return v;
+}
+
+// ---- attention planning ----------------------------------------------------
+struct AttnPlan {
+    int nt, rp, nsplit, tps;
+};
+
+AttnPlan plan_attn(int dtype, int rows, int t_len, int slabs) {
+    AttnPlan pl;
+    int tile, min_tps;
+    if (dtype == KVC_F32) {
+        pl.nt = 1;
+        pl.rp = 16;
+        tile = ATTN_TILE_F32;
+        min_tps = 1;
+    } else {
+        pl.nt = rows <= 16 ? 1 : rows <= 32 ? 2 : 4;
+        pl.rp = 16 * pl.nt;
+        tile = ATTN_TILE;
+        min_tps = ATTN_WAVES;   // at least one tile per wave
+    }
+    const int ntiles = std::max(1, (t_len + tile - 1) / tile);
+    const long long work = (long long)ntiles * std::max(1, slabs);
+    int tps = (int)std::max<long long>(min_tps, (work + attn_target_wgs() - 1) / attn_target_wgs());
+    int nsplit = (ntiles + tps - 1) / tps;
+    const int cap = MAX_SPLIT_ROWS / pl.rp;
+    if (nsplit > cap) {
+        tps = (ntiles + cap - 1) / cap;
+        nsplit = (ntiles + tps - 1) / tps;
+    }
+    pl.tps = tps;
+    pl.nsplit = nsplit;
+    return pl;
+}
+
+int max_rows_per_chunk(int dtype, int g) {
+    const int cap_rows = dtype == KVC_F32 ? 16 : 64;
+    const int ql = std::min(MAX_QL, cap_rows / g);
+    return ql * g;
+}
+
+size_t attn_ws_for(int dtype, int rows, int t_len, int slabs) {
+    const AttnPlan pl = plan_attn(dtype, rows, t_len, slabs);
+    return (size_t)slabs * pl.nsplit * pl.rp * (KVC_HEAD_DIM + 2) * sizeof(float);
+}
+
+size_t attn_ws_total(const kvc_cache* c, int rows) {
+    const int slabs = c->nb * c->n_kv_heads;
+    size_t part = 0;
+    for (int t = 1; t <= std::max(1, c->t_cap); t += (c->dtype == KVC_F32 ? ATTN_TILE_F32 : ATTN_TILE))
+        part = std::max(part, attn_ws_for(c->dtype, rows, t, slabs));
+    part = std::max(part, attn_ws_for(c->dtype, rows, std::max(1, c->t_cap), slabs));
+    return align_up((size_t)slabs * sizeof(uint32_t), 256) + part;
+}
+
+// ---- score planning --------------------------------------------------------
+struct ScorePlan {
+    int nsplit, tps, rows_pad;
+};
+
+ScorePlan plan_score(int dtype, int rows, int t_len, int slabs) {
+    ScorePlan pl;
+    const int tile = dtype == KVC_F32 ? 64 : SCORE_TILE;
+    const int ntiles = std::max(1, (t_len + tile - 1) / tile);
+    const long long work = (long long)ntiles * std::max(1, slabs);
+    int tps = (int)std::max<long long>(1, (work + 2047) / 2048);
+    if (dtype != KVC_F32) tps = std::min(tps, SCORE_MAX_TPS);
+    pl.tps = tps;
+    pl.nsplit = (ntiles + tps - 1) / tps;
+    pl.rows_pad = dtype == KVC_F32 ? rows : (rows + 31) / 32 * 32;
+    return pl;
+}
+
+struct ScoreWs {
+    size_t cnt_off, lse_off, stats_off, total;
+};
+
+ScoreWs score_ws_layout(int dtype, int rows, int t_len, int slabs) {
+    const ScorePlan pl = plan_score(dtype, rows, t_len, slabs);
+    ScoreWs w;
+    w.cnt_off = 0;
+    w.lse_off = align_up((size_t)slabs * sizeof(uint32_t), 256);
+    w.stats_off = w.lse_off + align_up((size_t)slabs * pl.rows_pad * sizeof(float), 256);
+    w.total = w.stats_off + (size_t)slabs * pl.nsplit * pl.rows_pad * 2 * sizeof(float);
+    return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvc_version(void) { return VERSION; }
+
+const char* kvc_strerror(int status) {
+    switch (status) {
+        case KVC_OK: return "success";
+        case KVC_EINVAL: return "invalid argument: a size, index or set is out of range";
+        case KVC_EDTYPE: return "unknown or mismatched element type";
+        case KVC_EALIGN: return "pointer is NULL or not 16-byte aligned";
+        case KVC_EWORKSPACE: return "workspace missing or too small";
+        case KVC_EALIAS: return "source and destination memory overlap";
+        case KVC_EHIP: return "HIP runtime error at launch";
+        default: return "unknown status";
+    }
+}
+
+int kvc_share_map(int n_layers, const int32_t* leaders, int n_leaders, int32_t* src_layer,
+                  int32_t* src_slot) {
+    if (!leaders || !src_layer || !src_slot) return KVC_EALIGN;
+    if (n_layers < 1 || n_leaders < 1 || n_leaders > n_layers) return KVC_EINVAL;
+    if (leaders[0] != 0) return KVC_EINVAL;
+    for (int i = 1; i < n_leaders; ++i)
+        if (leaders[i] <= leaders[i - 1]) return KVC_EINVAL;
+    if (leaders[n_leaders - 1] >= n_layers) return KVC_EINVAL;
+    int slot = 0;
+    for (int l = 0; l < n_layers; ++l) {
+        while (slot + 1 < n_leaders && leaders[slot + 1] <= l) ++slot;
+        src_layer[l] = leaders[slot];
+        src_slot[l] = slot;
+    }
+    return KVC_OK;
+}
+
+int kvc_append(const kvc_cache* c, int slot, const void* k_new, const void* v_new,
+               kvc_stream_t stream) {
+    int st = check_cache(c);
+    if (st) return st;
+    if (slot < 0 || slot >= c->n_slots || c->t_len < 1) return KVC_EINVAL;
+    if (!aligned16(k_new) || !aligned16(v_new)) return KVC_EALIGN;
+    if (c->nb == 0) return KVC_OK;
+    if (launch_append(slot_k(c, slot), slot_v(c, slot), c->nb, c->n_kv_heads, c->t_len,
+                      c->t_cap, k_new, v_new, (int)elem_size(c->dtype),
+                      (hipStream_t)stream) != hipSuccess)
+        return KVC_EHIP;
+    return hip_status();
+}
+
+int kvc_decode_attn_ws_bytes(const kvc_cache* c, int n_q_layers, int n_q_heads, size_t* bytes) {
+    int st = check_cache(c);
+    if (st) return st;
+    if (!bytes) return KVC_EALIGN;
+    if (n_q_layers < 0 || n_q_heads < 1 || n_q_heads % c->n_kv_heads) return KVC_EINVAL;
+    const int g = n_q_heads / c->n_kv_heads;
+    if (g > (c->dtype == KVC_F32 ? 16 : 64)) return KVC_EINVAL;
+    const int rows = std::min(n_q_layers * g, max_rows_per_chunk(c->dtype, g));
+    *bytes = (n_q_layers == 0 || c->nb == 0) ? 0 : attn_ws_total(c, std::max(rows, 1));
+    return KVC_OK;
+}
+
+int kvc_decode_attn(const kvc_cache* c, const void* q, int64_t q_layer_stride, int n_q_layers,
+                    const int32_t* q_slot, int n_q_heads, float scale, const void* k_new,
+                    const void* v_new, int append_slot, float* out, int64_t out_layer_stride,
+                    float* lse, int64_t lse_layer_stride, void* ws, size_t ws_bytes,
+                    kvc_stream_t stream) {
+    int st = check_cache(c);
+    if (st) return st;
+    if (n_q_layers < 0 || n_q_heads < 1 || n_q_heads % c->n_kv_heads) return KVC_EINVAL;
+    const int g = n_q_heads / c->n_kv_heads;
+    if (g > (c->dtype == KVC_F32 ? 16 : 64)) return KVC_EINVAL;
+    if (append_slot < -1 || append_slot >= c->n_slots) return KVC_EINVAL;
+    if (!isfinite(scale) || scale < 0.f) return KVC_EINVAL;
+    const int64_t packed_q = (int64_t)c->nb * n_q_heads * KVC_HEAD_DIM;
+    const int64_t packed_l = (int64_t)c->nb * n_q_heads;
+    if (q_layer_stride < 0 || out_layer_stride < 0 || lse_layer_stride < 0) return KVC_EINVAL;
+    if (q_layer_stride && q_layer_stride < packed_q) return KVC_EINVAL;
+    if (out_layer_stride && out_layer_stride < packed_q) return KVC_EINVAL;
+    if (lse_layer_stride && lse_layer_stride < packed_l) return KVC_EINVAL;
+    if (n_q_layers == 0 || c->nb == 0) {
+        if (append_slot < 0 || c->nb == 0) return KVC_OK;
+    }
+    if (c->t_len < 1) return KVC_EINVAL;
+    if (n_q_layers > 0) {
+        if (!q_slot) return KVC_EALIGN;
+        for (int i = 0; i < n_q_layers; ++i)
+            if (q_slot[i] < 0 || q_slot[i] >= c->n_slots) return KVC_EINVAL;
+        if (!aligned16(q) || !aligned16(out)) return KVC_EALIGN;
+        if (q_layer_stride % (16 / (int64_t)elem_size(c->dtype))) return KVC_EALIGN;
+        if (lse && !aligned4(lse)) return KVC_EALIGN;
+    }
+    if (append_slot >= 0 && (!aligned16(k_new) || !aligned16(v_new))) return KVC_EALIGN;
+    size_t need = 0;
+    if (n_q_layers > 0) {
+        const int rows = std::min(n_q_layers * g, max_rows_per_chunk(c->dtype, g));
+        need = attn_ws_total(c, rows);
+        if (!ws || ws_bytes < need || !aligned16(ws)) return KVC_EWORKSPACE;
+    }
+    if (scale == 0.f) scale = 1.0f / sqrtf((float)KVC_HEAD_DIM);
+    const hipStream_t s = (hipStream_t)stream;
+    const int slabs = c->nb * c->n_kv_heads;
+
+    // Group q-layers by slot (first appearance order) and cut each group into
+    // launches of at most max_rows_per_chunk rows.
+    std::vector<int> order;
+    std::vector<char> done(c->n_slots, 0);
+    bool append_done = false;
+    const int64_t qs = q_layer_stride ? q_layer_stride : packed_q;
+    const int64_t os = out_layer_stride ? out_layer_stride : packed_q;
+    const int64_t ls = lse_layer_stride ? lse_layer_stride : packed_l;
+    const int chunk_ql = max_rows_per_chunk(c->dtype, g) / g;
+    for (int i = 0; i < n_q_layers; ++i) {
+        const int slot = q_slot[i];
+        if (done[slot]) continue;
+        done[slot] = 1;
+        std::vector<int> members;
+        for (int k = i; k < n_q_layers; ++k)
+            if (q_slot[k] == slot) members.push_back(k);
+        for (size_t m0 = 0; m0 < members.size(); m0 += chunk_ql) {
+            const int nql = (int)std::min<size_t>(chunk_ql, members.size() - m0);
+            AttnLaunch p;
+            memset(&p, 0, sizeof(p));
+            p.k = slot_k(c, slot);
+            p.v = slot_v(c, slot);
+            p.nb = c->nb;
+            p.hkv = c->n_kv_heads;
+            p.g = g;
+            p.hq = n_q_heads;
+            p.t_len = c->t_len;
+            p.t_cap = c->t_cap;
+            p.nql = nql;
+            p.rows = nql * g;
+            for (int x = 0; x < nql; ++x) {
+                const int qi = members[m0 + x];
+                p.q_off[x] = qi * qs;
+                p.out_off[x] = qi * os;
+                p.lse_off[x] = qi * ls;
+            }
+            p.q = q;
+            p.out = out;
+            p.lse = lse;
+            p.scale = scale;
+            p.append_read = (slot == append_slot);
+            p.append_write = (slot == append_slot) && !append_done;
+            if (p.append_read) {
+                p.k_new = k_new;
+                p.v_new = v_new;
+            }
+            const AttnPlan pl = plan_attn(c->dtype, p.rows, c->t_len, slabs);
+            p.rp = pl.rp;
+            p.nsplit = pl.nsplit;
+            p.tps = pl.tps;
+            p.cnt = static_cast<uint32_t*>(ws);
+            p.part = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                              align_up((size_t)slabs * sizeof(uint32_t), 256));
+            if (launch_attn(p, c->dtype, pl.nt, s) != hipSuccess) return KVC_EHIP;
+            if (p.append_write) append_done = true;
+        }
+    }
+    if (append_slot >= 0 && !append_done) {
+        if (launch_append(slot_k(c, append_slot), slot_v(c, append_slot), c->nb, c->n_kv_heads,
+                          c->t_len, c->t_cap, k_new, v_new, (int)elem_size(c->dtype),
+                          s) != hipSuccess)
+            return KVC_EHIP;
+    }
+    return hip_status();
+}
+
+int kvc_value_range(const kvc_cache* c, int slot, float* range, kvc_stream_t stream) {
+    int st = check_cache(c);
+    if (st) return st;
+    if (slot < 0 || slot >= c->n_slots) return KVC_EINVAL;
+    if (!aligned4(range)) return KVC_EALIGN;
+    if (c->nb == 0 || c->t_len == 0) return KVC_OK;
+    if (launch_value_range(slot_v(c, slot), c->nb, c->n_kv_heads, c->t_len, c->t_cap, c->dtype,
+                           range, (hipStream_t)stream) != hipSuccess)
+        return KVC_EHIP;
+    return hip_status();
+}
+
+int kvc_score_ws_bytes(const kvc_cache* c, int n_q_heads, int w, size_t* bytes) {
+    int st = check_cache(c);
+    if (st) return st;
+    if (!bytes) return KVC_EALIGN;
+    if (n_q_heads < 1 || n_q_heads % c->n_kv_heads || w < 1) return KVC_EINVAL;
+    const int rows = (n_q_heads / c->n_kv_heads) * w;
+    const int slabs = c->nb * c->n_kv_heads;
+    size_t tot = 0;
+    const int tile = c->dtype == KVC_F32 ? 64 : SCORE_TILE;
+    for (int t = w; t <= std::max(w, c->t_cap); t += tile)
+        tot = std::max(tot, score_ws_layout(c->dtype, rows, t, slabs).total);
+    tot = std::max(tot, score_ws_layout(c->dtype, rows, std::max(w, c->t_cap), slabs).total);
+    *bytes = slabs ? tot : 0;
+    return KVC_OK;
+}
+
+int kvc_score(const kvc_cache* c, int slot, const void* q_obs, int n_q_heads, int w, float scale,
+              const float* lse_obs, float* score, float* range, void* ws, size_t ws_bytes,
+              kvc_stream_t stream) {
+    int st = check_cache(c);
+    if (st) return st;
+    if (slot < 0 || slot >= c->n_slots) return KVC_EINVAL;
+    if (n_q_heads < 1 || n_q_heads % c->n_kv_heads || w < 1) return KVC_EINVAL;
+    const int g = n_q_heads / c->n_kv_heads;
+    const int rows = g * w;
+    if (rows > (c->dtype == KVC_F32 ? 128 : 512)) return KVC_EINVAL;
+    if (!isfinite(scale) || scale < 0.f) return KVC_EINVAL;
+    if (c->nb == 0) return KVC_OK;
+    if (w > c->t_len) return KVC_EINVAL;
+    if (!aligned16(q_obs) || !aligned4(score)) return KVC_EALIGN;
+    if ((lse_obs && !aligned4(lse_obs)) || (range && !aligned4(range))) return KVC_EALIGN;
+    const int slabs = c->nb * c->n_kv_heads;
+    const ScoreWs lay = score_ws_layout(c->dtype, rows, c->t_len, slabs);
+    if (!lse_obs && (!ws || ws_bytes < lay.total || !aligned16(ws))) return KVC_EWORKSPACE;
+    if (scale == 0.f) scale = 1.0f / sqrtf((float)KVC_HEAD_DIM);
+    const ScorePlan pl = plan_score(c->dtype, rows, c->t_len, slabs);
+    ScoreLaunch p;
+    memset(&p, 0, sizeof(p));
+    p.k = slot_k(c, slot);
+    p.v = slot_v(c, slot);
+    p.nb = c->nb;
+    p.hkv = c->n_kv_heads;
+    p.g = g;
+    p.hq = n_q_heads;
+    p.w = w;
+    p.t_len = c->t_len;
+    p.t_cap = c->t_cap;
+    p.rows = rows;
+    p.q_obs = q_obs;
+    p.lse_obs = lse_obs;
+    p.scale = scale;
+    p.score = score;
+    p.range = range;
+    p.nsplit = pl.nsplit;
+    p.tps = pl.tps;
+    p.rows_pad = pl.rows_pad;
+    if (!lse_obs) {
+        char* base = static_cast<char*>(ws);
+        p.cnt = reinterpret_cast<uint32_t*>(base + lay.cnt_off);
+        p.lse_ws = reinterpret_cast<float*>(base + lay.lse_off);
+        p.stats = reinterpret_cast<float*>(base + lay.stats_off);
+    }
+    if (launch_score(p, c->dtype, (hipStream_t)stream) != hipSuccess) return KVC_EHIP;
+    return hip_status();
+}
+
+int kvc_select_ws_bytes(int nb, int n_kv_heads, int t_len, size_t* bytes) {
+    if (!bytes) return KVC_EALIGN;
+    if (nb < 0 || n_kv_heads < 1 || t_len < 0) return KVC_EINVAL;
+    *bytes = (size_t)nb * n_kv_heads * t_len * sizeof(uint32_t);
+    return KVC_OK;
+}
+
+int kvc_select(const float* score, const float* range, int nb, int n_kv_heads, int t_len,
+               int budget_k, int recent_b, int n_v, uint64_t seed, int layer_id, int32_t* kept,
+               void* ws, size_t ws_bytes, kvc_stream_t stream) {
+    if (nb < 0 || n_kv_heads < 1 || t_len < 0) return KVC_EINVAL;
+    if (budget_k < 0 || recent_b < 0 || n_v < 0 || n_v > budget_k) return KVC_EINVAL;
+    if ((long long)budget_k + recent_b < 1 || (long long)budget_k + recent_b > INT32_MAX)
+        return KVC_EINVAL;
+    if (layer_id < 0) return KVC_EINVAL;
+    if (nb == 0 || t_len == 0) return KVC_OK;
+    if (!aligned4(score) || !aligned4(kept)) return KVC_EALIGN;
+    if (n_v > 0 && !aligned4(range)) return KVC_EALIGN;
+    const size_t need = (size_t)nb * n_kv_heads * t_len * sizeof(uint32_t);
+    const bool evicts = t_len > budget_k + recent_b;
+    if (evicts && (!ws || ws_bytes < need || !aligned4(ws))) return KVC_EWORKSPACE;
+    SelectLaunch p;
+    memset(&p, 0, sizeof(p));
+    p.score = score;
+    p.range = range ? range : score;
+    p.nb = nb;
+    p.hkv = n_kv_heads;
+    p.t_len = t_len;
+    p.budget_k = budget_k;
+    p.recent_b = recent_b;
+    p.n_v = n_v;
+    p.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
+    p.seed_hi = (uint32_t)(seed >> 32);
+    p.layer_id = (uint32_t)layer_id;
+    p.kept = kept;
+    p.keys = static_cast<uint32_t*>(ws);
+    if (launch_select(p, (hipStream_t)stream) != hipSuccess) return KVC_EHIP;
+    return hip_status();
+}
+
+int kvc_compact(const kvc_cache* src, int slot, const int32_t* kept, int n_keep,
+                const kvc_cache* dst, kvc_stream_t stream) {
+    int st = check_cache(src);
+    if (st) return st;
+    st = check_cache(dst);
+    if (st) return st;
+    if (src->dtype != dst->dtype) return KVC_EDTYPE;
+    if (src->nb != dst->nb || src->n_kv_heads != dst->n_kv_heads) return KVC_EINVAL;
+    if (slot < 0 || slot >= src->n_slots || slot >= dst->n_slots) return KVC_EINVAL;
+    if (n_keep < 0 || n_keep > src->t_len || n_keep > dst->t_cap) return KVC_EINVAL;
+    if (src->nb == 0 || n_keep == 0) return KVC_OK;
+    if (!aligned4(kept)) return KVC_EALIGN;
+    const size_t es = elem_size(src->dtype);
+    const size_t sb = slot_elems(src) * es, db = slot_elems(dst) * es;
+    const char* sr[2] = {slot_k(src, slot), slot_v(src, slot)};
+    const char* dr[2] = {slot_k(dst, slot), slot_v(dst, slot)};
+    for (int a = 0; a < 2; ++a)
+        for (int b2 = 0; b2 < 2; ++b2)
+            if (sr[a] < dr[b2] + db && dr[b2] < sr[a] + sb) return KVC_EALIAS;
+    if (dr[0] < dr[1] + db && dr[1] < dr[0] + db) return KVC_EALIAS;
+    CompactLaunch p;
+    memset(&p, 0, sizeof(p));
+    p.sk = sr[0];
+    p.sv = sr[1];
+    p.dk = const_cast<char*>(dr[0]);
+    p.dv = const_cast<char*>(dr[1]);
+    p.nb = src->nb;
+    p.hkv = src->n_kv_heads;
+    p.src_t_len = src->t_len;
+    p.src_t_cap = src->t_cap;
+    p.dst_t_cap = dst->t_cap;
+    p.kept = kept;
+    p.n_keep = n_keep;
+    p.elem = (int)es;
+    if (launch_compact(p, (hipStream_t)stream) != hipSuccess) return KVC_EHIP;
+    return hip_status();
+}
+
+int kvc_philox_words(int64_t n, uint32_t c1, uint32_t c2, uint32_t c3, uint64_t seed,
+                     uint32_t* out, kvc_stream_t stream) {
+    if (n < 0 || n > (int64_t)1 << 32) return KVC_EINVAL;
+    if (n == 0) return KVC_OK;
+    if (!aligned16(out)) return KVC_EALIGN;
+    if (launch_philox(n, c1, c2, c3, (uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32), out,
+                      (hipStream_t)stream) != hipSuccess)
+        return KVC_EHIP;
+    return hip_status();
+}
+
+}  // extern "C"

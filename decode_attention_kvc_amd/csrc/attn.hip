@@ -1,0 +1,507 @@
+// Grouped-query decode attention over leader KV slots (split-K flash decode).
+//
+// Stochastic KV Routing (aitrends.kr article on R-CLA), inference and
+// implementation paragraphs: every layer reads the KV of its nearest earlier
+// leader, and only leaders store new rows.  One launch serves every q-layer
+// that reads one slot, so a leader's slab streams from HBM once for all of
+// its followers when the caller groups them.
+//
+// Work decomposition: grid (split, kv head, batch).  A workgroup of four
+// waves owns one contiguous range of 32-row tiles of one slab; its waves take
+// the tiles round-robin.  Per tile a wave
+//   * loads 32 K rows ([t][d]) and the 32-token slice of the token-minor V
+//     ([d][t]) straight from HBM into VGPRs with 16-byte loads,
+//   * forms S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (query rows on the N
+//     side, up to 16 per tile-column block),
+//   * runs the online softmax in registers (the MFMA output layout puts one
+//     query row per lane column, so the row max needs two cross-lane steps),
+//   * forms O^T += V^T P^T with the same MFMA, P split into a bf16 high part
+//     and a bf16 residual so the product keeps ~16 bits of P.
+// The K-row order inside a tile is permuted so that the S^T fragment a lane
+// holds is exactly its P^T operand fragment for the V^T product: no data
+// movement between the two products.
+// The four waves merge through LDS; each workgroup writes one partial
+// (m, l, acc) per query row; the last workgroup of a slab to finish (an
+// arrival counter in the workspace, reset by that workgroup) merges all
+// partials with log-sum-exp weights and writes out / lse.
+#include "common.h"
+#include "kvc_internal.h"
+
+namespace kvc {
+
+namespace {
+
+constexpr float LOG2E = 1.4426950408889634f;
+
+struct TileRegs {
+    u32x4 k[2][4];   // K rows: [column block c][d chunk kc]
+    u32x4 v[8];      // V^T slices: [d tile]
+};
+
+// Cache row that lane (l16) of column block c covers inside a 32-row tile.
+// Rows are ordered so that the S^T fragment of lane group lg covers tile
+// rows 8*lg .. 8*lg+7.
+__device__ __forceinline__ int tile_row(int c, int l16) {
+    return 8 * (l16 >> 2) + 4 * c + (l16 & 3);
+}
+
+__device__ __forceinline__ void load_tile(TileRegs& R, const uint16_t* kslab,
+                                          const uint16_t* vslab, int t_cap, int t0,
+                                          int l16, int lg, int append_row,
+                                          const uint16_t* knew_row) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int t = t0 + tile_row(c, l16);
+        const uint16_t* kr = (t == append_row) ? knew_row : kslab + (size_t)t * D;
+        kr += 8 * lg;
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) R.k[c][kc] = load_stream16(kr + 32 * kc);
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+        R.v[dt] = load_stream16(vslab + (size_t)(16 * dt + l16) * t_cap + t0 + 8 * lg);
+}
+
+__device__ __forceinline__ bf16x8 as_bf(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+// Merge the nsplit partials of one slab and write out / lse.
+// LDS `wgt` holds nsplit * rp floats.
+__device__ void combine_slab(const AttnLaunch& p, int slab, int b, int j, float* wgt) {
+    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+    const int nsplit = p.nsplit, rp = p.rp;
+    const size_t slabs = (size_t)p.nb * p.hkv;
+    const float* acc = p.part + (size_t)slab * nsplit * rp * D;
+    const float* ml = p.part + slabs * nsplit * rp * D + (size_t)slab * nsplit * rp * 2;
+    const int nwaves = blockDim.x / WAVE;
+    for (int r = wave; r < p.rows; r += nwaves) {
+        float m = -INFINITY;
+        for (int s = lane; s < nsplit; s += WAVE) m = fmaxf(m, ml[((size_t)s * rp + r) * 2]);
+        m = wave_max(m);
+        float l = 0.f;
+        for (int s = lane; s < nsplit; s += WAVE) {
+            const float ms = ml[((size_t)s * rp + r) * 2];
+            const float e = exp2f((ms - m) * LOG2E);
+            wgt[s * rp + r] = e;
+            l += e * ml[((size_t)s * rp + r) * 2 + 1];
+        }
+        l = wave_sum(l);
+        const float inv = 1.f / l;
+        for (int s = lane; s < nsplit; s += WAVE) wgt[s * rp + r] *= inv;
+        if (lane == 0 && p.lse) {
+            const int qi = r / p.g, h = j * p.g + r % p.g;
+            p.lse[p.lse_off[qi] + (size_t)b * p.hq + h] = m + logf(l);
+        }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < p.rows * D; idx += blockDim.x) {
+        const int r = idx / D, d = idx % D;
+        float o = 0.f;
+        int s = 0;
+        for (; s + 4 <= nsplit; s += 4) {
+            const float a0 = acc[((size_t)(s + 0) * rp + r) * D + d];
+            const float a1 = acc[((size_t)(s + 1) * rp + r) * D + d];
+            const float a2 = acc[((size_t)(s + 2) * rp + r) * D + d];
+            const float a3 = acc[((size_t)(s + 3) * rp + r) * D + d];
+            o += wgt[(s + 0) * rp + r] * a0;
+            o += wgt[(s + 1) * rp + r] * a1;
+            o += wgt[(s + 2) * rp + r] * a2;
+            o += wgt[(s + 3) * rp + r] * a3;
+        }
+        for (; s < nsplit; ++s) o += wgt[s * rp + r] * acc[((size_t)s * rp + r) * D + d];
+        const int qi = r / p.g, h = j * p.g + r % p.g;
+        p.out[p.out_off[qi] + ((size_t)b * p.hq + h) * D + d] = o;
+    }
+}
+
+// Publish this workgroup's partial and let the last one merge.  Returns
+// whether this workgroup merged.
+__device__ bool arrive_and_combine(const AttnLaunch& p, int slab, int b, int j, float* wgt) {
+    __shared__ int last;
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t old = atomicAdd(&p.cnt[slab], 1u);
+        last = (old == (uint32_t)(p.nsplit - 1));
+    }
+    __syncthreads();
+    if (!last) return false;
+    __threadfence();
+    combine_slab(p, slab, b, j, wgt);
+    if (threadIdx.x == 0) p.cnt[slab] = 0u;
+    return true;
+}
+
+template <typename T>
+__device__ void write_append_row(const AttnLaunch& p, int b, int j) {
+    const size_t slab = (size_t)b * p.hkv + j;
+    const T* kn = reinterpret_cast<const T*>(p.k_new) + slab * D;
+    const T* vn = reinterpret_cast<const T*>(p.v_new) + slab * D;
+    T* kc = const_cast<T*>(reinterpret_cast<const T*>(p.k)) + slab * p.t_cap * D;
+    T* vc = const_cast<T*>(reinterpret_cast<const T*>(p.v)) + slab * D * p.t_cap;
+    const int t = p.t_len - 1;
+    for (int d = threadIdx.x; d < D; d += blockDim.x) {
+        kc[(size_t)t * D + d] = kn[d];
+        vc[(size_t)d * p.t_cap + t] = vn[d];
+    }
+}
+
+template <int NT>
+__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnLaunch p) {
+    constexpr int RP = 16 * NT;
+    const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+    const int slab = b * p.hkv + j;
+    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int T = p.t_len;
+    const int ntiles = (T + ATTN_TILE - 1) / ATTN_TILE;
+    const int tile_begin = s * p.tps;
+    const int tile_end = min(tile_begin + p.tps, ntiles);
+
+    const uint16_t* kslab = reinterpret_cast<const uint16_t*>(p.k) + (size_t)slab * p.t_cap * D;
+    const uint16_t* vslab = reinterpret_cast<const uint16_t*>(p.v) + (size_t)slab * D * p.t_cap;
+    const int append_row = p.append_read ? T - 1 : -1;
+    const uint16_t* knew_row =
+        p.append_read ? reinterpret_cast<const uint16_t*>(p.k_new) + (size_t)slab * D : kslab;
+    const uint16_t* vnew_row =
+        p.append_read ? reinterpret_cast<const uint16_t*>(p.v_new) + (size_t)slab * D : kslab;
+
+    // Q^T operand fragments: lane holds query row nt*16 + l16, channels
+    // 32*kc + 8*lg .. +8.
+    bf16x8 qB[NT][4];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int r = nt * 16 + l16;
+        if (r < p.rows) {
+            const int qi = r / p.g, h = j * p.g + r % p.g;
+            const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + p.q_off[qi] +
+                                 ((size_t)b * p.hq + h) * D + 8 * lg;
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) qB[nt][kc] = as_bf(load16(qp + 32 * kc));
+        } else {
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) qB[nt][kc] = as_bf(u32x4{0u, 0u, 0u, 0u});
+        }
+    }
+
+    f32x4 acc[NT][8];
+    float m[NT], lsum[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        m[nt] = -INFINITY;
+        lsum[nt] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) acc[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const float scale = p.scale;
+
+    auto compute = [&](TileRegs& R, int t0) {
+        const bool tail = (t0 + ATTN_TILE > T);
+        if (tail) {
+            // Rows past the end hold arbitrary bits: zero their V entries
+            // (P is zero there too, but 0 * NaN would poison the sum) and
+            // take the appended row's values from v_new.
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                u16x8 e = __builtin_bit_cast(u16x8, R.v[dt]);
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const int t = t0 + 8 * lg + jj;
+                    if (t == append_row) e[jj] = vnew_row[16 * dt + l16];
+                    else if (t >= T) e[jj] = 0;
+                }
+                R.v[dt] = __builtin_bit_cast(u32x4, e);
+            }
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            f32x4 S[2];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                S[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kc = 0; kc < 4; ++kc)
+                    S[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(R.k[c][kc]), qB[nt][kc],
+                                                                    S[c], 0, 0, 0);
+            }
+            // S[c][i]: query row nt*16 + l16, cache row t0 + 8*lg + 4*c + i.
+            float sv[8];
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float x = S[c][i] * scale;
+                    if (tail && (t0 + 8 * lg + 4 * c + i >= T)) x = -INFINITY;
+                    sv[4 * c + i] = x;
+                }
+            float mx = sv[0];
+#pragma unroll
+            for (int jj = 1; jj < 8; ++jj) mx = fmaxf(mx, sv[jj]);
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mnew = fmaxf(m[nt], mx);
+            const float alpha = exp2f((m[nt] - mnew) * LOG2E);
+            m[nt] = mnew;
+            float ps = 0.f;
+            u16x8 hi, lo;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                const float pj = exp2f((sv[jj] - mnew) * LOG2E);
+                ps += pj;
+                const uint16_t h16 = f32_to_bf16(pj);
+                hi[jj] = h16;
+                lo[jj] = f32_to_bf16(pj - bf16_to_f32(h16));
+            }
+            lsum[nt] = lsum[nt] * alpha + ps;
+            const bf16x8 pH = __builtin_bit_cast(bf16x8, hi);
+            const bf16x8 pL = __builtin_bit_cast(bf16x8, lo);
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                acc[nt][dt] *= alpha;
+                acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(R.v[dt]), pH,
+                                                                       acc[nt][dt], 0, 0, 0);
+                acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(R.v[dt]), pL,
+                                                                       acc[nt][dt], 0, 0, 0);
+            }
+        }
+    };
+
+    // Tile loop: each wave keeps one tile (16 KB) of loads in flight; the
+    // other waves on the SIMD hide the latency.
+    for (int tile = tile_begin + wave; tile < tile_end; tile += ATTN_WAVES) {
+        TileRegs R;
+        load_tile(R, kslab, vslab, p.t_cap, tile * ATTN_TILE, l16, lg, append_row, knew_row);
+        compute(R, tile * ATTN_TILE);
+    }
+
+    // Row sums: each of the four lane groups holds a quarter of the rows.
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        lsum[nt] += __shfl_xor(lsum[nt], 16);
+        lsum[nt] += __shfl_xor(lsum[nt], 32);
+    }
+
+    // Merge the four waves through LDS, one 16-row block at a time, and
+    // write this workgroup's partial.
+    __shared__ float buf[ATTN_WAVES * 16 * D];   // also the combine weights
+    __shared__ float wm[ATTN_WAVES][16], wl[ATTN_WAVES][16];
+    const size_t slabs = (size_t)p.nb * p.hkv;
+    float* part_acc = p.part + ((size_t)slab * p.nsplit + s) * RP * D;
+    float* part_ml = p.part + slabs * p.nsplit * RP * D + ((size_t)slab * p.nsplit + s) * RP * 2;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        if (lg == 0) {
+            wm[wave][l16] = m[nt];
+            wl[wave][l16] = lsum[nt];
+        }
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) buf[(wave * 16 + l16) * D + 16 * dt + 4 * lg + i] = acc[nt][dt][i];
+        __syncthreads();
+        {
+            const int n = tid / 16, d0 = (tid % 16) * 8;
+            float M = wm[0][n];
+#pragma unroll
+            for (int w = 1; w < ATTN_WAVES; ++w) M = fmaxf(M, wm[w][n]);
+            float f[ATTN_WAVES], L = 0.f;
+#pragma unroll
+            for (int w = 0; w < ATTN_WAVES; ++w) {
+                f[w] = exp2f((wm[w][n] - M) * LOG2E);   // waves without rows: exp2(-inf) = 0
+                L += f[w] * wl[w][n];
+            }
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float a = 0.f;
+#pragma unroll
+                for (int w = 0; w < ATTN_WAVES; ++w) a += f[w] * buf[(w * 16 + n) * D + d0 + e];
+                o[e] = a;
+            }
+            float* dst = part_acc + (size_t)(nt * 16 + n) * D + d0;
+            *reinterpret_cast<f32x4*>(dst) = f32x4{o[0], o[1], o[2], o[3]};
+            *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
+            if (d0 == 0) {
+                part_ml[(nt * 16 + n) * 2] = M;
+                part_ml[(nt * 16 + n) * 2 + 1] = L;
+            }
+        }
+        __syncthreads();
+    }
+
+    if (p.append_write && s == p.nsplit - 1) write_append_row<uint16_t>(p, b, j);
+    arrive_and_combine(p, slab, b, j, buf);
+}
+
+// float32 path: plain VALU arithmetic, up to 16 query rows per launch.
+__global__ __launch_bounds__(256) void attn_f32_kernel(AttnLaunch p) {
+    constexpr int TT = ATTN_TILE_F32;
+    const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+    const int slab = b * p.hkv + j;
+    const int tid = threadIdx.x;
+    const int T = p.t_len;
+    const int ntiles = (T + TT - 1) / TT;
+    const int tile_begin = s * p.tps;
+    const int tile_end = min(tile_begin + p.tps, ntiles);
+    const float* kslab = reinterpret_cast<const float*>(p.k) + (size_t)slab * p.t_cap * D;
+    const float* vslab = reinterpret_cast<const float*>(p.v) + (size_t)slab * D * p.t_cap;
+    const float* knew = reinterpret_cast<const float*>(p.k_new) + (size_t)slab * D;
+    const float* vnew = reinterpret_cast<const float*>(p.v_new) + (size_t)slab * D;
+    const int append_row = p.append_read ? T - 1 : -1;
+
+    __shared__ float qs[16][D];
+    __shared__ float Sx[16][TT + 1];
+    __shared__ float mrow[16], lrow[16], arow[16];
+    __shared__ float wgt[MAX_SPLIT_ROWS];
+
+    for (int idx = tid; idx < 16 * D; idx += blockDim.x) {
+        const int r = idx / D, d = idx % D;
+        float x = 0.f;
+        if (r < p.rows) {
+            const int qi = r / p.g, h = j * p.g + r % p.g;
+            x = reinterpret_cast<const float*>(p.q)[p.q_off[qi] + ((size_t)b * p.hq + h) * D + d];
+        }
+        qs[r][d] = x;
+    }
+    if (tid < 16) {
+        mrow[tid] = -INFINITY;
+        lrow[tid] = 0.f;
+    }
+    __syncthreads();
+
+    const int d = tid % D, half = tid / D;   // P*V: channel d, rows half + 2k
+    float acc[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+
+    for (int tile = tile_begin; tile < tile_end; ++tile) {
+        const int t0 = tile * TT;
+        // S = scale * q . k for 64 rows; four lanes per row, 32 channels each.
+        {
+            const int tr = tid / 4, part = tid % 4;
+            const int t = t0 + tr;
+            float kv[32];
+            const float* kr = (t == append_row) ? knew : kslab + (size_t)t * D;
+#pragma unroll
+            for (int x = 0; x < 32; x += 4) {
+                const f32x4 v4 = *reinterpret_cast<const f32x4*>(kr + 32 * part + x);
+                kv[x] = v4[0]; kv[x + 1] = v4[1]; kv[x + 2] = v4[2]; kv[x + 3] = v4[3];
+            }
+            for (int r = 0; r < 16; ++r) {
+                float a = 0.f;
+#pragma unroll
+                for (int x = 0; x < 32; ++x) a = fmaf(qs[r][32 * part + x], kv[x], a);
+                a += __shfl_xor(a, 1);
+                a += __shfl_xor(a, 2);
+                if (part == 0) Sx[r][tr] = (t < T) ? a * p.scale : -INFINITY;
+            }
+        }
+        __syncthreads();
+        // Online softmax: 16 threads per row, 4 columns each.
+        {
+            const int r = tid / 16, sub = tid % 16;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) mx = fmaxf(mx, Sx[r][4 * sub + c]);
+#pragma unroll
+            for (int mk = 1; mk < 16; mk <<= 1) mx = fmaxf(mx, __shfl_xor(mx, mk));
+            const float mold = mrow[r];
+            const float mnew = fmaxf(mold, mx);
+            float ps = 0.f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float pv = expf(Sx[r][4 * sub + c] - mnew);
+                Sx[r][4 * sub + c] = pv;
+                ps += pv;
+            }
+#pragma unroll
+            for (int mk = 1; mk < 16; mk <<= 1) ps += __shfl_xor(ps, mk);
+            if (sub == 0) {
+                const float a = expf(mold - mnew);
+                arow[r] = a;
+                lrow[r] = lrow[r] * a + ps;
+                mrow[r] = mnew;
+            }
+        }
+        __syncthreads();
+        // acc[r][d] = acc * alpha + sum_t p[r][t] V^T[d][t]
+        {
+            float vv[TT];
+            const float* vr = vslab + (size_t)d * p.t_cap + t0;
+#pragma unroll
+            for (int x = 0; x < TT; x += 4) {
+                const f32x4 v4 = *reinterpret_cast<const f32x4*>(vr + x);
+                vv[x] = v4[0]; vv[x + 1] = v4[1]; vv[x + 2] = v4[2]; vv[x + 3] = v4[3];
+            }
+            if (t0 + TT > T) {
+#pragma unroll
+                for (int x = 0; x < TT; ++x) {
+                    if (t0 + x == append_row) vv[x] = vnew[d];
+                    else if (t0 + x >= T) vv[x] = 0.f;
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int r = half + 2 * k;
+                float a = acc[k] * arow[r];
+#pragma unroll
+                for (int x = 0; x < TT; ++x) a = fmaf(Sx[r][x], vv[x], a);
+                acc[k] = a;
+            }
+        }
+        __syncthreads();
+    }
+
+    const size_t slabs = (size_t)p.nb * p.hkv;
+    float* part_acc = p.part + ((size_t)slab * p.nsplit + s) * 16 * D;
+    float* part_ml = p.part + slabs * p.nsplit * 16 * D + ((size_t)slab * p.nsplit + s) * 16 * 2;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) part_acc[(size_t)(half + 2 * k) * D + d] = acc[k];
+    if (tid < 16) {
+        part_ml[tid * 2] = mrow[tid];
+        part_ml[tid * 2 + 1] = lrow[tid];
+    }
+    if (p.append_write && s == p.nsplit - 1) write_append_row<float>(p, b, j);
+    arrive_and_combine(p, slab, b, j, wgt);
+}
+
+template <typename T>
+__global__ __launch_bounds__(128) void append_kernel(T* k, T* v, int hkv, int t_len, int t_cap,
+                                                     const T* k_new, const T* v_new) {
+    const size_t slab = (size_t)blockIdx.y * hkv + blockIdx.x;
+    const int t = t_len - 1;
+    for (int d = threadIdx.x; d < D; d += blockDim.x) {
+        k[(slab * t_cap + t) * D + d] = k_new[slab * D + d];
+        v[(slab * D + d) * t_cap + t] = v_new[slab * D + d];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attn(const AttnLaunch& p, int dtype, int nt, hipStream_t st) {
+    const dim3 grid(p.nsplit, p.hkv, p.nb);
+    if (dtype == 0) {
+        hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(256), 0, st, p);
+    } else if (nt == 1) {
+        hipLaunchKernelGGL(attn_bf16_kernel<1>, grid, dim3(256), 0, st, p);
+    } else if (nt == 2) {
+        hipLaunchKernelGGL(attn_bf16_kernel<2>, grid, dim3(256), 0, st, p);
+    } else {
+        hipLaunchKernelGGL(attn_bf16_kernel<4>, grid, dim3(256), 0, st, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_append(const void* k, const void* v, int nb, int hkv, int t_len, int t_cap,
+                         const void* k_new, const void* v_new, int elem, hipStream_t st) {
+    const dim3 grid(hkv, nb);
+    if (elem == 4)
+        hipLaunchKernelGGL(append_kernel<float>, grid, dim3(128), 0, st, (float*)k, (float*)v,
+                           hkv, t_len, t_cap, (const float*)k_new, (const float*)v_new);
+    else
+        hipLaunchKernelGGL(append_kernel<uint16_t>, grid, dim3(128), 0, st, (uint16_t*)k,
+                           (uint16_t*)v, hkv, t_len, t_cap, (const uint16_t*)k_new,
+                           (const uint16_t*)v_new);
+    return hipGetLastError();
+}
+
+}  // namespace kvc

@@ -1,0 +1,98 @@
+// Internal launch descriptors shared by the host dispatcher (abi.cpp) and the
+// kernels.  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvc {
+
+constexpr int MAX_QL = 64;       // q-layers served by one attention launch
+constexpr int ATTN_TILE = 32;    // cache rows per attention step (bf16 path)
+constexpr int ATTN_TILE_F32 = 64;
+constexpr int ATTN_WAVES = 4;    // waves per attention workgroup
+constexpr int MAX_SPLIT_ROWS = 4096;  // nsplit * padded rows (combine weights)
+constexpr int SCORE_TILE = 32;
+constexpr int SCORE_MAX_TPS = 16;     // tiles per score workgroup
+constexpr int SELECT_THREADS = 1024;
+
+// One attention launch: a set of q-layers that all read one cache slot.
+struct AttnLaunch {
+    const void* k;          // slot base of K: [nb][hkv][t_cap][D]
+    const void* v;          // slot base of V: [nb][hkv][D][t_cap]
+    int nb, hkv, g, hq;
+    int t_len, t_cap;
+    int nql, rows;          // q-layers in this launch, rows = nql * g
+    int rp;                 // padded rows per slab in the workspace
+    const void* q;
+    int64_t q_off[MAX_QL];  // element offset of q-layer i
+    float* out;
+    int64_t out_off[MAX_QL];
+    float* lse;             // may be null
+    int64_t lse_off[MAX_QL];
+    float scale;
+    const void* k_new;      // [nb][hkv][D], read when append_read
+    const void* v_new;
+    int append_read;        // row t_len-1 comes from k_new / v_new
+    int append_write;       // and is written into the cache
+    int nsplit, tps;        // splits per slab, tiles per split
+    float* part;            // partial accumulators, then (m, l) pairs
+    uint32_t* cnt;          // one arrival counter per slab
+};
+
+// One observation-window score launch over one cache slot.
+struct ScoreLaunch {
+    const void* k;          // slot base of K
+    const void* v;          // slot base of V (for the fused range)
+    int nb, hkv, g, hq, w;
+    int t_len, t_cap;
+    int rows;               // g * w
+    const void* q_obs;      // [w][nb][hq][D]
+    const float* lse_obs;   // [w][nb][hq] or null (then `lse_ws` is used)
+    float scale;
+    float* score;           // [nb][hkv][t_len]
+    float* range;           // [nb][hkv][t_len] or null
+    int nsplit, tps;
+    float* stats;           // [slabs][nsplit][rows_pad][2] partial (m, z)
+    float* lse_ws;          // [slabs][rows_pad] merged log-normalisers
+    uint32_t* cnt;          // [slabs]
+    int rows_pad;
+};
+
+struct SelectLaunch {
+    const float* score;
+    const float* range;
+    int nb, hkv, t_len, budget_k, recent_b, n_v;
+    uint32_t seed_lo, seed_hi;
+    uint32_t layer_id;
+    int32_t* kept;
+    uint32_t* keys;         // workspace [slabs][t_len]
+};
+
+struct CompactLaunch {
+    const void* sk;
+    const void* sv;
+    void* dk;
+    void* dv;
+    int nb, hkv;
+    int src_t_len, src_t_cap, dst_t_cap;
+    const int32_t* kept;
+    int n_keep;
+    int elem;               // bytes per element
+};
+
+// Host-side launchers (defined next to their kernels).  Each returns
+// hipSuccess or the launch error.
+hipError_t launch_attn(const AttnLaunch& p, int dtype, int nt, hipStream_t s);
+hipError_t launch_append(const void* k, const void* v, int nb, int hkv, int t_len,
+                         int t_cap, const void* k_new, const void* v_new, int elem,
+                         hipStream_t s);
+hipError_t launch_value_range(const void* v, int nb, int hkv, int t_len, int t_cap,
+                              int dtype, float* range, hipStream_t s);
+hipError_t launch_score(const ScoreLaunch& p, int dtype, hipStream_t s);
+hipError_t launch_select(const SelectLaunch& p, hipStream_t s);
+hipError_t launch_compact(const CompactLaunch& p, hipStream_t s);
+hipError_t launch_philox(int64_t n, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                         uint32_t k1, uint32_t* out, hipStream_t s);
+
+}  // namespace kvc

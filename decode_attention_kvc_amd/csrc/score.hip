@@ -1,0 +1,474 @@
+// Observation-window score and value range over one cache slot.
+//
+// VASE summary (gist.science 2606.03928): §2.B scores rows by the attention
+// the last decode queries (SnapKV's observation window) pay them, and §2.A
+// measures each value row by Range(v) = max(v) - min(v).
+//
+// score[b][j][t] = sum over the g heads of kv head j and the w window rows i
+// of softmax_t(scale * q_obs[i][b][h] . K[t]), where window row i sees rows
+// t <= t_len - w + i.  The g*w query rows against a 32-row K tile are a real
+// dense contraction (128-160 rows x 128 channels x 32 rows), so it runs on
+// v_mfma_f32_16x16x32_bf16: A = 16 query rows x 32 channels, B = 32 channels
+// x 16 cache rows; the output lane layout puts one cache row per lane column,
+// so the column sums over query rows are in-lane adds plus two cross-lane
+// steps.  Each wave owns 32 query rows (one head's 32-query window), the
+// workgroup covers all g*w rows of one slab over a range of tiles, and the
+// waves' column sums meet in LDS in a fixed order (deterministic).
+//
+// Without the log-normalisers of the window rows a first pass computes them
+// (per-row online max / sum over the workgroup's tiles, merged across
+// workgroups by the last one to arrive).  The range is fused into the second
+// pass: per tile one wave also reads the tile's token-minor V slice.
+#include "common.h"
+#include "kvc_internal.h"
+
+namespace kvc {
+
+namespace {
+
+__device__ __forceinline__ bf16x8 as_bf(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+// Range of the 32 rows t0..t0+31 of one slab from its token-minor V slice;
+// one wave.  Lane (l16, lg) reads channels 16*dt + l16 of rows
+// t0 + 8*lg .. +8.
+__device__ __forceinline__ void range_tile_bf16(const uint16_t* vslab, int t_cap, int t0, int T,
+                                                float* range_out, int lane) {
+    const int l16 = lane & 15, lg = lane >> 4;
+    float mx[8], mn[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+        mx[jj] = -INFINITY;
+        mn[jj] = INFINITY;
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+        const u32x4 x = load16(vslab + (size_t)(16 * dt + l16) * t_cap + t0 + 8 * lg);
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+            const float a = bf16lo(x[w2]), b2 = bf16hi(x[w2]);
+            mx[2 * w2] = fmaxf(mx[2 * w2], a);
+            mn[2 * w2] = fminf(mn[2 * w2], a);
+            mx[2 * w2 + 1] = fmaxf(mx[2 * w2 + 1], b2);
+            mn[2 * w2 + 1] = fminf(mn[2 * w2 + 1], b2);
+        }
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            mx[jj] = fmaxf(mx[jj], __shfl_xor(mx[jj], m));
+            mn[jj] = fminf(mn[jj], __shfl_xor(mn[jj], m));
+        }
+    }
+    if (l16 == 0) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            const int t = t0 + 8 * lg + jj;
+            if (t < T) range_out[t] = mx[jj] - mn[jj];
+        }
+    }
+}
+
+// Query fragments of one wave: 2 blocks of 16 rows, 4 channel chunks.
+struct QFrag {
+    bf16x8 a[2][4];
+};
+
+__device__ __forceinline__ void load_qfrag(QFrag& Q, const ScoreLaunch& p, int b, int j, int wave,
+                                           int l16, int lg) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        const int R = wave * 32 + mt * 16 + l16;
+        if (R < p.rows) {
+            const int h = j * p.g + R / p.w, iw = R % p.w;
+            const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q_obs) +
+                                 (((size_t)iw * p.nb + b) * p.hq + h) * D + 8 * lg;
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) Q.a[mt][kc] = as_bf(load16(qp + 32 * kc));
+        } else {
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) Q.a[mt][kc] = as_bf(u32x4{0u, 0u, 0u, 0u});
+        }
+    }
+}
+
+// S[mt][cg][i] = q_row(wave*32 + mt*16 + 4*lg + i) . k_row(t0 + 16*cg + l16)
+__device__ __forceinline__ void score_tile_mfma(const QFrag& Q, const uint16_t* kslab, int t0,
+                                                int l16, int lg, f32x4 S[2][2]) {
+    u32x4 kb[2][4];
+#pragma unroll
+    for (int cg = 0; cg < 2; ++cg) {
+        const uint16_t* kr = kslab + (size_t)(t0 + 16 * cg + l16) * D + 8 * lg;
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) kb[cg][kc] = load16(kr + 32 * kc);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int cg = 0; cg < 2; ++cg) {
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Q.a[mt][kc], as_bf(kb[cg][kc]), acc,
+                                                              0, 0, 0);
+            S[mt][cg] = acc;
+        }
+}
+
+// Merge two (max, sum-of-exp) pairs.
+__device__ __forceinline__ void ms_merge(float& m, float& z, float m2, float z2) {
+    const float mn = fmaxf(m, m2);
+    if (mn == -INFINITY) return;
+    z = z * expf(m - mn) + z2 * expf(m2 - mn);
+    m = mn;
+}
+
+// Pass 1: per window row, max and sum of exp over its visible rows.
+__global__ __launch_bounds__(1024) void score_stats_bf16(ScoreLaunch p) {
+    const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+    const int slab = b * p.hkv + j;
+    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int T = p.t_len;
+    const int ntiles = (T + SCORE_TILE - 1) / SCORE_TILE;
+    const int tile_begin = s * p.tps, tile_end = min(tile_begin + p.tps, ntiles);
+    const uint16_t* kslab = reinterpret_cast<const uint16_t*>(p.k) + (size_t)slab * p.t_cap * D;
+
+    QFrag Q;
+    load_qfrag(Q, p, b, j, wave, l16, lg);
+    float m[2][4], z[2][4];
+    int lim[2][4];   // last visible cache row of each of the lane's rows
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            m[mt][i] = -INFINITY;
+            z[mt][i] = 0.f;
+            const int R = wave * 32 + mt * 16 + 4 * lg + i;
+            lim[mt][i] = (R < p.rows) ? T - p.w + R % p.w : -1;
+        }
+    for (int tile = tile_begin; tile < tile_end; ++tile) {
+        const int t0 = tile * SCORE_TILE;
+        f32x4 S[2][2];
+        score_tile_mfma(Q, kslab, t0, l16, lg, S);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float x0 = S[mt][0][i] * p.scale, x1 = S[mt][1][i] * p.scale;
+                if (t0 + l16 > lim[mt][i]) x0 = -INFINITY;
+                if (t0 + 16 + l16 > lim[mt][i]) x1 = -INFINITY;
+                const float mn = fmaxf(m[mt][i], fmaxf(x0, x1));
+                if (mn != -INFINITY) {
+                    z[mt][i] = z[mt][i] * expf(m[mt][i] - mn) + expf(x0 - mn) + expf(x1 - mn);
+                    m[mt][i] = mn;
+                }
+            }
+    }
+    // Merge the 16 lanes (cache-row columns) that share each query row.
+#pragma unroll
+    for (int k = 1; k < 16; k <<= 1)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float m2 = __shfl_xor(m[mt][i], k), z2 = __shfl_xor(z[mt][i], k);
+                ms_merge(m[mt][i], z[mt][i], m2, z2);
+            }
+    float* st = p.stats + ((size_t)slab * p.nsplit + s) * p.rows_pad * 2;
+    if (l16 == 0) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int R = wave * 32 + mt * 16 + 4 * lg + i;
+                st[R * 2] = m[mt][i];
+                st[R * 2 + 1] = z[mt][i];
+            }
+    }
+    // The last workgroup of the slab merges every split's pairs into lse.
+    __shared__ int last;
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) last = (atomicAdd(&p.cnt[slab], 1u) == (uint32_t)(p.nsplit - 1));
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+    const float* all = p.stats + (size_t)slab * p.nsplit * p.rows_pad * 2;
+    for (int R = tid; R < p.rows; R += blockDim.x) {
+        float mm = -INFINITY, zz = 0.f;
+        for (int sp = 0; sp < p.nsplit; ++sp)
+            ms_merge(mm, zz, all[((size_t)sp * p.rows_pad + R) * 2],
+                     all[((size_t)sp * p.rows_pad + R) * 2 + 1]);
+        p.lse_ws[(size_t)slab * p.rows_pad + R] = mm + logf(zz);
+    }
+    if (tid == 0) p.cnt[slab] = 0u;
+}
+
+// Pass 2: column sums of the window softmax, plus the fused value range.
+__global__ __launch_bounds__(1024) void score_main_bf16(ScoreLaunch p) {
+    const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+    const int slab = b * p.hkv + j;
+    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+    const int nwaves = blockDim.x / WAVE;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int T = p.t_len;
+    const int ntiles = (T + SCORE_TILE - 1) / SCORE_TILE;
+    const int tile_begin = s * p.tps, tile_end = min(tile_begin + p.tps, ntiles);
+    const uint16_t* kslab = reinterpret_cast<const uint16_t*>(p.k) + (size_t)slab * p.t_cap * D;
+    const uint16_t* vslab = reinterpret_cast<const uint16_t*>(p.v) + (size_t)slab * D * p.t_cap;
+    float* score = p.score + (size_t)slab * T;
+    float* range = p.range ? p.range + (size_t)slab * T : nullptr;
+
+    __shared__ float colsum[16][SCORE_MAX_TPS * SCORE_TILE];
+
+    QFrag Q;
+    load_qfrag(Q, p, b, j, wave, l16, lg);
+    float lse[2][4];
+    int lim[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int R = wave * 32 + mt * 16 + 4 * lg + i;
+            if (R < p.rows) {
+                const int h = j * p.g + R / p.w, iw = R % p.w;
+                lse[mt][i] = p.lse_obs ? p.lse_obs[((size_t)iw * p.nb + b) * p.hq + h]
+                                       : p.lse_ws[(size_t)slab * p.rows_pad + R];
+                lim[mt][i] = T - p.w + iw;
+            } else {
+                lse[mt][i] = 0.f;
+                lim[mt][i] = -1;
+            }
+        }
+    for (int tile = tile_begin; tile < tile_end; ++tile) {
+        const int t0 = tile * SCORE_TILE;
+        f32x4 S[2][2];
+        score_tile_mfma(Q, kslab, t0, l16, lg, S);
+#pragma unroll
+        for (int cg = 0; cg < 2; ++cg) {
+            float c = 0.f;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float pr = expf(S[mt][cg][i] * p.scale - lse[mt][i]);
+                    c += (t0 + 16 * cg + l16 <= lim[mt][i]) ? pr : 0.f;
+                }
+            c += __shfl_xor(c, 16);
+            c += __shfl_xor(c, 32);
+            if (lg == 0) colsum[wave][(tile - tile_begin) * SCORE_TILE + 16 * cg + l16] = c;
+        }
+        if (range && (tile - tile_begin) % nwaves == wave)
+            range_tile_bf16(vslab, p.t_cap, t0, T, range, lane);
+    }
+    __syncthreads();
+    const int n = (tile_end - tile_begin) * SCORE_TILE;
+    for (int x = tid; x < n; x += blockDim.x) {
+        float c = 0.f;
+        for (int w = 0; w < nwaves; ++w) c += colsum[w][x];
+        const int t = tile_begin * SCORE_TILE + x;
+        if (t < T) score[t] = c;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// float32 path (VALU), 64-row tiles staged in LDS.
+// ---------------------------------------------------------------------------
+constexpr int FT = 64;
+
+__device__ void f32_stage_k(float (*ks)[D + 1], const float* kslab, int t0, int tid, int nthr) {
+    for (int idx = tid; idx < FT * D; idx += nthr) {
+        const int t = idx / D, d = idx % D;
+        ks[t][d] = kslab[(size_t)(t0 + t) * D + d];
+    }
+}
+
+__device__ float f32_dot_row(const float* q, const float (*ks)[D + 1], int t) {
+    float a = 0.f;
+#pragma unroll 8
+    for (int d = 0; d < D; ++d) a = fmaf(q[d], ks[t][d], a);
+    return a;
+}
+
+// One workgroup (256 threads) per (split, kv head, batch); thread
+// (t = tid % 64, rgroup = tid / 64) handles window rows rgroup, rgroup+4, ...
+__global__ __launch_bounds__(256) void score_f32(ScoreLaunch p, int stats_pass) {
+    const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+    const int slab = b * p.hkv + j;
+    const int tid = threadIdx.x, tl = tid % FT, rg = tid / FT;
+    const int T = p.t_len;
+    const int ntiles = (T + FT - 1) / FT;
+    const int tile_begin = s * p.tps, tile_end = min(tile_begin + p.tps, ntiles);
+    const float* kslab = reinterpret_cast<const float*>(p.k) + (size_t)slab * p.t_cap * D;
+    const float* vslab = reinterpret_cast<const float*>(p.v) + (size_t)slab * D * p.t_cap;
+    __shared__ float ks[FT][D + 1];
+    __shared__ float csum[4][FT];
+    __shared__ int last;
+
+    // Rows rg + 4k, k < 32: at most 128 window rows on this path, so the
+    // per-row state stays in registers.
+    constexpr int MAXR = 32;
+    float m[MAXR], z[MAXR];
+#pragma unroll
+    for (int k = 0; k < MAXR; ++k) {
+        m[k] = -INFINITY;
+        z[k] = 0.f;
+    }
+    for (int tile = tile_begin; tile < tile_end; ++tile) {
+        const int t0 = tile * FT;
+        __syncthreads();
+        f32_stage_k(ks, kslab, t0, tid, blockDim.x);
+        __syncthreads();
+        const int t = t0 + tl;
+        float c = 0.f;
+#pragma unroll
+        for (int k = 0; k < MAXR; ++k) {
+            const int R = rg + 4 * k;
+            if (R >= p.rows) continue;
+            const int h = j * p.g + R / p.w, iw = R % p.w;
+            const float* q = reinterpret_cast<const float*>(p.q_obs) +
+                             (((size_t)iw * p.nb + b) * p.hq + h) * D;
+            const float x = f32_dot_row(q, ks, tl) * p.scale;
+            const bool vis = t <= T - p.w + iw;
+            if (stats_pass) {
+                if (vis) {
+                    const float mn = fmaxf(m[k], x);
+                    z[k] = z[k] * expf(m[k] - mn) + expf(x - mn);
+                    m[k] = mn;
+                }
+            } else if (vis) {
+                const float l = p.lse_obs ? p.lse_obs[((size_t)iw * p.nb + b) * p.hq + h]
+                                          : p.lse_ws[(size_t)slab * p.rows_pad + R];
+                c += expf(x - l);
+            }
+        }
+        if (!stats_pass) {
+            csum[rg][tl] = c;
+            __syncthreads();
+            if (tid < FT && t0 + tid < T) {
+                p.score[(size_t)slab * T + t0 + tid] =
+                    csum[0][tid] + csum[1][tid] + csum[2][tid] + csum[3][tid];
+                if (p.range) {
+                    float mx = -INFINITY, mn = INFINITY;
+                    for (int d = 0; d < D; ++d) {
+                        const float v = vslab[(size_t)d * p.t_cap + t0 + tid];
+                        mx = fmaxf(mx, v);
+                        mn = fminf(mn, v);
+                    }
+                    p.range[(size_t)slab * T + t0 + tid] = mx - mn;
+                }
+            }
+        }
+    }
+    if (!stats_pass) return;
+    // Merge across the 64 cache-row lanes of each row group, then across
+    // splits in the last workgroup.
+    float* st = p.stats + ((size_t)slab * p.nsplit + s) * p.rows_pad * 2;
+#pragma unroll
+    for (int k = 0; k < MAXR; ++k) {
+        const int R = rg + 4 * k;
+        float mm = m[k], zz = z[k];
+        for (int msk = 1; msk < 64; msk <<= 1) {
+            const float m2 = __shfl_xor(mm, msk), z2 = __shfl_xor(zz, msk);
+            ms_merge(mm, zz, m2, z2);
+        }
+        if (tl == 0 && R < p.rows) {
+            st[R * 2] = mm;
+            st[R * 2 + 1] = zz;
+        }
+    }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) last = (atomicAdd(&p.cnt[slab], 1u) == (uint32_t)(p.nsplit - 1));
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+    const float* all = p.stats + (size_t)slab * p.nsplit * p.rows_pad * 2;
+    for (int R = tid; R < p.rows; R += blockDim.x) {
+        float mm = -INFINITY, zz = 0.f;
+        for (int sp = 0; sp < p.nsplit; ++sp)
+            ms_merge(mm, zz, all[((size_t)sp * p.rows_pad + R) * 2],
+                     all[((size_t)sp * p.rows_pad + R) * 2 + 1]);
+        p.lse_ws[(size_t)slab * p.rows_pad + R] = mm + logf(zz);
+    }
+    if (tid == 0) p.cnt[slab] = 0u;
+}
+
+// Standalone value range: one workgroup of four waves per 512 rows of a
+// slab; wave w reduces channels 32w .. 32w+31, lanes own 8 rows each.
+template <typename E>
+__global__ __launch_bounds__(256) void value_range_kernel(const E* v, int hkv, int t_len,
+                                                          int t_cap, float* range) {
+    constexpr int VEC = 16 / sizeof(E);          // rows per 16-byte access
+    constexpr int ROWS = VEC * WAVE;             // rows per workgroup
+    const int slab = blockIdx.z * hkv + blockIdx.y;
+    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+    const int t0 = blockIdx.x * ROWS + lane * VEC;
+    const E* vs = v + (size_t)slab * D * t_cap;
+    __shared__ float smx[4][ROWS], smn[4][ROWS];
+    float mx[VEC], mn[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        mx[e] = -INFINITY;
+        mn[e] = INFINITY;
+    }
+    if (t0 < t_len) {
+        for (int d = 32 * wave; d < 32 * wave + 32; ++d) {
+            const u32x4 x = load16(vs + (size_t)d * t_cap + t0);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                float f;
+                if constexpr (sizeof(E) == 2) f = (e & 1) ? bf16hi(x[e / 2]) : bf16lo(x[e / 2]);
+                else f = __uint_as_float(x[e]);
+                mx[e] = fmaxf(mx[e], f);
+                mn[e] = fminf(mn[e], f);
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        smx[wave][lane * VEC + e] = mx[e];
+        smn[wave][lane * VEC + e] = mn[e];
+    }
+    __syncthreads();
+    for (int x = tid; x < ROWS; x += blockDim.x) {
+        const int t = blockIdx.x * ROWS + x;
+        if (t < t_len) {
+            const float a = fmaxf(fmaxf(smx[0][x], smx[1][x]), fmaxf(smx[2][x], smx[3][x]));
+            const float c = fminf(fminf(smn[0][x], smn[1][x]), fminf(smn[2][x], smn[3][x]));
+            range[(size_t)slab * t_len + t] = a - c;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_score(const ScoreLaunch& p, int dtype, hipStream_t st) {
+    const dim3 grid(p.nsplit, p.hkv, p.nb);
+    if (dtype == 0) {
+        if (!p.lse_obs) hipLaunchKernelGGL(score_f32, grid, dim3(256), 0, st, p, 1);
+        hipLaunchKernelGGL(score_f32, grid, dim3(256), 0, st, p, 0);
+    } else {
+        const int nw = (p.rows + 31) / 32;
+        if (!p.lse_obs) hipLaunchKernelGGL(score_stats_bf16, grid, dim3(nw * WAVE), 0, st, p);
+        hipLaunchKernelGGL(score_main_bf16, grid, dim3(nw * WAVE), 0, st, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_value_range(const void* v, int nb, int hkv, int t_len, int t_cap, int dtype,
+                              float* range, hipStream_t st) {
+    if (dtype == 0) {
+        const dim3 grid((t_len + 4 * WAVE - 1) / (4 * WAVE), hkv, nb);
+        hipLaunchKernelGGL(value_range_kernel<float>, grid, dim3(256), 0, st, (const float*)v, hkv,
+                           t_len, t_cap, range);
+    } else {
+        const dim3 grid((t_len + 8 * WAVE - 1) / (8 * WAVE), hkv, nb);
+        hipLaunchKernelGGL(value_range_kernel<uint16_t>, grid, dim3(256), 0, st,
+                           (const uint16_t*)v, hkv, t_len, t_cap, range);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kvc

@@ -1,0 +1,245 @@
+/*
+ * libkvc — decode attention over a compressed KV cache, for AMD MI355X
+ * (gfx950).  Plain C ABI: every argument is a host value, a host pointer or a
+ * device pointer; no C++ or framework types cross it.
+ *
+ * What the calls compute comes from three pages:
+ *   [RCLA]  "Stochastic KV Routing" (aitrends.kr article on R-CLA),
+ *           inference and implementation paragraphs: a fixed sharing set S of
+ *           leader layers; every other layer reuses the KV of the nearest
+ *           earlier leader, and only leaders store or update KV.
+ *   [VASE]  "VASE: value-aware stochastic KV-cache eviction"
+ *           (gist.science 2606.03928), §2 (periodic eviction with a
+ *           persistent budget K and a recent buffer B), §2.A
+ *           (Range(v) = max(v) - min(v); the N_v rows of largest range are
+ *           always kept), §2.B (weighted random sampling on SnapKV-style
+ *           observation-window attention scores), §1 (evicted pairs are
+ *           discarded for good, giving a static footprint).
+ *   Decode attention itself is standard softmax attention, one query row
+ *   per head, with grouped-query heads (GQA, named in the xKV summary,
+ *   gist.science 2503.18893, §4).
+ *
+ * Conventions shared by every call
+ *   - Status: every call returns KVC_OK (0) or a negative kvc_status.  All
+ *     arguments are validated on the host before anything is enqueued; on
+ *     an error nothing is enqueued and no output is touched.  KVC_EHIP
+ *     reports a launch failure seen right after enqueueing.
+ *   - Streams: device work is enqueued on `stream` (a hipStream_t; NULL is
+ *     the default stream) and runs asynchronously; the call returns before
+ *     it finishes.  Host outputs (kvc_share_map, *_ws_bytes) are ready on
+ *     return.
+ *   - Ownership: the caller allocates and owns all memory.  The library
+ *     allocates nothing and keeps no state between calls; calls are
+ *     reentrant.  Calls that share a workspace must be ordered on one stream.
+ *   - Alignment: cache, query and output pointers must be 16-byte aligned
+ *     (KVC_EALIGN otherwise).
+ *   - Sizes are element counts unless a name ends in _bytes.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t. */
+typedef struct ihipStream_t* kvc_stream_t;
+
+typedef enum kvc_status {
+    KVC_OK = 0,
+    KVC_EINVAL = -1,      /* a size, index or set is out of range          */
+    KVC_EDTYPE = -2,      /* unknown or mismatched element type            */
+    KVC_EALIGN = -3,      /* a pointer is NULL or not 16-byte aligned      */
+    KVC_EWORKSPACE = -4,  /* workspace missing or smaller than required    */
+    KVC_EALIAS = -5,      /* source and destination memory overlap         */
+    KVC_EHIP = -6         /* the HIP runtime reported a launch error       */
+} kvc_status;
+
+typedef enum kvc_dtype {
+    KVC_F32 = 0,          /* IEEE float32                                  */
+    KVC_BF16 = 1          /* bfloat16 (upper half of a float32)            */
+} kvc_dtype;
+
+/* Head dimension the kernels are built for. */
+#define KVC_HEAD_DIM 128
+/* t_cap must be a multiple of this (keeps every vector access in bounds). */
+#define KVC_T_ALIGN 64
+
+/*
+ * A KV cache of n_slots leader slots (one per layer in S), batch nb,
+ * n_kv_heads heads and head_dim = 128.  One slab = one (slot, b, kv head).
+ *   k: [n_slots][nb][n_kv_heads][t_cap][head_dim]   row-major rows
+ *   v: [n_slots][nb][n_kv_heads][head_dim][t_cap]   token-minor: the value
+ *      rows of a slab are stored transposed, so that the t-contiguous
+ *      operand of the P*V product loads with one 16-byte access per lane.
+ * Rows [0, t_len) are valid in every slot; t_len is shared by all slots.
+ * dtype is a kvc_dtype; both k and v hold that type.
+ */
+typedef struct kvc_cache {
+    void* k;
+    void* v;
+    int32_t dtype;
+    int32_t n_slots;
+    int32_t nb;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t t_len;
+    int32_t t_cap;
+} kvc_cache;
+
+/* Library version as major*10000 + minor*100 + patch. */
+int kvc_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* kvc_strerror(int status);
+
+/*
+ * Sharing map [RCLA, inference paragraph].  Host only, synchronous.
+ *   leaders[n_leaders]: the sorted set S; must start at layer 0, be strictly
+ *   increasing and lie in [0, n_layers).
+ *   src_layer[n_layers] (out): max{s in S : s <= l}.
+ *   src_slot[n_layers]  (out): index of src_layer[l] in S (the cache slot).
+ * KVC_EINVAL for a bad set, KVC_EALIGN for a NULL pointer.
+ */
+int kvc_share_map(int n_layers, const int32_t* leaders, int n_leaders,
+                  int32_t* src_layer, int32_t* src_slot);
+
+/*
+ * Leader append [RCLA, implementation paragraph]: write one new row per
+ * (b, kv head) at row t_len - 1 of `slot` (the caller has already counted
+ * the row in c->t_len).  k_new, v_new: device [nb][n_kv_heads][head_dim],
+ * same dtype as the cache.  Followers never call this.
+ */
+int kvc_append(const kvc_cache* c, int slot, const void* k_new,
+               const void* v_new, kvc_stream_t stream);
+
+/* Workspace bytes kvc_decode_attn needs for caches of this shape, for any
+ * t_len <= c->t_cap and any n_q_layers up to the given count. */
+int kvc_decode_attn_ws_bytes(const kvc_cache* c, int n_q_layers,
+                             int n_q_heads, size_t* bytes);
+
+/*
+ * Grouped-query decode attention over leader KV [RCLA; standard softmax].
+ * For q-layer i, batch b, query head h, with g = n_q_heads / n_kv_heads and
+ * kv head j = h / g (contiguous groups):
+ *     out[i][b][h] = softmax_t(scale * q[i][b][h] . K[s][b][j][t]) V[s][b][j][t]
+ *     lse[i][b][h] = log sum_t exp(scale * q[i][b][h] . K[s][b][j][t])
+ * over t in [0, c->t_len), where s = q_slot[i] (a host array; normally the
+ * src_slot of the layer).  Several q-layers that read one slot are served by
+ * one pass over that slot's KV (all followers of a leader in one call), or
+ * the caller makes one call per layer.
+ *   q:   device [n_q_layers][nb][n_q_heads][head_dim], cache dtype; q-layer
+ *        i starts q_layer_stride elements after q-layer i-1 (0 = packed).
+ *   scale: 0 means 1/sqrt(head_dim).
+ *   append_slot >= 0: row t_len-1 of that slot is taken from k_new/v_new
+ *        (device [nb][n_kv_heads][head_dim]) and also written into the
+ *        cache, as kvc_append does; -1: no append, k_new/v_new ignored.
+ *   out: device float32 [n_q_layers][nb][n_q_heads][head_dim], layer stride
+ *        out_layer_stride (0 = packed).
+ *   lse: device float32 [n_q_layers][nb][n_q_heads] or NULL, layer stride
+ *        lse_layer_stride (0 = packed).
+ *   ws:  device workspace of at least kvc_decode_attn_ws_bytes bytes, zero
+ *        filled before its first use; every call leaves it ready for the
+ *        next (its counters return to zero).
+ * Requires t_len >= 1, n_q_heads a multiple of n_kv_heads, head_dim 128.
+ */
+int kvc_decode_attn(const kvc_cache* c, const void* q, int64_t q_layer_stride,
+                    int n_q_layers, const int32_t* q_slot, int n_q_heads,
+                    float scale, const void* k_new, const void* v_new,
+                    int append_slot, float* out, int64_t out_layer_stride,
+                    float* lse, int64_t lse_layer_stride, void* ws,
+                    size_t ws_bytes, kvc_stream_t stream);
+
+/*
+ * Value range [VASE §2.A]: range[b][j][t] = max_c V[slot][b][j][t][c]
+ *                                         - min_c V[slot][b][j][t][c]
+ * over the head_dim channels of each value row, t in [0, t_len), computed
+ * in float32 (exact rounding of the true difference).
+ *   range: device float32 [nb][n_kv_heads][t_len].
+ */
+int kvc_value_range(const kvc_cache* c, int slot, float* range,
+                    kvc_stream_t stream);
+
+/* Workspace bytes kvc_score needs without lse_obs (two passes). */
+int kvc_score_ws_bytes(const kvc_cache* c, int n_q_heads, int w,
+                       size_t* bytes);
+
+/*
+ * Observation-window score [VASE §2.B, SnapKV-derived], one pass over the
+ * slot's KV.  For slab (b, j) the rows are (h in the group of j, i < w) with
+ * queries q_obs[i][b][h]; window row i sees cache rows t <= t_len - w + i
+ * (it was issued when the cache held t_len - w + i + 1 rows).
+ *     score[b][j][t] = sum_{h,i} softmax_t(scale * q_obs[i][b][h] . K[t])
+ *   q_obs:   device [w][nb][n_q_heads][head_dim], cache dtype, oldest first.
+ *   lse_obs: device float32 [w][nb][n_q_heads] holding the log-normaliser of
+ *            each window row over its visible rows (as kvc_decode_attn
+ *            returned it when the query was decoded, valid when no
+ *            compaction happened inside the window), or NULL: then a first
+ *            pass computes it and ws is required.
+ *   score:   device float32 [nb][n_kv_heads][t_len].
+ *   range:   NULL or device float32 [nb][n_kv_heads][t_len]: the value range
+ *            of kvc_value_range, fused into the same pass over the cache.
+ * Requires 1 <= w <= t_len and g*w <= 512.
+ */
+int kvc_score(const kvc_cache* c, int slot, const void* q_obs, int n_q_heads,
+              int w, float scale, const float* lse_obs, float* score,
+              float* range, void* ws, size_t ws_bytes, kvc_stream_t stream);
+
+/* Workspace bytes kvc_select needs for nb * n_kv_heads slabs of t_len rows. */
+int kvc_select_ws_bytes(int nb, int n_kv_heads, int t_len, size_t* bytes);
+
+/*
+ * VASE selection [VASE §2, §2.A, §2.B], per slab (b, j):
+ *   if t_len <= K + B every row is kept; otherwise
+ *   1. the last B rows [t_len - B, t_len) are kept;
+ *   2. among candidate rows [0, t_len - B) the N_v of largest range are
+ *      kept (ties to the lower row);
+ *   3. K - N_v more candidates are sampled without replacement with
+ *      probability proportional to score: row t gets the key
+ *      kappa_t = E_t / score_t (infinite when score_t <= 0), where
+ *      E_t = -ln((x_t + 1) / 2^32) and x_t is word 0 of Philox4x32-10 at
+ *      counter (t, j, layer_id, b) and key (seed mod 2^32, seed >> 32); the
+ *      K - N_v smallest keys are kept (ties to the lower row).
+ *   score, range: device float32 [nb][n_kv_heads][t_len].
+ *   kept (out):   device int32 [nb][n_kv_heads][n_keep], ascending, with
+ *                 n_keep = min(t_len, K + B).
+ *   ws: device workspace of kvc_select_ws_bytes bytes (no zeroing needed).
+ * Requires 0 <= N_v <= K, B >= 0, K + B >= 1.  The result is a pure
+ * function of its inputs; a driver that evicts repeatedly passes a new seed
+ * each pass.
+ */
+int kvc_select(const float* score, const float* range, int nb, int n_kv_heads,
+               int t_len, int budget_k, int recent_b, int n_v, uint64_t seed,
+               int layer_id, int32_t* kept, void* ws, size_t ws_bytes,
+               kvc_stream_t stream);
+
+/*
+ * Compaction [VASE §1: evicted pairs are dropped for good].  For every slab
+ * of `slot`: dst row i <- src row kept[b][j][i], i < n_keep, for K and V,
+ * written into the same slot of dst.  Out of place: the slot's K and V
+ * regions of src and dst must not overlap (KVC_EALIAS).  dst must have the
+ * same dtype, nb, n_kv_heads and head_dim, and dst->t_cap >= n_keep; the
+ * caller sets dst->t_len = n_keep afterwards.  kept: device int32
+ * [nb][n_kv_heads][n_keep] with entries in [0, src->t_len); a row whose
+ * index is out of that range is written as zeros.
+ */
+int kvc_compact(const kvc_cache* src, int slot, const int32_t* kept,
+                int n_keep, const kvc_cache* dst, kvc_stream_t stream);
+
+/*
+ * Diagnostic: the device Philox4x32-10 stream that kvc_select draws from.
+ * out[i][0..3] = Philox4x32-10(counter (i, c1, c2, c3),
+ *                              key (seed mod 2^32, seed >> 32)), i < n.
+ *   out: device uint32 [n][4].
+ */
+int kvc_philox_words(int64_t n, uint32_t c1, uint32_t c2, uint32_t c3,
+                     uint64_t seed, uint32_t* out, kvc_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

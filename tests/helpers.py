@@ -1,0 +1,56 @@
+"""Shared plumbing for the GPU parity tests (no method arithmetic here)."""
+import numpy as np
+import torch
+
+import kvc_synth
+import decode_attention_kvc_amd as kvc
+
+
+def make_cache(n_slots, nb, hkv, T, t_cap=None, dtype=torch.bfloat16, seed=0, device="cuda",
+               outlier_frac=0.01):
+    """A cache with T rows of synthetic K/V in every slot (garbage beyond T)."""
+    t_cap = t_cap or T + 64
+    c = kvc.Cache.empty(n_slots, nb, hkv, t_cap, dtype=dtype, device=device)
+    # fill the unused capacity with NaN bit patterns to catch reads past t_len
+    c.k.view(torch.int16).fill_(-1)
+    c.v.view(torch.int16).fill_(-1)
+    for s in range(n_slots):
+        K, V, _, _ = kvc_synth.kv_slot(nb, hkv, T, dtype=dtype, device=device, seed=seed * 1000 + s,
+                                       outlier_frac=outlier_frac)
+        c.fill(s, K, V)
+    return c
+
+
+def slab_np(cache, slot):
+    """Logical float64 K, V of a slot: [nb][hkv][T][d] each."""
+    K = cache.k_rows(slot).double().cpu().numpy()
+    V = cache.v_rows(slot).double().cpu().numpy()
+    return K, V
+
+
+def ws_tensor(nbytes, device="cuda"):
+    return torch.zeros(max(16, (nbytes + 15) // 16 * 16), dtype=torch.uint8, device=device)
+
+
+def to_np(t):
+    return t.detach().double().cpu().numpy()
+
+
+def band_compare(gpu_kept, detail, rel=1e-6):
+    """Compare a GPU kept set with the oracle's selection of one slab.
+
+    Returns (n_ties, n_bad): rows kept by exactly one side that are (are not)
+    within `rel` of the oracle's sampling cutoff (or of the range cutoff for
+    protected rows)."""
+    g = set(int(x) for x in gpu_kept)
+    o = set(int(x) for x in detail["kept"])
+    diff = g ^ o
+    ties = bad = 0
+    kc = detail["kappa_cut"]
+    for t in diff:
+        kap = detail["kappa"][t]
+        if kc is not None and np.isfinite(kap) and abs(kap - kc) <= rel * kc:
+            ties += 1
+        else:
+            bad += 1
+    return ties, bad

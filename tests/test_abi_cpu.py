@@ -1,0 +1,223 @@
+"""C-ABI checks that need no GPU: exports, host-only share map, validation.
+
+Every error path exercised here returns before the library enqueues any
+device work, so fake (but aligned) device addresses are safe."""
+import ctypes
+import itertools
+import os
+import re
+
+import pytest
+
+import oracle
+import decode_attention_kvc_amd as kvc
+from decode_attention_kvc_amd._lib import kvc_cache
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "kvc.h")
+L = kvc.lib()
+FAKE = 0x7F0000000000          # 16-byte aligned, never dereferenced
+FAKE2 = 0x7F8000000000
+
+
+def header_exports():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(kvc_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = header_exports()
+    assert len(names) >= 13
+    assert sorted(names) == sorted(kvc.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_strerror():
+    assert kvc.kvc_version() == 10000
+    for code in range(0, -7, -1):
+        assert kvc.kvc_strerror(code)
+    assert kvc.kvc_strerror(-99) == "unknown status"
+
+
+def test_share_map_matches_oracle_exhaustively():
+    for n in range(1, 9):
+        for r in range(0, n):
+            for rest in itertools.combinations(range(1, n), r):
+                S = [0, *rest]
+                src, slot = kvc.kvc_share_map(n, S)
+                osrc, oslot = oracle.share_map(n, S)
+                assert src == osrc.tolist() and slot == oslot.tolist()
+
+
+@pytest.mark.parametrize("bad", [[1], [0, 0], [0, 5, 3], [0, 8], [2, 4]])
+def test_share_map_rejects_bad_sets(bad):
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kvc_share_map(8, bad)
+    assert e.value.status == kvc.KVC_EINVAL
+
+
+def test_share_map_page_configs():
+    # 9 of 36, every 4th of 32, every 2nd of 40, all 36
+    for L_, S in [(36, range(0, 36, 4)), (32, range(0, 32, 4)), (40, range(0, 40, 2)),
+                  (36, range(36))]:
+        src, slot = kvc.kvc_share_map(L_, list(S))
+        assert max(slot) + 1 == len(list(S))
+
+
+def cache(**kw):
+    c = dict(k=FAKE, v=FAKE2, dtype=1, n_slots=2, nb=1, n_kv_heads=2, head_dim=128,
+             t_len=100, t_cap=128)
+    c.update(kw)
+    return kvc_cache(c["k"], c["v"], c["dtype"], c["n_slots"], c["nb"], c["n_kv_heads"],
+                     c["head_dim"], c["t_len"], c["t_cap"])
+
+
+def attn(c, **kw):
+    a = dict(q=FAKE, qs=0, nq=1, slots=[0], hq=8, scale=0.0, kn=None, vn=None, app=-1,
+             out=FAKE, os=0, lse=None, ls=0, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    arr = (ctypes.c_int32 * max(1, len(a["slots"])))(*a["slots"])
+    return L.kvc_decode_attn(ctypes.byref(c), a["q"], a["qs"], a["nq"], arr, a["hq"], a["scale"],
+                             a["kn"], a["vn"], a["app"], a["out"], a["os"], a["lse"], a["ls"],
+                             a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), kvc.KVC_EDTYPE),
+    (dict(head_dim=64), kvc.KVC_EINVAL),
+    (dict(t_len=200), kvc.KVC_EINVAL),
+    (dict(t_cap=100, t_len=10), kvc.KVC_EINVAL),
+    (dict(k=FAKE + 8), kvc.KVC_EALIGN),
+    (dict(v=0), kvc.KVC_EALIGN),
+    (dict(n_slots=0), kvc.KVC_EINVAL),
+    (dict(t_len=0), kvc.KVC_EINVAL),
+])
+def test_decode_attn_rejects_bad_cache(kw, code):
+    assert attn(cache(**kw)) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hq=7), kvc.KVC_EINVAL),                       # Hq % Hkv != 0
+    (dict(hq=2 * 65), kvc.KVC_EINVAL),                  # group larger than 64
+    (dict(slots=[2]), kvc.KVC_EINVAL),                  # q-slot out of range
+    (dict(slots=[-1]), kvc.KVC_EINVAL),
+    (dict(app=2), kvc.KVC_EINVAL),                      # append slot out of range
+    (dict(app=0), kvc.KVC_EALIGN),                      # append without k_new/v_new
+    (dict(q=FAKE + 2), kvc.KVC_EALIGN),
+    (dict(out=0), kvc.KVC_EALIGN),
+    (dict(qs=5), kvc.KVC_EINVAL),                       # stride below packed size
+    (dict(qs=8 * 128 + 3), kvc.KVC_EALIGN),             # stride breaks 16-byte loads
+    (dict(ws=0), kvc.KVC_EWORKSPACE),
+    (dict(wsb=16), kvc.KVC_EWORKSPACE),
+    (dict(scale=-1.0), kvc.KVC_EINVAL),
+    (dict(scale=float("nan")), kvc.KVC_EINVAL),
+    (dict(nq=-1), kvc.KVC_EINVAL),
+])
+def test_decode_attn_rejects_bad_args(kw, code):
+    assert attn(cache(), **kw) == code
+
+
+def test_decode_attn_empty_inputs_are_noops():
+    assert attn(cache(), nq=0, slots=[]) == kvc.KVC_OK
+    assert attn(cache(nb=0)) == kvc.KVC_OK
+
+
+def test_ws_bytes_queries():
+    c = cache(t_len=0, t_cap=4096)
+    n = ctypes.c_size_t()
+    assert L.kvc_decode_attn_ws_bytes(ctypes.byref(c), 4, 8, ctypes.byref(n)) == 0
+    assert n.value > 0
+    assert L.kvc_decode_attn_ws_bytes(ctypes.byref(c), 1, 7, ctypes.byref(n)) == kvc.KVC_EINVAL
+    assert L.kvc_score_ws_bytes(ctypes.byref(c), 8, 32, ctypes.byref(n)) == 0 and n.value > 0
+    assert L.kvc_select_ws_bytes(2, 8, 1000, ctypes.byref(n)) == 0 and n.value == 2 * 8 * 1000 * 4
+    assert L.kvc_select_ws_bytes(2, 0, 1000, ctypes.byref(n)) == kvc.KVC_EINVAL
+
+
+def score(c, **kw):
+    a = dict(slot=0, q=FAKE, hq=8, w=32, scale=0.0, lse=None, sc=FAKE, rg=None, ws=None, wsb=0)
+    a.update(kw)
+    return L.kvc_score(ctypes.byref(c), a["slot"], a["q"], a["hq"], a["w"], a["scale"], a["lse"],
+                       a["sc"], a["rg"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(slot=2), kvc.KVC_EINVAL),
+    (dict(w=101), kvc.KVC_EINVAL),                      # window longer than the cache
+    (dict(w=0), kvc.KVC_EINVAL),
+    (dict(hq=2 * 17, w=32), kvc.KVC_EINVAL),            # g*w > 512
+    (dict(hq=9), kvc.KVC_EINVAL),
+    (dict(q=FAKE + 4), kvc.KVC_EALIGN),
+    (dict(sc=0), kvc.KVC_EALIGN),
+    (dict(), kvc.KVC_EWORKSPACE),                       # two-pass needs a workspace
+])
+def test_score_rejects_bad_args(kw, code):
+    assert score(cache(), **kw) == code
+
+
+def test_score_f32_row_cap():
+    assert score(cache(dtype=0), hq=2 * 5, w=32) == kvc.KVC_EINVAL   # 5*32 > 128 on f32
+
+
+def select(**kw):
+    a = dict(sc=FAKE, rg=FAKE2, nb=1, h=2, T=300, K=100, B=10, nv=5, seed=0, layer=0,
+             kept=FAKE, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return L.kvc_select(a["sc"], a["rg"], a["nb"], a["h"], a["T"], a["K"], a["B"], a["nv"],
+                        a["seed"], a["layer"], a["kept"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(nv=101), kvc.KVC_EINVAL),
+    (dict(nv=-1), kvc.KVC_EINVAL),
+    (dict(B=-1), kvc.KVC_EINVAL),
+    (dict(K=0, B=0, nv=0), kvc.KVC_EINVAL),
+    (dict(h=0), kvc.KVC_EINVAL),
+    (dict(layer=-3), kvc.KVC_EINVAL),
+    (dict(wsb=100), kvc.KVC_EWORKSPACE),
+    (dict(ws=None), kvc.KVC_EWORKSPACE),
+    (dict(kept=FAKE + 2), kvc.KVC_EALIGN),
+    (dict(rg=None), kvc.KVC_EALIGN),
+])
+def test_select_rejects_bad_args(kw, code):
+    assert select(**kw) == code
+
+
+def test_select_empty_is_noop():
+    assert select(T=0) == kvc.KVC_OK
+    assert select(nb=0) == kvc.KVC_OK
+
+
+def compact(src, dst, **kw):
+    a = dict(slot=0, kept=FAKE, n=50)
+    a.update(kw)
+    return L.kvc_compact(ctypes.byref(src), a["slot"], a["kept"], a["n"], ctypes.byref(dst), None)
+
+
+def test_compact_validation():
+    src = cache(k=0x10000000, v=0x20000000)
+    dst = cache(k=0x30000000, v=0x40000000)
+    assert compact(src, cache(k=0x10000000 + 64, v=0x40000000)) == kvc.KVC_EALIAS
+    assert compact(src, cache(k=0x30000000, v=0x20000000)) == kvc.KVC_EALIAS
+    assert compact(src, cache(k=0x30000000, v=0x30000000)) == kvc.KVC_EALIAS
+    assert compact(src, cache(k=0x30000000, v=0x40000000, dtype=0)) == kvc.KVC_EDTYPE
+    assert compact(src, cache(k=0x30000000, v=0x40000000, nb=2)) == kvc.KVC_EINVAL
+    assert compact(src, dst, n=101) == kvc.KVC_EINVAL      # more than src t_len
+    assert compact(src, cache(k=0x30000000, v=0x40000000, t_cap=64, t_len=0), n=65) == kvc.KVC_EINVAL
+    assert compact(src, dst, slot=2) == kvc.KVC_EINVAL
+    assert compact(src, dst, kept=FAKE + 1) == kvc.KVC_EALIGN
+    assert compact(src, dst, n=0) == kvc.KVC_OK
+
+
+def test_append_and_range_and_philox_validation():
+    c = cache()
+    assert L.kvc_append(ctypes.byref(c), 2, FAKE, FAKE, None) == kvc.KVC_EINVAL
+    assert L.kvc_append(ctypes.byref(c), 0, None, FAKE, None) == kvc.KVC_EALIGN
+    assert L.kvc_append(ctypes.byref(cache(t_len=0)), 0, FAKE, FAKE, None) == kvc.KVC_EINVAL
+    assert L.kvc_value_range(ctypes.byref(c), -1, FAKE, None) == kvc.KVC_EINVAL
+    assert L.kvc_value_range(ctypes.byref(c), 0, FAKE + 1, None) == kvc.KVC_EALIGN
+    assert L.kvc_value_range(ctypes.byref(cache(t_len=0)), 0, FAKE, None) == kvc.KVC_OK
+    assert L.kvc_philox_words(-1, 0, 0, 0, 0, FAKE, None) == kvc.KVC_EINVAL
+    assert L.kvc_philox_words(4, 0, 0, 0, 0, FAKE + 4, None) == kvc.KVC_EALIGN
+    assert L.kvc_philox_words(0, 0, 0, 0, 0, FAKE, None) == kvc.KVC_OK
+    assert L.kvc_decode_attn(None, FAKE, 0, 1, (ctypes.c_int32 * 1)(0), 8, 0.0, None, None, -1,
+                             FAKE, 0, None, 0, FAKE, 1 << 30, None) == kvc.KVC_EALIGN
