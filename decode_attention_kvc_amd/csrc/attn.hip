@@ -195,7 +195,8 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnLaunch p) {
     const float scale = p.scale;
 
     auto compute = [&](TileRegs& R, int t0) {
-        const bool tail = (t0 + ATTN_TILE > T);
+        // The last tile of the slab (it holds row T-1, the appended row).
+        const bool tail = (t0 + ATTN_TILE >= T);
         if (tail) {
             // Rows past the end hold arbitrary bits: zero their V entries
             // (P is zero there too, but 0 * NaN would poison the sum) and
@@ -432,7 +433,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnLaunch p) {
                 const f32x4 v4 = *reinterpret_cast<const f32x4*>(vr + x);
                 vv[x] = v4[0]; vv[x + 1] = v4[1]; vv[x + 2] = v4[2]; vv[x + 3] = v4[3];
             }
-            if (t0 + TT > T) {
+            if (t0 + TT >= T) {   // last tile: rows past the end, appended row
 #pragma unroll
                 for (int x = 0; x < TT; ++x) {
                     if (t0 + x == append_row) vv[x] = vnew[d];

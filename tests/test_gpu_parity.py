@@ -93,10 +93,11 @@ def test_decode_attn_f32_tiny(T):
     assert np.abs(to_np(lse) - ref_lse).max() <= 1e-5 * max(1.0, np.abs(ref_lse).max())
 
 
+@pytest.mark.parametrize("T0", [95, 96, 127])      # appended row ends / starts / fills a tile
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_decode_attn_append(dtype):
-    say("decode append", dtype)
-    nb, hkv, hq, T0 = 2, 8 if dtype == torch.bfloat16 else 2, 32 if dtype == torch.bfloat16 else 8, 95
+def test_decode_attn_append(dtype, T0):
+    say("decode append", dtype, T0)
+    nb, hkv, hq = 2, 8 if dtype == torch.bfloat16 else 2, 32 if dtype == torch.bfloat16 else 8
     cache = make_cache(2, nb, hkv, T0, t_cap=192, dtype=dtype, seed=3)
     kn = kvc_synth.queries((nb, hkv, 128), dtype=dtype, device=DEV, seed=11)
     vn = kvc_synth.queries((nb, hkv, 128), dtype=dtype, device=DEV, seed=12) * 3
