@@ -1,0 +1,330 @@
+"""Decode throughput of attention + eviction over a compressed KV cache, 1 GPU.
+
+Workload (default): Llama-3.1-8B-shaped combined decode — 32 layers, one KV
+leader every 4th layer (8 slots), batch 16, 32 query / 8 KV heads, head dim
+128, bfloat16, 32K-token prompt cache compressed once to K + B = 8320 rows,
+then decode steps with a VASE eviction pass (K 8192, B 128, N_v 128, window
+32, every 128 steps) on the leaders.  A step = every layer's attention (with
+the leaders' fused append) + its share of the periodic eviction.  Inputs are
+synthetic (seeded normal draws with 1% x20 value outliers) and resident in
+HBM before timing starts.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--mode per-layer|grouped]
+
+Prints one JSON line.  Only the cpu_baseline leg touches oracle/.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "decode tokens/s and achieved HBM GB/s (% of peak), attn+eviction, 1 GPU"
+
+WORKLOADS = {
+    "llama3.1-8b-combined": dict(
+        desc="Llama-3.1-8B-shaped combined R-CLA sharing + VASE eviction decode",
+        n_layers=32, leaders=list(range(0, 32, 4)), nb=16, hq=32, hkv=8, t0=32768,
+        evict=dict(K=8192, B=128, N_v=128, w=32, period=128, seed=0)),
+    "qwen3-8b-rcla": dict(
+        desc="Qwen3-8B-shaped R-CLA decode, 9 of 36 layers lead, no eviction",
+        n_layers=36, leaders=list(range(0, 36, 4)), nb=1, hq=32, hkv=8, t0=32768, evict=None),
+    "qwen3-14b-long": dict(
+        desc="Qwen3-14B-shaped long-context decode: sharing every 2 layers, 128K prompt, VASE",
+        n_layers=40, leaders=list(range(0, 40, 2)), nb=4, hq=40, hkv=8, t0=131072,
+        evict=dict(K=32768, B=256, N_v=256, w=32, period=256, seed=0)),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attn_bytes(nb, hq, hkv, t_len, n_q_layers, lead):
+    """Algorithmic HBM bytes of one attention launch (bf16 cache): every K and
+    V row of the slab once, queries in, float32 outputs and lse out, and the
+    appended row written by leaders."""
+    kv = 2 * nb * hkv * t_len * 128 * 2
+    q = n_q_layers * nb * hq * 128 * 2
+    out = n_q_layers * nb * hq * (128 + 1) * 4
+    app = 2 * nb * hkv * 128 * 2 if lead else 0
+    return kv + q + out + app
+
+
+def evict_bytes(cfg, t_len):
+    """Algorithmic bytes of one eviction pass: K + V read once by the fused
+    score/range pass, score/range written and read, kept rows gathered (read)
+    and written."""
+    e = cfg["evict"]
+    slabs = cfg["nb"] * cfg["hkv"] * len(cfg["leaders"])
+    keep = e["K"] + e["B"]
+    return slabs * (2 * t_len * 256 + 2 * 4 * t_len * 2 + 4 * keep + 2 * 2 * keep * 256)
+
+
+def cpu_baseline(cfg, cache, qpool, s, budget_s=8.0):
+    """Time the float64 oracle on a bounded sample of the same workload."""
+    import numpy as np
+    import torch
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        blas = 1
+    nb, hq, hkv = cfg["nb"], cfg["hq"], cfg["hkv"]
+    g = hq // hkv
+    T = cache.t_len
+    # decode: slabs of layer 0 (slot 0), converted bf16 -> float64 per slab
+    Kc = cache.k_rows(0).cpu()
+    Vc = cache.v_rows(0).cpu()
+    qh = qpool[0, s].cpu()
+    t0 = time.perf_counter()
+    n_dec = 0
+    while time.perf_counter() - t0 < budget_s and n_dec < nb * hkv:
+        b, j = divmod(n_dec, hkv)
+        K = Kc[b, j].double().numpy()
+        V = Vc[b, j].double().numpy()
+        oracle.attention(qh[b, j * g:(j + 1) * g].double().numpy(), K, V)
+        n_dec += 1
+    t_dec = (time.perf_counter() - t0) / n_dec
+    t_step = t_dec * cfg["n_layers"] * nb * hkv
+    t_ev_total = 0.0
+    n_ev = 0
+    e = cfg["evict"]
+    if e:
+        w = e["w"]
+        qo = qpool[0, s - w + 1:s + 1].cpu()
+        t1 = time.perf_counter()
+        while time.perf_counter() - t1 < budget_s and n_ev < nb * hkv:
+            b, j = divmod(n_ev, hkv)
+            K = Kc[b, j].double().numpy()
+            V = Vc[b, j].double().numpy()
+            sc = oracle.window_score(qo[:, b, j * g:(j + 1) * g].double().numpy(), K, T)
+            vr = oracle.value_range(V)
+            kept = oracle.select(sc, vr, T, e["K"], e["B"], e["N_v"], 1, 0, b, j)
+            oracle.compact(K, V, kept)
+            n_ev += 1
+        t_ev = (time.perf_counter() - t1) / n_ev
+        t_ev_total = t_ev * nb * hkv * len(cfg["leaders"])
+    per_step = t_step + (t_ev_total / e["period"] if e else 0.0)
+    sample = (f"{n_dec} of {nb * hkv} slabs of one layer's decode attention at T={T}"
+              + (f" and {n_ev} slabs of one eviction pass (score+range+select+compact)"
+                 if e else "")
+              + f", extrapolated linearly to a full step of {cfg['n_layers']} layers"
+              + (f" plus 1/{e['period']} of a pass over {len(cfg['leaders'])} leader slots"
+                 if e else "")
+              + "; numpy float64, bf16 converted per slab")
+    return dict(value=round(nb / per_step, 4), unit="tokens/s", cores=int(blas), kind="oracle",
+                sample=sample, extrapolated=True,
+                cpu_model=_cpu_model(), host_cores=len(os.sched_getaffinity(0)))
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3.1-8b-combined", choices=list(WORKLOADS))
+    ap.add_argument("--mode", default="per-layer", choices=["per-layer", "grouped"])
+    ap.add_argument("--no-grouped", action="store_true", help="skip the grouped-mode leg")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one plain 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} "
+              "requested). The head/batch sharding it would use is described in DESIGN.md.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kvc_synth
+    import decode_attention_kvc_amd as kvc
+    from decode_attention_kvc_amd.loop import Decoder
+
+    cfg = WORKLOADS[args.workload]
+    dev = "cuda"
+    torch.cuda.init()
+    L, leaders, nb, hq, hkv, t0 = (cfg[k] for k in ("n_layers", "leaders", "nb", "hq", "hkv", "t0"))
+    ev = cfg["evict"]
+    n_slots = len(leaders)
+    W, S = args.warmup, args.steps
+    n_total = W + 2 * S + 2
+    if ev:
+        steady_cap = ev["K"] + ev["B"] + ev["period"]
+    else:
+        steady_cap = t0 + n_total
+    log(f"[bench] {args.workload}: setting up (prompt cache {t0} rows x {n_slots} slots)")
+
+    # ---- inputs (untimed): prompt cache, query / append pools
+    big = kvc.Cache.empty(n_slots, nb, hkv, t0 + (0 if ev else n_total), device=dev)
+    prev = None
+    for s_ in range(n_slots):
+        Kr, Vr, K32, V32 = kvc_synth.kv_slot(nb, hkv, t0, device=dev, seed=100 + s_,
+                                             prev=prev, rho=0.9 if not ev else None,
+                                             gap=leaders[1] - leaders[0] if n_slots > 1 else 1)
+        big.fill(s_, Kr, Vr)
+        prev = (K32, V32) if not ev else None
+        del Kr, Vr
+    del prev
+    qpool = kvc_synth.queries((L, n_total, nb, hq, 128), device=dev, seed=1)
+    lsepool = torch.zeros((L, n_total, nb, hq), device=dev)
+    knew = kvc_synth.queries((n_total, n_slots, nb, hkv, 128), device=dev, seed=2)
+    vnew = kvc_synth.queries((n_total, n_slots, nb, hkv, 128), device=dev, seed=3)
+    out = torch.empty((L, nb, hq, 128), device=dev)
+    torch.cuda.synchronize()
+
+    initial_ms = None
+    if ev:
+        cache = kvc.Cache.empty(n_slots, nb, hkv, steady_cap, device=dev)
+        spare = kvc.Cache.empty(n_slots, nb, hkv, steady_cap, device=dev)
+        dec = Decoder(L, leaders, big, cache, hq, evict=ev, mode=args.mode)
+        q_init = [kvc_synth.queries((ev["w"], nb, hq, 128), device=dev, seed=50 + i)
+                  for i in range(n_slots)]
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        dec.initial_pass(q_init)
+        b.record()
+        torch.cuda.synchronize()
+        initial_ms = a.elapsed_time(b)
+        log(f"[bench] initial compression {t0} -> {dec.cache.t_len} rows: {initial_ms:.2f} ms")
+        dec.spare = spare
+        del big, q_init
+        torch.cuda.empty_cache()
+    else:
+        dec = Decoder(L, leaders, big, None, hq, evict=None, mode=args.mode)
+
+    def run(steps, first, mode, events):
+        dec.mode = mode
+        if mode == "grouped":
+            dec.ws_attn = torch.zeros(max(16, kvc.kvc_decode_attn_ws_bytes(
+                dec.cache, max(len(g) for g in dec.groups), hq)), dtype=torch.uint8, device=dev)
+        dec.events = [] if events else None
+        n_ev = 0
+        for s in range(first, first + steps):
+            n_ev += bool(dec.step(s, qpool, lsepool, knew, vnew, out))
+        return n_ev
+
+    # ---- warm-up, then the timed steps
+    run(W, 0, args.mode, False)
+    torch.cuda.synchronize()
+    log(f"[bench] warm-up done ({W} steps), timing {S} steps ({args.mode})")
+    t_start = time.perf_counter()
+    n_evict = run(S, W, args.mode, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = 1e3 * wall / S
+    events = dec.events
+    att_ms = [a.elapsed_time(b) for a, b, _, _ in events]
+    # leaders' launches carry the appended row; followers' do not
+    if args.mode == "per-layer":
+        att_bytes = [attn_bytes(nb, hq, hkv, t, 1, (i % L) in leaders)
+                     for i, (_, _, t, _) in enumerate(events)]
+    else:
+        att_bytes = [attn_bytes(nb, hq, hkv, t, nql, True) for (_, _, t, nql) in events]
+    att_total_ms = sum(att_ms)
+    att_gbps = sum(att_bytes) / (att_total_ms * 1e-3) / 1e9
+    avg_launch_us = 1e3 * att_total_ms / len(att_ms)
+    tok_s = nb * S / wall
+    log(f"[bench] {S} steps in {wall:.3f} s: {tok_s:.1f} tok/s, attention {att_gbps:.0f} GB/s "
+        f"({100 * att_gbps / HBM_PEAK_GBPS:.1f}% of peak), avg launch {avg_launch_us:.1f} us, "
+        f"{n_evict} eviction passes")
+    # whole-step algorithmic bytes (attention + eviction) over the wall time
+    t_mean = sum(t for _, _, t, _ in events) / len(events)
+    step_bytes = sum(att_bytes) + (n_evict * evict_bytes(cfg, ev["K"] + ev["B"] + ev["period"])
+                                   if ev else 0)
+    step_gbps = step_bytes / wall / 1e9
+
+    grouped = None
+    if not args.no_grouped and args.mode == "per-layer" and n_slots < L:
+        first = W + S
+        torch.cuda.synchronize()
+        g0 = time.perf_counter()
+        g_ev = run(S, first, "grouped", True)
+        torch.cuda.synchronize()
+        gwall = time.perf_counter() - g0
+        gev = dec.events
+        g_ms = sum(a.elapsed_time(b) for a, b, _, _ in gev)
+        g_bytes = sum(attn_bytes(nb, hq, hkv, t, nql, True) for (_, _, t, nql) in gev)
+        grouped = dict(value=round(nb * S / gwall, 2), unit="tokens/s",
+                       ms_per_step=round(1e3 * gwall / S, 4),
+                       attention_GBps=round(g_bytes / (g_ms * 1e-3) / 1e9, 1),
+                       attention_frac=round(g_bytes / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                       avg_launch_us=round(1e3 * g_ms / len(gev), 2), eviction_passes=g_ev)
+        log(f"[bench] grouped: {grouped}")
+
+    if args.copy_calibration:
+        x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        y = torch.empty_like(x)
+        y.copy_(x)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 1 GiB read + 1 GiB write done")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host (bounded sample)")
+        cpu = cpu_baseline(cfg, dec.cache, qpool, W + S - 1)
+        log(f"[bench] cpu baseline: {cpu}")
+
+    res = {
+        "metric": METRIC,
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": S,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normal K/V/Q, 1% x20 value outliers), resident in HBM",
+        "config": {
+            "workload": cfg["desc"], "name": args.workload, "mode": args.mode,
+            "layers": L, "leaders": n_slots, "batch": nb, "q_heads": hq, "kv_heads": hkv,
+            "head_dim": 128, "prompt_tokens": t0,
+            **({"budget_K": ev["K"], "recent_B": ev["B"], "N_v": ev["N_v"], "window": ev["w"],
+                "period": ev["period"]} if ev else {}),
+            "mean_cache_rows": round(t_mean, 1),
+        },
+        "achieved_GBps": round(step_gbps, 1),
+        "hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "roofline": {
+            "kernel": "decode attention call: attn_bf16_kernel (split-K partials) + attn_combine_kernel",
+            "bound": "hbm",
+            "achieved": round(att_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(att_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "avg_launch_us": round(avg_launch_us, 3),
+            "launches": len(att_ms),
+            "bytes_per_launch": round(sum(att_bytes) / len(att_bytes)),
+        },
+        "eviction_passes_timed": n_evict,
+        "initial_pass_ms": None if initial_ms is None else round(initial_ms, 3),
+        "grouped": grouped,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

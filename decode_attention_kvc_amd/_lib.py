@@ -19,6 +19,7 @@ KVC_OK, KVC_EINVAL, KVC_EDTYPE, KVC_EALIGN, KVC_EWORKSPACE, KVC_EALIAS, KVC_EHIP
 KVC_F32, KVC_BF16 = 0, 1
 HEAD_DIM = 128
 T_ALIGN = 64
+V_TILE = 32
 
 EXPORTS = (
     "kvc_version", "kvc_strerror", "kvc_share_map", "kvc_append",
@@ -116,8 +117,9 @@ def _dtype_code(dt):
 class Cache:
     """A leader-slot KV cache in libkvc's layout (see include/kvc.h).
 
-    k: [n_slots][nb][n_kv_heads][t_cap][128]; v: [n_slots][nb][n_kv_heads]
-    [128][t_cap] (token-minor)."""
+    k: [n_slots][nb][n_kv_heads][t_cap][128] rows;
+    v: [n_slots][nb][n_kv_heads][t_cap/32][128][32], tiles of 32 tokens,
+    each tile channel-major."""
     k: torch.Tensor
     v: torch.Tensor
     t_len: int
@@ -126,7 +128,8 @@ class Cache:
     def empty(n_slots, nb, n_kv_heads, t_cap, dtype=torch.bfloat16, device="cuda", t_len=0):
         t_cap = int(math.ceil(t_cap / T_ALIGN) * T_ALIGN)
         k = torch.empty((n_slots, nb, n_kv_heads, t_cap, HEAD_DIM), dtype=dtype, device=device)
-        v = torch.empty((n_slots, nb, n_kv_heads, HEAD_DIM, t_cap), dtype=dtype, device=device)
+        v = torch.empty((n_slots, nb, n_kv_heads, t_cap // V_TILE, HEAD_DIM, V_TILE), dtype=dtype,
+                        device=device)
         return Cache(k, v, t_len)
 
     @property
@@ -159,13 +162,27 @@ class Cache:
         return self.k[slot, :, :, : self.t_len, :]
 
     def v_rows(self, slot):
-        return self.v[slot, :, :, :, : self.t_len].transpose(-1, -2)
+        """Logical value rows [nb][hkv][t_len][128] (a copy)."""
+        v = self.v[slot].transpose(-1, -2).reshape(self.nb, self.n_kv_heads, self.t_cap, HEAD_DIM)
+        return v[:, :, : self.t_len]
+
+    def v_row(self, slot, t):
+        """Value row t of every (b, kv head): [nb][hkv][128] (a view)."""
+        return self.v[slot, :, :, t // V_TILE, :, t % V_TILE]
 
     def fill(self, slot, k_rows, v_rows):
-        """Write logical rows [nb][hkv][T][d] into a slot and set t_len = T."""
+        """Write logical rows [nb][hkv][T][d] into a slot and set t_len = T;
+        rows past T keep their old contents."""
         T = k_rows.shape[2]
         self.k[slot, :, :, :T, :].copy_(k_rows)
-        self.v[slot, :, :, :, :T].copy_(v_rows.transpose(-1, -2))
+        nfull, rem = divmod(T, V_TILE)
+        nb, h = self.nb, self.n_kv_heads
+        if nfull:
+            self.v[slot, :, :, :nfull].copy_(
+                v_rows[:, :, : nfull * V_TILE].reshape(nb, h, nfull, V_TILE, HEAD_DIM)
+                .transpose(-1, -2))
+        if rem:
+            self.v[slot, :, :, nfull, :, :rem].copy_(v_rows[:, :, nfull * V_TILE:].transpose(-1, -2))
         self.t_len = T
 
 

@@ -52,7 +52,17 @@ int attn_target_wgs() {
     static int v = [] {
         const char* e = getenv("KVC_ATTN_TARGET_WGS");
         const int x = e ? atoi(e) : 0;
-        return x > 0 ? x : 1024;
+        return x > 0 ? x : 256;
+    }();
+    return v;
+}
+
+// Tuning knob for experiments: how split partials are merged (see attn.hip).
+int attn_combine_mode() {
+    static int v = [] {
+        const char* e = getenv("KVC_ATTN_COMBINE");
+        const int x = e ? atoi(e) : 0;
+        return (x >= 0 && x <= 2) ? x : 0;
     }();
     return v;
 }
@@ -298,7 +308,7 @@ int kvc_decode_attn(const kvc_cache* c, const void* q, int64_t q_layer_stride, i
             p.cnt = static_cast<uint32_t*>(ws);
             p.part = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                               align_up((size_t)slabs * sizeof(uint32_t), 256));
-            if (launch_attn(p, c->dtype, pl.nt, s) != hipSuccess) return KVC_EHIP;
+            if (launch_attn(p, c->dtype, pl.nt, attn_combine_mode(), s) != hipSuccess) return KVC_EHIP;
             if (p.append_write) append_done = true;
         }
     }

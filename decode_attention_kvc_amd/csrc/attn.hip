@@ -9,8 +9,8 @@
 // Work decomposition: grid (split, kv head, batch).  A workgroup of four
 // waves owns one contiguous range of 32-row tiles of one slab; its waves take
 // the tiles round-robin.  Per tile a wave
-//   * loads 32 K rows ([t][d]) and the 32-token slice of the token-minor V
-//     ([d][t]) straight from HBM into VGPRs with 16-byte loads,
+//   * loads 32 K rows ([t][d], 8 KB) and the matching 32-token V tile
+//     ([d][32], 8 KB) straight from HBM into VGPRs with 16-byte loads,
 //   * forms S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (query rows on the N
 //     side, up to 16 per tile-column block),
 //   * runs the online softmax in registers (the MFMA output layout puts one
@@ -46,9 +46,8 @@ __device__ __forceinline__ int tile_row(int c, int l16) {
 }
 
 __device__ __forceinline__ void load_tile(TileRegs& R, const uint16_t* kslab,
-                                          const uint16_t* vslab, int t_cap, int t0,
-                                          int l16, int lg, int append_row,
-                                          const uint16_t* knew_row) {
+                                          const uint16_t* vslab, int t0, int l16, int lg,
+                                          int append_row, const uint16_t* knew_row) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
         const int t = t0 + tile_row(c, l16);
@@ -59,13 +58,36 @@ __device__ __forceinline__ void load_tile(TileRegs& R, const uint16_t* kslab,
     }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
-        R.v[dt] = load_stream16(vslab + (size_t)(16 * dt + l16) * t_cap + t0 + 8 * lg);
+        R.v[dt] = load_stream16(vslab + vt_off(t0, 16 * dt + l16) + 8 * lg);
 }
 
 __device__ __forceinline__ bf16x8 as_bf(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
+// How the nsplit partials of a slab meet (template parameter CM):
+//   CM_KERNEL: plain stores; a second kernel merges them after this one.
+//   CM_FENCE:  agent-scope release fence before the arrival counter and an
+//              agent-scope acquire fence in the last workgroup (on this part
+//              that is an L2 writeback / invalidate per workgroup).
+//   CM_SC1:    partial stores and the merging loads are agent-scope atomic
+//              accesses, which are coherent across the XCDs' L2s by
+//              themselves; a completion wait orders the stores before the
+//              arrival counter, so no L2-wide maintenance is issued.
+enum { CM_KERNEL = 0, CM_FENCE = 1, CM_SC1 = 2 };
+
+template <int CM>
+__device__ __forceinline__ void st_part(float* p, float v) {
+    if constexpr (CM == CM_SC1) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *p = v;
+}
+template <int CM>
+__device__ __forceinline__ float ld_part(const float* p) {
+    if constexpr (CM == CM_SC1) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else return *p;
+}
+
 // Merge the nsplit partials of one slab and write out / lse.
 // LDS `wgt` holds nsplit * rp floats.
+template <int CM>
 __device__ void combine_slab(const AttnLaunch& p, int slab, int b, int j, float* wgt) {
     const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
     const int nsplit = p.nsplit, rp = p.rp;
@@ -75,14 +97,14 @@ __device__ void combine_slab(const AttnLaunch& p, int slab, int b, int j, float*
     const int nwaves = blockDim.x / WAVE;
     for (int r = wave; r < p.rows; r += nwaves) {
         float m = -INFINITY;
-        for (int s = lane; s < nsplit; s += WAVE) m = fmaxf(m, ml[((size_t)s * rp + r) * 2]);
+        for (int s = lane; s < nsplit; s += WAVE) m = fmaxf(m, ld_part<CM>(&ml[((size_t)s * rp + r) * 2]));
         m = wave_max(m);
         float l = 0.f;
         for (int s = lane; s < nsplit; s += WAVE) {
-            const float ms = ml[((size_t)s * rp + r) * 2];
+            const float ms = ld_part<CM>(&ml[((size_t)s * rp + r) * 2]);
             const float e = exp2f((ms - m) * LOG2E);
             wgt[s * rp + r] = e;
-            l += e * ml[((size_t)s * rp + r) * 2 + 1];
+            l += e * ld_part<CM>(&ml[((size_t)s * rp + r) * 2 + 1]);
         }
         l = wave_sum(l);
         const float inv = 1.f / l;
@@ -98,37 +120,47 @@ __device__ void combine_slab(const AttnLaunch& p, int slab, int b, int j, float*
         float o = 0.f;
         int s = 0;
         for (; s + 4 <= nsplit; s += 4) {
-            const float a0 = acc[((size_t)(s + 0) * rp + r) * D + d];
-            const float a1 = acc[((size_t)(s + 1) * rp + r) * D + d];
-            const float a2 = acc[((size_t)(s + 2) * rp + r) * D + d];
-            const float a3 = acc[((size_t)(s + 3) * rp + r) * D + d];
+            const float a0 = ld_part<CM>(&acc[((size_t)(s + 0) * rp + r) * D + d]);
+            const float a1 = ld_part<CM>(&acc[((size_t)(s + 1) * rp + r) * D + d]);
+            const float a2 = ld_part<CM>(&acc[((size_t)(s + 2) * rp + r) * D + d]);
+            const float a3 = ld_part<CM>(&acc[((size_t)(s + 3) * rp + r) * D + d]);
             o += wgt[(s + 0) * rp + r] * a0;
             o += wgt[(s + 1) * rp + r] * a1;
             o += wgt[(s + 2) * rp + r] * a2;
             o += wgt[(s + 3) * rp + r] * a3;
         }
-        for (; s < nsplit; ++s) o += wgt[s * rp + r] * acc[((size_t)s * rp + r) * D + d];
+        for (; s < nsplit; ++s) o += wgt[s * rp + r] * ld_part<CM>(&acc[((size_t)s * rp + r) * D + d]);
         const int qi = r / p.g, h = j * p.g + r % p.g;
         p.out[p.out_off[qi] + ((size_t)b * p.hq + h) * D + d] = o;
     }
 }
 
-// Publish this workgroup's partial and let the last one merge.  Returns
-// whether this workgroup merged.
-__device__ bool arrive_and_combine(const AttnLaunch& p, int slab, int b, int j, float* wgt) {
+// Publish this workgroup's partial and let the last one to arrive merge
+// (CM_FENCE, CM_SC1); with CM_KERNEL the merge is a separate launch.
+template <int CM>
+__device__ void arrive_and_combine(const AttnLaunch& p, int slab, int b, int j, float* wgt) {
+    if constexpr (CM == CM_KERNEL) return;
     __shared__ int last;
-    __threadfence();
+    if constexpr (CM == CM_FENCE) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    else __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
     if (threadIdx.x == 0) {
         const uint32_t old = atomicAdd(&p.cnt[slab], 1u);
         last = (old == (uint32_t)(p.nsplit - 1));
     }
     __syncthreads();
-    if (!last) return false;
-    __threadfence();
-    combine_slab(p, slab, b, j, wgt);
+    if (!last) return;
+    if constexpr (CM == CM_FENCE) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    else __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    combine_slab<CM>(p, slab, b, j, wgt);
     if (threadIdx.x == 0) p.cnt[slab] = 0u;
-    return true;
+}
+
+// Separate merge launch for CM_KERNEL: one workgroup per slab.
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch p) {
+    __shared__ float wgt[MAX_SPLIT_ROWS];
+    const int j = blockIdx.x, b = blockIdx.y;
+    combine_slab<CM_KERNEL>(p, b * p.hkv + j, b, j, wgt);
 }
 
 template <typename T>
@@ -137,15 +169,15 @@ __device__ void write_append_row(const AttnLaunch& p, int b, int j) {
     const T* kn = reinterpret_cast<const T*>(p.k_new) + slab * D;
     const T* vn = reinterpret_cast<const T*>(p.v_new) + slab * D;
     T* kc = const_cast<T*>(reinterpret_cast<const T*>(p.k)) + slab * p.t_cap * D;
-    T* vc = const_cast<T*>(reinterpret_cast<const T*>(p.v)) + slab * D * p.t_cap;
+    T* vc = const_cast<T*>(reinterpret_cast<const T*>(p.v)) + slab * p.t_cap * D;
     const int t = p.t_len - 1;
     for (int d = threadIdx.x; d < D; d += blockDim.x) {
         kc[(size_t)t * D + d] = kn[d];
-        vc[(size_t)d * p.t_cap + t] = vn[d];
+        vc[vt_off(t, d)] = vn[d];
     }
 }
 
-template <int NT>
+template <int NT, int CM>
 __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnLaunch p) {
     constexpr int RP = 16 * NT;
     const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
@@ -158,7 +190,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnLaunch p) {
     const int tile_end = min(tile_begin + p.tps, ntiles);
 
     const uint16_t* kslab = reinterpret_cast<const uint16_t*>(p.k) + (size_t)slab * p.t_cap * D;
-    const uint16_t* vslab = reinterpret_cast<const uint16_t*>(p.v) + (size_t)slab * D * p.t_cap;
+    const uint16_t* vslab = reinterpret_cast<const uint16_t*>(p.v) + (size_t)slab * p.t_cap * D;
     const int append_row = p.append_read ? T - 1 : -1;
     const uint16_t* knew_row =
         p.append_read ? reinterpret_cast<const uint16_t*>(p.k_new) + (size_t)slab * D : kslab;
@@ -270,7 +302,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnLaunch p) {
     // other waves on the SIMD hide the latency.
     for (int tile = tile_begin + wave; tile < tile_end; tile += ATTN_WAVES) {
         TileRegs R;
-        load_tile(R, kslab, vslab, p.t_cap, tile * ATTN_TILE, l16, lg, append_row, knew_row);
+        load_tile(R, kslab, vslab, tile * ATTN_TILE, l16, lg, append_row, knew_row);
         compute(R, tile * ATTN_TILE);
     }
 
@@ -319,21 +351,27 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnLaunch p) {
                 o[e] = a;
             }
             float* dst = part_acc + (size_t)(nt * 16 + n) * D + d0;
-            *reinterpret_cast<f32x4*>(dst) = f32x4{o[0], o[1], o[2], o[3]};
-            *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
+            if constexpr (CM == CM_SC1) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) st_part<CM>(dst + e, o[e]);
+            } else {
+                *reinterpret_cast<f32x4*>(dst) = f32x4{o[0], o[1], o[2], o[3]};
+                *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
+            }
             if (d0 == 0) {
-                part_ml[(nt * 16 + n) * 2] = M;
-                part_ml[(nt * 16 + n) * 2 + 1] = L;
+                st_part<CM>(&part_ml[(nt * 16 + n) * 2], M);
+                st_part<CM>(&part_ml[(nt * 16 + n) * 2 + 1], L);
             }
         }
         __syncthreads();
     }
 
     if (p.append_write && s == p.nsplit - 1) write_append_row<uint16_t>(p, b, j);
-    arrive_and_combine(p, slab, b, j, buf);
+    arrive_and_combine<CM>(p, slab, b, j, buf);
 }
 
 // float32 path: plain VALU arithmetic, up to 16 query rows per launch.
+template <int CM>
 __global__ __launch_bounds__(256) void attn_f32_kernel(AttnLaunch p) {
     constexpr int TT = ATTN_TILE_F32;
     const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
@@ -344,7 +382,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnLaunch p) {
     const int tile_begin = s * p.tps;
     const int tile_end = min(tile_begin + p.tps, ntiles);
     const float* kslab = reinterpret_cast<const float*>(p.k) + (size_t)slab * p.t_cap * D;
-    const float* vslab = reinterpret_cast<const float*>(p.v) + (size_t)slab * D * p.t_cap;
+    const float* vslab = reinterpret_cast<const float*>(p.v) + (size_t)slab * p.t_cap * D;
     const float* knew = reinterpret_cast<const float*>(p.k_new) + (size_t)slab * D;
     const float* vnew = reinterpret_cast<const float*>(p.v_new) + (size_t)slab * D;
     const int append_row = p.append_read ? T - 1 : -1;
@@ -427,10 +465,9 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnLaunch p) {
         // acc[r][d] = acc * alpha + sum_t p[r][t] V^T[d][t]
         {
             float vv[TT];
-            const float* vr = vslab + (size_t)d * p.t_cap + t0;
 #pragma unroll
             for (int x = 0; x < TT; x += 4) {
-                const f32x4 v4 = *reinterpret_cast<const f32x4*>(vr + x);
+                const f32x4 v4 = *reinterpret_cast<const f32x4*>(vslab + vt_off(t0 + x, d));
                 vv[x] = v4[0]; vv[x + 1] = v4[1]; vv[x + 2] = v4[2]; vv[x + 3] = v4[3];
             }
             if (t0 + TT >= T) {   // last tile: rows past the end, appended row
@@ -456,13 +493,13 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnLaunch p) {
     float* part_acc = p.part + ((size_t)slab * p.nsplit + s) * 16 * D;
     float* part_ml = p.part + slabs * p.nsplit * 16 * D + ((size_t)slab * p.nsplit + s) * 16 * 2;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) part_acc[(size_t)(half + 2 * k) * D + d] = acc[k];
+    for (int k = 0; k < 8; ++k) st_part<CM>(&part_acc[(size_t)(half + 2 * k) * D + d], acc[k]);
     if (tid < 16) {
-        part_ml[tid * 2] = mrow[tid];
-        part_ml[tid * 2 + 1] = lrow[tid];
+        st_part<CM>(&part_ml[tid * 2], mrow[tid]);
+        st_part<CM>(&part_ml[tid * 2 + 1], lrow[tid]);
     }
     if (p.append_write && s == p.nsplit - 1) write_append_row<float>(p, b, j);
-    arrive_and_combine(p, slab, b, j, wgt);
+    arrive_and_combine<CM>(p, slab, b, j, wgt);
 }
 
 template <typename T>
@@ -472,23 +509,32 @@ __global__ __launch_bounds__(128) void append_kernel(T* k, T* v, int hkv, int t_
     const int t = t_len - 1;
     for (int d = threadIdx.x; d < D; d += blockDim.x) {
         k[(slab * t_cap + t) * D + d] = k_new[slab * D + d];
-        v[(slab * D + d) * t_cap + t] = v_new[slab * D + d];
+        v[slab * t_cap * D + vt_off(t, d)] = v_new[slab * D + d];
     }
 }
 
 }  // namespace
 
-hipError_t launch_attn(const AttnLaunch& p, int dtype, int nt, hipStream_t st) {
+template <int CM>
+static void launch_attn_cm(const AttnLaunch& p, int dtype, int nt, hipStream_t st) {
     const dim3 grid(p.nsplit, p.hkv, p.nb);
     if (dtype == 0) {
-        hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(256), 0, st, p);
+        hipLaunchKernelGGL(attn_f32_kernel<CM>, grid, dim3(256), 0, st, p);
     } else if (nt == 1) {
-        hipLaunchKernelGGL(attn_bf16_kernel<1>, grid, dim3(256), 0, st, p);
+        hipLaunchKernelGGL((attn_bf16_kernel<1, CM>), grid, dim3(256), 0, st, p);
     } else if (nt == 2) {
-        hipLaunchKernelGGL(attn_bf16_kernel<2>, grid, dim3(256), 0, st, p);
+        hipLaunchKernelGGL((attn_bf16_kernel<2, CM>), grid, dim3(256), 0, st, p);
     } else {
-        hipLaunchKernelGGL(attn_bf16_kernel<4>, grid, dim3(256), 0, st, p);
+        hipLaunchKernelGGL((attn_bf16_kernel<4, CM>), grid, dim3(256), 0, st, p);
     }
+    if constexpr (CM == CM_KERNEL)
+        hipLaunchKernelGGL(attn_combine_kernel, dim3(p.hkv, p.nb), dim3(256), 0, st, p);
+}
+
+hipError_t launch_attn(const AttnLaunch& p, int dtype, int nt, int combine, hipStream_t st) {
+    if (combine == CM_FENCE) launch_attn_cm<CM_FENCE>(p, dtype, nt, st);
+    else if (combine == CM_SC1) launch_attn_cm<CM_SC1>(p, dtype, nt, st);
+    else launch_attn_cm<CM_KERNEL>(p, dtype, nt, st);
     return hipGetLastError();
 }
 

@@ -7,6 +7,15 @@ namespace kvc {
 
 constexpr int D = 128;          // head dimension
 constexpr int WAVE = 64;        // CDNA wavefront width
+constexpr int VT = 32;          // tokens per V tile
+
+// Element offset of value V[t][d] inside one slab.  Values are stored in
+// tiles of 32 tokens, each tile channel-major ([d][32]): the 32-token slice
+// of all 128 channels is one contiguous 8 KB (bf16) block, and the
+// token-contiguous operand of the P*V product is one 16-byte load per lane.
+__host__ __device__ __forceinline__ size_t vt_off(int t, int d) {
+    return (size_t)(t >> 5) * (D * VT) + (size_t)d * VT + (t & (VT - 1));
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -3,13 +3,13 @@
 // VASE summary (gist.science 2606.03928), §1: eviction discards the dropped
 // key/value pairs for good, which is what gives the cache its fixed
 // footprint.  dst row i <- src row kept[i] for every slab of the slot, K in
-// [t][d] rows and V in token-minor [d][t] columns, out of place.
+// [t][d] rows and V in 32-token channel-major tiles, out of place.
 //
 // One workgroup (256 threads) per 256 kept rows of a slab.  K rows are
 // copied with 16-byte accesses, 16 (bf16) or 32 (fp32) lanes per row.  For V
-// each thread owns one kept row and walks the 128 channel rows; the source
-// indices are ascending, so a wave's reads of one channel row fall on a few
-// cache lines.  An index outside [0, src t_len) produces a zero row instead
+// each thread owns one kept row and walks the 128 channels; the source
+// indices are ascending, so a wave's reads of one channel fall in a few
+// tiles.  An index outside [0, src t_len) produces a zero row instead
 // of an out-of-bounds read.
 #include "common.h"
 #include "kvc_internal.h"
@@ -29,9 +29,9 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactLaunch p) {
     const int tid = threadIdx.x;
     const int32_t* kept = p.kept + (size_t)slab * p.n_keep;
     const E* sk = reinterpret_cast<const E*>(p.sk) + (size_t)slab * p.src_t_cap * D;
-    const E* sv = reinterpret_cast<const E*>(p.sv) + (size_t)slab * D * p.src_t_cap;
+    const E* sv = reinterpret_cast<const E*>(p.sv) + (size_t)slab * p.src_t_cap * D;
     E* dk = reinterpret_cast<E*>(p.dk) + (size_t)slab * p.dst_t_cap * D;
-    E* dv = reinterpret_cast<E*>(p.dv) + (size_t)slab * D * p.dst_t_cap;
+    E* dv = reinterpret_cast<E*>(p.dv) + (size_t)slab * p.dst_t_cap * D;
     const int rows = min(CROWS, p.n_keep - i0);
 
     __shared__ int32_t src_row[CROWS];
@@ -54,8 +54,8 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactLaunch p) {
         const int32_t r = src_row[tid];
         for (int d = 0; d < D; ++d) {
             E v = E(0);
-            if (r >= 0) v = sv[(size_t)d * p.src_t_cap + r];
-            dv[(size_t)d * p.dst_t_cap + i0 + tid] = v;
+            if (r >= 0) v = sv[vt_off(r, d)];
+            dv[vt_off(i0 + tid, d)] = v;
         }
     }
 }

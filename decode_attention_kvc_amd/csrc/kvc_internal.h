@@ -83,7 +83,9 @@ struct CompactLaunch {
 
 // Host-side launchers (defined next to their kernels).  Each returns
 // hipSuccess or the launch error.
-hipError_t launch_attn(const AttnLaunch& p, int dtype, int nt, hipStream_t s);
+// combine: 0 = separate merge kernel, 1 = fenced last-workgroup merge,
+// 2 = last-workgroup merge through agent-scope atomic accesses.
+hipError_t launch_attn(const AttnLaunch& p, int dtype, int nt, int combine, hipStream_t s);
 hipError_t launch_append(const void* k, const void* v, int nb, int hkv, int t_len,
                          int t_cap, const void* k_new, const void* v_new, int elem,
                          hipStream_t s);

@@ -31,7 +31,7 @@ __device__ __forceinline__ bf16x8 as_bf(u32x4 x) { return __builtin_bit_cast(bf1
 // Range of the 32 rows t0..t0+31 of one slab from its token-minor V slice;
 // one wave.  Lane (l16, lg) reads channels 16*dt + l16 of rows
 // t0 + 8*lg .. +8.
-__device__ __forceinline__ void range_tile_bf16(const uint16_t* vslab, int t_cap, int t0, int T,
+__device__ __forceinline__ void range_tile_bf16(const uint16_t* vslab, int t0, int T,
                                                 float* range_out, int lane) {
     const int l16 = lane & 15, lg = lane >> 4;
     float mx[8], mn[8];
@@ -42,7 +42,7 @@ __device__ __forceinline__ void range_tile_bf16(const uint16_t* vslab, int t_cap
     }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-        const u32x4 x = load16(vslab + (size_t)(16 * dt + l16) * t_cap + t0 + 8 * lg);
+        const u32x4 x = load16(vslab + vt_off(t0, 16 * dt + l16) + 8 * lg);
 #pragma unroll
         for (int w2 = 0; w2 < 4; ++w2) {
             const float a = bf16lo(x[w2]), b2 = bf16hi(x[w2]);
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(1024) void score_main_bf16(ScoreLaunch p) {
     const int ntiles = (T + SCORE_TILE - 1) / SCORE_TILE;
     const int tile_begin = s * p.tps, tile_end = min(tile_begin + p.tps, ntiles);
     const uint16_t* kslab = reinterpret_cast<const uint16_t*>(p.k) + (size_t)slab * p.t_cap * D;
-    const uint16_t* vslab = reinterpret_cast<const uint16_t*>(p.v) + (size_t)slab * D * p.t_cap;
+    const uint16_t* vslab = reinterpret_cast<const uint16_t*>(p.v) + (size_t)slab * p.t_cap * D;
     float* score = p.score + (size_t)slab * T;
     float* range = p.range ? p.range + (size_t)slab * T : nullptr;
 
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(1024) void score_main_bf16(ScoreLaunch p) {
             if (lg == 0) colsum[wave][(tile - tile_begin) * SCORE_TILE + 16 * cg + l16] = c;
         }
         if (range && (tile - tile_begin) % nwaves == wave)
-            range_tile_bf16(vslab, p.t_cap, t0, T, range, lane);
+            range_tile_bf16(vslab, t0, T, range, lane);
     }
     __syncthreads();
     const int n = (tile_end - tile_begin) * SCORE_TILE;
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(256) void score_f32(ScoreLaunch p, int stats_pass) 
     const int ntiles = (T + FT - 1) / FT;
     const int tile_begin = s * p.tps, tile_end = min(tile_begin + p.tps, ntiles);
     const float* kslab = reinterpret_cast<const float*>(p.k) + (size_t)slab * p.t_cap * D;
-    const float* vslab = reinterpret_cast<const float*>(p.v) + (size_t)slab * D * p.t_cap;
+    const float* vslab = reinterpret_cast<const float*>(p.v) + (size_t)slab * p.t_cap * D;
     __shared__ float ks[FT][D + 1];
     __shared__ float csum[4][FT];
     __shared__ int last;
@@ -352,7 +352,7 @@ __global__ __launch_bounds__(256) void score_f32(ScoreLaunch p, int stats_pass) 
                 if (p.range) {
                     float mx = -INFINITY, mn = INFINITY;
                     for (int d = 0; d < D; ++d) {
-                        const float v = vslab[(size_t)d * p.t_cap + t0 + tid];
+                        const float v = vslab[vt_off(t0 + tid, d)];
                         mx = fmaxf(mx, v);
                         mn = fminf(mn, v);
                     }
@@ -405,7 +405,7 @@ __global__ __launch_bounds__(256) void value_range_kernel(const E* v, int hkv, i
     const int slab = blockIdx.z * hkv + blockIdx.y;
     const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
     const int t0 = blockIdx.x * ROWS + lane * VEC;
-    const E* vs = v + (size_t)slab * D * t_cap;
+    const E* vs = v + (size_t)slab * t_cap * D;
     __shared__ float smx[4][ROWS], smn[4][ROWS];
     float mx[VEC], mn[VEC];
 #pragma unroll
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(256) void value_range_kernel(const E* v, int hkv, i
     }
     if (t0 < t_len) {
         for (int d = 32 * wave; d < 32 * wave + 32; ++d) {
-            const u32x4 x = load16(vs + (size_t)d * t_cap + t0);
+            const u32x4 x = load16(vs + vt_off(t0, d));
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
                 float f;

@@ -67,14 +67,18 @@ typedef enum kvc_dtype {
 #define KVC_HEAD_DIM 128
 /* t_cap must be a multiple of this (keeps every vector access in bounds). */
 #define KVC_T_ALIGN 64
+/* Tokens per value tile. */
+#define KVC_V_TILE 32
 
 /*
  * A KV cache of n_slots leader slots (one per layer in S), batch nb,
  * n_kv_heads heads and head_dim = 128.  One slab = one (slot, b, kv head).
- *   k: [n_slots][nb][n_kv_heads][t_cap][head_dim]   row-major rows
- *   v: [n_slots][nb][n_kv_heads][head_dim][t_cap]   token-minor: the value
- *      rows of a slab are stored transposed, so that the t-contiguous
- *      operand of the P*V product loads with one 16-byte access per lane.
+ *   k: [n_slots][nb][n_kv_heads][t_cap][head_dim]        row-major rows
+ *   v: [n_slots][nb][n_kv_heads][t_cap/32][head_dim][32] tiles of 32 tokens,
+ *      each tile channel-major: value V[t][c] of a slab sits at element
+ *      (t/32)*head_dim*32 + c*32 + t%32.  A tile's values are one contiguous
+ *      block, and the token-contiguous operand of the P*V product loads with
+ *      one 16-byte access per lane.
  * Rows [0, t_len) are valid in every slot; t_len is shared by all slots.
  * dtype is a kvc_dtype; both k and v hold that type.
  */

@@ -221,3 +221,22 @@ def test_append_and_range_and_philox_validation():
     assert L.kvc_philox_words(0, 0, 0, 0, 0, FAKE, None) == kvc.KVC_OK
     assert L.kvc_decode_attn(None, FAKE, 0, 1, (ctypes.c_int32 * 1)(0), 8, 0.0, None, None, -1,
                              FAKE, 0, None, 0, FAKE, 1 << 30, None) == kvc.KVC_EALIGN
+
+
+@pytest.mark.parametrize("T", [1, 31, 32, 95, 128])
+def test_cache_layout_roundtrip(T):
+    import torch
+    c = kvc.Cache.empty(2, 2, 3, T, dtype=torch.float32, device="cpu")
+    c.v.fill_(float("nan"))
+    K = torch.randn(2, 3, T, 128)
+    V = torch.randn(2, 3, T, 128)
+    c.fill(1, K, V)
+    assert torch.equal(c.k_rows(1), K) and torch.equal(c.v_rows(1), V)
+    for t in (0, T - 1):
+        assert torch.equal(c.v_row(1, t), V[:, :, t])
+    # element offset of V[t][d] inside a slab: (t/32)*128*32 + d*32 + t%32
+    flat = c.v[1, 1, 2].reshape(-1)
+    t, d = T - 1, 77
+    assert flat[(t // 32) * 4096 + d * 32 + t % 32] == V[1, 2, t, d]
+    if T % 32:
+        assert torch.isnan(c.v[1, :, :, T // 32, :, T % 32:]).all()   # rows past T untouched

@@ -107,7 +107,7 @@ def test_decode_attn_append(dtype, T0):
     out, lse = run_decode(cache, q, [1, 1], k_new=kn, v_new=vn, append_slot=1)
     # the cache row was written
     assert torch.equal(cache.k[1, :, :, T0, :], kn)
-    assert torch.equal(cache.v[1, :, :, :, T0], vn)
+    assert torch.equal(cache.v_row(1, T0), vn)
     K = np.concatenate([K0, to_np(kn)[:, :, None]], axis=2)
     V = np.concatenate([V0, to_np(vn)[:, :, None]], axis=2)
     ref, ref_lse = oracle.decode_attention(to_np(q), [None, K], [None, V], [1, 1], hkv, T0 + 1)
@@ -121,7 +121,7 @@ def test_decode_attn_append(dtype, T0):
     assert torch.equal(cache.k[1, :, :, T0 + 1, :], kn2)
     kvc.kvc_append(cache, 0, kn2, kn2)
     torch.cuda.synchronize()
-    assert torch.equal(cache.v[0, :, :, :, T0 + 1], kn2)
+    assert torch.equal(cache.v_row(0, T0 + 1), kn2)
 
 
 def test_decode_attn_strided_layers_and_determinism():
