@@ -56,6 +56,14 @@ def attn_bytes(nb, hq, hkv, t_len, n_q_layers, lead):
     return kv + q + out + app
 
 
+def step_attn_bytes(dec, mode, nb, hq, hkv, t_len):
+    """Algorithmic bytes of one step's attention calls."""
+    if mode == "per-layer":
+        return sum(attn_bytes(nb, hq, hkv, t_len, 1, dec.src_layer[l] == l)
+                   for l in range(dec.n_layers))
+    return sum(attn_bytes(nb, hq, hkv, t_len, len(g), True) for g in dec.groups)
+
+
 def evict_bytes(cfg, t_len):
     """Algorithmic bytes of one eviction pass: K + V read once by the fused
     score/range pass, score/range written and read, kept rows gathered (read)
@@ -231,17 +239,13 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = 1e3 * wall / S
-    events = dec.events
+    events = dec.events            # one pair per step around its attention calls
     att_ms = [a.elapsed_time(b) for a, b, _, _ in events]
-    # leaders' launches carry the appended row; followers' do not
-    if args.mode == "per-layer":
-        att_bytes = [attn_bytes(nb, hq, hkv, t, 1, (i % L) in leaders)
-                     for i, (_, _, t, _) in enumerate(events)]
-    else:
-        att_bytes = [attn_bytes(nb, hq, hkv, t, nql, True) for (_, _, t, nql) in events]
+    att_bytes = [step_attn_bytes(dec, args.mode, nb, hq, hkv, t) for (_, _, t, _) in events]
+    n_calls = sum(n for _, _, _, n in events)
     att_total_ms = sum(att_ms)
     att_gbps = sum(att_bytes) / (att_total_ms * 1e-3) / 1e9
-    avg_launch_us = 1e3 * att_total_ms / len(att_ms)
+    avg_launch_us = 1e3 * att_total_ms / n_calls
     tok_s = nb * S / wall
     log(f"[bench] {S} steps in {wall:.3f} s: {tok_s:.1f} tok/s, attention {att_gbps:.0f} GB/s "
         f"({100 * att_gbps / HBM_PEAK_GBPS:.1f}% of peak), avg launch {avg_launch_us:.1f} us, "
@@ -262,12 +266,13 @@ def main():
         gwall = time.perf_counter() - g0
         gev = dec.events
         g_ms = sum(a.elapsed_time(b) for a, b, _, _ in gev)
-        g_bytes = sum(attn_bytes(nb, hq, hkv, t, nql, True) for (_, _, t, nql) in gev)
+        g_bytes = sum(step_attn_bytes(dec, "grouped", nb, hq, hkv, t) for (_, _, t, _) in gev)
+        g_calls = sum(n for _, _, _, n in gev)
         grouped = dict(value=round(nb * S / gwall, 2), unit="tokens/s",
                        ms_per_step=round(1e3 * gwall / S, 4),
                        attention_GBps=round(g_bytes / (g_ms * 1e-3) / 1e9, 1),
                        attention_frac=round(g_bytes / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                       avg_launch_us=round(1e3 * g_ms / len(gev), 2), eviction_passes=g_ev)
+                       avg_launch_us=round(1e3 * g_ms / g_calls, 2), eviction_passes=g_ev)
         log(f"[bench] grouped: {grouped}")
 
     if args.copy_calibration:
@@ -315,8 +320,9 @@ def main():
             "frac": round(att_gbps / HBM_PEAK_GBPS, 4),
             "traffic": None,
             "avg_launch_us": round(avg_launch_us, 3),
-            "launches": len(att_ms),
-            "bytes_per_launch": round(sum(att_bytes) / len(att_bytes)),
+            "launches": n_calls,
+            "bytes_per_launch": round(sum(att_bytes) / n_calls),
+            "timing": "HIP events around each step's attention calls (eviction outside)",
         },
         "eviction_passes_timed": n_evict,
         "initial_pass_ms": None if initial_ms is None else round(initial_ms, 3),

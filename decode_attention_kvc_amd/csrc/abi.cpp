@@ -57,6 +57,21 @@ int attn_target_wgs() {
     return v;
 }
 
+static int env_int(const char* name, int dflt) {
+    const char* e = getenv(name);
+    return e ? atoi(e) : dflt;
+}
+int attn_waves() {
+    static int v = env_int("KVC_ATTN_WAVES", 4) == 8 ? 8 : 4;
+    return v;
+}
+int attn_prefetch() {
+    static int v = env_int("KVC_ATTN_PREFETCH", 1) ? 1 : 0;
+    return v;
+}
+
+
+
 // Tuning knob for experiments: how split partials are merged (see attn.hip).
 int attn_combine_mode() {
     static int v = [] {
@@ -84,7 +99,7 @@ AttnPlan plan_attn(int dtype, int rows, int t_len, int slabs) {
         pl.nt = rows <= 16 ? 1 : rows <= 32 ? 2 : 4;
         pl.rp = 16 * pl.nt;
         tile = ATTN_TILE;
-        min_tps = ATTN_WAVES;   // at least one tile per wave
+        min_tps = (pl.nt == 1 && attn_combine_mode() == 0) ? attn_waves() : ATTN_WAVES;
     }
     const int ntiles = std::max(1, (t_len + tile - 1) / tile);
     const long long work = (long long)ntiles * std::max(1, slabs);
@@ -305,6 +320,8 @@ int kvc_decode_attn(const kvc_cache* c, const void* q, int64_t q_layer_stride, i
             p.rp = pl.rp;
             p.nsplit = pl.nsplit;
             p.tps = pl.tps;
+            p.waves = attn_waves();
+            p.prefetch = attn_prefetch();
             p.cnt = static_cast<uint32_t*>(ws);
             p.part = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                               align_up((size_t)slabs * sizeof(uint32_t), 256));

@@ -24,6 +24,8 @@
 // (m, l, acc) per query row; the last workgroup of a slab to finish (an
 // arrival counter in the workspace, reset by that workgroup) merges all
 // partials with log-sum-exp weights and writes out / lse.
+#include <type_traits>
+
 #include "common.h"
 #include "kvc_internal.h"
 
@@ -156,11 +158,47 @@ __device__ void arrive_and_combine(const AttnLaunch& p, int slab, int b, int j, 
     if (threadIdx.x == 0) p.cnt[slab] = 0u;
 }
 
-// Separate merge launch for CM_KERNEL: one workgroup per slab.
+// Separate merge launch for CM_KERNEL: one workgroup per slab; each thread
+// owns one query row and 8 channels and folds the splits in order with
+// running log-sum-exp weights, so all of a split's loads are independent
+// and no barrier or LDS round trip is needed.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch p) {
-    __shared__ float wgt[MAX_SPLIT_ROWS];
     const int j = blockIdx.x, b = blockIdx.y;
-    combine_slab<CM_KERNEL>(p, b * p.hkv + j, b, j, wgt);
+    const int slab = b * p.hkv + j;
+    const int nsplit = p.nsplit, rp = p.rp;
+    const size_t slabs = (size_t)p.nb * p.hkv;
+    const float* acc = p.part + (size_t)slab * nsplit * rp * D;
+    const float* ml = p.part + slabs * nsplit * rp * D + (size_t)slab * nsplit * rp * 2;
+    for (int idx = threadIdx.x; idx < p.rows * (D / 8); idx += blockDim.x) {
+        const int r = idx / (D / 8), d0 = (idx % (D / 8)) * 8;
+        float M = -INFINITY, L = 0.f, o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = 0.f;
+#pragma unroll 4
+        for (int sp = 0; sp < nsplit; ++sp) {
+            const float ms = ml[((size_t)sp * rp + r) * 2];
+            const float ls = ml[((size_t)sp * rp + r) * 2 + 1];
+            const float* a = acc + ((size_t)sp * rp + r) * D + d0;
+            const f32x4 a0 = *reinterpret_cast<const f32x4*>(a);
+            const f32x4 a1 = *reinterpret_cast<const f32x4*>(a + 4);
+            const float mn = fmaxf(M, ms);
+            const float fo = exp2f((M - mn) * LOG2E);   // 0 on the first split
+            const float fs = exp2f((ms - mn) * LOG2E);
+            L = L * fo + ls * fs;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                o[e] = o[e] * fo + a0[e] * fs;
+                o[4 + e] = o[4 + e] * fo + a1[e] * fs;
+            }
+            M = mn;
+        }
+        const float inv = 1.f / L;
+        const int qi = r / p.g, h = j * p.g + r % p.g;
+        float* dst = p.out + p.out_off[qi] + ((size_t)b * p.hq + h) * D + d0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[e] = o[e] * inv;
+        if (d0 == 0 && p.lse) p.lse[p.lse_off[qi] + (size_t)b * p.hq + h] = M + logf(L);
+    }
 }
 
 template <typename T>
@@ -177,8 +215,8 @@ __device__ void write_append_row(const AttnLaunch& p, int b, int j) {
     }
 }
 
-template <int NT, int CM>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnLaunch p) {
+template <int NT, int CM, int W, int PF>
+__global__ __launch_bounds__(W * 64) void attn_bf16_kernel(AttnLaunch p) {
     constexpr int RP = 16 * NT;
     const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int slab = b * p.hkv + j;
@@ -226,21 +264,21 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnLaunch p) {
     }
     const float scale = p.scale;
 
-    auto compute = [&](TileRegs& R, int t0) {
-        // The last tile of the slab (it holds row T-1, the appended row).
-        const bool tail = (t0 + ATTN_TILE >= T);
-        if (tail) {
-            // Rows past the end hold arbitrary bits: zero their V entries
-            // (P is zero there too, but 0 * NaN would poison the sum) and
-            // take the appended row's values from v_new.
+    // One 32-row tile.  TAIL marks the slab's last tile: rows past the end
+    // are masked (their K and V bits are arbitrary: P is zeroed and so is V,
+    // since 0 * NaN would poison the sum) and the appended row's V comes from
+    // v_new.  Interior tiles take no branch at all.
+    auto compute = [&](TileRegs& R, int t0, auto tail_tag) {
+        constexpr bool TAIL = decltype(tail_tag)::value;
+        if constexpr (TAIL) {
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
+                const uint16_t vn = vnew_row[16 * dt + l16];
                 u16x8 e = __builtin_bit_cast(u16x8, R.v[dt]);
 #pragma unroll
                 for (int jj = 0; jj < 8; ++jj) {
                     const int t = t0 + 8 * lg + jj;
-                    if (t == append_row) e[jj] = vnew_row[16 * dt + l16];
-                    else if (t >= T) e[jj] = 0;
+                    e[jj] = (t == append_row) ? vn : ((t >= T) ? (uint16_t)0 : e[jj]);
                 }
                 R.v[dt] = __builtin_bit_cast(u32x4, e);
             }
@@ -263,7 +301,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnLaunch p) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float x = S[c][i] * scale;
-                    if (tail && (t0 + 8 * lg + 4 * c + i >= T)) x = -INFINITY;
+                    if constexpr (TAIL) x = (t0 + 8 * lg + 4 * c + i >= T) ? -INFINITY : x;
                     sv[4 * c + i] = x;
                 }
             float mx = sv[0];
@@ -297,13 +335,53 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnLaunch p) {
             }
         }
     };
+    using Interior = std::integral_constant<bool, false>;
+    using Last = std::integral_constant<bool, true>;
 
-    // Tile loop: each wave keeps one tile (16 KB) of loads in flight; the
-    // other waves on the SIMD hide the latency.
-    for (int tile = tile_begin + wave; tile < tile_end; tile += ATTN_WAVES) {
+    // Interior tiles of this split (the slab's last tile is left out), taken
+    // round-robin by the waves.
+    const int main_end = min(tile_end, ntiles - 1);
+    const int n_main = max(0, main_end - tile_begin);
+    auto tile_at = [&](int i) { return tile_begin + i; };
+    if constexpr (PF == 0) {
+        // One tile (16 KB) of loads in flight per wave.
+        for (int i = wave; i < n_main; i += W) {
+            TileRegs R;
+            load_tile(R, kslab, vslab, tile_at(i) * ATTN_TILE, l16, lg, -1, kslab);
+            compute(R, tile_at(i) * ATTN_TILE, Interior{});
+        }
+    } else {
+        // Two tiles in flight per wave: the next tile's loads are issued
+        // before the current tile is computed.  Inside the loop body every
+        // load is unconditional, so the compiler's wait counts only cover
+        // the older tile; two named register sets avoid copies.
+        const int n = wave < n_main ? (n_main - wave + W - 1) / W : 0;   // tiles of this wave
+        auto t0_of = [&](int k) { return tile_at(wave + k * W) * ATTN_TILE; };
+        if (n > 0) {
+            TileRegs RA, RB;
+            load_tile(RA, kslab, vslab, t0_of(0), l16, lg, -1, kslab);
+            int k = 0;
+            for (; k + 2 < n; k += 2) {
+                load_tile(RB, kslab, vslab, t0_of(k + 1), l16, lg, -1, kslab);
+                compute(RA, t0_of(k), Interior{});
+                load_tile(RA, kslab, vslab, t0_of(k + 2), l16, lg, -1, kslab);
+                compute(RB, t0_of(k + 1), Interior{});
+            }
+            if (k + 1 < n) {
+                load_tile(RB, kslab, vslab, t0_of(k + 1), l16, lg, -1, kslab);
+                compute(RA, t0_of(k), Interior{});
+                compute(RB, t0_of(k + 1), Interior{});
+            } else {
+                compute(RA, t0_of(k), Interior{});
+            }
+        }
+    }
+    // The slab's last tile, by the wave whose round-robin turn it is.
+    if (tile_end == ntiles && wave == (ntiles - 1 - tile_begin) % W) {
         TileRegs R;
-        load_tile(R, kslab, vslab, tile * ATTN_TILE, l16, lg, append_row, knew_row);
-        compute(R, tile * ATTN_TILE);
+        const int t0 = (ntiles - 1) * ATTN_TILE;
+        load_tile(R, kslab, vslab, t0, l16, lg, append_row, knew_row);
+        compute(R, t0, Last{});
     }
 
     // Row sums: each of the four lane groups holds a quarter of the rows.
@@ -315,8 +393,9 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnLaunch p) {
 
     // Merge the four waves through LDS, one 16-row block at a time, and
     // write this workgroup's partial.
-    __shared__ float buf[ATTN_WAVES * 16 * D];   // also the combine weights
-    __shared__ float wm[ATTN_WAVES][16], wl[ATTN_WAVES][16];
+    __shared__ float buf[W * 16 * D];   // also the combine weights
+    __shared__ float wm[W][16], wl[W][16];
+    constexpr int EPT = 2048 / (W * 64);  // merged outputs per thread (16 rows x 128)
     const size_t slabs = (size_t)p.nb * p.hkv;
     float* part_acc = p.part + ((size_t)slab * p.nsplit + s) * RP * D;
     float* part_ml = p.part + slabs * p.nsplit * RP * D + ((size_t)slab * p.nsplit + s) * RP * 2;
@@ -332,31 +411,32 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnLaunch p) {
             for (int i = 0; i < 4; ++i) buf[(wave * 16 + l16) * D + 16 * dt + 4 * lg + i] = acc[nt][dt][i];
         __syncthreads();
         {
-            const int n = tid / 16, d0 = (tid % 16) * 8;
+            const int n = tid / (D / EPT), d0 = (tid % (D / EPT)) * EPT;
             float M = wm[0][n];
 #pragma unroll
-            for (int w = 1; w < ATTN_WAVES; ++w) M = fmaxf(M, wm[w][n]);
-            float f[ATTN_WAVES], L = 0.f;
+            for (int w = 1; w < W; ++w) M = fmaxf(M, wm[w][n]);
+            float f[W], L = 0.f;
 #pragma unroll
-            for (int w = 0; w < ATTN_WAVES; ++w) {
+            for (int w = 0; w < W; ++w) {
                 f[w] = exp2f((wm[w][n] - M) * LOG2E);   // waves without rows: exp2(-inf) = 0
                 L += f[w] * wl[w][n];
             }
-            float o[8];
+            float o[EPT];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+            for (int e = 0; e < EPT; ++e) {
                 float a = 0.f;
 #pragma unroll
-                for (int w = 0; w < ATTN_WAVES; ++w) a += f[w] * buf[(w * 16 + n) * D + d0 + e];
+                for (int w = 0; w < W; ++w) a += f[w] * buf[(w * 16 + n) * D + d0 + e];
                 o[e] = a;
             }
             float* dst = part_acc + (size_t)(nt * 16 + n) * D + d0;
             if constexpr (CM == CM_SC1) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) st_part<CM>(dst + e, o[e]);
+                for (int e = 0; e < EPT; ++e) st_part<CM>(dst + e, o[e]);
             } else {
-                *reinterpret_cast<f32x4*>(dst) = f32x4{o[0], o[1], o[2], o[3]};
-                *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
+#pragma unroll
+                for (int e = 0; e < EPT; e += 4)
+                    *reinterpret_cast<f32x4*>(dst + e) = f32x4{o[e], o[e + 1], o[e + 2], o[e + 3]};
             }
             if (d0 == 0) {
                 st_part<CM>(&part_ml[(nt * 16 + n) * 2], M);
@@ -521,11 +601,22 @@ static void launch_attn_cm(const AttnLaunch& p, int dtype, int nt, hipStream_t s
     if (dtype == 0) {
         hipLaunchKernelGGL(attn_f32_kernel<CM>, grid, dim3(256), 0, st, p);
     } else if (nt == 1) {
-        hipLaunchKernelGGL((attn_bf16_kernel<1, CM>), grid, dim3(256), 0, st, p);
+        if constexpr (CM == CM_KERNEL) {
+            if (p.waves == 8 && p.prefetch)
+                hipLaunchKernelGGL((attn_bf16_kernel<1, CM, 8, 1>), grid, dim3(512), 0, st, p);
+            else if (p.waves == 8)
+                hipLaunchKernelGGL((attn_bf16_kernel<1, CM, 8, 0>), grid, dim3(512), 0, st, p);
+            else if (p.prefetch)
+                hipLaunchKernelGGL((attn_bf16_kernel<1, CM, 4, 1>), grid, dim3(256), 0, st, p);
+            else
+                hipLaunchKernelGGL((attn_bf16_kernel<1, CM, 4, 0>), grid, dim3(256), 0, st, p);
+        } else {
+            hipLaunchKernelGGL((attn_bf16_kernel<1, CM, 4, 0>), grid, dim3(256), 0, st, p);
+        }
     } else if (nt == 2) {
-        hipLaunchKernelGGL((attn_bf16_kernel<2, CM>), grid, dim3(256), 0, st, p);
+        hipLaunchKernelGGL((attn_bf16_kernel<2, CM, 4, 0>), grid, dim3(256), 0, st, p);
     } else {
-        hipLaunchKernelGGL((attn_bf16_kernel<4, CM>), grid, dim3(256), 0, st, p);
+        hipLaunchKernelGGL((attn_bf16_kernel<4, CM, 4, 0>), grid, dim3(256), 0, st, p);
     }
     if constexpr (CM == CM_KERNEL)
         hipLaunchKernelGGL(attn_combine_kernel, dim3(p.hkv, p.nb), dim3(256), 0, st, p);

@@ -36,6 +36,7 @@ struct AttnLaunch {
     int append_read;        // row t_len-1 comes from k_new / v_new
     int append_write;       // and is written into the cache
     int nsplit, tps;        // splits per slab, tiles per split
+    int waves, prefetch;    // waves per workgroup, next-tile prefetch
     float* part;            // partial accumulators, then (m, l) pairs
     uint32_t* cnt;          // one arrival counter per slab
 };

@@ -57,26 +57,25 @@ class Decoder:
         c.t_len += 1
         n_steps = qpool.shape[1]
         nb, hq, d = qpool.shape[2], qpool.shape[3], qpool.shape[4]
+        ev = self._ev_begin()
         if self.mode == "per-layer":
             for l in range(self.n_layers):
                 slot = self.src_slot[l]
                 lead = self.src_layer[l] == l
-                ev = self._ev_begin()
                 K.kvc_decode_attn(c, qpool[l, s], [slot], out[l], lsepool[l, s], self.ws_attn,
                                   k_new=knew[s, slot] if lead else None,
                                   v_new=vnew[s, slot] if lead else None,
                                   append_slot=slot if lead else -1, n_q_heads=hq)
-                self._ev_end(ev, c, 1)
+            self._ev_end(ev, c, self.n_layers)
         else:
             for slot, layers in enumerate(self.groups):
-                ev = self._ev_begin()
                 K.kvc_decode_attn(c, qpool[layers[0], s], [slot] * len(layers), out[layers[0]],
                                   lsepool[layers[0], s], self.ws_attn, k_new=knew[s, slot],
                                   v_new=vnew[s, slot], append_slot=slot,
                                   q_layer_stride=n_steps * nb * hq * d,
                                   out_layer_stride=nb * hq * d,
                                   lse_layer_stride=n_steps * nb * hq, n_q_heads=hq)
-                self._ev_end(ev, c, len(layers))
+            self._ev_end(ev, c, len(self.groups))
         e = self.evict_cfg
         if e and (s + 1) % e["period"] == 0 and c.t_len > e["K"] + e["B"]:
             w = e["w"]
@@ -151,9 +150,11 @@ class Decoder:
         e.record()
         return e
 
-    def _ev_end(self, ev, c, n_q_layers):
+    def _ev_end(self, ev, c, n_calls):
+        """Close the event pair around one step's attention calls (the
+        eviction pass, if any, runs after it)."""
         if ev is None:
             return
         e = torch.cuda.Event(enable_timing=True)
         e.record()
-        self.events.append((ev, e, c.t_len, n_q_layers))
+        self.events.append((ev, e, c.t_len, n_calls))
