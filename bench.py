@@ -132,6 +132,22 @@ def cpu_baseline(cfg, cache, qpool, s, budget_s=8.0):
                 cpu_model=_cpu_model(), host_cores=len(os.sched_getaffinity(0)))
 
 
+def load_traffic(bytes_per_launch):
+    """HBM traffic per attention call from the committed counter summary,
+    or None when the attention source has changed since it was measured."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attn_traffic_llama31_8b_combined.json")
+    src = os.path.join(ROOT, "decode_attention_kvc_amd", "csrc", "attn.hip")
+    try:
+        t = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None, None
+    if t.get("attn_source_sha256") != sha:
+        return None, None
+    return round(t["traffic_over_algorithmic"] * bytes_per_launch), t
+
+
 def _cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -276,11 +292,19 @@ def main():
         log(f"[bench] grouped: {grouped}")
 
     if args.copy_calibration:
-        x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        # Two plain copies of known size for scaling the memory counters:
+        # a 1 GiB runtime blit, and a 512 MiB float32 copy done by a
+        # vectorized elementwise kernel (16-byte loads, like the kernels
+        # here).
+        x = torch.zeros(1 << 30, dtype=torch.uint8, device=dev)
         y = torch.empty_like(x)
         y.copy_(x)
+        a = torch.zeros(1 << 27, dtype=torch.float32, device=dev)
+        c = torch.empty_like(a)
+        torch.mul(a, 1.0, out=c)
         torch.cuda.synchronize()
-        log("[bench] copy calibration: 1 GiB read + 1 GiB write done")
+        del x, y, a, c
+        log("[bench] copy calibration done: 1 GiB blit, 512 MiB vectorized copy")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -288,6 +312,7 @@ def main():
         cpu = cpu_baseline(cfg, dec.cache, qpool, W + S - 1)
         log(f"[bench] cpu baseline: {cpu}")
 
+    traffic, tinfo = load_traffic(sum(att_bytes) / n_calls)
     res = {
         "metric": METRIC,
         "value": round(tok_s, 2),
@@ -318,7 +343,8 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(att_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_source": None if tinfo is None else tinfo["summary"],
             "avg_launch_us": round(avg_launch_us, 3),
             "launches": n_calls,
             "bytes_per_launch": round(sum(att_bytes) / n_calls),
