@@ -47,41 +47,6 @@ const char* slot_v(const kvc_cache* c, int slot) {
 
 int hip_status() { return hipGetLastError() == hipSuccess ? KVC_OK : KVC_EHIP; }
 
-// Tuning knob for experiments: workgroups an attention launch aims for.
-int attn_target_wgs() {
-    static int v = [] {
-        const char* e = getenv("KVC_ATTN_TARGET_WGS");
-        const int x = e ? atoi(e) : 0;
-        return x > 0 ? x : 256;
-    }();
-    return v;
-}
-
-static int env_int(const char* name, int dflt) {
-    const char* e = getenv(name);
-    return e ? atoi(e) : dflt;
-}
-int attn_waves() {
-    static int v = env_int("KVC_ATTN_WAVES", 4) == 8 ? 8 : 4;
-    return v;
-}
-int attn_prefetch() {
-    static int v = env_int("KVC_ATTN_PREFETCH", 1) ? 1 : 0;
-    return v;
-}
-
-
-
-// Tuning knob for experiments: how split partials are merged (see attn.hip).
-int attn_combine_mode() {
-    static int v = [] {
-        const char* e = getenv("KVC_ATTN_COMBINE");
-        const int x = e ? atoi(e) : 0;
-        return (x >= 0 && x <= 2) ? x : 0;
-    }();
-    return v;
-}
-
 // ---- attention planning ----------------------------------------------------
 struct AttnPlan {
     int nt, rp, nsplit, tps;
@@ -99,11 +64,11 @@ AttnPlan plan_attn(int dtype, int rows, int t_len, int slabs) {
         pl.nt = rows <= 16 ? 1 : rows <= 32 ? 2 : 4;
         pl.rp = 16 * pl.nt;
         tile = ATTN_TILE;
-        min_tps = (pl.nt == 1 && attn_combine_mode() == 0) ? attn_waves() : ATTN_WAVES;
+        min_tps = ATTN_WAVES;   // at least one tile per wave
     }
     const int ntiles = std::max(1, (t_len + tile - 1) / tile);
     const long long work = (long long)ntiles * std::max(1, slabs);
-    int tps = (int)std::max<long long>(min_tps, (work + attn_target_wgs() - 1) / attn_target_wgs());
+    int tps = (int)std::max<long long>(min_tps, (work + ATTN_TARGET_WGS - 1) / ATTN_TARGET_WGS);
     int nsplit = (ntiles + tps - 1) / tps;
     const int cap = MAX_SPLIT_ROWS / pl.rp;
     if (nsplit > cap) {
@@ -132,7 +97,7 @@ size_t attn_ws_total(const kvc_cache* c, int rows) {
     for (int t = 1; t <= std::max(1, c->t_cap); t += (c->dtype == KVC_F32 ? ATTN_TILE_F32 : ATTN_TILE))
         part = std::max(part, attn_ws_for(c->dtype, rows, t, slabs));
     part = std::max(part, attn_ws_for(c->dtype, rows, std::max(1, c->t_cap), slabs));
-    return align_up((size_t)slabs * sizeof(uint32_t), 256) + part;
+    return part;
 }
 
 // ---- score planning --------------------------------------------------------
@@ -154,14 +119,13 @@ ScorePlan plan_score(int dtype, int rows, int t_len, int slabs) {
 }
 
 struct ScoreWs {
-    size_t cnt_off, lse_off, stats_off, total;
+    size_t lse_off, stats_off, total;
 };
 
 ScoreWs score_ws_layout(int dtype, int rows, int t_len, int slabs) {
     const ScorePlan pl = plan_score(dtype, rows, t_len, slabs);
     ScoreWs w;
-    w.cnt_off = 0;
-    w.lse_off = align_up((size_t)slabs * sizeof(uint32_t), 256);
+    w.lse_off = 0;
     w.stats_off = w.lse_off + align_up((size_t)slabs * pl.rows_pad * sizeof(float), 256);
     w.total = w.stats_off + (size_t)slabs * pl.nsplit * pl.rows_pad * 2 * sizeof(float);
     return w;
@@ -320,12 +284,8 @@ int kvc_decode_attn(const kvc_cache* c, const void* q, int64_t q_layer_stride, i
             p.rp = pl.rp;
             p.nsplit = pl.nsplit;
             p.tps = pl.tps;
-            p.waves = attn_waves();
-            p.prefetch = attn_prefetch();
-            p.cnt = static_cast<uint32_t*>(ws);
-            p.part = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                              align_up((size_t)slabs * sizeof(uint32_t), 256));
-            if (launch_attn(p, c->dtype, pl.nt, attn_combine_mode(), s) != hipSuccess) return KVC_EHIP;
+            p.part = static_cast<float*>(ws);
+            if (launch_attn(p, c->dtype, pl.nt, s) != hipSuccess) return KVC_EHIP;
             if (p.append_write) append_done = true;
         }
     }
@@ -408,7 +368,6 @@ int kvc_score(const kvc_cache* c, int slot, const void* q_obs, int n_q_heads, in
     p.rows_pad = pl.rows_pad;
     if (!lse_obs) {
         char* base = static_cast<char*>(ws);
-        p.cnt = reinterpret_cast<uint32_t*>(base + lay.cnt_off);
         p.lse_ws = reinterpret_cast<float*>(base + lay.lse_off);
         p.stats = reinterpret_cast<float*>(base + lay.stats_off);
     }

@@ -21,9 +21,11 @@
 // holds is exactly its P^T operand fragment for the V^T product: no data
 // movement between the two products.
 // The four waves merge through LDS; each workgroup writes one partial
-// (m, l, acc) per query row; the last workgroup of a slab to finish (an
-// arrival counter in the workspace, reset by that workgroup) merges all
-// partials with log-sum-exp weights and writes out / lse.
+// (m, l, acc) per query row, and a second, small kernel merges each slab's
+// partials with log-sum-exp weights and writes out / lse.  (Merging in the
+// last workgroup to finish would need an agent-scope release per
+// workgroup, which on this multi-XCD part is an L2 writeback each time; the
+// separate kernel measured faster at every split count.)
 #include <type_traits>
 
 #include "common.h"
@@ -65,101 +67,8 @@ __device__ __forceinline__ void load_tile(TileRegs& R, const uint16_t* kslab,
 
 __device__ __forceinline__ bf16x8 as_bf(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
-// How the nsplit partials of a slab meet (template parameter CM):
-//   CM_KERNEL: plain stores; a second kernel merges them after this one.
-//   CM_FENCE:  agent-scope release fence before the arrival counter and an
-//              agent-scope acquire fence in the last workgroup (on this part
-//              that is an L2 writeback / invalidate per workgroup).
-//   CM_SC1:    partial stores and the merging loads are agent-scope atomic
-//              accesses, which are coherent across the XCDs' L2s by
-//              themselves; a completion wait orders the stores before the
-//              arrival counter, so no L2-wide maintenance is issued.
-enum { CM_KERNEL = 0, CM_FENCE = 1, CM_SC1 = 2 };
-
-template <int CM>
-__device__ __forceinline__ void st_part(float* p, float v) {
-    if constexpr (CM == CM_SC1) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else *p = v;
-}
-template <int CM>
-__device__ __forceinline__ float ld_part(const float* p) {
-    if constexpr (CM == CM_SC1) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else return *p;
-}
-
-// Merge the nsplit partials of one slab and write out / lse.
-// LDS `wgt` holds nsplit * rp floats.
-template <int CM>
-__device__ void combine_slab(const AttnLaunch& p, int slab, int b, int j, float* wgt) {
-    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
-    const int nsplit = p.nsplit, rp = p.rp;
-    const size_t slabs = (size_t)p.nb * p.hkv;
-    const float* acc = p.part + (size_t)slab * nsplit * rp * D;
-    const float* ml = p.part + slabs * nsplit * rp * D + (size_t)slab * nsplit * rp * 2;
-    const int nwaves = blockDim.x / WAVE;
-    for (int r = wave; r < p.rows; r += nwaves) {
-        float m = -INFINITY;
-        for (int s = lane; s < nsplit; s += WAVE) m = fmaxf(m, ld_part<CM>(&ml[((size_t)s * rp + r) * 2]));
-        m = wave_max(m);
-        float l = 0.f;
-        for (int s = lane; s < nsplit; s += WAVE) {
-            const float ms = ld_part<CM>(&ml[((size_t)s * rp + r) * 2]);
-            const float e = exp2f((ms - m) * LOG2E);
-            wgt[s * rp + r] = e;
-            l += e * ld_part<CM>(&ml[((size_t)s * rp + r) * 2 + 1]);
-        }
-        l = wave_sum(l);
-        const float inv = 1.f / l;
-        for (int s = lane; s < nsplit; s += WAVE) wgt[s * rp + r] *= inv;
-        if (lane == 0 && p.lse) {
-            const int qi = r / p.g, h = j * p.g + r % p.g;
-            p.lse[p.lse_off[qi] + (size_t)b * p.hq + h] = m + logf(l);
-        }
-    }
-    __syncthreads();
-    for (int idx = tid; idx < p.rows * D; idx += blockDim.x) {
-        const int r = idx / D, d = idx % D;
-        float o = 0.f;
-        int s = 0;
-        for (; s + 4 <= nsplit; s += 4) {
-            const float a0 = ld_part<CM>(&acc[((size_t)(s + 0) * rp + r) * D + d]);
-            const float a1 = ld_part<CM>(&acc[((size_t)(s + 1) * rp + r) * D + d]);
-            const float a2 = ld_part<CM>(&acc[((size_t)(s + 2) * rp + r) * D + d]);
-            const float a3 = ld_part<CM>(&acc[((size_t)(s + 3) * rp + r) * D + d]);
-            o += wgt[(s + 0) * rp + r] * a0;
-            o += wgt[(s + 1) * rp + r] * a1;
-            o += wgt[(s + 2) * rp + r] * a2;
-            o += wgt[(s + 3) * rp + r] * a3;
-        }
-        for (; s < nsplit; ++s) o += wgt[s * rp + r] * ld_part<CM>(&acc[((size_t)s * rp + r) * D + d]);
-        const int qi = r / p.g, h = j * p.g + r % p.g;
-        p.out[p.out_off[qi] + ((size_t)b * p.hq + h) * D + d] = o;
-    }
-}
-
-// Publish this workgroup's partial and let the last one to arrive merge
-// (CM_FENCE, CM_SC1); with CM_KERNEL the merge is a separate launch.
-template <int CM>
-__device__ void arrive_and_combine(const AttnLaunch& p, int slab, int b, int j, float* wgt) {
-    if constexpr (CM == CM_KERNEL) return;
-    __shared__ int last;
-    if constexpr (CM == CM_FENCE) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    else __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t old = atomicAdd(&p.cnt[slab], 1u);
-        last = (old == (uint32_t)(p.nsplit - 1));
-    }
-    __syncthreads();
-    if (!last) return;
-    if constexpr (CM == CM_FENCE) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    else __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    combine_slab<CM>(p, slab, b, j, wgt);
-    if (threadIdx.x == 0) p.cnt[slab] = 0u;
-}
-
-// Separate merge launch for CM_KERNEL: one workgroup per slab; each thread
-// owns one query row and 8 channels and folds the splits in order with
+// Merge kernel: one workgroup per slab; each thread owns one query row and
+// 8 channels and folds the splits in order with
 // running log-sum-exp weights, so all of a split's loads are independent
 // and no barrier or LDS round trip is needed.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch p) {
@@ -215,7 +124,7 @@ __device__ void write_append_row(const AttnLaunch& p, int b, int j) {
     }
 }
 
-template <int NT, int CM, int W, int PF>
+template <int NT, int W, int PF>
 __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(AttnLaunch p) {
     constexpr int RP = 16 * NT;
     const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
@@ -393,7 +302,7 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(AttnLaunch p) {
 
     // Merge the four waves through LDS, one 16-row block at a time, and
     // write this workgroup's partial.
-    __shared__ float buf[W * 16 * D];   // also the combine weights
+    __shared__ float buf[W * 16 * D];
     __shared__ float wm[W][16], wl[W][16];
     constexpr int EPT = 2048 / (W * 64);  // merged outputs per thread (16 rows x 128)
     const size_t slabs = (size_t)p.nb * p.hkv;
@@ -430,28 +339,21 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(AttnLaunch p) {
                 o[e] = a;
             }
             float* dst = part_acc + (size_t)(nt * 16 + n) * D + d0;
-            if constexpr (CM == CM_SC1) {
 #pragma unroll
-                for (int e = 0; e < EPT; ++e) st_part<CM>(dst + e, o[e]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < EPT; e += 4)
-                    *reinterpret_cast<f32x4*>(dst + e) = f32x4{o[e], o[e + 1], o[e + 2], o[e + 3]};
-            }
+            for (int e = 0; e < EPT; e += 4)
+                *reinterpret_cast<f32x4*>(dst + e) = f32x4{o[e], o[e + 1], o[e + 2], o[e + 3]};
             if (d0 == 0) {
-                st_part<CM>(&part_ml[(nt * 16 + n) * 2], M);
-                st_part<CM>(&part_ml[(nt * 16 + n) * 2 + 1], L);
+                part_ml[(nt * 16 + n) * 2] = M;
+                part_ml[(nt * 16 + n) * 2 + 1] = L;
             }
         }
         __syncthreads();
     }
 
     if (p.append_write && s == p.nsplit - 1) write_append_row<uint16_t>(p, b, j);
-    arrive_and_combine<CM>(p, slab, b, j, buf);
 }
 
 // float32 path: plain VALU arithmetic, up to 16 query rows per launch.
-template <int CM>
 __global__ __launch_bounds__(256) void attn_f32_kernel(AttnLaunch p) {
     constexpr int TT = ATTN_TILE_F32;
     const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
@@ -470,7 +372,6 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnLaunch p) {
     __shared__ float qs[16][D];
     __shared__ float Sx[16][TT + 1];
     __shared__ float mrow[16], lrow[16], arow[16];
-    __shared__ float wgt[MAX_SPLIT_ROWS];
 
     for (int idx = tid; idx < 16 * D; idx += blockDim.x) {
         const int r = idx / D, d = idx % D;
@@ -573,13 +474,12 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnLaunch p) {
     float* part_acc = p.part + ((size_t)slab * p.nsplit + s) * 16 * D;
     float* part_ml = p.part + slabs * p.nsplit * 16 * D + ((size_t)slab * p.nsplit + s) * 16 * 2;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) st_part<CM>(&part_acc[(size_t)(half + 2 * k) * D + d], acc[k]);
+    for (int k = 0; k < 8; ++k) part_acc[(size_t)(half + 2 * k) * D + d] = acc[k];
     if (tid < 16) {
-        st_part<CM>(&part_ml[tid * 2], mrow[tid]);
-        st_part<CM>(&part_ml[tid * 2 + 1], lrow[tid]);
+        part_ml[tid * 2] = mrow[tid];
+        part_ml[tid * 2 + 1] = lrow[tid];
     }
     if (p.append_write && s == p.nsplit - 1) write_append_row<float>(p, b, j);
-    arrive_and_combine<CM>(p, slab, b, j, wgt);
 }
 
 template <typename T>
@@ -595,37 +495,18 @@ __global__ __launch_bounds__(128) void append_kernel(T* k, T* v, int hkv, int t_
 
 }  // namespace
 
-template <int CM>
-static void launch_attn_cm(const AttnLaunch& p, int dtype, int nt, hipStream_t st) {
+hipError_t launch_attn(const AttnLaunch& p, int dtype, int nt, hipStream_t st) {
     const dim3 grid(p.nsplit, p.hkv, p.nb);
     if (dtype == 0) {
-        hipLaunchKernelGGL(attn_f32_kernel<CM>, grid, dim3(256), 0, st, p);
+        hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(256), 0, st, p);
     } else if (nt == 1) {
-        if constexpr (CM == CM_KERNEL) {
-            if (p.waves == 8 && p.prefetch)
-                hipLaunchKernelGGL((attn_bf16_kernel<1, CM, 8, 1>), grid, dim3(512), 0, st, p);
-            else if (p.waves == 8)
-                hipLaunchKernelGGL((attn_bf16_kernel<1, CM, 8, 0>), grid, dim3(512), 0, st, p);
-            else if (p.prefetch)
-                hipLaunchKernelGGL((attn_bf16_kernel<1, CM, 4, 1>), grid, dim3(256), 0, st, p);
-            else
-                hipLaunchKernelGGL((attn_bf16_kernel<1, CM, 4, 0>), grid, dim3(256), 0, st, p);
-        } else {
-            hipLaunchKernelGGL((attn_bf16_kernel<1, CM, 4, 0>), grid, dim3(256), 0, st, p);
-        }
+        hipLaunchKernelGGL((attn_bf16_kernel<1, ATTN_WAVES, 1>), grid, dim3(ATTN_WAVES * 64), 0, st, p);
     } else if (nt == 2) {
-        hipLaunchKernelGGL((attn_bf16_kernel<2, CM, 4, 0>), grid, dim3(256), 0, st, p);
+        hipLaunchKernelGGL((attn_bf16_kernel<2, ATTN_WAVES, 1>), grid, dim3(ATTN_WAVES * 64), 0, st, p);
     } else {
-        hipLaunchKernelGGL((attn_bf16_kernel<4, CM, 4, 0>), grid, dim3(256), 0, st, p);
+        hipLaunchKernelGGL((attn_bf16_kernel<4, ATTN_WAVES, 1>), grid, dim3(ATTN_WAVES * 64), 0, st, p);
     }
-    if constexpr (CM == CM_KERNEL)
-        hipLaunchKernelGGL(attn_combine_kernel, dim3(p.hkv, p.nb), dim3(256), 0, st, p);
-}
-
-hipError_t launch_attn(const AttnLaunch& p, int dtype, int nt, int combine, hipStream_t st) {
-    if (combine == CM_FENCE) launch_attn_cm<CM_FENCE>(p, dtype, nt, st);
-    else if (combine == CM_SC1) launch_attn_cm<CM_SC1>(p, dtype, nt, st);
-    else launch_attn_cm<CM_KERNEL>(p, dtype, nt, st);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(p.hkv, p.nb), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 

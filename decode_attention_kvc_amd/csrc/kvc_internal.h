@@ -11,7 +11,8 @@ constexpr int MAX_QL = 64;       // q-layers served by one attention launch
 constexpr int ATTN_TILE = 32;    // cache rows per attention step (bf16 path)
 constexpr int ATTN_TILE_F32 = 64;
 constexpr int ATTN_WAVES = 4;    // waves per attention workgroup
-constexpr int MAX_SPLIT_ROWS = 4096;  // nsplit * padded rows (combine weights)
+constexpr int ATTN_TARGET_WGS = 256;  // partial workgroups an attention launch aims for
+constexpr int MAX_SPLIT_ROWS = 4096;  // bound on nsplit * padded rows (workspace size)
 constexpr int SCORE_TILE = 32;
 constexpr int SCORE_MAX_TPS = 16;     // tiles per score workgroup
 constexpr int SELECT_THREADS = 1024;
@@ -36,9 +37,7 @@ struct AttnLaunch {
     int append_read;        // row t_len-1 comes from k_new / v_new
     int append_write;       // and is written into the cache
     int nsplit, tps;        // splits per slab, tiles per split
-    int waves, prefetch;    // waves per workgroup, next-tile prefetch
     float* part;            // partial accumulators, then (m, l) pairs
-    uint32_t* cnt;          // one arrival counter per slab
 };
 
 // One observation-window score launch over one cache slot.
@@ -56,7 +55,6 @@ struct ScoreLaunch {
     int nsplit, tps;
     float* stats;           // [slabs][nsplit][rows_pad][2] partial (m, z)
     float* lse_ws;          // [slabs][rows_pad] merged log-normalisers
-    uint32_t* cnt;          // [slabs]
     int rows_pad;
 };
 
@@ -84,9 +82,8 @@ struct CompactLaunch {
 
 // Host-side launchers (defined next to their kernels).  Each returns
 // hipSuccess or the launch error.
-// combine: 0 = separate merge kernel, 1 = fenced last-workgroup merge,
-// 2 = last-workgroup merge through agent-scope atomic accesses.
-hipError_t launch_attn(const AttnLaunch& p, int dtype, int nt, int combine, hipStream_t s);
+// Launches the partial kernel and the merge kernel.
+hipError_t launch_attn(const AttnLaunch& p, int dtype, int nt, hipStream_t s);
 hipError_t launch_append(const void* k, const void* v, int nb, int hkv, int t_len,
                          int t_cap, const void* k_new, const void* v_new, int elem,
                          hipStream_t s);

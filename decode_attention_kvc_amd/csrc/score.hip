@@ -15,10 +15,11 @@
 // workgroup covers all g*w rows of one slab over a range of tiles, and the
 // waves' column sums meet in LDS in a fixed order (deterministic).
 //
-// Without the log-normalisers of the window rows a first pass computes them
-// (per-row online max / sum over the workgroup's tiles, merged across
-// workgroups by the last one to arrive).  The range is fused into the second
-// pass: per tile one wave also reads the tile's token-minor V slice.
+// Without the log-normalisers of the window rows a first pass computes them:
+// per-row online max / sum over each workgroup's tiles, then a small kernel
+// merges the splits' pairs (kernel boundaries order the two, so no
+// cross-workgroup fences are needed).  The range is fused into the second
+// pass: per tile one wave also reads the tile's V block.
 #include "common.h"
 #include "kvc_internal.h"
 
@@ -115,11 +116,13 @@ __device__ __forceinline__ void score_tile_mfma(const QFrag& Q, const uint16_t* 
         }
 }
 
+constexpr float LOG2E = 1.4426950408889634f;
+
 // Merge two (max, sum-of-exp) pairs.
 __device__ __forceinline__ void ms_merge(float& m, float& z, float m2, float z2) {
     const float mn = fmaxf(m, m2);
     if (mn == -INFINITY) return;
-    z = z * expf(m - mn) + z2 * expf(m2 - mn);
+    z = z * exp2f((m - mn) * LOG2E) + z2 * exp2f((m2 - mn) * LOG2E);
     m = mn;
 }
 
@@ -160,7 +163,8 @@ __global__ __launch_bounds__(1024) void score_stats_bf16(ScoreLaunch p) {
                 if (t0 + 16 + l16 > lim[mt][i]) x1 = -INFINITY;
                 const float mn = fmaxf(m[mt][i], fmaxf(x0, x1));
                 if (mn != -INFINITY) {
-                    z[mt][i] = z[mt][i] * expf(m[mt][i] - mn) + expf(x0 - mn) + expf(x1 - mn);
+                    z[mt][i] = z[mt][i] * exp2f((m[mt][i] - mn) * LOG2E) +
+                               exp2f((x0 - mn) * LOG2E) + exp2f((x1 - mn) * LOG2E);
                     m[mt][i] = mn;
                 }
             }
@@ -186,23 +190,22 @@ __global__ __launch_bounds__(1024) void score_stats_bf16(ScoreLaunch p) {
                 st[R * 2 + 1] = z[mt][i];
             }
     }
-    // The last workgroup of the slab merges every split's pairs into lse.
-    __shared__ int last;
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) last = (atomicAdd(&p.cnt[slab], 1u) == (uint32_t)(p.nsplit - 1));
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
+}
+
+// Merge the splits' (max, sum) pairs of every window row into its
+// log-normaliser; one workgroup per slab, one thread per row, splits folded
+// in order.
+__global__ __launch_bounds__(256) void score_lse_merge(ScoreLaunch p) {
+    const int slab = blockIdx.y * p.hkv + blockIdx.x;
     const float* all = p.stats + (size_t)slab * p.nsplit * p.rows_pad * 2;
-    for (int R = tid; R < p.rows; R += blockDim.x) {
+    for (int R = threadIdx.x; R < p.rows; R += blockDim.x) {
         float mm = -INFINITY, zz = 0.f;
+#pragma unroll 4
         for (int sp = 0; sp < p.nsplit; ++sp)
             ms_merge(mm, zz, all[((size_t)sp * p.rows_pad + R) * 2],
                      all[((size_t)sp * p.rows_pad + R) * 2 + 1]);
         p.lse_ws[(size_t)slab * p.rows_pad + R] = mm + logf(zz);
     }
-    if (tid == 0) p.cnt[slab] = 0u;
 }
 
 // Pass 2: column sums of the window softmax, plus the fused value range.
@@ -304,7 +307,6 @@ __global__ __launch_bounds__(256) void score_f32(ScoreLaunch p, int stats_pass) 
     const float* vslab = reinterpret_cast<const float*>(p.v) + (size_t)slab * p.t_cap * D;
     __shared__ float ks[FT][D + 1];
     __shared__ float csum[4][FT];
-    __shared__ int last;
 
     // Rows rg + 4k, k < 32: at most 128 window rows on this path, so the
     // per-row state stays in registers.
@@ -362,8 +364,8 @@ __global__ __launch_bounds__(256) void score_f32(ScoreLaunch p, int stats_pass) 
         }
     }
     if (!stats_pass) return;
-    // Merge across the 64 cache-row lanes of each row group, then across
-    // splits in the last workgroup.
+    // Merge across the 64 cache-row lanes of each row group; a separate
+    // kernel merges the splits.
     float* st = p.stats + ((size_t)slab * p.nsplit + s) * p.rows_pad * 2;
 #pragma unroll
     for (int k = 0; k < MAXR; ++k) {
@@ -378,21 +380,6 @@ __global__ __launch_bounds__(256) void score_f32(ScoreLaunch p, int stats_pass) 
             st[R * 2 + 1] = zz;
         }
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) last = (atomicAdd(&p.cnt[slab], 1u) == (uint32_t)(p.nsplit - 1));
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
-    const float* all = p.stats + (size_t)slab * p.nsplit * p.rows_pad * 2;
-    for (int R = tid; R < p.rows; R += blockDim.x) {
-        float mm = -INFINITY, zz = 0.f;
-        for (int sp = 0; sp < p.nsplit; ++sp)
-            ms_merge(mm, zz, all[((size_t)sp * p.rows_pad + R) * 2],
-                     all[((size_t)sp * p.rows_pad + R) * 2 + 1]);
-        p.lse_ws[(size_t)slab * p.rows_pad + R] = mm + logf(zz);
-    }
-    if (tid == 0) p.cnt[slab] = 0u;
 }
 
 // Standalone value range: one workgroup of four waves per 512 rows of a
@@ -447,11 +434,17 @@ __global__ __launch_bounds__(256) void value_range_kernel(const E* v, int hkv, i
 hipError_t launch_score(const ScoreLaunch& p, int dtype, hipStream_t st) {
     const dim3 grid(p.nsplit, p.hkv, p.nb);
     if (dtype == 0) {
-        if (!p.lse_obs) hipLaunchKernelGGL(score_f32, grid, dim3(256), 0, st, p, 1);
+        if (!p.lse_obs) {
+            hipLaunchKernelGGL(score_f32, grid, dim3(256), 0, st, p, 1);
+            hipLaunchKernelGGL(score_lse_merge, dim3(p.hkv, p.nb), dim3(256), 0, st, p);
+        }
         hipLaunchKernelGGL(score_f32, grid, dim3(256), 0, st, p, 0);
     } else {
         const int nw = (p.rows + 31) / 32;
-        if (!p.lse_obs) hipLaunchKernelGGL(score_stats_bf16, grid, dim3(nw * WAVE), 0, st, p);
+        if (!p.lse_obs) {
+            hipLaunchKernelGGL(score_stats_bf16, grid, dim3(nw * WAVE), 0, st, p);
+            hipLaunchKernelGGL(score_lse_merge, dim3(p.hkv, p.nb), dim3(256), 0, st, p);
+        }
         hipLaunchKernelGGL(score_main_bf16, grid, dim3(nw * WAVE), 0, st, p);
     }
     return hipGetLastError();

@@ -145,9 +145,8 @@ int kvc_decode_attn_ws_bytes(const kvc_cache* c, int n_q_layers,
  *        out_layer_stride (0 = packed).
  *   lse: device float32 [n_q_layers][nb][n_q_heads] or NULL, layer stride
  *        lse_layer_stride (0 = packed).
- *   ws:  device workspace of at least kvc_decode_attn_ws_bytes bytes, zero
- *        filled before its first use; every call leaves it ready for the
- *        next (its counters return to zero).
+ *   ws:  device workspace of at least kvc_decode_attn_ws_bytes bytes (split
+ *        partials; no initialisation needed).
  * Requires t_len >= 1, n_q_heads a multiple of n_kv_heads, head_dim 128.
  */
 int kvc_decode_attn(const kvc_cache* c, const void* q, int64_t q_layer_stride,
@@ -182,7 +181,8 @@ int kvc_score_ws_bytes(const kvc_cache* c, int n_q_heads, int w,
  *            each window row over its visible rows (as kvc_decode_attn
  *            returned it when the query was decoded, valid when no
  *            compaction happened inside the window), or NULL: then a first
- *            pass computes it and ws is required.
+ *            pass computes it and ws (kvc_score_ws_bytes bytes, no
+ *            initialisation needed) is required.
  *   score:   device float32 [nb][n_kv_heads][t_len].
  *   range:   NULL or device float32 [nb][n_kv_heads][t_len]: the value range
  *            of kvc_value_range, fused into the same pass over the cache.
