@@ -292,3 +292,43 @@ def test_compact_bit_exact(dtype):
     Vr[1, 2, 7] = 0
     assert torch.equal(dst.k_rows(1), Kr)
     assert torch.equal(dst.v_rows(1), Vr)
+
+
+def test_select_sampling_law_gpu():
+    """10^4 draws of the 8-token, k = 3 weighted sampling through kvc_select:
+    every draw equals the oracle's, and the inclusion frequencies and the
+    56-subset distribution match the enumerated law."""
+    import itertools
+    from scipy import stats
+    say("select law")
+    w = np.array([0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, 9.0])
+    W = w.sum()
+    pi = np.zeros(8)
+    psub = {}
+    for a, b_, c in itertools.permutations(range(8), 3):
+        pr = w[a] / W * w[b_] / (W - w[a]) * w[c] / (W - w[a] - w[b_])
+        pi[[a, b_, c]] += pr
+        key = tuple(sorted((a, b_, c)))
+        psub[key] = psub.get(key, 0.0) + pr
+    nbat, calls = 100, 100
+    score = torch.tensor(w, dtype=torch.float32, device=DEV).repeat(nbat, 1, 1)
+    rng = torch.zeros_like(score)
+    kept = torch.empty((nbat, 1, 3), dtype=torch.int32, device=DEV)
+    ws = ws_tensor(kvc.kvc_select_ws_bytes(nbat, 1, 8))
+    freq = np.zeros(8)
+    sub_counts = {k: 0 for k in psub}
+    for seed in range(calls):
+        kvc.kvc_select(score, rng, nbat, 1, 8, 3, 0, 0, seed, 4, kept, ws)
+        torch.cuda.synchronize()
+        kp = kept.cpu().numpy()
+        for b in range(nbat):
+            ref = oracle.select(w, np.zeros(8), 8, 3, 0, 0, seed, 4, b, 0)
+            assert np.array_equal(kp[b, 0], ref), (seed, b)
+            freq[kp[b, 0]] += 1
+            sub_counts[tuple(kp[b, 0].tolist())] += 1
+    n = nbat * calls
+    sigma = np.sqrt(n * pi * (1 - pi))
+    assert np.all(np.abs(freq - n * pi) <= 4 * sigma)
+    obs = np.array([sub_counts[k] for k in psub])
+    exp = np.array([psub[k] for k in psub]) * n
+    assert stats.chi2.sf(((obs - exp) ** 2 / exp).sum(), 55) > 1e-3
