@@ -5,12 +5,21 @@
 // footprint.  dst row i <- src row kept[i] for every slab of the slot, K in
 // [t][d] rows and V in 32-token channel-major tiles, out of place.
 //
-// One workgroup (256 threads) per 256 kept rows of a slab.  K rows are
-// copied with 16-byte accesses, 16 (bf16) or 32 (fp32) lanes per row.  For V
-// each thread owns one kept row and walks the 128 channels; the source
-// indices are ascending, so a wave's reads of one channel fall in a few
-// tiles.  An index outside [0, src t_len) produces a zero row instead
-// of an out-of-bounds read.
+// One workgroup (256 threads) per 256 kept rows of a slab.
+//  * K rows are copied with 16-byte accesses (16 lanes per bf16 row).
+//  * V: the destination rows are taken in rounds of whole destination tiles.
+//    A round covers as many destination tiles as keep the source rows they
+//    need within the staging area's source tiles; those source tiles are
+//    loaded into LDS with coalesced 16-byte loads, and each (destination
+//    tile, channel, 8-row group) is assembled from LDS and written with one
+//    16-byte store.  With the kept rows ascending and dense (a steady-state
+//    eviction keeps ~98% of the rows) a round covers 5 to 8 destination
+//    tiles; sparse selections (a long prompt compressed 4x) take one round
+//    per destination tile.
+// Indices outside [0, src t_len) give zero rows; a row whose source tile is
+// not staged (only possible for indices out of ascending order) is read
+// straight from global memory, so no input can make an access leave the
+// slab.
 #include "common.h"
 #include "kvc_internal.h"
 
@@ -18,11 +27,21 @@ namespace kvc {
 
 namespace {
 
-constexpr int CROWS = 256;
+constexpr int CROWS = 256;                // destination rows per workgroup
+constexpr int LDS_BYTES = 64 * 1024;      // staging budget (two workgroups per CU)
+
+template <typename E>
+struct Stage {
+    static constexpr int VEC = 16 / sizeof(E);         // elements per 16 bytes
+    static constexpr int PITCH = VT + VEC;             // padded channel row (16-byte aligned)
+    static constexpr int TILE = D * PITCH;             // elements per staged tile
+    static constexpr int NT = LDS_BYTES / (TILE * (int)sizeof(E));
+};
 
 template <typename E>
 __global__ __launch_bounds__(256) void compact_kernel(CompactLaunch p) {
-    constexpr int VEC = 16 / sizeof(E);     // elements per 16-byte access
+    using S = Stage<E>;
+    constexpr int VEC = S::VEC;
     constexpr int CPR = D / VEC;            // 16-byte chunks per K row
     const int slab = blockIdx.z * p.hkv + blockIdx.y;
     const int i0 = blockIdx.x * CROWS;
@@ -33,30 +52,139 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactLaunch p) {
     E* dk = reinterpret_cast<E*>(p.dk) + (size_t)slab * p.dst_t_cap * D;
     E* dv = reinterpret_cast<E*>(p.dv) + (size_t)slab * p.dst_t_cap * D;
     const int rows = min(CROWS, p.n_keep - i0);
+    const int src_tiles = (p.src_t_len + VT - 1) / VT;
 
     __shared__ int32_t src_row[CROWS];
-    for (int x = tid; x < rows; x += blockDim.x) {
-        const int32_t r = kept[i0 + x];
-        src_row[x] = (r >= 0 && r < p.src_t_len) ? r : -1;
+    __shared__ __align__(16) E stage[S::NT * S::TILE];
+    for (int x = tid; x < CROWS; x += blockDim.x) {
+        int32_t r = -1;
+        if (x < rows) {
+            r = kept[i0 + x];
+            if (r < 0 || r >= p.src_t_len) r = -1;
+        }
+        src_row[x] = r;
     }
     __syncthreads();
 
-    // K rows
-    for (int x = tid; x < rows * CPR; x += blockDim.x) {
-        const int i = x / CPR, c = x % CPR;
-        const int32_t r = src_row[i];
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (r >= 0) v = load_stream16(sk + (size_t)r * D + c * VEC);
-        *reinterpret_cast<u32x4*>(dk + (size_t)(i0 + i) * D + c * VEC) = v;
-    }
-    // V columns
-    if (tid < rows) {
-        const int32_t r = src_row[tid];
-        for (int d = 0; d < D; ++d) {
-            E v = E(0);
-            if (r >= 0) v = sv[vt_off(r, d)];
-            dv[vt_off(i0 + tid, d)] = v;
+    // V rounds: every thread derives the same round boundaries from
+    // src_row, so the loop and its barriers are uniform across the
+    // workgroup.
+    const int ntile = (rows + VT - 1) / VT;
+    auto first_tile = [&](int a, int b) {       // source tile of the first valid row in [a, b)
+        for (int x = a; x < b; ++x)
+            if (src_row[x] >= 0) return src_row[x] / VT;
+        return -1;
+    };
+    auto last_tile = [&](int a, int b) {
+        for (int x = b - 1; x >= a; --x)
+            if (src_row[x] >= 0) return src_row[x] / VT;
+        return -1;
+    };
+    // Round starting at destination tile k: staged source tiles [lo, lo+n_st)
+    // serve destination tiles [k, k_end).
+    auto plan_round = [&](int k, int& lo, int& n_st, int& k_end) {
+        lo = first_tile(k * VT, min(rows, (k + 1) * VT));
+        int hi = last_tile(k * VT, min(rows, (k + 1) * VT));
+        k_end = k + 1;
+        if (lo >= 0) {
+            while (k_end < ntile) {
+                const int h2 = last_tile(k_end * VT, min(rows, (k_end + 1) * VT));
+                if (h2 >= 0 && h2 - lo + 1 > S::NT) break;
+                if (h2 > hi) hi = h2;
+                ++k_end;
+            }
         }
+        n_st = (lo >= 0 && hi >= lo) ? min(hi - lo + 1, S::NT) : 0;
+    };
+    constexpr int CH_PER_TILE = D * VT / VEC;          // 16-byte chunks per source tile
+    constexpr int SLOADS = (S::NT * CH_PER_TILE + 255) / 256;   // staging loads per thread
+    auto stage_load = [&](int lo, int n_st, u32x4* reg) {
+#pragma unroll
+        for (int u = 0; u < SLOADS; ++u) {
+            const int x = tid + 256 * u;
+            const int tl = x / CH_PER_TILE, c = x % CH_PER_TILE;
+            const int d = c / (VT / VEC), q = c % (VT / VEC);
+            if (tl < n_st && lo + tl < src_tiles)
+                reg[u] = load_stream16(sv + (size_t)(lo + tl) * D * VT + d * VT + q * VEC);
+        }
+    };
+    auto stage_store = [&](int lo, int n_st, const u32x4* reg) {
+#pragma unroll
+        for (int u = 0; u < SLOADS; ++u) {
+            const int x = tid + 256 * u;
+            const int tl = x / CH_PER_TILE, c = x % CH_PER_TILE;
+            const int d = c / (VT / VEC), q = c % (VT / VEC);
+            if (tl < n_st && lo + tl < src_tiles)
+                *reinterpret_cast<u32x4*>(&stage[tl * S::TILE + d * S::PITCH + q * VEC]) = reg[u];
+        }
+    };
+
+    // K rows and the first V round's staging loads are all issued before
+    // any of them is used: one memory round trip for the common case.
+    constexpr int KLOADS = CROWS * CPR / 256;           // K chunks per thread
+    u32x4 kreg[KLOADS];
+#pragma unroll
+    for (int u = 0; u < KLOADS; ++u) {
+        const int x = tid + 256 * u;
+        const int i = x / CPR, c = x % CPR;
+        const int32_t r = i < rows ? src_row[i] : -1;
+        kreg[u] = u32x4{0u, 0u, 0u, 0u};
+        if (r >= 0) kreg[u] = load_stream16(sk + (size_t)r * D + c * VEC);
+    }
+    int lo, n_st, k_end;
+    plan_round(0, lo, n_st, k_end);
+    u32x4 sreg[SLOADS];
+    stage_load(lo, n_st, sreg);
+#pragma unroll
+    for (int u = 0; u < KLOADS; ++u) {
+        const int x = tid + 256 * u;
+        const int i = x / CPR, c = x % CPR;
+        if (i < rows) *reinterpret_cast<u32x4*>(dk + (size_t)(i0 + i) * D + c * VEC) = kreg[u];
+    }
+
+    int k = 0;
+    while (k < ntile) {
+        if (k > 0) {
+            plan_round(k, lo, n_st, k_end);
+            stage_load(lo, n_st, sreg);
+        }
+        stage_store(lo, n_st, sreg);
+        __syncthreads();
+        // assemble destination tiles [k, k_end)
+        constexpr int GROUPS = VT / VEC;                // 16-byte groups per channel row
+        const int items = (k_end - k) * D * GROUPS;
+        for (int x = tid; x < items; x += blockDim.x) {
+            const int q = x % GROUPS, d = (x / GROUPS) % D, kk = k + x / (GROUPS * D);
+            const int base = kk * VT + q * VEC;         // first destination row of the group
+            union {
+                E e[VEC];
+                u32x4 v;
+            } vals;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const int i = base + e;
+                E v = E(0);
+                if (i < rows) {
+                    const int32_t r = src_row[i];
+                    if (r >= 0) {
+                        const int tl = r / VT - lo;
+                        if (tl >= 0 && tl < n_st) v = stage[tl * S::TILE + d * S::PITCH + (r % VT)];
+                        else v = sv[vt_off(r, d)];
+                    }
+                }
+                vals.e[e] = v;
+            }
+            const int di = i0 + base;                   // destination row of vals.e[0]
+            if (base + VEC <= rows) {
+                *reinterpret_cast<u32x4*>(dv + vt_off(di, d)) = vals.v;
+            } else {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    if (base + e < rows) dv[vt_off(di + e, d)] = vals.e[e];
+            }
+        }
+        __syncthreads();
+        k = k_end;
     }
 }
 
