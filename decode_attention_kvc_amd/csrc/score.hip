@@ -29,6 +29,27 @@ namespace {
 
 __device__ __forceinline__ bf16x8 as_bf(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
+// Lane permutation inside a 16-lane row (DPP, a plain VALU move).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// Max / min over the 16 lanes of a row; every lane of the row gets it.
+// Swap neighbours, swap pairs, mirror the half-rows, mirror the row.
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_mov<0xB1>(v));
+    v = fmaxf(v, dpp_mov<0x4E>(v));
+    v = fmaxf(v, dpp_mov<0x141>(v));
+    return fmaxf(v, dpp_mov<0x140>(v));
+}
+__device__ __forceinline__ float row16_min(float v) {
+    v = fminf(v, dpp_mov<0xB1>(v));
+    v = fminf(v, dpp_mov<0x4E>(v));
+    v = fminf(v, dpp_mov<0x141>(v));
+    return fminf(v, dpp_mov<0x140>(v));
+}
+
 // Range of the 32 rows t0..t0+31 of one slab from its token-minor V slice;
 // one wave.  Lane (l16, lg) reads channels 16*dt + l16 of rows
 // t0 + 8*lg .. +8.
@@ -54,12 +75,9 @@ __device__ __forceinline__ void range_tile_bf16(const uint16_t* vslab, int t0, i
         }
     }
 #pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            mx[jj] = fmaxf(mx[jj], __shfl_xor(mx[jj], m));
-            mn[jj] = fminf(mn[jj], __shfl_xor(mn[jj], m));
-        }
+    for (int jj = 0; jj < 8; ++jj) {
+        mx[jj] = row16_max(mx[jj]);
+        mn[jj] = row16_min(mn[jj]);
     }
     if (l16 == 0) {
 #pragma unroll
