@@ -16,7 +16,9 @@
 // 8-bit digits with LDS histograms find the k-th key; rows strictly before
 // it are in, rows equal to it are taken in ascending row order.  The kept
 // rows are emitted in ascending order with block-wide ordered scans.
-// Float keys of the sampling step live in a workspace (one uint32 per row).
+// The keys (first the range keys, then, in place, the sampling keys) live in
+// LDS when the slab has at most LDS_KEYS rows, otherwise in the caller's
+// workspace (one uint32 per row); all accesses stay inside one workgroup.
 #include "common.h"
 #include "kvc_internal.h"
 #include "philox.h"
@@ -28,6 +30,7 @@ namespace {
 constexpr int NT = SELECT_THREADS;
 constexpr int NWV = NT / WAVE;
 constexpr uint32_t EXCLUDED = 0xFFFFFFFFu;   // above every float key
+constexpr int LDS_KEYS = 36 * 1024;           // 144 KB of keys
 
 struct SelectSmem {
     uint32_t hist[256];
@@ -121,8 +124,10 @@ __device__ __forceinline__ uint32_t sample_key(const SelectLaunch& p, int t, int
     return __float_as_uint(kappa);
 }
 
+template <bool IN_LDS>
 __global__ __launch_bounds__(NT) void select_kernel(SelectLaunch p) {
     __shared__ SelectSmem sm;
+    __shared__ uint32_t lds_keys[IN_LDS ? LDS_KEYS : 1];
     const int slab = blockIdx.x;
     const int b = slab / p.hkv, j = slab % p.hkv;
     const int tid = threadIdx.x;
@@ -136,23 +141,25 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectLaunch p) {
     }
     const float* score = p.score + (size_t)slab * T;
     const float* range = p.range + (size_t)slab * T;
-    uint32_t* keys = p.keys + (size_t)slab * T;
+    uint32_t* keys = IN_LDS ? lds_keys : p.keys + (size_t)slab * T;
     const int ncand = T - p.recent_b;
 
     // 1. N_v candidates of largest range (ties to the lower row).
     uint32_t rthr = 0, rtake = 0;
-    if (p.n_v > 0)
-        rthr = radix_select(
-            ncand, (uint32_t)p.n_v, [&](int t) { return range_key(range[t]); }, sm, &rtake);
+    if (p.n_v > 0) {
+        for (int t = tid; t < ncand; t += NT) keys[t] = range_key(range[t]);
+        __syncthreads();
+        rthr = radix_select(ncand, (uint32_t)p.n_v, [&](int t) { return keys[t]; }, sm, &rtake);
+    }
 
-    // 2. Sampling keys for the remaining candidates; protected rows are
-    //    marked EXCLUDED.  Ordered pass: equal-range rows are protected in
-    //    row order.
+    // 2. Sampling keys for the remaining candidates, written over the range
+    //    keys; protected rows are marked EXCLUDED.  Ordered pass: equal-range
+    //    rows are protected in row order.
     uint32_t eq_seen = 0;
     for (int base = 0; base < ncand; base += NT) {
         const int t = base + tid;
         const bool valid = t < ncand;
-        const uint32_t rk = valid ? range_key(range[t]) : 0xFFFFFFFFu;
+        const uint32_t rk = (valid && p.n_v > 0) ? keys[t] : 0xFFFFFFFFu;
         const bool eq = valid && p.n_v > 0 && rk == rthr;
         uint32_t tot;
         const uint32_t rank = eq_seen + block_scan_flag(eq, sm, &tot);
@@ -162,7 +169,6 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectLaunch p) {
             keys[t] = prot ? EXCLUDED : sample_key(p, t, j, b, score[t]);
         }
     }
-    __threadfence();
     __syncthreads();
 
     // 3. K - N_v smallest sampling keys.
@@ -209,7 +215,10 @@ __global__ void philox_kernel(int64_t n, uint32_t c1, uint32_t c2, uint32_t c3, 
 }  // namespace
 
 hipError_t launch_select(const SelectLaunch& p, hipStream_t st) {
-    hipLaunchKernelGGL(select_kernel, dim3(p.nb * p.hkv), dim3(NT), 0, st, p);
+    if (p.t_len <= LDS_KEYS)
+        hipLaunchKernelGGL(select_kernel<true>, dim3(p.nb * p.hkv), dim3(NT), 0, st, p);
+    else
+        hipLaunchKernelGGL(select_kernel<false>, dim3(p.nb * p.hkv), dim3(NT), 0, st, p);
     return hipGetLastError();
 }
 
