@@ -58,7 +58,7 @@ def attn_bytes(nb, hq, hkv, t_len, n_q_layers, lead):
 
 def step_attn_bytes(dec, mode, nb, hq, hkv, t_len):
     """Algorithmic bytes of one step's attention calls."""
-    if mode == "per-layer":
+    if mode != "grouped":
         return sum(attn_bytes(nb, hq, hkv, t_len, 1, dec.src_layer[l] == l)
                    for l in range(dec.n_layers))
     return sum(attn_bytes(nb, hq, hkv, t_len, len(g), True) for g in dec.groups)
@@ -164,7 +164,10 @@ def main():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3.1-8b-combined", choices=list(WORKLOADS))
-    ap.add_argument("--mode", default="per-layer", choices=["per-layer", "grouped"])
+    ap.add_argument("--mode", default="per-layer",
+                    choices=["per-layer", "per-layer-interleaved", "grouped"],
+                    help="per-layer-interleaved issues the same calls round-robin over the "
+                         "slots, so no call can find its slab in the Infinity Cache")
     ap.add_argument("--no-grouped", action="store_true", help="skip the grouped-mode leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -273,7 +276,7 @@ def main():
     step_gbps = step_bytes / wall / 1e9
 
     grouped = None
-    if not args.no_grouped and args.mode == "per-layer" and n_slots < L:
+    if not args.no_grouped and args.mode != "grouped" and n_slots < L:
         first = W + S
         torch.cuda.synchronize()
         g0 = time.perf_counter()

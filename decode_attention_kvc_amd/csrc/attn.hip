@@ -22,7 +22,9 @@
 // movement between the two products.
 // The four waves merge through LDS; each workgroup writes one partial
 // (m, l, acc) per query row, and a second, small kernel merges each slab's
-// partials with log-sum-exp weights and writes out / lse.  (Merging in the
+// partials with log-sum-exp weights and writes out / lse.  When a launch has
+// one split per slab the workgroup normalises its rows itself and the merge
+// kernel is not launched.  (Merging in the
 // last workgroup to finish would need an agent-scope release per
 // workgroup, which on this multi-XCD part is an L2 writeback each time; the
 // separate kernel measured faster at every split count.)
@@ -305,6 +307,16 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(AttnLaunch p) {
     __shared__ float buf[W * 16 * D];
     __shared__ float wm[W][16], wl[W][16];
     constexpr int EPT = 2048 / (W * 64);  // merged outputs per thread (16 rows x 128)
+    auto store_ept = [](float* dst, const float* o) {
+        if constexpr (EPT % 4 == 0) {
+#pragma unroll
+            for (int e = 0; e < EPT; e += 4)
+                *reinterpret_cast<f32x4*>(dst + e) = f32x4{o[e], o[e + 1], o[e + 2], o[e + 3]};
+        } else {
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) dst[e] = o[e];
+        }
+    };
     const size_t slabs = (size_t)p.nb * p.hkv;
     float* part_acc = p.part + ((size_t)slab * p.nsplit + s) * RP * D;
     float* part_ml = p.part + slabs * p.nsplit * RP * D + ((size_t)slab * p.nsplit + s) * RP * 2;
@@ -338,13 +350,24 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(AttnLaunch p) {
                 for (int w = 0; w < W; ++w) a += f[w] * buf[(w * 16 + n) * D + d0 + e];
                 o[e] = a;
             }
-            float* dst = part_acc + (size_t)(nt * 16 + n) * D + d0;
+            const int r = nt * 16 + n;
+            if (p.nsplit == 1) {
+                // The whole slab is this workgroup's: finish the rows here.
+                if (r < p.rows) {
+                    const float inv = 1.f / L;
+                    const int qi = r / p.g, h = j * p.g + r % p.g;
+                    float* dst = p.out + p.out_off[qi] + ((size_t)b * p.hq + h) * D + d0;
 #pragma unroll
-            for (int e = 0; e < EPT; e += 4)
-                *reinterpret_cast<f32x4*>(dst + e) = f32x4{o[e], o[e + 1], o[e + 2], o[e + 3]};
-            if (d0 == 0) {
-                part_ml[(nt * 16 + n) * 2] = M;
-                part_ml[(nt * 16 + n) * 2 + 1] = L;
+                    for (int e = 0; e < EPT; ++e) o[e] *= inv;
+                    store_ept(dst, o);
+                    if (d0 == 0 && p.lse) p.lse[p.lse_off[qi] + (size_t)b * p.hq + h] = M + logf(L);
+                }
+            } else {
+                store_ept(part_acc + (size_t)r * D + d0, o);
+                if (d0 == 0) {
+                    part_ml[r * 2] = M;
+                    part_ml[r * 2 + 1] = L;
+                }
             }
         }
         __syncthreads();
@@ -499,14 +522,18 @@ hipError_t launch_attn(const AttnLaunch& p, int dtype, int nt, hipStream_t st) {
     const dim3 grid(p.nsplit, p.hkv, p.nb);
     if (dtype == 0) {
         hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(256), 0, st, p);
-    } else if (nt == 1) {
-        hipLaunchKernelGGL((attn_bf16_kernel<1, ATTN_WAVES, 1>), grid, dim3(ATTN_WAVES * 64), 0, st, p);
-    } else if (nt == 2) {
-        hipLaunchKernelGGL((attn_bf16_kernel<2, ATTN_WAVES, 1>), grid, dim3(ATTN_WAVES * 64), 0, st, p);
     } else {
-        hipLaunchKernelGGL((attn_bf16_kernel<4, ATTN_WAVES, 1>), grid, dim3(ATTN_WAVES * 64), 0, st, p);
+        auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(ATTN_WAVES * 64), 0, st, p); };
+        if (nt == 1)
+            go(attn_bf16_kernel<1, ATTN_WAVES, 1>);
+        else if (nt == 2)
+            go(attn_bf16_kernel<2, ATTN_WAVES, 1>);
+        else
+            go(attn_bf16_kernel<4, ATTN_WAVES, 1>);
     }
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(p.hkv, p.nb), dim3(256), 0, st, p);
+    // bf16 launches with one split per slab finish their rows themselves.
+    if (dtype == 0 || p.nsplit > 1)
+        hipLaunchKernelGGL(attn_combine_kernel, dim3(p.hkv, p.nb), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 

@@ -25,7 +25,13 @@ class Decoder:
     def __init__(self, n_layers, leaders, cache, spare, n_q_heads, evict=None,
                  mode="per-layer", record_events=False):
         """cache / spare: two Cache objects of the same shape (ping-pong for
-        compaction).  evict: None or dict(K, B, N_v, w, period, seed)."""
+        compaction).  evict: None or dict(K, B, N_v, w, period, seed).
+        mode: "per-layer" (one call per layer, in layer order), "grouped"
+        (one call per leader with all of its followers' queries) or
+        "per-layer-interleaved" (one call per layer, issued round-robin over
+        the slots -- every leader, then every first follower, ... -- so that
+        consecutive calls never read the same slab; each follower still runs
+        after its leader has appended)."""
         self.n_layers = n_layers
         self.leaders = list(leaders)
         self.src_layer, self.src_slot = K.kvc_share_map(n_layers, self.leaders)
@@ -38,7 +44,7 @@ class Decoder:
         dev = cache.k.device
         nb, hkv = cache.nb, cache.n_kv_heads
         # per-layer calls serve one q-layer; grouped calls all followers
-        nql = 1 if mode == "per-layer" else max(self.src_slot.count(s) for s in range(len(leaders)))
+        nql = 1 if mode != "grouped" else max(self.src_slot.count(s) for s in range(len(leaders)))
         self.ws_attn = torch.zeros(max(16, K.kvc_decode_attn_ws_bytes(cache, nql, n_q_heads)),
                                    dtype=torch.uint8, device=dev)
         self.groups = [[l for l in range(n_layers) if self.src_slot[l] == s]
@@ -46,6 +52,11 @@ class Decoder:
         for g in self.groups:
             if g != list(range(g[0], g[0] + len(g))):
                 raise ValueError("grouped mode needs each leader's followers to be contiguous")
+        self.order = {"per-layer": list(range(n_layers)),
+                      "per-layer-interleaved": [g[r] for r in range(max(map(len, self.groups)))
+                                                for g in self.groups if r < len(g)]}
+        if mode not in ("grouped", *self.order):
+            raise ValueError(f"unknown mode {mode!r}")
         self.events = [] if record_events else None
         self._evict_bufs = None
 
@@ -58,8 +69,8 @@ class Decoder:
         n_steps = qpool.shape[1]
         nb, hq, d = qpool.shape[2], qpool.shape[3], qpool.shape[4]
         ev = self._ev_begin()
-        if self.mode == "per-layer":
-            for l in range(self.n_layers):
+        if self.mode != "grouped":
+            for l in self.order[self.mode]:
                 slot = self.src_slot[l]
                 lead = self.src_layer[l] == l
                 K.kvc_decode_attn(c, qpool[l, s], [slot], out[l], lsepool[l, s], self.ws_attn,
