@@ -103,6 +103,7 @@ size_t attn_ws_total(const kvc_cache* c, int rows) {
 // ---- score planning --------------------------------------------------------
 struct ScorePlan {
     int nsplit, tps, rows_pad;
+    int main_nsplit, main_tps;
 };
 
 ScorePlan plan_score(int dtype, int rows, int t_len, int slabs) {
@@ -115,6 +116,14 @@ ScorePlan plan_score(int dtype, int rows, int t_len, int slabs) {
     pl.tps = tps;
     pl.nsplit = (ntiles + tps - 1) / tps;
     pl.rows_pad = dtype == KVC_F32 ? rows : (rows + 31) / 32 * 32;
+    // bf16 score pass: one round of workgroups, as many per CU as registers
+    // (four) and the staged queries' LDS allow, and at least two tiles per
+    // wave so that staging the window queries stays a small overhead.
+    const long long per_cu = std::max<long long>(
+        1, std::min<long long>(4, LDS_PER_CU / (long long)score_main_lds_bytes(rows)));
+    const long long target = per_cu * CU_COUNT;
+    pl.main_tps = (int)std::max<long long>(8, (work + target - 1) / target);
+    pl.main_nsplit = (ntiles + pl.main_tps - 1) / pl.main_tps;
     return pl;
 }
 
@@ -365,6 +374,8 @@ int kvc_score(const kvc_cache* c, int slot, const void* q_obs, int n_q_heads, in
     p.range = range;
     p.nsplit = pl.nsplit;
     p.tps = pl.tps;
+    p.main_nsplit = pl.main_nsplit;
+    p.main_tps = pl.main_tps;
     p.rows_pad = pl.rows_pad;
     if (!lse_obs) {
         char* base = static_cast<char*>(ws);

@@ -27,8 +27,15 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float(uint32_t(h) << 16);
 }
 // Low / high bfloat16 of a packed pair -> float (exact).
-__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// Written as bfloat16 -> float conversions (a shift or a mask in the
+// generated code), so the compiler knows the results are canonical floats and
+// max / min on them need no extra quieting instruction.
+__device__ __forceinline__ float bf16lo(uint32_t w) {
+    return (float)__builtin_bit_cast(__bf16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float bf16hi(uint32_t w) {
+    return (float)__builtin_bit_cast(__bf16, (uint16_t)(w >> 16));
+}
 
 // float -> bfloat16 bits, round to nearest even (hardware convert).
 __device__ __forceinline__ uint16_t f32_to_bf16(float x) {

@@ -14,7 +14,16 @@ constexpr int ATTN_WAVES = 4;    // waves per attention workgroup
 constexpr int ATTN_TARGET_WGS = 256;  // partial workgroups an attention launch aims for
 constexpr int MAX_SPLIT_ROWS = 4096;  // bound on nsplit * padded rows (workspace size)
 constexpr int SCORE_TILE = 32;
-constexpr int SCORE_MAX_TPS = 16;     // tiles per score workgroup
+constexpr int SCORE_MAX_TPS = 16;     // tiles per score-statistics workgroup
+constexpr int SCORE_QPITCH = 136;     // bf16 per window-query row staged in LDS (272 bytes)
+constexpr int CU_COUNT = 256;         // compute units of the part
+constexpr int LDS_PER_CU = 160 * 1024;
+
+// LDS of one bf16 score-pass workgroup: the window queries (16-row blocks)
+// plus one float (lse term) and one int (last visible row) per row.
+inline size_t score_main_lds_bytes(int rows) {
+    return (size_t)((rows + 15) / 16) * 16 * (SCORE_QPITCH * 2 + 8);
+}
 constexpr int SELECT_THREADS = 1024;
 
 // One attention launch: a set of q-layers that all read one cache slot.
@@ -52,7 +61,8 @@ struct ScoreLaunch {
     float scale;
     float* score;           // [nb][hkv][t_len]
     float* range;           // [nb][hkv][t_len] or null
-    int nsplit, tps;
+    int nsplit, tps;        // statistics pass (and the float32 path): splits, tiles per split
+    int main_nsplit, main_tps;   // bf16 score pass
     float* stats;           // [slabs][nsplit][rows_pad][2] partial (m, z)
     float* lse_ws;          // [slabs][rows_pad] merged log-normalisers
     int rows_pad;

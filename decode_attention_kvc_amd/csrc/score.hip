@@ -11,15 +11,17 @@
 // v_mfma_f32_16x16x32_bf16: A = 16 query rows x 32 channels, B = 32 channels
 // x 16 cache rows; the output lane layout puts one cache row per lane column,
 // so the column sums over query rows are in-lane adds plus two cross-lane
-// steps.  Each wave owns 32 query rows (one head's 32-query window), the
-// workgroup covers all g*w rows of one slab over a range of tiles, and the
-// waves' column sums meet in LDS in a fixed order (deterministic).
+// steps.  The score pass gives each wave whole tiles and all g*w query rows
+// (staged in LDS); every sum is taken in a fixed order (deterministic).
 //
 // Without the log-normalisers of the window rows a first pass computes them:
-// per-row online max / sum over each workgroup's tiles, then a small kernel
-// merges the splits' pairs (kernel boundaries order the two, so no
-// cross-workgroup fences are needed).  The range is fused into the second
-// pass: per tile one wave also reads the tile's V block.
+// each wave owns 32 query rows (one head's window) and keeps a per-row online
+// max / sum over its workgroup's tiles, then a small kernel merges the splits'
+// pairs (kernel boundaries order the two, so no cross-workgroup fences are
+// needed).  The range is fused into the score pass: the wave that takes a
+// tile also reads the tile's V block.
+#include <type_traits>
+
 #include "common.h"
 #include "kvc_internal.h"
 
@@ -50,10 +52,16 @@ __device__ __forceinline__ float row16_min(float v) {
     return fminf(v, dpp_mov<0x140>(v));
 }
 
-// Range of the 32 rows t0..t0+31 of one slab from its token-minor V slice;
-// one wave.  Lane (l16, lg) reads channels 16*dt + l16 of rows
-// t0 + 8*lg .. +8.
-__device__ __forceinline__ void range_tile_bf16(const uint16_t* vslab, int t0, int T,
+// V block of the 32 rows t0..t0+31 of one slab (one wave): lane (l16, lg)
+// gets channels 16*dt + l16 of rows t0 + 8*lg .. +8.
+__device__ __forceinline__ void load_vtile(u32x4 (&x)[8], const uint16_t* vslab, int t0, int lane) {
+    const int l16 = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) x[dt] = load_stream16(vslab + vt_off(t0, 16 * dt + l16) + 8 * lg);
+}
+
+// Range of those 32 rows from the loaded block.
+__device__ __forceinline__ void range_tile_bf16(const u32x4 (&x)[8], int t0, int T,
                                                 float* range_out, int lane) {
     const int l16 = lane & 15, lg = lane >> 4;
     float mx[8], mn[8];
@@ -62,16 +70,18 @@ __device__ __forceinline__ void range_tile_bf16(const uint16_t* vslab, int t0, i
         mx[jj] = -INFINITY;
         mn[jj] = INFINITY;
     }
+    // Two channel blocks per step, so each step is one three-input max and
+    // one three-input min per row.
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-        const u32x4 x = load16(vslab + vt_off(t0, 16 * dt + l16) + 8 * lg);
+    for (int dt = 0; dt < 8; dt += 2) {
 #pragma unroll
         for (int w2 = 0; w2 < 4; ++w2) {
-            const float a = bf16lo(x[w2]), b2 = bf16hi(x[w2]);
-            mx[2 * w2] = fmaxf(mx[2 * w2], a);
-            mn[2 * w2] = fminf(mn[2 * w2], a);
-            mx[2 * w2 + 1] = fmaxf(mx[2 * w2 + 1], b2);
-            mn[2 * w2 + 1] = fminf(mn[2 * w2 + 1], b2);
+            const float a0 = bf16lo(x[dt][w2]), a1 = bf16lo(x[dt + 1][w2]);
+            const float b0 = bf16hi(x[dt][w2]), b1 = bf16hi(x[dt + 1][w2]);
+            mx[2 * w2] = fmaxf(mx[2 * w2], fmaxf(a0, a1));
+            mn[2 * w2] = fminf(mn[2 * w2], fminf(a0, a1));
+            mx[2 * w2 + 1] = fmaxf(mx[2 * w2 + 1], fmaxf(b0, b1));
+            mn[2 * w2 + 1] = fminf(mn[2 * w2 + 1], fminf(b0, b1));
         }
     }
 #pragma unroll
@@ -227,71 +237,127 @@ __global__ __launch_bounds__(256) void score_lse_merge(ScoreLaunch p) {
 }
 
 // Pass 2: column sums of the window softmax, plus the fused value range.
-__global__ __launch_bounds__(1024) void score_main_bf16(ScoreLaunch p) {
+// The window queries of the slab (all g*w rows) and their log-normalisers
+// are staged in LDS once per workgroup; each wave then takes whole 32-row
+// tiles (round-robin), so every K and V byte is loaded by exactly one wave
+// and a wave keeps its tile's K and V loads in flight while the other waves
+// compute.  Per tile the wave runs all 16-row query blocks against the K
+// tile (the A operand comes from LDS), adds p' = 2^(s*scale*log2 e -
+// lse*log2 e + 64) over the block's rows in-lane with the bare hardware
+// exp2 (one fma and one v_exp_f32 per logit), finishes the column sums with
+// two cross-lane steps and scales them by 2^-64: the tile's 32 scores leave
+// without any cross-wave reduction.  The 2^64 bias keeps every p >= 2^-190
+// a normal float inside the sum (the bare exp2 does not return denormals),
+// and since p <= 1 the biased terms cannot overflow.  The row pitch of the
+// staged queries is 272 bytes, so the 16 rows one 16-byte A-operand read
+// touches fall in distinct LDS banks.
+constexpr int QPITCH = SCORE_QPITCH;
+static_assert(QPITCH >= D && QPITCH % 8 == 0, "16-byte aligned staged rows");
+constexpr float EXP_BIAS = 64.f;
+constexpr float EXP_UNBIAS = 5.421010862427522e-20f;   // 2^-64
+
+template <bool RANGE>
+__global__ __launch_bounds__(256) void score_main_bf16(ScoreLaunch p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int NW = 4;
     const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int slab = b * p.hkv + j;
     const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
-    const int nwaves = blockDim.x / WAVE;
     const int l16 = lane & 15, lg = lane >> 4;
     const int T = p.t_len;
-    const int ntiles = (T + SCORE_TILE - 1) / SCORE_TILE;
-    const int tile_begin = s * p.tps, tile_end = min(tile_begin + p.tps, ntiles);
+    const int MT = (p.rows + 15) / 16;
+    uint16_t* qs = reinterpret_cast<uint16_t*>(smem);                          // [MT*16][QPITCH]
+    float* l2s = reinterpret_cast<float*>(smem + (size_t)MT * 16 * QPITCH * 2);  // [MT*16] 64 - lse*log2 e
+    int* lims = reinterpret_cast<int*>(l2s + MT * 16);                          // [MT*16]
+
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q_obs);
+    for (int x = tid; x < MT * 16 * (D / 8); x += blockDim.x) {
+        const int R = x / (D / 8), c = x % (D / 8);
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (R < p.rows) {
+            const int h = j * p.g + R / p.w, iw = R % p.w;
+            v = load16(q + (((size_t)iw * p.nb + b) * p.hq + h) * D + 8 * c);
+        }
+        *reinterpret_cast<u32x4*>(qs + R * QPITCH + 8 * c) = v;
+    }
+    for (int R = tid; R < MT * 16; R += blockDim.x) {
+        if (R < p.rows) {
+            const int h = j * p.g + R / p.w, iw = R % p.w;
+            const float l = p.lse_obs ? p.lse_obs[((size_t)iw * p.nb + b) * p.hq + h]
+                                      : p.lse_ws[(size_t)slab * p.rows_pad + R];
+            l2s[R] = EXP_BIAS - l * LOG2E;
+            lims[R] = T - p.w + iw;
+        } else {
+            l2s[R] = -INFINITY;   // padding rows: p = 2^-inf = 0
+            lims[R] = -1;
+        }
+    }
+    __syncthreads();
+
     const uint16_t* kslab = reinterpret_cast<const uint16_t*>(p.k) + (size_t)slab * p.t_cap * D;
     const uint16_t* vslab = reinterpret_cast<const uint16_t*>(p.v) + (size_t)slab * p.t_cap * D;
     float* score = p.score + (size_t)slab * T;
-    float* range = p.range ? p.range + (size_t)slab * T : nullptr;
+    float* range = RANGE ? p.range + (size_t)slab * T : nullptr;
+    const float c1 = p.scale * LOG2E;
+    const int ntiles = (T + SCORE_TILE - 1) / SCORE_TILE;
+    const int tile_begin = s * p.main_tps, tile_end = min(tile_begin + p.main_tps, ntiles);
 
-    __shared__ float colsum[16][SCORE_MAX_TPS * SCORE_TILE];
-
-    QFrag Q;
-    load_qfrag(Q, p, b, j, wave, l16, lg);
-    float lse[2][4];
-    int lim[2][4];
+    // TAIL: some (row, column) pairs of the tile are not visible (the causal
+    // window, or columns past t_len whose K bits are arbitrary); they are
+    // replaced by 0 with a select, never multiplied.
+    auto body = [&](const u32x4 (&kb)[2][4], int t0, auto tail_tag) {
+        constexpr bool TAIL = decltype(tail_tag)::value;
+        float c[2] = {0.f, 0.f};
+        for (int mt = 0; mt < MT; ++mt) {
+            f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            const uint16_t* qrow = qs + (mt * 16 + l16) * QPITCH + 8 * lg;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int R = wave * 32 + mt * 16 + 4 * lg + i;
-            if (R < p.rows) {
-                const int h = j * p.g + R / p.w, iw = R % p.w;
-                lse[mt][i] = p.lse_obs ? p.lse_obs[((size_t)iw * p.nb + b) * p.hq + h]
-                                       : p.lse_ws[(size_t)slab * p.rows_pad + R];
-                lim[mt][i] = T - p.w + iw;
-            } else {
-                lse[mt][i] = 0.f;
-                lim[mt][i] = -1;
+            for (int kc = 0; kc < 4; ++kc) {
+                const bf16x8 a = as_bf(*reinterpret_cast<const u32x4*>(qrow + 32 * kc));
+                S[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf(kb[0][kc]), S[0], 0, 0, 0);
+                S[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf(kb[1][kc]), S[1], 0, 0, 0);
             }
-        }
-    for (int tile = tile_begin; tile < tile_end; ++tile) {
-        const int t0 = tile * SCORE_TILE;
-        f32x4 S[2][2];
-        score_tile_mfma(Q, kslab, t0, l16, lg, S);
+            // S[cg][i]: query row mt*16 + 4*lg + i, cache row t0 + 16*cg + l16
+            const f32x4 l2 = *reinterpret_cast<const f32x4*>(l2s + mt * 16 + 4 * lg);
 #pragma unroll
-        for (int cg = 0; cg < 2; ++cg) {
-            float c = 0.f;
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+            for (int cg = 0; cg < 2; ++cg)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float pr = expf(S[mt][cg][i] * p.scale - lse[mt][i]);
-                    c += (t0 + 16 * cg + l16 <= lim[mt][i]) ? pr : 0.f;
+                    float pr = __builtin_amdgcn_exp2f(fmaf(S[cg][i], c1, l2[i]));
+                    if constexpr (TAIL)
+                        pr = (t0 + 16 * cg + l16 <= lims[mt * 16 + 4 * lg + i]) ? pr : 0.f;
+                    c[cg] += pr;
                 }
-            c += __shfl_xor(c, 16);
-            c += __shfl_xor(c, 32);
-            if (lg == 0) colsum[wave][(tile - tile_begin) * SCORE_TILE + 16 * cg + l16] = c;
         }
-        if (range && (tile - tile_begin) % nwaves == wave)
-            range_tile_bf16(vslab, t0, T, range, lane);
-    }
-    __syncthreads();
-    const int n = (tile_end - tile_begin) * SCORE_TILE;
-    for (int x = tid; x < n; x += blockDim.x) {
-        float c = 0.f;
-        for (int w = 0; w < nwaves; ++w) c += colsum[w][x];
-        const int t = tile_begin * SCORE_TILE + x;
-        if (t < T) score[t] = c;
+#pragma unroll
+        for (int cg = 0; cg < 2; ++cg) {
+            c[cg] += __shfl_xor(c[cg], 16);
+            c[cg] += __shfl_xor(c[cg], 32);
+            const int t = t0 + 16 * cg + l16;
+            if (lg == 0 && t < T) score[t] = c[cg] * EXP_UNBIAS;
+        }
+    };
+    using Interior = std::integral_constant<bool, false>;
+    using Tail = std::integral_constant<bool, true>;
+
+    for (int tile = tile_begin + wave; tile < tile_end; tile += NW) {
+        const int t0 = tile * SCORE_TILE;
+        u32x4 kb[2][4], vb[8];
+#pragma unroll
+        for (int cg = 0; cg < 2; ++cg) {
+            const uint16_t* kr = kslab + (size_t)(t0 + 16 * cg + l16) * D + 8 * lg;
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) kb[cg][kc] = load_stream16(kr + 32 * kc);
+        }
+        if constexpr (RANGE) load_vtile(vb, vslab, t0, lane);
+        if (t0 + SCORE_TILE - 1 <= T - p.w)
+            body(kb, t0, Interior{});
+        else
+            body(kb, t0, Tail{});
+        if constexpr (RANGE) range_tile_bf16(vb, t0, T, range, lane);
     }
 }
+
 
 // ---------------------------------------------------------------------------
 // float32 path (VALU), 64-row tiles staged in LDS.
@@ -463,7 +529,18 @@ hipError_t launch_score(const ScoreLaunch& p, int dtype, hipStream_t st) {
             hipLaunchKernelGGL(score_stats_bf16, grid, dim3(nw * WAVE), 0, st, p);
             hipLaunchKernelGGL(score_lse_merge, dim3(p.hkv, p.nb), dim3(256), 0, st, p);
         }
-        hipLaunchKernelGGL(score_main_bf16, grid, dim3(nw * WAVE), 0, st, p);
+        const dim3 mgrid(p.main_nsplit, p.hkv, p.nb);
+        const size_t lds = score_main_lds_bytes(p.rows);
+        auto go = [&](auto kern) {
+            if (lds > 64 * 1024 &&
+                hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+                return hipErrorInvalidValue;
+            hipLaunchKernelGGL(kern, mgrid, dim3(256), lds, st, p);
+            return hipSuccess;
+        };
+        if ((p.range ? go(score_main_bf16<true>) : go(score_main_bf16<false>)) != hipSuccess)
+            return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
