@@ -15,10 +15,15 @@ Parity status of each function (what pins it is in tests/test_oracle_*.py):
   select          pinned (invariants, top-K reduction, exact 8-token law)
   compact         pinned (gather identity, restricted attention)
   run_decode      pinned through the functions above and the schedule count
+  dkv.gaussian_bf16  pinned (Box-Muller word roles in closed form, bf16
+                  round-to-nearest-even cases, normal law)
+  dkv.dkv_score   pinned (QR and SVD leverage, closed two-row form,
+                  subspace invariance, rank deficiency, isolated rows)
 End-to-end model quality (does the eviction keep accuracy?) is parity
 unpinned: it needs trained weights and datasets that are not available.
 """
 from .philox import philox4, philox4x32_10, seed_key, mulhilo
+from . import dkv
 from .kvc_oracle import (
     share_map, append_row, attention, decode_attention, value_range,
     window_score, philox_word0, exp_variate, select, select_detail, compact,
@@ -29,5 +34,5 @@ __all__ = [
     "philox4", "philox4x32_10", "seed_key", "mulhilo", "share_map",
     "append_row", "attention", "decode_attention", "value_range",
     "window_score", "philox_word0", "exp_variate", "select", "select_detail",
-    "compact", "eviction_due", "run_decode",
+    "compact", "eviction_due", "run_decode", "dkv",
 ]
