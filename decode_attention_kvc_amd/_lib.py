@@ -25,7 +25,8 @@ EXPORTS = (
     "kvc_version", "kvc_strerror", "kvc_share_map", "kvc_append",
     "kvc_decode_attn_ws_bytes", "kvc_decode_attn", "kvc_value_range",
     "kvc_score_ws_bytes", "kvc_score", "kvc_select_ws_bytes", "kvc_select",
-    "kvc_compact", "kvc_philox_words",
+    "kvc_compact", "kvc_philox_words", "kvc_dkv_ws_bytes", "kvc_dkv_score",
+    "kvc_gaussian_bf16",
 )
 
 
@@ -75,6 +76,10 @@ def lib():
             "kvc_compact": ([cp, i32, vp, i32, cp, vp], i32),
             "kvc_philox_words": ([i64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
                                   ctypes.c_uint64, vp, vp], i32),
+            "kvc_dkv_ws_bytes": ([cp, i32, szp], i32),
+            "kvc_dkv_score": ([cp, i32, vp, i32, vp, vp, vp, sz, vp], i32),
+            "kvc_gaussian_bf16": ([i64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, vp,
+                                   vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -284,3 +289,23 @@ def kvc_compact(src, slot, kept, n_keep, dst, stream=None):
 def kvc_philox_words(n, c1, c2, c3, seed, out, stream=None):
     _check(lib().kvc_philox_words(n, c1, c2, c3, int(seed) & (2**64 - 1), _ptr(out),
                                   _stream(stream)), "kvc_philox_words")
+
+
+def kvc_dkv_ws_bytes(cache, rank):
+    c = cache.desc()
+    out = ctypes.c_size_t()
+    _check(lib().kvc_dkv_ws_bytes(ctypes.byref(c), rank, ctypes.byref(out)), "kvc_dkv_ws_bytes")
+    return out.value
+
+
+def kvc_dkv_score(cache, slot, g, score, rng=None, ws=None, stream=None):
+    """g: bf16 [rank][2*head_dim] (row n = sketch column n)."""
+    c = cache.desc()
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().kvc_dkv_score(ctypes.byref(c), slot, _ptr(g), g.shape[0], _ptr(score), _ptr(rng),
+                               _ptr(ws), ws_bytes, _stream(stream)), "kvc_dkv_score")
+
+
+def kvc_gaussian_bf16(n, seed, c1, c2, out, stream=None):
+    _check(lib().kvc_gaussian_bf16(n, int(seed) & (2**64 - 1), c1, c2, _ptr(out),
+                                   _stream(stream)), "kvc_gaussian_bf16")

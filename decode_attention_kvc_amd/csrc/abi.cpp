@@ -140,6 +140,30 @@ ScoreWs score_ws_layout(int dtype, int rows, int t_len, int slabs) {
     return w;
 }
 
+// ---- VASE-DKV planning -----------------------------------------------------
+constexpr int DKV_TILE = 32;
+
+struct DkvWs {
+    int nsplit, tps;
+    size_t y_off, gram_off, w_off, total;
+};
+
+DkvWs dkv_layout(int rank, int t_len, int slabs) {
+    DkvWs w;
+    const int ntiles = std::max(1, (t_len + DKV_TILE - 1) / DKV_TILE);
+    const long long work = (long long)ntiles * std::max(1, slabs);
+    // one round of workgroups (rank 16: three per CU, bounded by LDS;
+    // rank 32: two, bounded by registers), at least two tiles per wave
+    const long long target = (rank == 16 ? 3LL : 2LL) * CU_COUNT;
+    w.tps = (int)std::max<long long>(8, (work + target - 1) / target);
+    w.nsplit = (ntiles + w.tps - 1) / w.tps;
+    w.y_off = 0;
+    w.gram_off = align_up((size_t)slabs * t_len * rank * sizeof(float), 256);
+    w.w_off = w.gram_off + align_up((size_t)slabs * w.nsplit * rank * rank * sizeof(double), 256);
+    w.total = w.w_off + (size_t)slabs * rank * rank * sizeof(float);
+    return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -461,6 +485,61 @@ int kvc_compact(const kvc_cache* src, int slot, const int32_t* kept, int n_keep,
     p.n_keep = n_keep;
     p.elem = (int)es;
     if (launch_compact(p, (hipStream_t)stream) != hipSuccess) return KVC_EHIP;
+    return hip_status();
+}
+
+int kvc_dkv_ws_bytes(const kvc_cache* c, int rank, size_t* bytes) {
+    int st = check_cache(c);
+    if (st) return st;
+    if (!bytes) return KVC_EALIGN;
+    if (rank != 16 && rank != 32) return KVC_EINVAL;
+    const int slabs = c->nb * c->n_kv_heads;
+    *bytes = dkv_layout(rank, std::max(c->t_len, c->t_cap), slabs).total;
+    return KVC_OK;
+}
+
+int kvc_dkv_score(const kvc_cache* c, int slot, const void* g, int rank, float* score,
+                  float* range, void* ws, size_t ws_bytes, kvc_stream_t stream) {
+    int st = check_cache(c);
+    if (st) return st;
+    if (c->dtype != KVC_BF16) return KVC_EDTYPE;
+    if (slot < 0 || slot >= c->n_slots) return KVC_EINVAL;
+    if (rank != 16 && rank != 32) return KVC_EINVAL;
+    if (c->nb == 0 || c->t_len == 0) return KVC_OK;
+    if (!aligned16(g) || !aligned4(score) || (range && !aligned4(range))) return KVC_EALIGN;
+    const int slabs = c->nb * c->n_kv_heads;
+    const DkvWs lay = dkv_layout(rank, c->t_len, slabs);
+    if (!ws || ws_bytes < lay.total || !aligned16(ws)) return KVC_EWORKSPACE;
+    DkvLaunch p;
+    memset(&p, 0, sizeof(p));
+    p.k = slot_k(c, slot);
+    p.v = slot_v(c, slot);
+    p.nb = c->nb;
+    p.hkv = c->n_kv_heads;
+    p.t_len = c->t_len;
+    p.t_cap = c->t_cap;
+    p.g = g;
+    p.rank = rank;
+    p.score = score;
+    p.range = range;
+    p.nsplit = lay.nsplit;
+    p.tps = lay.tps;
+    char* base = static_cast<char*>(ws);
+    p.y = reinterpret_cast<float*>(base + lay.y_off);
+    p.gram = reinterpret_cast<double*>(base + lay.gram_off);
+    p.w = reinterpret_cast<float*>(base + lay.w_off);
+    if (launch_dkv(p, (hipStream_t)stream) != hipSuccess) return KVC_EHIP;
+    return hip_status();
+}
+
+int kvc_gaussian_bf16(int64_t n, uint64_t seed, uint32_t c1, uint32_t c2, void* out,
+                      kvc_stream_t stream) {
+    if (n < 0 || n > (int64_t)1 << 32) return KVC_EINVAL;
+    if (n == 0) return KVC_OK;
+    if (!aligned4(out)) return KVC_EALIGN;
+    if (launch_gaussian(n, c1, c2, (uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32), out,
+                        (hipStream_t)stream) != hipSuccess)
+        return KVC_EHIP;
     return hip_status();
 }
 

@@ -68,6 +68,21 @@ struct ScoreLaunch {
     int rows_pad;
 };
 
+// VASE-DKV scores of one cache slot (bf16).
+struct DkvLaunch {
+    const void* k;          // slot base of K
+    const void* v;          // slot base of V
+    int nb, hkv, t_len, t_cap;
+    const void* g;          // bf16 [rank][2*D]: row n is sketch column n
+    int rank;               // 16 or 32
+    float* score;           // [nb][hkv][t_len]
+    float* range;           // [nb][hkv][t_len] or null
+    int nsplit, tps;        // sketch pass: splits per slab, tiles per split
+    float* y;               // workspace [slabs][t_len][rank]
+    double* gram;           // workspace [slabs][nsplit][rank][rank]
+    float* w;               // workspace [slabs][rank][rank]
+};
+
 struct SelectLaunch {
     const float* score;
     const float* range;
@@ -101,6 +116,9 @@ hipError_t launch_value_range(const void* v, int nb, int hkv, int t_len, int t_c
                               int dtype, float* range, hipStream_t s);
 hipError_t launch_score(const ScoreLaunch& p, int dtype, hipStream_t s);
 hipError_t launch_select(const SelectLaunch& p, hipStream_t s);
+hipError_t launch_dkv(const DkvLaunch& p, hipStream_t s);
+hipError_t launch_gaussian(int64_t n, uint32_t c1, uint32_t c2, uint32_t k0, uint32_t k1,
+                           void* out, hipStream_t s);
 hipError_t launch_compact(const CompactLaunch& p, hipStream_t s);
 hipError_t launch_philox(int64_t n, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
                          uint32_t k1, uint32_t* out, hipStream_t s);

@@ -233,6 +233,50 @@ int kvc_select(const float* score, const float* range, int nb, int n_kv_heads,
 int kvc_compact(const kvc_cache* src, int slot, const int32_t* kept,
                 int n_keep, const kvc_cache* dst, kvc_stream_t stream);
 
+/* Workspace bytes kvc_dkv_score needs for any t_len <= max(t_len, t_cap). */
+int kvc_dkv_ws_bytes(const kvc_cache* c, int rank, size_t* bytes);
+
+/*
+ * VASE-DKV token scores [VASE §2.B: CurDKV's leverage scores, with a
+ * Gaussian projection G drawn afresh at every eviction pass].  The page gives
+ * no formula; this library scores token t of slab (b, j) by the leverage of
+ * row t of the sketch Y = [K | V] G (key row then value row, T x 2d, times
+ * G of shape 2d x rank):
+ *   score_t = y_t (Y^T Y)^+ y_t^T,
+ * the squared norm of row t of an orthonormal basis of Y's column space
+ * (sum over t = rank(Y)).  The pseudo-inverse is taken through a Cholesky
+ * factorisation of Y^T Y in float64 that drops every direction whose pivot
+ * is at most 1e-12 of the trace.  Y is accumulated in float32 from the bf16
+ * cache and G, Y^T Y in float64.  The scores are sampling weights for
+ * kvc_select, which runs
+ * unchanged (value-range protection, recent buffer, exponential keys).
+ *   g:     device bf16 [rank][2 * head_dim]; row n is sketch column n
+ *          (entries 0..d-1 multiply the key channels, d..2d-1 the value
+ *          channels).  Draw it per pass, e.g. with kvc_gaussian_bf16.
+ *   rank:  16 or 32.
+ *   score: device float32 [nb][n_kv_heads][t_len].
+ *   range: NULL or device float32 [nb][n_kv_heads][t_len]: the value range
+ *          of kvc_value_range, fused into the same pass over the cache.
+ *   ws:    kvc_dkv_ws_bytes bytes, 16-byte aligned, no initialisation needed.
+ * bf16 caches only (KVC_EDTYPE otherwise).
+ */
+int kvc_dkv_score(const kvc_cache* c, int slot, const void* g, int rank,
+                  float* score, float* range, void* ws, size_t ws_bytes,
+                  kvc_stream_t stream);
+
+/*
+ * N(0, 1) draws rounded to bf16, for the Gaussian projection of
+ * kvc_dkv_score: Box-Muller (1958) on Philox4x32-10.  Elements 2p and 2p+1
+ * come from words x0, x1 at counter (p, c1, c2, 0) under key
+ * (seed mod 2^32, seed >> 32):
+ *   u1 = (x0 + 1) / 2^32,  u2 = x1 / 2^32,
+ *   out[2p] = sqrt(-2 ln u1) cos(2 pi u2), out[2p+1] = ... sin(2 pi u2),
+ * evaluated in float64, rounded to float32, then to bf16 (nearest even).
+ *   out: device bf16 [n], 4-byte aligned; n <= 2^32.
+ */
+int kvc_gaussian_bf16(int64_t n, uint64_t seed, uint32_t c1, uint32_t c2,
+                      void* out, kvc_stream_t stream);
+
 /*
  * Diagnostic: the device Philox4x32-10 stream that kvc_select draws from.
  * out[i][0..3] = Philox4x32-10(counter (i, c1, c2, c3),

@@ -240,3 +240,42 @@ def test_cache_layout_roundtrip(T):
     assert flat[(t // 32) * 4096 + d * 32 + t % 32] == V[1, 2, t, d]
     if T % 32:
         assert torch.isnan(c.v[1, :, :, T // 32, :, T % 32:]).all()   # rows past T untouched
+
+
+def dkv(c, **kw):
+    a = dict(slot=0, g=FAKE, rank=32, sc=FAKE, rg=None, ws=FAKE2, wsb=1 << 40)
+    a.update(kw)
+    return L.kvc_dkv_score(ctypes.byref(c), a["slot"], a["g"], a["rank"], a["sc"], a["rg"],
+                           a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(slot=2), kvc.KVC_EINVAL),
+    (dict(rank=24), kvc.KVC_EINVAL),
+    (dict(rank=64), kvc.KVC_EINVAL),
+    (dict(g=FAKE + 4), kvc.KVC_EALIGN),
+    (dict(sc=FAKE + 2), kvc.KVC_EALIGN),
+    (dict(rg=FAKE + 2), kvc.KVC_EALIGN),
+    (dict(ws=None), kvc.KVC_EWORKSPACE),
+    (dict(wsb=16), kvc.KVC_EWORKSPACE),
+    (dict(ws=FAKE2 + 8), kvc.KVC_EWORKSPACE),
+])
+def test_dkv_rejects_bad_args(kw, code):
+    assert dkv(cache(), **kw) == code
+
+
+def test_dkv_validation_and_sizes():
+    assert dkv(cache(dtype=0)) == kvc.KVC_EDTYPE
+    assert dkv(cache(t_len=0)) == kvc.KVC_OK
+    assert dkv(cache(nb=0)) == kvc.KVC_OK
+    n16, n32 = ctypes.c_size_t(), ctypes.c_size_t()
+    c = cache(nb=2, n_kv_heads=4, t_len=100, t_cap=192)
+    assert L.kvc_dkv_ws_bytes(ctypes.byref(c), 16, ctypes.byref(n16)) == 0
+    assert L.kvc_dkv_ws_bytes(ctypes.byref(c), 32, ctypes.byref(n32)) == 0
+    # at least the sketch rows of the capacity: slabs * t_cap * rank floats
+    assert n16.value >= 8 * 192 * 16 * 4 and n32.value >= 8 * 192 * 32 * 4
+    assert L.kvc_dkv_ws_bytes(ctypes.byref(c), 8, ctypes.byref(n16)) == kvc.KVC_EINVAL
+    assert L.kvc_gaussian_bf16(-1, 0, 0, 0, FAKE, None) == kvc.KVC_EINVAL
+    assert L.kvc_gaussian_bf16((1 << 32) + 1, 0, 0, 0, FAKE, None) == kvc.KVC_EINVAL
+    assert L.kvc_gaussian_bf16(4, 0, 0, 0, FAKE + 2, None) == kvc.KVC_EALIGN
+    assert L.kvc_gaussian_bf16(0, 0, 0, 0, FAKE, None) == kvc.KVC_OK

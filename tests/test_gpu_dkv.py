@@ -1,0 +1,174 @@
+"""GPU parity of the VASE-DKV scoring path (kvc_gaussian_bf16, kvc_dkv_score)
+against oracle/dkv.py, through the C ABI.
+
+Tolerance of the scores (derived from the arithmetic, not fitted): Y = [K|V] G
+is accumulated in float32 from exact bf16 products over 256 terms, so each
+entry carries a relative error of a few 1e-7; the Gram matrix and its
+factorisation are float64 and add nothing; the float32 inverse factor W and
+the float32 quadratic form each add rounding of order cond(Y) * 1e-7.  For
+the synthetic slabs cond(Y) stays below ~30, so the bound used is
+|l_gpu - l_ref| <= 2e-5 * max(l_ref) + 1e-6 * l_ref per row; the sum of the
+scores must equal rank(Y) to 1e-4 relative."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import dkv as odkv
+import kvc_synth
+import decode_attention_kvc_amd as kvc
+from helpers import make_cache, slab_np, ws_tensor
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def sketch_matrix(rank, seed):
+    """G as the library takes it: bf16 [rank][256]."""
+    return kvc_synth.queries((rank, 256), dtype=torch.bfloat16, device=DEV, seed=seed)
+
+
+def g_for_oracle(g):
+    return g.double().cpu().numpy().T           # [256][rank]
+
+
+@pytest.mark.parametrize("n,seed,c1,c2", [(100003, 7, 3, 0xFFFFFFFF), (64, 0, 0, 0),
+                                          (4097, 2**40 + 5, 17, 9)])
+def test_gaussian_bit_exact(n, seed, c1, c2):
+    say("gaussian", n, seed, c1, c2)
+    out = torch.zeros(n + 1, dtype=torch.bfloat16, device=DEV)
+    out[n] = 12.5                                     # sentinel past the end
+    kvc.kvc_gaussian_bf16(n, seed, c1, c2, out)
+    torch.cuda.synchronize()
+    got = out[:n].view(torch.int16).cpu().numpy().astype(np.uint16)
+    want = odkv.gaussian_bf16(n, seed, c1, c2)
+    mism = int((got != want).sum())
+    say(f"  mismatching words: {mism} of {n}")
+    assert mism == 0
+    assert out[n].item() == 12.5
+
+
+DKV_CASES = [
+    # (nb, hkv, T, rank)
+    (1, 2, 100, 16),
+    (1, 2, 100, 32),
+    (2, 8, 1000, 32),
+    (1, 8, 4097, 32),          # ragged last tile
+    (3, 2, 33, 16),
+    (1, 1, 20, 32),            # fewer rows than sketch columns: dropped pivots
+    (1, 4, 8448, 32),
+]
+
+
+def check_scores(got, ref):
+    err = np.abs(got - ref)
+    bound = 2e-5 * ref.max() + 1e-6 * ref
+    assert np.all(err <= bound), float((err / (ref.max())).max())
+    return float(err.max() / ref.max())
+
+
+@pytest.mark.parametrize("case", DKV_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_dkv_score_matches_oracle(case):
+    nb, hkv, T, rank = case
+    say("dkv score", case)
+    cache = make_cache(2, nb, hkv, T, seed=T + rank)
+    g = sketch_matrix(rank, seed=T)
+    score = torch.full((nb, hkv, T), float("nan"), device=DEV)
+    rng = torch.full((nb, hkv, T), float("nan"), device=DEV)
+    ws = ws_tensor(kvc.kvc_dkv_ws_bytes(cache, rank))
+    kvc.kvc_dkv_score(cache, 1, g, score, rng, ws)
+    torch.cuda.synchronize()
+    K, V = slab_np(cache, 1)
+    G = g_for_oracle(g)
+    worst = 0.0
+    for b in range(nb):
+        for j in range(hkv):
+            ref = odkv.dkv_score(K[b, j], V[b, j], G)
+            got = score[b, j].double().cpu().numpy()
+            worst = max(worst, check_scores(got, ref))
+            rk = min(T, rank)
+            assert got.sum() == pytest.approx(rk, rel=1e-4)
+            assert np.array_equal(rng[b, j].cpu().numpy(),
+                                  oracle.value_range(V[b, j]).astype(np.float32))
+    say(f"  max error / max score: {worst:.2e}")
+
+
+def test_dkv_rank_deficient_rows():
+    # every row of the slab is one of three (K, V) rows: rank 3 < 16
+    say("dkv rank deficient")
+    nb, hkv, T, rank = 1, 2, 200, 16
+    cache = make_cache(1, nb, hkv, T, seed=3)
+    K = cache.k_rows(0)
+    V = cache.v_rows(0)
+    idx = torch.arange(T, device=DEV) % 3
+    cache.fill(0, K[:, :, idx].contiguous(), V[:, :, idx].contiguous())
+    g = sketch_matrix(rank, seed=11)
+    score = torch.empty((nb, hkv, T), device=DEV)
+    ws = ws_tensor(kvc.kvc_dkv_ws_bytes(cache, rank))
+    kvc.kvc_dkv_score(cache, 0, g, score, None, ws)
+    torch.cuda.synchronize()
+    Kn, Vn = slab_np(cache, 0)
+    for j in range(hkv):
+        got = score[0, j].double().cpu().numpy()
+        ref = odkv.dkv_score(Kn[0, j], Vn[0, j], g_for_oracle(g))
+        assert got.sum() == pytest.approx(3.0, rel=1e-4)
+        check_scores(got, ref)
+
+
+def test_dkv_workspace_reuse_and_determinism():
+    say("dkv reuse")
+    cache = make_cache(1, 2, 8, 3000, seed=5)
+    g = sketch_matrix(32, seed=1)
+    ws = ws_tensor(kvc.kvc_dkv_ws_bytes(cache, 32))
+    s1 = torch.empty((2, 8, 3000), device=DEV)
+    s2 = torch.empty_like(s1)
+    kvc.kvc_dkv_score(cache, 0, g, s1, None, ws)
+    cache.t_len = 1700                       # a shorter slab in the same workspace
+    s3 = torch.empty((2, 8, 1700), device=DEV)
+    kvc.kvc_dkv_score(cache, 0, g, s3, None, ws)
+    cache.t_len = 3000
+    kvc.kvc_dkv_score(cache, 0, g, s2, None, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
+    K, V = slab_np(cache, 0)
+    ref = odkv.dkv_score(K[1, 3, :1700], V[1, 3, :1700], g_for_oracle(g))
+    check_scores(s3[1, 3].double().cpu().numpy(), ref)
+
+
+def test_dkv_kept_sets_match_oracle():
+    """End to end: DKV scores -> VASE selection, against the oracle's own
+    scores and selection.  Rows within the score tolerance of the sampling
+    cutoff may flip; they are counted."""
+    say("dkv select")
+    nb, hkv, T, rank = 1, 8, 4352, 32
+    Kb, B, Nv = 4096, 128, 64
+    cache = make_cache(1, nb, hkv, T, seed=9)
+    g = sketch_matrix(rank, seed=21)
+    score = torch.empty((nb, hkv, T), device=DEV)
+    rng = torch.empty((nb, hkv, T), device=DEV)
+    kvc.kvc_dkv_score(cache, 0, g, score, rng, ws_tensor(kvc.kvc_dkv_ws_bytes(cache, rank)))
+    kept = torch.empty((nb, hkv, Kb + B), dtype=torch.int32, device=DEV)
+    kvc.kvc_select(score, rng, nb, hkv, T, Kb, B, Nv, 99, 3, kept,
+                   ws_tensor(kvc.kvc_select_ws_bytes(nb, hkv, T)))
+    torch.cuda.synchronize()
+    K, V = slab_np(cache, 0)
+    ties = 0
+    for j in range(hkv):
+        sc = odkv.dkv_score(K[0, j], V[0, j], g_for_oracle(g))
+        d = oracle.select_detail(sc, oracle.value_range(V[0, j]), T, Kb, B, Nv, 99, 3, 0, j)
+        kc = d["kappa_cut"]
+        diff = set(kept[0, j].cpu().numpy().tolist()) ^ set(d["kept"].tolist())
+        for t in diff:
+            # a row may flip when its key and the cutoff's are closer than
+            # the score tolerance (relative to the row's own score) allows
+            eps = 2 * (2e-5 * sc.max() / sc[t] + 1e-6)
+            assert abs(d["kappa"][t] - kc) <= eps * kc, (j, t)
+        ties += len(diff)
+        assert len(diff) <= 8
+    say(f"  rows flipped inside the score tolerance: {ties}")
