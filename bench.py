@@ -67,11 +67,13 @@ def step_attn_bytes(dec, mode, nb, hq, hkv, t_len):
 def evict_bytes(cfg, t_len):
     """Algorithmic bytes of one eviction pass: K + V read once by the fused
     score/range pass, score/range written and read, kept rows gathered (read)
-    and written."""
+    and written; VASE-DKV adds its float32 sketch rows (written once, read
+    once)."""
     e = cfg["evict"]
     slabs = cfg["nb"] * cfg["hkv"] * len(cfg["leaders"])
     keep = e["K"] + e["B"]
-    return slabs * (2 * t_len * 256 + 2 * 4 * t_len * 2 + 4 * keep + 2 * 2 * keep * 256)
+    sketch = 2 * 4 * e.get("rank", 32) * t_len if e.get("scoring") == "dkv" else 0
+    return slabs * (2 * t_len * 256 + 2 * 4 * t_len * 2 + 4 * keep + 2 * 2 * keep * 256 + sketch)
 
 
 def cpu_baseline(cfg, cache, qpool, s, budget_s=8.0):
@@ -107,12 +109,20 @@ def cpu_baseline(cfg, cache, qpool, s, budget_s=8.0):
     if e:
         w = e["w"]
         qo = qpool[0, s - w + 1:s + 1].cpu()
+        dkv = e.get("scoring") == "dkv"
+        if dkv:
+            r = e.get("rank", 32)
+            G = oracle.dkv.bf16_bits_to_f64(oracle.dkv.gaussian_bf16(r * 256, 1, 0, 0xFFFFFFFF))
+            G = G.reshape(r, 256).T
         t1 = time.perf_counter()
         while time.perf_counter() - t1 < budget_s and n_ev < nb * hkv:
             b, j = divmod(n_ev, hkv)
             K = Kc[b, j].double().numpy()
             V = Vc[b, j].double().numpy()
-            sc = oracle.window_score(qo[:, b, j * g:(j + 1) * g].double().numpy(), K, T)
+            if dkv:
+                sc = oracle.dkv.dkv_score(K, V, G)
+            else:
+                sc = oracle.window_score(qo[:, b, j * g:(j + 1) * g].double().numpy(), K, T)
             vr = oracle.value_range(V)
             kept = oracle.select(sc, vr, T, e["K"], e["B"], e["N_v"], 1, 0, b, j)
             oracle.compact(K, V, kept)
@@ -121,8 +131,9 @@ def cpu_baseline(cfg, cache, qpool, s, budget_s=8.0):
         t_ev_total = t_ev * nb * hkv * len(cfg["leaders"])
     per_step = t_step + (t_ev_total / e["period"] if e else 0.0)
     sample = (f"{n_dec} of {nb * hkv} slabs of one layer's decode attention at T={T}"
-              + (f" and {n_ev} slabs of one eviction pass (score+range+select+compact)"
-                 if e else "")
+              + (f" and {n_ev} slabs of one eviction pass ("
+                 + ("VASE-DKV leverage" if e and e.get("scoring") == "dkv" else "window score")
+                 + "+range+select+compact)" if e else "")
               + f", extrapolated linearly to a full step of {cfg['n_layers']} layers"
               + (f" plus 1/{e['period']} of a pass over {len(cfg['leaders'])} leader slots"
                  if e else "")
@@ -168,6 +179,11 @@ def main():
                     choices=["per-layer", "per-layer-interleaved", "grouped"],
                     help="per-layer-interleaved issues the same calls round-robin over the "
                          "slots, so no call can find its slab in the Infinity Cache")
+    ap.add_argument("--scoring", default="attnv", choices=["attnv", "dkv"],
+                    help="eviction scores: observation-window attention (VASE-AttnV) or the "
+                         "leverage of Gaussian-sketched [K|V] rows (VASE-DKV)")
+    ap.add_argument("--rank", type=int, default=32, choices=[16, 32],
+                    help="sketch columns of the VASE-DKV scores")
     ap.add_argument("--no-grouped", action="store_true", help="skip the grouped-mode leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -184,7 +200,9 @@ def main():
     import decode_attention_kvc_amd as kvc
     from decode_attention_kvc_amd.loop import Decoder
 
-    cfg = WORKLOADS[args.workload]
+    cfg = dict(WORKLOADS[args.workload])
+    if cfg["evict"]:
+        cfg["evict"] = dict(cfg["evict"], scoring=args.scoring, rank=args.rank)
     dev = "cuda"
     torch.cuda.init()
     L, leaders, nb, hq, hkv, t0 = (cfg[k] for k in ("n_layers", "leaders", "nb", "hq", "hkv", "t0"))
@@ -221,8 +239,8 @@ def main():
         cache = kvc.Cache.empty(n_slots, nb, hkv, steady_cap, device=dev)
         spare = kvc.Cache.empty(n_slots, nb, hkv, steady_cap, device=dev)
         dec = Decoder(L, leaders, big, cache, hq, evict=ev, mode=args.mode)
-        q_init = [kvc_synth.queries((ev["w"], nb, hq, 128), device=dev, seed=50 + i)
-                  for i in range(n_slots)]
+        q_init = ([kvc_synth.queries((ev["w"], nb, hq, 128), device=dev, seed=50 + i)
+                   for i in range(n_slots)] if args.scoring == "attnv" else None)
         torch.cuda.synchronize()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
@@ -334,7 +352,8 @@ def main():
             "layers": L, "leaders": n_slots, "batch": nb, "q_heads": hq, "kv_heads": hkv,
             "head_dim": 128, "prompt_tokens": t0,
             **({"budget_K": ev["K"], "recent_B": ev["B"], "N_v": ev["N_v"], "window": ev["w"],
-                "period": ev["period"]} if ev else {}),
+                "period": ev["period"], "scoring": ev["scoring"]} if ev else {}),
+            **({"sketch_rank": ev["rank"]} if ev and ev["scoring"] == "dkv" else {}),
             "mean_cache_rows": round(t_mean, 1),
         },
         "achieved_GBps": round(step_gbps, 1),

@@ -5,7 +5,11 @@ each layer reads the KV of its nearest earlier leader; only leaders append.
 VASE summary (gist.science 2606.03928), §2: every `period` steps, when the
 cache holds more than K + B rows, an eviction pass (score + range, select,
 compact) shrinks every leader slab back to K + B rows; pass r draws its
-random keys with seed + r.
+random keys with seed + r.  The scores are the observation-window attention
+(VASE-AttnV, the default) or, with scoring="dkv", the leverage of the
+Gaussian-sketched [K | V] rows (VASE-DKV, §2.B), whose projection G is drawn
+afresh for every pass and leader: kvc_gaussian_bf16 with key seed + r and
+counter (element pair, leader layer, 0xFFFFFFFF).
 
 This module only orders library calls on the current stream; every step of
 the computation runs in libkvc's kernels.
@@ -25,7 +29,8 @@ class Decoder:
     def __init__(self, n_layers, leaders, cache, spare, n_q_heads, evict=None,
                  mode="per-layer", record_events=False):
         """cache / spare: two Cache objects of the same shape (ping-pong for
-        compaction).  evict: None or dict(K, B, N_v, w, period, seed).
+        compaction).  evict: None or dict(K, B, N_v, w, period, seed[,
+        scoring="attnv"|"dkv", rank=32]).
         mode: "per-layer" (one call per layer, in layer order), "grouped"
         (one call per leader with all of its followers' queries) or
         "per-layer-interleaved" (one call per layer, issued round-robin over
@@ -114,6 +119,8 @@ class Decoder:
             t_alloc = max(t_len, c.t_cap)
             b = dict(t=t_alloc,
                      score=torch.empty(nb * hkv * t_alloc, device=dev),
+                     g=torch.empty((e.get("rank", 32), 256), dtype=torch.bfloat16, device=dev),
+                     dkv_ws=None,
                      rng=torch.empty(nb * hkv * t_alloc, device=dev),
                      kept=torch.empty(nb * hkv * (e["K"] + e["B"]), dtype=torch.int32, device=dev),
                      sel_ws=torch.empty(max(16, K.kvc_select_ws_bytes(nb, hkv, t_alloc)),
@@ -137,21 +144,34 @@ class Decoder:
         score = b["score"][: nb * hkv * T]
         rng = b["rng"][: nb * hkv * T]
         kept = b["kept"][: nb * hkv * n_keep]
-        if b["score_ws"].numel() < K.kvc_score_ws_bytes(c, self.hq, e["w"]):
+        dkv = e.get("scoring", "attnv") == "dkv"
+        if dkv:
+            need = K.kvc_dkv_ws_bytes(c, b["g"].shape[0])
+            if b["dkv_ws"] is None or b["dkv_ws"].numel() < need:
+                b["dkv_ws"] = torch.empty(need, dtype=torch.uint8, device=c.k.device)
+        elif b["score_ws"].numel() < K.kvc_score_ws_bytes(c, self.hq, e["w"]):
             b["score_ws"] = torch.zeros(K.kvc_score_ws_bytes(c, self.hq, e["w"]),
                                         dtype=torch.uint8, device=c.k.device)
         for slot, leader in enumerate(self.leaders):
-            q_obs, lse = windows[slot]
-            K.kvc_score(c, slot, q_obs, score, rng, lse, None if lse is not None else b["score_ws"])
+            if dkv:
+                g = b["g"]
+                K.kvc_gaussian_bf16(g.numel(), e["seed"] + r, leader, 0xFFFFFFFF, g)
+                K.kvc_dkv_score(c, slot, g, score, rng, b["dkv_ws"])
+            else:
+                q_obs, lse = windows[slot]
+                K.kvc_score(c, slot, q_obs, score, rng, lse,
+                            None if lse is not None else b["score_ws"])
             K.kvc_select(score, rng, nb, hkv, T, e["K"], e["B"], e["N_v"], e["seed"] + r, leader,
                          kept, b["sel_ws"])
             K.kvc_compact(c, slot, kept, n_keep, dst)
         dst.t_len = n_keep
         self.cache, self.spare = dst, c
 
-    def initial_pass(self, q_obs_by_slot):
-        """Compress the prompt cache once (pass 0, two-pass scores)."""
-        self.evict([(q, None) for q in q_obs_by_slot], 0)
+    def initial_pass(self, q_obs_by_slot=None):
+        """Compress the prompt cache once (pass 0; window scores take two
+        passes here, VASE-DKV scores need no queries)."""
+        qs = q_obs_by_slot or [None] * len(self.leaders)
+        self.evict([(q, None) for q in qs], 0)
 
     # ------------------------------------------------------------------ events
     def _ev_begin(self):

@@ -5,10 +5,10 @@ Tolerance of the scores (derived from the arithmetic, not fitted): Y = [K|V] G
 is accumulated in float32 from exact bf16 products over 256 terms, so each
 entry carries a relative error of a few 1e-7; the Gram matrix and its
 factorisation are float64 and add nothing; the float32 inverse factor W and
-the float32 quadratic form each add rounding of order cond(Y) * 1e-7.  For
-the synthetic slabs cond(Y) stays below ~30, so the bound used is
-|l_gpu - l_ref| <= 2e-5 * max(l_ref) + 1e-6 * l_ref per row; the sum of the
-scores must equal rank(Y) to 1e-4 relative."""
+the float32 quadratic form each add rounding of order cond(Y) * 1e-7.  A
+Gaussian sketch of these slabs has cond(Y) of order 10, so the bound used is
+|l_gpu - l_ref| <= 5e-6 * max(l_ref) + 1e-6 * l_ref per row (measured: below
+5e-7 * max); the sum of the scores must equal rank(Y) to 1e-4 relative."""
 import sys
 
 import numpy as np
@@ -68,7 +68,7 @@ DKV_CASES = [
 
 def check_scores(got, ref):
     err = np.abs(got - ref)
-    bound = 2e-5 * ref.max() + 1e-6 * ref
+    bound = 5e-6 * ref.max() + 1e-6 * ref
     assert np.all(err <= bound), float((err / (ref.max())).max())
     return float(err.max() / ref.max())
 
@@ -167,8 +167,48 @@ def test_dkv_kept_sets_match_oracle():
         for t in diff:
             # a row may flip when its key and the cutoff's are closer than
             # the score tolerance (relative to the row's own score) allows
-            eps = 2 * (2e-5 * sc.max() / sc[t] + 1e-6)
+            eps = 2 * (5e-6 * sc.max() / sc[t] + 1e-6)
             assert abs(d["kappa"][t] - kc) <= eps * kc, (j, t)
         ties += len(diff)
         assert len(diff) <= 8
     say(f"  rows flipped inside the score tolerance: {ties}")
+
+
+def test_decoder_dkv_initial_pass():
+    """The decode loop's VASE-DKV pass: G drawn by the library per leader
+    (key seed + pass, counter (pair, leader layer, 0xFFFFFFFF)), scores,
+    selection and compaction; the oracle regenerates G from the same
+    definition and selects on its own scores."""
+    from decode_attention_kvc_amd.loop import Decoder
+    say("decoder dkv initial pass")
+    L, leaders, nb, hq, hkv, T0 = 4, [0, 2], 2, 16, 4, 3000
+    ev = dict(K=1024, B=64, N_v=32, w=32, period=64, seed=11, scoring="dkv", rank=32)
+    big = make_cache(len(leaders), nb, hkv, T0, seed=4)
+    pre = [slab_np(big, s) for s in range(len(leaders))]
+    cap = ev["K"] + ev["B"] + ev["period"]
+    cache = kvc.Cache.empty(len(leaders), nb, hkv, cap, device=DEV)
+    dec = Decoder(L, leaders, big, cache, hq, evict=ev)
+    dec.initial_pass()
+    torch.cuda.synchronize()
+    assert dec.cache.t_len == ev["K"] + ev["B"]
+    flips = 0
+    for s, leader in enumerate(leaders):
+        G = odkv.bf16_bits_to_f64(odkv.gaussian_bf16(32 * 256, ev["seed"], leader, 0xFFFFFFFF))
+        G = G.reshape(32, 256).T
+        K0, V0 = pre[s]
+        K1, V1 = slab_np(dec.cache, s)
+        for b in range(nb):
+            for j in range(hkv):
+                sc = odkv.dkv_score(K0[b, j], V0[b, j], G)
+                d = oracle.select_detail(sc, oracle.value_range(V0[b, j]), T0, ev["K"], ev["B"],
+                                         ev["N_v"], ev["seed"], leader, b, j)
+                rows = {K0[b, j, t].tobytes(): t for t in range(T0)}
+                kept = np.array([rows[K1[b, j, i].tobytes()] for i in range(len(K1[b, j]))])
+                assert np.all(np.diff(kept) > 0)
+                assert np.array_equal(V1[b, j], V0[b, j, kept])
+                diff = set(kept.tolist()) ^ set(d["kept"].tolist())
+                for t in diff:
+                    eps = 2 * (5e-6 * sc.max() / sc[t] + 1e-6)
+                    assert abs(d["kappa"][t] - d["kappa_cut"]) <= eps * d["kappa_cut"]
+                flips += len(diff)
+    say(f"  rows flipped inside the score tolerance: {flips}")
