@@ -25,8 +25,8 @@
 //     The value range of the tile is taken from the same V registers.  Each
 //     workgroup writes its partial Gram (float64).
 //  2. dkv_factor: one wave per slab sums the partial Grams in split order,
-//     factors them (Cholesky with dropped pivots, float64) and writes
-//     W = R^{-1} (zero rows for dropped directions) as float32.
+//     factors them (Cholesky with dropped pivots, float64, in registers) and
+//     writes W = R^{-1} (zero rows for dropped directions) as float32.
 //  3. dkv_leverage: score_t = ||y_t W||^2, one thread per row.
 #include <type_traits>
 
@@ -263,55 +263,72 @@ __global__ __launch_bounds__(256) void dkv_sketch(DkvLaunch p) {
     }
 }
 
-// One wave per slab: merge, factor, invert.
+// Broadcast of lane `src`'s double (src is a compile-time constant in the
+// unrolled loops below, so this is two v_readlane into scalar registers).
+__device__ __forceinline__ double lane_bcast(double v, int src) {
+    const long long bits = __builtin_bit_cast(long long, v);
+    const int lo = __builtin_amdgcn_readlane((int)(bits & 0xFFFFFFFF), src);
+    const int hi = __builtin_amdgcn_readlane((int)(bits >> 32), src);
+    return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
+}
+
+// One wave per slab: merge, factor, invert.  Lane i (< R) keeps column i of
+// the Gram matrix in registers and the factorisation is right-looking: at
+// pivot j every lane turns its entry of row j into U[j][i] and updates its
+// column of the Schur complement, with the row's entries broadcast from the
+// lanes that own them.  The inverse is a back substitution per column, again
+// with broadcast entries of U.  Everything is float64 and fully unrolled.
 template <int R>
 __global__ __launch_bounds__(64) void dkv_factor(DkvLaunch p) {
-    __shared__ double M[R][R + 1];
-    __shared__ double U[R][R + 1];     // upper Cholesky factor
-    __shared__ double Wd[R][R + 1];    // its inverse on the kept directions
-    __shared__ int keep[R];
     const int slab = blockIdx.y * p.hkv + blockIdx.x;
     const int lane = threadIdx.x;
+    const int col = lane < R ? lane : 0;
     const double* part = p.gram + (size_t)slab * p.nsplit * R * R;
-    for (int x = lane; x < R * R; x += 64) {
-        double v = 0.0;
-        for (int sp = 0; sp < p.nsplit; ++sp) v += part[(size_t)sp * R * R + x];
-        M[x / R][x % R] = v;
-        U[x / R][x % R] = 0.0;
-        Wd[x / R][x % R] = 0.0;
+    double m[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) m[k] = 0.0;
+    for (int sp = 0; sp < p.nsplit; ++sp) {
+#pragma unroll
+        for (int k = 0; k < R; ++k) m[k] += part[((size_t)sp * R + k) * R + col];
     }
-    __syncthreads();
     double tr = 0.0;
-    for (int jj = 0; jj < R; ++jj) tr += M[jj][jj];
+#pragma unroll
+    for (int k = 0; k < R; ++k) tr += lane_bcast(m[k], k);
     const double floor = 1e-12 * fmax(tr, 0.0);
-    // Cholesky, one pivot at a time; lanes take the row's columns.
-    for (int jj = 0; jj < R; ++jj) {
-        double sj = M[jj][jj];
-        for (int k = 0; k < jj; ++k) sj -= U[k][jj] * U[k][jj];
-        const bool kj = sj > floor;
-        const double piv = kj ? sqrt(sj) : 0.0;
-        if (lane == 0) keep[jj] = kj;
-        for (int i = jj + 1 + lane; i < R; i += 64) {
-            double v = M[jj][i];
-            for (int k = 0; k < jj; ++k) v -= U[k][jj] * U[k][i];
-            U[jj][i] = kj ? v / piv : 0.0;
-        }
-        if (lane == 0) U[jj][jj] = piv;
-        __syncthreads();
-    }
-    // W = U^{-1} on the kept directions: column c solves U w = e_c by back
-    // substitution over kept rows (dropped rows stay zero).
-    for (int c = lane; c < R; c += 64) {
-        for (int i = c; i >= 0; --i) {
-            if (!keep[i]) continue;
-            double v = (i == c) ? 1.0 : 0.0;
-            for (int k = i + 1; k <= c; ++k) v -= U[i][k] * Wd[k][c];
-            Wd[i][c] = v / U[i][i];
+
+    double u[R];          // column `col` of U: u[j] = U[j][col]
+    bool keep[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const double piv = lane_bcast(m[j], j);      // Schur complement's M[j][j]
+        keep[j] = piv > floor;
+        const double r = keep[j] ? sqrt(piv) : 1.0;
+        const double uj = (keep[j] && col >= j) ? m[j] / r : 0.0;
+        u[j] = uj;
+        // rows j+1.. of this column: m[k] -= U[j][k] * U[j][col], k <= col
+#pragma unroll
+        for (int k = j + 1; k < R; ++k) {
+            const double ujk = lane_bcast(uj, k);
+            if (k <= col) m[k] -= ujk * uj;
         }
     }
-    __syncthreads();
-    float* w = p.w + (size_t)slab * R * R;
-    for (int x = lane; x < R * R; x += 64) w[x] = (float)Wd[x / R][x % R];
+    // W = U^{-1} on the kept directions, column `col`: back substitution.
+    double w[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) w[i] = 0.0;
+#pragma unroll
+    for (int i = R - 1; i >= 0; --i) {
+        double acc = (i == col) ? 1.0 : 0.0;
+#pragma unroll
+        for (int k = i + 1; k < R; ++k) acc -= lane_bcast(u[i], k) * w[k];
+        const double uii = lane_bcast(u[i], i);
+        w[i] = (keep[i] && i <= col) ? acc / uii : 0.0;
+    }
+    if (lane < R) {
+        float* wo = p.w + (size_t)slab * R * R;
+#pragma unroll
+        for (int i = 0; i < R; ++i) wo[i * R + col] = (float)w[i];
+    }
 }
 
 // score_t = ||y_t W||^2, W upper triangular; one thread per row.
