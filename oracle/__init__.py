@@ -19,11 +19,14 @@ Parity status of each function (what pins it is in tests/test_oracle_*.py):
                   round-to-nearest-even cases, normal law)
   dkv.dkv_score   pinned (QR and SVD leverage, closed two-row form,
                   subspace invariance, rank deficiency, isolated rows)
+  quant.*         pinned (hand values with half-even rounding, the rounding
+                  bound, power-of-two scalings, the protection rule, exact
+                  cases equal to plain attention, the large-range-row claim)
 End-to-end model quality (does the eviction keep accuracy?) is parity
 unpinned: it needs trained weights and datasets that are not available.
 """
 from .philox import philox4, philox4x32_10, seed_key, mulhilo
-from . import dkv
+from . import dkv, quant
 from .kvc_oracle import (
     share_map, append_row, attention, decode_attention, value_range,
     window_score, philox_word0, exp_variate, select, select_detail, compact,
@@ -34,5 +37,5 @@ __all__ = [
     "philox4", "philox4x32_10", "seed_key", "mulhilo", "share_map",
     "append_row", "attention", "decode_attention", "value_range",
     "window_score", "philox_word0", "exp_variate", "select", "select_detail",
-    "compact", "eviction_due", "run_decode", "dkv",
+    "compact", "eviction_due", "run_decode", "dkv", "quant",
 ]
