@@ -26,7 +26,8 @@ EXPORTS = (
     "kvc_decode_attn_ws_bytes", "kvc_decode_attn", "kvc_value_range",
     "kvc_score_ws_bytes", "kvc_score", "kvc_select_ws_bytes", "kvc_select",
     "kvc_compact", "kvc_philox_words", "kvc_dkv_ws_bytes", "kvc_dkv_score",
-    "kvc_gaussian_bf16",
+    "kvc_gaussian_bf16", "kvc_q8_quantize", "kvc_q8_append", "kvc_q8_decode_attn_ws_bytes",
+    "kvc_q8_decode_attn",
 )
 
 
@@ -43,6 +44,15 @@ class kvc_cache(ctypes.Structure):
                 ("t_len", ctypes.c_int32), ("t_cap", ctypes.c_int32)]
 
 
+class kvc_qcache(ctypes.Structure):
+    _fields_ = [("kq", ctypes.c_void_p), ("vq", ctypes.c_void_p), ("sk", ctypes.c_void_p),
+                ("sv", ctypes.c_void_p), ("kp", ctypes.c_void_p), ("vp", ctypes.c_void_p),
+                ("n_slots", ctypes.c_int32), ("nb", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("t_len", ctypes.c_int32), ("t_cap", ctypes.c_int32),
+                ("p_len", ctypes.c_int32), ("p_cap", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -57,6 +67,7 @@ def lib():
         vp, i32, i64, sz, f32 = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                  ctypes.c_size_t, ctypes.c_float)
         cp = ctypes.POINTER(kvc_cache)
+        qp = ctypes.POINTER(kvc_qcache)
         ip = ctypes.POINTER(ctypes.c_int32)
         szp = ctypes.POINTER(ctypes.c_size_t)
         sig = {
@@ -80,6 +91,11 @@ def lib():
             "kvc_dkv_score": ([cp, i32, vp, i32, vp, vp, vp, sz, vp], i32),
             "kvc_gaussian_bf16": ([i64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, vp,
                                    vp], i32),
+            "kvc_q8_quantize": ([cp, i32, vp, i32, qp, vp], i32),
+            "kvc_q8_append": ([qp, i32, vp, vp, vp], i32),
+            "kvc_q8_decode_attn_ws_bytes": ([qp, i32, i32, szp], i32),
+            "kvc_q8_decode_attn": ([qp, vp, i64, i32, ip, i32, f32, vp, i64, vp, i64, vp, sz,
+                                    vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -189,6 +205,66 @@ class Cache:
         if rem:
             self.v[slot, :, :, nfull, :, :rem].copy_(v_rows[:, :, nfull * V_TILE:].transpose(-1, -2))
         self.t_len = T
+
+
+@dataclass
+class QCache:
+    """A range-protected int8 cache in libkvc's layout (see include/kvc.h).
+
+    kq: uint8 [n_slots][nb][hkv][t_cap][128] key codes + 128;
+    vq: uint8 [n_slots][nb][hkv][t_cap/32][128][32] value codes + 128;
+    sk, sv: float32 [n_slots][nb][hkv][t_cap] row scales (sk < 0: protected);
+    kp, vp: bf16 protected rows, [n_slots][nb][hkv][p_cap][128] and tiled."""
+    kq: torch.Tensor
+    vq: torch.Tensor
+    sk: torch.Tensor
+    sv: torch.Tensor
+    kp: torch.Tensor
+    vp: torch.Tensor
+    t_len: int
+    p_len: int
+
+    @staticmethod
+    def empty(n_slots, nb, n_kv_heads, t_cap, p_cap, device="cuda"):
+        t_cap = int(math.ceil(t_cap / T_ALIGN) * T_ALIGN)
+        p_cap = int(math.ceil(max(p_cap, 1) / T_ALIGN) * T_ALIGN)
+        u8 = dict(dtype=torch.uint8, device=device)
+        kq = torch.empty((n_slots, nb, n_kv_heads, t_cap, HEAD_DIM), **u8)
+        vq = torch.empty((n_slots, nb, n_kv_heads, t_cap // V_TILE, HEAD_DIM, V_TILE), **u8)
+        sk = torch.empty((n_slots, nb, n_kv_heads, t_cap), dtype=torch.float32, device=device)
+        sv = torch.empty_like(sk)
+        kp = Cache.empty(n_slots, nb, n_kv_heads, p_cap, device=device)
+        return QCache(kq, vq, sk, sv, kp.k, kp.v, 0, 0)
+
+    @property
+    def n_slots(self):
+        return self.kq.shape[0]
+
+    @property
+    def nb(self):
+        return self.kq.shape[1]
+
+    @property
+    def n_kv_heads(self):
+        return self.kq.shape[2]
+
+    @property
+    def t_cap(self):
+        return self.kq.shape[3]
+
+    @property
+    def p_cap(self):
+        return self.kp.shape[3]
+
+    def desc(self):
+        return kvc_qcache(self.kq.data_ptr(), self.vq.data_ptr(), self.sk.data_ptr(),
+                          self.sv.data_ptr(), self.kp.data_ptr(), self.vp.data_ptr(),
+                          self.n_slots, self.nb, self.n_kv_heads, HEAD_DIM, int(self.t_len),
+                          self.t_cap, int(self.p_len), self.p_cap)
+
+    def nbytes_per_row(self):
+        """HBM bytes decode attention reads per quantized row (codes + scales)."""
+        return 2 * HEAD_DIM + 2 * 4
 
 
 # ---------------------------------------------------------------------------
@@ -309,3 +385,40 @@ def kvc_dkv_score(cache, slot, g, score, rng=None, ws=None, stream=None):
 def kvc_gaussian_bf16(n, seed, c1, c2, out, stream=None):
     _check(lib().kvc_gaussian_bf16(n, int(seed) & (2**64 - 1), c1, c2, _ptr(out),
                                    _stream(stream)), "kvc_gaussian_bf16")
+
+
+def kvc_q8_quantize(src, slot, protect, n_protect, dst, stream=None):
+    """protect: device int32 [nb][hkv][n_protect] ascending (None if 0).
+    Sets dst.t_len and dst.p_len before the call."""
+    dst.t_len, dst.p_len = src.t_len, n_protect
+    cs, cd = src.desc(), dst.desc()
+    _check(lib().kvc_q8_quantize(ctypes.byref(cs), slot, _ptr(protect), n_protect,
+                                 ctypes.byref(cd), _stream(stream)), "kvc_q8_quantize")
+
+
+def kvc_q8_append(cache, slot, k_new, v_new, stream=None):
+    c = cache.desc()
+    _check(lib().kvc_q8_append(ctypes.byref(c), slot, _ptr(k_new), _ptr(v_new), _stream(stream)),
+           "kvc_q8_append")
+
+
+def kvc_q8_decode_attn_ws_bytes(cache, n_q_layers, n_q_heads):
+    c = cache.desc()
+    out = ctypes.c_size_t()
+    _check(lib().kvc_q8_decode_attn_ws_bytes(ctypes.byref(c), n_q_layers, n_q_heads,
+                                             ctypes.byref(out)), "kvc_q8_decode_attn_ws_bytes")
+    return out.value
+
+
+def kvc_q8_decode_attn(cache, q, q_slot, out, lse, ws, n_q_heads=None, scale=0.0,
+                       q_layer_stride=0, out_layer_stride=0, lse_layer_stride=0, stream=None):
+    """q: bf16 [nq][nb][Hq][d] (or strided); out float32 like q."""
+    c = cache.desc()
+    nq = len(q_slot)
+    hq = n_q_heads if n_q_heads is not None else q.shape[-2]
+    slots = (ctypes.c_int32 * max(1, nq))(*[int(x) for x in q_slot])
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().kvc_q8_decode_attn(ctypes.byref(c), _ptr(q), q_layer_stride, nq, slots, hq,
+                                    float(scale), _ptr(out), out_layer_stride, _ptr(lse),
+                                    lse_layer_stride, _ptr(ws), ws_bytes, _stream(stream)),
+           "kvc_q8_decode_attn")

@@ -140,6 +140,91 @@ ScoreWs score_ws_layout(int dtype, int rows, int t_len, int slabs) {
     return w;
 }
 
+// ---- attention launches ----------------------------------------------------
+// Group the q-layers by slot (first-appearance order) and cut each group into
+// launches of at most chunk_ql q-layers: fn(slot, q-layer ids, count).
+template <typename F>
+int for_each_attn_chunk(int n_slots, int n_q_layers, const int32_t* q_slot, int chunk_ql, F&& fn) {
+    std::vector<char> done(n_slots, 0);
+    for (int i = 0; i < n_q_layers; ++i) {
+        const int slot = q_slot[i];
+        if (done[slot]) continue;
+        done[slot] = 1;
+        std::vector<int> members;
+        for (int k = i; k < n_q_layers; ++k)
+            if (q_slot[k] == slot) members.push_back(k);
+        for (size_t m0 = 0; m0 < members.size(); m0 += chunk_ql) {
+            const int nql = (int)std::min<size_t>(chunk_ql, members.size() - m0);
+            const int st = fn(slot, members.data() + m0, nql);
+            if (st) return st;
+        }
+    }
+    return KVC_OK;
+}
+
+// The fields every attention launch of one chunk shares.
+void fill_attn(AttnLaunch& p, int nb, int hkv, int g, int hq, int t_len, int t_cap,
+               const int* members, int nql, int64_t qs, int64_t os, int64_t ls, const void* q,
+               float* out, float* lse, float scale) {
+    memset(&p, 0, sizeof(p));
+    p.nb = nb;
+    p.hkv = hkv;
+    p.g = g;
+    p.hq = hq;
+    p.t_len = t_len;
+    p.t_cap = t_cap;
+    p.nql = nql;
+    p.rows = nql * g;
+    for (int x = 0; x < nql; ++x) {
+        p.q_off[x] = members[x] * qs;
+        p.out_off[x] = members[x] * os;
+        p.lse_off[x] = members[x] * ls;
+    }
+    p.q = q;
+    p.out = out;
+    p.lse = lse;
+    p.scale = scale;
+}
+
+// ---- int8 range-protected caches --------------------------------------------
+int check_qcache(const kvc_qcache* c) {
+    if (!c) return KVC_EALIGN;
+    if (c->head_dim != KVC_HEAD_DIM) return KVC_EINVAL;
+    if (c->n_slots < 1 || c->nb < 0 || c->n_kv_heads < 1) return KVC_EINVAL;
+    if (c->t_cap < 0 || c->t_len < 0 || c->t_len > c->t_cap || c->t_cap % KVC_T_ALIGN)
+        return KVC_EINVAL;
+    if (c->p_cap < 0 || c->p_len < 0 || c->p_len > c->p_cap || c->p_cap % KVC_T_ALIGN)
+        return KVC_EINVAL;
+    if (c->p_len > c->t_len) return KVC_EINVAL;
+    if (!aligned16(c->kq) || !aligned16(c->vq) || !aligned16(c->sk) || !aligned16(c->sv))
+        return KVC_EALIGN;
+    if (c->p_cap > 0 && (!aligned16(c->kp) || !aligned16(c->vp))) return KVC_EALIGN;
+    return KVC_OK;
+}
+size_t q_slot_rows(const kvc_qcache* c) { return (size_t)c->nb * c->n_kv_heads * c->t_cap; }
+size_t p_slot_rows(const kvc_qcache* c) { return (size_t)c->nb * c->n_kv_heads * c->p_cap; }
+uint8_t* q_kq(const kvc_qcache* c, int slot) {
+    return static_cast<uint8_t*>(c->kq) + (size_t)slot * q_slot_rows(c) * KVC_HEAD_DIM;
+}
+uint8_t* q_vq(const kvc_qcache* c, int slot) {
+    return static_cast<uint8_t*>(c->vq) + (size_t)slot * q_slot_rows(c) * KVC_HEAD_DIM;
+}
+float* q_sk(const kvc_qcache* c, int slot) { return c->sk + (size_t)slot * q_slot_rows(c); }
+float* q_sv(const kvc_qcache* c, int slot) { return c->sv + (size_t)slot * q_slot_rows(c); }
+uint16_t* q_kp(const kvc_qcache* c, int slot) {
+    return static_cast<uint16_t*>(c->kp) + (size_t)slot * p_slot_rows(c) * KVC_HEAD_DIM;
+}
+uint16_t* q_vp(const kvc_qcache* c, int slot) {
+    return static_cast<uint16_t*>(c->vp) + (size_t)slot * p_slot_rows(c) * KVC_HEAD_DIM;
+}
+
+// Quantized and protected tiles are planned together as one tile range.
+int q8_virtual_rows(const kvc_qcache* c) {
+    const int nq = (c->t_len + ATTN_TILE - 1) / ATTN_TILE;
+    const int np = (c->p_len + ATTN_TILE - 1) / ATTN_TILE;
+    return (nq + np) * ATTN_TILE;
+}
+
 // ---- VASE-DKV planning -----------------------------------------------------
 constexpr int DKV_TILE = 32;
 
@@ -267,61 +352,34 @@ int kvc_decode_attn(const kvc_cache* c, const void* q, int64_t q_layer_stride, i
     const hipStream_t s = (hipStream_t)stream;
     const int slabs = c->nb * c->n_kv_heads;
 
-    // Group q-layers by slot (first appearance order) and cut each group into
-    // launches of at most max_rows_per_chunk rows.
-    std::vector<int> order;
-    std::vector<char> done(c->n_slots, 0);
     bool append_done = false;
     const int64_t qs = q_layer_stride ? q_layer_stride : packed_q;
     const int64_t os = out_layer_stride ? out_layer_stride : packed_q;
     const int64_t ls = lse_layer_stride ? lse_layer_stride : packed_l;
     const int chunk_ql = max_rows_per_chunk(c->dtype, g) / g;
-    for (int i = 0; i < n_q_layers; ++i) {
-        const int slot = q_slot[i];
-        if (done[slot]) continue;
-        done[slot] = 1;
-        std::vector<int> members;
-        for (int k = i; k < n_q_layers; ++k)
-            if (q_slot[k] == slot) members.push_back(k);
-        for (size_t m0 = 0; m0 < members.size(); m0 += chunk_ql) {
-            const int nql = (int)std::min<size_t>(chunk_ql, members.size() - m0);
-            AttnLaunch p;
-            memset(&p, 0, sizeof(p));
-            p.k = slot_k(c, slot);
-            p.v = slot_v(c, slot);
-            p.nb = c->nb;
-            p.hkv = c->n_kv_heads;
-            p.g = g;
-            p.hq = n_q_heads;
-            p.t_len = c->t_len;
-            p.t_cap = c->t_cap;
-            p.nql = nql;
-            p.rows = nql * g;
-            for (int x = 0; x < nql; ++x) {
-                const int qi = members[m0 + x];
-                p.q_off[x] = qi * qs;
-                p.out_off[x] = qi * os;
-                p.lse_off[x] = qi * ls;
-            }
-            p.q = q;
-            p.out = out;
-            p.lse = lse;
-            p.scale = scale;
-            p.append_read = (slot == append_slot);
-            p.append_write = (slot == append_slot) && !append_done;
-            if (p.append_read) {
-                p.k_new = k_new;
-                p.v_new = v_new;
-            }
-            const AttnPlan pl = plan_attn(c->dtype, p.rows, c->t_len, slabs);
-            p.rp = pl.rp;
-            p.nsplit = pl.nsplit;
-            p.tps = pl.tps;
-            p.part = static_cast<float*>(ws);
-            if (launch_attn(p, c->dtype, pl.nt, s) != hipSuccess) return KVC_EHIP;
-            if (p.append_write) append_done = true;
+    st = for_each_attn_chunk(c->n_slots, n_q_layers, q_slot, chunk_ql,
+                             [&](int slot, const int* members, int nql) {
+        AttnLaunch p;
+        fill_attn(p, c->nb, c->n_kv_heads, g, n_q_heads, c->t_len, c->t_cap, members, nql, qs,
+                  os, ls, q, out, lse, scale);
+        p.k = slot_k(c, slot);
+        p.v = slot_v(c, slot);
+        p.append_read = (slot == append_slot);
+        p.append_write = (slot == append_slot) && !append_done;
+        if (p.append_read) {
+            p.k_new = k_new;
+            p.v_new = v_new;
         }
-    }
+        const AttnPlan pl = plan_attn(c->dtype, p.rows, c->t_len, slabs);
+        p.rp = pl.rp;
+        p.nsplit = pl.nsplit;
+        p.tps = pl.tps;
+        p.part = static_cast<float*>(ws);
+        if (launch_attn(p, c->dtype, pl.nt, s) != hipSuccess) return (int)KVC_EHIP;
+        if (p.append_write) append_done = true;
+        return (int)KVC_OK;
+    });
+    if (st) return st;
     if (append_slot >= 0 && !append_done) {
         if (launch_append(slot_k(c, append_slot), slot_v(c, append_slot), c->nb, c->n_kv_heads,
                           c->t_len, c->t_cap, k_new, v_new, (int)elem_size(c->dtype),
@@ -485,6 +543,162 @@ int kvc_compact(const kvc_cache* src, int slot, const int32_t* kept, int n_keep,
     p.n_keep = n_keep;
     p.elem = (int)es;
     if (launch_compact(p, (hipStream_t)stream) != hipSuccess) return KVC_EHIP;
+    return hip_status();
+}
+
+int kvc_q8_quantize(const kvc_cache* src, int slot, const int32_t* protect, int n_protect,
+                    const kvc_qcache* dst, kvc_stream_t stream) {
+    int st = check_cache(src);
+    if (st) return st;
+    st = check_qcache(dst);
+    if (st) return st;
+    if (src->dtype != KVC_BF16) return KVC_EDTYPE;
+    if (src->nb != dst->nb || src->n_kv_heads != dst->n_kv_heads) return KVC_EINVAL;
+    if (slot < 0 || slot >= src->n_slots || slot >= dst->n_slots) return KVC_EINVAL;
+    if (dst->t_len != src->t_len || dst->p_len != n_protect) return KVC_EINVAL;
+    if (n_protect < 0 || n_protect > dst->p_cap || n_protect > src->t_len) return KVC_EINVAL;
+    if (src->nb == 0 || src->t_len == 0) return KVC_OK;
+    if (n_protect > 0 && !aligned4(protect)) return KVC_EALIGN;
+    const hipStream_t s = (hipStream_t)stream;
+    Q8QuantLaunch p;
+    memset(&p, 0, sizeof(p));
+    p.k = slot_k(src, slot);
+    p.v = slot_v(src, slot);
+    p.nb = src->nb;
+    p.hkv = src->n_kv_heads;
+    p.t_len = src->t_len;
+    p.src_t_cap = src->t_cap;
+    p.protect = protect;
+    p.n_protect = n_protect;
+    p.kq = q_kq(dst, slot);
+    p.vq = q_vq(dst, slot);
+    p.sk = q_sk(dst, slot);
+    p.sv = q_sv(dst, slot);
+    p.dst_t_cap = dst->t_cap;
+    if (launch_q8_quantize(p, s) != hipSuccess) return KVC_EHIP;
+    if (n_protect > 0) {
+        // the protected rows, gathered into the bf16 mini-slabs
+        CompactLaunch cp;
+        memset(&cp, 0, sizeof(cp));
+        cp.sk = slot_k(src, slot);
+        cp.sv = slot_v(src, slot);
+        cp.dk = q_kp(dst, slot);
+        cp.dv = q_vp(dst, slot);
+        cp.nb = src->nb;
+        cp.hkv = src->n_kv_heads;
+        cp.src_t_len = src->t_len;
+        cp.src_t_cap = src->t_cap;
+        cp.dst_t_cap = dst->p_cap;
+        cp.kept = protect;
+        cp.n_keep = n_protect;
+        cp.elem = 2;
+        if (launch_compact(cp, s) != hipSuccess) return KVC_EHIP;
+    }
+    return hip_status();
+}
+
+int kvc_q8_append(const kvc_qcache* c, int slot, const void* k_new, const void* v_new,
+                  kvc_stream_t stream) {
+    int st = check_qcache(c);
+    if (st) return st;
+    if (slot < 0 || slot >= c->n_slots || c->t_len < 1) return KVC_EINVAL;
+    if (!aligned16(k_new) || !aligned16(v_new)) return KVC_EALIGN;
+    if (c->nb == 0) return KVC_OK;
+    Q8QuantLaunch p;
+    memset(&p, 0, sizeof(p));
+    p.nb = c->nb;
+    p.hkv = c->n_kv_heads;
+    p.t_len = c->t_len;
+    p.kq = q_kq(c, slot);
+    p.vq = q_vq(c, slot);
+    p.sk = q_sk(c, slot);
+    p.sv = q_sv(c, slot);
+    p.dst_t_cap = c->t_cap;
+    p.k_row = k_new;
+    p.v_row = v_new;
+    if (launch_q8_quantize(p, (hipStream_t)stream) != hipSuccess) return KVC_EHIP;
+    return hip_status();
+}
+
+int kvc_q8_decode_attn_ws_bytes(const kvc_qcache* c, int n_q_layers, int n_q_heads,
+                                size_t* bytes) {
+    int st = check_qcache(c);
+    if (st) return st;
+    if (!bytes) return KVC_EALIGN;
+    if (n_q_layers < 0 || n_q_heads < 1 || n_q_heads % c->n_kv_heads) return KVC_EINVAL;
+    const int g = n_q_heads / c->n_kv_heads;
+    if (g > 64) return KVC_EINVAL;
+    const int rows = std::min(std::max(1, n_q_layers) * g, max_rows_per_chunk(KVC_BF16, g));
+    const int slabs = c->nb * c->n_kv_heads;
+    const int vmax = ((c->t_cap + ATTN_TILE - 1) / ATTN_TILE +
+                      (c->p_cap + ATTN_TILE - 1) / ATTN_TILE) * ATTN_TILE;
+    size_t part = 0;
+    for (int t = ATTN_TILE; t <= std::max(ATTN_TILE, vmax); t += ATTN_TILE)
+        part = std::max(part, attn_ws_for(KVC_BF16, rows, t, slabs));
+    *bytes = part;
+    return KVC_OK;
+}
+
+int kvc_q8_decode_attn(const kvc_qcache* c, const void* q, int64_t q_layer_stride,
+                       int n_q_layers, const int32_t* q_slot, int n_q_heads, float scale,
+                       float* out, int64_t out_layer_stride, float* lse, int64_t lse_layer_stride,
+                       void* ws, size_t ws_bytes, kvc_stream_t stream) {
+    int st = check_qcache(c);
+    if (st) return st;
+    if (n_q_layers < 0 || n_q_heads < 1 || n_q_heads % c->n_kv_heads) return KVC_EINVAL;
+    const int g = n_q_heads / c->n_kv_heads;
+    if (g > 64) return KVC_EINVAL;
+    if (!isfinite(scale) || scale < 0.f) return KVC_EINVAL;
+    const int64_t packed_q = (int64_t)c->nb * n_q_heads * KVC_HEAD_DIM;
+    const int64_t packed_l = (int64_t)c->nb * n_q_heads;
+    if (q_layer_stride < 0 || out_layer_stride < 0 || lse_layer_stride < 0) return KVC_EINVAL;
+    if (q_layer_stride && q_layer_stride < packed_q) return KVC_EINVAL;
+    if (out_layer_stride && out_layer_stride < packed_q) return KVC_EINVAL;
+    if (lse_layer_stride && lse_layer_stride < packed_l) return KVC_EINVAL;
+    if (n_q_layers == 0 || c->nb == 0) return KVC_OK;
+    if (c->t_len < 1) return KVC_EINVAL;
+    if (!q_slot) return KVC_EALIGN;
+    for (int i = 0; i < n_q_layers; ++i)
+        if (q_slot[i] < 0 || q_slot[i] >= c->n_slots) return KVC_EINVAL;
+    if (!aligned16(q) || !aligned16(out)) return KVC_EALIGN;
+    if (q_layer_stride % 8) return KVC_EALIGN;
+    if (lse && !aligned4(lse)) return KVC_EALIGN;
+    size_t need = 0;
+    st = kvc_q8_decode_attn_ws_bytes(c, n_q_layers, n_q_heads, &need);
+    if (st) return st;
+    if (!ws || ws_bytes < need || !aligned16(ws)) return KVC_EWORKSPACE;
+    if (scale == 0.f) scale = 1.0f / sqrtf((float)KVC_HEAD_DIM);
+    const hipStream_t s = (hipStream_t)stream;
+    const int slabs = c->nb * c->n_kv_heads;
+    const int64_t qs = q_layer_stride ? q_layer_stride : packed_q;
+    const int64_t os = out_layer_stride ? out_layer_stride : packed_q;
+    const int64_t ls = lse_layer_stride ? lse_layer_stride : packed_l;
+    const int chunk_ql = max_rows_per_chunk(KVC_BF16, g) / g;
+    const int vrows = q8_virtual_rows(c);
+    st = for_each_attn_chunk(c->n_slots, n_q_layers, q_slot, chunk_ql,
+                             [&](int slot, const int* members, int nql) {
+        Q8AttnLaunch p;
+        memset(&p, 0, sizeof(p));
+        fill_attn(p.a, c->nb, c->n_kv_heads, g, n_q_heads, c->t_len, c->t_cap, members, nql, qs,
+                  os, ls, q, out, lse, scale);
+        p.a.k = q_kq(c, slot);
+        p.a.v = q_vq(c, slot);
+        const AttnPlan pl = plan_attn(KVC_BF16, p.a.rows, vrows, slabs);
+        p.a.rp = pl.rp;
+        p.a.nsplit = pl.nsplit;
+        p.a.tps = pl.tps;
+        p.a.part = static_cast<float*>(ws);
+        p.sk = q_sk(c, slot);
+        p.sv = q_sv(c, slot);
+        p.kp = q_kp(c, slot);
+        p.vp = q_vp(c, slot);
+        p.p_len = c->p_len;
+        p.p_cap = c->p_cap;
+        p.nq_tiles = (c->t_len + ATTN_TILE - 1) / ATTN_TILE;
+        if (launch_attn_q8(p, pl.nt, s) != hipSuccess) return (int)KVC_EHIP;
+        return (int)KVC_OK;
+    });
+    if (st) return st;
     return hip_status();
 }
 

@@ -89,6 +89,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch p) {
         for (int sp = 0; sp < nsplit; ++sp) {
             const float ms = ml[((size_t)sp * rp + r) * 2];
             const float ls = ml[((size_t)sp * rp + r) * 2 + 1];
+            if (ms == -INFINITY) continue;   // a split with no visible row
             const float* a = acc + ((size_t)sp * rp + r) * D + d0;
             const f32x4 a0 = *reinterpret_cast<const f32x4*>(a);
             const f32x4 a1 = *reinterpret_cast<const f32x4*>(a + 4);
@@ -532,8 +533,12 @@ hipError_t launch_attn(const AttnLaunch& p, int dtype, int nt, hipStream_t st) {
             go(attn_bf16_kernel<4, ATTN_WAVES, 1>);
     }
     // bf16 launches with one split per slab finish their rows themselves.
-    if (dtype == 0 || p.nsplit > 1)
-        hipLaunchKernelGGL(attn_combine_kernel, dim3(p.hkv, p.nb), dim3(256), 0, st, p);
+    if (dtype == 0 || p.nsplit > 1) return launch_attn_combine(p, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_combine(const AttnLaunch& p, hipStream_t st) {
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(p.hkv, p.nb), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 

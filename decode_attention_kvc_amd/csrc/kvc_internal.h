@@ -68,6 +68,36 @@ struct ScoreLaunch {
     int rows_pad;
 };
 
+// Decode attention over a range-protected int8 slot.  `a` carries the
+// attention fields (a.k / a.v are the code slot bases, a.t_len / a.t_cap the
+// quantized rows); the protected rows are a bf16 mini-slab per (b, j).
+struct Q8AttnLaunch {
+    AttnLaunch a;
+    const float* sk;        // [nb][hkv][t_cap] key scales; < 0: the row is protected
+    const float* sv;        // [nb][hkv][t_cap] value scales
+    const void* kp;         // bf16 [nb][hkv][p_cap][D]
+    const void* vp;         // bf16 [nb][hkv][p_cap/32][D][32]
+    int p_len, p_cap;
+    int nq_tiles;           // 32-row tiles of quantized rows; protected tiles follow
+};
+
+// Quantization of one bf16 slot into a range-protected int8 slot.
+struct Q8QuantLaunch {
+    const void* k;          // bf16 slot bases of the source
+    const void* v;
+    int nb, hkv, t_len, src_t_cap;
+    const int32_t* protect; // [nb][hkv][n_protect], ascending
+    int n_protect;
+    void* kq;               // uint8 code slot bases of the destination (code + 128)
+    void* vq;
+    float* sk;
+    float* sv;
+    int dst_t_cap;
+    int row0, nrows;        // rows [row0, row0 + nrows) are quantized (an append: one row)
+    const void* k_row;      // append: bf16 [nb][hkv][D] new rows instead of the source slot
+    const void* v_row;
+};
+
 // VASE-DKV scores of one cache slot (bf16).
 struct DkvLaunch {
     const void* k;          // slot base of K
@@ -109,6 +139,9 @@ struct CompactLaunch {
 // hipSuccess or the launch error.
 // Launches the partial kernel and the merge kernel.
 hipError_t launch_attn(const AttnLaunch& p, int dtype, int nt, hipStream_t s);
+hipError_t launch_attn_combine(const AttnLaunch& p, hipStream_t s);
+hipError_t launch_attn_q8(const Q8AttnLaunch& p, int nt, hipStream_t s);
+hipError_t launch_q8_quantize(const Q8QuantLaunch& p, hipStream_t s);
 hipError_t launch_append(const void* k, const void* v, int nb, int hkv, int t_len,
                          int t_cap, const void* k_new, const void* v_new, int elem,
                          hipStream_t s);

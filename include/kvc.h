@@ -94,6 +94,41 @@ typedef struct kvc_cache {
     int32_t t_cap;
 } kvc_cache;
 
+/*
+ * A range-protected int8 cache [VASE §3, §5: large-range value states
+ * dominate per-token quantization error, so they keep full precision].
+ * Per slot, per (batch entry b, KV head j):
+ *   kq: uint8 [t_cap][head_dim]      key codes + 128 (code = round-half-even
+ *                                     of x / scale, clamped to +-127)
+ *   vq: uint8 [t_cap/32][head_dim][32] value codes + 128, 32-token tiles
+ *   sk: float32 [t_cap]               key row scale max|k| / 127; a negative
+ *                                     scale marks a protected row (its codes
+ *                                     are ignored)
+ *   sv: float32 [t_cap]               value row scale max|v| / 127
+ *   kp: bf16 [p_cap][head_dim]        keys of the p_len protected rows
+ *   vp: bf16 [p_cap/32][head_dim][32] values of the protected rows
+ * Slots follow each other in every array; t_cap and p_cap are multiples of
+ * 64, p_len <= t_len, every pointer is 16-byte aligned.  A quantized row
+ * reconstructs as code * scale; attention sees every row once (protected
+ * rows through kp / vp only).
+ */
+typedef struct kvc_qcache {
+    void* kq;
+    void* vq;
+    float* sk;
+    float* sv;
+    void* kp;
+    void* vp;
+    int32_t n_slots;
+    int32_t nb;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t t_len;
+    int32_t t_cap;
+    int32_t p_len;
+    int32_t p_cap;
+} kvc_qcache;
+
 /* Library version as major*10000 + minor*100 + patch. */
 int kvc_version(void);
 
@@ -276,6 +311,47 @@ int kvc_dkv_score(const kvc_cache* c, int slot, const void* g, int rank,
  */
 int kvc_gaussian_bf16(int64_t n, uint64_t seed, uint32_t c1, uint32_t c2,
                       void* out, kvc_stream_t stream);
+
+/*
+ * Range-protected quantization of one bf16 slot into the same slot of an
+ * int8 cache [VASE §3, §5].  protect: device int32 [nb][n_kv_heads]
+ * [n_protect], each list ascending with entries in [0, src->t_len) -- the
+ * rows that keep bf16 (typically the n_protect largest value ranges:
+ * kvc_value_range, then kvc_select with K = N_v = n_protect, B = 0).  Every
+ * other row's key and value are quantized per row.  The caller sets
+ * dst->t_len = src->t_len and dst->p_len = n_protect before the call;
+ * n_protect <= dst->p_cap.  src must be bf16 (KVC_EDTYPE), with the same nb
+ * and n_kv_heads as dst.
+ */
+int kvc_q8_quantize(const kvc_cache* src, int slot, const int32_t* protect,
+                    int n_protect, const kvc_qcache* dst, kvc_stream_t stream);
+
+/*
+ * Leader append into an int8 cache [R-CLA implementation paragraph]: row
+ * t_len - 1 of every slab of `slot` becomes the per-row quantization of
+ * k_new, v_new (device bf16 [nb][n_kv_heads][head_dim]); appended rows are
+ * not protected.  The caller has already bumped t_len.
+ */
+int kvc_q8_append(const kvc_qcache* c, int slot, const void* k_new,
+                  const void* v_new, kvc_stream_t stream);
+
+/* Workspace bytes kvc_q8_decode_attn needs (any t_len <= t_cap). */
+int kvc_q8_decode_attn_ws_bytes(const kvc_qcache* c, int n_q_layers,
+                                int n_q_heads, size_t* bytes);
+
+/*
+ * Decode attention over an int8 range-protected cache: exactly
+ * kvc_decode_attn's contract (same q / out / lse layouts and strides, GQA,
+ * q-layer grouping; no fused append -- use kvc_q8_append first), with each
+ * row's key and value taken as code * scale, or as the bf16 protected row.
+ * q: bf16.  Requires g = n_q_heads / n_kv_heads <= 64.
+ */
+int kvc_q8_decode_attn(const kvc_qcache* c, const void* q,
+                       int64_t q_layer_stride, int n_q_layers,
+                       const int32_t* q_slot, int n_q_heads, float scale,
+                       float* out, int64_t out_layer_stride, float* lse,
+                       int64_t lse_layer_stride, void* ws, size_t ws_bytes,
+                       kvc_stream_t stream);
 
 /*
  * Diagnostic: the device Philox4x32-10 stream that kvc_select draws from.
