@@ -169,6 +169,73 @@ def _cpu_model():
     return "unknown"
 
 
+def int8_leg(args, cfg, dec, qpool, lsepool, knew, vnew, out, steps):
+    """Decode attention over the range-protected int8 form of the current
+    cache: the same per-layer calls (leaders append quantized rows) with no
+    eviction, timed like the main leg."""
+    import torch
+    import decode_attention_kvc_amd as kvc
+    dev = "cuda"
+    c = dec.cache
+    nb, hkv, hq, L = c.nb, c.n_kv_heads, cfg["hq"], cfg["n_layers"]
+    n_slots = c.n_slots
+    T0 = c.t_len
+    P = int(math.ceil(args.protect_frac * T0))
+    qc = kvc.QCache.empty(n_slots, nb, hkv, T0 + steps + 64, max(P, 1), device=dev)
+    for slot in range(n_slots):
+        prot = None
+        if P:
+            rng = torch.empty((nb, hkv, T0), device=dev)
+            kvc.kvc_value_range(c, slot, rng)
+            prot = torch.empty((nb, hkv, P), dtype=torch.int32, device=dev)
+            kvc.kvc_select(rng, rng, nb, hkv, T0, P, 0, P, 0, 0, prot,
+                           torch.empty(kvc.kvc_select_ws_bytes(nb, hkv, T0), dtype=torch.uint8,
+                                       device=dev))
+        kvc.kvc_q8_quantize(c, slot, prot, P, qc)
+    ws = torch.zeros(max(16, kvc.kvc_q8_decode_attn_ws_bytes(qc, 1, hq)), dtype=torch.uint8,
+                     device=dev)
+    n_pool = qpool.shape[1]
+
+    def step(s, events):
+        qc.t_len += 1
+        sp = s % n_pool
+        a = b = None
+        if events is not None:
+            a = torch.cuda.Event(enable_timing=True)
+            a.record()
+        for l in range(L):
+            slot = dec.src_slot[l]
+            if dec.src_layer[l] == l:
+                kvc.kvc_q8_append(qc, slot, knew[sp, slot], vnew[sp, slot])
+            kvc.kvc_q8_decode_attn(qc, qpool[l, sp], [slot], out[l], lsepool[l, sp], ws,
+                                   n_q_heads=hq)
+        if events is not None:
+            b = torch.cuda.Event(enable_timing=True)
+            b.record()
+            events.append((a, b, qc.t_len))
+
+    for s in range(3):
+        step(s, None)
+    torch.cuda.synchronize()
+    events = []
+    t0 = time.perf_counter()
+    for s in range(steps):
+        step(3 + s, events)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = sum(a.elapsed_time(b) for a, b, _ in events)
+    row = 2 * (128 + 4)
+    byts = sum(L * nb * hkv * (t * row + P * 2 * 256) + L * nb * hq * (128 * 2 + 129 * 4)
+               for _, _, t in events)
+    gbps = byts / (ms * 1e-3) / 1e9
+    return dict(value=round(nb * steps / wall, 2), unit="tokens/s",
+                ms_per_step=round(1e3 * wall / steps, 4),
+                attention_GBps=round(gbps, 1), attention_frac=round(gbps / HBM_PEAK_GBPS, 4),
+                avg_launch_us=round(1e3 * ms / (steps * L), 2), protected_rows=P,
+                rows=[T0 + 4, T0 + 3 + steps], bytes_per_row=row,
+                kernel="attn_q8_kernel (+ merge) and q8_append_kernel, per-layer calls, no eviction")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +252,10 @@ def main():
     ap.add_argument("--rank", type=int, default=32, choices=[16, 32],
                     help="sketch columns of the VASE-DKV scores")
     ap.add_argument("--no-grouped", action="store_true", help="skip the grouped-mode leg")
+    ap.add_argument("--no-int8", action="store_true",
+                    help="skip the range-protected int8 cache leg (decode attention only)")
+    ap.add_argument("--protect-frac", type=float, default=0.01,
+                    help="fraction of rows per slab the int8 leg keeps in bf16 (largest ranges)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain 1 GiB device copy (for counter calibration)")
@@ -312,6 +383,11 @@ def main():
                        avg_launch_us=round(1e3 * g_ms / g_calls, 2), eviction_passes=g_ev)
         log(f"[bench] grouped: {grouped}")
 
+    int8 = None
+    if not args.no_int8:
+        int8 = int8_leg(args, cfg, dec, qpool, lsepool, knew, vnew, out, S)
+        log(f"[bench] int8: {int8}")
+
     if args.copy_calibration:
         # Two plain copies of known size for scaling the memory counters:
         # a 1 GiB runtime blit, and a 512 MiB float32 copy done by a
@@ -375,6 +451,7 @@ def main():
         "eviction_passes_timed": n_evict,
         "initial_pass_ms": None if initial_ms is None else round(initial_ms, 3),
         "grouped": grouped,
+        "int8": int8,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
