@@ -10,10 +10,12 @@
 // value range per slab keep bf16 keys and values in a side mini-slab, and
 // their int8 slots are flagged by a negative key scale.  Codes are stored
 // biased (code + 128, an unsigned byte) so that v_cvt_f32_ubyte turns each
-// byte into its float in one instruction; the bias is removed after the
-// products: q . (u - 128) = q . u - 128 sum(q), and sum_t p'_t (u_t - 128) =
-// sum_t p'_t u_t - 128 sum_t p'_t.  The integers 0..255 are exact in bf16,
-// so the MFMA products are exact.
+// byte into an fp16 MFMA operand with one byte permute per two values: the
+// halfword 0x64uu is the fp16 number 1024 + uu, i.e. 1152 + code.  The offset
+// is removed after the products: q . (1152 + c) = q . (1152 + c) - 1152 sum(q),
+// and likewise with the running sum of p * scale for the values.  Products
+// of these integers with fp16 queries / P are exact in the float32
+// accumulators.
 //
 // Layouts (per slab): codes K [t_cap][128] (row-major, 128 bytes a row),
 // codes V [t_cap/32][128][32] (32-token tiles, channel-major, 4 KB a tile),
@@ -24,9 +26,11 @@
 // Decode attention follows the bf16 kernel (split-K, four waves per
 // workgroup, S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16, P
 // split into two bf16 halves, the same permuted K-row order) with two tile
-// kinds in one online softmax: quantized tiles (codes dequantized in
-// registers, row scales folded into the logits and into P) and the slab's
-// protected rows from the bf16 mini-slab.  A lane's 32 key channels are
+// kinds in one online softmax: quantized tiles (fp16 MFMA on the code
+// operands, fp16 queries, P split into two fp16 halves, row scales folded
+// into the logits and into P) and the slab's protected rows from the bf16
+// mini-slab (bf16 MFMA as in the bf16 kernel).  Queries go to fp16 exactly
+// for any normal value above 2^-14 in magnitude.  A lane's 32 key channels are
 // contiguous here (channels 32*lg .. +32, so one row fragment is two 16-byte
 // loads of codes) and the query fragments use the same channel order.
 #include <type_traits>
@@ -43,19 +47,25 @@ constexpr int QT = 32;                 // rows per tile
 constexpr int QMAX = 127;
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x8v __attribute__((ext_vector_type(8)));
+
+constexpr float CODE_OFFSET = 1152.f;
+constexpr float M_FLOOR = -1e30f;      // below any logit of a finite cache   // fp16 0x64uu = 1024 + uu, uu = code + 128
+
+// Four biased codes (one dword) -> two dwords of fp16 halfwords 0x64uu.
+__device__ __forceinline__ uint32_t codes_lo_f16(uint32_t w) {
+    return __builtin_amdgcn_perm(0x64646464u, w, 0x04010400u);
+}
+__device__ __forceinline__ uint32_t codes_hi_f16(uint32_t w) {
+    return __builtin_amdgcn_perm(0x64646464u, w, 0x04030402u);
+}
+__device__ __forceinline__ f16x8 codes8_f16(uint32_t w0, uint32_t w1) {
+    return __builtin_bit_cast(f16x8, u32x4{codes_lo_f16(w0), codes_hi_f16(w0), codes_lo_f16(w1),
+                                           codes_hi_f16(w1)});
+}
 
 __device__ __forceinline__ bf16x8 as_bf(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
-}
-// Eight biased codes (two dwords) -> their values as bf16x8 (exact).
-__device__ __forceinline__ u32x4 codes_to_bf16(uint32_t w0, uint32_t w1) {
-    return u32x4{pack_bf16x2((float)(w0 & 0xff), (float)((w0 >> 8) & 0xff)),
-                 pack_bf16x2((float)((w0 >> 16) & 0xff), (float)(w0 >> 24)),
-                 pack_bf16x2((float)(w1 & 0xff), (float)((w1 >> 8) & 0xff)),
-                 pack_bf16x2((float)((w1 >> 16) & 0xff), (float)(w1 >> 24))};
-}
 
 // Code of x for a row of scale s > 0: round-half-even(x / s), clamped, biased.
 __device__ __forceinline__ uint32_t quant_byte(float x, float s) {
@@ -263,8 +273,10 @@ __global__ __launch_bounds__(256) void attn_q8_kernel(Q8AttnLaunch P) {
     const uint16_t* vp = reinterpret_cast<const uint16_t*>(P.vp) + (size_t)slab * P.p_cap * D;
 
     // Query fragments, channel chunk kc of lane group lg = channels
-    // 32*lg + 8*kc .. +8 (the codes' order); qsum = sum of the row's channels.
+    // 32*lg + 8*kc .. +8 (the codes' order), in bf16 (protected rows) and in
+    // fp16 (codes); qsum = sum of the row's fp16 channels.
     bf16x8 qB[NT][4];
+    f16x8 qH[NT][4];
     float qsum[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -279,22 +291,32 @@ __global__ __launch_bounds__(256) void attn_q8_kernel(Q8AttnLaunch P) {
                 const u32x4 x = load16(qp + 8 * kc);
                 qB[nt][kc] = as_bf(x);
 #pragma unroll
-                for (int w2 = 0; w2 < 4; ++w2) part += bf16lo(x[w2]) + bf16hi(x[w2]);
+                for (int w2 = 0; w2 < 4; ++w2) {
+                    const _Float16 lo = (_Float16)bf16lo(x[w2]), hi = (_Float16)bf16hi(x[w2]);
+                    qH[nt][kc][2 * w2] = lo;
+                    qH[nt][kc][2 * w2 + 1] = hi;
+                    part += (float)lo + (float)hi;
+                }
             }
         } else {
 #pragma unroll
-            for (int kc = 0; kc < 4; ++kc) qB[nt][kc] = as_bf(u32x4{0u, 0u, 0u, 0u});
+            for (int kc = 0; kc < 4; ++kc) {
+                qB[nt][kc] = as_bf(u32x4{0u, 0u, 0u, 0u});
+                qH[nt][kc] = __builtin_bit_cast(f16x8, u32x4{0u, 0u, 0u, 0u});
+            }
         }
         part += __shfl_xor(part, 16);
         part += __shfl_xor(part, 32);
         qsum[nt] = part;
     }
 
+    // The running maxima start at a finite floor, so masked logits (-inf)
+    // always give p = 0 without a guard, even before the first visible row.
     f32x4 acc[NT][8];
-    float m[NT], lsum[NT], psum[NT];   // psum: sum of p * value scale (bias removal)
+    float m[NT], lsum[NT], psum[NT];   // psum: sum of p * value scale (offset removal)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        m[nt] = -INFINITY;
+        m[nt] = M_FLOOR;
         lsum[nt] = 0.f;
         psum[nt] = 0.f;
 #pragma unroll
@@ -305,39 +327,57 @@ __global__ __launch_bounds__(256) void attn_q8_kernel(Q8AttnLaunch P) {
     // Online softmax step shared by both tile kinds: x[jj] are the logits of
     // tile rows 8*lg + jj, pv[jj] the factor each row's p is multiplied by
     // before the value product, V the value fragments.
+    // F16: code tiles (fp16 P halves and value operands, offset mass
+    // tracked in psum); otherwise bf16 protected rows.
     auto softmax_pv = [&](int nt, const float (&x)[8], const float (&pv)[8], const u32x4 (&V)[8],
-                          bool biased) {
+                          auto f16_tag) {
+        constexpr bool F16 = decltype(f16_tag)::value;
         float mx = x[0];
 #pragma unroll
         for (int jj = 1; jj < 8; ++jj) mx = fmaxf(mx, x[jj]);
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float mnew = fmaxf(m[nt], mx);
-        const float alpha = mnew == -INFINITY ? 1.f : exp2f((m[nt] - mnew) * LOG2E);
+        const float alpha = exp2f((m[nt] - mnew) * LOG2E);
         m[nt] = mnew;
         float ps = 0.f, pss = 0.f;
         u16x8 hi, lo;
+        f16x8 hh, ll;
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
-            const float pj = mnew == -INFINITY ? 0.f : exp2f((x[jj] - mnew) * LOG2E);
+            const float pj = exp2f((x[jj] - mnew) * LOG2E);
             ps += pj;
             const float pw = pj * pv[jj];
-            pss += pw;
-            const uint16_t h16 = f32_to_bf16(pw);
-            hi[jj] = h16;
-            lo[jj] = f32_to_bf16(pw - bf16_to_f32(h16));
+            if constexpr (F16) {
+                const _Float16 h = (_Float16)pw;
+                hh[jj] = h;
+                ll[jj] = (_Float16)(pw - (float)h);
+                pss += pw;
+            } else {
+                const uint16_t h16 = f32_to_bf16(pw);
+                hi[jj] = h16;
+                lo[jj] = f32_to_bf16(pw - bf16_to_f32(h16));
+            }
         }
         lsum[nt] = lsum[nt] * alpha + ps;
-        psum[nt] = psum[nt] * alpha + (biased ? pss : 0.f);
-        const bf16x8 pH = __builtin_bit_cast(bf16x8, hi);
-        const bf16x8 pL = __builtin_bit_cast(bf16x8, lo);
+        psum[nt] = psum[nt] * alpha + pss;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
             acc[nt][dt] *= alpha;
-            acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(V[dt]), pH, acc[nt][dt], 0, 0, 0);
-            acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(V[dt]), pL, acc[nt][dt], 0, 0, 0);
+            if constexpr (F16) {
+                const f16x8 vf = __builtin_bit_cast(f16x8, V[dt]);
+                acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, hh, acc[nt][dt], 0, 0, 0);
+                acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, ll, acc[nt][dt], 0, 0, 0);
+            } else {
+                const bf16x8 pH = __builtin_bit_cast(bf16x8, hi);
+                const bf16x8 pL = __builtin_bit_cast(bf16x8, lo);
+                acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(V[dt]), pH, acc[nt][dt], 0, 0, 0);
+                acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(V[dt]), pL, acc[nt][dt], 0, 0, 0);
+            }
         }
     };
+    using F16Tiles = std::integral_constant<bool, true>;
+    using BF16Tiles = std::integral_constant<bool, false>;
 
     // A tile of codes.  TAIL: rows at or past t_len are masked.
     auto compute_q8 = [&](const Q8Regs& R, int t0, auto tail_tag) {
@@ -347,9 +387,11 @@ __global__ __launch_bounds__(256) void attn_q8_kernel(Q8AttnLaunch P) {
         for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc)
-                KF[c][kc] = codes_to_bf16(R.k[c][kc / 2][2 * (kc % 2)], R.k[c][kc / 2][2 * (kc % 2) + 1]);
+                KF[c][kc] = __builtin_bit_cast(
+                    u32x4, codes8_f16(R.k[c][kc / 2][2 * (kc % 2)], R.k[c][kc / 2][2 * (kc % 2) + 1]));
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) V[dt] = codes_to_bf16(R.v[dt][0], R.v[dt][1]);
+        for (int dt = 0; dt < 8; ++dt)
+            V[dt] = __builtin_bit_cast(u32x4, codes8_f16(R.v[dt][0], R.v[dt][1]));
         float skr[8], svr[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -366,10 +408,11 @@ __global__ __launch_bounds__(256) void attn_q8_kernel(Q8AttnLaunch P) {
                 S[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kc = 0; kc < 4; ++kc)
-                    S[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(KF[c][kc]), qB[nt][kc], S[c], 0, 0, 0);
+                    S[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, KF[c][kc]),
+                                                                   qH[nt][kc], S[c], 0, 0, 0);
             }
             // S[c][i]: tile row 8*lg + 4*c + i
-            const float bias = 128.f * qsum[nt];
+            const float bias = CODE_OFFSET * qsum[nt];
             float x[8], pv[8];
 #pragma unroll
             for (int c = 0; c < 2; ++c)
@@ -388,7 +431,7 @@ __global__ __launch_bounds__(256) void attn_q8_kernel(Q8AttnLaunch P) {
                     x[jj] = keep ? v : -INFINITY;
                     pv[jj] = w;
                 }
-            softmax_pv(nt, x, pv, V, true);
+            softmax_pv(nt, x, pv, V, F16Tiles{});
         }
     };
 
@@ -431,7 +474,7 @@ __global__ __launch_bounds__(256) void attn_q8_kernel(Q8AttnLaunch P) {
                     x[jj] = (r0 + 8 * lg + jj < P.p_len) ? S[c][i] * scale : -INFINITY;
                     pv[jj] = 1.f;
                 }
-            softmax_pv(nt, x, pv, V, false);
+            softmax_pv(nt, x, pv, V, BF16Tiles{});
         }
     };
     using Interior = std::integral_constant<bool, false>;
@@ -483,7 +526,7 @@ __global__ __launch_bounds__(256) void attn_q8_kernel(Q8AttnLaunch P) {
         lsum[nt] += __shfl_xor(lsum[nt], 32);
         psum[nt] += __shfl_xor(psum[nt], 16);
         psum[nt] += __shfl_xor(psum[nt], 32);
-        const float corr = 128.f * psum[nt];
+        const float corr = CODE_OFFSET * psum[nt];
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) acc[nt][dt] -= corr;
     }
@@ -515,7 +558,7 @@ __global__ __launch_bounds__(256) void attn_q8_kernel(Q8AttnLaunch P) {
             float f[W], L = 0.f;
 #pragma unroll
             for (int w = 0; w < W; ++w) {
-                f[w] = wm[w][nrow] == -INFINITY ? 0.f : exp2f((wm[w][nrow] - M) * LOG2E);
+                f[w] = exp2f((wm[w][nrow] - M) * LOG2E);
                 L += f[w] * wl[w][nrow];
             }
             float o[EPT];
