@@ -337,8 +337,14 @@ __global__ __launch_bounds__(256) void attn_q8_kernel(Q8AttnLaunch P) {
         for (int jj = 1; jj < 8; ++jj) mx = fmaxf(mx, x[jj]);
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(m[nt], mx);
+        // The reference maximum only moves when a logit exceeds it by more
+        // than 2^8 in p (then p <= 256 against a stale reference, harmless in
+        // float32 and in the fp16/bf16 halves); the accumulators are rescaled
+        // only on the (wave-uniform) tiles where some row moved.
+        const bool move = (mx - m[nt]) * LOG2E > 8.f;
+        const float mnew = move ? mx : m[nt];
         const float alpha = exp2f((m[nt] - mnew) * LOG2E);
+        const bool any_move = __ballot(move) != 0;
         m[nt] = mnew;
         float ps = 0.f, pss = 0.f;
         u16x8 hi, lo;
@@ -361,9 +367,12 @@ __global__ __launch_bounds__(256) void attn_q8_kernel(Q8AttnLaunch P) {
         }
         lsum[nt] = lsum[nt] * alpha + ps;
         psum[nt] = psum[nt] * alpha + pss;
+        if (any_move) {
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) acc[nt][dt] *= alpha;
+        }
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-            acc[nt][dt] *= alpha;
             if constexpr (F16) {
                 const f16x8 vf = __builtin_bit_cast(f16x8, V[dt]);
                 acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, hh, acc[nt][dt], 0, 0, 0);
