@@ -38,6 +38,7 @@ namespace kvc {
 namespace {
 
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float M_FLOOR = -1e30f;      // below any logit of a finite cache
 
 struct TileRegs {
     u32x4 k[2][4];   // K rows: [column block c][d chunk kc]
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(AttnLaunch p) {
     float m[NT], lsum[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        m[nt] = -INFINITY;
+        m[nt] = M_FLOOR;      // finite: the first tile's rows always move it
         lsum[nt] = 0.f;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) acc[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -221,8 +222,13 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(AttnLaunch p) {
             for (int jj = 1; jj < 8; ++jj) mx = fmaxf(mx, sv[jj]);
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mnew = fmaxf(m[nt], mx);
+            // The reference maximum moves only when a logit exceeds it by more
+            // than 2^8 in p; the accumulators are rescaled only on the
+            // (wave-uniform) tiles where some row's reference moved.
+            const bool move = (mx - m[nt]) * LOG2E > 8.f;
+            const float mnew = move ? mx : m[nt];
             const float alpha = exp2f((m[nt] - mnew) * LOG2E);
+            const bool any_move = __ballot(move) != 0;
             m[nt] = mnew;
             float ps = 0.f;
             u16x8 hi, lo;
@@ -237,9 +243,12 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(AttnLaunch p) {
             lsum[nt] = lsum[nt] * alpha + ps;
             const bf16x8 pH = __builtin_bit_cast(bf16x8, hi);
             const bf16x8 pL = __builtin_bit_cast(bf16x8, lo);
+            if (any_move) {
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) acc[nt][dt] *= alpha;
+            }
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
-                acc[nt][dt] *= alpha;
                 acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(R.v[dt]), pH,
                                                                        acc[nt][dt], 0, 0, 0);
                 acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(R.v[dt]), pL,
@@ -340,7 +349,7 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(AttnLaunch p) {
             float f[W], L = 0.f;
 #pragma unroll
             for (int w = 0; w < W; ++w) {
-                f[w] = exp2f((wm[w][n] - M) * LOG2E);   // waves without rows: exp2(-inf) = 0
+                f[w] = exp2f((wm[w][n] - M) * LOG2E);   // waves without rows: 2^(-huge) = 0
                 L += f[w] * wl[w][n];
             }
             float o[EPT];
