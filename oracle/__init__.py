@@ -22,11 +22,14 @@ Parity status of each function (what pins it is in tests/test_oracle_*.py):
   quant.*         pinned (hand values with half-even rounding, the rounding
                   bound, power-of-two scalings, the protection rule, exact
                   cases equal to plain attention, the large-range-row claim)
+  ragged.*        pinned (short-window scores by brute force and row sums,
+                  reduction to the uniform trajectory and to a batch of one,
+                  sequence independence, the length schedule)
 End-to-end model quality (does the eviction keep accuracy?) is parity
 unpinned: it needs trained weights and datasets that are not available.
 """
 from .philox import philox4, philox4x32_10, seed_key, mulhilo
-from . import dkv, quant
+from . import dkv, quant, ragged
 from .kvc_oracle import (
     share_map, append_row, attention, decode_attention, value_range,
     window_score, philox_word0, exp_variate, select, select_detail, compact,
@@ -37,5 +40,5 @@ __all__ = [
     "philox4", "philox4x32_10", "seed_key", "mulhilo", "share_map",
     "append_row", "attention", "decode_attention", "value_range",
     "window_score", "philox_word0", "exp_variate", "select", "select_detail",
-    "compact", "eviction_due", "run_decode", "dkv", "quant",
+    "compact", "eviction_due", "run_decode", "dkv", "quant", "ragged",
 ]
