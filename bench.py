@@ -236,6 +236,75 @@ def int8_leg(args, cfg, dec, qpool, lsepool, knew, vnew, out, steps):
                 kernel="attn_q8_kernel (+ merge) and q8_append_kernel, per-layer calls, no eviction")
 
 
+def ragged_leg(args, cfg, qpool, lsepool, knew, vnew, out, steps, warm=3):
+    """The same model shape as a ragged batch: prompt lengths from a seeded
+    length mix (uniform in [t0/16, t0]), and every sequence evicting on its own
+    steps (phase b * period / nb), through RaggedDecoder.  Timed like the main
+    leg; attention bytes count each sequence's own rows."""
+    import torch
+    import kvc_synth
+    import decode_attention_kvc_amd as kvc
+    from decode_attention_kvc_amd.loop import RaggedDecoder, ragged_plan
+    dev = "cuda"
+    e0 = cfg["evict"]
+    L, leaders, nb, hq, hkv, tmax = (cfg[k] for k in ("n_layers", "leaders", "nb", "hq", "hkv",
+                                                       "t0"))
+    n_slots = len(leaders)
+    t0 = kvc_synth.length_mix(nb, tmax // 16, tmax, seed=11)
+    ev = dict(K=e0["K"], B=e0["B"], N_v=e0["N_v"], w=e0["w"], period=e0["period"],
+              seed=e0["seed"], phase=[b * e0["period"] // nb for b in range(nb)])
+    n_total = warm + steps
+    mode = args.mode if args.mode in ("per-layer", "grouped") else "per-layer"
+    plan = ragged_plan(t0, n_total, ev)
+    prompt = kvc.Cache.empty(n_slots, nb, hkv, max(t0), device=dev)
+    for s_ in range(n_slots):
+        Kr, Vr, _, _ = kvc_synth.kv_slot(nb, hkv, max(t0), device=dev, seed=300 + s_)
+        prompt.fill(s_, Kr, Vr)
+        del Kr, Vr
+    cache = kvc.Cache.empty(n_slots, plan["entries"], hkv, plan["peak"], device=dev)
+    dec = RaggedDecoder(L, leaders, cache, hq, t0, n_total, ev, mode=mode)
+    q_init = [kvc_synth.queries((ev["w"], nb, hq, 128), device=dev, seed=350 + i)
+              for i in range(n_slots)]
+    dec.initial_pass(prompt, q_init)
+    torch.cuda.synchronize()
+    del prompt, q_init
+    torch.cuda.empty_cache()
+    for s in range(warm):
+        dec.step(s, qpool, lsepool, knew, vnew, out)
+    torch.cuda.synchronize()
+    dec.events, dec.pass_events = [], []
+    t_start = time.perf_counter()
+    for s in range(warm, n_total):
+        dec.step(s, qpool, lsepool, knew, vnew, out)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    att_ms = sum(a.elapsed_time(b) for a, b, _, _ in dec.events)
+    n_calls = sum(n for _, _, _, n in dec.events)
+    rows = [sum(plan["att_len"][s]) for _, _, s, _ in dec.events]   # rows of all sequences
+    per_row = 2 * hkv * 128 * 2                                         # K + V of one row, all heads
+    q_out = nb * hq * (128 * 2 + 129 * 4)
+    if mode == "per-layer":
+        byts = sum(L * r * per_row + L * q_out + n_slots * 2 * nb * hkv * 256 for r in rows)
+    else:
+        byts = sum(n_slots * r * per_row + L * q_out + n_slots * 2 * nb * hkv * 256 for r in rows)
+    gbps = byts / (att_ms * 1e-3) / 1e9
+    pass_ms = [a.elapsed_time(b) for a, b, _, _ in dec.pass_events]
+    seq_passes = sum(n for _, _, _, n in dec.pass_events)
+    lens = [plan["att_len"][s] for s in range(warm, n_total)]
+    return dict(value=round(nb * steps / wall, 2), unit="tokens/s",
+                ms_per_step=round(1e3 * wall / steps, 4), mode=mode,
+                attention_GBps=round(gbps, 1), attention_frac=round(gbps / HBM_PEAK_GBPS, 4),
+                avg_launch_us=round(1e3 * att_ms / n_calls, 2),
+                prompt_tokens=t0, phases=ev["phase"],
+                rows_min_mean_max=[min(map(min, lens)), round(sum(map(sum, lens)) /
+                                   (len(lens) * nb), 1), max(map(max, lens))],
+                batch_entries=plan["entries"],
+                eviction_passes=len(pass_ms), sequence_passes=seq_passes,
+                pass_ms_mean=round(sum(pass_ms) / max(1, len(pass_ms)), 3),
+                kernel="attn_bf16_kernel (+ merge) over per-sequence lengths; passes: "
+                       "score, select, compact on the due sequences only")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -252,6 +321,8 @@ def main():
     ap.add_argument("--rank", type=int, default=32, choices=[16, 32],
                     help="sketch columns of the VASE-DKV scores")
     ap.add_argument("--no-grouped", action="store_true", help="skip the grouped-mode leg")
+    ap.add_argument("--no-ragged", action="store_true",
+                    help="skip the ragged-batch leg (length mix, per-sequence eviction steps)")
     ap.add_argument("--no-int8", action="store_true",
                     help="skip the range-protected int8 cache leg (decode attention only)")
     ap.add_argument("--protect-frac", type=float, default=0.01,
@@ -388,6 +459,12 @@ def main():
         int8 = int8_leg(args, cfg, dec, qpool, lsepool, knew, vnew, out, S)
         log(f"[bench] int8: {int8}")
 
+    ragged_res = None
+    if not args.no_ragged and ev and args.scoring == "attnv":
+        log("[bench] ragged leg: setting up")
+        ragged_res = ragged_leg(args, cfg, qpool, lsepool, knew, vnew, out, S)
+        log(f"[bench] ragged: {ragged_res}")
+
     if args.copy_calibration:
         # Two plain copies of known size for scaling the memory counters:
         # a 1 GiB runtime blit, and a 512 MiB float32 copy done by a
@@ -452,6 +529,7 @@ def main():
         "initial_pass_ms": None if initial_ms is None else round(initial_ms, 3),
         "grouped": grouped,
         "int8": int8,
+        "ragged": ragged_res,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

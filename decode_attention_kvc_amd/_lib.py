@@ -6,9 +6,11 @@ stream), and raises KvcError on a non-zero status.  All computation runs in
 the library's HIP kernels; there is no fallback path.
 """
 import ctypes
+import dataclasses
 import math
 import os
 from dataclasses import dataclass
+from typing import Optional
 
 import torch
 
@@ -24,7 +26,7 @@ V_TILE = 32
 EXPORTS = (
     "kvc_version", "kvc_strerror", "kvc_share_map", "kvc_append",
     "kvc_decode_attn_ws_bytes", "kvc_decode_attn", "kvc_value_range",
-    "kvc_score_ws_bytes", "kvc_score", "kvc_select_ws_bytes", "kvc_select",
+    "kvc_score_ws_bytes", "kvc_score", "kvc_select_ws_bytes", "kvc_select", "kvc_select_seq",
     "kvc_compact", "kvc_philox_words", "kvc_dkv_ws_bytes", "kvc_dkv_score",
     "kvc_gaussian_bf16", "kvc_q8_quantize", "kvc_q8_append", "kvc_q8_decode_attn_ws_bytes",
     "kvc_q8_decode_attn",
@@ -41,7 +43,9 @@ class kvc_cache(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("dtype", ctypes.c_int32),
                 ("n_slots", ctypes.c_int32), ("nb", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("t_len", ctypes.c_int32), ("t_cap", ctypes.c_int32)]
+                ("t_len", ctypes.c_int32), ("t_cap", ctypes.c_int32),
+                ("nb_cap", ctypes.c_int32), ("batch_idx", ctypes.c_void_p),
+                ("seq_len", ctypes.c_void_p)]
 
 
 class kvc_qcache(ctypes.Structure):
@@ -84,6 +88,8 @@ def lib():
             "kvc_select_ws_bytes": ([i32, i32, i32, szp], i32),
             "kvc_select": ([vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_uint64, i32, vp, vp,
                             sz, vp], i32),
+            "kvc_select_seq": ([vp, vp, i32, i32, i32, vp, vp, i32, i32, i32, ctypes.c_uint64,
+                                i32, vp, vp, sz, vp], i32),
             "kvc_compact": ([cp, i32, vp, i32, cp, vp], i32),
             "kvc_philox_words": ([i64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
                                   ctypes.c_uint64, vp, vp], i32),
@@ -138,12 +144,28 @@ def _dtype_code(dt):
 class Cache:
     """A leader-slot KV cache in libkvc's layout (see include/kvc.h).
 
-    k: [n_slots][nb][n_kv_heads][t_cap][128] rows;
-    v: [n_slots][nb][n_kv_heads][t_cap/32][128][32], tiles of 32 tokens,
-    each tile channel-major."""
+    k: [n_slots][nb_cap][n_kv_heads][t_cap][128] rows;
+    v: [n_slots][nb_cap][n_kv_heads][t_cap/32][128][32], tiles of 32 tokens,
+    each tile channel-major.
+    Ragged batches: batch_idx (device int32 [n]: the entry of each sequence)
+    and seq_len (device int32 [n]: its rows) make the object address n
+    sequences; t_len is then the bound on their lengths.  seqs() makes such a
+    view of the same buffers."""
     k: torch.Tensor
     v: torch.Tensor
     t_len: int
+    batch_idx: Optional[torch.Tensor] = None
+    seq_len: Optional[torch.Tensor] = None
+
+    def seqs(self, batch_idx=None, seq_len=None, t_len=None):
+        """The same buffers addressing the sequences of batch_idx / seq_len."""
+        for a in (batch_idx, seq_len):
+            if a is not None and (a.dtype != torch.int32 or not a.is_contiguous()):
+                raise ValueError("batch_idx / seq_len must be contiguous int32 tensors")
+        if batch_idx is not None and seq_len is not None and batch_idx.numel() != seq_len.numel():
+            raise ValueError("batch_idx and seq_len differ in length")
+        return dataclasses.replace(self, batch_idx=batch_idx, seq_len=seq_len,
+                                   t_len=self.t_len if t_len is None else t_len)
 
     @staticmethod
     def empty(n_slots, nb, n_kv_heads, t_cap, dtype=torch.bfloat16, device="cuda", t_len=0):
@@ -158,8 +180,16 @@ class Cache:
         return self.k.shape[0]
 
     @property
-    def nb(self):
+    def nb_cap(self):
         return self.k.shape[1]
+
+    @property
+    def nb(self):
+        """Sequences the object addresses."""
+        for a in (self.batch_idx, self.seq_len):
+            if a is not None:
+                return a.numel()
+        return self.nb_cap
 
     @property
     def n_kv_heads(self):
@@ -176,7 +206,7 @@ class Cache:
     def desc(self):
         return kvc_cache(self.k.data_ptr(), self.v.data_ptr(), _dtype_code(self.k.dtype),
                          self.n_slots, self.nb, self.n_kv_heads, HEAD_DIM, int(self.t_len),
-                         self.t_cap)
+                         self.t_cap, self.nb_cap, _ptr(self.batch_idx), _ptr(self.seq_len))
 
     # views in logical [..][t][d] form (plumbing for tests and data setup)
     def k_rows(self, slot):
@@ -184,7 +214,8 @@ class Cache:
 
     def v_rows(self, slot):
         """Logical value rows [nb][hkv][t_len][128] (a copy)."""
-        v = self.v[slot].transpose(-1, -2).reshape(self.nb, self.n_kv_heads, self.t_cap, HEAD_DIM)
+        v = self.v[slot].transpose(-1, -2).reshape(self.nb_cap, self.n_kv_heads, self.t_cap,
+                                                    HEAD_DIM)
         return v[:, :, : self.t_len]
 
     def v_row(self, slot, t):
@@ -197,7 +228,7 @@ class Cache:
         T = k_rows.shape[2]
         self.k[slot, :, :, :T, :].copy_(k_rows)
         nfull, rem = divmod(T, V_TILE)
-        nb, h = self.nb, self.n_kv_heads
+        nb, h = self.nb_cap, self.n_kv_heads
         if nfull:
             self.v[slot, :, :, :nfull].copy_(
                 v_rows[:, :, : nfull * V_TILE].reshape(nb, h, nfull, V_TILE, HEAD_DIM)
@@ -354,6 +385,16 @@ def kvc_select(score, rng, nb, n_kv_heads, t_len, budget_k, recent_b, n_v, seed,
     _check(lib().kvc_select(_ptr(score), _ptr(rng), nb, n_kv_heads, t_len, budget_k, recent_b,
                             n_v, int(seed) & (2**64 - 1), layer_id, _ptr(kept), _ptr(ws),
                             ws_bytes, _stream(stream)), "kvc_select")
+
+
+def kvc_select_seq(score, rng, nb, n_kv_heads, t_len, seq_len, seq_id, budget_k, recent_b, n_v,
+                   seed, layer_id, kept, ws=None, stream=None):
+    """seq_len, seq_id: device int32 [nb] or None."""
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().kvc_select_seq(_ptr(score), _ptr(rng), nb, n_kv_heads, t_len, _ptr(seq_len),
+                                _ptr(seq_id), budget_k, recent_b, n_v, int(seed) & (2**64 - 1),
+                                layer_id, _ptr(kept), _ptr(ws), ws_bytes, _stream(stream)),
+           "kvc_select_seq")
 
 
 def kvc_compact(src, slot, kept, n_keep, dst, stream=None):

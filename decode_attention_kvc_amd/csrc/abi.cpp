@@ -24,6 +24,9 @@ bool aligned4(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 3u)
 size_t elem_size(int dtype) { return dtype == KVC_F32 ? 4 : 2; }
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Batch entries the buffers hold (0 means nb).
+int nb_cap_of(const kvc_cache* c) { return c->nb_cap ? c->nb_cap : c->nb; }
+
 int check_cache(const kvc_cache* c) {
     if (!c) return KVC_EALIGN;
     if (c->dtype != KVC_F32 && c->dtype != KVC_BF16) return KVC_EDTYPE;
@@ -31,12 +34,28 @@ int check_cache(const kvc_cache* c) {
     if (c->n_slots < 1 || c->nb < 0 || c->n_kv_heads < 1) return KVC_EINVAL;
     if (c->t_cap < 0 || c->t_len < 0 || c->t_len > c->t_cap) return KVC_EINVAL;
     if (c->t_cap % KVC_T_ALIGN) return KVC_EINVAL;
+    if (c->nb_cap < 0) return KVC_EINVAL;
+    // without a map, sequence b is entry b
+    if (!c->batch_idx && c->nb > nb_cap_of(c)) return KVC_EINVAL;
     if (!aligned16(c->k) || !aligned16(c->v)) return KVC_EALIGN;
+    if ((c->batch_idx && !aligned4(c->batch_idx)) || (c->seq_len && !aligned4(c->seq_len)))
+        return KVC_EALIGN;
     return KVC_OK;
 }
 
+bool is_ragged(const kvc_cache* c) { return c->batch_idx || c->seq_len; }
+
+SeqMap seq_map(const kvc_cache* c) {
+    SeqMap m;
+    m.idx = c->batch_idx;
+    m.len = c->seq_len;
+    m.nb_cap = nb_cap_of(c);
+    m.t_len = c->t_len;
+    return m;
+}
+
 size_t slot_elems(const kvc_cache* c) {
-    return (size_t)c->nb * c->n_kv_heads * c->t_cap * KVC_HEAD_DIM;
+    return (size_t)nb_cap_of(c) * c->n_kv_heads * c->t_cap * KVC_HEAD_DIM;
 }
 const char* slot_k(const kvc_cache* c, int slot) {
     return static_cast<const char*>(c->k) + (size_t)slot * slot_elems(c) * elem_size(c->dtype);
@@ -292,8 +311,8 @@ int kvc_append(const kvc_cache* c, int slot, const void* k_new, const void* v_ne
     if (slot < 0 || slot >= c->n_slots || c->t_len < 1) return KVC_EINVAL;
     if (!aligned16(k_new) || !aligned16(v_new)) return KVC_EALIGN;
     if (c->nb == 0) return KVC_OK;
-    if (launch_append(slot_k(c, slot), slot_v(c, slot), c->nb, c->n_kv_heads, c->t_len,
-                      c->t_cap, k_new, v_new, (int)elem_size(c->dtype),
+    if (launch_append(slot_k(c, slot), slot_v(c, slot), c->nb, c->n_kv_heads, c->t_cap,
+                      seq_map(c), k_new, v_new, (int)elem_size(c->dtype),
                       (hipStream_t)stream) != hipSuccess)
         return KVC_EHIP;
     return hip_status();
@@ -375,6 +394,7 @@ int kvc_decode_attn(const kvc_cache* c, const void* q, int64_t q_layer_stride, i
         p.nsplit = pl.nsplit;
         p.tps = pl.tps;
         p.part = static_cast<float*>(ws);
+        p.sm = seq_map(c);
         if (launch_attn(p, c->dtype, pl.nt, s) != hipSuccess) return (int)KVC_EHIP;
         if (p.append_write) append_done = true;
         return (int)KVC_OK;
@@ -382,7 +402,7 @@ int kvc_decode_attn(const kvc_cache* c, const void* q, int64_t q_layer_stride, i
     if (st) return st;
     if (append_slot >= 0 && !append_done) {
         if (launch_append(slot_k(c, append_slot), slot_v(c, append_slot), c->nb, c->n_kv_heads,
-                          c->t_len, c->t_cap, k_new, v_new, (int)elem_size(c->dtype),
+                          c->t_cap, seq_map(c), k_new, v_new, (int)elem_size(c->dtype),
                           s) != hipSuccess)
             return KVC_EHIP;
     }
@@ -395,7 +415,7 @@ int kvc_value_range(const kvc_cache* c, int slot, float* range, kvc_stream_t str
     if (slot < 0 || slot >= c->n_slots) return KVC_EINVAL;
     if (!aligned4(range)) return KVC_EALIGN;
     if (c->nb == 0 || c->t_len == 0) return KVC_OK;
-    if (launch_value_range(slot_v(c, slot), c->nb, c->n_kv_heads, c->t_len, c->t_cap, c->dtype,
+    if (launch_value_range(slot_v(c, slot), c->nb, c->n_kv_heads, c->t_cap, seq_map(c), c->dtype,
                            range, (hipStream_t)stream) != hipSuccess)
         return KVC_EHIP;
     return hip_status();
@@ -459,6 +479,7 @@ int kvc_score(const kvc_cache* c, int slot, const void* q_obs, int n_q_heads, in
     p.main_nsplit = pl.main_nsplit;
     p.main_tps = pl.main_tps;
     p.rows_pad = pl.rows_pad;
+    p.sm = seq_map(c);
     if (!lse_obs) {
         char* base = static_cast<char*>(ws);
         p.lse_ws = reinterpret_cast<float*>(base + lay.lse_off);
@@ -478,6 +499,14 @@ int kvc_select_ws_bytes(int nb, int n_kv_heads, int t_len, size_t* bytes) {
 int kvc_select(const float* score, const float* range, int nb, int n_kv_heads, int t_len,
                int budget_k, int recent_b, int n_v, uint64_t seed, int layer_id, int32_t* kept,
                void* ws, size_t ws_bytes, kvc_stream_t stream) {
+    return kvc_select_seq(score, range, nb, n_kv_heads, t_len, nullptr, nullptr, budget_k,
+                          recent_b, n_v, seed, layer_id, kept, ws, ws_bytes, stream);
+}
+
+int kvc_select_seq(const float* score, const float* range, int nb, int n_kv_heads, int t_len,
+                   const int32_t* seq_len, const int32_t* seq_id, int budget_k, int recent_b,
+                   int n_v, uint64_t seed, int layer_id, int32_t* kept, void* ws,
+                   size_t ws_bytes, kvc_stream_t stream) {
     if (nb < 0 || n_kv_heads < 1 || t_len < 0) return KVC_EINVAL;
     if (budget_k < 0 || recent_b < 0 || n_v < 0 || n_v > budget_k) return KVC_EINVAL;
     if ((long long)budget_k + recent_b < 1 || (long long)budget_k + recent_b > INT32_MAX)
@@ -486,6 +515,7 @@ int kvc_select(const float* score, const float* range, int nb, int n_kv_heads, i
     if (nb == 0 || t_len == 0) return KVC_OK;
     if (!aligned4(score) || !aligned4(kept)) return KVC_EALIGN;
     if (n_v > 0 && !aligned4(range)) return KVC_EALIGN;
+    if ((seq_len && !aligned4(seq_len)) || (seq_id && !aligned4(seq_id))) return KVC_EALIGN;
     const size_t need = (size_t)nb * n_kv_heads * t_len * sizeof(uint32_t);
     const bool evicts = t_len > budget_k + recent_b;
     if (evicts && (!ws || ws_bytes < need || !aligned4(ws))) return KVC_EWORKSPACE;
@@ -504,6 +534,8 @@ int kvc_select(const float* score, const float* range, int nb, int n_kv_heads, i
     p.layer_id = (uint32_t)layer_id;
     p.kept = kept;
     p.keys = static_cast<uint32_t*>(ws);
+    p.len = seq_len;
+    p.seq_id = seq_id;
     if (launch_select(p, (hipStream_t)stream) != hipSuccess) return KVC_EHIP;
     return hip_status();
 }
@@ -524,9 +556,14 @@ int kvc_compact(const kvc_cache* src, int slot, const int32_t* kept, int n_keep,
     const size_t sb = slot_elems(src) * es, db = slot_elems(dst) * es;
     const char* sr[2] = {slot_k(src, slot), slot_v(src, slot)};
     const char* dr[2] = {slot_k(dst, slot), slot_v(dst, slot)};
+    // With batch maps the two sides may share buffers (other entries of one
+    // cache); the maps themselves live on the device and keeping the
+    // entries apart is the caller's part.  Without maps the regions must
+    // not overlap at all.
+    const bool mapped = src->batch_idx || dst->batch_idx;
     for (int a = 0; a < 2; ++a)
         for (int b2 = 0; b2 < 2; ++b2)
-            if (sr[a] < dr[b2] + db && dr[b2] < sr[a] + sb) return KVC_EALIAS;
+            if (!mapped && sr[a] < dr[b2] + db && dr[b2] < sr[a] + sb) return KVC_EALIAS;
     if (dr[0] < dr[1] + db && dr[1] < dr[0] + db) return KVC_EALIAS;
     CompactLaunch p;
     memset(&p, 0, sizeof(p));
@@ -536,12 +573,13 @@ int kvc_compact(const kvc_cache* src, int slot, const int32_t* kept, int n_keep,
     p.dv = const_cast<char*>(dr[1]);
     p.nb = src->nb;
     p.hkv = src->n_kv_heads;
-    p.src_t_len = src->t_len;
     p.src_t_cap = src->t_cap;
     p.dst_t_cap = dst->t_cap;
     p.kept = kept;
     p.n_keep = n_keep;
     p.elem = (int)es;
+    p.src_sm = seq_map(src);
+    p.dst_sm = seq_map(dst);
     if (launch_compact(p, (hipStream_t)stream) != hipSuccess) return KVC_EHIP;
     return hip_status();
 }
@@ -553,6 +591,7 @@ int kvc_q8_quantize(const kvc_cache* src, int slot, const int32_t* protect, int 
     st = check_qcache(dst);
     if (st) return st;
     if (src->dtype != KVC_BF16) return KVC_EDTYPE;
+    if (is_ragged(src) || nb_cap_of(src) != src->nb) return KVC_EINVAL;   // uniform batches only
     if (src->nb != dst->nb || src->n_kv_heads != dst->n_kv_heads) return KVC_EINVAL;
     if (slot < 0 || slot >= src->n_slots || slot >= dst->n_slots) return KVC_EINVAL;
     if (dst->t_len != src->t_len || dst->p_len != n_protect) return KVC_EINVAL;
@@ -586,7 +625,8 @@ int kvc_q8_quantize(const kvc_cache* src, int slot, const int32_t* protect, int 
         cp.dv = q_vp(dst, slot);
         cp.nb = src->nb;
         cp.hkv = src->n_kv_heads;
-        cp.src_t_len = src->t_len;
+        cp.src_sm.t_len = src->t_len;
+        cp.src_sm.nb_cap = cp.dst_sm.nb_cap = src->nb;
         cp.src_t_cap = src->t_cap;
         cp.dst_t_cap = dst->p_cap;
         cp.kept = protect;
@@ -742,6 +782,7 @@ int kvc_dkv_score(const kvc_cache* c, int slot, const void* g, int rank, float* 
     p.y = reinterpret_cast<float*>(base + lay.y_off);
     p.gram = reinterpret_cast<double*>(base + lay.gram_off);
     p.w = reinterpret_cast<float*>(base + lay.w_off);
+    p.sm = seq_map(c);
     if (launch_dkv(p, (hipStream_t)stream) != hipSuccess) return KVC_EHIP;
     return hip_status();
 }

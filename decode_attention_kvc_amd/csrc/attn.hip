@@ -28,6 +28,11 @@
 // last workgroup to finish would need an agent-scope release per
 // workgroup, which on this multi-XCD part is an L2 writeback each time; the
 // separate kernel measured faster at every split count.)
+//
+// Ragged batches: sequence b reads rows [0, rows(b)) of cache entry phys(b);
+// the launch is planned for the longest sequence and the splits past a
+// sequence's end leave at once (an empty partial that the merge skips).  A
+// sequence without rows gets a zero output and lse = -inf.
 #include <type_traits>
 
 #include "common.h"
@@ -105,23 +110,23 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch p) {
             }
             M = mn;
         }
-        const float inv = 1.f / L;
+        const float inv = L > 0.f ? 1.f / L : 0.f;   // no split saw a row: zeros
         const int qi = r / p.g, h = j * p.g + r % p.g;
         float* dst = p.out + p.out_off[qi] + ((size_t)b * p.hq + h) * D + d0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) dst[e] = o[e] * inv;
-        if (d0 == 0 && p.lse) p.lse[p.lse_off[qi] + (size_t)b * p.hq + h] = M + logf(L);
+        if (d0 == 0 && p.lse)
+            p.lse[p.lse_off[qi] + (size_t)b * p.hq + h] = L > 0.f ? M + logf(L) : -INFINITY;
     }
 }
 
+// Row t of cache slab cslab <- the new row of sequence slab `slab`.
 template <typename T>
-__device__ void write_append_row(const AttnLaunch& p, int b, int j) {
-    const size_t slab = (size_t)b * p.hkv + j;
+__device__ void write_append_row(const AttnLaunch& p, size_t slab, size_t cslab, int t) {
     const T* kn = reinterpret_cast<const T*>(p.k_new) + slab * D;
     const T* vn = reinterpret_cast<const T*>(p.v_new) + slab * D;
-    T* kc = const_cast<T*>(reinterpret_cast<const T*>(p.k)) + slab * p.t_cap * D;
-    T* vc = const_cast<T*>(reinterpret_cast<const T*>(p.v)) + slab * p.t_cap * D;
-    const int t = p.t_len - 1;
+    T* kc = const_cast<T*>(reinterpret_cast<const T*>(p.k)) + cslab * p.t_cap * D;
+    T* vc = const_cast<T*>(reinterpret_cast<const T*>(p.v)) + cslab * p.t_cap * D;
     for (int d = threadIdx.x; d < D; d += blockDim.x) {
         kc[(size_t)t * D + d] = kn[d];
         vc[vt_off(t, d)] = vn[d];
@@ -135,13 +140,34 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(AttnLaunch p) {
     const int slab = b * p.hkv + j;
     const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
     const int l16 = lane & 15, lg = lane >> 4;
-    const int T = p.t_len;
+    const int phys = seq_phys(p.sm, b);
+    const int T = seq_rows(p.sm, b, phys);
     const int ntiles = (T + ATTN_TILE - 1) / ATTN_TILE;
     const int tile_begin = s * p.tps;
     const int tile_end = min(tile_begin + p.tps, ntiles);
+    if (tile_begin >= ntiles) {
+        // A split past the sequence's end (the launch is planned for the
+        // longest one): an empty partial, or, for a sequence without rows
+        // and a single split, its final zero output.
+        const size_t slabs = (size_t)p.nb * p.hkv;
+        for (int r = tid; r < p.rows; r += blockDim.x) {
+            if (p.nsplit == 1) {
+                const int qi = r / p.g, h = j * p.g + r % p.g;
+                float* dst = p.out + p.out_off[qi] + ((size_t)b * p.hq + h) * D;
+                for (int d = 0; d < D; ++d) dst[d] = 0.f;
+                if (p.lse) p.lse[p.lse_off[qi] + (size_t)b * p.hq + h] = -INFINITY;
+            } else {
+                float* ml = p.part + slabs * p.nsplit * RP * D + ((size_t)slab * p.nsplit + s) * RP * 2;
+                ml[r * 2] = -INFINITY;
+                ml[r * 2 + 1] = 0.f;
+            }
+        }
+        return;
+    }
+    const size_t cslab = (size_t)phys * p.hkv + j;
 
-    const uint16_t* kslab = reinterpret_cast<const uint16_t*>(p.k) + (size_t)slab * p.t_cap * D;
-    const uint16_t* vslab = reinterpret_cast<const uint16_t*>(p.v) + (size_t)slab * p.t_cap * D;
+    const uint16_t* kslab = reinterpret_cast<const uint16_t*>(p.k) + cslab * p.t_cap * D;
+    const uint16_t* vslab = reinterpret_cast<const uint16_t*>(p.v) + cslab * p.t_cap * D;
     const int append_row = p.append_read ? T - 1 : -1;
     const uint16_t* knew_row =
         p.append_read ? reinterpret_cast<const uint16_t*>(p.k_new) + (size_t)slab * D : kslab;
@@ -383,7 +409,7 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(AttnLaunch p) {
         __syncthreads();
     }
 
-    if (p.append_write && s == p.nsplit - 1) write_append_row<uint16_t>(p, b, j);
+    if (p.append_write && tile_end == ntiles) write_append_row<uint16_t>(p, slab, cslab, T - 1);
 }
 
 // float32 path: plain VALU arithmetic, up to 16 query rows per launch.
@@ -392,12 +418,14 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnLaunch p) {
     const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int slab = b * p.hkv + j;
     const int tid = threadIdx.x;
-    const int T = p.t_len;
+    const int phys = seq_phys(p.sm, b);
+    const int T = seq_rows(p.sm, b, phys);     // 0 rows: no tile, an empty partial
     const int ntiles = (T + TT - 1) / TT;
     const int tile_begin = s * p.tps;
     const int tile_end = min(tile_begin + p.tps, ntiles);
-    const float* kslab = reinterpret_cast<const float*>(p.k) + (size_t)slab * p.t_cap * D;
-    const float* vslab = reinterpret_cast<const float*>(p.v) + (size_t)slab * p.t_cap * D;
+    const size_t cslab = (size_t)max(phys, 0) * p.hkv + j;
+    const float* kslab = reinterpret_cast<const float*>(p.k) + cslab * p.t_cap * D;
+    const float* vslab = reinterpret_cast<const float*>(p.v) + cslab * p.t_cap * D;
     const float* knew = reinterpret_cast<const float*>(p.k_new) + (size_t)slab * D;
     const float* vnew = reinterpret_cast<const float*>(p.v_new) + (size_t)slab * D;
     const int append_row = p.append_read ? T - 1 : -1;
@@ -512,17 +540,23 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnLaunch p) {
         part_ml[tid * 2] = mrow[tid];
         part_ml[tid * 2 + 1] = lrow[tid];
     }
-    if (p.append_write && s == p.nsplit - 1) write_append_row<float>(p, b, j);
+    if (p.append_write && tile_begin < ntiles && tile_end == ntiles)
+        write_append_row<float>(p, slab, cslab, T - 1);
 }
 
+// Row rows(b) - 1 of every slab of sequence b <- its new row.
 template <typename T>
-__global__ __launch_bounds__(128) void append_kernel(T* k, T* v, int hkv, int t_len, int t_cap,
+__global__ __launch_bounds__(128) void append_kernel(T* k, T* v, int hkv, int t_cap, SeqMap sm,
                                                      const T* k_new, const T* v_new) {
-    const size_t slab = (size_t)blockIdx.y * hkv + blockIdx.x;
-    const int t = t_len - 1;
+    const int b = blockIdx.y;
+    const size_t slab = (size_t)b * hkv + blockIdx.x;
+    const int phys = seq_phys(sm, b);
+    const int t = seq_rows(sm, b, phys) - 1;
+    if (t < 0) return;
+    const size_t cslab = (size_t)phys * hkv + blockIdx.x;
     for (int d = threadIdx.x; d < D; d += blockDim.x) {
-        k[(slab * t_cap + t) * D + d] = k_new[slab * D + d];
-        v[slab * t_cap * D + vt_off(t, d)] = v_new[slab * D + d];
+        k[(cslab * t_cap + t) * D + d] = k_new[slab * D + d];
+        v[cslab * t_cap * D + vt_off(t, d)] = v_new[slab * D + d];
     }
 }
 
@@ -551,15 +585,16 @@ hipError_t launch_attn_combine(const AttnLaunch& p, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_append(const void* k, const void* v, int nb, int hkv, int t_len, int t_cap,
-                         const void* k_new, const void* v_new, int elem, hipStream_t st) {
+hipError_t launch_append(const void* k, const void* v, int nb, int hkv, int t_cap,
+                         const SeqMap& sm, const void* k_new, const void* v_new, int elem,
+                         hipStream_t st) {
     const dim3 grid(hkv, nb);
     if (elem == 4)
         hipLaunchKernelGGL(append_kernel<float>, grid, dim3(128), 0, st, (float*)k, (float*)v,
-                           hkv, t_len, t_cap, (const float*)k_new, (const float*)v_new);
+                           hkv, t_cap, sm, (const float*)k_new, (const float*)v_new);
     else
         hipLaunchKernelGGL(append_kernel<uint16_t>, grid, dim3(128), 0, st, (uint16_t*)k,
-                           (uint16_t*)v, hkv, t_len, t_cap, (const uint16_t*)k_new,
+                           (uint16_t*)v, hkv, t_cap, sm, (const uint16_t*)k_new,
                            (const uint16_t*)v_new);
     return hipGetLastError();
 }

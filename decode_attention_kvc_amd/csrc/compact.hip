@@ -20,6 +20,10 @@
 // not staged (only possible for indices out of ascending order) is read
 // straight from global memory, so no input can make an access leave the
 // slab.
+// Ragged batches: sequence b is read from source entry phys_src(b) and
+// written to destination entry phys_dst(b); it keeps min(T_b, n_keep) rows
+// (n_keep is the stride of `kept`), and indices at or past T_b give zero
+// rows.
 #include "common.h"
 #include "kvc_internal.h"
 
@@ -43,16 +47,21 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactLaunch p) {
     using S = Stage<E>;
     constexpr int VEC = S::VEC;
     constexpr int CPR = D / VEC;            // 16-byte chunks per K row
-    const int slab = blockIdx.z * p.hkv + blockIdx.y;
+    const int b = blockIdx.z;
+    const int slab = b * p.hkv + blockIdx.y;
     const int i0 = blockIdx.x * CROWS;
     const int tid = threadIdx.x;
+    const int sphys = seq_phys(p.src_sm, b), dphys = seq_phys(p.dst_sm, b);
+    const int src_t_len = seq_rows(p.src_sm, b, sphys);
+    const int rows = min(CROWS, min(src_t_len, p.n_keep) - i0);
+    if (dphys < 0 || rows <= 0) return;          // whole workgroup
     const int32_t* kept = p.kept + (size_t)slab * p.n_keep;
-    const E* sk = reinterpret_cast<const E*>(p.sk) + (size_t)slab * p.src_t_cap * D;
-    const E* sv = reinterpret_cast<const E*>(p.sv) + (size_t)slab * p.src_t_cap * D;
-    E* dk = reinterpret_cast<E*>(p.dk) + (size_t)slab * p.dst_t_cap * D;
-    E* dv = reinterpret_cast<E*>(p.dv) + (size_t)slab * p.dst_t_cap * D;
-    const int rows = min(CROWS, p.n_keep - i0);
-    const int src_tiles = (p.src_t_len + VT - 1) / VT;
+    const size_t scs = (size_t)sphys * p.hkv + blockIdx.y, dcs = (size_t)dphys * p.hkv + blockIdx.y;
+    const E* sk = reinterpret_cast<const E*>(p.sk) + scs * p.src_t_cap * D;
+    const E* sv = reinterpret_cast<const E*>(p.sv) + scs * p.src_t_cap * D;
+    E* dk = reinterpret_cast<E*>(p.dk) + dcs * p.dst_t_cap * D;
+    E* dv = reinterpret_cast<E*>(p.dv) + dcs * p.dst_t_cap * D;
+    const int src_tiles = (src_t_len + VT - 1) / VT;
 
     __shared__ int32_t src_row[CROWS];
     __shared__ __align__(16) E stage[S::NT * S::TILE];
@@ -60,7 +69,7 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactLaunch p) {
         int32_t r = -1;
         if (x < rows) {
             r = kept[i0 + x];
-            if (r < 0 || r >= p.src_t_len) r = -1;
+            if (r < 0 || r >= src_t_len) r = -1;
         }
         src_row[x] = r;
     }

@@ -28,6 +28,9 @@
 //     factors them (Cholesky with dropped pivots, float64, in registers) and
 //     writes W = R^{-1} (zero rows for dropped directions) as float32.
 //  3. dkv_leverage: score_t = ||y_t W||^2, one thread per row.
+// Ragged batches: sequence b sketches rows [0, T_b) of cache entry phys(b)
+// (splits past its end contribute a zero Gram); Y and the scores keep the
+// launch's t_len as their row stride.
 #include <type_traits>
 
 #include "common.h"
@@ -112,7 +115,8 @@ __global__ __launch_bounds__(256) void dkv_sketch(DkvLaunch p) {
     const int slab = b * p.hkv + j;
     const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
     const int l16 = lane & 15, lg = lane >> 4;
-    const int T = p.t_len;
+    const int phys = seq_phys(p.sm, b);
+    const int T = seq_rows(p.sm, b, phys);
 
     // Stage G: sketch column n is row n of g ([R][2d] bf16).
     const uint16_t* g = reinterpret_cast<const uint16_t*>(p.g);
@@ -122,10 +126,11 @@ __global__ __launch_bounds__(256) void dkv_sketch(DkvLaunch p) {
     }
     __syncthreads();
 
-    const uint16_t* kslab = reinterpret_cast<const uint16_t*>(p.k) + (size_t)slab * p.t_cap * D;
-    const uint16_t* vslab = reinterpret_cast<const uint16_t*>(p.v) + (size_t)slab * p.t_cap * D;
-    float* ys = p.y + (size_t)slab * T * R;
-    float* range = RANGE ? p.range + (size_t)slab * T : nullptr;
+    const size_t cslab = (size_t)max(phys, 0) * p.hkv + j;
+    const uint16_t* kslab = reinterpret_cast<const uint16_t*>(p.k) + cslab * p.t_cap * D;
+    const uint16_t* vslab = reinterpret_cast<const uint16_t*>(p.v) + cslab * p.t_cap * D;
+    float* ys = p.y + (size_t)slab * p.t_len * R;
+    float* range = RANGE ? p.range + (size_t)slab * p.t_len : nullptr;
     uint16_t* vb = vbuf[wave];
     const int ntiles = (T + DT - 1) / DT;
     const int tile_begin = s * p.tps, tile_end = min(tile_begin + p.tps, ntiles);
@@ -340,7 +345,8 @@ __global__ __launch_bounds__(256) void dkv_leverage(DkvLaunch p) {
     for (int x = threadIdx.x; x < R * R; x += blockDim.x) ws[x / R][x % R] = w[x];
     __syncthreads();
     const int t = blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= p.t_len) return;
+    const int b = blockIdx.z;
+    if (t >= seq_rows(p.sm, b, seq_phys(p.sm, b))) return;
     const float* y = p.y + ((size_t)slab * p.t_len + t) * R;
     float yv[R];
 #pragma unroll

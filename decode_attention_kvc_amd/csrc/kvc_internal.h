@@ -26,6 +26,28 @@ inline size_t score_main_lds_bytes(int rows) {
 }
 constexpr int SELECT_THREADS = 1024;
 
+// Ragged batches.  A launch addresses nb sequences; sequence b is stored in
+// batch entry phys(b) of buffers that hold nb_cap entries and has rows(b)
+// rows.  Per-sequence inputs and outputs are indexed by b.  Both arrays live
+// on the device and are not trusted: an entry index outside [0, nb_cap)
+// makes the sequence empty and lengths are clamped to [0, t_len].
+struct SeqMap {
+    const int32_t* idx;     // [nb] batch entry per sequence, or null (entry b)
+    const int32_t* len;     // [nb] rows per sequence, or null (t_len each)
+    int nb_cap;             // batch entries of the buffers
+    int t_len;              // bound on every length
+};
+__device__ __forceinline__ int seq_phys(const SeqMap& m, int b) {
+    if (!m.idx) return b;
+    const int c = m.idx[b];
+    return (c >= 0 && c < m.nb_cap) ? c : -1;
+}
+__device__ __forceinline__ int seq_rows(const SeqMap& m, int b, int phys) {
+    if (phys < 0) return 0;
+    if (!m.len) return m.t_len;
+    return min(max(m.len[b], 0), m.t_len);
+}
+
 // One attention launch: a set of q-layers that all read one cache slot.
 struct AttnLaunch {
     const void* k;          // slot base of K: [nb][hkv][t_cap][D]
@@ -47,6 +69,7 @@ struct AttnLaunch {
     int append_write;       // and is written into the cache
     int nsplit, tps;        // splits per slab, tiles per split
     float* part;            // partial accumulators, then (m, l) pairs
+    SeqMap sm;              // cache entry and rows of each sequence
 };
 
 // One observation-window score launch over one cache slot.
@@ -66,6 +89,7 @@ struct ScoreLaunch {
     float* stats;           // [slabs][nsplit][rows_pad][2] partial (m, z)
     float* lse_ws;          // [slabs][rows_pad] merged log-normalisers
     int rows_pad;
+    SeqMap sm;
 };
 
 // Decode attention over a range-protected int8 slot.  `a` carries the
@@ -111,6 +135,7 @@ struct DkvLaunch {
     float* y;               // workspace [slabs][t_len][rank]
     double* gram;           // workspace [slabs][nsplit][rank][rank]
     float* w;               // workspace [slabs][rank][rank]
+    SeqMap sm;
 };
 
 struct SelectLaunch {
@@ -121,6 +146,8 @@ struct SelectLaunch {
     uint32_t layer_id;
     int32_t* kept;
     uint32_t* keys;         // workspace [slabs][t_len]
+    const int32_t* len;     // [nb] rows per slab's sequence, or null (t_len)
+    const int32_t* seq_id;  // [nb] sequence word of the Philox counter, or null (b)
 };
 
 struct CompactLaunch {
@@ -129,10 +156,11 @@ struct CompactLaunch {
     void* dk;
     void* dv;
     int nb, hkv;
-    int src_t_len, src_t_cap, dst_t_cap;
+    int src_t_cap, dst_t_cap;
     const int32_t* kept;
-    int n_keep;
+    int n_keep;             // stride of kept; sequence b keeps min(rows(b), n_keep)
     int elem;               // bytes per element
+    SeqMap src_sm, dst_sm;  // src_sm.len gives the source rows
 };
 
 // Host-side launchers (defined next to their kernels).  Each returns
@@ -142,10 +170,10 @@ hipError_t launch_attn(const AttnLaunch& p, int dtype, int nt, hipStream_t s);
 hipError_t launch_attn_combine(const AttnLaunch& p, hipStream_t s);
 hipError_t launch_attn_q8(const Q8AttnLaunch& p, int nt, hipStream_t s);
 hipError_t launch_q8_quantize(const Q8QuantLaunch& p, hipStream_t s);
-hipError_t launch_append(const void* k, const void* v, int nb, int hkv, int t_len,
-                         int t_cap, const void* k_new, const void* v_new, int elem,
+hipError_t launch_append(const void* k, const void* v, int nb, int hkv, int t_cap,
+                         const SeqMap& sm, const void* k_new, const void* v_new, int elem,
                          hipStream_t s);
-hipError_t launch_value_range(const void* v, int nb, int hkv, int t_len, int t_cap,
+hipError_t launch_value_range(const void* v, int nb, int hkv, int t_cap, const SeqMap& sm,
                               int dtype, float* range, hipStream_t s);
 hipError_t launch_score(const ScoreLaunch& p, int dtype, hipStream_t s);
 hipError_t launch_select(const SelectLaunch& p, hipStream_t s);

@@ -20,6 +20,11 @@
 // pairs (kernel boundaries order the two, so no cross-workgroup fences are
 // needed).  The range is fused into the score pass: the wave that takes a
 // tile also reads the tile's V block.
+//
+// Ragged batches: sequence b has its own row count T_b (window row i sees
+// t <= T_b - w + i; a row that sees nothing adds nothing) and is read from
+// cache entry phys(b); per-row outputs keep the launch's t_len as their row
+// stride.
 #include <type_traits>
 
 #include "common.h"
@@ -160,10 +165,12 @@ __global__ __launch_bounds__(1024) void score_stats_bf16(ScoreLaunch p) {
     const int slab = b * p.hkv + j;
     const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
     const int l16 = lane & 15, lg = lane >> 4;
-    const int T = p.t_len;
+    const int phys = seq_phys(p.sm, b);
+    const int T = seq_rows(p.sm, b, phys);   // a split past the end writes (-inf, 0)
     const int ntiles = (T + SCORE_TILE - 1) / SCORE_TILE;
     const int tile_begin = s * p.tps, tile_end = min(tile_begin + p.tps, ntiles);
-    const uint16_t* kslab = reinterpret_cast<const uint16_t*>(p.k) + (size_t)slab * p.t_cap * D;
+    const uint16_t* kslab =
+        reinterpret_cast<const uint16_t*>(p.k) + ((size_t)max(phys, 0) * p.hkv + j) * p.t_cap * D;
 
     QFrag Q;
     load_qfrag(Q, p, b, j, wave, l16, lg);
@@ -264,7 +271,11 @@ __global__ __launch_bounds__(256) void score_main_bf16(ScoreLaunch p) {
     const int slab = b * p.hkv + j;
     const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
     const int l16 = lane & 15, lg = lane >> 4;
-    const int T = p.t_len;
+    const int phys = seq_phys(p.sm, b);
+    const int T = seq_rows(p.sm, b, phys);
+    const int ntiles = (T + SCORE_TILE - 1) / SCORE_TILE;
+    const int tile_begin = s * p.main_tps, tile_end = min(tile_begin + p.main_tps, ntiles);
+    if (tile_begin >= ntiles) return;   // past the sequence's end (whole workgroup)
     const int MT = (p.rows + 15) / 16;
     uint16_t* qs = reinterpret_cast<uint16_t*>(smem);                          // [MT*16][QPITCH]
     float* l2s = reinterpret_cast<float*>(smem + (size_t)MT * 16 * QPITCH * 2);  // [MT*16] 64 - lse*log2 e
@@ -294,13 +305,12 @@ __global__ __launch_bounds__(256) void score_main_bf16(ScoreLaunch p) {
     }
     __syncthreads();
 
-    const uint16_t* kslab = reinterpret_cast<const uint16_t*>(p.k) + (size_t)slab * p.t_cap * D;
-    const uint16_t* vslab = reinterpret_cast<const uint16_t*>(p.v) + (size_t)slab * p.t_cap * D;
-    float* score = p.score + (size_t)slab * T;
-    float* range = RANGE ? p.range + (size_t)slab * T : nullptr;
+    const size_t cslab = (size_t)phys * p.hkv + j;
+    const uint16_t* kslab = reinterpret_cast<const uint16_t*>(p.k) + cslab * p.t_cap * D;
+    const uint16_t* vslab = reinterpret_cast<const uint16_t*>(p.v) + cslab * p.t_cap * D;
+    float* score = p.score + (size_t)slab * p.t_len;
+    float* range = RANGE ? p.range + (size_t)slab * p.t_len : nullptr;
     const float c1 = p.scale * LOG2E;
-    const int ntiles = (T + SCORE_TILE - 1) / SCORE_TILE;
-    const int tile_begin = s * p.main_tps, tile_end = min(tile_begin + p.main_tps, ntiles);
 
     // TAIL: some (row, column) pairs of the tile are not visible (the causal
     // window, or columns past t_len whose K bits are arbitrary); they are
@@ -384,11 +394,13 @@ __global__ __launch_bounds__(256) void score_f32(ScoreLaunch p, int stats_pass) 
     const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int slab = b * p.hkv + j;
     const int tid = threadIdx.x, tl = tid % FT, rg = tid / FT;
-    const int T = p.t_len;
+    const int phys = seq_phys(p.sm, b);
+    const int T = seq_rows(p.sm, b, phys);
     const int ntiles = (T + FT - 1) / FT;
     const int tile_begin = s * p.tps, tile_end = min(tile_begin + p.tps, ntiles);
-    const float* kslab = reinterpret_cast<const float*>(p.k) + (size_t)slab * p.t_cap * D;
-    const float* vslab = reinterpret_cast<const float*>(p.v) + (size_t)slab * p.t_cap * D;
+    const size_t cslab = (size_t)max(phys, 0) * p.hkv + j;
+    const float* kslab = reinterpret_cast<const float*>(p.k) + cslab * p.t_cap * D;
+    const float* vslab = reinterpret_cast<const float*>(p.v) + cslab * p.t_cap * D;
     __shared__ float ks[FT][D + 1];
     __shared__ float csum[4][FT];
 
@@ -433,7 +445,7 @@ __global__ __launch_bounds__(256) void score_f32(ScoreLaunch p, int stats_pass) 
             csum[rg][tl] = c;
             __syncthreads();
             if (tid < FT && t0 + tid < T) {
-                p.score[(size_t)slab * T + t0 + tid] =
+                p.score[(size_t)slab * p.t_len + t0 + tid] =
                     csum[0][tid] + csum[1][tid] + csum[2][tid] + csum[3][tid];
                 if (p.range) {
                     float mx = -INFINITY, mn = INFINITY;
@@ -442,7 +454,7 @@ __global__ __launch_bounds__(256) void score_f32(ScoreLaunch p, int stats_pass) 
                         mx = fmaxf(mx, v);
                         mn = fminf(mn, v);
                     }
-                    p.range[(size_t)slab * T + t0 + tid] = mx - mn;
+                    p.range[(size_t)slab * p.t_len + t0 + tid] = mx - mn;
                 }
             }
         }
@@ -469,14 +481,18 @@ __global__ __launch_bounds__(256) void score_f32(ScoreLaunch p, int stats_pass) 
 // Standalone value range: one workgroup of four waves per 512 rows of a
 // slab; wave w reduces channels 32w .. 32w+31, lanes own 8 rows each.
 template <typename E>
-__global__ __launch_bounds__(256) void value_range_kernel(const E* v, int hkv, int t_len,
-                                                          int t_cap, float* range) {
+__global__ __launch_bounds__(256) void value_range_kernel(const E* v, int hkv, int t_cap,
+                                                          SeqMap sm, float* range) {
     constexpr int VEC = 16 / sizeof(E);          // rows per 16-byte access
     constexpr int ROWS = VEC * WAVE;             // rows per workgroup
-    const int slab = blockIdx.z * hkv + blockIdx.y;
+    const int b = blockIdx.z;
+    const int slab = b * hkv + blockIdx.y;
+    const int phys = seq_phys(sm, b);
+    const int t_len = seq_rows(sm, b, phys);
+    if (blockIdx.x * ROWS >= t_len) return;      // past the sequence's end
     const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
     const int t0 = blockIdx.x * ROWS + lane * VEC;
-    const E* vs = v + (size_t)slab * t_cap * D;
+    const E* vs = v + ((size_t)phys * hkv + blockIdx.y) * t_cap * D;
     __shared__ float smx[4][ROWS], smn[4][ROWS];
     float mx[VEC], mn[VEC];
 #pragma unroll
@@ -508,7 +524,7 @@ __global__ __launch_bounds__(256) void value_range_kernel(const E* v, int hkv, i
         if (t < t_len) {
             const float a = fmaxf(fmaxf(smx[0][x], smx[1][x]), fmaxf(smx[2][x], smx[3][x]));
             const float c = fminf(fminf(smn[0][x], smn[1][x]), fminf(smn[2][x], smn[3][x]));
-            range[(size_t)slab * t_len + t] = a - c;
+            range[(size_t)slab * sm.t_len + t] = a - c;
         }
     }
 }
@@ -545,16 +561,16 @@ hipError_t launch_score(const ScoreLaunch& p, int dtype, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_value_range(const void* v, int nb, int hkv, int t_len, int t_cap, int dtype,
-                              float* range, hipStream_t st) {
+hipError_t launch_value_range(const void* v, int nb, int hkv, int t_cap, const SeqMap& sm,
+                              int dtype, float* range, hipStream_t st) {
     if (dtype == 0) {
-        const dim3 grid((t_len + 4 * WAVE - 1) / (4 * WAVE), hkv, nb);
+        const dim3 grid((sm.t_len + 4 * WAVE - 1) / (4 * WAVE), hkv, nb);
         hipLaunchKernelGGL(value_range_kernel<float>, grid, dim3(256), 0, st, (const float*)v, hkv,
-                           t_len, t_cap, range);
+                           t_cap, sm, range);
     } else {
-        const dim3 grid((t_len + 8 * WAVE - 1) / (8 * WAVE), hkv, nb);
+        const dim3 grid((sm.t_len + 8 * WAVE - 1) / (8 * WAVE), hkv, nb);
         hipLaunchKernelGGL(value_range_kernel<uint16_t>, grid, dim3(256), 0, st,
-                           (const uint16_t*)v, hkv, t_len, t_cap, range);
+                           (const uint16_t*)v, hkv, t_cap, sm, range);
     }
     return hipGetLastError();
 }

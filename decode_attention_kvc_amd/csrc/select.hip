@@ -113,10 +113,10 @@ __device__ __forceinline__ uint32_t range_key(float r) {
 }
 
 // Exponential key of row t; +inf when the weight is not positive.
-__device__ __forceinline__ uint32_t sample_key(const SelectLaunch& p, int t, int j, int b,
+__device__ __forceinline__ uint32_t sample_key(const SelectLaunch& p, int t, int j, uint32_t seq,
                                                float score) {
     if (!(score > 0.f)) return 0x7F800000u;
-    const Philox4 r = philox4x32_10((uint32_t)t, (uint32_t)j, p.layer_id, (uint32_t)b, p.seed_lo,
+    const Philox4 r = philox4x32_10((uint32_t)t, (uint32_t)j, p.layer_id, seq, p.seed_lo,
                                     p.seed_hi);
     const double m = 4294967295.0 - (double)r.x0;          // 2^32 - 1 - x
     const double e = -log1p(-m * 2.3283064365386963e-10);  // -ln((x + 1) / 2^32)
@@ -131,17 +131,22 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectLaunch p) {
     const int slab = blockIdx.x;
     const int b = slab / p.hkv, j = slab % p.hkv;
     const int tid = threadIdx.x;
-    const int T = p.t_len;
+    // Ragged batches: the slab's own row count T (at most t_len, which is
+    // the row stride of score / range / keys) and kept stride min(t_len, K+B);
+    // kept entries past the slab's min(T, K+B) are -1.
+    const int T = p.len ? min(max(p.len[b], 0), p.t_len) : p.t_len;
+    const uint32_t seq = p.seq_id ? (uint32_t)p.seq_id[b] : (uint32_t)b;
     const int kb = p.budget_k + p.recent_b;
-    const int n_keep = min(T, kb);
-    int32_t* kept = p.kept + (size_t)slab * n_keep;
+    const int stride = min(p.t_len, kb);
+    int32_t* kept = p.kept + (size_t)slab * stride;
     if (T <= kb) {
-        for (int t = tid; t < T; t += NT) kept[t] = t;
+        for (int t = tid; t < stride; t += NT) kept[t] = t < T ? t : -1;
         return;
     }
-    const float* score = p.score + (size_t)slab * T;
-    const float* range = p.range + (size_t)slab * T;
-    uint32_t* keys = IN_LDS ? lds_keys : p.keys + (size_t)slab * T;
+    const int n_keep = kb;
+    const float* score = p.score + (size_t)slab * p.t_len;
+    const float* range = p.range + (size_t)slab * p.t_len;
+    uint32_t* keys = IN_LDS ? lds_keys : p.keys + (size_t)slab * p.t_len;
     const int ncand = T - p.recent_b;
 
     // 1. N_v candidates of largest range (ties to the lower row).
@@ -166,7 +171,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectLaunch p) {
         eq_seen += tot;
         if (valid) {
             const bool prot = p.n_v > 0 && (rk < rthr || (eq && rank < rtake));
-            keys[t] = prot ? EXCLUDED : sample_key(p, t, j, b, score[t]);
+            keys[t] = prot ? EXCLUDED : sample_key(p, t, j, seq, score[t]);
         }
     }
     __syncthreads();

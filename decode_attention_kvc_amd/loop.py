@@ -189,3 +189,231 @@ class Decoder:
         e = torch.cuda.Event(enable_timing=True)
         e.record()
         self.events.append((ev, e, c.t_len, n_calls))
+
+
+# ---------------------------------------------------------------------------
+# Ragged batches
+# ---------------------------------------------------------------------------
+def ragged_plan(t0, n_steps, evict):
+    """The ragged schedule as host bookkeeping: per step the entry and length
+    of every sequence during attention ("att_idx", "att_len"), the passes
+    ({step: dict(seqs, src, dst, lens, t_len, round, fresh)}), the longest
+    length reached ("peak") and the batch entries used ("entries").
+    `fresh`: no sequence of the pass was compacted inside its window, so the
+    window's log-normalisers from decode attention are valid."""
+    nb, ev = len(t0), evict
+    kb = ev["K"] + ev["B"] if ev else None
+    lens = [min(int(t), kb) for t in t0] if ev else [int(t) for t in t0]
+    entry = list(range(nb))
+    free = []
+    att_idx, att_len, passes = [], [], {}
+    last = [-1] * nb                     # step of each sequence's last pass
+    peak = max(lens) if lens else 0
+    n_entries = nb
+    r = 1
+    for s in range(n_steps):
+        lens = [t + 1 for t in lens]
+        peak = max(peak, max(lens))
+        att_idx.append(list(entry))
+        att_len.append(list(lens))
+        if not ev:
+            continue
+        due = [b for b in range(nb)
+               if (s + 1 + ev["phase"][b]) % ev["period"] == 0 and s + 1 >= ev["w"]
+               and lens[b] > kb]
+        if not due:
+            continue
+        src = [entry[b] for b in due]
+        dst = []
+        for b in due:
+            if free:
+                dst.append(free.pop(0))
+            else:
+                dst.append(n_entries)
+                n_entries += 1
+        passes[s] = dict(seqs=due, src=src, dst=dst, lens=[lens[b] for b in due],
+                         t_len=max(lens[b] for b in due), round=r,
+                         fresh=all(last[b] <= s - ev["w"] for b in due))
+        for b, d in zip(due, dst):
+            entry[b] = d
+            lens[b] = kb
+            last[b] = s
+        free.extend(src)
+        r += 1
+    return dict(att_idx=att_idx or [[0] * nb], att_len=att_len or [[0] * nb], passes=passes,
+                peak=peak, entries=n_entries, final_len=lens, final_entry=entry)
+
+
+class RaggedDecoder:
+    """Decode loop of a ragged batch: every sequence has its own length and
+    runs its eviction passes on its own steps.
+
+    VASE summary (gist.science 2606.03928), §2 gives the periodic pass per
+    sequence.  Sequence b has a phase p_b and is due after step s when
+    (s + 1 + p_b) is a multiple of the period, it has decoded at least w
+    steps, and it holds more than K + B rows.  The sequences due after one
+    step form one pass (pass r uses seed + r, the prompt compression being
+    pass 0); the Philox counter's batch word is the sequence index.
+
+    Every sequence lives in one batch entry of `cache`, which holds a few
+    more entries than sequences: a pass compacts each due sequence into a
+    free entry and frees the one it leaves (no second cache, and sequences
+    that are not due are not touched).  Because every sequence appends one
+    row per step, the whole schedule (lengths, due sets, entries) is host
+    bookkeeping fixed by the prompt lengths; it is planned here once and its
+    per-step device arrays are uploaded once, so a step only launches
+    kernels.  Window queries of the due sequences are gathered into the
+    [w][n_due][Hq][d] layout kvc_score takes (argument marshalling).
+    """
+
+    def __init__(self, n_layers, leaders, cache, n_q_heads, t0, n_steps, evict=None,
+                 mode="grouped", record_events=False):
+        """record_events: keep HIP event pairs around each step's attention
+        calls (self.events: (start, end, step, n_calls)) and each eviction
+        pass (self.pass_events: (start, end, step, n_sequences))."""
+        self.events = [] if record_events else None
+        self.pass_events = [] if record_events else None
+        self.n_layers = n_layers
+        self.leaders = list(leaders)
+        self.src_layer, self.src_slot = K.kvc_share_map(n_layers, self.leaders)
+        self.cache = cache
+        self.hq = n_q_heads
+        self.ev = evict
+        self.mode = mode
+        self.nb = nb = len(t0)
+        self.t0 = [int(x) for x in t0]
+        self.groups = [[l for l in range(n_layers) if self.src_slot[l] == s]
+                       for s in range(len(leaders))]
+        if mode == "grouped":
+            for g in self.groups:
+                if g != list(range(g[0], g[0] + len(g))):
+                    raise ValueError("grouped mode needs each leader's followers to be contiguous")
+        elif mode != "per-layer":
+            raise ValueError(f"unknown mode {mode!r}")
+        dev = cache.k.device
+        plan = ragged_plan(self.t0, n_steps, evict)
+        if max(plan["peak"], 1) > cache.t_cap:
+            raise ValueError(f"the schedule reaches {plan['peak']} rows; t_cap is {cache.t_cap}")
+        if plan["entries"] > cache.nb_cap:
+            raise ValueError(f"the schedule needs {plan['entries']} batch entries; "
+                             f"the cache has {cache.nb_cap}")
+        self.plan = plan
+        # per-step entries and lengths, one upload
+        self.att_idx = torch.tensor(plan["att_idx"], dtype=torch.int32, device=dev)
+        self.att_len = torch.tensor(plan["att_len"], dtype=torch.int32, device=dev)
+        self.passes = {}
+        for s, p in plan["passes"].items():
+            arr = torch.tensor([p["seqs"], p["src"], p["dst"], p["lens"]], dtype=torch.int32,
+                               device=dev)
+            self.passes[s] = dict(p, seqs_d=arr[0], src_d=arr[1], dst_d=arr[2], lens_d=arr[3])
+        self.prompt_len = torch.tensor(self.t0, dtype=torch.int32, device=dev)
+        self.seq_ids = torch.arange(nb, dtype=torch.int32, device=dev)
+        nql = 1 if mode != "grouped" else max(len(g) for g in self.groups)
+        self.ws_attn = torch.zeros(max(16, K.kvc_decode_attn_ws_bytes(
+            cache.seqs(self.seq_ids, self.prompt_len, t_len=cache.t_cap), nql, n_q_heads)),
+            dtype=torch.uint8, device=dev)
+        self._ebufs = None
+
+    def view(self, s):
+        """The cache as decode step s addresses it."""
+        return self.cache.seqs(self.att_idx[s], self.att_len[s],
+                               t_len=int(max(self.plan["att_len"][s])))
+
+    # ------------------------------------------------------------------ decode
+    def step(self, s, qpool, lsepool, knew, vnew, out):
+        """Decode step s: every sequence appends (leaders) and attends, then
+        the sequences due run their eviction pass.  Returns True if a pass
+        ran."""
+        c = self.view(s)
+        n_steps = qpool.shape[1]
+        nb, hq, d = qpool.shape[2], qpool.shape[3], qpool.shape[4]
+        ev0 = self._event()
+        if self.mode == "per-layer":
+            for l in range(self.n_layers):
+                slot = self.src_slot[l]
+                lead = self.src_layer[l] == l
+                K.kvc_decode_attn(c, qpool[l, s], [slot], out[l], lsepool[l, s], self.ws_attn,
+                                  k_new=knew[s, slot] if lead else None,
+                                  v_new=vnew[s, slot] if lead else None,
+                                  append_slot=slot if lead else -1, n_q_heads=hq)
+        else:
+            for slot, layers in enumerate(self.groups):
+                K.kvc_decode_attn(c, qpool[layers[0], s], [slot] * len(layers), out[layers[0]],
+                                  lsepool[layers[0], s], self.ws_attn, k_new=knew[s, slot],
+                                  v_new=vnew[s, slot], append_slot=slot,
+                                  q_layer_stride=n_steps * nb * hq * d,
+                                  out_layer_stride=nb * hq * d,
+                                  lse_layer_stride=n_steps * nb * hq, n_q_heads=hq)
+        if ev0 is not None:
+            self.events.append((ev0, self._event(), s,
+                                self.n_layers if self.mode == "per-layer" else len(self.groups)))
+        p = self.passes.get(s)
+        if p is None:
+            return False
+        ev1 = self._event()
+        w = self.ev["w"]
+        windows = []
+        for leader in self.leaders:
+            q_obs = qpool[leader, s - w + 1:s + 1].index_select(1, p["seqs_d"].long())
+            lse = (lsepool[leader, s - w + 1:s + 1].index_select(1, p["seqs_d"].long())
+                   if p["fresh"] else None)
+            windows.append((q_obs, lse))
+        src = self.cache.seqs(p["src_d"], p["lens_d"], t_len=p["t_len"])
+        dst = self.cache.seqs(p["dst_d"], None, t_len=self.ev["K"] + self.ev["B"])
+        self._pass(src, dst, windows, p["seqs_d"], p["round"])
+        if ev1 is not None:
+            self.pass_events.append((ev1, self._event(), s, len(p["seqs"])))
+        return True
+
+    def _event(self):
+        if self.events is None:
+            return None
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    # ---------------------------------------------------------------- eviction
+    def _bufs(self, src):
+        """Eviction buffers for a pass over the sequences of `src` (grown on
+        demand, kept between passes)."""
+        n, t, hkv = src.nb, src.t_len, src.n_kv_heads
+        e, dev = self.ev, src.k.device
+        b = self._ebufs
+        if b is None or b["n"] < n or b["t"] < t:
+            n, t = max(n, b["n"] if b else 0), max(t, b["t"] if b else 0)
+            b = dict(n=n, t=t, score=torch.empty(n * hkv * t, device=dev),
+                     rng=torch.empty(n * hkv * t, device=dev),
+                     kept=torch.empty(n * hkv * (e["K"] + e["B"]), dtype=torch.int32, device=dev),
+                     sel_ws=torch.empty(max(16, K.kvc_select_ws_bytes(n, hkv, t)),
+                                        dtype=torch.uint8, device=dev),
+                     score_ws=torch.zeros(16, dtype=torch.uint8, device=dev))
+            self._ebufs = b
+        need = K.kvc_score_ws_bytes(src, self.hq, e["w"])
+        if b["score_ws"].numel() < need:
+            b["score_ws"] = torch.zeros(need, dtype=torch.uint8, device=dev)
+        return b
+
+    def _pass(self, src, dst, windows, seq_ids, r):
+        """One eviction pass over the sequences of `src` (moved to the entries
+        of `dst`), every leader slot."""
+        e = self.ev
+        n, hkv, T = src.nb, src.n_kv_heads, src.t_len
+        n_keep = min(T, e["K"] + e["B"])
+        b = self._bufs(src)
+        score = b["score"][: n * hkv * T]
+        rng = b["rng"][: n * hkv * T]
+        kept = b["kept"][: n * hkv * n_keep]
+        for slot, leader in enumerate(self.leaders):
+            q_obs, lse = windows[slot]
+            K.kvc_score(src, slot, q_obs, score, rng, lse, None if lse is not None else b["score_ws"])
+            K.kvc_select_seq(score, rng, n, hkv, T, src.seq_len, seq_ids, e["K"], e["B"], e["N_v"],
+                             e["seed"] + r, leader, kept, b["sel_ws"])
+            K.kvc_compact(src, slot, kept, n_keep, dst)
+
+    def initial_pass(self, prompt, q_obs_by_slot):
+        """Pass 0: compress each sequence's prompt (entry b of `prompt`, t0[b]
+        rows) into its entry of the decode cache (min(t0[b], K + B) rows;
+        shorter prompts are copied whole)."""
+        src = prompt.seqs(None, self.prompt_len, t_len=max(self.t0))
+        dst = self.cache.seqs(self.seq_ids, None, t_len=self.ev["K"] + self.ev["B"])
+        self._pass(src, dst, [(q, None) for q in q_obs_by_slot], self.seq_ids, 0)

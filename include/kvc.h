@@ -71,16 +71,35 @@ typedef enum kvc_dtype {
 #define KVC_V_TILE 32
 
 /*
- * A KV cache of n_slots leader slots (one per layer in S), batch nb,
- * n_kv_heads heads and head_dim = 128.  One slab = one (slot, b, kv head).
- *   k: [n_slots][nb][n_kv_heads][t_cap][head_dim]        row-major rows
- *   v: [n_slots][nb][n_kv_heads][t_cap/32][head_dim][32] tiles of 32 tokens,
- *      each tile channel-major: value V[t][c] of a slab sits at element
- *      (t/32)*head_dim*32 + c*32 + t%32.  A tile's values are one contiguous
- *      block, and the token-contiguous operand of the P*V product loads with
- *      one 16-byte access per lane.
- * Rows [0, t_len) are valid in every slot; t_len is shared by all slots.
+ * A KV cache of n_slots leader slots (one per layer in S), nb_cap batch
+ * entries, n_kv_heads heads and head_dim = 128.  One slab = one (slot, batch
+ * entry, kv head).
+ *   k: [n_slots][nb_cap][n_kv_heads][t_cap][head_dim]        row-major rows
+ *   v: [n_slots][nb_cap][n_kv_heads][t_cap/32][head_dim][32] tiles of 32
+ *      tokens, each tile channel-major: value V[t][c] of a slab sits at
+ *      element (t/32)*head_dim*32 + c*32 + t%32.  A tile's values are one
+ *      contiguous block, and the token-contiguous operand of the P*V product
+ *      loads with one 16-byte access per lane.
  * dtype is a kvc_dtype; both k and v hold that type.
+ *
+ * A call addresses nb sequences.  Uniform batches (batch_idx = seq_len =
+ * NULL, nb_cap = 0 or nb): sequence b is batch entry b and rows [0, t_len)
+ * are valid in every slot.
+ * Ragged batches (per-sequence lengths, and eviction passes that run on
+ * each sequence's own steps):
+ *   batch_idx: NULL or device int32 [nb]: sequence b is stored in batch
+ *              entry batch_idx[b] (an entry outside [0, nb_cap) makes the
+ *              sequence empty).  Lets a call address any subset of the
+ *              entries, and lets a sequence move between entries (an
+ *              eviction pass compacts it into a free entry).
+ *   seq_len:   NULL or device int32 [nb]: sequence b holds rows
+ *              [0, seq_len[b]) (entries are clamped to [0, t_len]).  t_len
+ *              is then the bound that sizes launches and workspaces and the
+ *              row stride of per-row outputs (score, range).
+ * Per-sequence inputs and outputs (queries, new rows, out, lse, score,
+ * range, kept) are indexed by b, the sequence's position in the call.  An
+ * empty sequence reads and writes no cache row; its attention output is zero
+ * with lse = -inf.  Both arrays are read on the device, in stream order.
  */
 typedef struct kvc_cache {
     void* k;
@@ -92,6 +111,9 @@ typedef struct kvc_cache {
     int32_t head_dim;
     int32_t t_len;
     int32_t t_cap;
+    int32_t nb_cap;              /* batch entries of k / v; 0 means nb     */
+    const int32_t* batch_idx;    /* device [nb] or NULL                    */
+    const int32_t* seq_len;      /* device [nb] or NULL                    */
 } kvc_cache;
 
 /*
@@ -148,9 +170,10 @@ int kvc_share_map(int n_layers, const int32_t* leaders, int n_leaders,
 
 /*
  * Leader append [RCLA, implementation paragraph]: write one new row per
- * (b, kv head) at row t_len - 1 of `slot` (the caller has already counted
- * the row in c->t_len).  k_new, v_new: device [nb][n_kv_heads][head_dim],
- * same dtype as the cache.  Followers never call this.
+ * (b, kv head) at row t_len - 1 of `slot` (ragged: row seq_len[b] - 1; the
+ * caller has already counted the row).  k_new, v_new: device
+ * [nb][n_kv_heads][head_dim], same dtype as the cache.  Followers never
+ * call this.
  */
 int kvc_append(const kvc_cache* c, int slot, const void* k_new,
                const void* v_new, kvc_stream_t stream);
@@ -166,14 +189,16 @@ int kvc_decode_attn_ws_bytes(const kvc_cache* c, int n_q_layers,
  * kv head j = h / g (contiguous groups):
  *     out[i][b][h] = softmax_t(scale * q[i][b][h] . K[s][b][j][t]) V[s][b][j][t]
  *     lse[i][b][h] = log sum_t exp(scale * q[i][b][h] . K[s][b][j][t])
- * over t in [0, c->t_len), where s = q_slot[i] (a host array; normally the
- * src_slot of the layer).  Several q-layers that read one slot are served by
- * one pass over that slot's KV (all followers of a leader in one call), or
- * the caller makes one call per layer.
+ * over t in [0, c->t_len) (ragged: [0, seq_len[b])), where s = q_slot[i]
+ * (a host array; normally the src_slot of the layer).  Several q-layers
+ * that read one slot are served by one pass over that slot's KV (all
+ * followers of a leader in one call), or the caller makes one call per
+ * layer.
  *   q:   device [n_q_layers][nb][n_q_heads][head_dim], cache dtype; q-layer
  *        i starts q_layer_stride elements after q-layer i-1 (0 = packed).
  *   scale: 0 means 1/sqrt(head_dim).
- *   append_slot >= 0: row t_len-1 of that slot is taken from k_new/v_new
+ *   append_slot >= 0: row t_len-1 (ragged: seq_len[b]-1) of that slot is
+ *        taken from k_new/v_new
  *        (device [nb][n_kv_heads][head_dim]) and also written into the
  *        cache, as kvc_append does; -1: no append, k_new/v_new ignored.
  *   out: device float32 [n_q_layers][nb][n_q_heads][head_dim], layer stride
@@ -194,8 +219,9 @@ int kvc_decode_attn(const kvc_cache* c, const void* q, int64_t q_layer_stride,
 /*
  * Value range [VASE §2.A]: range[b][j][t] = max_c V[slot][b][j][t][c]
  *                                         - min_c V[slot][b][j][t][c]
- * over the head_dim channels of each value row, t in [0, t_len), computed
- * in float32 (exact rounding of the true difference).
+ * over the head_dim channels of each value row, t in [0, t_len) (ragged:
+ * [0, seq_len[b]); rows past it are not written), computed in float32
+ * (exact rounding of the true difference).
  *   range: device float32 [nb][n_kv_heads][t_len].
  */
 int kvc_value_range(const kvc_cache* c, int slot, float* range,
@@ -209,7 +235,10 @@ int kvc_score_ws_bytes(const kvc_cache* c, int n_q_heads, int w,
  * Observation-window score [VASE §2.B, SnapKV-derived], one pass over the
  * slot's KV.  For slab (b, j) the rows are (h in the group of j, i < w) with
  * queries q_obs[i][b][h]; window row i sees cache rows t <= t_len - w + i
- * (it was issued when the cache held t_len - w + i + 1 rows).
+ * (it was issued when the cache held t_len - w + i + 1 rows).  Ragged:
+ * t <= seq_len[b] - w + i, and a window row that sees no row adds nothing
+ * (its lse_obs entry is ignored); rows past seq_len[b] are
+ * not written.
  *     score[b][j][t] = sum_{h,i} softmax_t(scale * q_obs[i][b][h] . K[t])
  *   q_obs:   device [w][nb][n_q_heads][head_dim], cache dtype, oldest first.
  *   lse_obs: device float32 [w][nb][n_q_heads] holding the log-normaliser of
@@ -229,6 +258,19 @@ int kvc_score(const kvc_cache* c, int slot, const void* q_obs, int n_q_heads,
 
 /* Workspace bytes kvc_select needs for nb * n_kv_heads slabs of t_len rows. */
 int kvc_select_ws_bytes(int nb, int n_kv_heads, int t_len, size_t* bytes);
+
+/*
+ * kvc_select for ragged batches: slab (b, j) has T_b = seq_len[b] rows
+ * (clamped to [0, t_len]; NULL: t_len each) and keeps min(T_b, K + B) of
+ * them; kept keeps the stride n_keep = min(t_len, K + B) and its entries
+ * past min(T_b, K + B) are -1.  The Philox counter's batch word is
+ * seq_id[b] (NULL: b), so that a sequence draws the same keys whatever its
+ * position in the call.  score / range rows keep the stride t_len.
+ */
+int kvc_select_seq(const float* score, const float* range, int nb, int n_kv_heads,
+                   int t_len, const int32_t* seq_len, const int32_t* seq_id,
+                   int budget_k, int recent_b, int n_v, uint64_t seed, int layer_id,
+                   int32_t* kept, void* ws, size_t ws_bytes, kvc_stream_t stream);
 
 /*
  * VASE selection [VASE §2, §2.A, §2.B], per slab (b, j):
@@ -264,6 +306,13 @@ int kvc_select(const float* score, const float* range, int nb, int n_kv_heads,
  * caller sets dst->t_len = n_keep afterwards.  kept: device int32
  * [nb][n_kv_heads][n_keep] with entries in [0, src->t_len); a row whose
  * index is out of that range is written as zeros.
+ * Ragged batches: sequence b is read from its src entry and written to its
+ * dst entry (each side's batch_idx) and keeps min(T_b, n_keep) rows, T_b its
+ * src length; the caller then sets its dst length to that.  With a batch
+ * map on either side, src and dst may be one cache: the caller keeps every
+ * sequence's src and dst entries apart (not checked, the maps are device
+ * data); a shared entry gives unspecified rows, never an access outside the
+ * buffers.
  */
 int kvc_compact(const kvc_cache* src, int slot, const int32_t* kept,
                 int n_keep, const kvc_cache* dst, kvc_stream_t stream);
@@ -321,7 +370,8 @@ int kvc_gaussian_bf16(int64_t n, uint64_t seed, uint32_t c1, uint32_t c2,
  * other row's key and value are quantized per row.  The caller sets
  * dst->t_len = src->t_len and dst->p_len = n_protect before the call;
  * n_protect <= dst->p_cap.  src must be bf16 (KVC_EDTYPE), with the same nb
- * and n_kv_heads as dst.
+ * and n_kv_heads as dst, and a uniform batch (no batch_idx / seq_len,
+ * nb_cap 0 or nb; KVC_EINVAL otherwise).
  */
 int kvc_q8_quantize(const kvc_cache* src, int slot, const int32_t* protect,
                     int n_protect, const kvc_qcache* dst, kvc_stream_t stream);

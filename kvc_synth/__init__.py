@@ -13,7 +13,8 @@ shapes are kept):
     (1% and x20 by default: a heavy-tailed value range);
   * optional depth correlation between consecutive leader slots:
     X_s = rho**gap * X_{s-1} + sqrt(1 - rho**(2*gap)) * eps, i.e. a
-    per-layer correlation rho applied over `gap` layers.
+    per-layer correlation rho applied over `gap` layers;
+  * ragged batches: prompt lengths uniform in [t_min, t_max] (length_mix).
 All tensors are logical: K and V as [.., T, d] rows.
 """
 import math
@@ -63,6 +64,13 @@ def kv_slot(nb, hkv, T, d=128, dtype=torch.bfloat16, device="cpu", seed=0,
         sel = idx.unsqueeze(-1).expand(-1, -1, -1, d)
         v_out.scatter_(2, sel, v.gather(2, sel) * outlier_scale)
     return k.to(dtype), v_out.to(dtype), k, v
+
+
+def length_mix(n, t_min, t_max, seed=0):
+    """Prompt lengths of a ragged batch: n integers uniform in [t_min, t_max]
+    (a seeded CPU generator), as a list."""
+    g = generator(seed, "cpu")
+    return [int(x) for x in torch.randint(t_min, t_max + 1, (n,), generator=g)]
 
 
 def queries(shape, dtype=torch.bfloat16, device="cpu", seed=0):
