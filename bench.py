@@ -240,7 +240,9 @@ def ragged_leg(args, cfg, qpool, lsepool, knew, vnew, out, steps, warm=3):
     """The same model shape as a ragged batch: prompt lengths from a seeded
     length mix (uniform in [t0/16, t0]), and every sequence evicting on its own
     steps (phase b * period / nb), through RaggedDecoder.  Timed like the main
-    leg; attention bytes count each sequence's own rows."""
+    leg; attention bytes count each sequence's own rows.  The warm-up covers
+    at least one period, so that the timed steps start with every code path
+    (including the first per-sequence pass) already loaded."""
     import torch
     import kvc_synth
     import decode_attention_kvc_amd as kvc
@@ -250,6 +252,9 @@ def ragged_leg(args, cfg, qpool, lsepool, knew, vnew, out, steps, warm=3):
     L, leaders, nb, hq, hkv, tmax = (cfg[k] for k in ("n_layers", "leaders", "nb", "hq", "hkv",
                                                        "t0"))
     n_slots = len(leaders)
+    warm = max(warm, e0["period"])
+    if warm + steps > qpool.shape[1]:
+        raise ValueError("the query pool is shorter than the ragged leg's warm-up and steps")
     t0 = kvc_synth.length_mix(nb, tmax // 16, tmax, seed=11)
     ev = dict(K=e0["K"], B=e0["B"], N_v=e0["N_v"], w=e0["w"], period=e0["period"],
               seed=e0["seed"], phase=[b * e0["period"] // nb for b in range(nb)])
@@ -273,9 +278,12 @@ def ragged_leg(args, cfg, qpool, lsepool, knew, vnew, out, steps, warm=3):
         dec.step(s, qpool, lsepool, knew, vnew, out)
     torch.cuda.synchronize()
     dec.events, dec.pass_events = [], []
+    host = {True: [], False: []}         # host time of step() calls, with / without a pass
     t_start = time.perf_counter()
     for s in range(warm, n_total):
+        h0 = time.perf_counter()
         dec.step(s, qpool, lsepool, knew, vnew, out)
+        host[s in plan["passes"]].append(time.perf_counter() - h0)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     att_ms = sum(a.elapsed_time(b) for a, b, _, _ in dec.events)
@@ -292,7 +300,7 @@ def ragged_leg(args, cfg, qpool, lsepool, knew, vnew, out, steps, warm=3):
     seq_passes = sum(n for _, _, _, n in dec.pass_events)
     lens = [plan["att_len"][s] for s in range(warm, n_total)]
     return dict(value=round(nb * steps / wall, 2), unit="tokens/s",
-                ms_per_step=round(1e3 * wall / steps, 4), mode=mode,
+                ms_per_step=round(1e3 * wall / steps, 4), mode=mode, warmup_steps=warm,
                 attention_GBps=round(gbps, 1), attention_frac=round(gbps / HBM_PEAK_GBPS, 4),
                 avg_launch_us=round(1e3 * att_ms / n_calls, 2),
                 prompt_tokens=t0, phases=ev["phase"],
@@ -301,6 +309,8 @@ def ragged_leg(args, cfg, qpool, lsepool, knew, vnew, out, steps, warm=3):
                 batch_entries=plan["entries"],
                 eviction_passes=len(pass_ms), sequence_passes=seq_passes,
                 pass_ms_mean=round(sum(pass_ms) / max(1, len(pass_ms)), 3),
+                host_ms_step=round(1e3 * sum(host[False]) / max(1, len(host[False])), 3),
+                host_ms_pass_step=round(1e3 * sum(host[True]) / max(1, len(host[True])), 3),
                 kernel="attn_bf16_kernel (+ merge) over per-sequence lengths; passes: "
                        "score, select, compact on the due sequences only")
 
@@ -323,6 +333,8 @@ def main():
     ap.add_argument("--no-grouped", action="store_true", help="skip the grouped-mode leg")
     ap.add_argument("--no-ragged", action="store_true",
                     help="skip the ragged-batch leg (length mix, per-sequence eviction steps)")
+    ap.add_argument("--ragged-only", action="store_true",
+                    help="profiling aid: run only the ragged-batch leg and print its result")
     ap.add_argument("--no-int8", action="store_true",
                     help="skip the range-protected int8 cache leg (decode attention only)")
     ap.add_argument("--protect-frac", type=float, default=0.01,
@@ -352,10 +364,24 @@ def main():
     n_slots = len(leaders)
     W, S = args.warmup, args.steps
     n_total = W + 2 * S + 2
+    if ev and not args.no_ragged:        # the ragged leg warms up for a full period
+        n_total = max(n_total, max(W, ev["period"]) + S + 1)
     if ev:
         steady_cap = ev["K"] + ev["B"] + ev["period"]
     else:
         steady_cap = t0 + n_total
+    if args.ragged_only:
+        if not ev or args.scoring != "attnv":
+            sys.exit("--ragged-only needs an eviction workload with window scores")
+        qpool = kvc_synth.queries((L, n_total, nb, hq, 128), device=dev, seed=1)
+        lsepool = torch.zeros((L, n_total, nb, hq), device=dev)
+        knew = kvc_synth.queries((n_total, n_slots, nb, hkv, 128), device=dev, seed=2)
+        vnew = kvc_synth.queries((n_total, n_slots, nb, hkv, 128), device=dev, seed=3)
+        out = torch.empty((L, nb, hq, 128), device=dev)
+        r = ragged_leg(args, cfg, qpool, lsepool, knew, vnew, out, S, warm=W)
+        print(json.dumps({"ragged_only": True, "workload": cfg["desc"], "steps": S, "warmup": W,
+                          "ragged": r}), flush=True)
+        return
     log(f"[bench] {args.workload}: setting up (prompt cache {t0} rows x {n_slots} slots)")
 
     # ---- inputs (untimed): prompt cache, query / append pools
@@ -462,7 +488,7 @@ def main():
     ragged_res = None
     if not args.no_ragged and ev and args.scoring == "attnv":
         log("[bench] ragged leg: setting up")
-        ragged_res = ragged_leg(args, cfg, qpool, lsepool, knew, vnew, out, S)
+        ragged_res = ragged_leg(args, cfg, qpool, lsepool, knew, vnew, out, S, warm=W)
         log(f"[bench] ragged: {ragged_res}")
 
     if args.copy_calibration:

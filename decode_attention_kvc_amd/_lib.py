@@ -124,12 +124,17 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+_HAS_GPU = None
+
+
 def _stream(stream):
+    """The caller's stream, else torch's current stream (None without a GPU)."""
+    global _HAS_GPU
     if stream is not None:
         return stream
-    if torch.cuda.is_available():
-        return torch.cuda.current_stream().cuda_stream
-    return None
+    if _HAS_GPU is None:
+        _HAS_GPU = torch.cuda.is_available()
+    return torch.cuda.current_stream().cuda_stream if _HAS_GPU else None
 
 
 def _dtype_code(dt):
@@ -204,9 +209,15 @@ class Cache:
         return self.k.dtype
 
     def desc(self):
-        return kvc_cache(self.k.data_ptr(), self.v.data_ptr(), _dtype_code(self.k.dtype),
-                         self.n_slots, self.nb, self.n_kv_heads, HEAD_DIM, int(self.t_len),
-                         self.t_cap, self.nb_cap, _ptr(self.batch_idx), _ptr(self.seq_len))
+        """The kvc_cache descriptor (built once per object; t_len refreshed)."""
+        d = self.__dict__.get("_desc")
+        key = (self.k.data_ptr(), self.v.data_ptr(), _ptr(self.batch_idx), _ptr(self.seq_len))
+        if d is None or self.__dict__.get("_desc_key") != key:
+            d = kvc_cache(key[0], key[1], _dtype_code(self.k.dtype), self.n_slots, self.nb,
+                          self.n_kv_heads, HEAD_DIM, 0, self.t_cap, self.nb_cap, key[2], key[3])
+            self.__dict__["_desc"], self.__dict__["_desc_key"] = d, key
+        d.t_len = int(self.t_len)
+        return d
 
     # views in logical [..][t][d] form (plumbing for tests and data setup)
     def k_rows(self, slot):

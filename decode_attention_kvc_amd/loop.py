@@ -305,7 +305,8 @@ class RaggedDecoder:
         for s, p in plan["passes"].items():
             arr = torch.tensor([p["seqs"], p["src"], p["dst"], p["lens"]], dtype=torch.int32,
                                device=dev)
-            self.passes[s] = dict(p, seqs_d=arr[0], src_d=arr[1], dst_d=arr[2], lens_d=arr[3])
+            self.passes[s] = dict(p, seqs_d=arr[0], src_d=arr[1], dst_d=arr[2], lens_d=arr[3],
+                                  seqs_l=arr[0].long())
         self.prompt_len = torch.tensor(self.t0, dtype=torch.int32, device=dev)
         self.seq_ids = torch.arange(nb, dtype=torch.int32, device=dev)
         nql = 1 if mode != "grouped" else max(len(g) for g in self.groups)
@@ -354,8 +355,8 @@ class RaggedDecoder:
         w = self.ev["w"]
         windows = []
         for leader in self.leaders:
-            q_obs = qpool[leader, s - w + 1:s + 1].index_select(1, p["seqs_d"].long())
-            lse = (lsepool[leader, s - w + 1:s + 1].index_select(1, p["seqs_d"].long())
+            q_obs = qpool[leader, s - w + 1:s + 1].index_select(1, p["seqs_l"])
+            lse = (lsepool[leader, s - w + 1:s + 1].index_select(1, p["seqs_l"])
                    if p["fresh"] else None)
             windows.append((q_obs, lse))
         src = self.cache.seqs(p["src_d"], p["lens_d"], t_len=p["t_len"])
@@ -388,7 +389,10 @@ class RaggedDecoder:
                                         dtype=torch.uint8, device=dev),
                      score_ws=torch.zeros(16, dtype=torch.uint8, device=dev))
             self._ebufs = b
-        need = K.kvc_score_ws_bytes(src, self.hq, e["w"])
+        key = (n, src.t_cap)
+        need = b.get(key)
+        if need is None:
+            need = b[key] = K.kvc_score_ws_bytes(src, self.hq, e["w"])
         if b["score_ws"].numel() < need:
             b["score_ws"] = torch.zeros(need, dtype=torch.uint8, device=dev)
         return b

@@ -279,3 +279,58 @@ def test_dkv_validation_and_sizes():
     assert L.kvc_gaussian_bf16((1 << 32) + 1, 0, 0, 0, FAKE, None) == kvc.KVC_EINVAL
     assert L.kvc_gaussian_bf16(4, 0, 0, 0, FAKE + 2, None) == kvc.KVC_EALIGN
     assert L.kvc_gaussian_bf16(0, 0, 0, 0, FAKE, None) == kvc.KVC_OK
+
+
+def ragged_cache(nb_cap=0, batch_idx=None, seq_len=None, **kw):
+    c = cache(**kw)
+    c.nb_cap = nb_cap
+    c.batch_idx = batch_idx
+    c.seq_len = seq_len
+    return c
+
+
+def test_ragged_cache_validation():
+    rng = lambda c: L.kvc_value_range(ctypes.byref(c), 0, FAKE, None)
+    # without a map, sequence b is entry b: nb <= nb_cap
+    assert rng(ragged_cache(nb=3, nb_cap=2)) == kvc.KVC_EINVAL
+    assert rng(ragged_cache(nb_cap=-1)) == kvc.KVC_EINVAL
+    # with a map any entry count is addressable (t_len 0: validated, nothing launched)
+    assert rng(ragged_cache(nb=3, nb_cap=2, batch_idx=FAKE, t_len=0)) == kvc.KVC_OK
+    assert rng(ragged_cache(nb=3, nb_cap=3, seq_len=FAKE, t_len=0)) == kvc.KVC_OK
+    assert rng(ragged_cache(batch_idx=FAKE + 2)) == kvc.KVC_EALIGN
+    assert rng(ragged_cache(seq_len=FAKE + 1)) == kvc.KVC_EALIGN
+    assert attn(ragged_cache(seq_len=FAKE + 2)) == kvc.KVC_EALIGN
+
+
+def test_select_seq_validation():
+    f = lambda **kw: L.kvc_select_seq(FAKE, FAKE, 1, 2, kw.get("T", 100), kw.get("sl", None),
+                                      kw.get("sid", None), 50, 8, 4, 1, 0, FAKE, FAKE, 1 << 30,
+                                      None)
+    assert f(sl=FAKE + 2) == kvc.KVC_EALIGN
+    assert f(sid=FAKE + 1) == kvc.KVC_EALIGN
+    assert f(T=0, sl=FAKE) == kvc.KVC_OK
+
+
+def test_q8_quantize_rejects_ragged_sources():
+    from decode_attention_kvc_amd._lib import kvc_qcache
+    q = kvc_qcache(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 1, 2, 128, 100, 128, 0, 64)
+    for c in (ragged_cache(seq_len=FAKE), ragged_cache(batch_idx=FAKE, nb_cap=1),
+              ragged_cache(nb_cap=2)):
+        assert L.kvc_q8_quantize(ctypes.byref(c), 0, None, 0, ctypes.byref(q), None) == \
+            kvc.KVC_EINVAL
+
+
+def test_cache_seqs_view():
+    import torch
+    c = kvc.Cache.empty(2, 5, 2, 64, device="cpu", t_len=10)
+    idx = torch.tensor([4, 1, 3], dtype=torch.int32)
+    ln = torch.tensor([7, 0, 10], dtype=torch.int32)
+    v = c.seqs(idx, ln)
+    assert (v.nb, v.nb_cap, c.nb, v.t_len) == (3, 5, 5, 10)
+    d = v.desc()
+    assert (d.nb, d.nb_cap, d.batch_idx, d.seq_len) == (3, 5, idx.data_ptr(), ln.data_ptr())
+    assert c.desc().batch_idx is None and c.desc().nb_cap == 5
+    with pytest.raises(ValueError):
+        c.seqs(idx.long())
+    with pytest.raises(ValueError):
+        c.seqs(idx, ln[:2])
