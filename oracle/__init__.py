@@ -25,11 +25,16 @@ Parity status of each function (what pins it is in tests/test_oracle_*.py):
   ragged.*        pinned (short-window scores by brute force and row sums,
                   reduction to the uniform trajectory and to a batch of one,
                   sequence independence, the length schedule)
+  xkv.*           pinned (the page's storage formula, exact reconstruction at
+                  full rank and for shared cross-layer structure, a closed
+                  rank-1 case, optimality against other subspaces, landmarks
+                  and chunk scores by brute force, the selection rule, the
+                  exact merge of two attention parts)
 End-to-end model quality (does the eviction keep accuracy?) is parity
 unpinned: it needs trained weights and datasets that are not available.
 """
 from .philox import philox4, philox4x32_10, seed_key, mulhilo
-from . import dkv, quant, ragged
+from . import dkv, quant, ragged, xkv
 from .kvc_oracle import (
     share_map, append_row, attention, decode_attention, value_range,
     window_score, philox_word0, exp_variate, select, select_detail, compact,
@@ -40,5 +45,5 @@ __all__ = [
     "philox4", "philox4x32_10", "seed_key", "mulhilo", "share_map",
     "append_row", "attention", "decode_attention", "value_range",
     "window_score", "philox_word0", "exp_variate", "select", "select_detail",
-    "compact", "eviction_due", "run_decode", "dkv", "quant", "ragged",
+    "compact", "eviction_due", "run_decode", "dkv", "quant", "ragged", "xkv",
 ]
