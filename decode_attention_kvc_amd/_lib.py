@@ -29,7 +29,7 @@ EXPORTS = (
     "kvc_score_ws_bytes", "kvc_score", "kvc_select_ws_bytes", "kvc_select", "kvc_select_seq",
     "kvc_compact", "kvc_philox_words", "kvc_dkv_ws_bytes", "kvc_dkv_score",
     "kvc_gaussian_bf16", "kvc_q8_quantize", "kvc_q8_append", "kvc_q8_decode_attn_ws_bytes",
-    "kvc_q8_decode_attn",
+    "kvc_q8_decode_attn", "kvc_xkv_factor_ws_bytes", "kvc_xkv_factor", "kvc_xkv_decode_attn",
 )
 
 
@@ -57,6 +57,14 @@ class kvc_qcache(ctypes.Structure):
                 ("p_len", ctypes.c_int32), ("p_cap", ctypes.c_int32)]
 
 
+class kvc_xkv(ctypes.Structure):
+    _fields_ = [("ak", ctypes.c_void_p), ("av", ctypes.c_void_p), ("lk", ctypes.c_void_p),
+                ("bk", ctypes.c_void_p), ("bv", ctypes.c_void_p), ("nb", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("rank", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("t_len", ctypes.c_int32), ("t_cap", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -72,6 +80,7 @@ def lib():
                                  ctypes.c_size_t, ctypes.c_float)
         cp = ctypes.POINTER(kvc_cache)
         qp = ctypes.POINTER(kvc_qcache)
+        xp = ctypes.POINTER(kvc_xkv)
         ip = ctypes.POINTER(ctypes.c_int32)
         szp = ctypes.POINTER(ctypes.c_size_t)
         sig = {
@@ -102,6 +111,9 @@ def lib():
             "kvc_q8_decode_attn_ws_bytes": ([qp, i32, i32, szp], i32),
             "kvc_q8_decode_attn": ([qp, vp, i64, i32, ip, i32, f32, vp, i64, vp, i64, vp, sz,
                                     vp], i32),
+            "kvc_xkv_factor_ws_bytes": ([xp, szp], i32),
+            "kvc_xkv_factor": ([cp, i32, i32, ctypes.c_uint64, xp, vp, sz, vp], i32),
+            "kvc_xkv_decode_attn": ([xp, i32, vp, i32, f32, i32, vp, vp, vp, vp, vp, vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -309,6 +321,61 @@ class QCache:
         return 2 * HEAD_DIM + 2 * 4
 
 
+@dataclass
+class XkvStore:
+    """One window's cross-layer factorisation in libkvc's layout (see
+    include/kvc.h): token bases ak, av (bf16 [nb][hkv][t_cap][rank]), key
+    landmarks lk (bf16 [nb][hkv][t_cap/8][rank]) and the per-layer matrices,
+    stored transposed in bk, bv (float32 [nb][hkv][window*128][rank])."""
+    ak: torch.Tensor
+    av: torch.Tensor
+    lk: torch.Tensor
+    bk: torch.Tensor
+    bv: torch.Tensor
+    window: int
+    t_len: int
+
+    CHUNK = 8
+
+    @staticmethod
+    def empty(nb, n_kv_heads, window, rank, t_cap, device="cuda", t_len=0):
+        t_cap = int(math.ceil(max(t_cap, 1) / T_ALIGN) * T_ALIGN)
+        bf = dict(dtype=torch.bfloat16, device=device)
+        ak = torch.empty((nb, n_kv_heads, t_cap, rank), **bf)
+        av = torch.empty_like(ak)
+        lk = torch.empty((nb, n_kv_heads, t_cap // XkvStore.CHUNK, rank), **bf)
+        bk = torch.empty((nb, n_kv_heads, window * HEAD_DIM, rank), dtype=torch.float32,
+                         device=device)
+        bv = torch.empty_like(bk)
+        return XkvStore(ak, av, lk, bk, bv, window, t_len)
+
+    @property
+    def nb(self):
+        return self.ak.shape[0]
+
+    @property
+    def n_kv_heads(self):
+        return self.ak.shape[1]
+
+    @property
+    def t_cap(self):
+        return self.ak.shape[2]
+
+    @property
+    def rank(self):
+        return self.ak.shape[3]
+
+    def desc(self):
+        return kvc_xkv(self.ak.data_ptr(), self.av.data_ptr(), self.lk.data_ptr(),
+                       self.bk.data_ptr(), self.bv.data_ptr(), self.nb, self.n_kv_heads,
+                       HEAD_DIM, self.window, self.rank, self.CHUNK, int(self.t_len), self.t_cap)
+
+    def nbytes(self):
+        """Bytes the window's factorisation occupies (bases, matrices, landmarks)."""
+        return sum(t.numel() * t.element_size() for t in (self.ak, self.av, self.lk, self.bk,
+                                                           self.bv))
+
+
 # ---------------------------------------------------------------------------
 # exports
 # ---------------------------------------------------------------------------
@@ -474,3 +541,33 @@ def kvc_q8_decode_attn(cache, q, q_slot, out, lse, ws, n_q_heads=None, scale=0.0
                                     float(scale), _ptr(out), out_layer_stride, _ptr(lse),
                                     lse_layer_stride, _ptr(ws), ws_bytes, _stream(stream)),
            "kvc_q8_decode_attn")
+
+
+def kvc_xkv_factor_ws_bytes(store):
+    x = store.desc()
+    out = ctypes.c_size_t()
+    _check(lib().kvc_xkv_factor_ws_bytes(ctypes.byref(x), ctypes.byref(out)),
+           "kvc_xkv_factor_ws_bytes")
+    return out.value
+
+
+def kvc_xkv_factor(cache, slot0, store, ws, iters=12, seed=0, stream=None):
+    """Factorise slots [slot0, slot0 + store.window) of `cache` into `store`
+    (sets store.t_len = cache.t_len first)."""
+    store.t_len = cache.t_len
+    c, x = cache.desc(), store.desc()
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().kvc_xkv_factor(ctypes.byref(c), slot0, iters, int(seed) & (2**64 - 1),
+                                ctypes.byref(x), _ptr(ws), ws_bytes, _stream(stream)),
+           "kvc_xkv_factor")
+
+
+def kvc_xkv_decode_attn(store, layer, q, out, lse=None, n_select=256, scale=0.0, o_in=None,
+                        lse_in=None, selected=None, n_q_heads=None, stream=None):
+    """q: bf16 [nb][Hq][d]; out float32 like q (o_in / lse_in: a second part
+    to merge, e.g. attention over rows appended after the factorisation)."""
+    x = store.desc()
+    hq = q.shape[-2] if n_q_heads is None else n_q_heads
+    _check(lib().kvc_xkv_decode_attn(ctypes.byref(x), layer, _ptr(q), hq, float(scale), n_select,
+                                     _ptr(o_in), _ptr(lse_in), _ptr(out), _ptr(lse),
+                                     _ptr(selected), _stream(stream)), "kvc_xkv_decode_attn")

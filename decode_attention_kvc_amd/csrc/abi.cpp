@@ -268,6 +268,48 @@ DkvWs dkv_layout(int rank, int t_len, int slabs) {
     return w;
 }
 
+// ---- cross-layer factorisation ---------------------------------------------
+constexpr int XKV_MAXG = 8;          // query heads per KV head on the decode path
+constexpr int XKV_CHUNK = 8;
+constexpr size_t XKV_LDS_LIMIT = LDS_PER_CU - 4096;   // dynamic LDS of one decode workgroup
+
+int check_xkv(const kvc_xkv* x) {
+    if (!x) return KVC_EALIGN;
+    if (x->head_dim != KVC_HEAD_DIM) return KVC_EINVAL;
+    if (x->nb < 0 || x->n_kv_heads < 1) return KVC_EINVAL;
+    if (x->window < 1 || x->window > 4) return KVC_EINVAL;
+    if (x->rank != 32 && x->rank != 64) return KVC_EINVAL;
+    if (x->chunk != XKV_CHUNK) return KVC_EINVAL;
+    if (x->t_cap < 0 || x->t_cap % KVC_T_ALIGN || x->t_len < 0 || x->t_len > x->t_cap)
+        return KVC_EINVAL;
+    if (!aligned16(x->ak) || !aligned16(x->av) || !aligned16(x->lk) || !aligned16(x->bk) ||
+        !aligned16(x->bv))
+        return KVC_EALIGN;
+    return KVC_OK;
+}
+
+struct XkvWs {
+    size_t gram_off, vt_off, total;
+};
+
+XkvWs xkv_ws(const kvc_xkv* x) {
+    const size_t n = (size_t)x->window * KVC_HEAD_DIM;
+    const size_t probs = 2 * (size_t)x->nb * x->n_kv_heads;
+    XkvWs w;
+    w.gram_off = 0;
+    w.vt_off = align_up(probs * n * n * sizeof(float), 256);
+    w.total = w.vt_off + probs * x->rank * n * sizeof(uint16_t);
+    return w;
+}
+
+size_t xkv_decode_lds(const kvc_xkv* x, int g, int n_select) {
+    const size_t nch = ((size_t)x->t_len + XKV_CHUNK - 1) / XKV_CHUNK;
+    const size_t ksel = std::min<size_t>((size_t)n_select, nch);
+    const size_t rg = 256 / x->rank;
+    return (XKV_MAXG * (size_t)x->rank + nch + ksel + ksel * XKV_CHUNK * g +
+            rg * XKV_MAXG * x->rank) * 4;
+}
+
 }  // namespace
 
 extern "C" {
@@ -784,6 +826,109 @@ int kvc_dkv_score(const kvc_cache* c, int slot, const void* g, int rank, float* 
     p.w = reinterpret_cast<float*>(base + lay.w_off);
     p.sm = seq_map(c);
     if (launch_dkv(p, (hipStream_t)stream) != hipSuccess) return KVC_EHIP;
+    return hip_status();
+}
+
+int kvc_xkv_factor_ws_bytes(const kvc_xkv* x, size_t* bytes) {
+    int st = check_xkv(x);
+    if (st) return st;
+    if (!bytes) return KVC_EALIGN;
+    *bytes = xkv_ws(x).total;
+    return KVC_OK;
+}
+
+int kvc_xkv_factor(const kvc_cache* c, int slot0, int iters, uint64_t seed, const kvc_xkv* x,
+                   void* ws, size_t ws_bytes, kvc_stream_t stream) {
+    int st = check_cache(c);
+    if (st) return st;
+    st = check_xkv(x);
+    if (st) return st;
+    if (c->dtype != KVC_BF16) return KVC_EDTYPE;
+    if (is_ragged(c) || nb_cap_of(c) != c->nb) return KVC_EINVAL;   // uniform batches only
+    if (slot0 < 0 || slot0 + x->window > c->n_slots) return KVC_EINVAL;
+    if (x->nb != c->nb || x->n_kv_heads != c->n_kv_heads) return KVC_EINVAL;
+    if (x->t_len != c->t_len) return KVC_EINVAL;
+    if (iters < 1 || iters > 64) return KVC_EINVAL;
+    if (c->nb == 0 || c->t_len == 0) return KVC_OK;
+    const XkvWs lay = xkv_ws(x);
+    if (!ws || ws_bytes < lay.total || !aligned16(ws)) return KVC_EWORKSPACE;
+    XkvLaunch p;
+    memset(&p, 0, sizeof(p));
+    p.k = slot_k(c, slot0);
+    p.v = slot_v(c, slot0);
+    p.slot_stride = slot_elems(c);
+    p.nb = c->nb;
+    p.hkv = c->n_kv_heads;
+    p.t_len = c->t_len;
+    p.t_cap = c->t_cap;
+    p.window = x->window;
+    p.rank = x->rank;
+    char* base = static_cast<char*>(ws);
+    p.gram = reinterpret_cast<float*>(base + lay.gram_off);
+    p.vt = reinterpret_cast<uint16_t*>(base + lay.vt_off);
+    p.ak = x->ak;
+    p.av = x->av;
+    p.lk = x->lk;
+    p.bk = x->bk;
+    p.bv = x->bv;
+    p.x_tcap = x->t_cap;
+    p.iters = iters;
+    p.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
+    p.seed_hi = (uint32_t)(seed >> 32);
+    // projection: about two workgroups per CU, at least four tiles per wave
+    const int ntiles = (c->t_len + 31) / 32;
+    const long long work = (long long)ntiles * c->nb * c->n_kv_heads;
+    p.tps = (int)std::max<long long>(16, (work + 2 * CU_COUNT - 1) / (2 * CU_COUNT));
+    p.nsplit = (ntiles + p.tps - 1) / p.tps;
+    if (launch_xkv_factor(p, (hipStream_t)stream) != hipSuccess) return KVC_EHIP;
+    return hip_status();
+}
+
+int kvc_xkv_decode_attn(const kvc_xkv* x, int layer, const void* q, int n_q_heads, float scale,
+                        int n_select, const float* o_in, const float* lse_in, float* out,
+                        float* lse, int32_t* selected, kvc_stream_t stream) {
+    int st = check_xkv(x);
+    if (st) return st;
+    if (layer < 0 || layer >= x->window) return KVC_EINVAL;
+    if (n_q_heads < 1 || n_q_heads % x->n_kv_heads) return KVC_EINVAL;
+    const int g = n_q_heads / x->n_kv_heads;
+    if (g > XKV_MAXG) return KVC_EINVAL;
+    if (n_select < 1 || (long long)n_select * XKV_CHUNK * g > 16384) return KVC_EINVAL;
+    if (!isfinite(scale) || scale < 0.f) return KVC_EINVAL;
+    if ((o_in == nullptr) != (lse_in == nullptr)) return KVC_EINVAL;
+    if (x->nb == 0) return KVC_OK;
+    if (!aligned16(q) || !aligned4(out)) return KVC_EALIGN;
+    if ((lse && !aligned4(lse)) || (o_in && (!aligned4(o_in) || !aligned4(lse_in))) ||
+        (selected && !aligned4(selected)))
+        return KVC_EALIGN;
+    const size_t lds = xkv_decode_lds(x, g, n_select);
+    if (lds > XKV_LDS_LIMIT) return KVC_EINVAL;
+    if (scale == 0.f) scale = 1.0f / sqrtf((float)KVC_HEAD_DIM);
+    XkvDecodeLaunch p;
+    memset(&p, 0, sizeof(p));
+    p.ak = x->ak;
+    p.av = x->av;
+    p.lk = x->lk;
+    p.bk = x->bk;
+    p.bv = x->bv;
+    p.nb = x->nb;
+    p.hkv = x->n_kv_heads;
+    p.g = g;
+    p.hq = n_q_heads;
+    p.t_len = x->t_len;
+    p.x_tcap = x->t_cap;
+    p.window = x->window;
+    p.rank = x->rank;
+    p.layer = layer;
+    p.n_select = n_select;
+    p.q = q;
+    p.scale = scale;
+    p.o_in = o_in;
+    p.lse_in = lse_in;
+    p.out = out;
+    p.lse = lse;
+    p.selected = selected;
+    if (launch_xkv_decode(p, lds, (hipStream_t)stream) != hipSuccess) return KVC_EHIP;
     return hip_status();
 }
 

@@ -163,6 +163,42 @@ struct CompactLaunch {
     SeqMap src_sm, dst_sm;  // src_sm.len gives the source rows
 };
 
+// Cross-layer factorisation of one window of W slots (bf16, uniform batch).
+struct XkvLaunch {
+    const void* k;          // K of the window's first slot
+    const void* v;          // V of the window's first slot
+    size_t slot_stride;     // elements from one slot to the next
+    int nb, hkv, t_len, t_cap, window, rank;
+    float* gram;            // workspace [2][nb][hkv][n][n], n = window * D (keys, then values)
+    uint16_t* vt;           // workspace [2][nb][hkv][rank][n]: bf16 transpose of the bases
+    void* ak;               // bf16 [nb][hkv][x_tcap][rank]
+    void* av;
+    void* lk;               // bf16 [nb][hkv][x_tcap / 8][rank]
+    float* bk;              // [nb][hkv][n][rank]
+    float* bv;
+    int x_tcap;
+    int iters;
+    uint32_t seed_lo, seed_hi;
+    int nsplit, tps;        // projection: splits per slab, 32-row tiles per split
+};
+
+// Selective-reconstruction decode attention for one layer of a window.
+struct XkvDecodeLaunch {
+    const void* ak;
+    const void* av;
+    const void* lk;
+    const float* bk;
+    const float* bv;
+    int nb, hkv, g, hq, t_len, x_tcap, window, rank, layer, n_select;
+    const void* q;          // bf16 [nb][hq][D]
+    float scale;
+    const float* o_in;      // float32 [nb][hq][D] or null: a second part to merge
+    const float* lse_in;
+    float* out;
+    float* lse;             // may be null
+    int32_t* selected;      // [nb][hkv][n_select] or null
+};
+
 // Host-side launchers (defined next to their kernels).  Each returns
 // hipSuccess or the launch error.
 // Launches the partial kernel and the merge kernel.
@@ -181,6 +217,8 @@ hipError_t launch_dkv(const DkvLaunch& p, hipStream_t s);
 hipError_t launch_gaussian(int64_t n, uint32_t c1, uint32_t c2, uint32_t k0, uint32_t k1,
                            void* out, hipStream_t s);
 hipError_t launch_compact(const CompactLaunch& p, hipStream_t s);
+hipError_t launch_xkv_factor(const XkvLaunch& p, hipStream_t s);
+hipError_t launch_xkv_decode(const XkvDecodeLaunch& p, size_t lds, hipStream_t s);
 hipError_t launch_philox(int64_t n, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
                          uint32_t k1, uint32_t* out, hipStream_t s);
 

@@ -22,6 +22,7 @@
 #include "common.h"
 #include "kvc_internal.h"
 #include "philox.h"
+#include "radix.h"
 
 namespace kvc {
 
@@ -32,80 +33,7 @@ constexpr int NWV = NT / WAVE;
 constexpr uint32_t EXCLUDED = 0xFFFFFFFFu;   // above every float key
 constexpr int LDS_KEYS = 36 * 1024;           // 144 KB of keys
 
-struct SelectSmem {
-    uint32_t hist[256];
-    uint32_t wave_tot[NWV];
-    uint32_t bcast[4];
-};
-
-// Exclusive prefix count of `flag` over the block in thread order; returns
-// this thread's offset and writes the block total to *total.
-__device__ __forceinline__ uint32_t block_scan_flag(bool flag, SelectSmem& sm, uint32_t* total) {
-    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
-    const unsigned long long bal = __ballot(flag);
-    const uint32_t before = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) sm.wave_tot[wave] = __popcll(bal);
-    __syncthreads();
-    uint32_t off = 0, tot = 0;
-    for (int w = 0; w < NWV; ++w) {
-        const uint32_t c = sm.wave_tot[w];
-        off += (w < wave) ? c : 0u;
-        tot += c;
-    }
-    __syncthreads();
-    *total = tot;
-    return off + before;
-}
-
-// k-th smallest (1-based) of key(t), t < n.  Returns the key; *take gets how
-// many rows equal to it belong to the k smallest (lowest rows first).
-template <typename KeyFn>
-__device__ uint32_t radix_select(int n, uint32_t k, KeyFn key, SelectSmem& sm, uint32_t* take) {
-    const int tid = threadIdx.x;
-    uint32_t prefix = 0, mask = 0;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = tid; i < 256; i += NT) sm.hist[i] = 0;
-        __syncthreads();
-        for (int t = tid; t < n; t += NT) {
-            const uint32_t u = key(t);
-            if ((u & mask) == prefix) atomicAdd(&sm.hist[(u >> shift) & 255u], 1u);
-        }
-        __syncthreads();
-        if (tid < WAVE) {
-            // lane owns bins 4*lane .. 4*lane+3
-            uint32_t c[4], s = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                c[e] = sm.hist[4 * tid + e];
-                s += c[e];
-            }
-            // inclusive scan of s across the wave
-            uint32_t incl = s;
-#pragma unroll
-            for (int o = 1; o < WAVE; o <<= 1) {
-                const uint32_t y = __shfl_up(incl, o);
-                if (tid >= o) incl += y;
-            }
-            uint32_t run = incl - s;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (run < k && k <= run + c[e]) {
-                    sm.bcast[0] = 4 * tid + e;
-                    sm.bcast[1] = run;
-                }
-                run += c[e];
-            }
-        }
-        __syncthreads();
-        const uint32_t bin = sm.bcast[0], below = sm.bcast[1];
-        __syncthreads();
-        k -= below;
-        prefix |= bin << shift;
-        mask |= 255u << shift;
-    }
-    *take = k;
-    return prefix;
-}
+using SelectSmem = RadixSmem<NT>;
 
 __device__ __forceinline__ uint32_t range_key(float r) {
     // larger range first: invert the (non-negative) float's bits
@@ -154,7 +82,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectLaunch p) {
     if (p.n_v > 0) {
         for (int t = tid; t < ncand; t += NT) keys[t] = range_key(range[t]);
         __syncthreads();
-        rthr = radix_select(ncand, (uint32_t)p.n_v, [&](int t) { return keys[t]; }, sm, &rtake);
+        rthr = radix_select<NT>(ncand, (uint32_t)p.n_v, [&](int t) { return keys[t]; }, sm, &rtake);
     }
 
     // 2. Sampling keys for the remaining candidates, written over the range
@@ -167,7 +95,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectLaunch p) {
         const uint32_t rk = (valid && p.n_v > 0) ? keys[t] : 0xFFFFFFFFu;
         const bool eq = valid && p.n_v > 0 && rk == rthr;
         uint32_t tot;
-        const uint32_t rank = eq_seen + block_scan_flag(eq, sm, &tot);
+        const uint32_t rank = eq_seen + block_scan_flag<NT>(eq, sm, &tot);
         eq_seen += tot;
         if (valid) {
             const bool prot = p.n_v > 0 && (rk < rthr || (eq && rank < rtake));
@@ -179,7 +107,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectLaunch p) {
     // 3. K - N_v smallest sampling keys.
     const uint32_t ns = (uint32_t)(p.budget_k - p.n_v);
     uint32_t kthr = 0, ktake = 0;
-    if (ns > 0) kthr = radix_select(
+    if (ns > 0) kthr = radix_select<NT>(
         ncand, ns, [&](int t) { return keys[t]; }, sm, &ktake);
 
     // 4. Emit kept rows in ascending order.
@@ -199,10 +127,10 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectLaunch p) {
             }
         }
         uint32_t tot;
-        const uint32_t rank = keq_seen + block_scan_flag(eq, sm, &tot);
+        const uint32_t rank = keq_seen + block_scan_flag<NT>(eq, sm, &tot);
         keq_seen += tot;
         if (eq && rank < ktake) keep = true;
-        const uint32_t pos = written + block_scan_flag(keep, sm, &tot);
+        const uint32_t pos = written + block_scan_flag<NT>(keep, sm, &tot);
         written += tot;
         if (keep && pos < (uint32_t)n_keep) kept[pos] = t;
     }

@@ -1,0 +1,622 @@
+// Cross-layer factorisation and selective reconstruction (xKV).
+//
+// xKV summary (gist.science 2503.18893), §2.2: the caches of W consecutive
+// layers are concatenated side by side and a rank-r SVD gives one token basis
+// A shared by the window and one reconstruction matrix B_l per layer; §2.3:
+// at decode only the rows of the chunks whose landmarks score best against
+// the query are rebuilt from A and B_l and attended.
+//
+// Factorisation, per (keys or values, batch entry b, KV head j), of
+// X = [X_1 | ... | X_W] (T x n, n = W * 128):
+//  1. xkv_gram: G = X^T X on v_mfma_f32_16x16x32_bf16, one workgroup per
+//     pair of layers (I <= J) streaming the rows once; each 32-row tile of
+//     both layers is staged in LDS channel-major (key rows are transposed on
+//     the way in, value tiles already are), so both operands are 16-byte
+//     reads.  Rows past t_len are staged as zeros.
+//  2. xkv_subspace: one workgroup per problem runs `iters` steps of subspace
+//     iteration on G from a Gaussian start (Box-Muller on Philox words):
+//     Z = G V on v_mfma_f32_16x16x4f32 (the A operand is read along G's rows,
+//     which G's symmetry allows), then modified Gram-Schmidt in LDS (twice
+//     after the last step).  V (n x r, orthonormal columns) converges to the
+//     top-r right singular subspace of X; X V V^T is the rank-r truncation,
+//     A = X V and B_l = (rows l*128 .. l*128+127 of V)^T.
+//  3. xkv_project: A = X V on MFMA with V^T as bf16 in LDS, stored as bf16,
+//     and for keys the landmark of every 8-row chunk: the mean of its stored
+//     A rows.
+// Decode (xkv_decode), one workgroup per (b, j):
+//  q~_h = B_l q_h (r numbers per head); chunk score max_h q~_h . landmark;
+//  exact top-k of the chunks (radix select, ties to the lower chunk); then
+//  attention over the kept rows in the rank space: q_h . (A_t B_l) =
+//  q~_h . A_t and sum_t p_t A_t B_l = (sum_t p_t A_t) B_l, so the selected
+//  rows are rebuilt implicitly and never written.  An optional second part
+//  (rows appended after the factorisation, attended separately) is merged
+//  with log-sum-exp weights.
+#include "common.h"
+#include "kvc_internal.h"
+#include "philox.h"
+#include "radix.h"
+
+namespace kvc {
+
+namespace {
+
+constexpr int XT = 32;          // rows per tile
+constexpr int GP = 40;          // bf16 per staged channel row of a tile (80 bytes)
+constexpr int CHUNK = 8;        // rows per landmark chunk
+constexpr int VPITCH = XT + 2;  // bf16 per channel in a wave's value transpose buffer
+constexpr int MAXG = 8;         // query heads per KV head on the decode path
+
+__device__ __forceinline__ bf16x8 as_bf(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+// ---------------------------------------------------------------------------
+// 1. Gram matrix
+// ---------------------------------------------------------------------------
+template <bool IS_V>
+__global__ __launch_bounds__(256) void xkv_gram(XkvLaunch p) {
+    __shared__ __align__(16) uint16_t st[2][D * GP];
+    const int j = blockIdx.y, b = blockIdx.z;
+    int I = 0, J = 0;
+    {
+        int q = blockIdx.x;
+        for (int a = 0; a < p.window; ++a) {
+            if (q < p.window - a) {
+                I = a;
+                J = a + q;
+                break;
+            }
+            q -= p.window - a;
+        }
+    }
+    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const size_t cs = ((size_t)b * p.hkv + j) * p.t_cap * D;
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(IS_V ? p.v : p.k);
+    const uint16_t* xI = src + (size_t)I * p.slot_stride + cs;
+    const uint16_t* xJ = src + (size_t)J * p.slot_stride + cs;
+    const int T = p.t_len, n = p.window * D;
+    const int nside = (I == J) ? 1 : 2;
+
+    f32x4 acc[2][8];
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int jb = 0; jb < 8; ++jb) acc[ib][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int ntiles = (T + XT - 1) / XT;
+    for (int tile = 0; tile < ntiles; ++tile) {
+        const int t0 = tile * XT;
+        for (int side = 0; side < nside; ++side) {
+            const uint16_t* x = side ? xJ : xI;
+            uint16_t* dst = st[side];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {          // 512 16-byte pieces of the 8 KB tile
+                const int c = tid + 256 * u;
+                if constexpr (IS_V) {
+                    const int ch = c >> 2, q4 = c & 3;    // channel, 8-row group
+                    u32x4 v = load_stream16(x + vt_off(t0, ch) + 8 * q4);
+                    if (t0 + 8 * q4 + 8 > T) {
+                        u16x8 e = __builtin_bit_cast(u16x8, v);
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) e[k] = (t0 + 8 * q4 + k < T) ? e[k] : (uint16_t)0;
+                        v = __builtin_bit_cast(u32x4, e);
+                    }
+                    *reinterpret_cast<u32x4*>(dst + ch * GP + 8 * q4) = v;
+                } else {
+                    const int r = c >> 4, c8 = (c & 15) * 8;   // row, first channel
+                    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+                    if (t0 + r < T) v = load_stream16(x + (size_t)(t0 + r) * D + c8);
+                    const u16x8 e = __builtin_bit_cast(u16x8, v);
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) dst[(c8 + k) * GP + r] = e[k];
+                }
+            }
+        }
+        __syncthreads();
+        const uint16_t* sI = st[0];
+        const uint16_t* sJ = st[nside - 1];
+        bf16x8 a[2], bb[8];
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+            a[ib] = as_bf(*reinterpret_cast<const u32x4*>(sI + (32 * wave + 16 * ib + l16) * GP + 8 * lg));
+#pragma unroll
+        for (int jb = 0; jb < 8; ++jb)
+            bb[jb] = as_bf(*reinterpret_cast<const u32x4*>(sJ + (16 * jb + l16) * GP + 8 * lg));
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+            for (int jb = 0; jb < 8; ++jb)
+                acc[ib][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ib], bb[jb], acc[ib][jb], 0, 0, 0);
+        __syncthreads();
+    }
+    // acc[ib][jb][i]: G[I*128 + 32*wave + 16*ib + 4*lg + i][J*128 + 16*jb + l16]
+    float* G = p.gram + ((size_t)((IS_V ? p.nb : 0) + b) * p.hkv + j) * n * n;
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int jb = 0; jb < 8; ++jb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = I * D + 32 * wave + 16 * ib + 4 * lg + i;
+                const int col = J * D + 16 * jb + l16;
+                G[(size_t)row * n + col] = acc[ib][jb][i];
+                if (I != J) G[(size_t)col * n + row] = acc[ib][jb][i];
+            }
+}
+
+// ---------------------------------------------------------------------------
+// 2. Subspace iteration
+// ---------------------------------------------------------------------------
+// Modified Gram-Schmidt on the R columns of Z ([n][R + 1] floats in LDS), one
+// column at a time: normalise it (a column of norm 0 stays 0), then remove it
+// from the later columns (wave w takes columns j+1+w, j+5+w, ...).
+template <int R>
+__device__ void mgs(float* Z, int n, float* red) {
+    constexpr int RP = R + 1;
+    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+    for (int j = 0; j < R; ++j) {
+        float s = 0.f;
+        for (int i = tid; i < n; i += 256) {
+            const float z = Z[i * RP + j];
+            s = fmaf(z, z, s);
+        }
+        s = wave_sum(s);
+        if (lane == 0) red[wave] = s;
+        __syncthreads();
+        const float nrm2 = (red[0] + red[1]) + (red[2] + red[3]);
+        const float inv = nrm2 > 1e-30f ? 1.0f / sqrtf(nrm2) : 0.f;
+        for (int i = tid; i < n; i += 256) Z[i * RP + j] *= inv;
+        __syncthreads();
+        for (int k = j + 1 + wave; k < R; k += 4) {
+            float d = 0.f;
+            for (int i = lane; i < n; i += WAVE) d = fmaf(Z[i * RP + j], Z[i * RP + k], d);
+            d = wave_sum(d);
+            for (int i = lane; i < n; i += WAVE) Z[i * RP + k] = fmaf(-d, Z[i * RP + j], Z[i * RP + k]);
+        }
+        __syncthreads();
+    }
+}
+
+template <int R>
+__global__ __launch_bounds__(256) void xkv_subspace(XkvLaunch p) {
+    extern __shared__ float Zs[];          // [n][R + 1]
+    __shared__ float red[4];
+    constexpr int RP = R + 1;
+    constexpr int CB = R / 16;
+    const int prob = blockIdx.x;           // (keys, values) x nb x hkv
+    const int n = p.window * D;
+    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const float* G = p.gram + (size_t)prob * n * n;
+
+    // Gaussian start: element x from words 0, 1 of Philox4x32-10 at counter
+    // (x, problem, 0x786b76, 0) under the caller's seed.
+    for (int x = tid; x < n * R; x += 256) {
+        const Philox4 w = philox4x32_10((uint32_t)x, (uint32_t)prob, 0x786b76u, 0u, p.seed_lo,
+                                        p.seed_hi);
+        const float u1 = ((float)w.x0 + 1.0f) * 2.3283064365386963e-10f;
+        const float u2 = (float)w.x1 * 2.3283064365386963e-10f;
+        Zs[(x / R) * RP + x % R] = sqrtf(-2.0f * logf(u1)) * cosf(6.283185307179586f * u2);
+    }
+    __syncthreads();
+    mgs<R>(Zs, n, red);
+
+    const int nib = n / 16;                // 16-row blocks of Z; wave w owns w, w+4, ...
+    for (int it = 0; it < p.iters; ++it) {
+        f32x4 acc[8][CB];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) acc[u][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < n; k0 += 4) {
+            float bv[CB];
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) bv[cb] = Zs[(k0 + lg) * RP + 16 * cb + l16];
+            const float* grow = G + (size_t)(k0 + lg) * n;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int ib = wave + 4 * u;
+                if (ib < nib) {
+                    const float a = grow[16 * ib + l16];     // G[16ib + l16][k0 + lg] by symmetry
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb)
+                        acc[u][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv[cb], acc[u][cb], 0, 0, 0);
+                }
+            }
+        }
+        __syncthreads();                   // every wave is done reading V
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int ib = wave + 4 * u;
+            if (ib < nib) {
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        Zs[(16 * ib + 4 * lg + i) * RP + 16 * cb + l16] = acc[u][cb][i];
+            }
+        }
+        __syncthreads();
+        mgs<R>(Zs, n, red);
+        if (it == p.iters - 1) mgs<R>(Zs, n, red);
+    }
+
+    const int slabs = p.nb * p.hkv;
+    const bool is_v = prob >= slabs;
+    float* out = (is_v ? p.bv : p.bk) + (size_t)(prob % slabs) * n * R;
+    uint16_t* vt = p.vt + (size_t)prob * R * n;
+    for (int x = tid; x < n * R; x += 256) {
+        const int i = x / R, c = x % R;
+        const float v = Zs[i * RP + c];
+        out[x] = v;
+        vt[(size_t)c * n + i] = f32_to_bf16(v);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 3. Projection A = X V and key landmarks
+// ---------------------------------------------------------------------------
+template <bool IS_V, int R>
+__global__ __launch_bounds__(256) void xkv_project(XkvLaunch p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int CB = R / 16;
+    const int n = p.window * D, vtp = n + 8;
+    uint16_t* vts = reinterpret_cast<uint16_t*>(smem);          // [R][vtp] bf16 V^T
+    uint16_t* tbuf = vts + R * vtp;                              // values: [4][D * VPITCH]
+    const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+    const int slab = b * p.hkv + j;
+    const int prob = (IS_V ? p.nb * p.hkv : 0) + slab;
+    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+    const int l16 = lane & 15, lg = lane >> 4;
+
+    const uint16_t* vt = p.vt + (size_t)prob * R * n;
+    for (int x = tid; x < R * (n / 8); x += 256) {
+        const int c = x / (n / 8), q = x % (n / 8);
+        *reinterpret_cast<u32x4*>(vts + c * vtp + 8 * q) = load16(vt + (size_t)c * n + 8 * q);
+    }
+    __syncthreads();
+
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(IS_V ? p.v : p.k) +
+                          ((size_t)b * p.hkv + j) * p.t_cap * D;
+    uint16_t* A = reinterpret_cast<uint16_t*>(IS_V ? p.av : p.ak) + (size_t)slab * p.x_tcap * R;
+    uint16_t* L = reinterpret_cast<uint16_t*>(p.lk) + (size_t)slab * (p.x_tcap / CHUNK) * R;
+    uint16_t* vb = tbuf + wave * D * VPITCH;
+    const int T = p.t_len;
+    const int ntiles = (T + XT - 1) / XT;
+    const int tile_begin = s * p.tps, tile_end = min(tile_begin + p.tps, ntiles);
+
+    for (int tile = tile_begin + wave; tile < tile_end; tile += 4) {
+        const int t0 = tile * XT;
+        f32x4 Y[2][CB];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) Y[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int l = 0; l < p.window; ++l) {
+            const uint16_t* x = src + (size_t)l * p.slot_stride;
+            // A operand: row t0 + 16*rb + l16, channels 32*kc + 8*lg .. +8
+            u32x4 xa[2][4];
+            if constexpr (!IS_V) {
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int kc = 0; kc < 4; ++kc)
+                        xa[rb][kc] = load_stream16(x + (size_t)(t0 + 16 * rb + l16) * D + 32 * kc + 8 * lg);
+            } else {
+                // the value tile is channel-major: through the wave's LDS
+                // buffer (one wave's LDS accesses execute in issue order)
+                u32x4 vtl[8];
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt)
+                    vtl[dt] = load_stream16(x + vt_off(t0, 16 * dt + l16) + 8 * lg);
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) {
+                    uint32_t* dst = reinterpret_cast<uint32_t*>(vb + (16 * dt + l16) * VPITCH + 8 * lg);
+#pragma unroll
+                    for (int w2 = 0; w2 < 4; ++w2) dst[w2] = vtl[dt][w2];
+                }
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int kc = 0; kc < 4; ++kc) {
+                        u16x8 e;
+#pragma unroll
+                        for (int jj = 0; jj < 8; ++jj)
+                            e[jj] = vb[(32 * kc + 8 * lg + jj) * VPITCH + 16 * rb + l16];
+                        xa[rb][kc] = __builtin_bit_cast(u32x4, e);
+                    }
+                __builtin_amdgcn_wave_barrier();
+            }
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int kc = 0; kc < 4; ++kc) {
+                    const bf16x8 gb = as_bf(*reinterpret_cast<const u32x4*>(
+                        vts + (16 * cb + l16) * vtp + l * D + 32 * kc + 8 * lg));
+#pragma unroll
+                    for (int rb = 0; rb < 2; ++rb)
+                        Y[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(xa[rb][kc]), gb,
+                                                                            Y[rb][cb], 0, 0, 0);
+                }
+        }
+        // Y[rb][cb][i]: row t0 + 16*rb + 4*lg + i, column 16*cb + l16.  Rows
+        // past t_len (arbitrary cache bits) become zeros and are not stored.
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                float sum = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = t0 + 16 * rb + 4 * lg + i;
+                    const uint16_t h = f32_to_bf16(t < T ? Y[rb][cb][i] : 0.f);
+                    if (t < T) A[(size_t)t * R + 16 * cb + l16] = h;
+                    sum += bf16_to_f32(h);
+                }
+                if constexpr (!IS_V) {
+                    // chunk 2*rb + (lg >> 1) of the tile: lanes lg = 2h, 2h+1
+                    sum += __shfl_xor(sum, 16);
+                    const int chunk = t0 / CHUNK + 2 * rb + (lg >> 1);
+                    const int cnt = min(CHUNK, T - chunk * CHUNK);
+                    if ((lg & 1) == 0 && cnt > 0)
+                        L[(size_t)chunk * R + 16 * cb + l16] = f32_to_bf16(sum / (float)cnt);
+                }
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 4. Selective-reconstruction decode attention
+// ---------------------------------------------------------------------------
+// Ascending key for descending score (order-preserving float bits, inverted).
+__device__ __forceinline__ uint32_t desc_key(float s) {
+    const uint32_t u = __float_as_uint(s);
+    const uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ~asc;
+}
+
+template <int R>
+__global__ __launch_bounds__(256) void xkv_decode(XkvDecodeLaunch p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ RadixSmem<256> rs;
+    __shared__ float red[4][MAXG];
+    __shared__ float hm[MAXG], hz[MAXG];
+    constexpr int RG = 256 / R;            // row groups of the value reduction
+    const int j = blockIdx.x, b = blockIdx.y;
+    const int slab = b * p.hkv + j, g = p.g, n = p.window * D;
+    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+    const int T = p.t_len, nch = (T + CHUNK - 1) / CHUNK;
+    const int ksel = min(p.n_select, nch), nrows = ksel * CHUNK;
+    float* qt = reinterpret_cast<float*>(smem);                  // [MAXG][R]
+    uint32_t* keys = reinterpret_cast<uint32_t*>(qt + MAXG * R); // [nch]
+    int32_t* sel = reinterpret_cast<int32_t*>(keys + nch);       // [ksel]
+    float* lgt = reinterpret_cast<float*>(sel + ksel);           // [nrows][g]
+    float* part = lgt + (size_t)nrows * g;                       // [RG][MAXG][R]
+
+    // q~_h = B_l q_h: B_l^T is rows layer*128 .. of the key basis [n][R]
+    const float* BK = p.bk + (size_t)slab * n * R + (size_t)p.layer * D * R;
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)b * p.hq + j * g) * D;
+    for (int x = tid; x < g * R; x += 256) {
+        const int h = x / R, c = x % R;
+        float a = 0.f;
+        for (int i = 0; i < D; ++i) a = fmaf(bf16_to_f32(q[h * D + i]), BK[i * R + c], a);
+        qt[h * R + c] = a;
+    }
+    __syncthreads();
+
+    // chunk scores: max over the heads of q~_h . landmark
+    const uint16_t* L = reinterpret_cast<const uint16_t*>(p.lk) + (size_t)slab * (p.x_tcap / CHUNK) * R;
+    for (int ch = tid; ch < nch; ch += 256) {
+        float lm[R];
+#pragma unroll
+        for (int c8 = 0; c8 < R / 8; ++c8) {
+            const u32x4 w = load16(L + (size_t)ch * R + 8 * c8);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                lm[8 * c8 + 2 * e] = bf16lo(w[e]);
+                lm[8 * c8 + 2 * e + 1] = bf16hi(w[e]);
+            }
+        }
+        float best = -INFINITY;
+        for (int h = 0; h < g; ++h) {
+            float s = 0.f;
+#pragma unroll
+            for (int c = 0; c < R; ++c) s = fmaf(qt[h * R + c], lm[c], s);
+            best = fmaxf(best, s);
+        }
+        keys[ch] = desc_key(best);
+    }
+    __syncthreads();
+
+    // the ksel best chunks, ascending (all of them when there are fewer)
+    if (ksel < nch) {
+        uint32_t take;
+        const uint32_t thr = radix_select<256>(nch, (uint32_t)ksel, [&](int t) { return keys[t]; },
+                                               rs, &take);
+        uint32_t written = 0, eq_seen = 0;
+        for (int base = 0; base < nch; base += 256) {
+            const int ch = base + tid;
+            const bool valid = ch < nch;
+            const uint32_t u = valid ? keys[ch] : 0xFFFFFFFFu;
+            const bool eq = valid && u == thr;
+            uint32_t tot;
+            const uint32_t rank = eq_seen + block_scan_flag<256>(eq, rs, &tot);
+            eq_seen += tot;
+            const bool keep = valid && (u < thr || (eq && rank < take));
+            const uint32_t pos = written + block_scan_flag<256>(keep, rs, &tot);
+            written += tot;
+            if (keep && pos < (uint32_t)ksel) sel[pos] = ch;
+        }
+    } else {
+        for (int ch = tid; ch < nch; ch += 256) sel[ch] = ch;
+    }
+    __syncthreads();
+    if (p.selected)
+        for (int x = tid; x < p.n_select; x += 256)
+            p.selected[(size_t)slab * p.n_select + x] = x < ksel ? sel[x] : -1;
+
+    // logits of the kept rows in the rank space
+    const uint16_t* AK = reinterpret_cast<const uint16_t*>(p.ak) + (size_t)slab * p.x_tcap * R;
+    const uint16_t* AV = reinterpret_cast<const uint16_t*>(p.av) + (size_t)slab * p.x_tcap * R;
+    for (int r = tid; r < nrows; r += 256) {
+        const int t = sel[r / CHUNK] * CHUNK + r % CHUNK;
+        if (t < T) {
+            float a[R];
+#pragma unroll
+            for (int c8 = 0; c8 < R / 8; ++c8) {
+                const u32x4 w = load16(AK + (size_t)t * R + 8 * c8);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    a[8 * c8 + 2 * e] = bf16lo(w[e]);
+                    a[8 * c8 + 2 * e + 1] = bf16hi(w[e]);
+                }
+            }
+            for (int h = 0; h < g; ++h) {
+                float s = 0.f;
+#pragma unroll
+                for (int c = 0; c < R; ++c) s = fmaf(qt[h * R + c], a[c], s);
+                lgt[r * g + h] = s * p.scale;
+            }
+        } else {
+            for (int h = 0; h < g; ++h) lgt[r * g + h] = -INFINITY;
+        }
+    }
+    __syncthreads();
+
+    // softmax statistics per head (fixed order: rows by thread, then waves)
+    {
+        float mh[MAXG];
+#pragma unroll
+        for (int h = 0; h < MAXG; ++h) mh[h] = -INFINITY;
+        for (int r = tid; r < nrows; r += 256)
+            for (int h = 0; h < g; ++h) mh[h] = fmaxf(mh[h], lgt[r * g + h]);
+#pragma unroll
+        for (int h = 0; h < MAXG; ++h) {
+            const float m = wave_max(mh[h]);
+            if (lane == 0) red[wave][h] = m;
+        }
+        __syncthreads();
+        if (tid < MAXG) hm[tid] = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
+        __syncthreads();
+        float zh[MAXG];
+#pragma unroll
+        for (int h = 0; h < MAXG; ++h) zh[h] = 0.f;
+        for (int r = tid; r < nrows; r += 256)
+            for (int h = 0; h < g; ++h) {
+                const float l = lgt[r * g + h];
+                const float e = (l == -INFINITY) ? 0.f : expf(l - hm[h]);
+                lgt[r * g + h] = e;
+                zh[h] += e;
+            }
+        __syncthreads();
+#pragma unroll
+        for (int h = 0; h < MAXG; ++h) {
+            const float z = wave_sum(zh[h]);
+            if (lane == 0) red[wave][h] = z;
+        }
+        __syncthreads();
+        if (tid < MAXG) hz[tid] = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+        __syncthreads();
+    }
+
+    // a~_h = sum_t p_t,h A^V_t: thread (column c, row group rg)
+    {
+        const int c = tid % R, rg = tid / R;
+        float acc[MAXG];
+#pragma unroll
+        for (int h = 0; h < MAXG; ++h) acc[h] = 0.f;
+        for (int r = rg; r < nrows; r += RG) {
+            const int t = sel[r / CHUNK] * CHUNK + r % CHUNK;
+            if (t < T) {
+                const float a = bf16_to_f32(AV[(size_t)t * R + c]);
+                for (int h = 0; h < g; ++h) acc[h] = fmaf(lgt[r * g + h], a, acc[h]);
+            }
+        }
+        for (int h = 0; h < g; ++h) part[(rg * MAXG + h) * R + c] = acc[h];
+    }
+    __syncthreads();
+    for (int x = tid; x < g * R; x += 256) {
+        const int h = x / R, c = x % R;
+        float s = 0.f;
+        for (int rg = 0; rg < RG; ++rg) s += part[(rg * MAXG + h) * R + c];
+        qt[h * R + c] = s;               // q~ is no longer needed
+    }
+    __syncthreads();
+
+    // o_h = B_l^V a~_h / z_h, merged with the second part if given
+    const float* BV = p.bv + (size_t)slab * n * R + (size_t)p.layer * D * R;
+    for (int x = tid; x < g * D; x += 256) {
+        const int h = x / D, i = x % D;
+        float o = 0.f;
+#pragma unroll 8
+        for (int c = 0; c < R; ++c) o = fmaf(BV[i * R + c], qt[h * R + c], o);
+        const float z = hz[h];
+        float l1 = z > 0.f ? hm[h] + logf(z) : -INFINITY;
+        o = z > 0.f ? o / z : 0.f;
+        const size_t row = (size_t)b * p.hq + j * g + h;
+        if (p.o_in) {
+            const float l2 = p.lse_in[row];
+            const float o2 = p.o_in[row * D + i];
+            const float m = fmaxf(l1, l2);
+            if (m != -INFINITY) {
+                const float w1 = (l1 == -INFINITY) ? 0.f : expf(l1 - m);
+                const float w2 = (l2 == -INFINITY) ? 0.f : expf(l2 - m);
+                o = (o * w1 + o2 * w2) / (w1 + w2);
+                l1 = m + logf(w1 + w2);
+            }
+        }
+        p.out[row * D + i] = o;
+        if (i == 0 && p.lse) p.lse[row] = l1;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_xkv_factor(const XkvLaunch& p, hipStream_t st) {
+    const int n = p.window * D;
+    const dim3 ggrid(p.window * (p.window + 1) / 2, p.hkv, p.nb);
+    hipLaunchKernelGGL(xkv_gram<false>, ggrid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL(xkv_gram<true>, ggrid, dim3(256), 0, st, p);
+    auto big = [&](const void* kern, size_t lds) {
+        return lds <= 64 * 1024 ||
+               hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) ==
+                   hipSuccess;
+    };
+    const size_t zlds = (size_t)n * (p.rank + 1) * sizeof(float);
+    const dim3 sgrid(2 * p.nb * p.hkv);
+    const size_t vlds = (size_t)p.rank * (n + 8) * 2;
+    const size_t tlds = (size_t)4 * D * VPITCH * 2;
+    const dim3 pgrid(p.nsplit, p.hkv, p.nb);
+    if (p.rank == 32) {
+        if (!big((const void*)xkv_subspace<32>, zlds) || !big((const void*)xkv_project<false, 32>, vlds) ||
+            !big((const void*)xkv_project<true, 32>, vlds + tlds))
+            return hipErrorInvalidValue;
+        hipLaunchKernelGGL(xkv_subspace<32>, sgrid, dim3(256), zlds, st, p);
+        hipLaunchKernelGGL((xkv_project<false, 32>), pgrid, dim3(256), vlds, st, p);
+        hipLaunchKernelGGL((xkv_project<true, 32>), pgrid, dim3(256), vlds + tlds, st, p);
+    } else {
+        if (!big((const void*)xkv_subspace<64>, zlds) || !big((const void*)xkv_project<false, 64>, vlds) ||
+            !big((const void*)xkv_project<true, 64>, vlds + tlds))
+            return hipErrorInvalidValue;
+        hipLaunchKernelGGL(xkv_subspace<64>, sgrid, dim3(256), zlds, st, p);
+        hipLaunchKernelGGL((xkv_project<false, 64>), pgrid, dim3(256), vlds, st, p);
+        hipLaunchKernelGGL((xkv_project<true, 64>), pgrid, dim3(256), vlds + tlds, st, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_xkv_decode(const XkvDecodeLaunch& p, size_t lds, hipStream_t st) {
+    const dim3 grid(p.hkv, p.nb);
+    const void* kern = p.rank == 32 ? (const void*)xkv_decode<32> : (const void*)xkv_decode<64>;
+    if (lds > 64 * 1024 &&
+        hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return hipErrorInvalidValue;
+    if (p.rank == 32)
+        hipLaunchKernelGGL(xkv_decode<32>, grid, dim3(256), lds, st, p);
+    else
+        hipLaunchKernelGGL(xkv_decode<64>, grid, dim3(256), lds, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace kvc

@@ -15,9 +15,12 @@
  *           always kept), §2.B (weighted random sampling on SnapKV-style
  *           observation-window attention scores), §1 (evicted pairs are
  *           discarded for good, giving a static footprint).
+ *   [XKV]   "xKV: cross-layer KV-cache compression" (gist.science
+ *           2503.18893), §2.2 (cross-layer factorisation of windows of W
+ *           layers), §2.3 (selective reconstruction with landmark chunk
+ *           selection).
  *   Decode attention itself is standard softmax attention, one query row
- *   per head, with grouped-query heads (GQA, named in the xKV summary,
- *   gist.science 2503.18893, §4).
+ *   per head, with grouped-query heads (GQA, named in [XKV] §4).
  *
  * Conventions shared by every call
  *   - Status: every call returns KVC_OK (0) or a negative kvc_status.  All
@@ -402,6 +405,80 @@ int kvc_q8_decode_attn(const kvc_qcache* c, const void* q,
                        float* out, int64_t out_layer_stride, float* lse,
                        int64_t lse_layer_stride, void* ws, size_t ws_bytes,
                        kvc_stream_t stream);
+
+/*
+ * Cross-layer factorisation store for one window of W consecutive layers
+ * [XKV §2.2: the window's caches concatenated side by side, a rank-r SVD,
+ * one token basis A shared by the window and one matrix B_l per layer].
+ * Per (batch entry b, KV head j), keys and values separately:
+ *   ak, av: bf16 [nb][n_kv_heads][t_cap][rank]      token bases A
+ *   bk, bv: float32 [nb][n_kv_heads][window*head_dim][rank]: rows
+ *           l*head_dim .. l*head_dim + head_dim - 1 hold B_l^T, so layer l's
+ *           row t is rebuilt as A[t] B_l
+ *   lk:     bf16 [nb][n_kv_heads][t_cap/chunk][rank]  key landmarks: the
+ *           mean of each chunk's rows of the key basis [XKV §2.3]
+ * window 1..4, rank 32 or 64 (<= window*head_dim), chunk 8, t_cap a
+ * multiple of 64, rows [0, t_len) valid, every pointer 16-byte aligned.
+ * Memory: t_cap*rank + window*head_dim*rank numbers per basis instead of
+ * window*t_cap*head_dim.
+ */
+typedef struct kvc_xkv {
+    void* ak;
+    void* av;
+    void* lk;
+    float* bk;
+    float* bv;
+    int32_t nb;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t window;
+    int32_t rank;
+    int32_t chunk;
+    int32_t t_len;
+    int32_t t_cap;
+} kvc_xkv;
+
+/* Workspace bytes kvc_xkv_factor needs for stores of this shape. */
+int kvc_xkv_factor_ws_bytes(const kvc_xkv* x, size_t* bytes);
+
+/*
+ * Cross-layer factorisation [XKV §2.2] of slots [slot0, slot0 + window) of
+ * a bf16 cache (uniform batch: no batch_idx / seq_len, nb_cap 0 or nb) into
+ * x, for keys and values.  The rank-r truncated SVD of X = [X_1 | ... | X_W]
+ * (T x window*head_dim, T = c->t_len = x->t_len) is computed by `iters`
+ * steps of subspace iteration on X^T X (float32) from a Gaussian start drawn
+ * with `seed`, modified Gram-Schmidt after every step: the bases' columns
+ * are orthonormal and converge to the top-r right singular subspace, so A B_l
+ * is the rank-r truncation up to that convergence (exact when X has rank
+ * <= r).  A = X V is rounded to bf16; the landmarks are the chunk means of
+ * the stored key rows.  iters 1..64.  ws: kvc_xkv_factor_ws_bytes bytes, no
+ * initialisation needed.
+ */
+int kvc_xkv_factor(const kvc_cache* c, int slot0, int iters, uint64_t seed,
+                   const kvc_xkv* x, void* ws, size_t ws_bytes, kvc_stream_t stream);
+
+/*
+ * Selective-reconstruction decode attention [XKV §2.3] for layer `layer`
+ * (0..window-1) of the window x stores.  For batch entry b and KV head j with
+ * query heads h of its group (g = n_q_heads / n_kv_heads <= 8):
+ *   chunk score s_c = max_h q_h . (lk[c] B_layer)       (landmark key)
+ *   kept chunks    = the n_select largest s_c (ties to the lower chunk; all
+ *                    chunks when there are fewer), ascending
+ *   out[b][h]      = softmax(scale * q_h . K^_t) V^_t over the rows t of the
+ *                    kept chunks, K^_t = ak[t] B^K_layer, V^_t = av[t] B^V_layer
+ * computed in the rank space (the rebuilt rows are never stored).  With o_in
+ * and lse_in (float32 [nb][n_q_heads][head_dim] and [nb][n_q_heads], e.g.
+ * kvc_decode_attn over the rows appended after the factorisation) the two
+ * parts merge into attention over their union; lse (optional) is the
+ * union's log-normaliser.  q: bf16 [nb][n_q_heads][head_dim]; out: float32
+ * like o_in; selected: NULL or int32 [nb][n_kv_heads][n_select] (-1 past the
+ * kept count).  n_select * chunk * g <= 16384 and the chunk keys of t_len
+ * rows must fit the workgroup's LDS (KVC_EINVAL otherwise).
+ */
+int kvc_xkv_decode_attn(const kvc_xkv* x, int layer, const void* q, int n_q_heads,
+                        float scale, int n_select, const float* o_in,
+                        const float* lse_in, float* out, float* lse, int32_t* selected,
+                        kvc_stream_t stream);
 
 /*
  * Diagnostic: the device Philox4x32-10 stream that kvc_select draws from.

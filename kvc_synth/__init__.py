@@ -14,7 +14,10 @@ shapes are kept):
   * optional depth correlation between consecutive leader slots:
     X_s = rho**gap * X_{s-1} + sqrt(1 - rho**(2*gap)) * eps, i.e. a
     per-layer correlation rho applied over `gap` layers;
-  * ragged batches: prompt lengths uniform in [t_min, t_max] (length_mix).
+  * ragged batches: prompt lengths uniform in [t_min, t_max] (length_mix);
+  * cross-layer low-rank caches for the factorisation path: W layers sharing
+    a token basis Z (T x k) with per-layer correlated mixing and optional
+    isotropic noise (lowrank_layers).
 All tensors are logical: K and V as [.., T, d] rows.
 """
 import math
@@ -64,6 +67,30 @@ def kv_slot(nb, hkv, T, d=128, dtype=torch.bfloat16, device="cpu", seed=0,
         sel = idx.unsqueeze(-1).expand(-1, -1, -1, d)
         v_out.scatter_(2, sel, v.gather(2, sel) * outlier_scale)
     return k.to(dtype), v_out.to(dtype), k, v
+
+
+def lowrank_layers(nb, hkv, T, W, k, noise=0.0, rho=0.9, d=128, dtype=torch.bfloat16,
+                   device="cpu", seed=0):
+    """K and V rows [nb][hkv][T][d] of W consecutive layers whose caches share
+    a token basis: per (batch entry, KV head) and for keys and values
+    separately, X_l = Z M_l + noise * E_l with Z ~ N(0, 1) of shape T x k
+    shared by the layers, M_1 ~ N(0, 1/k) (k x d) and
+    M_l = rho M_{l-1} + sqrt(1 - rho^2) N(0, 1/k) (a per-layer correlation),
+    E_l ~ N(0, 1).  Returns a list of W (K, V) pairs."""
+    gen = generator(seed, device)
+    out = [[None, None] for _ in range(W)]
+    for kv in range(2):
+        Z = torch.randn((nb, hkv, T, k), generator=gen, device=device)
+        M = torch.randn((nb, hkv, k, d), generator=gen, device=device) / math.sqrt(k)
+        for l in range(W):
+            if l:
+                M = rho * M + math.sqrt(1 - rho * rho) * torch.randn(
+                    (nb, hkv, k, d), generator=gen, device=device) / math.sqrt(k)
+            X = Z @ M
+            if noise:
+                X = X + noise * torch.randn((nb, hkv, T, d), generator=gen, device=device)
+            out[l][kv] = X.to(dtype)
+    return [tuple(x) for x in out]
 
 
 def length_mix(n, t_min, t_max, seed=0):

@@ -334,3 +334,54 @@ def test_cache_seqs_view():
         c.seqs(idx.long())
     with pytest.raises(ValueError):
         c.seqs(idx, ln[:2])
+
+
+def xkv_desc(**kw):
+    from decode_attention_kvc_amd._lib import kvc_xkv
+    d = dict(ak=FAKE, av=FAKE, lk=FAKE, bk=FAKE, bv=FAKE, nb=1, n_kv_heads=2, head_dim=128,
+             window=4, rank=64, chunk=8, t_len=100, t_cap=128)
+    d.update(kw)
+    return kvc_xkv(d["ak"], d["av"], d["lk"], d["bk"], d["bv"], d["nb"], d["n_kv_heads"],
+                   d["head_dim"], d["window"], d["rank"], d["chunk"], d["t_len"], d["t_cap"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(window=5), kvc.KVC_EINVAL), (dict(window=0), kvc.KVC_EINVAL),
+    (dict(rank=48), kvc.KVC_EINVAL), (dict(chunk=4), kvc.KVC_EINVAL),
+    (dict(t_cap=100), kvc.KVC_EINVAL), (dict(t_len=200), kvc.KVC_EINVAL),
+    (dict(head_dim=64), kvc.KVC_EINVAL), (dict(lk=FAKE + 4), kvc.KVC_EALIGN),
+])
+def test_xkv_store_validation(kw, code):
+    n = ctypes.c_size_t()
+    assert L.kvc_xkv_factor_ws_bytes(ctypes.byref(xkv_desc(**kw)), ctypes.byref(n)) == code
+
+
+def test_xkv_ws_bytes_and_factor_validation():
+    n = ctypes.c_size_t()
+    x = xkv_desc()
+    assert L.kvc_xkv_factor_ws_bytes(ctypes.byref(x), ctypes.byref(n)) == kvc.KVC_OK
+    assert n.value >= 2 * 2 * 512 * 512 * 4 + 2 * 2 * 64 * 512 * 2
+    f = lambda c, slot0=0, iters=12, x=x: L.kvc_xkv_factor(ctypes.byref(c), slot0, iters, 0,
+                                                           ctypes.byref(x), FAKE, 1 << 40, None)
+    c4 = cache(n_slots=4, n_kv_heads=2)
+    assert f(c4, slot0=1) == kvc.KVC_EINVAL                      # window past the last slot
+    assert f(c4, iters=0) == kvc.KVC_EINVAL
+    assert f(cache(n_slots=4, dtype=0)) == kvc.KVC_EDTYPE
+    assert f(c4, x=xkv_desc(t_len=99)) == kvc.KVC_EINVAL         # lengths disagree
+    assert f(c4, x=xkv_desc(n_kv_heads=1)) == kvc.KVC_EINVAL
+    assert f(ragged_cache(n_slots=4, seq_len=FAKE)) == kvc.KVC_EINVAL
+    assert f(cache(n_slots=4, t_len=0), x=xkv_desc(t_len=0)) == kvc.KVC_OK
+
+
+def test_xkv_decode_validation():
+    x = xkv_desc()
+    d = lambda layer=0, hq=8, nsel=64, o_in=None, lse_in=None, q=FAKE, x=x: L.kvc_xkv_decode_attn(
+        ctypes.byref(x), layer, q, hq, 0.0, nsel, o_in, lse_in, FAKE, None, None, None)
+    assert d(layer=4) == kvc.KVC_EINVAL
+    assert d(hq=7) == kvc.KVC_EINVAL
+    assert d(hq=2 * 9) == kvc.KVC_EINVAL                         # group of 9 heads
+    assert d(nsel=0) == kvc.KVC_EINVAL
+    assert d(nsel=600) == kvc.KVC_EINVAL                         # 600 * 8 * 4 > 16384
+    assert d(o_in=FAKE) == kvc.KVC_EINVAL                        # lse_in missing
+    assert d(q=FAKE + 2) == kvc.KVC_EALIGN
+    assert d(x=xkv_desc(nb=0)) == kvc.KVC_OK
