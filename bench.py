@@ -315,6 +315,110 @@ def ragged_leg(args, cfg, qpool, lsepool, knew, vnew, out, steps, warm=3):
                        "score, select, compact on the due sequences only")
 
 
+def xkv_leg(args, cfg, qpool, knew, vnew, steps, warm=3):
+    """Cross-layer factorisation + selective reconstruction on the same model
+    shape, every layer its own cache (no sharing): the 32K-row caches of each
+    window of 4 layers are factorised once (rank 64, keys and values), then
+    each decode step runs, per layer, attention over the rows appended since
+    (kvc_decode_attn with the append, an uncompressed tail) and the selective
+    reconstruction of 256 chunks of 8 rows merged into it.  Synthetic caches
+    with the structure the factorisation relies on: per window, keys and
+    values share a rank-48 token basis across the layers (per-layer mixing
+    correlated 0.9) plus N(0, 0.1^2) noise.  Also times full attention over
+    one uncompressed layer for comparison."""
+    import torch
+    import kvc_synth
+    import decode_attention_kvc_amd as kvc
+    dev = "cuda"
+    L, nb, hq, hkv, T = (cfg[k] for k in ("n_layers", "nb", "hq", "hkv", "t0"))
+    W, rank, n_sel, iters = 4, 64, 256, 12
+    n_win = L // W
+    n_slots_pool = knew.shape[1]
+    stores, fact_ms = [], []
+    base = None
+    g = hq // hkv
+    for w in range(n_win):
+        layers = kvc_synth.lowrank_layers(nb, hkv, T, W, 48, noise=0.1, device=dev, seed=400 + w)
+        c = kvc.Cache.empty(W, nb, hkv, T, device=dev)
+        for l, (K, V) in enumerate(layers):
+            c.fill(l, K, V)
+        del layers, K, V
+        st = kvc.XkvStore.empty(nb, hkv, W, rank, T, device=dev)
+        ws = torch.empty(kvc.kvc_xkv_factor_ws_bytes(st), dtype=torch.uint8, device=dev)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        kvc.kvc_xkv_factor(c, 0, st, ws, iters=iters, seed=w)
+        b.record()
+        torch.cuda.synchronize()
+        fact_ms.append(a.elapsed_time(b))
+        if w == 0:
+            # full attention over one uncompressed layer of the same cache
+            out1 = torch.empty((1, nb, hq, 128), device=dev)
+            wsa = torch.zeros(kvc.kvc_decode_attn_ws_bytes(c, 1, hq), dtype=torch.uint8, device=dev)
+            for _ in range(3):
+                kvc.kvc_decode_attn(c, qpool[0, 0:1], [0], out1, None, wsa)
+            torch.cuda.synchronize()
+            a.record()
+            for r in range(20):
+                kvc.kvc_decode_attn(c, qpool[r % W, 0:1], [r % W], out1, None, wsa)
+            b.record()
+            torch.cuda.synchronize()
+            base = a.elapsed_time(b) / 20
+            del wsa, out1
+        del c, ws
+        torch.cuda.empty_cache()
+        stores.append(st)
+    tail = kvc.Cache.empty(L, nb, hkv, warm + steps + 64, device=dev)
+    tail.t_len = 0
+    ws_t = torch.zeros(kvc.kvc_decode_attn_ws_bytes(tail, 1, hq), dtype=torch.uint8, device=dev)
+    o_t = torch.empty((L, nb, hq, 128), device=dev)
+    l_t = torch.empty((L, nb, hq), device=dev)
+    out = torch.empty((L, nb, hq, 128), device=dev)
+
+    def step(s):
+        tail.t_len += 1
+        for l in range(L):
+            sl = l % n_slots_pool
+            kvc.kvc_decode_attn(tail, qpool[l, s], [l], o_t[l], l_t[l], ws_t, k_new=knew[s, sl],
+                                v_new=vnew[s, sl], append_slot=l, n_q_heads=hq)
+            kvc.kvc_xkv_decode_attn(stores[l // W], l % W, qpool[l, s], out[l], None,
+                                    n_select=n_sel, o_in=o_t[l], lse_in=l_t[l])
+
+    for s in range(warm):
+        step(s)
+    torch.cuda.synchronize()
+    evs = []
+    t0 = time.perf_counter()
+    for s in range(warm, warm + steps):
+        a = torch.cuda.Event(enable_timing=True)
+        a.record()
+        step(s)
+        b = torch.cuda.Event(enable_timing=True)
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    nch = (T + 7) // 8
+    sr_bytes = nb * hkv * (nch * rank * 2 + 2 * n_sel * 8 * rank * 2 + 2 * 128 * rank * 4
+                           + g * (128 * 2 + 129 * 4 + 128 * 4))
+    stored = stores[0].nbytes() * n_win
+    full = 2 * L * nb * hkv * T * 128 * 2
+    return dict(value=round(nb * steps / wall, 2), unit="tokens/s",
+                ms_per_step=round(1e3 * wall / steps, 4), gpu_ms_per_step=round(gpu_ms, 4),
+                window=W, rank=rank, chunk=8, n_select=n_sel, iters=iters, prompt_tokens=T,
+                tail_rows=[warm + 1, warm + steps],
+                factor_ms_per_window=round(sum(fact_ms) / len(fact_ms), 3),
+                store_GB=round(stored / 1e9, 3), full_cache_GB=round(full / 1e9, 3),
+                compression=round(full / stored, 2),
+                sr_bytes_per_call=sr_bytes,
+                full_attention_us_per_layer=round(1e3 * base, 2),
+                full_attention_ms_per_step=round(L * base, 3),
+                kernel="per layer: attn_bf16_kernel over the tail (+ merge) and xkv_decode<64>",
+                data="synthetic cross-layer low-rank caches (rank-48 shared basis + 0.1 noise)")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -335,6 +439,10 @@ def main():
                     help="skip the ragged-batch leg (length mix, per-sequence eviction steps)")
     ap.add_argument("--ragged-only", action="store_true",
                     help="profiling aid: run only the ragged-batch leg and print its result")
+    ap.add_argument("--no-xkv", action="store_true",
+                    help="skip the cross-layer factorisation / selective reconstruction leg")
+    ap.add_argument("--xkv-only", action="store_true",
+                    help="profiling aid: run only the cross-layer factorisation leg")
     ap.add_argument("--no-int8", action="store_true",
                     help="skip the range-protected int8 cache leg (decode attention only)")
     ap.add_argument("--protect-frac", type=float, default=0.01,
@@ -370,6 +478,14 @@ def main():
         steady_cap = ev["K"] + ev["B"] + ev["period"]
     else:
         steady_cap = t0 + n_total
+    if args.xkv_only:
+        qpool = kvc_synth.queries((L, n_total, nb, hq, 128), device=dev, seed=1)
+        knew = kvc_synth.queries((n_total, n_slots, nb, hkv, 128), device=dev, seed=2)
+        vnew = kvc_synth.queries((n_total, n_slots, nb, hkv, 128), device=dev, seed=3)
+        r = xkv_leg(args, cfg, qpool, knew, vnew, S, warm=W)
+        print(json.dumps({"xkv_only": True, "workload": cfg["desc"], "steps": S, "warmup": W,
+                          "xkv": r}), flush=True)
+        return
     if args.ragged_only:
         if not ev or args.scoring != "attnv":
             sys.exit("--ragged-only needs an eviction workload with window scores")
@@ -491,6 +607,14 @@ def main():
         ragged_res = ragged_leg(args, cfg, qpool, lsepool, knew, vnew, out, S, warm=W)
         log(f"[bench] ragged: {ragged_res}")
 
+    xkv_res = None
+    if not args.no_xkv and args.workload == "llama3.1-8b-combined":
+        log("[bench] xkv leg: factorising the windows")
+        dec.spare = None
+        torch.cuda.empty_cache()
+        xkv_res = xkv_leg(args, cfg, qpool, knew, vnew, S, warm=W)
+        log(f"[bench] xkv: {xkv_res}")
+
     if args.copy_calibration:
         # Two plain copies of known size for scaling the memory counters:
         # a 1 GiB runtime blit, and a 512 MiB float32 copy done by a
@@ -556,6 +680,7 @@ def main():
         "grouped": grouped,
         "int8": int8,
         "ragged": ragged_res,
+        "xkv": xkv_res,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -305,9 +305,8 @@ XkvWs xkv_ws(const kvc_xkv* x) {
 size_t xkv_decode_lds(const kvc_xkv* x, int g, int n_select) {
     const size_t nch = ((size_t)x->t_len + XKV_CHUNK - 1) / XKV_CHUNK;
     const size_t ksel = std::min<size_t>((size_t)n_select, nch);
-    const size_t rg = 256 / x->rank;
     return (XKV_MAXG * (size_t)x->rank + nch + ksel + ksel * XKV_CHUNK * g +
-            rg * XKV_MAXG * x->rank) * 4;
+            8 * XKV_MAXG * (x->rank + 1)) * 4;   // 8 waves' value partials
 }
 
 }  // namespace

@@ -44,6 +44,31 @@ __device__ __forceinline__ uint32_t block_scan_flag(bool flag, RadixSmem<NT>& sm
     return off + before;
 }
 
+// Exclusive prefix sum of v over the block in thread order; returns this
+// thread's offset and writes the block total to *total.
+template <int NT>
+__device__ __forceinline__ uint32_t block_scan_u32(uint32_t v, RadixSmem<NT>& sm, uint32_t* total) {
+    constexpr int NWV = NT / WAVE;
+    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+    uint32_t incl = v;
+#pragma unroll
+    for (int o = 1; o < WAVE; o <<= 1) {
+        const uint32_t y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    if (lane == WAVE - 1) sm.wave_tot[wave] = incl;
+    __syncthreads();
+    uint32_t off = 0, tot = 0;
+    for (int w = 0; w < NWV; ++w) {
+        const uint32_t c = sm.wave_tot[w];
+        off += (w < wave) ? c : 0u;
+        tot += c;
+    }
+    __syncthreads();
+    *total = tot;
+    return off + incl - v;
+}
+
 // k-th smallest (1-based) of key(t), t < n.  Returns the key; *take gets how
 // many rows equal to it belong to the k smallest (lowest rows first).
 template <int NT, typename KeyFn>

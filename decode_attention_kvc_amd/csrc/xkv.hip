@@ -45,6 +45,8 @@ constexpr int GP = 40;          // bf16 per staged channel row of a tile (80 byt
 constexpr int CHUNK = 8;        // rows per landmark chunk
 constexpr int VPITCH = XT + 2;  // bf16 per channel in a wave's value transpose buffer
 constexpr int MAXG = 8;         // query heads per KV head on the decode path
+constexpr int XNT = 512;        // threads of a decode workgroup (two waves per SIMD)
+constexpr int XNW = XNT / WAVE;
 
 __device__ __forceinline__ bf16x8 as_bf(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
@@ -376,181 +378,301 @@ __device__ __forceinline__ uint32_t desc_key(float s) {
     return ~asc;
 }
 
-template <int R>
-__global__ __launch_bounds__(256) void xkv_decode(XkvDecodeLaunch p) {
+// Lane permutations inside a 16-lane row (DPP: plain VALU moves).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// Sum over aligned groups of N lanes (N = 4 or 8; every lane gets it): swap
+// neighbours, swap pairs, then (N = 8) mirror the half-row.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+    v += dpp_mov<0xB1>(v);
+    v += dpp_mov<0x4E>(v);
+    if constexpr (N == 8) v += dpp_mov<0x141>(v);
+    return v;
+}
+// Sum over the lanes of a wave whose index agrees modulo N (N = 2 or 4):
+// rotations inside each 16-lane row, then across the four rows.
+template <int N>
+__device__ __forceinline__ float strided_sum(float v) {
+    if constexpr (N == 2) v += dpp_mov<0x122>(v);      // row_ror:2
+    if constexpr (N <= 4) v += dpp_mov<0x124>(v);      // row_ror:4
+    v += dpp_mov<0x128>(v);                             // row_ror:8
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+// Lanes per row of the rank space (8 columns each) and the dot products of
+// one row with the G query vectors q~ held in registers, summed over the
+// row's lanes (every lane of the group gets the sums).
+template <int R, int G>
+__device__ __forceinline__ void rank_dots(const u32x4& w, const float (&qr)[G][8], float (&s)[G]) {
+    constexpr int LPR = R / 8;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a = fmaf(qr[h][2 * e], bf16lo(w[e]), a);
+            a = fmaf(qr[h][2 * e + 1], bf16hi(w[e]), a);
+        }
+        s[h] = group_sum<LPR>(a);
+    }
+}
+
+template <int R, int G>
+__global__ __launch_bounds__(XNT) void xkv_decode(XkvDecodeLaunch p) {
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ RadixSmem<256> rs;
-    __shared__ float red[4][MAXG];
+    __shared__ RadixSmem<XNT> rs;
+    __shared__ float red[XNW][MAXG];
     __shared__ float hm[MAXG], hz[MAXG];
-    constexpr int RG = 256 / R;            // row groups of the value reduction
+    constexpr int LPR = R / 8;             // lanes per rank-space row
+    constexpr int NGRP = XNT / LPR;        // rows per block pass
+    constexpr int CW = G <= 4 ? 16 : 8;    // value phase: columns per lane
+    constexpr int CG = R / CW;             //              column groups
+    constexpr int RGW = WAVE / CG;         //              row groups per wave
+    constexpr int RGS = XNW * RGW;         //              row groups per block
     const int j = blockIdx.x, b = blockIdx.y;
     const int slab = b * p.hkv + j, g = p.g, n = p.window * D;
     const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+    const int sub = lane % LPR, grp = tid / LPR;
     const int T = p.t_len, nch = (T + CHUNK - 1) / CHUNK;
     const int ksel = min(p.n_select, nch), nrows = ksel * CHUNK;
     float* qt = reinterpret_cast<float*>(smem);                  // [MAXG][R]
     uint32_t* keys = reinterpret_cast<uint32_t*>(qt + MAXG * R); // [nch]
     int32_t* sel = reinterpret_cast<int32_t*>(keys + nch);       // [ksel]
     float* lgt = reinterpret_cast<float*>(sel + ksel);           // [nrows][g]
-    float* part = lgt + (size_t)nrows * g;                       // [RG][MAXG][R]
+    float* part = lgt + (size_t)nrows * g;                       // [XNW][MAXG][R + 1]
 
-    // q~_h = B_l q_h: B_l^T is rows layer*128 .. of the key basis [n][R]
+    // q~_h = B_l q_h: B_l^T is rows layer*128 .. of the key basis [n][R].
+    // The queries go through LDS (part is free until the value reduction).
     const float* BK = p.bk + (size_t)slab * n * R + (size_t)p.layer * D * R;
-    const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)b * p.hq + j * g) * D;
-    for (int x = tid; x < g * R; x += 256) {
-        const int h = x / R, c = x % R;
-        float a = 0.f;
-        for (int i = 0; i < D; ++i) a = fmaf(bf16_to_f32(q[h * D + i]), BK[i * R + c], a);
-        qt[h * R + c] = a;
-    }
-    __syncthreads();
-
-    // chunk scores: max over the heads of q~_h . landmark
-    const uint16_t* L = reinterpret_cast<const uint16_t*>(p.lk) + (size_t)slab * (p.x_tcap / CHUNK) * R;
-    for (int ch = tid; ch < nch; ch += 256) {
-        float lm[R];
-#pragma unroll
-        for (int c8 = 0; c8 < R / 8; ++c8) {
-            const u32x4 w = load16(L + (size_t)ch * R + 8 * c8);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                lm[8 * c8 + 2 * e] = bf16lo(w[e]);
-                lm[8 * c8 + 2 * e + 1] = bf16hi(w[e]);
+    {
+        const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)b * p.hq + j * g) * D;
+        for (int x = tid; x < g * D; x += XNT) part[x] = bf16_to_f32(q[x]);
+        __syncthreads();
+        for (int x = tid; x < MAXG * R; x += XNT) {
+            const int h = x / R, c = x % R;
+            float a0 = 0.f, a1 = 0.f;
+            if (h < g) {
+                const float* qs = part + h * D;
+#pragma unroll 16
+                for (int i = 0; i < D; i += 2) {
+                    a0 = fmaf(qs[i], BK[i * R + c], a0);
+                    a1 = fmaf(qs[i + 1], BK[(i + 1) * R + c], a1);
+                }
             }
+            qt[h * R + c] = a0 + a1;     // heads past g: zero
         }
-        float best = -INFINITY;
-        for (int h = 0; h < g; ++h) {
-            float s = 0.f;
+    }
+    __syncthreads();
+    float qr[G][8];                      // this lane's 8 columns of every q~_h
 #pragma unroll
-            for (int c = 0; c < R; ++c) s = fmaf(qt[h * R + c], lm[c], s);
-            best = fmaxf(best, s);
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qr[h][e] = qt[h * R + 8 * sub + e];
+
+    // chunk scores: max over the heads of q~_h . landmark; LPR lanes per
+    // chunk, UNR chunks in flight per lane group
+    constexpr int UNR = G <= 4 ? 16 : 8;     // loads in flight per lane (registers)
+    const uint16_t* L = reinterpret_cast<const uint16_t*>(p.lk) + (size_t)slab * (p.x_tcap / CHUNK) * R;
+    for (int base = 0; base < nch; base += UNR * NGRP) {
+        u32x4 w[UNR];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int ch = base + u * NGRP + grp;
+            w[u] = ch < nch ? load16(L + (size_t)ch * R + 8 * sub) : u32x4{0u, 0u, 0u, 0u};
         }
-        keys[ch] = desc_key(best);
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int ch = base + u * NGRP + grp;
+            float s[G];
+            rank_dots<R, G>(w[u], qr, s);
+            float best = -INFINITY;
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+                if (h < g) best = fmaxf(best, s[h]);
+            if (sub == 0 && ch < nch) keys[ch] = desc_key(best);
+        }
     }
     __syncthreads();
 
-    // the ksel best chunks, ascending (all of them when there are fewer)
+    // the ksel best chunks, ascending (all of them when there are fewer):
+    // thread t owns the contiguous chunks [t*per, (t+1)*per), so one block
+    // scan places the equal keys in chunk order and another the kept ones
     if (ksel < nch) {
         uint32_t take;
-        const uint32_t thr = radix_select<256>(nch, (uint32_t)ksel, [&](int t) { return keys[t]; },
+        const uint32_t thr = radix_select<XNT>(nch, (uint32_t)ksel, [&](int t) { return keys[t]; },
                                                rs, &take);
-        uint32_t written = 0, eq_seen = 0;
-        for (int base = 0; base < nch; base += 256) {
-            const int ch = base + tid;
-            const bool valid = ch < nch;
-            const uint32_t u = valid ? keys[ch] : 0xFFFFFFFFu;
-            const bool eq = valid && u == thr;
-            uint32_t tot;
-            const uint32_t rank = eq_seen + block_scan_flag<256>(eq, rs, &tot);
-            eq_seen += tot;
-            const bool keep = valid && (u < thr || (eq && rank < take));
-            const uint32_t pos = written + block_scan_flag<256>(keep, rs, &tot);
-            written += tot;
-            if (keep && pos < (uint32_t)ksel) sel[pos] = ch;
+        const int per = (nch + XNT - 1) / XNT;
+        const int c0 = min(nch, tid * per), c1 = min(nch, c0 + per);
+        uint32_t n_eq = 0;
+        for (int ch = c0; ch < c1; ++ch) n_eq += keys[ch] == thr;
+        uint32_t tot;
+        uint32_t eq_rank = block_scan_u32<XNT>(n_eq, rs, &tot);
+        uint32_t n_keep = 0;
+        for (int ch = c0; ch < c1; ++ch) {
+            const uint32_t u = keys[ch];
+            n_keep += (u < thr) || (u == thr && eq_rank++ < take);
+        }
+        eq_rank -= n_eq;                           // back to this thread's first equal key
+        uint32_t pos = block_scan_u32<XNT>(n_keep, rs, &tot);
+        for (int ch = c0; ch < c1; ++ch) {
+            const uint32_t u = keys[ch];
+            if ((u < thr) || (u == thr && eq_rank++ < take)) {
+                if (pos < (uint32_t)ksel) sel[pos] = ch;
+                ++pos;
+            }
         }
     } else {
-        for (int ch = tid; ch < nch; ch += 256) sel[ch] = ch;
+        for (int ch = tid; ch < nch; ch += XNT) sel[ch] = ch;
     }
     __syncthreads();
     if (p.selected)
-        for (int x = tid; x < p.n_select; x += 256)
+        for (int x = tid; x < p.n_select; x += XNT)
             p.selected[(size_t)slab * p.n_select + x] = x < ksel ? sel[x] : -1;
 
-    // logits of the kept rows in the rank space
+    // logits of the kept rows in the rank space (LPR lanes per row, UNR
+    // rows in flight), and the per-head maximum
     const uint16_t* AK = reinterpret_cast<const uint16_t*>(p.ak) + (size_t)slab * p.x_tcap * R;
     const uint16_t* AV = reinterpret_cast<const uint16_t*>(p.av) + (size_t)slab * p.x_tcap * R;
-    for (int r = tid; r < nrows; r += 256) {
-        const int t = sel[r / CHUNK] * CHUNK + r % CHUNK;
-        if (t < T) {
-            float a[R];
+    {
+        float mh[G];
 #pragma unroll
-            for (int c8 = 0; c8 < R / 8; ++c8) {
-                const u32x4 w = load16(AK + (size_t)t * R + 8 * c8);
+        for (int h = 0; h < G; ++h) mh[h] = -INFINITY;
+        for (int base = 0; base < nrows; base += UNR * NGRP) {
+            u32x4 w[UNR];
+            int tr[UNR];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    a[8 * c8 + 2 * e] = bf16lo(w[e]);
-                    a[8 * c8 + 2 * e + 1] = bf16hi(w[e]);
+            for (int u = 0; u < UNR; ++u) {
+                const int r = base + u * NGRP + grp;
+                tr[u] = r < nrows ? sel[r / CHUNK] * CHUNK + r % CHUNK : T;
+                w[u] = tr[u] < T ? load16(AK + (size_t)tr[u] * R + 8 * sub) : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                const int r = base + u * NGRP + grp;
+                float s[G];
+                rank_dots<R, G>(w[u], qr, s);
+                if (r < nrows) {
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        if (h < g) {
+                            const float l = tr[u] < T ? s[h] * p.scale : -INFINITY;
+                            mh[h] = fmaxf(mh[h], l);
+                            if (sub == 0) lgt[r * g + h] = l;
+                        }
+                    }
                 }
             }
-            for (int h = 0; h < g; ++h) {
-                float s = 0.f;
-#pragma unroll
-                for (int c = 0; c < R; ++c) s = fmaf(qt[h * R + c], a[c], s);
-                lgt[r * g + h] = s * p.scale;
-            }
-        } else {
-            for (int h = 0; h < g; ++h) lgt[r * g + h] = -INFINITY;
         }
-    }
-    __syncthreads();
-
-    // softmax statistics per head (fixed order: rows by thread, then waves)
-    {
-        float mh[MAXG];
 #pragma unroll
-        for (int h = 0; h < MAXG; ++h) mh[h] = -INFINITY;
-        for (int r = tid; r < nrows; r += 256)
-            for (int h = 0; h < g; ++h) mh[h] = fmaxf(mh[h], lgt[r * g + h]);
-#pragma unroll
-        for (int h = 0; h < MAXG; ++h) {
+        for (int h = 0; h < G; ++h) {
             const float m = wave_max(mh[h]);
             if (lane == 0) red[wave][h] = m;
         }
         __syncthreads();
-        if (tid < MAXG) hm[tid] = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
-        __syncthreads();
-        float zh[MAXG];
-#pragma unroll
-        for (int h = 0; h < MAXG; ++h) zh[h] = 0.f;
-        for (int r = tid; r < nrows; r += 256)
-            for (int h = 0; h < g; ++h) {
-                const float l = lgt[r * g + h];
-                const float e = (l == -INFINITY) ? 0.f : expf(l - hm[h]);
-                lgt[r * g + h] = e;
-                zh[h] += e;
-            }
-        __syncthreads();
-#pragma unroll
-        for (int h = 0; h < MAXG; ++h) {
-            const float z = wave_sum(zh[h]);
-            if (lane == 0) red[wave][h] = z;
+        if (tid < MAXG) {
+            float m = red[0][tid];
+            for (int w2 = 1; w2 < XNW; ++w2) m = fmaxf(m, red[w2][tid]);
+            hm[tid] = m;
         }
-        __syncthreads();
-        if (tid < MAXG) hz[tid] = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
         __syncthreads();
     }
 
-    // a~_h = sum_t p_t,h A^V_t: thread (column c, row group rg)
+    // a~_h = sum_t p_t,h A^V_t and z_h = sum_t p_t,h with p = exp(l - max):
+    // lane (row group, CW-column group), 16-byte value reads, VR rows in
+    // flight; then sums over the row groups (lanes, then waves)
     {
-        const int c = tid % R, rg = tid / R;
-        float acc[MAXG];
+        const int cg = lane % CG, rgl = lane / CG;
+        const int rg = wave * RGW + rgl;
+        float mx[G];
 #pragma unroll
-        for (int h = 0; h < MAXG; ++h) acc[h] = 0.f;
-        for (int r = rg; r < nrows; r += RG) {
-            const int t = sel[r / CHUNK] * CHUNK + r % CHUNK;
-            if (t < T) {
-                const float a = bf16_to_f32(AV[(size_t)t * R + c]);
-                for (int h = 0; h < g; ++h) acc[h] = fmaf(lgt[r * g + h], a, acc[h]);
+        for (int h = 0; h < G; ++h) mx[h] = hm[h];
+        float acc[G][CW], zs[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            zs[h] = 0.f;
+#pragma unroll
+            for (int e = 0; e < CW; ++e) acc[h][e] = 0.f;
+        }
+        constexpr int VR = 8;
+        constexpr int NL = CW / 8;                 // 16-byte loads per row and lane
+        for (int base = rg; base < nrows; base += VR * RGS) {
+            u32x4 w[VR][NL];
+            int tr[VR];
+#pragma unroll
+            for (int u = 0; u < VR; ++u) {
+                const int r = base + u * RGS;
+                tr[u] = r < nrows ? sel[r / CHUNK] * CHUNK + r % CHUNK : T;
+                const bool ok = tr[u] < T;
+#pragma unroll
+                for (int q2 = 0; q2 < NL; ++q2)
+                    w[u][q2] = ok ? load16(AV + (size_t)tr[u] * R + CW * cg + 8 * q2)
+                                  : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < VR; ++u) {
+                const int r = base + u * RGS;
+                if (tr[u] < T) {
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        if (h < g) {
+                            const float pr = expf(lgt[r * g + h] - mx[h]);
+                            zs[h] += pr;
+#pragma unroll
+                            for (int q2 = 0; q2 < NL; ++q2)
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    acc[h][8 * q2 + 2 * e] =
+                                        fmaf(pr, bf16lo(w[u][q2][e]), acc[h][8 * q2 + 2 * e]);
+                                    acc[h][8 * q2 + 2 * e + 1] =
+                                        fmaf(pr, bf16hi(w[u][q2][e]), acc[h][8 * q2 + 2 * e + 1]);
+                                }
+                        }
+                    }
+                }
             }
         }
-        for (int h = 0; h < g; ++h) part[(rg * MAXG + h) * R + c] = acc[h];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            zs[h] = strided_sum<CG>(zs[h]);
+#pragma unroll
+            for (int e = 0; e < CW; ++e) acc[h][e] = strided_sum<CG>(acc[h][e]);
+        }
+        if (rgl == 0) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+#pragma unroll
+                for (int e = 0; e < CW; ++e) part[(wave * MAXG + h) * (R + 1) + CW * cg + e] = acc[h][e];
+                if (cg == 0) part[(wave * MAXG + h) * (R + 1) + R] = zs[h];
+            }
+        }
     }
     __syncthreads();
-    for (int x = tid; x < g * R; x += 256) {
-        const int h = x / R, c = x % R;
-        float s = 0.f;
-        for (int rg = 0; rg < RG; ++rg) s += part[(rg * MAXG + h) * R + c];
-        qt[h * R + c] = s;               // q~ is no longer needed
+    for (int x = tid; x < MAXG * (R + 1); x += XNT) {
+        const int h = x / (R + 1), c = x % (R + 1);
+        float s4 = 0.f;
+        for (int w2 = 0; w2 < XNW; ++w2) s4 += part[(w2 * MAXG + h) * (R + 1) + c];
+        if (c < R) qt[h * R + c] = s4;   // q~ is no longer needed
+        else hz[h] = s4;
     }
     __syncthreads();
 
     // o_h = B_l^V a~_h / z_h, merged with the second part if given
     const float* BV = p.bv + (size_t)slab * n * R + (size_t)p.layer * D * R;
-    for (int x = tid; x < g * D; x += 256) {
+    for (int x = tid; x < g * D; x += XNT) {
         const int h = x / D, i = x % D;
         float o = 0.f;
-#pragma unroll 8
-        for (int c = 0; c < R; ++c) o = fmaf(BV[i * R + c], qt[h * R + c], o);
+#pragma unroll
+        for (int c4 = 0; c4 < R / 4; ++c4) {
+            const f32x4 bvv = *reinterpret_cast<const f32x4*>(BV + i * R + 4 * c4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o = fmaf(bvv[e], qt[h * R + 4 * c4 + e], o);
+        }
         const float z = hz[h];
         float l1 = z > 0.f ? hm[h] + logf(z) : -INFINITY;
         o = z > 0.f ? o / z : 0.f;
@@ -608,15 +730,16 @@ hipError_t launch_xkv_factor(const XkvLaunch& p, hipStream_t st) {
 
 hipError_t launch_xkv_decode(const XkvDecodeLaunch& p, size_t lds, hipStream_t st) {
     const dim3 grid(p.hkv, p.nb);
-    const void* kern = p.rank == 32 ? (const void*)xkv_decode<32> : (const void*)xkv_decode<64>;
-    if (lds > 64 * 1024 &&
-        hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-        return hipErrorInvalidValue;
-    if (p.rank == 32)
-        hipLaunchKernelGGL(xkv_decode<32>, grid, dim3(256), lds, st, p);
-    else
-        hipLaunchKernelGGL(xkv_decode<64>, grid, dim3(256), lds, st, p);
-    return hipGetLastError();
+    auto go = [&](auto kern) {
+        if (lds > 64 * 1024 &&
+            hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+            return hipErrorInvalidValue;
+        hipLaunchKernelGGL(kern, grid, dim3(XNT), lds, st, p);
+        return hipGetLastError();
+    };
+    if (p.rank == 32) return p.g <= 4 ? go(xkv_decode<32, 4>) : go(xkv_decode<32, 8>);
+    return p.g <= 4 ? go(xkv_decode<64, 4>) : go(xkv_decode<64, 8>);
 }
 
 }  // namespace kvc
