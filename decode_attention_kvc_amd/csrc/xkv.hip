@@ -104,7 +104,9 @@ __global__ __launch_bounds__(256) void xkv_gram(XkvLaunch p) {
                     }
                     *reinterpret_cast<u32x4*>(dst + ch * GP + 8 * q4) = v;
                 } else {
-                    const int r = c >> 4, c8 = (c & 15) * 8;   // row, first channel
+                    // a wave writes 32 consecutive rows of each channel: no
+                    // two lanes of a write share an LDS bank
+                    const int r = c & 31, c8 = (c >> 5) * 8;   // row, first channel
                     u32x4 v = u32x4{0u, 0u, 0u, 0u};
                     if (t0 + r < T) v = load_stream16(x + (size_t)(t0 + r) * D + c8);
                     const u16x8 e = __builtin_bit_cast(u16x8, v);
@@ -209,19 +211,31 @@ __global__ __launch_bounds__(256) void xkv_subspace(XkvLaunch p) {
         for (int u = 0; u < 8; ++u)
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) acc[u][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < n; k0 += 4) {
-            float bv[CB];
+        // four k-steps per round: their 32 G loads are issued together
+        for (int k0 = 0; k0 < n; k0 += 16) {
+            float ga[4][8];
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb) bv[cb] = Zs[(k0 + lg) * RP + 16 * cb + l16];
-            const float* grow = G + (size_t)(k0 + lg) * n;
+            for (int kk = 0; kk < 4; ++kk) {
+                const float* grow = G + (size_t)(k0 + 4 * kk + lg) * n;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int ib = wave + 4 * u;
-                if (ib < nib) {
-                    const float a = grow[16 * ib + l16];     // G[16ib + l16][k0 + lg] by symmetry
+                for (int u = 0; u < 8; ++u) {
+                    const int ib = wave + 4 * u;
+                    ga[kk][u] = ib < nib ? grow[16 * ib + l16] : 0.f;   // G[16ib + l16][k] by symmetry
+                }
+            }
 #pragma unroll
-                    for (int cb = 0; cb < CB; ++cb)
-                        acc[u][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv[cb], acc[u][cb], 0, 0, 0);
+            for (int kk = 0; kk < 4; ++kk) {
+                float bv[CB];
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) bv[cb] = Zs[(k0 + 4 * kk + lg) * RP + 16 * cb + l16];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    if (wave + 4 * u < nib) {
+#pragma unroll
+                        for (int cb = 0; cb < CB; ++cb)
+                            acc[u][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ga[kk][u], bv[cb],
+                                                                              acc[u][cb], 0, 0, 0);
+                    }
                 }
             }
         }
