@@ -61,6 +61,11 @@ ATTN_CASES = [
     (1, 16, 8, 300, 3, [0, 0, 0]),            # 6 rows
     (2, 32, 8, 1500, 4, [0, 1, 0, 1]),        # two slots in one call
     (1, 8, 8, 200, 20, [0] * 20),             # 20 layers, MHA: two launches
+    # 128-255 slabs: two workgroups per slab split the value channels
+    (16, 32, 8, 1031, 1, [0]),
+    (33, 16, 4, 300, 1, [1]),                 # 132 slabs: part of the last group idle
+    (16, 32, 8, 500, 4, [0, 0, 0, 0]),        # grouped, 16 rows
+    (16, 32, 8, 400, 8, [1] * 8),             # 32 rows (two column blocks)
 ]
 
 
@@ -93,12 +98,13 @@ def test_decode_attn_f32_tiny(T):
     assert np.abs(to_np(lse) - ref_lse).max() <= 1e-5 * max(1.0, np.abs(ref_lse).max())
 
 
-@pytest.mark.parametrize("T0", [95, 96, 127])      # appended row ends / starts / fills a tile
+@pytest.mark.parametrize("nb", [2, 16])            # 16 x 8 slabs: value-channel halves
+@pytest.mark.parametrize("T0", [95, 96, 127, 200])  # appended row ends / starts / fills a tile
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_decode_attn_append(dtype, T0):
-    say("decode append", dtype, T0)
-    nb, hkv, hq = 2, 8 if dtype == torch.bfloat16 else 2, 32 if dtype == torch.bfloat16 else 8
-    cache = make_cache(2, nb, hkv, T0, t_cap=192, dtype=dtype, seed=3)
+def test_decode_attn_append(dtype, T0, nb):
+    say("decode append", dtype, T0, nb)
+    hkv, hq = 8 if dtype == torch.bfloat16 else 2, 32 if dtype == torch.bfloat16 else 8
+    cache = make_cache(2, nb, hkv, T0, t_cap=256, dtype=dtype, seed=3)
     kn = kvc_synth.queries((nb, hkv, 128), dtype=dtype, device=DEV, seed=11)
     vn = kvc_synth.queries((nb, hkv, 128), dtype=dtype, device=DEV, seed=12) * 3
     K0, V0 = slab_np(cache, 1)

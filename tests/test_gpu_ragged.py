@@ -62,6 +62,9 @@ ATTN_CASES = [
     (torch.bfloat16, 40, 8, 4, [3, 1, 0, 2], [31, 8448, 2, 700], [1]),   # many splits
     (torch.bfloat16, 16, 4, 5, [1, 7, -1, 3], [300, 50, 60, 0], [0]),    # bad entries: empty
     (torch.float32, 8, 2, 3, [2, 0, 1], [1024, 65, 0], [0]),
+    # 17 x 8 slabs: two workgroups per slab split the value channels
+    (torch.bfloat16, 32, 8, 17, [16, 3, 0, 5, 9, 1, 2, 4, 6, 7, 8, 10, 11, 12, 13, -1, 15],
+     [400, 0, 1, 33, 256, 257, 31, 32, 100, 7, 399, 64, 65, 200, 150, 90, 12], [1]),
 ]
 
 
