@@ -375,6 +375,8 @@ def xkv_leg(args, cfg, qpool, knew, vnew, steps, warm=3):
     o_t = torch.empty((L, nb, hq, 128), device=dev)
     l_t = torch.empty((L, nb, hq), device=dev)
     out = torch.empty((L, nb, hq, 128), device=dev)
+    ws_x = torch.zeros(kvc.kvc_xkv_decode_ws_bytes(stores[0], hq, n_sel), dtype=torch.uint8,
+                       device=dev)
 
     def step(s):
         tail.t_len += 1
@@ -383,7 +385,7 @@ def xkv_leg(args, cfg, qpool, knew, vnew, steps, warm=3):
             kvc.kvc_decode_attn(tail, qpool[l, s], [l], o_t[l], l_t[l], ws_t, k_new=knew[s, sl],
                                 v_new=vnew[s, sl], append_slot=l, n_q_heads=hq)
             kvc.kvc_xkv_decode_attn(stores[l // W], l % W, qpool[l, s], out[l], None,
-                                    n_select=n_sel, o_in=o_t[l], lse_in=l_t[l])
+                                    n_select=n_sel, o_in=o_t[l], lse_in=l_t[l], ws=ws_x)
 
     for s in range(warm):
         step(s)
@@ -415,7 +417,7 @@ def xkv_leg(args, cfg, qpool, knew, vnew, steps, warm=3):
                 sr_bytes_per_call=sr_bytes,
                 full_attention_us_per_layer=round(1e3 * base, 2),
                 full_attention_ms_per_step=round(L * base, 3),
-                kernel="per layer: attn_bf16_kernel over the tail (+ merge) and xkv_decode<64>",
+                kernel="per layer: attn_bf16_kernel over the tail (+ merge), then xkv_scores, xkv_attend, xkv_output",
                 data="synthetic cross-layer low-rank caches (rank-48 shared basis + 0.1 noise)")
 
 

@@ -29,7 +29,8 @@ EXPORTS = (
     "kvc_score_ws_bytes", "kvc_score", "kvc_select_ws_bytes", "kvc_select", "kvc_select_seq",
     "kvc_compact", "kvc_philox_words", "kvc_dkv_ws_bytes", "kvc_dkv_score",
     "kvc_gaussian_bf16", "kvc_q8_quantize", "kvc_q8_append", "kvc_q8_decode_attn_ws_bytes",
-    "kvc_q8_decode_attn", "kvc_xkv_factor_ws_bytes", "kvc_xkv_factor", "kvc_xkv_decode_attn",
+    "kvc_q8_decode_attn", "kvc_xkv_factor_ws_bytes", "kvc_xkv_factor", "kvc_xkv_decode_ws_bytes",
+    "kvc_xkv_decode_attn",
 )
 
 
@@ -113,7 +114,9 @@ def lib():
                                     vp], i32),
             "kvc_xkv_factor_ws_bytes": ([xp, szp], i32),
             "kvc_xkv_factor": ([cp, i32, i32, ctypes.c_uint64, xp, vp, sz, vp], i32),
-            "kvc_xkv_decode_attn": ([xp, i32, vp, i32, f32, i32, vp, vp, vp, vp, vp, vp], i32),
+            "kvc_xkv_decode_ws_bytes": ([xp, i32, i32, szp], i32),
+            "kvc_xkv_decode_attn": ([xp, i32, vp, i32, f32, i32, vp, vp, vp, vp, vp, vp, sz, vp],
+                                    i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -562,12 +565,23 @@ def kvc_xkv_factor(cache, slot0, store, ws, iters=12, seed=0, stream=None):
            "kvc_xkv_factor")
 
 
+def kvc_xkv_decode_ws_bytes(store, n_q_heads, n_select=256):
+    x = store.desc()
+    out = ctypes.c_size_t()
+    _check(lib().kvc_xkv_decode_ws_bytes(ctypes.byref(x), n_q_heads, n_select, ctypes.byref(out)),
+           "kvc_xkv_decode_ws_bytes")
+    return out.value
+
+
 def kvc_xkv_decode_attn(store, layer, q, out, lse=None, n_select=256, scale=0.0, o_in=None,
-                        lse_in=None, selected=None, n_q_heads=None, stream=None):
+                        lse_in=None, selected=None, n_q_heads=None, ws=None, stream=None):
     """q: bf16 [nb][Hq][d]; out float32 like q (o_in / lse_in: a second part
-    to merge, e.g. attention over rows appended after the factorisation)."""
+    to merge, e.g. attention over rows appended after the factorisation);
+    ws: kvc_xkv_decode_ws_bytes bytes of device memory."""
     x = store.desc()
     hq = q.shape[-2] if n_q_heads is None else n_q_heads
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().kvc_xkv_decode_attn(ctypes.byref(x), layer, _ptr(q), hq, float(scale), n_select,
                                      _ptr(o_in), _ptr(lse_in), _ptr(out), _ptr(lse),
-                                     _ptr(selected), _stream(stream)), "kvc_xkv_decode_attn")
+                                     _ptr(selected), _ptr(ws), ws_bytes, _stream(stream)),
+           "kvc_xkv_decode_attn")

@@ -302,11 +302,38 @@ XkvWs xkv_ws(const kvc_xkv* x) {
     return w;
 }
 
-size_t xkv_decode_lds(const kvc_xkv* x, int g, int n_select) {
-    const size_t nch = ((size_t)x->t_len + XKV_CHUNK - 1) / XKV_CHUNK;
-    const size_t ksel = std::min<size_t>((size_t)n_select, nch);
-    return (XKV_MAXG * (size_t)x->rank + nch + ksel + ksel * XKV_CHUNK * g +
-            8 * XKV_MAXG * (x->rank + 1)) * 4;   // 8 waves' value partials
+// Decode launch shape: chunk splits for the score launch and kept-row splits
+// for the attention launch, so that each launch has about XKV_TARGET_WGS
+// workgroups without splits smaller than XKV_MIN_CHUNKS chunks or
+// XKV_MIN_ROWS rows.
+constexpr int XKV_TARGET_WGS = 256;
+constexpr int XKV_MIN_CHUNKS = 128;
+constexpr int XKV_MIN_ROWS = 256;
+
+struct XkvDecodePlan {
+    int nch, ksel, nscore, cps, nattend, rpw;
+    size_t keys_off, qt_off, part_off, ws_bytes, lds;
+};
+
+XkvDecodePlan plan_xkv_decode(const kvc_xkv* x, int g, int n_select) {
+    XkvDecodePlan pl;
+    const long long slabs = std::max<long long>(1, (long long)x->nb * x->n_kv_heads);
+    const int want = (int)std::max<long long>(1, (XKV_TARGET_WGS + slabs - 1) / slabs);
+    pl.nch = (x->t_len + XKV_CHUNK - 1) / XKV_CHUNK;
+    pl.ksel = std::min(n_select, pl.nch);
+    const int nrows = pl.ksel * XKV_CHUNK;
+    pl.nscore = std::max(1, std::min(want, (pl.nch + XKV_MIN_CHUNKS - 1) / XKV_MIN_CHUNKS));
+    pl.cps = std::max(1, (pl.nch + pl.nscore - 1) / pl.nscore);
+    pl.nattend = std::max(1, std::min({want, XKV_MAX_ATTEND, (nrows + XKV_MIN_ROWS - 1) / XKV_MIN_ROWS}));
+    pl.rpw = std::max(1, (nrows + pl.nattend - 1) / pl.nattend);
+    const size_t sl = (size_t)x->nb * x->n_kv_heads;
+    pl.keys_off = 0;
+    pl.qt_off = align_up(sl * pl.nch * 4, 256);
+    pl.part_off = pl.qt_off + align_up(sl * XKV_MAXG * x->rank * 4, 256);
+    pl.ws_bytes = pl.part_off + sl * pl.nattend * XKV_MAXG * (x->rank + 2) * 4;
+    // attention launch: keys, kept chunks, logits of its rows, 8 waves' value partials
+    pl.lds = ((size_t)pl.nch + pl.ksel + (size_t)pl.rpw * g + 8 * XKV_MAXG * (x->rank + 1)) * 4;
+    return pl;
 }
 
 }  // namespace
@@ -883,9 +910,22 @@ int kvc_xkv_factor(const kvc_cache* c, int slot0, int iters, uint64_t seed, cons
     return hip_status();
 }
 
+int kvc_xkv_decode_ws_bytes(const kvc_xkv* x, int n_q_heads, int n_select, size_t* bytes) {
+    int st = check_xkv(x);
+    if (st) return st;
+    if (!bytes) return KVC_EINVAL;
+    if (n_q_heads < 1 || n_q_heads % x->n_kv_heads) return KVC_EINVAL;
+    const int g = n_q_heads / x->n_kv_heads;
+    if (g > XKV_MAXG) return KVC_EINVAL;
+    if (n_select < 1 || (long long)n_select * XKV_CHUNK * g > 16384) return KVC_EINVAL;
+    *bytes = plan_xkv_decode(x, g, n_select).ws_bytes;
+    return KVC_OK;
+}
+
 int kvc_xkv_decode_attn(const kvc_xkv* x, int layer, const void* q, int n_q_heads, float scale,
                         int n_select, const float* o_in, const float* lse_in, float* out,
-                        float* lse, int32_t* selected, kvc_stream_t stream) {
+                        float* lse, int32_t* selected, void* ws, size_t ws_bytes,
+                        kvc_stream_t stream) {
     int st = check_xkv(x);
     if (st) return st;
     if (layer < 0 || layer >= x->window) return KVC_EINVAL;
@@ -900,8 +940,9 @@ int kvc_xkv_decode_attn(const kvc_xkv* x, int layer, const void* q, int n_q_head
     if ((lse && !aligned4(lse)) || (o_in && (!aligned4(o_in) || !aligned4(lse_in))) ||
         (selected && !aligned4(selected)))
         return KVC_EALIGN;
-    const size_t lds = xkv_decode_lds(x, g, n_select);
-    if (lds > XKV_LDS_LIMIT) return KVC_EINVAL;
+    const XkvDecodePlan pl = plan_xkv_decode(x, g, n_select);
+    if (pl.lds > XKV_LDS_LIMIT) return KVC_EINVAL;
+    if (!ws || ws_bytes < pl.ws_bytes || !aligned16(ws)) return KVC_EWORKSPACE;
     if (scale == 0.f) scale = 1.0f / sqrtf((float)KVC_HEAD_DIM);
     XkvDecodeLaunch p;
     memset(&p, 0, sizeof(p));
@@ -927,7 +968,14 @@ int kvc_xkv_decode_attn(const kvc_xkv* x, int layer, const void* q, int n_q_head
     p.out = out;
     p.lse = lse;
     p.selected = selected;
-    if (launch_xkv_decode(p, lds, (hipStream_t)stream) != hipSuccess) return KVC_EHIP;
+    p.nscore = pl.nscore;
+    p.cps = pl.cps;
+    p.nattend = pl.nattend;
+    p.rpw = pl.rpw;
+    p.ws_keys = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + pl.keys_off);
+    p.ws_qt = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.qt_off);
+    p.ws_part = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.part_off);
+    if (launch_xkv_decode(p, pl.lds, (hipStream_t)stream) != hipSuccess) return KVC_EHIP;
     return hip_status();
 }
 

@@ -18,6 +18,7 @@ constexpr int SCORE_MAX_TPS = 16;     // tiles per score-statistics workgroup
 constexpr int SCORE_QPITCH = 136;     // bf16 per window-query row staged in LDS (272 bytes)
 constexpr int CU_COUNT = 256;         // compute units of the part
 constexpr int LDS_PER_CU = 160 * 1024;
+constexpr int XKV_MAX_ATTEND = 64;  // kept-row splits per (b, j) of a cross-layer decode
 
 // LDS of one bf16 score-pass workgroup: the window queries (16-row blocks)
 // plus one float (lse term) and one int (last visible row) per row.
@@ -197,6 +198,11 @@ struct XkvDecodeLaunch {
     float* out;
     float* lse;             // may be null
     int32_t* selected;      // [nb][hkv][n_select] or null
+    int nscore, cps;        // chunk splits per (b, j) and chunks per split
+    int nattend, rpw;       // kept-row splits per (b, j) and rows per split
+    uint32_t* ws_keys;      // [nb][hkv][nch] chunk score keys
+    float* ws_qt;           // [nb][hkv][8][rank] q~
+    float* ws_part;         // [nb][hkv][nattend][8][rank + 2] partials (a~, max, z)
 };
 
 // Host-side launchers (defined next to their kernels).  Each returns

@@ -33,7 +33,7 @@ constexpr int NWV = NT / WAVE;
 constexpr uint32_t EXCLUDED = 0xFFFFFFFFu;   // above every float key
 constexpr int LDS_KEYS = 36 * 1024;           // 144 KB of keys
 
-using SelectSmem = RadixSmem<NT>;
+using SelectSmem = RadixSmem<NT, 8>;   // 8 histogram copies: range keys share their top digit
 
 __device__ __forceinline__ uint32_t range_key(float r) {
     // larger range first: invert the (non-negative) float's bits

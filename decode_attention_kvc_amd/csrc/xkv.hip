@@ -23,14 +23,19 @@
 //  3. xkv_project: A = X V on MFMA with V^T as bf16 in LDS, stored as bf16,
 //     and for keys the landmark of every 8-row chunk: the mean of its stored
 //     A rows.
-// Decode (xkv_decode), one workgroup per (b, j):
-//  q~_h = B_l q_h (r numbers per head); chunk score max_h q~_h . landmark;
-//  exact top-k of the chunks (radix select, ties to the lower chunk); then
-//  attention over the kept rows in the rank space: q_h . (A_t B_l) =
-//  q~_h . A_t and sum_t p_t A_t B_l = (sum_t p_t A_t) B_l, so the selected
-//  rows are rebuilt implicitly and never written.  An optional second part
-//  (rows appended after the factorisation, attended separately) is merged
-//  with log-sum-exp weights.
+// Decode, three launches so that the whole chip streams the landmarks and
+// the kept rows (one workgroup per (b, j) would leave half the CUs idle):
+//  1. xkv_scores, (chunk split, b, j): q~_h = B_l q_h (r numbers per head)
+//     and the chunk scores max_h q~_h . landmark;
+//  2. xkv_attend, (row split, b, j): exact top-k of the chunks (radix
+//     select, ties to the lower chunk; each split repeats it), then attention
+//     over the split's share of the kept rows in the rank space:
+//     q_h . (A_t B_l) = q~_h . A_t and sum_t p_t A_t B_l = (sum_t p_t A_t)
+//     B_l, so the selected rows are rebuilt implicitly and never written;
+//  3. xkv_output, (b, j): the splits' partials merge with log-sum-exp
+//     weights, the output is projected by B_l^V, and an optional second part
+//     (rows appended after the factorisation, attended separately) is merged
+//     the same way.
 #include "common.h"
 #include "kvc_internal.h"
 #include "philox.h"
@@ -47,6 +52,7 @@ constexpr int VPITCH = XT + 2;  // bf16 per channel in a wave's value transpose 
 constexpr int MAXG = 8;         // query heads per KV head on the decode path
 constexpr int XNT = 512;        // threads of a decode workgroup (two waves per SIMD)
 constexpr int XNW = XNT / WAVE;
+static_assert(XNT == 4 * D, "the output step maps one thread to a (head, channel) pair");
 
 __device__ __forceinline__ bf16x8 as_bf(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
@@ -437,81 +443,128 @@ __device__ __forceinline__ void rank_dots(const u32x4& w, const float (&qr)[G][8
     }
 }
 
-template <int R, int G>
-__global__ __launch_bounds__(XNT) void xkv_decode(XkvDecodeLaunch p) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ RadixSmem<XNT> rs;
-    __shared__ float red[XNW][MAXG];
-    __shared__ float hm[MAXG], hz[MAXG];
-    constexpr int LPR = R / 8;             // lanes per rank-space row
-    constexpr int NGRP = XNT / LPR;        // rows per block pass
-    constexpr int CW = G <= 4 ? 16 : 8;    // value phase: columns per lane
-    constexpr int CG = R / CW;             //              column groups
-    constexpr int RGW = WAVE / CG;         //              row groups per wave
-    constexpr int RGS = XNW * RGW;         //              row groups per block
-    const int j = blockIdx.x, b = blockIdx.y;
-    const int slab = b * p.hkv + j, g = p.g, n = p.window * D;
-    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
-    const int sub = lane % LPR, grp = tid / LPR;
-    const int T = p.t_len, nch = (T + CHUNK - 1) / CHUNK;
-    const int ksel = min(p.n_select, nch), nrows = ksel * CHUNK;
-    float* qt = reinterpret_cast<float*>(smem);                  // [MAXG][R]
-    uint32_t* keys = reinterpret_cast<uint32_t*>(qt + MAXG * R); // [nch]
-    int32_t* sel = reinterpret_cast<int32_t*>(keys + nch);       // [ksel]
-    float* lgt = reinterpret_cast<float*>(sel + ksel);           // [nrows][g]
-    float* part = lgt + (size_t)nrows * g;                       // [XNW][MAXG][R + 1]
-
-    // q~_h = B_l q_h: B_l^T is rows layer*128 .. of the key basis [n][R].
-    // The queries go through LDS (part is free until the value reduction).
+// q~_h = B_l q_h for the g heads of one (b, j) into LDS qt [MAXG][R] (heads
+// past g: zero); qs is scratch for the queries as float [g][D].
+template <int R>
+__device__ __forceinline__ void rank_queries(const XkvDecodeLaunch& p, int slab, int b, int j,
+                                             float* qs, float* qt) {
+    const int tid = threadIdx.x, g = p.g, n = p.window * D;
     const float* BK = p.bk + (size_t)slab * n * R + (size_t)p.layer * D * R;
-    {
-        const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)b * p.hq + j * g) * D;
-        for (int x = tid; x < g * D; x += XNT) part[x] = bf16_to_f32(q[x]);
-        __syncthreads();
-        for (int x = tid; x < MAXG * R; x += XNT) {
-            const int h = x / R, c = x % R;
-            float a0 = 0.f, a1 = 0.f;
-            if (h < g) {
-                const float* qs = part + h * D;
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)b * p.hq + j * g) * D;
+    for (int x = tid; x < g * D; x += XNT) qs[x] = bf16_to_f32(q[x]);
+    __syncthreads();
+    for (int x = tid; x < MAXG * R; x += XNT) {
+        const int h = x / R, c = x % R;
+        float a0 = 0.f, a1 = 0.f;
+        if (h < g) {
+            const float* qh = qs + h * D;
 #pragma unroll 16
-                for (int i = 0; i < D; i += 2) {
-                    a0 = fmaf(qs[i], BK[i * R + c], a0);
-                    a1 = fmaf(qs[i + 1], BK[(i + 1) * R + c], a1);
-                }
+            for (int i = 0; i < D; i += 2) {
+                a0 = fmaf(qh[i], BK[i * R + c], a0);
+                a1 = fmaf(qh[i + 1], BK[(i + 1) * R + c], a1);
             }
-            qt[h * R + c] = a0 + a1;     // heads past g: zero
         }
+        qt[h * R + c] = a0 + a1;
     }
     __syncthreads();
-    float qr[G][8];                      // this lane's 8 columns of every q~_h
+}
+
+// Decode, step 1: grid (chunk split, j, b).  q~ (the first split also keeps
+// it in the workspace for step 2) and the score keys of this split's chunks:
+// max over the heads of q~_h . landmark, LPR lanes per chunk, UNR chunks in
+// flight per lane group.
+template <int R, int G>
+__global__ __launch_bounds__(XNT) void xkv_scores(XkvDecodeLaunch p) {
+    __shared__ float qs[MAXG * D];
+    __shared__ float qt[MAXG * R];
+    constexpr int LPR = R / 8;
+    constexpr int NGRP = XNT / LPR;
+    constexpr int UNR = G <= 4 ? 16 : 8;
+    const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+    const int slab = b * p.hkv + j, g = p.g;
+    const int tid = threadIdx.x, lane = tid % WAVE;
+    const int sub = lane % LPR, grp = tid / LPR;
+    const int nch = (p.t_len + CHUNK - 1) / CHUNK;
+    const int c0 = s * p.cps, c1 = min(nch, c0 + p.cps);
+    rank_queries<R>(p, slab, b, j, qs, qt);
+    if (s == 0)
+        for (int x = tid; x < MAXG * R; x += XNT) p.ws_qt[(size_t)slab * MAXG * R + x] = qt[x];
+    float qr[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) qr[h][e] = qt[h * R + 8 * sub + e];
-
-    // chunk scores: max over the heads of q~_h . landmark; LPR lanes per
-    // chunk, UNR chunks in flight per lane group
-    constexpr int UNR = G <= 4 ? 16 : 8;     // loads in flight per lane (registers)
     const uint16_t* L = reinterpret_cast<const uint16_t*>(p.lk) + (size_t)slab * (p.x_tcap / CHUNK) * R;
-    for (int base = 0; base < nch; base += UNR * NGRP) {
+    uint32_t* keys = p.ws_keys + (size_t)slab * nch;
+    for (int base = c0; base < c1; base += UNR * NGRP) {
         u32x4 w[UNR];
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
             const int ch = base + u * NGRP + grp;
-            w[u] = ch < nch ? load16(L + (size_t)ch * R + 8 * sub) : u32x4{0u, 0u, 0u, 0u};
+            w[u] = ch < c1 ? load16(L + (size_t)ch * R + 8 * sub) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
             const int ch = base + u * NGRP + grp;
-            float s[G];
-            rank_dots<R, G>(w[u], qr, s);
+            float sc[G];
+            rank_dots<R, G>(w[u], qr, sc);
             float best = -INFINITY;
 #pragma unroll
             for (int h = 0; h < G; ++h)
-                if (h < g) best = fmaxf(best, s[h]);
-            if (sub == 0 && ch < nch) keys[ch] = desc_key(best);
+                if (h < g) best = fmaxf(best, sc[h]);
+            if (sub == 0 && ch < c1) keys[ch] = desc_key(best);
         }
     }
+}
+
+// Decode, step 2: grid (row split, j, b).  Every workgroup of a (b, j)
+// selects the same ksel chunks from the keys (exact radix select, ties to
+// the lower chunk; the first workgroup reports them), then takes its share
+// [r0, r1) of the kept rows: logits in the rank space, its own maximum per
+// head, and a~_h = sum_t p_t,h A^V_t with z_h = sum_t p_t,h; the partial
+// (a~, max, z) goes to the workspace.
+template <int R, int G>
+__global__ __launch_bounds__(XNT) void xkv_attend(XkvDecodeLaunch p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ RadixSmem<XNT, 8> rs;
+    __shared__ float red[XNW][MAXG];
+    __shared__ float hm[MAXG];
+    constexpr int LPR = R / 8;             // lanes per rank-space row
+    constexpr int NGRP = XNT / LPR;        // rows per block pass
+    constexpr int UNR = G <= 4 ? 16 : 8;   // logit rows in flight per lane group
+    constexpr int CW = G <= 4 ? 16 : 8;    // value phase: columns per lane
+    constexpr int CG = R / CW;             //              column groups
+    constexpr int RGW = WAVE / CG;         //              row groups per wave
+    constexpr int RGS = XNW * RGW;         //              row groups per block
+    const int a = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+    const int slab = b * p.hkv + j, g = p.g;
+    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+    const int sub = lane % LPR, grp = tid / LPR;
+    const int T = p.t_len, nch = (T + CHUNK - 1) / CHUNK;
+    const int ksel = min(p.n_select, nch), nrows = ksel * CHUNK;
+    const int r0 = min(nrows, a * p.rpw), r1 = min(nrows, r0 + p.rpw);
+    uint32_t* keys = reinterpret_cast<uint32_t*>(smem);          // [nch]
+    int32_t* sel = reinterpret_cast<int32_t*>(keys + nch);       // [ksel]
+    float* lgt = reinterpret_cast<float*>(sel + ksel);           // [rpw][g]
+    float* part = lgt + (size_t)p.rpw * g;                       // [XNW][MAXG][R + 1]
+    float* out_part = p.ws_part + ((size_t)slab * p.nattend + a) * MAXG * (R + 2);
+
+    if (r0 >= r1 && !(a == 0 && p.selected)) {
+        // no rows here and nothing to report: an empty partial
+        for (int h = tid; h < MAXG; h += XNT) {
+            out_part[h * (R + 2) + R] = -INFINITY;
+            out_part[h * (R + 2) + R + 1] = 0.f;
+        }
+        return;
+    }
+    const float* qtg = p.ws_qt + (size_t)slab * MAXG * R;
+    float qr[G][8];                      // this lane's 8 columns of every q~_h
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qr[h][e] = qtg[h * R + 8 * sub + e];
+    const uint32_t* kg = p.ws_keys + (size_t)slab * nch;
+    for (int ch = tid; ch < nch; ch += XNT) keys[ch] = kg[ch];
     __syncthreads();
 
     // the ksel best chunks, ascending (all of them when there are fewer):
@@ -545,39 +598,39 @@ __global__ __launch_bounds__(XNT) void xkv_decode(XkvDecodeLaunch p) {
         for (int ch = tid; ch < nch; ch += XNT) sel[ch] = ch;
     }
     __syncthreads();
-    if (p.selected)
+    if (a == 0 && p.selected)
         for (int x = tid; x < p.n_select; x += XNT)
             p.selected[(size_t)slab * p.n_select + x] = x < ksel ? sel[x] : -1;
 
-    // logits of the kept rows in the rank space (LPR lanes per row, UNR
-    // rows in flight), and the per-head maximum
+    // logits of this workgroup's rows in the rank space (LPR lanes per row,
+    // UNR rows in flight) and its maximum per head
     const uint16_t* AK = reinterpret_cast<const uint16_t*>(p.ak) + (size_t)slab * p.x_tcap * R;
     const uint16_t* AV = reinterpret_cast<const uint16_t*>(p.av) + (size_t)slab * p.x_tcap * R;
     {
         float mh[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) mh[h] = -INFINITY;
-        for (int base = 0; base < nrows; base += UNR * NGRP) {
+        for (int base = r0; base < r1; base += UNR * NGRP) {
             u32x4 w[UNR];
             int tr[UNR];
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
                 const int r = base + u * NGRP + grp;
-                tr[u] = r < nrows ? sel[r / CHUNK] * CHUNK + r % CHUNK : T;
+                tr[u] = r < r1 ? sel[r / CHUNK] * CHUNK + r % CHUNK : T;
                 w[u] = tr[u] < T ? load16(AK + (size_t)tr[u] * R + 8 * sub) : u32x4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
                 const int r = base + u * NGRP + grp;
-                float s[G];
-                rank_dots<R, G>(w[u], qr, s);
-                if (r < nrows) {
+                float sc[G];
+                rank_dots<R, G>(w[u], qr, sc);
+                if (r < r1) {
 #pragma unroll
                     for (int h = 0; h < G; ++h) {
                         if (h < g) {
-                            const float l = tr[u] < T ? s[h] * p.scale : -INFINITY;
+                            const float l = tr[u] < T ? sc[h] * p.scale : -INFINITY;
                             mh[h] = fmaxf(mh[h], l);
-                            if (sub == 0) lgt[r * g + h] = l;
+                            if (sub == 0) lgt[(r - r0) * g + h] = l;
                         }
                     }
                 }
@@ -597,9 +650,9 @@ __global__ __launch_bounds__(XNT) void xkv_decode(XkvDecodeLaunch p) {
         __syncthreads();
     }
 
-    // a~_h = sum_t p_t,h A^V_t and z_h = sum_t p_t,h with p = exp(l - max):
-    // lane (row group, CW-column group), 16-byte value reads, VR rows in
-    // flight; then sums over the row groups (lanes, then waves)
+    // a~ and z over this workgroup's rows: lane (row group, CW-column
+    // group), 16-byte value reads, VR rows in flight; then sums over the row
+    // groups (lanes, then waves)
     {
         const int cg = lane % CG, rgl = lane / CG;
         const int rg = wave * RGW + rgl;
@@ -615,13 +668,13 @@ __global__ __launch_bounds__(XNT) void xkv_decode(XkvDecodeLaunch p) {
         }
         constexpr int VR = 8;
         constexpr int NL = CW / 8;                 // 16-byte loads per row and lane
-        for (int base = rg; base < nrows; base += VR * RGS) {
+        for (int base = r0 + rg; base < r1; base += VR * RGS) {
             u32x4 w[VR][NL];
             int tr[VR];
 #pragma unroll
             for (int u = 0; u < VR; ++u) {
                 const int r = base + u * RGS;
-                tr[u] = r < nrows ? sel[r / CHUNK] * CHUNK + r % CHUNK : T;
+                tr[u] = r < r1 ? sel[r / CHUNK] * CHUNK + r % CHUNK : T;
                 const bool ok = tr[u] < T;
 #pragma unroll
                 for (int q2 = 0; q2 < NL; ++q2)
@@ -635,7 +688,7 @@ __global__ __launch_bounds__(XNT) void xkv_decode(XkvDecodeLaunch p) {
 #pragma unroll
                     for (int h = 0; h < G; ++h) {
                         if (h < g) {
-                            const float pr = expf(lgt[r * g + h] - mx[h]);
+                            const float pr = expf(lgt[(r - r0) * g + h] - mx[h]);
                             zs[h] += pr;
 #pragma unroll
                             for (int q2 = 0; q2 < NL; ++q2)
@@ -671,35 +724,74 @@ __global__ __launch_bounds__(XNT) void xkv_decode(XkvDecodeLaunch p) {
         const int h = x / (R + 1), c = x % (R + 1);
         float s4 = 0.f;
         for (int w2 = 0; w2 < XNW; ++w2) s4 += part[(w2 * MAXG + h) * (R + 1) + c];
-        if (c < R) qt[h * R + c] = s4;   // q~ is no longer needed
-        else hz[h] = s4;
+        out_part[h * (R + 2) + (c < R ? c : R + 1)] = s4;
+        if (c == R) out_part[h * (R + 2) + R] = hm[h];
+    }
+}
+
+// Decode, step 3: grid (j, b).  The row splits' partials merge with
+// log-sum-exp weights; o_h = B_l^V a~_h / z_h, merged with the second part
+// if given.  Thread (h, i) owns output channel i of head h; its row of B_l^V
+// is loaded first, so that read overlaps the merge.
+template <int R>
+__global__ __launch_bounds__(XNT) void xkv_output(XkvDecodeLaunch p) {
+    __shared__ float at[MAXG * R];
+    __shared__ float hz[MAXG], hmx[MAXG];
+    __shared__ float wts[XKV_MAX_ATTEND * MAXG];
+    const int j = blockIdx.x, b = blockIdx.y;
+    const int slab = b * p.hkv + j, g = p.g, n = p.window * D, tid = threadIdx.x;
+    const int na = p.nattend;
+    const float* P = p.ws_part + (size_t)slab * na * MAXG * (R + 2);
+    const float* BV = p.bv + (size_t)slab * n * R + (size_t)p.layer * D * R;
+    const int oh = tid / D, oi = tid % D;      // XNT = 4 * D: heads oh, oh + 4
+    f32x4 bvv[R / 4];
+#pragma unroll
+    for (int c4 = 0; c4 < R / 4; ++c4) bvv[c4] = *reinterpret_cast<const f32x4*>(BV + oi * R + 4 * c4);
+    for (int x = tid; x < na * MAXG; x += XNT) wts[x] = P[(size_t)x * (R + 2) + R];
+    __syncthreads();
+    if (tid < MAXG) {
+        float M = -INFINITY;
+        for (int a = 0; a < na; ++a) M = fmaxf(M, wts[a * MAXG + tid]);
+        for (int a = 0; a < na; ++a) {
+            const float ma = wts[a * MAXG + tid];
+            wts[a * MAXG + tid] = ma == -INFINITY ? 0.f : expf(ma - M);   // a split without rows
+        }
+        hmx[tid] = M;
     }
     __syncthreads();
-
-    // o_h = B_l^V a~_h / z_h, merged with the second part if given
-    const float* BV = p.bv + (size_t)slab * n * R + (size_t)p.layer * D * R;
-    for (int x = tid; x < g * D; x += XNT) {
-        const int h = x / D, i = x % D;
+    for (int x = tid; x < g * (R + 1); x += XNT) {
+        const int h = x / (R + 1), c = x % (R + 1);
+        float sum = 0.f;
+#pragma unroll 4
+        for (int a = 0; a < na; ++a) {
+            const float w = wts[a * MAXG + h];
+            const float v = P[((size_t)a * MAXG + h) * (R + 2) + (c < R ? c : R + 1)];
+            sum = w == 0.f ? sum : fmaf(w, v, sum);
+        }
+        if (c < R) at[h * R + c] = sum;
+        else hz[h] = sum;
+    }
+    __syncthreads();
+    for (int h = oh; h < g; h += XNT / D) {
+        const int i = oi;
         float o = 0.f;
 #pragma unroll
-        for (int c4 = 0; c4 < R / 4; ++c4) {
-            const f32x4 bvv = *reinterpret_cast<const f32x4*>(BV + i * R + 4 * c4);
+        for (int c4 = 0; c4 < R / 4; ++c4)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o = fmaf(bvv[e], qt[h * R + 4 * c4 + e], o);
-        }
-        const float z = hz[h];
-        float l1 = z > 0.f ? hm[h] + logf(z) : -INFINITY;
-        o = z > 0.f ? o / z : 0.f;
+            for (int e = 0; e < 4; ++e) o = fmaf(bvv[c4][e], at[h * R + 4 * c4 + e], o);
+        const float zz = hz[h];
+        float l1 = zz > 0.f ? hmx[h] + logf(zz) : -INFINITY;
+        o = zz > 0.f ? o / zz : 0.f;
         const size_t row = (size_t)b * p.hq + j * g + h;
         if (p.o_in) {
             const float l2 = p.lse_in[row];
             const float o2 = p.o_in[row * D + i];
-            const float m = fmaxf(l1, l2);
-            if (m != -INFINITY) {
-                const float w1 = (l1 == -INFINITY) ? 0.f : expf(l1 - m);
-                const float w2 = (l2 == -INFINITY) ? 0.f : expf(l2 - m);
+            const float mm = fmaxf(l1, l2);
+            if (mm != -INFINITY) {
+                const float w1 = (l1 == -INFINITY) ? 0.f : expf(l1 - mm);
+                const float w2 = (l2 == -INFINITY) ? 0.f : expf(l2 - mm);
                 o = (o * w1 + o2 * w2) / (w1 + w2);
-                l1 = m + logf(w1 + w2);
+                l1 = mm + logf(w1 + w2);
             }
         }
         p.out[row * D + i] = o;
@@ -743,17 +835,22 @@ hipError_t launch_xkv_factor(const XkvLaunch& p, hipStream_t st) {
 }
 
 hipError_t launch_xkv_decode(const XkvDecodeLaunch& p, size_t lds, hipStream_t st) {
-    const dim3 grid(p.hkv, p.nb);
-    auto go = [&](auto kern) {
+    const dim3 sgrid(p.nscore, p.hkv, p.nb), agrid(p.nattend, p.hkv, p.nb), ogrid(p.hkv, p.nb);
+    auto go = [&](auto score, auto attend, auto output) {
         if (lds > 64 * 1024 &&
-            hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+            hipFuncSetAttribute(reinterpret_cast<const void*>(attend),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
             return hipErrorInvalidValue;
-        hipLaunchKernelGGL(kern, grid, dim3(XNT), lds, st, p);
+        hipLaunchKernelGGL(score, sgrid, dim3(XNT), 0, st, p);
+        hipLaunchKernelGGL(attend, agrid, dim3(XNT), lds, st, p);
+        hipLaunchKernelGGL(output, ogrid, dim3(XNT), 0, st, p);
         return hipGetLastError();
     };
-    if (p.rank == 32) return p.g <= 4 ? go(xkv_decode<32, 4>) : go(xkv_decode<32, 8>);
-    return p.g <= 4 ? go(xkv_decode<64, 4>) : go(xkv_decode<64, 8>);
+    if (p.rank == 32)
+        return p.g <= 4 ? go(xkv_scores<32, 4>, xkv_attend<32, 4>, xkv_output<32>)
+                        : go(xkv_scores<32, 8>, xkv_attend<32, 8>, xkv_output<32>);
+    return p.g <= 4 ? go(xkv_scores<64, 4>, xkv_attend<64, 4>, xkv_output<64>)
+                    : go(xkv_scores<64, 8>, xkv_attend<64, 8>, xkv_output<64>);
 }
 
 }  // namespace kvc

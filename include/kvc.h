@@ -473,12 +473,20 @@ int kvc_xkv_factor(const kvc_cache* c, int slot0, int iters, uint64_t seed,
  * union's log-normaliser.  q: bf16 [nb][n_q_heads][head_dim]; out: float32
  * like o_in; selected: NULL or int32 [nb][n_kv_heads][n_select] (-1 past the
  * kept count).  n_select * chunk * g <= 16384 and the chunk keys of t_len
- * rows must fit the workgroup's LDS (KVC_EINVAL otherwise).
+ * rows must fit one workgroup's LDS (KVC_EINVAL otherwise).  ws:
+ * kvc_xkv_decode_ws_bytes bytes for the same store shape, head count and
+ * n_select (16-byte aligned, no initialisation needed; KVC_EWORKSPACE if
+ * smaller); it holds the chunk keys, q~ and the row splits' partials between
+ * the three launches, so calls that share a workspace must be ordered.
  */
-int kvc_xkv_decode_attn(const kvc_xkv* x, int layer, const void* q, int n_q_heads,
-                        float scale, int n_select, const float* o_in,
-                        const float* lse_in, float* out, float* lse, int32_t* selected,
+int kvc_xkv_decode_attn(const kvc_xkv* x, int layer, const void* q, int n_q_heads, float scale,
+                        int n_select, const float* o_in, const float* lse_in, float* out,
+                        float* lse, int32_t* selected, void* ws, size_t ws_bytes,
                         kvc_stream_t stream);
+
+/* Workspace bytes kvc_xkv_decode_attn needs for this store shape, query head
+ * count and n_select (same argument checks as the call). */
+int kvc_xkv_decode_ws_bytes(const kvc_xkv* x, int n_q_heads, int n_select, size_t* bytes);
 
 /*
  * Diagnostic: the device Philox4x32-10 stream that kvc_select draws from.

@@ -375,8 +375,9 @@ def test_xkv_ws_bytes_and_factor_validation():
 
 def test_xkv_decode_validation():
     x = xkv_desc()
-    d = lambda layer=0, hq=8, nsel=64, o_in=None, lse_in=None, q=FAKE, x=x: L.kvc_xkv_decode_attn(
-        ctypes.byref(x), layer, q, hq, 0.0, nsel, o_in, lse_in, FAKE, None, None, None)
+    d = lambda layer=0, hq=8, nsel=64, o_in=None, lse_in=None, q=FAKE, x=x, ws=FAKE, wsb=1 << 40: \
+        L.kvc_xkv_decode_attn(ctypes.byref(x), layer, q, hq, 0.0, nsel, o_in, lse_in, FAKE, None,
+                              None, ws, wsb, None)
     assert d(layer=4) == kvc.KVC_EINVAL
     assert d(hq=7) == kvc.KVC_EINVAL
     assert d(hq=2 * 9) == kvc.KVC_EINVAL                         # group of 9 heads
@@ -385,3 +386,14 @@ def test_xkv_decode_validation():
     assert d(o_in=FAKE) == kvc.KVC_EINVAL                        # lse_in missing
     assert d(q=FAKE + 2) == kvc.KVC_EALIGN
     assert d(x=xkv_desc(nb=0)) == kvc.KVC_OK
+    # the workspace: keys of 13 chunks, q~ for 8 heads and one row split's
+    # partials per (b, j) at least; checked after the arguments
+    n = ctypes.c_size_t()
+    assert L.kvc_xkv_decode_ws_bytes(ctypes.byref(x), 8, 64, ctypes.byref(n)) == kvc.KVC_OK
+    assert n.value >= 2 * (13 * 4 + 8 * 64 * 4 + 8 * 66 * 4)
+    assert L.kvc_xkv_decode_ws_bytes(ctypes.byref(x), 7, 64, ctypes.byref(n)) == kvc.KVC_EINVAL
+    assert L.kvc_xkv_decode_ws_bytes(ctypes.byref(x), 8, 0, ctypes.byref(n)) == kvc.KVC_EINVAL
+    assert d(wsb=n.value - 1) == kvc.KVC_EWORKSPACE
+    assert d(ws=None) == kvc.KVC_EWORKSPACE
+    assert d(ws=FAKE + 4) == kvc.KVC_EWORKSPACE
+    assert d(ws=None, hq=7) == kvc.KVC_EINVAL

@@ -155,12 +155,13 @@ def test_decode_on_oracle_factors(case):
     g = hq // hkv
     q = kvc_synth.queries((nb, hq, 128), device=DEV, seed=T + 1)
     qn = to_np(q)
+    ws = ws_tensor(kvc.kvc_xkv_decode_ws_bytes(st, hq, n_select))
     flips = 0
     for layer in range(W):
         out = torch.full((nb, hq, 128), float("nan"), device=DEV)
         lse = torch.full((nb, hq), float("nan"), device=DEV)
         sel = torch.full((nb, hkv, n_select), -7, dtype=torch.int32, device=DEV)
-        kvc.kvc_xkv_decode_attn(st, layer, q, out, lse, n_select=n_select, selected=sel)
+        kvc.kvc_xkv_decode_attn(st, layer, q, out, lse, n_select=n_select, selected=sel, ws=ws)
         torch.cuda.synchronize()
         o, l, s = to_np(out), to_np(lse), sel.cpu().numpy()
         nch = (T + 7) // 8
@@ -202,7 +203,8 @@ def test_decode_merges_a_second_part():
     kvc.kvc_decode_attn(tc, q, [1], o_t, l_t, ws_tensor(kvc.kvc_decode_attn_ws_bytes(tc, 1, hq)))
     out = torch.empty((nb, hq, 128), device=DEV)
     lse = torch.empty((nb, hq), device=DEV)
-    kvc.kvc_xkv_decode_attn(st, 1, q[0], out, lse, n_select=n_sel, o_in=o_t[0], lse_in=l_t[0])
+    kvc.kvc_xkv_decode_attn(st, 1, q[0], out, lse, n_select=n_sel, o_in=o_t[0], lse_in=l_t[0],
+                            ws=ws_tensor(kvc.kvc_xkv_decode_ws_bytes(st, hq, n_sel)))
     torch.cuda.synchronize()
     g = hq // hkv
     qn = to_np(q[0])
@@ -229,9 +231,10 @@ def test_factor_then_decode_end_to_end():
     g = hq // hkv
     qn = to_np(q)
     worst = 0.0
+    ws = ws_tensor(kvc.kvc_xkv_decode_ws_bytes(st, hq, 512))
     for layer in range(W):
         out = torch.empty((nb, hq, 128), device=DEV)
-        kvc.kvc_xkv_decode_attn(st, layer, q, out, n_select=512)
+        kvc.kvc_xkv_decode_attn(st, layer, q, out, n_select=512, ws=ws)
         torch.cuda.synchronize()
         for j in range(hkv):
             ro, _ = oracle.attention(qn[0, j * g:(j + 1) * g], Ks[layer][0, j], Vs[layer][0, j])
