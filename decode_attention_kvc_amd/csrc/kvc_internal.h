@@ -18,7 +18,7 @@ constexpr int SCORE_MAX_TPS = 16;     // tiles per score-statistics workgroup
 constexpr int SCORE_QPITCH = 136;     // bf16 per window-query row staged in LDS (272 bytes)
 constexpr int CU_COUNT = 256;         // compute units of the part
 constexpr int LDS_PER_CU = 160 * 1024;
-constexpr int XKV_MAX_ATTEND = 64;  // kept-row splits per (b, j) of a cross-layer decode
+constexpr int XKV_MAX_ATTEND = 16;  // kept-row splits per (b, j) of a cross-layer decode
 
 // LDS of one bf16 score-pass workgroup: the window queries (16-row blocks)
 // plus one float (lse term) and one int (last visible row) per row.

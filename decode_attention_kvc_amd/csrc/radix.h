@@ -19,6 +19,24 @@
 
 namespace kvc {
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (plain
+// VALU work, no LDS round trip): shifts by 1, 2, 4, 8 inside each 16-lane
+// row, then the last lane of row 0 into rows 1 and 3 and the last lane of
+// row 1 into rows 2 and 3.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+    v += dpp_u32<0x111, 0xF>(v);   // row_shr:1
+    v += dpp_u32<0x112, 0xF>(v);   // row_shr:2
+    v += dpp_u32<0x114, 0xF>(v);   // row_shr:4
+    v += dpp_u32<0x118, 0xF>(v);   // row_shr:8
+    v += dpp_u32<0x142, 0xA>(v);   // row_bcast:15
+    v += dpp_u32<0x143, 0xC>(v);   // row_bcast:31
+    return v;
+}
+
 template <int NT, int NC = 1>
 struct RadixSmem {
     static constexpr int PITCH = NC == 1 ? 256 : 257;
@@ -56,12 +74,7 @@ __device__ __forceinline__ uint32_t block_scan_u32(uint32_t v, RadixSmem<NT, NC>
                                                    uint32_t* total) {
     constexpr int NWV = NT / WAVE;
     const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
-    uint32_t incl = v;
-#pragma unroll
-    for (int o = 1; o < WAVE; o <<= 1) {
-        const uint32_t y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
-    }
+    const uint32_t incl = wave_incl_scan(v);
     if (lane == WAVE - 1) sm.wave_tot[wave] = incl;
     __syncthreads();
     uint32_t off = 0, tot = 0;
@@ -87,6 +100,7 @@ __device__ uint32_t radix_select(int n, uint32_t k, KeyFn key, RadixSmem<NT, NC>
     for (int shift = 24; shift >= 0; shift -= 8) {
         for (int i = tid; i < NC * PITCH; i += NT) sm.hist[i] = 0;
         __syncthreads();
+#pragma unroll 4
         for (int t = tid; t < n; t += NT) {
             const uint32_t u = key(t);
             if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
@@ -103,12 +117,7 @@ __device__ uint32_t radix_select(int n, uint32_t k, KeyFn key, RadixSmem<NT, NC>
                 s += c[e];
             }
             // inclusive scan of s across the wave
-            uint32_t incl = s;
-#pragma unroll
-            for (int o = 1; o < WAVE; o <<= 1) {
-                const uint32_t y = __shfl_up(incl, o);
-                if (tid >= o) incl += y;
-            }
+            const uint32_t incl = wave_incl_scan(s);
             uint32_t run = incl - s;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {

@@ -731,29 +731,40 @@ __global__ __launch_bounds__(XNT) void xkv_attend(XkvDecodeLaunch p) {
 
 // Decode, step 3: grid (j, b).  The row splits' partials merge with
 // log-sum-exp weights; o_h = B_l^V a~_h / z_h, merged with the second part
-// if given.  Thread (h, i) owns output channel i of head h; its row of B_l^V
-// is loaded first, so that read overlaps the merge.
+// if given.  Thread (h, i) owns output channel i of heads h and h + 4.
+// Every global read (its row of B_l^V, the second part, the partials) is
+// issued before the first barrier, so the kernel waits on one round trip.
 template <int R>
 __global__ __launch_bounds__(XNT) void xkv_output(XkvDecodeLaunch p) {
+    __shared__ float ps[XKV_MAX_ATTEND * MAXG * (R + 2)];
     __shared__ float at[MAXG * R];
     __shared__ float hz[MAXG], hmx[MAXG];
     __shared__ float wts[XKV_MAX_ATTEND * MAXG];
+    constexpr int HPT = MAXG / (XNT / D);      // heads per thread
     const int j = blockIdx.x, b = blockIdx.y;
     const int slab = b * p.hkv + j, g = p.g, n = p.window * D, tid = threadIdx.x;
     const int na = p.nattend;
     const float* P = p.ws_part + (size_t)slab * na * MAXG * (R + 2);
     const float* BV = p.bv + (size_t)slab * n * R + (size_t)p.layer * D * R;
-    const int oh = tid / D, oi = tid % D;      // XNT = 4 * D: heads oh, oh + 4
+    const int oh = tid / D, i = tid % D;
     f32x4 bvv[R / 4];
 #pragma unroll
-    for (int c4 = 0; c4 < R / 4; ++c4) bvv[c4] = *reinterpret_cast<const f32x4*>(BV + oi * R + 4 * c4);
-    for (int x = tid; x < na * MAXG; x += XNT) wts[x] = P[(size_t)x * (R + 2) + R];
+    for (int c4 = 0; c4 < R / 4; ++c4) bvv[c4] = *reinterpret_cast<const f32x4*>(BV + i * R + 4 * c4);
+    float o2[HPT], l2[HPT];
+#pragma unroll
+    for (int k = 0; k < HPT; ++k) {
+        const int h = oh + k * (XNT / D);
+        const size_t row = (size_t)b * p.hq + j * g + h;
+        o2[k] = (p.o_in && h < g) ? p.o_in[row * D + i] : 0.f;
+        l2[k] = (p.o_in && h < g) ? p.lse_in[row] : -INFINITY;
+    }
+    for (int x = tid; x < na * MAXG * (R + 2); x += XNT) ps[x] = P[x];
     __syncthreads();
     if (tid < MAXG) {
         float M = -INFINITY;
-        for (int a = 0; a < na; ++a) M = fmaxf(M, wts[a * MAXG + tid]);
+        for (int a = 0; a < na; ++a) M = fmaxf(M, ps[(a * MAXG + tid) * (R + 2) + R]);
         for (int a = 0; a < na; ++a) {
-            const float ma = wts[a * MAXG + tid];
+            const float ma = ps[(a * MAXG + tid) * (R + 2) + R];
             wts[a * MAXG + tid] = ma == -INFINITY ? 0.f : expf(ma - M);   // a split without rows
         }
         hmx[tid] = M;
@@ -762,18 +773,19 @@ __global__ __launch_bounds__(XNT) void xkv_output(XkvDecodeLaunch p) {
     for (int x = tid; x < g * (R + 1); x += XNT) {
         const int h = x / (R + 1), c = x % (R + 1);
         float sum = 0.f;
-#pragma unroll 4
         for (int a = 0; a < na; ++a) {
             const float w = wts[a * MAXG + h];
-            const float v = P[((size_t)a * MAXG + h) * (R + 2) + (c < R ? c : R + 1)];
+            const float v = ps[(a * MAXG + h) * (R + 2) + (c < R ? c : R + 1)];
             sum = w == 0.f ? sum : fmaf(w, v, sum);
         }
         if (c < R) at[h * R + c] = sum;
         else hz[h] = sum;
     }
     __syncthreads();
-    for (int h = oh; h < g; h += XNT / D) {
-        const int i = oi;
+#pragma unroll
+    for (int k = 0; k < HPT; ++k) {
+        const int h = oh + k * (XNT / D);
+        if (h >= g) break;
         float o = 0.f;
 #pragma unroll
         for (int c4 = 0; c4 < R / 4; ++c4)
@@ -784,13 +796,11 @@ __global__ __launch_bounds__(XNT) void xkv_output(XkvDecodeLaunch p) {
         o = zz > 0.f ? o / zz : 0.f;
         const size_t row = (size_t)b * p.hq + j * g + h;
         if (p.o_in) {
-            const float l2 = p.lse_in[row];
-            const float o2 = p.o_in[row * D + i];
-            const float mm = fmaxf(l1, l2);
+            const float mm = fmaxf(l1, l2[k]);
             if (mm != -INFINITY) {
                 const float w1 = (l1 == -INFINITY) ? 0.f : expf(l1 - mm);
-                const float w2 = (l2 == -INFINITY) ? 0.f : expf(l2 - mm);
-                o = (o * w1 + o2 * w2) / (w1 + w2);
+                const float w2 = (l2[k] == -INFINITY) ? 0.f : expf(l2[k] - mm);
+                o = (o * w1 + o2[k] * w2) / (w1 + w2);
                 l1 = mm + logf(w1 + w2);
             }
         }
