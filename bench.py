@@ -195,6 +195,7 @@ def int8_leg(args, cfg, dec, qpool, lsepool, knew, vnew, out, steps):
     ws = torch.zeros(max(16, kvc.kvc_q8_decode_attn_ws_bytes(qc, 1, hq)), dtype=torch.uint8,
                      device=dev)
     n_pool = qpool.shape[1]
+    slots = [[x] for x in range(n_slots)]
 
     def step(s, events):
         qc.t_len += 1
@@ -203,12 +204,13 @@ def int8_leg(args, cfg, dec, qpool, lsepool, knew, vnew, out, steps):
         if events is not None:
             a = torch.cuda.Event(enable_timing=True)
             a.record()
+        qs, ls, outs = qpool[:, sp].unbind(0), lsepool[:, sp].unbind(0), out.unbind(0)
+        kn, vn = knew[sp].unbind(0), vnew[sp].unbind(0)
         for l in range(L):
             slot = dec.src_slot[l]
             if dec.src_layer[l] == l:
-                kvc.kvc_q8_append(qc, slot, knew[sp, slot], vnew[sp, slot])
-            kvc.kvc_q8_decode_attn(qc, qpool[l, sp], [slot], out[l], lsepool[l, sp], ws,
-                                   n_q_heads=hq)
+                kvc.kvc_q8_append(qc, slot, kn[slot], vn[slot])
+            kvc.kvc_q8_decode_attn(qc, qs[l], slots[slot], outs[l], ls[l], ws, n_q_heads=hq)
         if events is not None:
             b = torch.cuda.Event(enable_timing=True)
             b.record()

@@ -314,10 +314,16 @@ class QCache:
         return self.kp.shape[3]
 
     def desc(self):
-        return kvc_qcache(self.kq.data_ptr(), self.vq.data_ptr(), self.sk.data_ptr(),
-                          self.sv.data_ptr(), self.kp.data_ptr(), self.vp.data_ptr(),
-                          self.n_slots, self.nb, self.n_kv_heads, HEAD_DIM, int(self.t_len),
-                          self.t_cap, int(self.p_len), self.p_cap)
+        """The kvc_qcache descriptor (built once per object; lengths refreshed)."""
+        d = self.__dict__.get("_desc")
+        key = tuple(t.data_ptr() for t in (self.kq, self.vq, self.sk, self.sv, self.kp, self.vp))
+        if d is None or self.__dict__.get("_desc_key") != key:
+            d = kvc_qcache(*key, self.n_slots, self.nb, self.n_kv_heads, HEAD_DIM, 0, self.t_cap,
+                           0, self.p_cap)
+            self.__dict__["_desc"], self.__dict__["_desc_key"] = d, key
+        d.t_len = int(self.t_len)
+        d.p_len = int(self.p_len)
+        return d
 
     def nbytes_per_row(self):
         """HBM bytes decode attention reads per quantized row (codes + scales)."""

@@ -75,48 +75,119 @@ __device__ __forceinline__ void load_tile(TileRegs& R, const uint16_t* kslab,
 
 __device__ __forceinline__ bf16x8 as_bf(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
-// Merge kernel: one workgroup per slab; each thread owns one query row and
-// 8 channels and folds the splits in order with
-// running log-sum-exp weights, so all of a split's loads are independent
-// and no barrier or LDS round trip is needed.
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch p) {
-    const int j = blockIdx.x, b = blockIdx.y;
+// Merge kernel: one workgroup per slab.  A work item is (query row, 8
+// channels).  With at most four splits a thread folds all of an item's
+// splits with running log-sum-exp weights (all of its reads issued
+// together).  With more, SG threads share an item when the slab has fewer
+// items than threads, each folding every SG-th split, in two passes: the
+// row's maximum over all splits' m (independent reads), then the weighted
+// sums sum_s e^(m_s - M) acc_s and sum_s e^(m_s - M) l_s (again independent
+// reads); the split groups' sums add up in a fixed order through LDS.
+// Slabs with many splits (few slabs per launch) use 1024 threads.
+template <int NTH>
+__global__ __launch_bounds__(NTH) void attn_combine_kernel(AttnLaunch p) {
+    __shared__ float red[NTH * 9];
+    const int j = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int slab = b * p.hkv + j;
     const int nsplit = p.nsplit, rp = p.rp;
     const size_t slabs = (size_t)p.nb * p.hkv;
     const float* acc = p.part + (size_t)slab * nsplit * rp * D;
     const float* ml = p.part + slabs * nsplit * rp * D + (size_t)slab * nsplit * rp * 2;
-    for (int idx = threadIdx.x; idx < p.rows * (D / 8); idx += blockDim.x) {
-        const int r = idx / (D / 8), d0 = (idx % (D / 8)) * 8;
-        float M = -INFINITY, L = 0.f, o[8];
+    const int items = p.rows * (D / 8);
+    if (nsplit <= 4) {
+        for (int idx = tid; idx < items; idx += NTH) {
+            const int r = idx / (D / 8), d0 = (idx % (D / 8)) * 8;
+            float M = -INFINITY, L = 0.f, o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = 0.f;
+#pragma unroll 4
+            for (int sp = 0; sp < nsplit; ++sp) {
+                const float ms = ml[((size_t)sp * rp + r) * 2];
+                const float ls = ml[((size_t)sp * rp + r) * 2 + 1];
+                const float* a = acc + ((size_t)sp * rp + r) * D + d0;
+                const f32x4 a0 = *reinterpret_cast<const f32x4*>(a);
+                const f32x4 a1 = *reinterpret_cast<const f32x4*>(a + 4);
+                if (ms == -INFINITY) continue;   // a split with no visible row
+                const float mn = fmaxf(M, ms);
+                const float fo = exp2f((M - mn) * LOG2E);   // 0 on the first split
+                const float fs = exp2f((ms - mn) * LOG2E);
+                L = L * fo + ls * fs;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    o[e] = o[e] * fo + a0[e] * fs;
+                    o[4 + e] = o[4 + e] * fo + a1[e] * fs;
+                }
+                M = mn;
+            }
+            const float inv = L > 0.f ? 1.f / L : 0.f;   // no split saw a row: zeros
+            const int qi = r / p.g, h = j * p.g + r % p.g;
+            float* dst = p.out + p.out_off[qi] + ((size_t)b * p.hq + h) * D + d0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dst[e] = o[e] * inv;
+            if (d0 == 0 && p.lse)
+                p.lse[p.lse_off[qi] + (size_t)b * p.hq + h] = L > 0.f ? M + logf(L) : -INFINITY;
+        }
+        return;
+    }
+    const int SG = max(1, min(nsplit, NTH / items));    // split groups per item
+    const int per = SG == 1 ? NTH : items;              // items per block pass
+    for (int i0 = 0; i0 < items; i0 += per) {
+        const int sg = tid / per, item = i0 + tid % per;
+        const bool act = sg < SG && item < items;
+        const int r = act ? item / (D / 8) : 0, d0 = act ? (item % (D / 8)) * 8 : 0;
+        float M = -INFINITY;
+        if (act)
+            for (int sp = sg; sp < nsplit; sp += SG) M = fmaxf(M, ml[((size_t)sp * rp + r) * 2]);
+        red[tid] = M;
+        __syncthreads();
+        if (act)
+            for (int s2 = 0; s2 < SG; ++s2) M = fmaxf(M, red[s2 * per + tid % per]);
+        __syncthreads();
+        float L = 0.f, o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = 0.f;
+        if (act && M != -INFINITY) {
 #pragma unroll 4
-        for (int sp = 0; sp < nsplit; ++sp) {
-            const float ms = ml[((size_t)sp * rp + r) * 2];
-            const float ls = ml[((size_t)sp * rp + r) * 2 + 1];
-            if (ms == -INFINITY) continue;   // a split with no visible row
-            const float* a = acc + ((size_t)sp * rp + r) * D + d0;
-            const f32x4 a0 = *reinterpret_cast<const f32x4*>(a);
-            const f32x4 a1 = *reinterpret_cast<const f32x4*>(a + 4);
-            const float mn = fmaxf(M, ms);
-            const float fo = exp2f((M - mn) * LOG2E);   // 0 on the first split
-            const float fs = exp2f((ms - mn) * LOG2E);
-            L = L * fo + ls * fs;
+            for (int sp = sg; sp < nsplit; sp += SG) {
+                const float ms = ml[((size_t)sp * rp + r) * 2];
+                const float ls = ml[((size_t)sp * rp + r) * 2 + 1];
+                const float* a = acc + ((size_t)sp * rp + r) * D + d0;
+                const f32x4 a0 = *reinterpret_cast<const f32x4*>(a);
+                const f32x4 a1 = *reinterpret_cast<const f32x4*>(a + 4);
+                if (ms == -INFINITY) continue;   // a split with no visible row
+                const float w = exp2f((ms - M) * LOG2E);
+                L = fmaf(w, ls, L);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                o[e] = o[e] * fo + a0[e] * fs;
-                o[4 + e] = o[4 + e] * fo + a1[e] * fs;
+                for (int e = 0; e < 4; ++e) {
+                    o[e] = fmaf(w, a0[e], o[e]);
+                    o[4 + e] = fmaf(w, a1[e], o[4 + e]);
+                }
             }
-            M = mn;
         }
-        const float inv = L > 0.f ? 1.f / L : 0.f;   // no split saw a row: zeros
-        const int qi = r / p.g, h = j * p.g + r % p.g;
-        float* dst = p.out + p.out_off[qi] + ((size_t)b * p.hq + h) * D + d0;
+        if (SG > 1) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dst[e] = o[e] * inv;
-        if (d0 == 0 && p.lse)
-            p.lse[p.lse_off[qi] + (size_t)b * p.hq + h] = L > 0.f ? M + logf(L) : -INFINITY;
+            for (int e = 0; e < 8; ++e) red[tid * 9 + e] = o[e];
+            red[tid * 9 + 8] = L;
+            __syncthreads();
+            if (act && sg == 0) {
+                for (int s2 = 1; s2 < SG; ++s2) {
+                    const float* q2 = red + (s2 * per + tid % per) * 9;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) o[e] += q2[e];
+                    L += q2[8];
+                }
+            }
+            __syncthreads();
+        }
+        if (act && sg == 0) {
+            const float inv = L > 0.f ? 1.f / L : 0.f;   // no split saw a row: zeros
+            const int qi = r / p.g, h = j * p.g + r % p.g;
+            float* dst = p.out + p.out_off[qi] + ((size_t)b * p.hq + h) * D + d0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dst[e] = o[e] * inv;
+            if (d0 == 0 && p.lse)
+                p.lse[p.lse_off[qi] + (size_t)b * p.hq + h] = L > 0.f ? M + logf(L) : -INFINITY;
+        }
     }
 }
 
@@ -398,7 +469,7 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(AttnLaunch p) {
                     store_ept(dst, o);
                     if (d0 == 0 && p.lse) p.lse[p.lse_off[qi] + (size_t)b * p.hq + h] = M + logf(L);
                 }
-            } else {
+            } else if (r < p.rows) {          // padding rows are never merged
                 store_ept(part_acc + (size_t)r * D + d0, o);
                 if (d0 == 0) {
                     part_ml[r * 2] = M;
@@ -581,7 +652,11 @@ hipError_t launch_attn(const AttnLaunch& p, int dtype, int nt, hipStream_t st) {
 }
 
 hipError_t launch_attn_combine(const AttnLaunch& p, hipStream_t st) {
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(p.hkv, p.nb), dim3(256), 0, st, p);
+    const long long work = (long long)p.rows * (D / 8) * p.nsplit;   // (item, split) pairs per slab
+    if (p.nsplit >= 8 && work > 4 * 256)
+        hipLaunchKernelGGL(attn_combine_kernel<1024>, dim3(p.hkv, p.nb), dim3(1024), 0, st, p);
+    else
+        hipLaunchKernelGGL(attn_combine_kernel<256>, dim3(p.hkv, p.nb), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 

@@ -230,16 +230,45 @@ __global__ __launch_bounds__(1024) void score_stats_bf16(ScoreLaunch p) {
 // Merge the splits' (max, sum) pairs of every window row into its
 // log-normaliser; one workgroup per slab, one thread per row, splits folded
 // in order.
-__global__ __launch_bounds__(256) void score_lse_merge(ScoreLaunch p) {
-    const int slab = blockIdx.y * p.hkv + blockIdx.x;
+// Merge of the statistics splits: one workgroup per slab; SG threads share a
+// window row when the slab has fewer rows than threads, each folding every
+// SG-th split, in two passes with independent reads (the row's maximum over
+// the splits' m, then sum_s z_s e^(m_s - M); a split without visible rows
+// has m = -inf), the split groups combined through LDS in a fixed order.
+__global__ __launch_bounds__(1024) void score_lse_merge(ScoreLaunch p) {
+    constexpr int NTH = 1024;
+    __shared__ float red[NTH];
+    const int slab = blockIdx.y * p.hkv + blockIdx.x, tid = threadIdx.x;
     const float* all = p.stats + (size_t)slab * p.nsplit * p.rows_pad * 2;
-    for (int R = threadIdx.x; R < p.rows; R += blockDim.x) {
+    const int SG = max(1, min(p.nsplit, NTH / max(1, p.rows)));
+    const int per = SG == 1 ? NTH : p.rows;
+    for (int R0 = 0; R0 < p.rows; R0 += per) {
+        const int sg = tid / per, R = R0 + tid % per;
+        const bool act = sg < SG && R < p.rows;
         float mm = -INFINITY, zz = 0.f;
+        if (act)
 #pragma unroll 4
-        for (int sp = 0; sp < p.nsplit; ++sp)
-            ms_merge(mm, zz, all[((size_t)sp * p.rows_pad + R) * 2],
-                     all[((size_t)sp * p.rows_pad + R) * 2 + 1]);
-        p.lse_ws[(size_t)slab * p.rows_pad + R] = mm + logf(zz);
+            for (int sp = sg; sp < p.nsplit; sp += SG)
+                mm = fmaxf(mm, all[((size_t)sp * p.rows_pad + R) * 2]);
+        red[tid] = mm;
+        __syncthreads();
+        if (act)
+            for (int s2 = 0; s2 < SG; ++s2) mm = fmaxf(mm, red[s2 * per + tid % per]);
+        __syncthreads();
+        if (act && mm != -INFINITY)
+#pragma unroll 4
+            for (int sp = sg; sp < p.nsplit; sp += SG) {
+                const float m2 = all[((size_t)sp * p.rows_pad + R) * 2];
+                const float z2 = all[((size_t)sp * p.rows_pad + R) * 2 + 1];
+                zz += m2 == -INFINITY ? 0.f : z2 * exp2f((m2 - mm) * LOG2E);
+            }
+        red[tid] = zz;
+        __syncthreads();
+        if (act && sg == 0) {
+            for (int s2 = 1; s2 < SG; ++s2) zz += red[s2 * per + tid % per];
+            p.lse_ws[(size_t)slab * p.rows_pad + R] = mm + logf(zz);
+        }
+        __syncthreads();
     }
 }
 
@@ -536,14 +565,14 @@ hipError_t launch_score(const ScoreLaunch& p, int dtype, hipStream_t st) {
     if (dtype == 0) {
         if (!p.lse_obs) {
             hipLaunchKernelGGL(score_f32, grid, dim3(256), 0, st, p, 1);
-            hipLaunchKernelGGL(score_lse_merge, dim3(p.hkv, p.nb), dim3(256), 0, st, p);
+            hipLaunchKernelGGL(score_lse_merge, dim3(p.hkv, p.nb), dim3(1024), 0, st, p);
         }
         hipLaunchKernelGGL(score_f32, grid, dim3(256), 0, st, p, 0);
     } else {
         const int nw = (p.rows + 31) / 32;
         if (!p.lse_obs) {
             hipLaunchKernelGGL(score_stats_bf16, grid, dim3(nw * WAVE), 0, st, p);
-            hipLaunchKernelGGL(score_lse_merge, dim3(p.hkv, p.nb), dim3(256), 0, st, p);
+            hipLaunchKernelGGL(score_lse_merge, dim3(p.hkv, p.nb), dim3(1024), 0, st, p);
         }
         const dim3 mgrid(p.main_nsplit, p.hkv, p.nb);
         const size_t lds = score_main_lds_bytes(p.rows);

@@ -24,6 +24,21 @@ import torch
 
 from . import _lib as K
 
+# One-element slot lists for the per-layer calls (built once).
+_SLOT_LISTS = [[i] for i in range(256)]
+
+
+def _one(slot):
+    return _SLOT_LISTS[slot] if slot < len(_SLOT_LISTS) else [slot]
+
+
+def _step_views(qpool, lsepool, knew, vnew, out, s):
+    """Per-layer views of step s, made in one call each (indexing the pools
+    once per layer costs more host time than the GPU spends on a short
+    call)."""
+    return (qpool[:, s].unbind(0), lsepool[:, s].unbind(0), out.unbind(0), knew[s].unbind(0),
+            vnew[s].unbind(0))
+
 
 class Decoder:
     def __init__(self, n_layers, leaders, cache, spare, n_q_heads, evict=None,
@@ -75,12 +90,13 @@ class Decoder:
         nb, hq, d = qpool.shape[2], qpool.shape[3], qpool.shape[4]
         ev = self._ev_begin()
         if self.mode != "grouped":
+            qs, ls, outs, kn, vn = _step_views(qpool, lsepool, knew, vnew, out, s)
             for l in self.order[self.mode]:
                 slot = self.src_slot[l]
                 lead = self.src_layer[l] == l
-                K.kvc_decode_attn(c, qpool[l, s], [slot], out[l], lsepool[l, s], self.ws_attn,
-                                  k_new=knew[s, slot] if lead else None,
-                                  v_new=vnew[s, slot] if lead else None,
+                K.kvc_decode_attn(c, qs[l], _one(slot), outs[l], ls[l], self.ws_attn,
+                                  k_new=kn[slot] if lead else None,
+                                  v_new=vn[slot] if lead else None,
                                   append_slot=slot if lead else -1, n_q_heads=hq)
             self._ev_end(ev, c, self.n_layers)
         else:
@@ -330,12 +346,13 @@ class RaggedDecoder:
         nb, hq, d = qpool.shape[2], qpool.shape[3], qpool.shape[4]
         ev0 = self._event()
         if self.mode == "per-layer":
+            qs, ls, outs, kn, vn = _step_views(qpool, lsepool, knew, vnew, out, s)
             for l in range(self.n_layers):
                 slot = self.src_slot[l]
                 lead = self.src_layer[l] == l
-                K.kvc_decode_attn(c, qpool[l, s], [slot], out[l], lsepool[l, s], self.ws_attn,
-                                  k_new=knew[s, slot] if lead else None,
-                                  v_new=vnew[s, slot] if lead else None,
+                K.kvc_decode_attn(c, qs[l], _one(slot), outs[l], ls[l], self.ws_attn,
+                                  k_new=kn[slot] if lead else None,
+                                  v_new=vn[slot] if lead else None,
                                   append_slot=slot if lead else -1, n_q_heads=hq)
         else:
             for slot, layers in enumerate(self.groups):
