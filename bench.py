@@ -456,8 +456,8 @@ def main():
                     help="run one plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} "
-              "requested). The head/batch sharding it would use is described in DESIGN.md.",
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (--gpus {args.gpus} "
+              "requested); its head/batch sharding is a design note, not built.",
               file=sys.stderr)
         sys.exit(2)
 

@@ -23,7 +23,7 @@ Arrays are numpy; every floating-point step is float64 unless a docstring
 says otherwise.  One "slab" is the [T][d] block of one (batch entry, cache
 slot, KV head).  K and V are passed in logical row-major form [T][d].
 
-Readings of points the pages leave open (each is listed in the design doc):
+Readings of points the pages leave open:
   GQA: query head h reads KV head h // g (contiguous groups).
   Scale: softmax of q.k / sqrt(d) unless a scale is given.
   S must contain layer 0; the recent buffer is the last B rows; N_v is
