@@ -241,3 +241,55 @@ def test_factor_then_decode_end_to_end():
             worst = max(worst, np.abs(to_np(out[0, j * g:(j + 1) * g]) - ro).max())
     say(f"  max |o - attention over the original rows| = {worst:.2e}")
     assert worst <= 2e-2
+
+
+def test_decode_full_size_sampled():
+    """The launch shape of the bench's cross-layer leg (batch 16, 8 KV heads,
+    32 query heads, 32768 rows, a window of 4 layers at rank 64, 256 of 4096
+    chunks kept, a tail part merged in): seeded store contents and tail
+    outputs are the inputs, and sampled (batch entry, KV head) pairs are
+    checked against the oracle's selective reconstruction and merge."""
+    nb, hkv, hq, T, W, R, n_sel = 16, 8, 32, 32768, 4, 64, 256
+    g = hq // hkv
+    say("xkv decode full size")
+    st = kvc.XkvStore.empty(nb, hkv, W, R, T, device=DEV, t_len=T)
+    st.ak.copy_(kvc_synth.queries(st.ak.shape, device=DEV, seed=101))
+    st.av.copy_(kvc_synth.queries(st.av.shape, device=DEV, seed=102))
+    st.lk.copy_(kvc_synth.queries(st.lk.shape, device=DEV, seed=103))
+    st.bk.copy_(kvc_synth.queries(st.bk.shape, dtype=torch.float32, device=DEV, seed=104) * 128 ** -0.5)
+    st.bv.copy_(kvc_synth.queries(st.bv.shape, dtype=torch.float32, device=DEV, seed=105) * 128 ** -0.5)
+    q = kvc_synth.queries((nb, hq, 128), device=DEV, seed=106)
+    o_in = kvc_synth.queries((nb, hq, 128), dtype=torch.float32, device=DEV, seed=107)
+    lse_in = kvc_synth.queries((nb, hq), dtype=torch.float32, device=DEV, seed=108) + 8.0
+    layer = 2
+    out = torch.full((nb, hq, 128), float("nan"), device=DEV)
+    lse = torch.full((nb, hq), float("nan"), device=DEV)
+    sel = torch.full((nb, hkv, n_sel), -7, dtype=torch.int32, device=DEV)
+    ws = ws_tensor(kvc.kvc_xkv_decode_ws_bytes(st, hq, n_sel))
+    kvc.kvc_xkv_decode_attn(st, layer, q, out, lse, n_select=n_sel, o_in=o_in, lse_in=lse_in,
+                            selected=sel, ws=ws)
+    torch.cuda.synchronize()
+    nch = T // 8
+    flips = 0
+    for (b, j) in [(0, 0), (7, 3), (15, 7), (9, 5)]:
+        AK = st.ak[b, j, :T].double().cpu().numpy()
+        AV = st.av[b, j, :T].double().cpu().numpy()
+        L = st.lk[b, j, :nch].double().cpu().numpy()
+        BK = st.bk[b, j, layer * 128:(layer + 1) * 128].double().cpu().numpy().T
+        BV = st.bv[b, j, layer * 128:(layer + 1) * 128].double().cpu().numpy().T
+        qh = to_np(q[b, j * g:(j + 1) * g])
+        o1, l1, kept = oxkv.sr_attention(qh, AK, AV, BK, BV, L, 8, n_sel)
+        ro, rl = oxkv.merge_attention(o1, l1, to_np(o_in[b, j * g:(j + 1) * g]),
+                                      to_np(lse_in[b, j * g:(j + 1) * g]))
+        got = sel[b, j].cpu().numpy()
+        if not np.array_equal(got, kept):
+            sc = oxkv.chunk_scores(qh, BK, L)
+            cut = np.sort(sc)[::-1][n_sel - 1]
+            for ch in set(got.tolist()) ^ set(kept.tolist()):
+                assert abs(sc[ch] - cut) <= 1e-5 * np.abs(sc).max(), (b, j, ch)
+            flips += 1
+            continue
+        assert np.abs(to_np(out[b, j * g:(j + 1) * g]) - ro).max() <= 1e-3, (b, j)
+        assert np.abs(to_np(lse[b, j * g:(j + 1) * g]) - rl).max() <= 1e-4, (b, j)
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    say(f"  sampled pairs with a flipped chunk inside the band: {flips}")
