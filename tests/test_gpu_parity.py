@@ -277,15 +277,22 @@ def test_select_matches_oracle(case):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_compact_bit_exact(dtype):
-    say("compact", dtype)
+@pytest.mark.parametrize("pattern", ["sparse", "dense", "unordered"])
+def test_compact_bit_exact(dtype, pattern):
+    """sparse: 600 of 1000 rows; dense: 985 of 1000 (a steady-state pass,
+    the last 64-row block ragged); unordered: the dense rows shuffled within
+    each slab, so rows fall outside the staged source tiles."""
+    say("compact", dtype, pattern)
     nb, hkv, T = 2, 4, 1000
     src = make_cache(2, nb, hkv, T, dtype=dtype, seed=9)
-    dst = kvc.Cache.empty(2, nb, hkv, 640, dtype=dtype, device=DEV)
+    dst = kvc.Cache.empty(2, nb, hkv, 1024, dtype=dtype, device=DEV)
     g = torch.Generator(device="cpu").manual_seed(1)
-    n_keep = 600
+    n_keep = 600 if pattern == "sparse" else 985
     kept = torch.stack([torch.stack([torch.randperm(T, generator=g)[:n_keep].sort().values
-                                     for _ in range(hkv)]) for _ in range(nb)]).int().to(DEV)
+                                     for _ in range(hkv)]) for _ in range(nb)])
+    if pattern == "unordered":
+        kept = kept[..., torch.randperm(n_keep, generator=g)]
+    kept = kept.int().contiguous().to(DEV)
     kept[1, 2, 7] = T + 5                                   # out of range -> zero row
     kvc.kvc_compact(src, 1, kept, n_keep, dst)
     torch.cuda.synchronize()
