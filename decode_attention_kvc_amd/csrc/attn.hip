@@ -79,14 +79,13 @@ __device__ __forceinline__ bf16x8 as_bf(u32x4 x) { return __builtin_bit_cast(bf1
 // channels).  With at most four splits a thread folds all of an item's
 // splits with running log-sum-exp weights (all of its reads issued
 // together).  With more, SG threads share an item when the slab has fewer
-// items than threads, each folding every SG-th split, in two passes: the
-// row's maximum over all splits' m (independent reads), then the weighted
-// sums sum_s e^(m_s - M) acc_s and sum_s e^(m_s - M) l_s (again independent
-// reads); the split groups' sums add up in a fixed order through LDS.
+// items than threads, each folding every SG-th split with running weights
+// (one pass of independent reads); the split groups' (max, sum, acc) meet
+// once in LDS, rescaled to the largest maximum and added in a fixed order.
 // Slabs with many splits (few slabs per launch) use 1024 threads.
 template <int NTH>
 __global__ __launch_bounds__(NTH) void attn_combine_kernel(AttnLaunch p) {
-    __shared__ float red[NTH * 9];
+    __shared__ float red[NTH * 10];
     const int j = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int slab = b * p.hkv + j;
     const int nsplit = p.nsplit, rp = p.rp;
@@ -135,18 +134,12 @@ __global__ __launch_bounds__(NTH) void attn_combine_kernel(AttnLaunch p) {
         const int sg = tid / per, item = i0 + tid % per;
         const bool act = sg < SG && item < items;
         const int r = act ? item / (D / 8) : 0, d0 = act ? (item % (D / 8)) * 8 : 0;
-        float M = -INFINITY;
-        if (act)
-            for (int sp = sg; sp < nsplit; sp += SG) M = fmaxf(M, ml[((size_t)sp * rp + r) * 2]);
-        red[tid] = M;
-        __syncthreads();
-        if (act)
-            for (int s2 = 0; s2 < SG; ++s2) M = fmaxf(M, red[s2 * per + tid % per]);
-        __syncthreads();
-        float L = 0.f, o[8];
+        // This thread's splits (every SG-th), folded with running weights;
+        // the loads of four splits are issued together.
+        float M = -INFINITY, L = 0.f, o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = 0.f;
-        if (act && M != -INFINITY) {
+        if (act) {
 #pragma unroll 4
             for (int sp = sg; sp < nsplit; sp += SG) {
                 const float ms = ml[((size_t)sp * rp + r) * 2];
@@ -155,27 +148,44 @@ __global__ __launch_bounds__(NTH) void attn_combine_kernel(AttnLaunch p) {
                 const f32x4 a0 = *reinterpret_cast<const f32x4*>(a);
                 const f32x4 a1 = *reinterpret_cast<const f32x4*>(a + 4);
                 if (ms == -INFINITY) continue;   // a split with no visible row
-                const float w = exp2f((ms - M) * LOG2E);
-                L = fmaf(w, ls, L);
+                const float mn = fmaxf(M, ms);
+                const float fo = exp2f((M - mn) * LOG2E);   // 0 on the first split
+                const float fs = exp2f((ms - mn) * LOG2E);
+                L = L * fo + ls * fs;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    o[e] = fmaf(w, a0[e], o[e]);
-                    o[4 + e] = fmaf(w, a1[e], o[4 + e]);
+                    o[e] = o[e] * fo + a0[e] * fs;
+                    o[4 + e] = o[4 + e] * fo + a1[e] * fs;
                 }
+                M = mn;
             }
         }
         if (SG > 1) {
+            // The split groups of an item meet in LDS once: group 0 rescales
+            // every group's sums to the largest maximum and adds them in
+            // group order.
 #pragma unroll
-            for (int e = 0; e < 8; ++e) red[tid * 9 + e] = o[e];
-            red[tid * 9 + 8] = L;
+            for (int e = 0; e < 8; ++e) red[tid * 10 + e] = o[e];
+            red[tid * 10 + 8] = L;
+            red[tid * 10 + 9] = M;
             __syncthreads();
             if (act && sg == 0) {
-                for (int s2 = 1; s2 < SG; ++s2) {
-                    const float* q2 = red + (s2 * per + tid % per) * 9;
+                float Mx = M;
+                for (int s2 = 1; s2 < SG; ++s2) Mx = fmaxf(Mx, red[(s2 * per + tid % per) * 10 + 9]);
+                if (Mx != -INFINITY) {
+                    const float f0 = exp2f((M - Mx) * LOG2E);
+                    L *= f0;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) o[e] += q2[e];
-                    L += q2[8];
+                    for (int e = 0; e < 8; ++e) o[e] *= f0;
+                    for (int s2 = 1; s2 < SG; ++s2) {
+                        const float* q2 = red + (s2 * per + tid % per) * 10;
+                        const float f = exp2f((q2[9] - Mx) * LOG2E);   // empty group: 0
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) o[e] = fmaf(f, q2[e], o[e]);
+                        L = fmaf(f, q2[8], L);
+                    }
                 }
+                M = Mx;
             }
             __syncthreads();
         }

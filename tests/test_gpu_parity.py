@@ -61,7 +61,7 @@ ATTN_CASES = [
     (1, 16, 8, 300, 3, [0, 0, 0]),            # 6 rows
     (2, 32, 8, 1500, 4, [0, 1, 0, 1]),        # two slots in one call
     (1, 8, 8, 200, 20, [0] * 20),             # 20 layers, MHA: two launches
-    # 128-255 slabs: two workgroups per slab split the value channels
+    # 128-255 slabs: two splits per slab
     (16, 32, 8, 1031, 1, [0]),
     (33, 16, 4, 300, 1, [1]),                 # 132 slabs: part of the last group idle
     (16, 32, 8, 500, 4, [0, 0, 0, 0]),        # grouped, 16 rows
