@@ -77,10 +77,16 @@ def evict_bytes(cfg, t_len):
 
 
 def cpu_baseline(cfg, cache, qpool, s, budget_s=8.0):
-    """Time the float64 oracle on a bounded sample of the same workload."""
+    """Time the float64 oracle on a bounded sample of the same workload, and
+    compare the library's outputs with the oracle's on that sample (the
+    slabs of cache slot 0 at the bench's final cache state): decode attention
+    of layer 0's queries of step s, and, for window-score eviction, the
+    window scores and kept sets of one pass with the last w queries.
+    Returns (baseline, parity)."""
     import numpy as np
     import torch
     import oracle
+    import decode_attention_kvc_amd as kvc
     try:
         from threadpoolctl import threadpool_info
         blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
@@ -89,6 +95,31 @@ def cpu_baseline(cfg, cache, qpool, s, budget_s=8.0):
     nb, hq, hkv = cfg["nb"], cfg["hq"], cfg["hkv"]
     g = hq // hkv
     T = cache.t_len
+    e = cfg["evict"]
+    dev = cache.k.device
+    # The library's outputs on the same inputs, before any timing: layer 0's
+    # decode attention (no append, the cache is unchanged) and one eviction
+    # pass's window scores, ranges and kept sets on slot 0.
+    g_out = torch.empty((1, nb, hq, 128), device=dev)
+    kvc.kvc_decode_attn(cache, qpool[0, s:s + 1], [0], g_out, None,
+                        torch.zeros(kvc.kvc_decode_attn_ws_bytes(cache, 1, hq),
+                                    dtype=torch.uint8, device=dev))
+    g_kept = g_score = None
+    window = bool(e) and e.get("scoring", "attnv") == "attnv"
+    if window:
+        w = e["w"]
+        g_score = torch.empty((nb, hkv, T), device=dev)
+        g_rng = torch.empty((nb, hkv, T), device=dev)
+        kvc.kvc_score(cache, 0, qpool[0, s - w + 1:s + 1], g_score, g_rng, None,
+                      torch.zeros(kvc.kvc_score_ws_bytes(cache, hq, w), dtype=torch.uint8,
+                                  device=dev))
+        g_kept = torch.empty((nb, hkv, min(T, e["K"] + e["B"])), dtype=torch.int32, device=dev)
+        kvc.kvc_select(g_score, g_rng, nb, hkv, T, e["K"], e["B"], e["N_v"], 1, 0, g_kept,
+                       torch.empty(kvc.kvc_select_ws_bytes(nb, hkv, T), dtype=torch.uint8,
+                                   device=dev))
+        g_kept, g_score = g_kept.cpu().numpy(), g_score.cpu().numpy()
+    g_out = g_out.cpu().numpy()
+    ref_out, ref_ev = [], []
     # decode: slabs of layer 0 (slot 0), converted bf16 -> float64 per slab
     Kc = cache.k_rows(0).cpu()
     Vc = cache.v_rows(0).cpu()
@@ -99,13 +130,12 @@ def cpu_baseline(cfg, cache, qpool, s, budget_s=8.0):
         b, j = divmod(n_dec, hkv)
         K = Kc[b, j].double().numpy()
         V = Vc[b, j].double().numpy()
-        oracle.attention(qh[b, j * g:(j + 1) * g].double().numpy(), K, V)
+        ref_out.append(oracle.attention(qh[b, j * g:(j + 1) * g].double().numpy(), K, V)[0])
         n_dec += 1
     t_dec = (time.perf_counter() - t0) / n_dec
     t_step = t_dec * cfg["n_layers"] * nb * hkv
     t_ev_total = 0.0
     n_ev = 0
-    e = cfg["evict"]
     if e:
         w = e["w"]
         qo = qpool[0, s - w + 1:s + 1].cpu()
@@ -124,8 +154,10 @@ def cpu_baseline(cfg, cache, qpool, s, budget_s=8.0):
             else:
                 sc = oracle.window_score(qo[:, b, j * g:(j + 1) * g].double().numpy(), K, T)
             vr = oracle.value_range(V)
-            kept = oracle.select(sc, vr, T, e["K"], e["B"], e["N_v"], 1, 0, b, j)
-            oracle.compact(K, V, kept)
+            det = oracle.select_detail(sc, vr, T, e["K"], e["B"], e["N_v"], 1, 0, b, j)
+            oracle.compact(K, V, det["kept"])
+            if not dkv:
+                ref_ev.append((sc, det))
             n_ev += 1
         t_ev = (time.perf_counter() - t1) / n_ev
         t_ev_total = t_ev * nb * hkv * len(cfg["leaders"])
@@ -138,9 +170,39 @@ def cpu_baseline(cfg, cache, qpool, s, budget_s=8.0):
               + (f" plus 1/{e['period']} of a pass over {len(cfg['leaders'])} leader slots"
                  if e else "")
               + "; numpy float64, bf16 converted per slab")
-    return dict(value=round(nb / per_step, 4), unit="tokens/s", cores=int(blas), kind="oracle",
-                sample=sample, extrapolated=True,
-                cpu_model=_cpu_model(), host_cores=len(os.sched_getaffinity(0)))
+    baseline = dict(value=round(nb / per_step, 4), unit="tokens/s", cores=int(blas),
+                    kind="oracle", sample=sample, extrapolated=True,
+                    cpu_model=_cpu_model(), host_cores=len(os.sched_getaffinity(0)))
+
+    # Parity on the sampled slabs.  Attention: max |o - o_ref| against the
+    # bf16 tolerance 2e-2.  Kept sets: rows kept by one side only are ties
+    # when their key lies within 1e-6 (relative) of the oracle's sampling
+    # cutoff, otherwise mismatches.
+    err = 0.0
+    for i, ref in enumerate(ref_out):
+        b, j = divmod(i, hkv)
+        err = max(err, float(np.abs(g_out[0, b, j * g:(j + 1) * g] - ref).max()))
+    parity = dict(sample=f"slot 0 at {T} rows, layer 0's queries of the last step",
+                  attention_slabs=len(ref_out), attention_max_abs_err=float(f"{err:.3e}"),
+                  attention_tol=2e-2, attention_ok=err <= 2e-2)
+    if window and ref_ev:
+        ties = bad = 0
+        srel = 0.0
+        for i, (sc, det) in enumerate(ref_ev):
+            b, j = divmod(i, hkv)
+            srel = max(srel, float(np.max(np.abs(g_score[b, j] - sc) / np.maximum(sc, 1e-30))))
+            diff = set(g_kept[b, j].tolist()) ^ set(det["kept"].tolist())
+            kc = det["kappa_cut"]
+            for t in diff:
+                kap = det["kappa"][t]
+                if kc is not None and np.isfinite(kap) and abs(kap - kc) <= 1e-6 * kc:
+                    ties += 1
+                else:
+                    bad += 1
+        parity.update(eviction_slabs=len(ref_ev), score_max_rel_err=float(f"{srel:.3e}"),
+                      kept_rows_per_slab=int(g_kept.shape[-1]), kept_ties_within_1e_6=ties,
+                      kept_mismatches=bad, kept_ok=bad == 0)
+    return baseline, parity
 
 
 def load_traffic(bytes_per_launch):
@@ -634,11 +696,12 @@ def main():
         del x, y, a, c
         log("[bench] copy calibration done: 1 GiB blit, 512 MiB vectorized copy")
 
-    cpu = None
+    cpu = parity = None
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host (bounded sample)")
-        cpu = cpu_baseline(cfg, dec.cache, qpool, W + S - 1)
+        cpu, parity = cpu_baseline(cfg, dec.cache, qpool, W + S - 1)
         log(f"[bench] cpu baseline: {cpu}")
+        log(f"[bench] parity on the sample: {parity}")
 
     traffic, tinfo = load_traffic(sum(att_bytes) / n_calls)
     res = {
@@ -686,6 +749,7 @@ def main():
         "ragged": ragged_res,
         "xkv": xkv_res,
         "cpu_baseline": cpu,
+        "parity": parity,
     }
     print(json.dumps(res), flush=True)
 
