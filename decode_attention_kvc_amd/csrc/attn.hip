@@ -92,10 +92,15 @@ __global__ __launch_bounds__(NTH) void attn_combine_kernel(AttnLaunch p) {
     const size_t slabs = (size_t)p.nb * p.hkv;
     const float* acc = p.part + (size_t)slab * nsplit * rp * D;
     const float* ml = p.part + slabs * nsplit * rp * D + (size_t)slab * nsplit * rp * 2;
-    const int items = p.rows * (D / 8);
+    // blockIdx.z: a block of the slab's query rows (one block unless the
+    // launch spreads many-split rows over several workgroups).
+    const int rpb = (p.rows + gridDim.z - 1) / gridDim.z;
+    const int r0 = blockIdx.z * rpb;
+    const int items = min(rpb, p.rows - r0) * (D / 8);
+    if (items <= 0) return;
     if (nsplit <= 4) {
         for (int idx = tid; idx < items; idx += NTH) {
-            const int r = idx / (D / 8), d0 = (idx % (D / 8)) * 8;
+            const int r = r0 + idx / (D / 8), d0 = (idx % (D / 8)) * 8;
             float M = -INFINITY, L = 0.f, o[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) o[e] = 0.f;
@@ -133,7 +138,7 @@ __global__ __launch_bounds__(NTH) void attn_combine_kernel(AttnLaunch p) {
     for (int i0 = 0; i0 < items; i0 += per) {
         const int sg = tid / per, item = i0 + tid % per;
         const bool act = sg < SG && item < items;
-        const int r = act ? item / (D / 8) : 0, d0 = act ? (item % (D / 8)) * 8 : 0;
+        const int r = act ? r0 + item / (D / 8) : 0, d0 = act ? (item % (D / 8)) * 8 : 0;
         // This thread's splits (every SG-th), folded with running weights;
         // the loads of four splits are issued together.
         float M = -INFINITY, L = 0.f, o[8];
@@ -663,10 +668,17 @@ hipError_t launch_attn(const AttnLaunch& p, int dtype, int nt, hipStream_t st) {
 
 hipError_t launch_attn_combine(const AttnLaunch& p, hipStream_t st) {
     const long long work = (long long)p.rows * (D / 8) * p.nsplit;   // (item, split) pairs per slab
-    if (p.nsplit >= 8 && work > 4 * 256)
-        hipLaunchKernelGGL(attn_combine_kernel<1024>, dim3(p.hkv, p.nb), dim3(1024), 0, st, p);
-    else
+    if (p.nsplit >= 8 && work > 4 * 256) {
+        // Up to 16 split groups per item and 1024 threads: a workgroup takes
+        // 1024 / (16 * groups) rows (4 once a slab has 16 splits or more),
+        // so every thread folds about nsplit / 16 splits.
+        const int groups = std::min(p.nsplit, 16);
+        const int rpb = std::max(1, 1024 / ((D / 8) * groups));
+        const int nrb = (p.rows + rpb - 1) / rpb;
+        hipLaunchKernelGGL(attn_combine_kernel<1024>, dim3(p.hkv, p.nb, nrb), dim3(1024), 0, st, p);
+    } else {
         hipLaunchKernelGGL(attn_combine_kernel<256>, dim3(p.hkv, p.nb), dim3(256), 0, st, p);
+    }
     return hipGetLastError();
 }
 
