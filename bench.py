@@ -34,6 +34,11 @@ WORKLOADS = {
     "qwen3-8b-rcla": dict(
         desc="Qwen3-8B-shaped R-CLA decode, 9 of 36 layers lead, no eviction",
         n_layers=36, leaders=list(range(0, 36, 4)), nb=1, hq=32, hkv=8, t0=32768, evict=None),
+    "qwen3-4b-vase": dict(
+        desc="Qwen3-4B-shaped VASE decode: every layer its own cache, 16K tokens generated "
+             "from an empty cache",
+        n_layers=36, leaders=list(range(36)), nb=8, hq=32, hkv=8, t0=0, steps=16384,
+        evict=dict(K=4096, B=128, N_v=64, w=32, period=128, seed=0)),
     "qwen3-14b-long": dict(
         desc="Qwen3-14B-shaped long-context decode: sharing every 2 layers, 128K prompt, VASE",
         n_layers=40, leaders=list(range(0, 40, 2)), nb=4, hq=40, hkv=8, t0=131072,
@@ -488,7 +493,9 @@ def xkv_leg(args, cfg, qpool, knew, vnew, steps, warm=3):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed decode steps (default 256; the Qwen3-4B workload: its 16384 "
+                         "generated tokens)")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3.1-8b-combined", choices=list(WORKLOADS))
     ap.add_argument("--mode", default="per-layer",
@@ -536,8 +543,17 @@ def main():
     L, leaders, nb, hq, hkv, t0 = (cfg[k] for k in ("n_layers", "leaders", "nb", "hq", "hkv", "t0"))
     ev = cfg["evict"]
     n_slots = len(leaders)
-    W, S = args.warmup, args.steps
-    n_total = W + 2 * S + 2
+    W = args.warmup
+    S = args.steps if args.steps is not None else cfg.get("steps", 256)
+    if t0 == 0:
+        # A cache grown from empty: the legs built around a prompt cache
+        # (ragged prompts, the int8 form of the compressed prompt, the
+        # cross-layer factorisation) do not apply.
+        args.no_ragged = args.no_int8 = args.no_xkv = True
+        if args.ragged_only or args.xkv_only:
+            sys.exit("--ragged-only / --xkv-only need a workload with a prompt")
+    grouped_leg = not args.no_grouped and args.mode != "grouped" and n_slots < L
+    n_total = W + S + 1 + (S + 1 if grouped_leg else 0)
     if ev and not args.no_ragged:        # the ragged leg warms up for a full period
         n_total = max(n_total, max(W, ev["period"]) + S + 1)
     if ev:
@@ -569,7 +585,7 @@ def main():
     # ---- inputs (untimed): prompt cache, query / append pools
     big = kvc.Cache.empty(n_slots, nb, hkv, t0 + (0 if ev else n_total), device=dev)
     prev = None
-    for s_ in range(n_slots):
+    for s_ in range(n_slots if t0 else 0):
         Kr, Vr, K32, V32 = kvc_synth.kv_slot(nb, hkv, t0, device=dev, seed=100 + s_,
                                              prev=prev, rho=0.9 if not ev else None,
                                              gap=leaders[1] - leaders[0] if n_slots > 1 else 1)
@@ -579,13 +595,22 @@ def main():
     del prev
     qpool = kvc_synth.queries((L, n_total, nb, hq, 128), device=dev, seed=1)
     lsepool = torch.zeros((L, n_total, nb, hq), device=dev)
-    knew = kvc_synth.queries((n_total, n_slots, nb, hkv, 128), device=dev, seed=2)
-    vnew = kvc_synth.queries((n_total, n_slots, nb, hkv, 128), device=dev, seed=3)
+    if t0:
+        knew = kvc_synth.queries((n_total, n_slots, nb, hkv, 128), device=dev, seed=2)
+        vnew = kvc_synth.queries((n_total, n_slots, nb, hkv, 128), device=dev, seed=3)
+    else:
+        # the whole cache is generated rows: they carry the value outliers
+        knew, vnew = kvc_synth.append_rows(n_total, n_slots, nb, hkv, device=dev, seed=2)
     out = torch.empty((L, nb, hq, 128), device=dev)
     torch.cuda.synchronize()
 
     initial_ms = None
-    if ev:
+    if ev and t0 == 0:
+        cache = kvc.Cache.empty(n_slots, nb, hkv, steady_cap, device=dev)
+        spare = kvc.Cache.empty(n_slots, nb, hkv, steady_cap, device=dev)
+        dec = Decoder(L, leaders, cache, spare, hq, evict=ev, mode=args.mode)
+        del big
+    elif ev:
         cache = kvc.Cache.empty(n_slots, nb, hkv, steady_cap, device=dev)
         spare = kvc.Cache.empty(n_slots, nb, hkv, steady_cap, device=dev)
         dec = Decoder(L, leaders, big, cache, hq, evict=ev, mode=args.mode)
@@ -644,7 +669,7 @@ def main():
     step_gbps = step_bytes / wall / 1e9
 
     grouped = None
-    if not args.no_grouped and args.mode != "grouped" and n_slots < L:
+    if grouped_leg:
         first = W + S
         torch.cuda.synchronize()
         g0 = time.perf_counter()

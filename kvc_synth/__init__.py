@@ -69,6 +69,25 @@ def kv_slot(nb, hkv, T, d=128, dtype=torch.bfloat16, device="cpu", seed=0,
     return k.to(dtype), v_out.to(dtype), k, v
 
 
+def append_rows(n_steps, n_slots, nb, hkv, d=128, dtype=torch.bfloat16, device="cpu", seed=0,
+                outlier_frac=0.01, outlier_scale=20.0):
+    """New K and V rows [n_steps][n_slots][nb][hkv][d] for a decode whose
+    cache grows from empty: N(0, 1), and for every (slot, batch entry, KV
+    head) round(outlier_frac * n_steps) uniformly chosen steps whose value
+    row is scaled by outlier_scale (the value outliers of a prompt cache,
+    spread over the generated rows).  Returns (k_new, v_new)."""
+    gen = generator(seed, device)
+    k = normal((n_steps, n_slots, nb, hkv, d), dtype, device, gen)
+    v = torch.randn((n_steps, n_slots, nb, hkv, d), generator=gen, device=device)
+    idx = outlier_rows(n_slots * nb, hkv, n_steps, outlier_frac, gen, device)
+    if idx.shape[-1]:
+        hit = torch.zeros((n_slots * nb, hkv, n_steps), dtype=torch.bool, device=device)
+        hit.scatter_(-1, idx, True)
+        hit = hit.reshape(n_slots, nb, hkv, n_steps).permute(3, 0, 1, 2)
+        v[hit] *= outlier_scale
+    return k, v.to(dtype)
+
+
 def lowrank_layers(nb, hkv, T, W, k, noise=0.0, rho=0.9, d=128, dtype=torch.bfloat16,
                    device="cpu", seed=0):
     """K and V rows [nb][hkv][T][d] of W consecutive layers whose caches share
