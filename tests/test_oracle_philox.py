@@ -90,3 +90,19 @@ def test_exp_variate_end_points_and_law():
     y = m / 2**32
     e_small = exp_variate(2**32 - 1 - m)
     assert np.allclose(e_small, y + y * y / 2 + y**3 / 3, rtol=1e-13, atol=0)
+
+
+def test_weyl_increments_closed_forms():
+    # The key increments are the leading fraction bits of the golden ratio
+    # and of sqrt(3) (SC'11, the Philox key schedule); the 32-bit ones are
+    # the high words of the 64-bit ones, which the numpy check above fixes.
+    from decimal import Decimal, getcontext
+    from oracle.philox import WEYL
+    getcontext().prec = 60
+    phi_frac = (Decimal(5).sqrt() - 1) / 2
+    sqrt3_frac = Decimal(3).sqrt() - 1
+    for width in (32, 64):
+        scale = Decimal(2) ** width
+        assert WEYL[width][0] == int(phi_frac * scale)
+        assert WEYL[width][1] == int(sqrt3_frac * scale)
+    assert WEYL[32] == tuple(w >> 32 for w in WEYL[64])
