@@ -51,16 +51,24 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactLaunch p) {
     using S = Stage<E>;
     constexpr int VEC = S::VEC;
     constexpr int CPR = D / VEC;            // 16-byte chunks per K row
-    const int b = blockIdx.z;
-    const int slab = b * p.hkv + blockIdx.y;
-    const int i0 = blockIdx.x * CROWS;
+    // Workgroups are dealt to the eight XCDs in turn; renumber them so that
+    // each XCD takes a contiguous run of (row block, head, batch) blocks.
+    // Neighbouring row blocks of a slab share a boundary source tile of V,
+    // and on one XCD its second read finds the tile in that XCD's L2.
+    const int gx = gridDim.x, gy = gridDim.y;
+    const int nwg = gx * gy * gridDim.z;
+    int blk = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+    if (nwg % XCD_COUNT == 0) blk = (blk % XCD_COUNT) * (nwg / XCD_COUNT) + blk / XCD_COUNT;
+    const int bx = blk % gx, by = (blk / gx) % gy, b = blk / (gx * gy);
+    const int slab = b * p.hkv + by;
+    const int i0 = bx * CROWS;
     const int tid = threadIdx.x;
     const int sphys = seq_phys(p.src_sm, b), dphys = seq_phys(p.dst_sm, b);
     const int src_t_len = seq_rows(p.src_sm, b, sphys);
     const int rows = min(CROWS, min(src_t_len, p.n_keep) - i0);
     if (dphys < 0 || rows <= 0) return;          // whole workgroup
     const int32_t* kept = p.kept + (size_t)slab * p.n_keep;
-    const size_t scs = (size_t)sphys * p.hkv + blockIdx.y, dcs = (size_t)dphys * p.hkv + blockIdx.y;
+    const size_t scs = (size_t)sphys * p.hkv + by, dcs = (size_t)dphys * p.hkv + by;
     const E* sk = reinterpret_cast<const E*>(p.sk) + scs * p.src_t_cap * D;
     const E* sv = reinterpret_cast<const E*>(p.sv) + scs * p.src_t_cap * D;
     E* dk = reinterpret_cast<E*>(p.dk) + dcs * p.dst_t_cap * D;

@@ -17,6 +17,7 @@ constexpr int SCORE_TILE = 32;
 constexpr int SCORE_MAX_TPS = 16;     // tiles per score-statistics workgroup
 constexpr int SCORE_QPITCH = 136;     // bf16 per window-query row staged in LDS (272 bytes)
 constexpr int CU_COUNT = 256;         // compute units of the part
+constexpr int XCD_COUNT = 8;          // accelerator dies; workgroups are dealt to them in turn
 constexpr int LDS_PER_CU = 160 * 1024;
 constexpr int XKV_MAX_ATTEND = 16;  // kept-row splits per (b, j) of a cross-layer decode
 
