@@ -461,6 +461,7 @@ int kvc_decode_attn(const kvc_cache* c, const void* q, int64_t q_layer_stride, i
         p.rp = pl.rp;
         p.nsplit = pl.nsplit;
         p.tps = pl.tps;
+        p.xcd_runs = pl.nsplit >= 8;
         p.part = static_cast<float*>(ws);
         p.sm = seq_map(c);
         if (launch_attn(p, c->dtype, pl.nt, s) != hipSuccess) return (int)KVC_EHIP;

@@ -222,7 +222,18 @@ __device__ void write_append_row(const AttnLaunch& p, size_t slab, size_t cslab,
 template <int NT, int W, int PF>
 __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(AttnLaunch p) {
     constexpr int RP = 16 * NT;
-    const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+    // Workgroups are dealt to the eight XCDs in turn.  With many splits per
+    // slab the launch renumbers them so that each XCD streams a contiguous
+    // run of (split, head, batch) blocks: at batch 1, 8 KV heads and 33K
+    // rows (32 splits per slab) every XCD then streams one whole slab,
+    // measured 2.5% faster per call; launches with few splits per slab were
+    // 0.2-0.5% slower with it and keep the plain order.
+    const int gx = gridDim.x, gy = gridDim.y;
+    const int nwg = gx * gy * gridDim.z;
+    int blk = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+    if (p.xcd_runs && nwg % XCD_COUNT == 0)
+        blk = (blk % XCD_COUNT) * (nwg / XCD_COUNT) + blk / XCD_COUNT;
+    const int s = blk % gx, j = (blk / gx) % gy, b = blk / (gx * gy);
     const int slab = b * p.hkv + j;
     const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
     const int l16 = lane & 15, lg = lane >> 4;

@@ -70,6 +70,7 @@ struct AttnLaunch {
     int append_read;        // row t_len-1 comes from k_new / v_new
     int append_write;       // and is written into the cache
     int nsplit, tps;        // splits per slab, tiles per split
+    int xcd_runs;           // workgroups renumbered into contiguous runs per XCD
     float* part;            // partial accumulators, then (m, l) pairs
     SeqMap sm;              // cache entry and rows of each sequence
 };
