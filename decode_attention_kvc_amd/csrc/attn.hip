@@ -228,12 +228,8 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(AttnLaunch p) {
     // rows (32 splits per slab) every XCD then streams one whole slab,
     // measured 2.5% faster per call; launches with few splits per slab were
     // 0.2-0.5% slower with it and keep the plain order.
-    const int gx = gridDim.x, gy = gridDim.y;
-    const int nwg = gx * gy * gridDim.z;
-    int blk = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
-    if (p.xcd_runs && nwg % XCD_COUNT == 0)
-        blk = (blk % XCD_COUNT) * (nwg / XCD_COUNT) + blk / XCD_COUNT;
-    const int s = blk % gx, j = (blk / gx) % gy, b = blk / (gx * gy);
+    const BlockXYZ blk = xcd_run_block(p.xcd_runs);
+    const int s = blk.x, j = blk.y, b = blk.z;
     const int slab = b * p.hkv + j;
     const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
     const int l16 = lane & 15, lg = lane >> 4;

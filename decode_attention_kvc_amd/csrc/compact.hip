@@ -51,15 +51,11 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactLaunch p) {
     using S = Stage<E>;
     constexpr int VEC = S::VEC;
     constexpr int CPR = D / VEC;            // 16-byte chunks per K row
-    // Workgroups are dealt to the eight XCDs in turn; renumber them so that
-    // each XCD takes a contiguous run of (row block, head, batch) blocks.
-    // Neighbouring row blocks of a slab share a boundary source tile of V,
+    // Contiguous runs of (row block, head, batch) blocks per XCD:
+    // neighbouring row blocks of a slab share a boundary source tile of V,
     // and on one XCD its second read finds the tile in that XCD's L2.
-    const int gx = gridDim.x, gy = gridDim.y;
-    const int nwg = gx * gy * gridDim.z;
-    int blk = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
-    if (nwg % XCD_COUNT == 0) blk = (blk % XCD_COUNT) * (nwg / XCD_COUNT) + blk / XCD_COUNT;
-    const int bx = blk % gx, by = (blk / gx) % gy, b = blk / (gx * gy);
+    const BlockXYZ blk = xcd_run_block(true);
+    const int bx = blk.x, by = blk.y, b = blk.z;
     const int slab = b * p.hkv + by;
     const int i0 = bx * CROWS;
     const int tid = threadIdx.x;

@@ -28,6 +28,21 @@ inline size_t score_main_lds_bytes(int rows) {
 }
 constexpr int SELECT_THREADS = 1024;
 
+// Workgroups are dealt to the XCDs in turn (linear id modulo XCD_COUNT).
+// With `runs`, the block coordinates are renumbered so that each XCD takes a
+// contiguous run of linear blocks (x fastest) when the grid divides evenly:
+// neighbouring blocks that read the same data then share one XCD's L2.
+struct BlockXYZ {
+    int x, y, z;
+};
+__device__ __forceinline__ BlockXYZ xcd_run_block(bool runs) {
+    const int gx = gridDim.x, gy = gridDim.y;
+    const int nwg = gx * gy * gridDim.z;
+    int blk = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+    if (runs && nwg % XCD_COUNT == 0) blk = (blk % XCD_COUNT) * (nwg / XCD_COUNT) + blk / XCD_COUNT;
+    return BlockXYZ{blk % gx, (blk / gx) % gy, blk / (gx * gy)};
+}
+
 // Ragged batches.  A launch addresses nb sequences; sequence b is stored in
 // batch entry phys(b) of buffers that hold nb_cap entries and has rows(b)
 // rows.  Per-sequence inputs and outputs are indexed by b.  Both arrays live

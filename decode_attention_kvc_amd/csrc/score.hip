@@ -296,14 +296,10 @@ template <bool RANGE>
 __global__ __launch_bounds__(256) void score_main_bf16(ScoreLaunch p) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int NW = 4;
-    // Workgroups are dealt to the eight XCDs in turn; renumbered so that
-    // each XCD takes a contiguous run of (split, head, batch) blocks, the
-    // splits of a slab share the window queries they stage through one L2.
-    const int gx = gridDim.x, gy = gridDim.y;
-    const int nwg = gx * gy * gridDim.z;
-    int blk = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
-    if (nwg % XCD_COUNT == 0) blk = (blk % XCD_COUNT) * (nwg / XCD_COUNT) + blk / XCD_COUNT;
-    const int s = blk % gx, j = (blk / gx) % gy, b = blk / (gx * gy);
+    // Contiguous runs of (split, head, batch) blocks per XCD: the splits of
+    // a slab share the window queries they stage through one L2.
+    const BlockXYZ blk = xcd_run_block(true);
+    const int s = blk.x, j = blk.y, b = blk.z;
     const int slab = b * p.hkv + j;
     const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
     const int l16 = lane & 15, lg = lane >> 4;

@@ -480,7 +480,10 @@ __global__ __launch_bounds__(XNT) void xkv_scores(XkvDecodeLaunch p) {
     constexpr int LPR = R / 8;
     constexpr int NGRP = XNT / LPR;
     constexpr int UNR = G <= 4 ? 16 : 8;
-    const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+    // The chunk splits of a (batch, KV head) pair read the same query
+    // projection inputs: contiguous runs of blocks per XCD share them in L2.
+    const BlockXYZ blk = xcd_run_block(true);
+    const int s = blk.x, j = blk.y, b = blk.z;
     const int slab = b * p.hkv + j, g = p.g;
     const int tid = threadIdx.x, lane = tid % WAVE;
     const int sub = lane % LPR, grp = tid / LPR;
@@ -536,7 +539,10 @@ __global__ __launch_bounds__(XNT) void xkv_attend(XkvDecodeLaunch p) {
     constexpr int CG = R / CW;             //              column groups
     constexpr int RGW = WAVE / CG;         //              row groups per wave
     constexpr int RGS = XNW * RGW;         //              row groups per block
-    const int a = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+    // The row splits of a pair read the same chunk scores and query
+    // projection: contiguous runs of blocks per XCD share them in L2.
+    const BlockXYZ blk = xcd_run_block(true);
+    const int a = blk.x, j = blk.y, b = blk.z;
     const int slab = b * p.hkv + j, g = p.g;
     const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
     const int sub = lane % LPR, grp = tid / LPR;
