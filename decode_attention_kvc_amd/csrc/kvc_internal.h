@@ -14,7 +14,7 @@ constexpr int ATTN_WAVES = 4;    // waves per attention workgroup
 constexpr int ATTN_TARGET_WGS = 256;  // partial workgroups an attention launch aims for
 constexpr int MAX_SPLIT_ROWS = 4096;  // bound on nsplit * padded rows (workspace size)
 constexpr int SCORE_TILE = 32;
-constexpr int SCORE_MAX_TPS = 16;     // tiles per score-statistics workgroup
+constexpr int SCORE_MAX_TPS = 64;     // tiles per score-statistics workgroup
 constexpr int SCORE_QPITCH = 136;     // bf16 per window-query row staged in LDS (272 bytes)
 constexpr int CU_COUNT = 256;         // compute units of the part
 constexpr int XCD_COUNT = 8;          // accelerator dies; workgroups are dealt to them in turn
