@@ -126,16 +126,20 @@ __device__ __forceinline__ void load_qfrag(QFrag& Q, const ScoreLaunch& p, int b
     }
 }
 
-// S[mt][cg][i] = q_row(wave*32 + mt*16 + 4*lg + i) . k_row(t0 + 16*cg + l16)
-__device__ __forceinline__ void score_tile_mfma(const QFrag& Q, const uint16_t* kslab, int t0,
-                                                int l16, int lg, f32x4 S[2][2]) {
-    u32x4 kb[2][4];
+// The K operand fragments of one 32-row tile: rows t0 + 16*cg + l16.
+__device__ __forceinline__ void load_ktile(u32x4 (&kb)[2][4], const uint16_t* kslab, int t0,
+                                           int l16, int lg) {
 #pragma unroll
     for (int cg = 0; cg < 2; ++cg) {
         const uint16_t* kr = kslab + (size_t)(t0 + 16 * cg + l16) * D + 8 * lg;
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) kb[cg][kc] = load16(kr + 32 * kc);
     }
+}
+
+// S[mt][cg][i] = q_row(wave*32 + mt*16 + 4*lg + i) . k_row(t0 + 16*cg + l16)
+__device__ __forceinline__ void score_tile_product(const QFrag& Q, const u32x4 (&kb)[2][4],
+                                                   f32x4 S[2][2]) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -159,8 +163,13 @@ __device__ __forceinline__ void ms_merge(float& m, float& z, float m2, float z2)
     m = mn;
 }
 
-// Pass 1: per window row, max and sum of exp over its visible rows.
-__global__ __launch_bounds__(1024) void score_stats_bf16(ScoreLaunch p) {
+// Pass 1: per window row, max and sum of exp over its visible rows.  Each
+// wave owns 32 window rows and runs them against every tile of its split.
+// PF = 1 keeps the next tile's K loads in flight while a tile is computed
+// (two register sets; at most 512 threads, i.e. 256 window rows, so that
+// the registers fit); PF = 0 serves larger windows one tile at a time.
+template <int PF>
+__global__ __launch_bounds__(PF ? 512 : 1024) void score_stats_bf16(ScoreLaunch p) {
     const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int slab = b * p.hkv + j;
     const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
@@ -185,10 +194,9 @@ __global__ __launch_bounds__(1024) void score_stats_bf16(ScoreLaunch p) {
             const int R = wave * 32 + mt * 16 + 4 * lg + i;
             lim[mt][i] = (R < p.rows) ? T - p.w + R % p.w : -1;
         }
-    for (int tile = tile_begin; tile < tile_end; ++tile) {
-        const int t0 = tile * SCORE_TILE;
+    auto fold = [&](const u32x4 (&kb)[2][4], int t0) {
         f32x4 S[2][2];
-        score_tile_mfma(Q, kslab, t0, l16, lg, S);
+        score_tile_product(Q, kb, S);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -203,6 +211,36 @@ __global__ __launch_bounds__(1024) void score_stats_bf16(ScoreLaunch p) {
                     m[mt][i] = mn;
                 }
             }
+    };
+    if constexpr (PF == 0) {
+        for (int tile = tile_begin; tile < tile_end; ++tile) {
+            u32x4 kb[2][4];
+            load_ktile(kb, kslab, tile * SCORE_TILE, l16, lg);
+            fold(kb, tile * SCORE_TILE);
+        }
+    } else {
+        // Tiles in order (the fold's order is the same as with PF = 0); the
+        // loads inside the loop body are unconditional.
+        const int n = max(0, tile_end - tile_begin);
+        auto t0_of = [&](int k) { return (tile_begin + k) * SCORE_TILE; };
+        if (n > 0) {
+            u32x4 KA[2][4], KB[2][4];
+            load_ktile(KA, kslab, t0_of(0), l16, lg);
+            int k = 0;
+            for (; k + 2 < n; k += 2) {
+                load_ktile(KB, kslab, t0_of(k + 1), l16, lg);
+                fold(KA, t0_of(k));
+                load_ktile(KA, kslab, t0_of(k + 2), l16, lg);
+                fold(KB, t0_of(k + 1));
+            }
+            if (k + 1 < n) {
+                load_ktile(KB, kslab, t0_of(k + 1), l16, lg);
+                fold(KA, t0_of(k));
+                fold(KB, t0_of(k + 1));
+            } else {
+                fold(KA, t0_of(k));
+            }
+        }
     }
     // Merge the 16 lanes (cache-row columns) that share each query row.
 #pragma unroll
@@ -574,7 +612,10 @@ hipError_t launch_score(const ScoreLaunch& p, int dtype, hipStream_t st) {
     } else {
         const int nw = (p.rows + 31) / 32;
         if (!p.lse_obs) {
-            hipLaunchKernelGGL(score_stats_bf16, grid, dim3(nw * WAVE), 0, st, p);
+            if (nw <= 8)
+                hipLaunchKernelGGL(score_stats_bf16<1>, grid, dim3(nw * WAVE), 0, st, p);
+            else
+                hipLaunchKernelGGL(score_stats_bf16<0>, grid, dim3(nw * WAVE), 0, st, p);
             hipLaunchKernelGGL(score_lse_merge, dim3(p.hkv, p.nb), dim3(1024), 0, st, p);
         }
         const dim3 mgrid(p.main_nsplit, p.hkv, p.nb);
