@@ -106,3 +106,28 @@ def test_weyl_increments_closed_forms():
         assert WEYL[width][0] == int(phi_frac * scale)
         assert WEYL[width][1] == int(sqrt3_frac * scale)
     assert WEYL[32] == tuple(w >> 32 for w in WEYL[64])
+
+
+def test_philox4x32_10_known_answer_vectors():
+    # The published known-answer vectors of Philox4x32-10 (Random123, the
+    # library of Salmon et al., SC'11): all-zero, all-ones and the pi-digit
+    # counter/key.  They pin both 32-bit multipliers, the Weyl increments,
+    # the word order of a round and the round count at once.
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "philox4x32_10_kat.json")
+    vecs = json.load(open(path))["vectors"]
+    assert len(vecs) == 3
+    for v in vecs:
+        c = [int(x, 16) for x in v["counter"]]
+        k = [int(x, 16) for x in v["key"]]
+        got = [int(w) for w in philox4x32_10(*c, *k)]
+        assert got == [int(x, 16) for x in v["out"]], v
+    # a plausible slip anywhere in the round changes every vector
+    from oracle import philox as ph
+    c = [int(x, 16) for x in vecs[2]["counter"]]
+    k = [int(x, 16) for x in vecs[2]["key"]]
+    want = [int(x, 16) for x in vecs[2]["out"]]
+    assert [int(w) for w in ph.philox4(c, k, width=32, rounds=9)] != want
+    swapped = ph.philox4([c[2], c[1], c[0], c[3]], k, width=32, rounds=10)
+    assert [int(w) for w in swapped] != want
