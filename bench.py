@@ -1,15 +1,18 @@
 """Decode throughput of attention + eviction over a compressed KV cache, 1 GPU.
 
-Workload (default): Llama-3.1-8B-shaped combined decode — 32 layers, one KV
-leader every 4th layer (8 slots), batch 16, 32 query / 8 KV heads, head dim
-128, bfloat16, 32K-token prompt cache compressed once to K + B = 8320 rows,
-then decode steps with a VASE eviction pass (K 8192, B 128, N_v 128, window
-32, every 128 steps) on the leaders.  A step = every layer's attention (with
-the leaders' fused append) + its share of the periodic eviction.  Inputs are
+Workload (default): Qwen3-14B-shaped long-context decode -- 40 layers, one KV
+leader every 2nd layer (20 slots), batch 4, 40 query / 8 KV heads, head dim
+128, bfloat16, a 128K-token prompt cache compressed once to K + B = 33024
+rows, then decode steps with a VASE eviction pass (K 32768, B 256, N_v 256,
+window 32, every 256 steps) on the leaders.  A step = every layer's attention
+(with the leaders' fused append) + its share of the periodic eviction: the
+timed steps run at the steady state's mean cache length (untimed pre-roll
+steps get there), one pass at its steady-state length (K + B + period rows)
+is timed with HIP events, and its time counts once per period.  Inputs are
 synthetic (seeded normal draws with 1% x20 value outliers) and resident in
 HBM before timing starts.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--mode per-layer|grouped]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--mode ...]
 
 Prints one JSON line.  Only the cpu_baseline leg touches oracle/.
 """
@@ -33,7 +36,10 @@ WORKLOADS = {
         evict=dict(K=8192, B=128, N_v=128, w=32, period=128, seed=0)),
     "qwen3-8b-rcla": dict(
         desc="Qwen3-8B-shaped R-CLA decode, 9 of 36 layers lead, no eviction",
-        n_layers=36, leaders=list(range(0, 36, 4)), nb=1, hq=32, hkv=8, t0=32768, evict=None),
+        n_layers=36, leaders=list(range(0, 36, 4)), nb=1, hq=32, hkv=8, t0=32768, evict=None,
+        # a 135 MB slot fits the 256 MB Infinity Cache: no call follows one
+        # that read the same slot
+        mode="per-layer-interleaved"),
     "qwen3-4b-vase": dict(
         desc="Qwen3-4B-shaped VASE decode: every layer its own cache, 16K tokens generated "
              "from an empty cache",
@@ -44,6 +50,10 @@ WORKLOADS = {
         n_layers=40, leaders=list(range(0, 40, 2)), nb=4, hq=40, hkv=8, t0=131072,
         evict=dict(K=32768, B=256, N_v=256, w=32, period=256, seed=0)),
 }
+
+
+# The largest configuration that fits one GPU: the metric's workload.
+DEFAULT_WORKLOAD = "qwen3-14b-long"
 
 
 def log(*a):
@@ -115,7 +125,8 @@ def cpu_baseline(cfg, cache, qpool, s, budget_s=8.0):
         w = e["w"]
         g_score = torch.empty((nb, hkv, T), device=dev)
         g_rng = torch.empty((nb, hkv, T), device=dev)
-        kvc.kvc_score(cache, 0, qpool[0, s - w + 1:s + 1], g_score, g_rng, None,
+        lo, hi = window_rows(s, w, qpool.shape[1])
+        kvc.kvc_score(cache, 0, qpool[0, lo:hi], g_score, g_rng, None,
                       torch.zeros(kvc.kvc_score_ws_bytes(cache, hq, w), dtype=torch.uint8,
                                   device=dev))
         g_kept = torch.empty((nb, hkv, min(T, e["K"] + e["B"])), dtype=torch.int32, device=dev)
@@ -143,7 +154,8 @@ def cpu_baseline(cfg, cache, qpool, s, budget_s=8.0):
     n_ev = 0
     if e:
         w = e["w"]
-        qo = qpool[0, s - w + 1:s + 1].cpu()
+        lo, hi = window_rows(s, w, qpool.shape[1])
+        qo = qpool[0, lo:hi].cpu()
         dkv = e.get("scoring") == "dkv"
         if dkv:
             r = e.get("rank", 32)
@@ -210,18 +222,28 @@ def cpu_baseline(cfg, cache, qpool, s, budget_s=8.0):
     return baseline, parity
 
 
-def load_traffic(bytes_per_launch):
-    """HBM traffic per attention call from the committed counter summary,
-    or None when the attention source has changed since it was measured."""
+TRAFFIC_FILES = {
+    "llama3.1-8b-combined": "attn_traffic_llama31_8b_combined.json",
+    "qwen3-14b-long": "attn_traffic_qwen3_14b_long.json",
+}
+
+
+def load_traffic(workload, mode, bytes_per_launch):
+    """HBM traffic per attention call from the committed counter summary of
+    the same workload and call order, or None when there is none or the
+    attention source has changed since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "attn_traffic_llama31_8b_combined.json")
+    name = TRAFFIC_FILES.get(workload)
+    if name is None:
+        return None, None
+    path = os.path.join(ROOT, "profiles", name)
     src = os.path.join(ROOT, "decode_attention_kvc_amd", "csrc", "attn.hip")
     try:
         t = json.load(open(path))
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     except (OSError, ValueError):
         return None, None
-    if t.get("attn_source_sha256") != sha:
+    if t.get("attn_source_sha256") != sha or t.get("mode", "per-layer") != mode:
         return None, None
     return round(t["traffic_over_algorithmic"] * bytes_per_launch), t
 
@@ -490,18 +512,71 @@ def xkv_leg(args, cfg, qpool, knew, vnew, steps, warm=3):
                 data="synthetic cross-layer low-rank caches (rank-48 shared basis + 0.1 noise)")
 
 
+def window_rows(s, w, n_pool):
+    """Rows [lo, lo + w) of a query pool that form the observation window of
+    a pass after step s: the w rows ending at row s, or the pool's first w
+    rows while fewer than w steps have run (a slice never starts below 0)."""
+    if w < 1 or n_pool < w:
+        raise ValueError(f"a window of {w} rows needs a query pool of at least {w} rows "
+                         f"(it has {n_pool})")
+    hi = min(max(s, 0) + 1, n_pool)
+    lo = max(0, hi - w)
+    return lo, lo + w
+
+
+def step_plan(ev, t0, W, S):
+    """Where the timed steps sit in the decode, and how far the decode runs
+    on after them so that one eviction pass is timed.
+
+    Returns (pre, n_main, pass_step): `pre` untimed steps run before the
+    warm-up, so that the timed steps centre on the mean steady-state length
+    K + B + (P + 1) / 2 of a prompt workload (the cache starts at K + B rows
+    after the prompt compression and grows by one row per step until the
+    pass at K + B + P); the warm-up and timed steps end at step n_main - 1;
+    `pass_step` is the step after which the next pass runs (None without
+    eviction).  A cache grown from empty (t0 = 0) starts timing at once, and
+    its next pass is the first step that leaves more than K + B rows on a
+    period boundary."""
+    if not ev:
+        return 0, W + S, None
+    P, kb = ev["period"], ev["K"] + ev["B"]
+    pre = max(0, (P + 1) // 2 - W - S // 2) if t0 else 0
+    n_main = pre + W + S
+    s = n_main - 1
+    while True:
+        if (s + 1) % P == 0 and (t0 == 0 and s + 1 > kb or t0 > 0 and s >= n_main - 1):
+            if s + 1 >= ev["w"]:
+                return pre, n_main, s
+        s += 1
+
+
+def _leg(name, fn, *a, **k):
+    """Run one side leg; a Python exception becomes an "error" entry so that
+    the headline line is still printed."""
+    try:
+        r = fn(*a, **k)
+        log(f"[bench] {name}: {r}")
+        return r
+    except Exception as exc:              # noqa: BLE001  (reported, not hidden)
+        import traceback
+        traceback.print_exc(file=sys.stderr)
+        log(f"[bench] {name} leg failed: {type(exc).__name__}: {exc}")
+        return {"error": f"{type(exc).__name__}: {exc}"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
-                    help="timed decode steps (default 256; the Qwen3-4B workload: its 16384 "
+                    help="timed decode steps (default 20; the Qwen3-4B workload: its 16384 "
                          "generated tokens)")
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama3.1-8b-combined", choices=list(WORKLOADS))
-    ap.add_argument("--mode", default="per-layer",
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(WORKLOADS))
+    ap.add_argument("--mode", default=None,
                     choices=["per-layer", "per-layer-interleaved", "grouped"],
-                    help="per-layer-interleaved issues the same calls round-robin over the "
-                         "slots, so no call can find its slab in the Infinity Cache")
+                    help="call order (default: the workload's own; per-layer-interleaved "
+                         "issues the calls round-robin over the slots, so that no call can "
+                         "find its slab in the Infinity Cache)")
     ap.add_argument("--scoring", default="attnv", choices=["attnv", "dkv"],
                     help="eviction scores: observation-window attention (VASE-AttnV) or the "
                          "leverage of Gaussian-sketched [K|V] rows (VASE-DKV)")
@@ -536,6 +611,8 @@ def main():
     from decode_attention_kvc_amd.loop import Decoder
 
     cfg = dict(WORKLOADS[args.workload])
+    if args.mode is None:
+        args.mode = cfg.get("mode", "per-layer")
     if cfg["evict"]:
         cfg["evict"] = dict(cfg["evict"], scoring=args.scoring, rank=args.rank)
     dev = "cuda"
@@ -544,7 +621,9 @@ def main():
     ev = cfg["evict"]
     n_slots = len(leaders)
     W = args.warmup
-    S = args.steps if args.steps is not None else cfg.get("steps", 256)
+    S = args.steps if args.steps is not None else cfg.get("steps", 20)
+    if S < 1 or W < 0:
+        sys.exit("--steps must be >= 1 and --warmup >= 0")
     if t0 == 0:
         # A cache grown from empty: the legs built around a prompt cache
         # (ragged prompts, the int8 form of the compressed prompt, the
@@ -553,10 +632,14 @@ def main():
         if args.ragged_only or args.xkv_only:
             sys.exit("--ragged-only / --xkv-only need a workload with a prompt")
     grouped_leg = not args.no_grouped and args.mode != "grouped" and n_slots < L
-    n_total = W + S + 1 + (S + 1 if grouped_leg else 0)
-    if ev and not args.no_ragged:        # the ragged leg warms up for a full period
+    pre, n_main, pass_step = step_plan(ev, t0, W, S)
+    n_dec = (pass_step + 1) if pass_step is not None else n_main   # main leg + the run-on
+    n_total = n_dec + (S + 1 if grouped_leg else 0)
+    if ev and not args.no_ragged and args.workload == "llama3.1-8b-combined":
+        # the ragged leg warms up for a full period
         n_total = max(n_total, max(W, ev["period"]) + S + 1)
     if ev:
+        n_total = max(n_total, ev["w"])
         steady_cap = ev["K"] + ev["B"] + ev["period"]
     else:
         steady_cap = t0 + n_total
@@ -637,74 +720,121 @@ def main():
             dec.ws_attn = torch.zeros(max(16, kvc.kvc_decode_attn_ws_bytes(
                 dec.cache, max(len(g) for g in dec.groups), hq)), dtype=torch.uint8, device=dev)
         dec.events = [] if events else None
+        dec.pass_events = [] if events else None
         n_ev = 0
         for s in range(first, first + steps):
             n_ev += bool(dec.step(s, qpool, lsepool, knew, vnew, out))
         return n_ev
 
-    # ---- warm-up, then the timed steps
-    run(W, 0, args.mode, False)
+    # ---- pre-roll and warm-up (untimed), then the timed steps
+    if pre:
+        run(pre, 0, args.mode, False)
+        log(f"[bench] pre-roll: {pre} steps to {dec.cache.t_len} rows (timed steps centre on the "
+            f"mean steady-state length)")
+    run(W, pre, args.mode, False)
     torch.cuda.synchronize()
     log(f"[bench] warm-up done ({W} steps), timing {S} steps ({args.mode})")
     t_start = time.perf_counter()
-    n_evict = run(S, W, args.mode, True)
+    n_evict = run(S, pre + W, args.mode, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    ms_per_step = 1e3 * wall / S
     events = dec.events            # one pair per step around its attention calls
+    pass_in = [(a.elapsed_time(b), t, s) for a, b, t, s in dec.pass_events]
     att_ms = [a.elapsed_time(b) for a, b, _, _ in events]
     att_bytes = [step_attn_bytes(dec, args.mode, nb, hq, hkv, t) for (_, _, t, _) in events]
     n_calls = sum(n for _, _, _, n in events)
     att_total_ms = sum(att_ms)
     att_gbps = sum(att_bytes) / (att_total_ms * 1e-3) / 1e9
     avg_launch_us = 1e3 * att_total_ms / n_calls
-    tok_s = nb * S / wall
-    log(f"[bench] {S} steps in {wall:.3f} s: {tok_s:.1f} tok/s, attention {att_gbps:.0f} GB/s "
-        f"({100 * att_gbps / HBM_PEAK_GBPS:.1f}% of peak), avg launch {avg_launch_us:.1f} us, "
-        f"{n_evict} eviction passes")
-    # whole-step algorithmic bytes (attention + eviction) over the wall time
     t_mean = sum(t for _, _, t, _ in events) / len(events)
-    step_bytes = sum(att_bytes) + (n_evict * evict_bytes(cfg, ev["K"] + ev["B"] + ev["period"])
-                                   if ev else 0)
-    step_gbps = step_bytes / wall / 1e9
+    last_step = n_main - 1
+
+    # ---- the eviction pass: timed inside the region, else on the next one
+    passes = list(pass_in)
+    if ev and not pass_in:
+        n_run = pass_step - n_main + 1
+        run(n_run, n_main, args.mode, True)
+        torch.cuda.synchronize()
+        passes = [(a.elapsed_time(b), t, s) for a, b, t, s in dec.pass_events]
+        last_step = pass_step
+        log(f"[bench] ran on {n_run} untimed steps to the pass after step {pass_step}")
+    eviction = None
+    if ev:
+        if not passes:
+            raise RuntimeError("no eviction pass ran")
+        t_pass_ms = sum(p[0] for p in passes) / len(passes)
+        pass_rows = max(p[1] for p in passes)
+        # passes per step: a prompt workload runs one every P steps in its
+        # steady state; a cache grown from empty is timed over its whole
+        # generation, so the passes it ran are the ones it has
+        per_step = (len(pass_in) / S) if t0 == 0 else 1.0 / ev["period"]
+        e_bytes = evict_bytes(cfg, pass_rows)
+        eviction = dict(ms_per_pass=round(t_pass_ms, 4), rows_at_pass=pass_rows,
+                        passes_timed=len(passes), passes_in_timed_steps=len(pass_in),
+                        passes_per_step=round(per_step, 6),
+                        bytes_per_pass=e_bytes,
+                        GBps=round(e_bytes / (t_pass_ms * 1e-3) / 1e9, 1),
+                        timing="HIP events around each pass's calls (score + range, select, "
+                               "compact on every leader slot)")
+    else:
+        t_pass_ms, per_step, e_bytes = 0.0, 0.0, 0
+    pass_in_ms = sum(p[0] for p in pass_in)
+    ms_per_step = (1e3 * wall - pass_in_ms) / S + per_step * t_pass_ms
+    tok_s = nb * 1e3 / ms_per_step
+    step_bytes = sum(att_bytes) / S + per_step * e_bytes
+    step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"[bench] {S} steps in {wall:.3f} s wall ({len(pass_in)} passes inside); "
+        f"attention {att_gbps:.0f} GB/s ({100 * att_gbps / HBM_PEAK_GBPS:.1f}% of peak), avg "
+        f"call {avg_launch_us:.1f} us; pass {t_pass_ms:.3f} ms every {ev['period'] if ev else '-'} "
+        f"steps -> {ms_per_step:.4f} ms/step, {tok_s:.1f} tok/s")
 
     grouped = None
     if grouped_leg:
-        first = W + S
-        torch.cuda.synchronize()
-        g0 = time.perf_counter()
-        g_ev = run(S, first, "grouped", True)
-        torch.cuda.synchronize()
-        gwall = time.perf_counter() - g0
-        gev = dec.events
-        g_ms = sum(a.elapsed_time(b) for a, b, _, _ in gev)
-        g_bytes = sum(step_attn_bytes(dec, "grouped", nb, hq, hkv, t) for (_, _, t, _) in gev)
-        g_calls = sum(n for _, _, _, n in gev)
-        grouped = dict(value=round(nb * S / gwall, 2), unit="tokens/s",
-                       ms_per_step=round(1e3 * gwall / S, 4),
-                       attention_GBps=round(g_bytes / (g_ms * 1e-3) / 1e9, 1),
-                       attention_frac=round(g_bytes / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                       avg_launch_us=round(1e3 * g_ms / g_calls, 2), eviction_passes=g_ev)
-        log(f"[bench] grouped: {grouped}")
+        def grouped_run():
+            first = n_dec
+            torch.cuda.synchronize()
+            g0 = time.perf_counter()
+            g_ev = run(S, first, "grouped", True)
+            torch.cuda.synchronize()
+            gwall = time.perf_counter() - g0
+            gev = dec.events
+            g_ms = sum(a.elapsed_time(b) for a, b, _, _ in gev)
+            g_pass_ms = sum(a.elapsed_time(b) for a, b, _, _ in dec.pass_events)
+            g_bytes = sum(step_attn_bytes(dec, "grouped", nb, hq, hkv, t) for (_, _, t, _) in gev)
+            g_calls = sum(n for _, _, _, n in gev)
+            g_ms_step = (1e3 * gwall - g_pass_ms) / S + per_step * t_pass_ms
+            return dict(value=round(nb * 1e3 / g_ms_step, 2), unit="tokens/s",
+                        ms_per_step=round(g_ms_step, 4),
+                        attention_GBps=round(g_bytes / (g_ms * 1e-3) / 1e9, 1),
+                        attention_frac=round(g_bytes / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                        avg_launch_us=round(1e3 * g_ms / g_calls, 2),
+                        eviction_passes_in_timed_steps=g_ev,
+                        eviction="the main leg's pass time, amortized the same way")
+        grouped = _leg("grouped", grouped_run)
+        if isinstance(grouped, dict) and "error" not in grouped:
+            last_step = n_dec + S - 1
+        dec.mode = args.mode
 
     int8 = None
     if not args.no_int8:
-        int8 = int8_leg(args, cfg, dec, qpool, lsepool, knew, vnew, out, S)
-        log(f"[bench] int8: {int8}")
+        int8 = _leg("int8", int8_leg, args, cfg, dec, qpool, lsepool, knew, vnew, out, S)
+        torch.cuda.empty_cache()
 
     ragged_res = None
-    if not args.no_ragged and ev and args.scoring == "attnv":
+    if (not args.no_ragged and ev and args.scoring == "attnv"
+            and args.workload == "llama3.1-8b-combined"):
         log("[bench] ragged leg: setting up")
-        ragged_res = ragged_leg(args, cfg, qpool, lsepool, knew, vnew, out, S, warm=W)
-        log(f"[bench] ragged: {ragged_res}")
+        ragged_res = _leg("ragged", ragged_leg, args, cfg, qpool, lsepool, knew, vnew, out, S,
+                          warm=W)
+        torch.cuda.empty_cache()
 
     xkv_res = None
     if not args.no_xkv and args.workload == "llama3.1-8b-combined":
         log("[bench] xkv leg: factorising the windows")
         dec.spare = None
         torch.cuda.empty_cache()
-        xkv_res = xkv_leg(args, cfg, qpool, knew, vnew, S, warm=W)
-        log(f"[bench] xkv: {xkv_res}")
+        xkv_res = _leg("xkv", xkv_leg, args, cfg, qpool, knew, vnew, S, warm=W)
+        torch.cuda.empty_cache()
 
     if args.copy_calibration:
         # Two plain copies of known size for scaling the memory counters:
@@ -724,11 +854,13 @@ def main():
     cpu = parity = None
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host (bounded sample)")
-        cpu, parity = cpu_baseline(cfg, dec.cache, qpool, W + S - 1)
-        log(f"[bench] cpu baseline: {cpu}")
-        log(f"[bench] parity on the sample: {parity}")
+        r = _leg("cpu_baseline", cpu_baseline, cfg, dec.cache, qpool, last_step)
+        if isinstance(r, tuple):
+            cpu, parity = r
+        else:
+            cpu = parity = r
 
-    traffic, tinfo = load_traffic(sum(att_bytes) / n_calls)
+    traffic, tinfo = load_traffic(args.workload, args.mode, sum(att_bytes) / n_calls)
     res = {
         "metric": METRIC,
         "value": round(tok_s, 2),
@@ -750,7 +882,11 @@ def main():
                 "period": ev["period"], "scoring": ev["scoring"]} if ev else {}),
             **({"sketch_rank": ev["rank"]} if ev and ev["scoring"] == "dkv" else {}),
             "mean_cache_rows": round(t_mean, 1),
+            "pre_roll_steps": pre,
         },
+        "step_time": ("(wall of the timed steps - the GPU time of passes inside them) / steps "
+                      "+ passes per step x the timed pass's GPU time"),
+        "decode_ms_per_step": round((1e3 * wall - pass_in_ms) / S, 4),
         "achieved_GBps": round(step_gbps, 1),
         "hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
         "roofline": {
@@ -765,9 +901,10 @@ def main():
             "avg_launch_us": round(avg_launch_us, 3),
             "launches": n_calls,
             "bytes_per_launch": round(sum(att_bytes) / n_calls),
-            "timing": "HIP events around each step's attention calls (eviction outside)",
+            "timing": "HIP events around each step's attention calls, on the stream they run on",
         },
-        "eviction_passes_timed": n_evict,
+        "eviction": eviction,
+        "eviction_passes_timed": len(passes) if ev else 0,
         "initial_pass_ms": None if initial_ms is None else round(initial_ms, 3),
         "grouped": grouped,
         "int8": int8,

@@ -77,7 +77,12 @@ class Decoder:
                                                 for g in self.groups if r < len(g)]}
         if mode not in ("grouped", *self.order):
             raise ValueError(f"unknown mode {mode!r}")
+        if evict and evict["period"] < evict["w"]:
+            # a pass after step s scores the window of steps s - w + 1 .. s
+            raise ValueError(f"the eviction period ({evict['period']}) must be at least the "
+                             f"observation window ({evict['w']})")
         self.events = [] if record_events else None
+        self.pass_events = [] if record_events else None
         self._evict_bufs = None
 
     # ------------------------------------------------------------------ decode
@@ -111,6 +116,9 @@ class Decoder:
         e = self.evict_cfg
         if e and (s + 1) % e["period"] == 0 and c.t_len > e["K"] + e["B"]:
             w = e["w"]
+            if s + 1 < w or s >= n_steps:
+                raise ValueError(f"step {s}: the window needs query rows {s - w + 1}..{s} of a "
+                                 f"pool of {n_steps}")
             fresh = (s + 1 >= w and (self.last_compaction is None
                                      or self.last_compaction <= s - w + 1 - 1))
             windows = []
@@ -118,7 +126,13 @@ class Decoder:
                 q_obs = qpool[leader, s - w + 1:s + 1]
                 lse = lsepool[leader, s - w + 1:s + 1] if fresh else None
                 windows.append((q_obs, lse))
+            ev1 = self._ev_begin()
+            t_pass = c.t_len
             self.evict(windows, self.round)
+            if ev1 is not None:
+                e1 = torch.cuda.Event(enable_timing=True)
+                e1.record()
+                self.pass_events.append((ev1, e1, t_pass, s))
             self.round += 1
             self.last_compaction = s
             return True

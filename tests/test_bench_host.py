@@ -68,3 +68,54 @@ def test_append_rows_outliers():
     assert torch.all(per_seq == round(0.01 * n))     # round(1% of the rows) each
     assert torch.equal(v1[changed], 20.0 * v0[changed])
     assert torch.equal(v1[~changed], v0[~changed])
+
+
+@pytest.mark.parametrize("W,S", [(5, 20), (2, 1), (0, 1), (3, 256)])
+@pytest.mark.parametrize("name", list(bench.WORKLOADS))
+def test_step_plan_and_windows(name, W, S):
+    """The steps the bench runs and the window slices it takes stay inside
+    the query pool, a pass is always timed, and the timed steps of a prompt
+    workload centre on the steady state's mean length."""
+    w_ = bench.WORKLOADS[name]
+    ev, t0 = w_["evict"], w_["t0"]
+    pre, n_main, pass_step = bench.step_plan(ev, t0, W, S)
+    assert n_main == pre + W + S
+    if ev is None:
+        assert pass_step is None and pre == 0
+        return
+    P, kb = ev["period"], ev["K"] + ev["B"]
+    assert pass_step >= n_main - 1 and (pass_step + 1) % P == 0
+    assert pass_step + 1 >= ev["w"]
+    if t0:
+        assert pass_step - (n_main - 1) < P            # the next pass, not a later one
+        first = pre + W                                  # rows = K + B + step + 1
+        if S < P - W:
+            mid = kb + first + 1 + (S - 1) / 2
+            assert abs(mid - (kb + (P + 1) / 2)) <= 1.0
+    else:
+        assert pass_step + 1 > kb
+    # every window the bench slices exists and has w rows
+    n_pool = pass_step + 1
+    for s in range(0, n_pool):
+        lo, hi = bench.window_rows(s, ev["w"], max(n_pool, ev["w"]))
+        assert 0 <= lo and hi - lo == ev["w"] and hi <= max(n_pool, ev["w"])
+        if s + 1 >= ev["w"]:
+            assert hi == s + 1                           # the w rows ending at step s
+
+
+def test_window_rows_driver_command():
+    # --steps 20 --warmup 5 with w = 32: the last step is 24; the slice used
+    # to start at -7 (an empty slice); now it is the pool's first 32 rows
+    assert bench.window_rows(24, 32, 400) == (0, 32)
+    assert bench.window_rows(255, 32, 400) == (224, 256)
+    assert bench.window_rows(1, 32, 33) == (0, 32)
+    with pytest.raises(ValueError):
+        bench.window_rows(5, 32, 31)
+
+
+def test_decoder_rejects_period_shorter_than_window():
+    from decode_attention_kvc_amd.loop import Decoder
+    import decode_attention_kvc_amd as kvc
+    c = kvc.Cache.empty(1, 1, 2, 64, dtype=torch.float32, device="cpu")
+    with pytest.raises(ValueError, match="period"):
+        Decoder(2, [0], c, c, 8, evict=dict(K=8, B=2, N_v=1, w=32, period=16, seed=0))

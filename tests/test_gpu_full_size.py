@@ -219,3 +219,69 @@ def test_qwen3_14b_long_initial_pass_full_size():
                                     [(0, 0, 0), (1, 2, 3), (38, 3, 7), (39, 1, 5)], L, hq, hkv)
     say(f"  decode at T={dec.cache.t_len}: max |o - ref| = {worst:.2e}")
     assert worst <= 2e-2
+
+
+def _steady_pass(L, leaders, nb, hq, hkv, ev, picks, seed, label):
+    """A steady-state periodic pass at full size, in the bench's launch
+    configuration: the cache starts at K + B rows, the Decoder runs one
+    period of steps with fused appends, and the pass after the last step
+    scores the window with the decode log-normalisers (no compaction inside
+    the window), selects and compacts every leader slab.  The sampled slabs
+    are snapshotted one step before the pass; the oracle re-runs that pass
+    (window score, range, selection with seed + 1, compaction) on the
+    snapshot plus the appended row."""
+    t0, P, w = ev["K"] + ev["B"], ev["period"], ev["w"]
+    n_slots = len(leaders)
+    say(f"steady pass {label}: setup ({t0} rows, {P} steps)")
+    big, qpool, lsepool, knew, vnew = make_state(L, leaders, nb, hq, hkv, t0, ev, P, seed=seed,
+                                                 t_cap=t0 + P + 64)
+    spare = kvc.Cache.empty(n_slots, nb, hkv, t0 + P + 64, device=DEV)
+    dec = Decoder(L, leaders, big, spare, hq, evict=ev)
+    out = torch.empty((L, nb, hq, 128), device=DEV)
+    for s in range(P - 1):
+        assert not dec.step(s, qpool, lsepool, knew, vnew, out)
+    torch.cuda.synchronize()
+    snap = {p: slab64(dec.cache, *p) for p in picks}
+    assert dec.step(P - 1, qpool, lsepool, knew, vnew, out)     # appends, then the pass
+    torch.cuda.synchronize()
+    pre_t = t0 + P
+    assert dec.cache.t_len == t0
+    say(f"  pass at {pre_t} rows done; checking {len(picks)} sampled slabs against the oracle")
+    g = hq // hkv
+    ties = 0
+    for (slot, b, j) in picks:
+        K0, V0 = snap[(slot, b, j)]
+        Kp = np.concatenate([K0, knew[P - 1, slot, b, j].double().cpu().numpy()[None]], 0)
+        Vp = np.concatenate([V0, vnew[P - 1, slot, b, j].double().cpu().numpy()[None]], 0)
+        assert len(Kp) == pre_t
+        leader = leaders[slot]
+        qo = qpool[leader, P - w:P, b, j * g:(j + 1) * g].double().cpu().numpy()
+        sc = oracle.window_score(qo, Kp, pre_t)
+        d = oracle.select_detail(sc, oracle.value_range(Vp), pre_t, ev["K"], ev["B"], ev["N_v"],
+                                 ev["seed"] + 1, leader, b, j)
+        K1, V1 = slab64(dec.cache, slot, b, j)
+        kept = _rows_of(Kp, K1)
+        assert np.all(np.diff(kept) > 0)                 # ascending original rows
+        t, bad = band_compare(kept, d)
+        say(f"  slab (slot {slot}, b {b}, kv head {j}): {len(kept)} kept, {t} ties, "
+            f"{bad} mismatches")
+        ties += t
+        assert bad == 0, (slot, b, j)
+        assert np.array_equal(K1, Kp[kept]) and np.array_equal(V1, Vp[kept])
+    say(f"  steady-state pass {label}: kept sets match, {ties} ties within the band")
+
+
+def test_llama31_8b_combined_steady_pass_full_size():
+    """32 layers, 8 leaders, batch 16, 32/8 heads: the pass at 8448 rows
+    (K 8192, B 128, N_v 128, w 32, every 128 steps)."""
+    ev = dict(K=8192, B=128, N_v=128, w=32, period=128, seed=0)
+    _steady_pass(32, list(range(0, 32, 4)), 16, 32, 8, ev,
+                 [(0, 0, 0), (3, 9, 4), (7, 15, 7)], seed=11, label="Llama-3.1-8B shape")
+
+
+def test_qwen3_14b_long_steady_pass_full_size():
+    """40 layers, 20 leaders, batch 4, 40/8 heads (g = 5, 160 window rows):
+    the pass at 33280 rows (K 32768, B 256, N_v 256, w 32, every 256 steps)."""
+    ev = dict(K=32768, B=256, N_v=256, w=32, period=256, seed=3)
+    _steady_pass(40, list(range(0, 40, 2)), 4, 40, 8, ev,
+                 [(0, 0, 0), (11, 2, 5), (19, 3, 7)], seed=13, label="Qwen3-14B shape")

@@ -201,6 +201,8 @@ SCORE_CASES = [
     (torch.bfloat16, 1, 40, 8, 2113, 32, False),
     (torch.bfloat16, 2, 32, 8, 1500, 32, True),
     (torch.bfloat16, 1, 16, 8, 300, 5, True),
+    (torch.bfloat16, 1, 32, 8, 8448, 32, True),      # Llama-3.1-8B steady pass length
+    (torch.bfloat16, 1, 40, 8, 33280, 32, True),     # Qwen3-14B steady pass: g 5, 160 rows
     (torch.float32, 1, 8, 2, 1024, 32, False),
     (torch.float32, 1, 8, 2, 1024, 32, True),
 ]
@@ -242,6 +244,9 @@ SELECT_CASES = [
     (2, 8, 4352, 4096, 128, 64),
     (1, 8, 8448, 8192, 128, 128),
     (1, 2, 32768, 8192, 128, 128),
+    (1, 2, 33280, 32768, 256, 256),      # Qwen3-14B steady pass
+    (1, 1, 36864, 32768, 256, 256),      # the longest slab whose keys stay in LDS
+    (1, 1, 36865, 32768, 256, 256),      # one row more: keys in the workspace
     (1, 1, 300, 100, 0, 0),
     (1, 1, 300, 100, 10, 100),
     (1, 2, 200, 250, 32, 16),            # keep everything
@@ -297,14 +302,18 @@ def test_compact_bit_exact(dtype, pattern):
     kvc.kvc_compact(src, 1, kept, n_keep, dst)
     torch.cuda.synchronize()
     dst.t_len = n_keep
-    Ks, Vs = src.k_rows(1), src.v_rows(1)
-    idx = kept.long().clamp(max=T - 1)
-    Kr = torch.gather(Ks, 2, idx[..., None].expand(-1, -1, -1, 128))
-    Vr = torch.gather(Vs, 2, idx[..., None].expand(-1, -1, -1, 128))
-    Kr[1, 2, 7] = 0
-    Vr[1, 2, 7] = 0
-    assert torch.equal(dst.k_rows(1), Kr)
-    assert torch.equal(dst.v_rows(1), Vr)
+    K, V = slab_np(src, 1)
+    Kd, Vd = slab_np(dst, 1)
+    kp = kept.cpu().numpy()
+    for b in range(nb):
+        for j in range(hkv):
+            rows = kp[b, j]
+            ok = rows < T
+            Kr, Vr = oracle.compact(K[b, j], V[b, j], rows[ok])
+            assert np.array_equal(Kd[b, j][ok], Kr) and np.array_equal(Vd[b, j][ok], Vr)
+            # an index past the slab's rows gives a zero row (library contract)
+            assert np.all(Kd[b, j][~ok] == 0) and np.all(Vd[b, j][~ok] == 0)
+    assert not np.all(kp[1, 2] < T)
 
 
 def test_select_sampling_law_gpu():
