@@ -6,9 +6,11 @@ Importing the package loads the library and fails if it is not built.
 """
 from ._lib import (  # noqa: F401
     Cache, KvcError, EXPORTS, HEAD_DIM, T_ALIGN, KVC_F32, KVC_BF16, KVC_OK, KVC_EINVAL,
-    KVC_EDTYPE, KVC_EALIGN, KVC_EWORKSPACE, KVC_EALIAS, KVC_EHIP, lib, strerror,
+    KVC_EDTYPE, KVC_EALIGN, KVC_EWORKSPACE, KVC_EALIAS, KVC_EHIP, KVC_ESCRATCH,
+    NOALLOC_SCRATCH_BYTES, lib, strerror,
     kvc_version, kvc_strerror, kvc_share_map, kvc_append, kvc_decode_attn_ws_bytes,
-    kvc_decode_attn, kvc_value_range, kvc_score_ws_bytes, kvc_score, kvc_select_ws_bytes,
+    kvc_decode_attn, kvc_decode_attn_noalloc, kvc_value_range, kvc_score_ws_bytes, kvc_score,
+    kvc_select_ws_bytes,
     kvc_select, kvc_select_seq, kvc_compact, kvc_philox_words, kvc_dkv_ws_bytes, kvc_dkv_score,
     kvc_gaussian_bf16, QCache, kvc_q8_quantize, kvc_q8_append, kvc_q8_decode_attn_ws_bytes,
     kvc_q8_decode_attn, XkvStore, kvc_xkv_factor_ws_bytes, kvc_xkv_factor, kvc_xkv_decode_ws_bytes,

@@ -18,6 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvc.so")
 
 KVC_OK, KVC_EINVAL, KVC_EDTYPE, KVC_EALIGN, KVC_EWORKSPACE, KVC_EALIAS, KVC_EHIP = 0, -1, -2, -3, -4, -5, -6
+KVC_ESCRATCH = -7
+NOALLOC_SCRATCH_BYTES = 32 << 20
 KVC_F32, KVC_BF16 = 0, 1
 HEAD_DIM = 128
 T_ALIGN = 64
@@ -25,7 +27,7 @@ V_TILE = 32
 
 EXPORTS = (
     "kvc_version", "kvc_strerror", "kvc_share_map", "kvc_append",
-    "kvc_decode_attn_ws_bytes", "kvc_decode_attn", "kvc_value_range",
+    "kvc_decode_attn_ws_bytes", "kvc_decode_attn", "kvc_decode_attn_noalloc", "kvc_value_range",
     "kvc_score_ws_bytes", "kvc_score", "kvc_select_ws_bytes", "kvc_select", "kvc_select_seq",
     "kvc_compact", "kvc_philox_words", "kvc_dkv_ws_bytes", "kvc_dkv_score",
     "kvc_gaussian_bf16", "kvc_q8_quantize", "kvc_q8_append", "kvc_q8_decode_attn_ws_bytes",
@@ -92,6 +94,8 @@ def lib():
             "kvc_decode_attn_ws_bytes": ([cp, i32, i32, szp], i32),
             "kvc_decode_attn": ([cp, vp, i64, i32, ip, i32, f32, vp, vp, i32, vp, i64, vp, i64,
                                  vp, sz, vp], i32),
+            "kvc_decode_attn_noalloc": ([cp, vp, i64, i32, ip, i32, f32, vp, vp, i32, vp, i64,
+                                         vp, i64, vp], i32),
             "kvc_value_range": ([cp, i32, vp, vp], i32),
             "kvc_score_ws_bytes": ([cp, i32, i32, szp], i32),
             "kvc_score": ([cp, i32, vp, i32, i32, f32, vp, vp, vp, vp, sz, vp], i32),
@@ -432,6 +436,22 @@ def kvc_decode_attn(cache, q, q_slot, out, lse=None, ws=None, scale=0.0, k_new=N
                                  float(scale), _ptr(k_new), _ptr(v_new), append_slot, _ptr(out),
                                  out_layer_stride, _ptr(lse), lse_layer_stride, _ptr(ws),
                                  ws_bytes, _stream(stream)), "kvc_decode_attn")
+
+
+def kvc_decode_attn_noalloc(cache, q, q_slot, out, lse=None, scale=0.0, k_new=None,
+                            v_new=None, append_slot=-1, q_layer_stride=0, out_layer_stride=0,
+                            lse_layer_stride=0, n_q_layers=None, n_q_heads=None, stream=None):
+    """kvc_decode_attn with its partials in the library's own device array
+    (no workspace argument, nothing allocated)."""
+    c = cache.desc()
+    nq = len(q_slot) if n_q_layers is None else n_q_layers
+    hq = q.shape[-2] if n_q_heads is None else n_q_heads
+    slots = (ctypes.c_int32 * max(1, nq))(*[int(s) for s in q_slot])
+    _check(lib().kvc_decode_attn_noalloc(ctypes.byref(c), _ptr(q), q_layer_stride, nq, slots, hq,
+                                         float(scale), _ptr(k_new), _ptr(v_new), append_slot,
+                                         _ptr(out), out_layer_stride, _ptr(lse),
+                                         lse_layer_stride, _stream(stream)),
+           "kvc_decode_attn_noalloc")
 
 
 def kvc_value_range(cache, slot, rng, stream=None):

@@ -351,6 +351,9 @@ const char* kvc_strerror(int status) {
         case KVC_EWORKSPACE: return "workspace missing or too small";
         case KVC_EALIAS: return "source and destination memory overlap";
         case KVC_EHIP: return "HIP runtime error at launch";
+        case KVC_ESCRATCH:
+            return "the call needs more scratch than the no-allocation entry point's "
+                   "32 MiB device array holds; use the call with a caller workspace";
         default: return "unknown status";
     }
 }
@@ -476,6 +479,22 @@ int kvc_decode_attn(const kvc_cache* c, const void* q, int64_t q_layer_stride, i
             return KVC_EHIP;
     }
     return hip_status();
+}
+
+int kvc_decode_attn_noalloc(const kvc_cache* c, const void* q, int64_t q_layer_stride,
+                            int n_q_layers, const int32_t* q_slot, int n_q_heads, float scale,
+                            const void* k_new, const void* v_new, int append_slot, float* out,
+                            int64_t out_layer_stride, float* lse, int64_t lse_layer_stride,
+                            kvc_stream_t stream) {
+    size_t need = 0;
+    int st = kvc_decode_attn_ws_bytes(c, n_q_layers, n_q_heads, &need);
+    if (st) return st;
+    if (need > (size_t)KVC_NOALLOC_SCRATCH_BYTES) return KVC_ESCRATCH;
+    void* ws = nullptr;
+    if (noalloc_scratch((hipStream_t)stream, &ws) != hipSuccess) return KVC_EHIP;
+    return kvc_decode_attn(c, q, q_layer_stride, n_q_layers, q_slot, n_q_heads, scale, k_new,
+                           v_new, append_slot, out, out_layer_stride, lse, lse_layer_stride, ws,
+                           (size_t)KVC_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int kvc_value_range(const kvc_cache* c, int slot, float* range, kvc_stream_t stream) {

@@ -226,6 +226,9 @@ struct XkvDecodeLaunch {
 // hipSuccess or the launch error.
 // Launches the partial kernel and the merge kernel.
 hipError_t launch_attn(const AttnLaunch& p, int dtype, int nt, hipStream_t s);
+// Device address of the current device's no-allocation scratch array
+// (KVC_NOALLOC_SCRATCH_BYTES); `stream` (may be NULL) must be on that device.
+hipError_t noalloc_scratch(hipStream_t stream, void** ptr);
 hipError_t launch_attn_combine(const AttnLaunch& p, hipStream_t s);
 hipError_t launch_attn_q8(const Q8AttnLaunch& p, int nt, hipStream_t s);
 hipError_t launch_q8_quantize(const Q8QuantLaunch& p, hipStream_t s);

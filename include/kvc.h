@@ -58,7 +58,9 @@ typedef enum kvc_status {
     KVC_EALIGN = -3,      /* a pointer is NULL or not 16-byte aligned      */
     KVC_EWORKSPACE = -4,  /* workspace missing or smaller than required    */
     KVC_EALIAS = -5,      /* source and destination memory overlap         */
-    KVC_EHIP = -6         /* the HIP runtime reported a launch error       */
+    KVC_EHIP = -6,        /* the HIP runtime reported a launch error       */
+    KVC_ESCRATCH = -7     /* the call needs more than the library's own
+                             scratch array (no-allocation entry point)     */
 } kvc_status;
 
 typedef enum kvc_dtype {
@@ -218,6 +220,38 @@ int kvc_decode_attn(const kvc_cache* c, const void* q, int64_t q_layer_stride,
                     int append_slot, float* out, int64_t out_layer_stride,
                     float* lse, int64_t lse_layer_stride, void* ws,
                     size_t ws_bytes, kvc_stream_t stream);
+
+/*
+ * kvc_decode_attn for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and kernels as kvc_decode_attn,
+ * without ws / ws_bytes: the split partials go to a device array the library
+ * owns, KVC_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, which each GPU the
+ * library runs on holds until the process ends.  The caller still passes
+ * and owns the inputs and outputs.  The call allocates nothing (no
+ * hipMalloc, no allocating library routine); its first call on a device
+ * looks up that device's copy of the array (hipGetSymbolAddress), with the
+ * device current.
+ *   - KVC_ESCRATCH when the call needs more than KVC_NOALLOC_SCRATCH_BYTES
+ *     (the kvc_decode_attn_ws_bytes of the same arguments); nothing is
+ *     enqueued.  Every call on at most 256 (batch entry, kv head) slabs fits,
+ *     and so does every call with at most 16 query rows per slab (q-layers
+ *     x g) on at most 2048 slabs.
+ *   - The stream must belong to the current device (KVC_EHIP otherwise).
+ *   - Every call on one GPU shares that GPU's array and leaves its partials
+ *     there; calls that overlap on one GPU (different streams, or different
+ *     host threads without ordering) race and may return wrong results.
+ *     Calls ordered on one stream are safe.  The partials need no clearing:
+ *     every launch writes what it reads.
+ */
+#define KVC_NOALLOC_SCRATCH_BYTES (32u << 20)
+int kvc_decode_attn_noalloc(const kvc_cache* c, const void* q,
+                            int64_t q_layer_stride, int n_q_layers,
+                            const int32_t* q_slot, int n_q_heads, float scale,
+                            const void* k_new, const void* v_new,
+                            int append_slot, float* out,
+                            int64_t out_layer_stride, float* lse,
+                            int64_t lse_layer_stride, kvc_stream_t stream);
 
 /*
  * Value range [VASE §2.A]: range[b][j][t] = max_c V[slot][b][j][t][c]
