@@ -352,7 +352,7 @@ def ragged_leg(args, cfg, qpool, lsepool, knew, vnew, out, steps, warm=3):
     n_total = warm + steps
     mode = args.mode if args.mode in ("per-layer", "grouped") else "per-layer"
     plan = ragged_plan(t0, n_total, ev)
-    prompt = kvc.Cache.empty(n_slots, nb, hkv, max(t0), device=dev)
+    prompt = kvc.Cache.empty(n_slots, nb, hkv, max(t0), device=dev, v_layout="rows")
     for s_ in range(n_slots):
         Kr, Vr, _, _ = kvc_synth.kv_slot(nb, hkv, max(t0), device=dev, seed=300 + s_)
         prompt.fill(s_, Kr, Vr)
@@ -665,8 +665,9 @@ def main():
         return
     log(f"[bench] {args.workload}: setting up (prompt cache {t0} rows x {n_slots} slots)")
 
-    # ---- inputs (untimed): prompt cache, query / append pools
-    big = kvc.Cache.empty(n_slots, nb, hkv, t0 + (0 if ev else n_total), device=dev)
+    # ---- inputs (untimed): the prompt cache in a prefill's layout ([t][d]
+    # value rows, like the keys), query / append pools
+    big = kvc.Cache.empty(n_slots, nb, hkv, t0, device=dev, v_layout="rows") if t0 else None
     prev = None
     for s_ in range(n_slots if t0 else 0):
         Kr, Vr, K32, V32 = kvc_synth.kv_slot(nb, hkv, t0, device=dev, seed=100 + s_,
@@ -712,7 +713,23 @@ def main():
         del big, q_init
         torch.cuda.empty_cache()
     else:
-        dec = Decoder(L, leaders, big, None, hq, evict=None, mode=args.mode)
+        # no eviction: the prompt's rows enter the decode layout in one copy
+        # (kvc_compact with no kept list)
+        cache = kvc.Cache.empty(n_slots, nb, hkv, t0 + n_total, device=dev)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for s_ in range(n_slots):
+            kvc.kvc_compact(big, s_, None, t0, cache)
+        b.record()
+        torch.cuda.synchronize()
+        cache.t_len = t0
+        initial_ms = a.elapsed_time(b)
+        log(f"[bench] prompt ingest ({t0} rows x {n_slots} slots, rows -> tiles): "
+            f"{initial_ms:.2f} ms")
+        del big
+        torch.cuda.empty_cache()
+        dec = Decoder(L, leaders, cache, None, hq, evict=None, mode=args.mode)
 
     def run(steps, first, mode, events):
         dec.mode = mode
@@ -906,6 +923,9 @@ def main():
         "eviction": eviction,
         "eviction_passes_timed": len(passes) if ev else 0,
         "initial_pass_ms": None if initial_ms is None else round(initial_ms, 3),
+        "initial_pass": ("prompt compression from the prefill layout (value rows) into the "
+                         "tiled decode cache" if ev else "prompt ingest: value rows -> tiles")
+        if t0 else None,
         "grouped": grouped,
         "int8": int8,
         "ragged": ragged_res,

@@ -6,7 +6,8 @@ Importing the package loads the library and fails if it is not built.
 """
 from ._lib import (  # noqa: F401
     Cache, KvcError, EXPORTS, HEAD_DIM, T_ALIGN, KVC_F32, KVC_BF16, KVC_OK, KVC_EINVAL,
-    KVC_EDTYPE, KVC_EALIGN, KVC_EWORKSPACE, KVC_EALIAS, KVC_EHIP, KVC_ESCRATCH,
+    KVC_EDTYPE, KVC_EALIGN, KVC_EWORKSPACE, KVC_EALIAS, KVC_EHIP, KVC_ESCRATCH, KVC_V_TILES,
+    KVC_V_ROWS,
     NOALLOC_SCRATCH_BYTES, lib, strerror,
     kvc_version, kvc_strerror, kvc_share_map, kvc_append, kvc_decode_attn_ws_bytes,
     kvc_decode_attn, kvc_decode_attn_noalloc, kvc_value_range, kvc_score_ws_bytes, kvc_score,

@@ -21,6 +21,7 @@ KVC_OK, KVC_EINVAL, KVC_EDTYPE, KVC_EALIGN, KVC_EWORKSPACE, KVC_EALIAS, KVC_EHIP
 KVC_ESCRATCH = -7
 NOALLOC_SCRATCH_BYTES = 32 << 20
 KVC_F32, KVC_BF16 = 0, 1
+KVC_V_TILES, KVC_V_ROWS = 0, 1
 HEAD_DIM = 128
 T_ALIGN = 64
 V_TILE = 32
@@ -48,7 +49,7 @@ class kvc_cache(ctypes.Structure):
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("t_len", ctypes.c_int32), ("t_cap", ctypes.c_int32),
                 ("nb_cap", ctypes.c_int32), ("batch_idx", ctypes.c_void_p),
-                ("seq_len", ctypes.c_void_p)]
+                ("seq_len", ctypes.c_void_p), ("v_layout", ctypes.c_int32)]
 
 
 class kvc_qcache(ctypes.Structure):
@@ -170,7 +171,9 @@ class Cache:
 
     k: [n_slots][nb_cap][n_kv_heads][t_cap][128] rows;
     v: [n_slots][nb_cap][n_kv_heads][t_cap/32][128][32], tiles of 32 tokens,
-    each tile channel-major.
+    each tile channel-major (v_layout "tiles", the decode layout), or
+    [n_slots][nb_cap][n_kv_heads][t_cap][128] rows like k (v_layout "rows",
+    a prefill's layout: an input of the prompt compression).
     Ragged batches: batch_idx (device int32 [n]: the entry of each sequence)
     and seq_len (device int32 [n]: its rows) make the object address n
     sequences; t_len is then the bound on their lengths.  seqs() makes such a
@@ -180,6 +183,7 @@ class Cache:
     t_len: int
     batch_idx: Optional[torch.Tensor] = None
     seq_len: Optional[torch.Tensor] = None
+    v_layout: str = "tiles"
 
     def seqs(self, batch_idx=None, seq_len=None, t_len=None):
         """The same buffers addressing the sequences of batch_idx / seq_len."""
@@ -192,12 +196,18 @@ class Cache:
                                    t_len=self.t_len if t_len is None else t_len)
 
     @staticmethod
-    def empty(n_slots, nb, n_kv_heads, t_cap, dtype=torch.bfloat16, device="cuda", t_len=0):
+    def empty(n_slots, nb, n_kv_heads, t_cap, dtype=torch.bfloat16, device="cuda", t_len=0,
+              v_layout="tiles"):
         t_cap = int(math.ceil(t_cap / T_ALIGN) * T_ALIGN)
         k = torch.empty((n_slots, nb, n_kv_heads, t_cap, HEAD_DIM), dtype=dtype, device=device)
-        v = torch.empty((n_slots, nb, n_kv_heads, t_cap // V_TILE, HEAD_DIM, V_TILE), dtype=dtype,
-                        device=device)
-        return Cache(k, v, t_len)
+        if v_layout == "rows":
+            v = torch.empty_like(k)
+        elif v_layout == "tiles":
+            v = torch.empty((n_slots, nb, n_kv_heads, t_cap // V_TILE, HEAD_DIM, V_TILE),
+                            dtype=dtype, device=device)
+        else:
+            raise ValueError(f"unknown value layout {v_layout!r}")
+        return Cache(k, v, t_len, v_layout=v_layout)
 
     @property
     def n_slots(self):
@@ -232,8 +242,11 @@ class Cache:
         d = self.__dict__.get("_desc")
         key = (self.k.data_ptr(), self.v.data_ptr(), _ptr(self.batch_idx), _ptr(self.seq_len))
         if d is None or self.__dict__.get("_desc_key") != key:
+            if self.v_layout not in ("tiles", "rows"):
+                raise ValueError(f"unknown value layout {self.v_layout!r}")
             d = kvc_cache(key[0], key[1], _dtype_code(self.k.dtype), self.n_slots, self.nb,
-                          self.n_kv_heads, HEAD_DIM, 0, self.t_cap, self.nb_cap, key[2], key[3])
+                          self.n_kv_heads, HEAD_DIM, 0, self.t_cap, self.nb_cap, key[2], key[3],
+                          KVC_V_ROWS if self.v_layout == "rows" else KVC_V_TILES)
             self.__dict__["_desc"], self.__dict__["_desc_key"] = d, key
         d.t_len = int(self.t_len)
         return d
@@ -243,13 +256,18 @@ class Cache:
         return self.k[slot, :, :, : self.t_len, :]
 
     def v_rows(self, slot):
-        """Logical value rows [nb][hkv][t_len][128] (a copy)."""
+        """Logical value rows [nb][hkv][t_len][128] (a copy for tiles, a view
+        for rows)."""
+        if self.v_layout == "rows":
+            return self.v[slot, :, :, : self.t_len, :]
         v = self.v[slot].transpose(-1, -2).reshape(self.nb_cap, self.n_kv_heads, self.t_cap,
                                                     HEAD_DIM)
         return v[:, :, : self.t_len]
 
     def v_row(self, slot, t):
         """Value row t of every (b, kv head): [nb][hkv][128] (a view)."""
+        if self.v_layout == "rows":
+            return self.v[slot, :, :, t, :]
         return self.v[slot, :, :, t // V_TILE, :, t % V_TILE]
 
     def fill(self, slot, k_rows, v_rows):
@@ -257,6 +275,10 @@ class Cache:
         rows past T keep their old contents."""
         T = k_rows.shape[2]
         self.k[slot, :, :, :T, :].copy_(k_rows)
+        if self.v_layout == "rows":
+            self.v[slot, :, :, :T, :].copy_(v_rows)
+            self.t_len = T
+            return
         nfull, rem = divmod(T, V_TILE)
         nb, h = self.nb_cap, self.n_kv_heads
         if nfull:
@@ -505,6 +527,7 @@ def kvc_select_seq(score, rng, nb, n_kv_heads, t_len, seq_len, seq_id, budget_k,
 
 
 def kvc_compact(src, slot, kept, n_keep, dst, stream=None):
+    """kept: device int32 [nb][hkv][n_keep], or None for rows [0, n_keep)."""
     cs, cd = src.desc(), dst.desc()
     _check(lib().kvc_compact(ctypes.byref(cs), slot, _ptr(kept), n_keep, ctypes.byref(cd),
                              _stream(stream)), "kvc_compact")

@@ -37,6 +37,7 @@ int check_cache(const kvc_cache* c) {
     if (c->nb_cap < 0) return KVC_EINVAL;
     // without a map, sequence b is entry b
     if (!c->batch_idx && c->nb > nb_cap_of(c)) return KVC_EINVAL;
+    if (c->v_layout != KVC_V_TILES && c->v_layout != KVC_V_ROWS) return KVC_EINVAL;
     if (!aligned16(c->k) || !aligned16(c->v)) return KVC_EALIGN;
     if ((c->batch_idx && !aligned4(c->batch_idx)) || (c->seq_len && !aligned4(c->seq_len)))
         return KVC_EALIGN;
@@ -44,6 +45,17 @@ int check_cache(const kvc_cache* c) {
 }
 
 bool is_ragged(const kvc_cache* c) { return c->batch_idx || c->seq_len; }
+
+// A cache whose values are [t][D] rows (a prefill's layout): only the prompt
+// compression's calls (range, score, compaction source) read it.
+bool v_rows(const kvc_cache* c) { return c->v_layout == KVC_V_ROWS; }
+
+// check_cache, then require the tiled value layout.
+int check_tiled(const kvc_cache* c) {
+    const int st = check_cache(c);
+    if (st) return st;
+    return v_rows(c) ? KVC_EINVAL : KVC_OK;
+}
 
 SeqMap seq_map(const kvc_cache* c) {
     SeqMap m;
@@ -377,7 +389,7 @@ int kvc_share_map(int n_layers, const int32_t* leaders, int n_leaders, int32_t* 
 
 int kvc_append(const kvc_cache* c, int slot, const void* k_new, const void* v_new,
                kvc_stream_t stream) {
-    int st = check_cache(c);
+    int st = check_tiled(c);
     if (st) return st;
     if (slot < 0 || slot >= c->n_slots || c->t_len < 1) return KVC_EINVAL;
     if (!aligned16(k_new) || !aligned16(v_new)) return KVC_EALIGN;
@@ -390,7 +402,7 @@ int kvc_append(const kvc_cache* c, int slot, const void* k_new, const void* v_ne
 }
 
 int kvc_decode_attn_ws_bytes(const kvc_cache* c, int n_q_layers, int n_q_heads, size_t* bytes) {
-    int st = check_cache(c);
+    int st = check_tiled(c);
     if (st) return st;
     if (!bytes) return KVC_EALIGN;
     if (n_q_layers < 0 || n_q_heads < 1 || n_q_heads % c->n_kv_heads) return KVC_EINVAL;
@@ -406,7 +418,7 @@ int kvc_decode_attn(const kvc_cache* c, const void* q, int64_t q_layer_stride, i
                     const void* v_new, int append_slot, float* out, int64_t out_layer_stride,
                     float* lse, int64_t lse_layer_stride, void* ws, size_t ws_bytes,
                     kvc_stream_t stream) {
-    int st = check_cache(c);
+    int st = check_tiled(c);
     if (st) return st;
     if (n_q_layers < 0 || n_q_heads < 1 || n_q_heads % c->n_kv_heads) return KVC_EINVAL;
     const int g = n_q_heads / c->n_kv_heads;
@@ -503,8 +515,8 @@ int kvc_value_range(const kvc_cache* c, int slot, float* range, kvc_stream_t str
     if (slot < 0 || slot >= c->n_slots) return KVC_EINVAL;
     if (!aligned4(range)) return KVC_EALIGN;
     if (c->nb == 0 || c->t_len == 0) return KVC_OK;
-    if (launch_value_range(slot_v(c, slot), c->nb, c->n_kv_heads, c->t_cap, seq_map(c), c->dtype,
-                           range, (hipStream_t)stream) != hipSuccess)
+    if (launch_value_range(slot_v(c, slot), v_rows(c), c->nb, c->n_kv_heads, c->t_cap,
+                           seq_map(c), c->dtype, range, (hipStream_t)stream) != hipSuccess)
         return KVC_EHIP;
     return hip_status();
 }
@@ -561,7 +573,9 @@ int kvc_score(const kvc_cache* c, int slot, const void* q_obs, int n_q_heads, in
     p.lse_obs = lse_obs;
     p.scale = scale;
     p.score = score;
-    p.range = range;
+    // Values stored as rows: the score pass reads the keys only and the
+    // range comes from the rows kernel (the same bytes, one launch more).
+    p.range = v_rows(c) ? nullptr : range;
     p.nsplit = pl.nsplit;
     p.tps = pl.tps;
     p.main_nsplit = pl.main_nsplit;
@@ -574,6 +588,10 @@ int kvc_score(const kvc_cache* c, int slot, const void* q_obs, int n_q_heads, in
         p.stats = reinterpret_cast<float*>(base + lay.stats_off);
     }
     if (launch_score(p, c->dtype, (hipStream_t)stream) != hipSuccess) return KVC_EHIP;
+    if (range && v_rows(c) &&
+        launch_value_range(slot_v(c, slot), true, c->nb, c->n_kv_heads, c->t_cap, seq_map(c),
+                           c->dtype, range, (hipStream_t)stream) != hipSuccess)
+        return KVC_EHIP;
     return hip_status();
 }
 
@@ -632,14 +650,14 @@ int kvc_compact(const kvc_cache* src, int slot, const int32_t* kept, int n_keep,
                 const kvc_cache* dst, kvc_stream_t stream) {
     int st = check_cache(src);
     if (st) return st;
-    st = check_cache(dst);
+    st = check_tiled(dst);
     if (st) return st;
     if (src->dtype != dst->dtype) return KVC_EDTYPE;
     if (src->nb != dst->nb || src->n_kv_heads != dst->n_kv_heads) return KVC_EINVAL;
     if (slot < 0 || slot >= src->n_slots || slot >= dst->n_slots) return KVC_EINVAL;
     if (n_keep < 0 || n_keep > src->t_len || n_keep > dst->t_cap) return KVC_EINVAL;
     if (src->nb == 0 || n_keep == 0) return KVC_OK;
-    if (!aligned4(kept)) return KVC_EALIGN;
+    if (kept && !aligned4(kept)) return KVC_EALIGN;
     const size_t es = elem_size(src->dtype);
     const size_t sb = slot_elems(src) * es, db = slot_elems(dst) * es;
     const char* sr[2] = {slot_k(src, slot), slot_v(src, slot)};
@@ -668,13 +686,14 @@ int kvc_compact(const kvc_cache* src, int slot, const int32_t* kept, int n_keep,
     p.elem = (int)es;
     p.src_sm = seq_map(src);
     p.dst_sm = seq_map(dst);
+    p.src_rows = v_rows(src);
     if (launch_compact(p, (hipStream_t)stream) != hipSuccess) return KVC_EHIP;
     return hip_status();
 }
 
 int kvc_q8_quantize(const kvc_cache* src, int slot, const int32_t* protect, int n_protect,
                     const kvc_qcache* dst, kvc_stream_t stream) {
-    int st = check_cache(src);
+    int st = check_tiled(src);
     if (st) return st;
     st = check_qcache(dst);
     if (st) return st;
@@ -831,7 +850,7 @@ int kvc_q8_decode_attn(const kvc_qcache* c, const void* q, int64_t q_layer_strid
 }
 
 int kvc_dkv_ws_bytes(const kvc_cache* c, int rank, size_t* bytes) {
-    int st = check_cache(c);
+    int st = check_tiled(c);
     if (st) return st;
     if (!bytes) return KVC_EALIGN;
     if (rank != 16 && rank != 32) return KVC_EINVAL;
@@ -842,7 +861,7 @@ int kvc_dkv_ws_bytes(const kvc_cache* c, int rank, size_t* bytes) {
 
 int kvc_dkv_score(const kvc_cache* c, int slot, const void* g, int rank, float* score,
                   float* range, void* ws, size_t ws_bytes, kvc_stream_t stream) {
-    int st = check_cache(c);
+    int st = check_tiled(c);
     if (st) return st;
     if (c->dtype != KVC_BF16) return KVC_EDTYPE;
     if (slot < 0 || slot >= c->n_slots) return KVC_EINVAL;
@@ -885,7 +904,7 @@ int kvc_xkv_factor_ws_bytes(const kvc_xkv* x, size_t* bytes) {
 
 int kvc_xkv_factor(const kvc_cache* c, int slot0, int iters, uint64_t seed, const kvc_xkv* x,
                    void* ws, size_t ws_bytes, kvc_stream_t stream) {
-    int st = check_cache(c);
+    int st = check_tiled(c);
     if (st) return st;
     st = check_xkv(x);
     if (st) return st;

@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactLaunch p) {
     const int src_t_len = seq_rows(p.src_sm, b, sphys);
     const int rows = min(CROWS, min(src_t_len, p.n_keep) - i0);
     if (dphys < 0 || rows <= 0) return;          // whole workgroup
-    const int32_t* kept = p.kept + (size_t)slab * p.n_keep;
+    const int32_t* kept = p.kept ? p.kept + (size_t)slab * p.n_keep : nullptr;
     const size_t scs = (size_t)sphys * p.hkv + by, dcs = (size_t)dphys * p.hkv + by;
     const E* sk = reinterpret_cast<const E*>(p.sk) + scs * p.src_t_cap * D;
     const E* sv = reinterpret_cast<const E*>(p.sv) + scs * p.src_t_cap * D;
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactLaunch p) {
     for (int x = tid; x < CROWS; x += blockDim.x) {
         int32_t r = -1;
         if (x < rows) {
-            r = kept[i0 + x];
+            r = kept ? kept[i0 + x] : i0 + x;
             if (r < 0 || r >= src_t_len) r = -1;
         }
         src_row[x] = r;
@@ -205,14 +205,107 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactLaunch p) {
     }
 }
 
+// Compaction from a source whose values are [t][D] rows (a prefill's
+// layout) into the tiled layout.  A workgroup gathers its 64 kept rows of K
+// and of V with 16-byte loads (only the kept rows are read: no source tile is
+// fetched whole), writes the K rows, stages the V rows in LDS and writes
+// them out as the destination's channel-major 32-token tiles with 16-byte
+// stores.  Indices outside [0, src t_len) give zero rows, as above.
+template <typename E>
+__global__ __launch_bounds__(256) void compact_rows_kernel(CompactLaunch p) {
+    constexpr int VEC = 16 / sizeof(E);
+    constexpr int CPR = D / VEC;                // 16-byte chunks per row
+    constexpr int PITCH = D + VEC;              // staged row pitch, 16-byte aligned
+    constexpr int LOADS = CROWS * CPR / 256;    // chunks per thread, for K and for V
+    const BlockXYZ blk = xcd_run_block(true);
+    const int bx = blk.x, by = blk.y, b = blk.z;
+    const int slab = b * p.hkv + by;
+    const int i0 = bx * CROWS;
+    const int tid = threadIdx.x;
+    const int sphys = seq_phys(p.src_sm, b), dphys = seq_phys(p.dst_sm, b);
+    const int src_t_len = seq_rows(p.src_sm, b, sphys);
+    const int rows = min(CROWS, min(src_t_len, p.n_keep) - i0);
+    if (dphys < 0 || rows <= 0) return;          // whole workgroup
+    const int32_t* kept = p.kept ? p.kept + (size_t)slab * p.n_keep : nullptr;
+    const size_t scs = (size_t)sphys * p.hkv + by, dcs = (size_t)dphys * p.hkv + by;
+    const E* sk = reinterpret_cast<const E*>(p.sk) + scs * p.src_t_cap * D;
+    const E* sv = reinterpret_cast<const E*>(p.sv) + scs * p.src_t_cap * D;
+    E* dk = reinterpret_cast<E*>(p.dk) + dcs * p.dst_t_cap * D;
+    E* dv = reinterpret_cast<E*>(p.dv) + dcs * p.dst_t_cap * D;
+
+    __shared__ int32_t src_row[CROWS];
+    __shared__ __align__(16) E stage[CROWS * PITCH];
+    for (int x = tid; x < CROWS; x += blockDim.x) {
+        int32_t r = -1;
+        if (x < rows) {
+            r = kept ? kept[i0 + x] : i0 + x;
+            if (r < 0 || r >= src_t_len) r = -1;
+        }
+        src_row[x] = r;
+    }
+    __syncthreads();
+
+    // every load of the block in flight at once
+    u32x4 kreg[LOADS], vreg[LOADS];
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+        const int x = tid + 256 * u;
+        const int i = x / CPR, c = x % CPR;
+        const int32_t r = src_row[i];               // -1 past `rows`
+        kreg[u] = vreg[u] = u32x4{0u, 0u, 0u, 0u};
+        if (r >= 0) {
+            kreg[u] = load_stream16(sk + (size_t)r * D + c * VEC);
+            vreg[u] = load_stream16(sv + (size_t)r * D + c * VEC);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+        const int x = tid + 256 * u;
+        const int i = x / CPR, c = x % CPR;
+        if (i < rows) *reinterpret_cast<u32x4*>(dk + (size_t)(i0 + i) * D + c * VEC) = kreg[u];
+        *reinterpret_cast<u32x4*>(&stage[i * PITCH + c * VEC]) = vreg[u];
+    }
+    __syncthreads();
+
+    // destination tiles: channel d of tile kk holds rows kk*32 .. kk*32+31,
+    // written VEC rows per 16-byte store
+    constexpr int GROUPS = VT / VEC;
+    const int ntile = (rows + VT - 1) / VT;
+    const int items = ntile * D * GROUPS;
+    for (int x = tid; x < items; x += blockDim.x) {
+        const int q = x % GROUPS, d = (x / GROUPS) % D, kk = x / (GROUPS * D);
+        const int base = kk * VT + q * VEC;             // first block row of the group
+        union {
+            E e[VEC];
+            u32x4 v;
+        } vals;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) vals.e[e] = stage[(base + e) * PITCH + d];
+        const int di = i0 + base;
+        if (base + VEC <= rows) {
+            *reinterpret_cast<u32x4*>(dv + vt_off(di, d)) = vals.v;
+        } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                if (base + e < rows) dv[vt_off(di + e, d)] = vals.e[e];
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_compact(const CompactLaunch& p, hipStream_t st) {
     const dim3 grid((p.n_keep + CROWS - 1) / CROWS, p.hkv, p.nb);
-    if (p.elem == 4)
+    if (p.src_rows) {
+        if (p.elem == 4)
+            hipLaunchKernelGGL(compact_rows_kernel<float>, grid, dim3(256), 0, st, p);
+        else
+            hipLaunchKernelGGL(compact_rows_kernel<uint16_t>, grid, dim3(256), 0, st, p);
+    } else if (p.elem == 4) {
         hipLaunchKernelGGL(compact_kernel<float>, grid, dim3(256), 0, st, p);
-    else
+    } else {
         hipLaunchKernelGGL(compact_kernel<uint16_t>, grid, dim3(256), 0, st, p);
+    }
     return hipGetLastError();
 }
 

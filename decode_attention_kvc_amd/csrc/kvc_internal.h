@@ -179,6 +179,7 @@ struct CompactLaunch {
     int n_keep;             // stride of kept; sequence b keeps min(rows(b), n_keep)
     int elem;               // bytes per element
     SeqMap src_sm, dst_sm;  // src_sm.len gives the source rows
+    int src_rows;           // source values stored as [t][D] rows (else tiles)
 };
 
 // Cross-layer factorisation of one window of W slots (bf16, uniform batch).
@@ -235,7 +236,7 @@ hipError_t launch_q8_quantize(const Q8QuantLaunch& p, hipStream_t s);
 hipError_t launch_append(const void* k, const void* v, int nb, int hkv, int t_cap,
                          const SeqMap& sm, const void* k_new, const void* v_new, int elem,
                          hipStream_t s);
-hipError_t launch_value_range(const void* v, int nb, int hkv, int t_cap, const SeqMap& sm,
+hipError_t launch_value_range(const void* v, bool v_rows, int nb, int hkv, int t_cap, const SeqMap& sm,
                               int dtype, float* range, hipStream_t s);
 hipError_t launch_score(const ScoreLaunch& p, int dtype, hipStream_t s);
 hipError_t launch_select(const SelectLaunch& p, hipStream_t s);

@@ -599,6 +599,54 @@ __global__ __launch_bounds__(256) void value_range_kernel(const E* v, int hkv, i
     }
 }
 
+// Value range of a cache whose values are [t][D] rows (a prefill's layout):
+// a group of D / VEC lanes reads one row with 16-byte loads, and the group's
+// maximum and minimum meet through lane exchanges inside the group.  Each
+// group takes ITER rows of the workgroup's block, every load issued before
+// the first reduction.
+template <typename E>
+__global__ __launch_bounds__(256) void value_range_rows_kernel(const E* v, int hkv, int t_cap,
+                                                               SeqMap sm, float* range) {
+    constexpr int VEC = 16 / sizeof(E);          // elements per 16-byte access
+    constexpr int LPR = D / VEC;                 // lanes per row: 16 (bf16), 32 (float)
+    constexpr int RPI = 256 / LPR;               // rows per iteration of the workgroup
+    constexpr int ITER = 4;
+    const int b = blockIdx.z;
+    const int slab = b * hkv + blockIdx.y;
+    const int phys = seq_phys(sm, b);
+    const int t_len = seq_rows(sm, b, phys);
+    const int base = blockIdx.x * RPI * ITER;
+    if (base >= t_len) return;                   // past the sequence's end
+    const int tid = threadIdx.x, grp = tid / LPR, ln = tid % LPR;
+    const E* vs = v + ((size_t)phys * hkv + blockIdx.y) * t_cap * D;
+    u32x4 x[ITER];
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+        const int t = base + it * RPI + grp;
+        x[it] = u32x4{0u, 0u, 0u, 0u};
+        if (t < t_len) x[it] = load_stream16(vs + (size_t)t * D + ln * VEC);
+    }
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+        float mx = -INFINITY, mn = INFINITY;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            float f;
+            if constexpr (sizeof(E) == 2) f = (e & 1) ? bf16hi(x[it][e / 2]) : bf16lo(x[it][e / 2]);
+            else f = __uint_as_float(x[it][e]);
+            mx = fmaxf(mx, f);
+            mn = fminf(mn, f);
+        }
+#pragma unroll
+        for (int m = LPR / 2; m >= 1; m >>= 1) {      // stays inside the lane group
+            mx = fmaxf(mx, __shfl_xor(mx, m));
+            mn = fminf(mn, __shfl_xor(mn, m));
+        }
+        const int t = base + it * RPI + grp;
+        if (ln == 0 && t < t_len) range[(size_t)slab * sm.t_len + t] = mx - mn;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_score(const ScoreLaunch& p, int dtype, hipStream_t st) {
@@ -634,8 +682,19 @@ hipError_t launch_score(const ScoreLaunch& p, int dtype, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_value_range(const void* v, int nb, int hkv, int t_cap, const SeqMap& sm,
-                              int dtype, float* range, hipStream_t st) {
+hipError_t launch_value_range(const void* v, bool v_rows, int nb, int hkv, int t_cap,
+                              const SeqMap& sm, int dtype, float* range, hipStream_t st) {
+    if (v_rows) {
+        const int rows_per_wg = (dtype == 0 ? 8 : 16) * 4;
+        const dim3 grid((sm.t_len + rows_per_wg - 1) / rows_per_wg, hkv, nb);
+        if (dtype == 0)
+            hipLaunchKernelGGL(value_range_rows_kernel<float>, grid, dim3(256), 0, st,
+                               (const float*)v, hkv, t_cap, sm, range);
+        else
+            hipLaunchKernelGGL(value_range_rows_kernel<uint16_t>, grid, dim3(256), 0, st,
+                               (const uint16_t*)v, hkv, t_cap, sm, range);
+        return hipGetLastError();
+    }
     if (dtype == 0) {
         const dim3 grid((sm.t_len + 4 * WAVE - 1) / (4 * WAVE), hkv, nb);
         hipLaunchKernelGGL(value_range_kernel<float>, grid, dim3(256), 0, st, (const float*)v, hkv,

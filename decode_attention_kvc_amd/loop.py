@@ -63,9 +63,12 @@ class Decoder:
         self.last_compaction = None
         dev = cache.k.device
         nb, hkv = cache.nb, cache.n_kv_heads
-        # per-layer calls serve one q-layer; grouped calls all followers
+        # per-layer calls serve one q-layer; grouped calls all followers.  A
+        # prompt cache in a prefill's layout (value rows) is only compressed,
+        # never attended: the workspace is sized for the decode cache.
         nql = 1 if mode != "grouped" else max(self.src_slot.count(s) for s in range(len(leaders)))
-        self.ws_attn = torch.zeros(max(16, K.kvc_decode_attn_ws_bytes(cache, nql, n_q_heads)),
+        att = cache if cache.v_layout == "tiles" or spare is None else spare
+        self.ws_attn = torch.zeros(max(16, K.kvc_decode_attn_ws_bytes(att, nql, n_q_heads)),
                                    dtype=torch.uint8, device=dev)
         self.groups = [[l for l in range(n_layers) if self.src_slot[l] == s]
                        for s in range(len(leaders))]
@@ -292,8 +295,9 @@ class RaggedDecoder:
     row per step, the whole schedule (lengths, due sets, entries) is host
     bookkeeping fixed by the prompt lengths; it is planned here once and its
     per-step device arrays are uploaded once, so a step only launches
-    kernels.  Window queries of the due sequences are gathered into the
-    [w][n_due][Hq][d] layout kvc_score takes (argument marshalling).
+    kernels.  A pass's calls address the whole batch, the sequences that
+    are not due as empty ones, so its window queries are the pools' own
+    [w][nb][Hq][d] slices.
     """
 
     def __init__(self, n_layers, leaders, cache, n_q_heads, t0, n_steps, evict=None,
@@ -331,12 +335,20 @@ class RaggedDecoder:
         # per-step entries and lengths, one upload
         self.att_idx = torch.tensor(plan["att_idx"], dtype=torch.int32, device=dev)
         self.att_len = torch.tensor(plan["att_len"], dtype=torch.int32, device=dev)
+        # A pass addresses every sequence of the batch: the due ones through
+        # their source / destination entries and lengths, the others
+        # through an entry past the cache's (an empty sequence: the kernels
+        # read and write none of its rows).  So the window queries and
+        # log-normalisers are the pools' plain [w][nb] slices, and no
+        # gather runs between the steps' library calls.
         self.passes = {}
+        off = cache.nb_cap
         for s, p in plan["passes"].items():
-            arr = torch.tensor([p["seqs"], p["src"], p["dst"], p["lens"]], dtype=torch.int32,
-                               device=dev)
-            self.passes[s] = dict(p, seqs_d=arr[0], src_d=arr[1], dst_d=arr[2], lens_d=arr[3],
-                                  seqs_l=arr[0].long())
+            src, dst, lens = [off] * nb, [off] * nb, [0] * nb
+            for b, e_src, e_dst, t in zip(p["seqs"], p["src"], p["dst"], p["lens"]):
+                src[b], dst[b], lens[b] = e_src, e_dst, t
+            arr = torch.tensor([src, dst, lens], dtype=torch.int32, device=dev)
+            self.passes[s] = dict(p, src_d=arr[0], dst_d=arr[1], lens_d=arr[2])
         self.prompt_len = torch.tensor(self.t0, dtype=torch.int32, device=dev)
         self.seq_ids = torch.arange(nb, dtype=torch.int32, device=dev)
         nql = 1 if mode != "grouped" else max(len(g) for g in self.groups)
@@ -384,15 +396,17 @@ class RaggedDecoder:
             return False
         ev1 = self._event()
         w = self.ev["w"]
+        if s + 1 < w or s >= n_steps:
+            raise ValueError(f"step {s}: the window needs query rows {s - w + 1}..{s} of a "
+                             f"pool of {n_steps}")
         windows = []
         for leader in self.leaders:
-            q_obs = qpool[leader, s - w + 1:s + 1].index_select(1, p["seqs_l"])
-            lse = (lsepool[leader, s - w + 1:s + 1].index_select(1, p["seqs_l"])
-                   if p["fresh"] else None)
+            q_obs = qpool[leader, s - w + 1:s + 1]
+            lse = lsepool[leader, s - w + 1:s + 1] if p["fresh"] else None
             windows.append((q_obs, lse))
         src = self.cache.seqs(p["src_d"], p["lens_d"], t_len=p["t_len"])
         dst = self.cache.seqs(p["dst_d"], None, t_len=self.ev["K"] + self.ev["B"])
-        self._pass(src, dst, windows, p["seqs_d"], p["round"])
+        self._pass(src, dst, windows, self.seq_ids, p["round"])
         if ev1 is not None:
             self.pass_events.append((ev1, self._event(), s, len(p["seqs"])))
         return True

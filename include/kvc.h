@@ -87,6 +87,18 @@ typedef enum kvc_dtype {
  *      loads with one 16-byte access per lane.
  * dtype is a kvc_dtype; both k and v hold that type.
  *
+ * v_layout (kvc_v_layout) says how v is stored:
+ *   KVC_V_TILES (0, the default of a zero-initialised descriptor): the
+ *     tiled layout above, which decode attention, appends, the int8 and
+ *     sketch paths and compaction destinations use;
+ *   KVC_V_ROWS (1): v stored like k, [n_slots][nb_cap][n_kv_heads][t_cap]
+ *     [head_dim] rows -- the layout a prefill writes.  A rows cache is an
+ *     input of the prompt compression: kvc_value_range, kvc_score (with the
+ *     fused range) and kvc_compact (as the source) read it, and kvc_compact
+ *     re-lays the rows it gathers into a tiled destination (with kept =
+ *     NULL it copies rows [0, n_keep): a bulk ingest).  Every other call
+ *     returns KVC_EINVAL for it.
+ *
  * A call addresses nb sequences.  Uniform batches (batch_idx = seq_len =
  * NULL, nb_cap = 0 or nb): sequence b is batch entry b and rows [0, t_len)
  * are valid in every slot.
@@ -119,7 +131,13 @@ typedef struct kvc_cache {
     int32_t nb_cap;              /* batch entries of k / v; 0 means nb     */
     const int32_t* batch_idx;    /* device [nb] or NULL                    */
     const int32_t* seq_len;      /* device [nb] or NULL                    */
+    int32_t v_layout;            /* kvc_v_layout; 0 = KVC_V_TILES          */
 } kvc_cache;
+
+typedef enum kvc_v_layout {
+    KVC_V_TILES = 0,      /* [t_cap/32][head_dim][32] tiles (decode layout) */
+    KVC_V_ROWS = 1        /* [t_cap][head_dim] rows, like k (prefill)       */
+} kvc_v_layout;
 
 /*
  * A range-protected int8 cache [VASE §3, §5: large-range value states
@@ -350,6 +368,12 @@ int kvc_select(const float* score, const float* range, int nb, int n_kv_heads,
  * sequence's src and dst entries apart (not checked, the maps are device
  * data); a shared entry gives unspecified rows, never an access outside the
  * buffers.
+ * kept may be NULL: dst row i <- src row i for i < n_keep (ragged: i <
+ * min(T_b, n_keep)), a bulk copy.
+ * Layouts: dst must be KVC_V_TILES; src may be either.  From a KVC_V_ROWS
+ * src the gather reads exactly the kept value rows and writes them as
+ * tiles, so a prefill's [t][head_dim] cache enters the decode layout in the
+ * prompt compression itself (or, with kept = NULL, in one copy).
  */
 int kvc_compact(const kvc_cache* src, int slot, const int32_t* kept,
                 int n_keep, const kvc_cache* dst, kvc_stream_t stream);

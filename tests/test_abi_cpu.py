@@ -397,3 +397,36 @@ def test_xkv_decode_validation():
     assert d(ws=None) == kvc.KVC_EWORKSPACE
     assert d(ws=FAKE + 4) == kvc.KVC_EWORKSPACE
     assert d(ws=None, hq=7) == kvc.KVC_EINVAL
+
+
+def rows_cache(**kw):
+    c = cache(**kw)
+    c.v_layout = kvc.KVC_V_ROWS
+    return c
+
+
+def test_value_layout_validation():
+    """A rows-layout cache (a prefill's [t][d] values) is refused by every
+    call that reads the tiled decode layout; an unknown layout by all."""
+    bad = cache()
+    bad.v_layout = 2
+    assert attn(bad) == kvc.KVC_EINVAL
+    assert L.kvc_value_range(ctypes.byref(bad), 0, FAKE, None) == kvc.KVC_EINVAL
+    r = rows_cache()
+    assert attn(r) == kvc.KVC_EINVAL
+    out = ctypes.c_size_t()
+    assert L.kvc_decode_attn_ws_bytes(ctypes.byref(r), 1, 8, ctypes.byref(out)) == kvc.KVC_EINVAL
+    assert L.kvc_append(ctypes.byref(r), 0, FAKE, FAKE, None) == kvc.KVC_EINVAL
+    assert L.kvc_dkv_ws_bytes(ctypes.byref(r), 32, ctypes.byref(out)) == kvc.KVC_EINVAL
+    slots = (ctypes.c_int32 * 1)(0)
+    assert L.kvc_decode_attn_noalloc(ctypes.byref(r), FAKE, 0, 1, slots, 8, 0.0, None, None, -1,
+                                     FAKE, 0, None, 0, None) == kvc.KVC_EINVAL
+    # compaction: a rows source passes validation, a rows destination does not
+    src = rows_cache(k=0x10000000, v=0x20000000)
+    assert compact(src, rows_cache(k=0x30000000, v=0x40000000)) == kvc.KVC_EINVAL
+    assert compact(src, cache(k=0x30000000, v=0x40000000), n=0) == kvc.KVC_OK
+    assert compact(src, cache(k=0x30000000, v=0x40000000), kept=FAKE + 2) == kvc.KVC_EALIGN
+    # kept = NULL (a copy of rows [0, n)) is not an alignment error
+    assert compact(src, cache(k=0x30000000, v=0x40000000), kept=None, n=0) == kvc.KVC_OK
+    # the score's size and argument checks still apply to rows caches
+    assert L.kvc_score_ws_bytes(ctypes.byref(r), 8, 32, ctypes.byref(out)) == kvc.KVC_OK

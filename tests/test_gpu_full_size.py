@@ -25,10 +25,11 @@ def say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def make_state(L, leaders, nb, hq, hkv, t0, ev, steps, seed=0, t_cap=None):
-    """The bench's setup: a prompt cache, query/append pools, a Decoder."""
+def make_state(L, leaders, nb, hq, hkv, t0, ev, steps, seed=0, t_cap=None, v_layout="tiles"):
+    """The bench's setup: a prompt cache (v_layout "rows": a prefill's layout,
+    as the bench holds its prompts), query/append pools, a Decoder."""
     n_slots = len(leaders)
-    big = kvc.Cache.empty(n_slots, nb, hkv, t_cap or t0, device=DEV)
+    big = kvc.Cache.empty(n_slots, nb, hkv, t_cap or t0, device=DEV, v_layout=v_layout)
     for s in range(n_slots):
         K, V, _, _ = kvc_synth.kv_slot(nb, hkv, t0, device=DEV, seed=seed * 100 + s)
         big.fill(s, K, V)
@@ -65,8 +66,9 @@ def test_llama31_8b_combined_full_size():
     L, leaders, nb, hq, hkv, t0 = 32, list(range(0, 32, 4)), 16, 32, 8, 32768
     ev = dict(K=8192, B=128, N_v=128, w=32, period=128, seed=0)
     steps = 4
-    say("full-size combined: setup")
-    big, qpool, lsepool, knew, vnew = make_state(L, leaders, nb, hq, hkv, t0, ev, steps)
+    say("full-size combined: setup (prompt cache with value rows)")
+    big, qpool, lsepool, knew, vnew = make_state(L, leaders, nb, hq, hkv, t0, ev, steps,
+                                                 v_layout="rows")
     cap = ev["K"] + ev["B"] + ev["period"]
     cache = kvc.Cache.empty(len(leaders), nb, hkv, cap, device=DEV)
     spare = kvc.Cache.empty(len(leaders), nb, hkv, cap, device=DEV)
@@ -182,8 +184,9 @@ def test_qwen3_14b_long_initial_pass_full_size():
     L, leaders, nb, hq, hkv, t0 = 40, list(range(0, 40, 2)), 4, 40, 8, 131072
     ev = dict(K=32768, B=256, N_v=256, w=32, period=256, seed=3)
     steps = 2
-    say("full-size long context: setup (43 GB prompt cache)")
-    big, qpool, lsepool, knew, vnew = make_state(L, leaders, nb, hq, hkv, t0, ev, steps, seed=5)
+    say("full-size long context: setup (43 GB prompt cache, value rows)")
+    big, qpool, lsepool, knew, vnew = make_state(L, leaders, nb, hq, hkv, t0, ev, steps, seed=5,
+                                                 v_layout="rows")
     cap = ev["K"] + ev["B"] + ev["period"]
     cache = kvc.Cache.empty(len(leaders), nb, hkv, cap, device=DEV)
     dec = Decoder(L, leaders, big, cache, hq, evict=ev)
