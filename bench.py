@@ -17,6 +17,7 @@ HBM before timing starts.
 Prints one JSON line.  Only the cpu_baseline leg touches oracle/.
 """
 import argparse
+import gc
 import json
 import math
 import os
@@ -743,7 +744,12 @@ def main():
             n_ev += bool(dec.step(s, qpool, lsepool, knew, vnew, out))
         return n_ev
 
-    # ---- pre-roll and warm-up (untimed), then the timed steps
+    # ---- pre-roll and warm-up (untimed), then the timed steps.  Python's
+    # cyclic collector stays off while GPU work is issued: a full collection
+    # stalls the issuing thread for tens of milliseconds, long enough to
+    # drain the GPU's queue in the middle of a timed leg.
+    gc.collect()
+    gc.disable()
     if pre:
         run(pre, 0, args.mode, False)
         log(f"[bench] pre-roll: {pre} steps to {dec.cache.t_len} rows (timed steps centre on the "
@@ -868,6 +874,7 @@ def main():
         del x, y, a, c
         log("[bench] copy calibration done: 1 GiB blit, 512 MiB vectorized copy")
 
+    gc.enable()
     cpu = parity = None
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host (bounded sample)")
