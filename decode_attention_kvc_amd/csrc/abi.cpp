@@ -155,6 +155,11 @@ ScorePlan plan_score(int dtype, int rows, int t_len, int slabs) {
     const long long target = per_cu * CU_COUNT;
     pl.main_tps = (int)std::max<long long>(8, (work + target - 1) / target);
     pl.main_nsplit = (ntiles + pl.main_tps - 1) / pl.main_tps;
+    if (dtype != KVC_F32 && score_stats_tiled(rows)) {
+        // the statistics pass runs on the score pass's grid
+        pl.tps = pl.main_tps;
+        pl.nsplit = pl.main_nsplit;
+    }
     return pl;
 }
 

@@ -23,6 +23,9 @@ constexpr int XKV_MAX_ATTEND = 16;  // kept-row splits per (b, j) of a cross-lay
 
 // LDS of one bf16 score-pass workgroup: the window queries (16-row blocks)
 // plus one float (lse term) and one int (last visible row) per row.
+// bf16 windows of up to 256 rows run the statistics pass on the score
+// pass's grid and tiling (its splits then size the statistics workspace).
+inline bool score_stats_tiled(int rows) { return rows <= 256; }
 inline size_t score_main_lds_bytes(int rows) {
     return (size_t)((rows + 15) / 16) * 16 * (SCORE_QPITCH * 2 + 8);
 }

@@ -265,6 +265,152 @@ __global__ __launch_bounds__(PF ? 512 : 1024) void score_stats_bf16(ScoreLaunch 
     }
 }
 
+// Pass 1 in the score pass's structure (windows of up to 256 rows): the
+// slab's g*w window queries are staged in LDS once per workgroup and each
+// wave takes whole 32-row tiles (round-robin), so every K byte is loaded by
+// one wave once.  The product runs transposed, S^T = K Q^T (the K tile is
+// the A operand as loaded, the staged queries the B operand), so a lane
+// holds one window row and eight cache rows of the tile per 16-row query
+// block, and each row needs one running (reference, sum) pair per lane:
+// sum += e^(x - ref), one fma and one bare exp2 per logit.  The reference is
+// a logit the lane has seen; it moves (rescaling the sum) only when a
+// logit exceeds it by more than RESCALE (a wave-uniform branch, taken on the
+// first tile and then rarely), so a term is at most e^RESCALE and a slab's
+// sum stays far below the float32 range, while the largest term is at least
+// 1 (terms the bare exp2 flushes to zero are below 2^-126 of the sum).  The
+// four lanes that share a row and then the four waves merge their pairs in a
+// fixed order; the workgroup writes one (reference, sum) pair per row and
+// split, in natural-log units, for score_lse_merge.
+constexpr float RESCALE = 40.f;
+
+template <int MT>
+__global__ __launch_bounds__(256) void score_stats_tiles_bf16(ScoreLaunch p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int NW = 4;
+    const BlockXYZ blk = xcd_run_block(true);
+    const int s = blk.x, j = blk.y, b = blk.z;
+    const int slab = b * p.hkv + j;
+    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int phys = seq_phys(p.sm, b);
+    const int T = seq_rows(p.sm, b, phys);     // a split past the end writes (-inf, 0)
+    const int ntiles = (T + SCORE_TILE - 1) / SCORE_TILE;
+    const int tile_begin = s * p.tps, tile_end = min(tile_begin + p.tps, ntiles);
+    uint16_t* qs = reinterpret_cast<uint16_t*>(smem);                          // [MT*16][QPITCH]
+
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q_obs);
+    for (int x = tid; x < MT * 16 * (D / 8); x += blockDim.x) {
+        const int R = x / (D / 8), c = x % (D / 8);
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (R < p.rows) {
+            const int h = j * p.g + R / p.w, iw = R % p.w;
+            v = load16(q + (((size_t)iw * p.nb + b) * p.hq + h) * D + 8 * c);
+        }
+        *reinterpret_cast<u32x4*>(qs + R * SCORE_QPITCH + 8 * c) = v;
+    }
+    __syncthreads();
+
+    const uint16_t* kslab =
+        reinterpret_cast<const uint16_t*>(p.k) + ((size_t)max(phys, 0) * p.hkv + j) * p.t_cap * D;
+    const float c1 = p.scale * LOG2E;
+    float m[MT], z[MT];
+    int lim[MT];                  // last cache row the lane's window row sees
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        m[mt] = -INFINITY;
+        z[mt] = 0.f;
+        const int R = mt * 16 + l16;
+        lim[mt] = R < p.rows ? T - p.w + R % p.w : -1;   // padding rows see nothing
+    }
+
+    auto body = [&](const u32x4 (&kb)[2][4], int t0, auto tail_tag) {
+        constexpr bool TAIL = decltype(tail_tag)::value;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            const uint16_t* qrow = qs + (mt * 16 + l16) * SCORE_QPITCH + 8 * lg;
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) {
+                const bf16x8 bq = as_bf(*reinterpret_cast<const u32x4*>(qrow + 32 * kc));
+                S[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(kb[0][kc]), bq, S[0], 0, 0, 0);
+                S[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(kb[1][kc]), bq, S[1], 0, 0, 0);
+            }
+            // S[cg][i]: cache row t0 + 16*cg + 4*lg + i, window row mt*16 + l16
+            float xm = -INFINITY;
+#pragma unroll
+            for (int cg = 0; cg < 2; ++cg)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool v = !TAIL || t0 + 16 * cg + 4 * lg + i <= lim[mt];
+                    xm = fmaxf(xm, v ? S[cg][i] : -INFINITY);
+                }
+            xm *= p.scale;
+            const bool need = xm > m[mt] + RESCALE;
+            if (__builtin_amdgcn_ballot_w64(need)) {
+                if (need) {
+                    z[mt] = m[mt] == -INFINITY ? 0.f : z[mt] * exp2f((m[mt] - xm) * LOG2E);
+                    m[mt] = xm;
+                }
+            }
+            const float nl = -m[mt] * LOG2E;
+            float acc = 0.f;
+#pragma unroll
+            for (int cg = 0; cg < 2; ++cg)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float pr = __builtin_amdgcn_exp2f(fmaf(S[cg][i], c1, nl));
+                    if constexpr (TAIL) pr = t0 + 16 * cg + 4 * lg + i <= lim[mt] ? pr : 0.f;
+                    acc += pr;
+                }
+            if (m[mt] != -INFINITY) z[mt] += acc;     // a row with no reference yet saw nothing
+        }
+    };
+    using Interior = std::integral_constant<bool, false>;
+    using Tail = std::integral_constant<bool, true>;
+    for (int tile = tile_begin + wave; tile < tile_end; tile += NW) {
+        const int t0 = tile * SCORE_TILE;
+        u32x4 kb[2][4];
+#pragma unroll
+        for (int cg = 0; cg < 2; ++cg) {
+            const uint16_t* kr = kslab + (size_t)(t0 + 16 * cg + l16) * D + 8 * lg;
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) kb[cg][kc] = load_stream16(kr + 32 * kc);
+        }
+        if (t0 + SCORE_TILE - 1 <= T - p.w)
+            body(kb, t0, Interior{});
+        else
+            body(kb, t0, Tail{});
+    }
+    // the four lane groups (cache rows) that share each window row
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int k = 16; k < 64; k <<= 1) {
+            const float m2 = __shfl_xor(m[mt], k), z2 = __shfl_xor(z[mt], k);
+            ms_merge(m[mt], z[mt], m2, z2);
+        }
+    // the four waves, in order, through LDS (the staged queries are done)
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(smem);                 // [NW][MT*16][2]
+    if (lg == 0) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int R = mt * 16 + l16;
+            red[(wave * MT * 16 + R) * 2] = m[mt];
+            red[(wave * MT * 16 + R) * 2 + 1] = z[mt];
+        }
+    }
+    __syncthreads();
+    float* st = p.stats + ((size_t)slab * p.nsplit + s) * p.rows_pad * 2;
+    for (int R = tid; R < p.rows; R += blockDim.x) {
+        float mm = red[R * 2], zz = red[R * 2 + 1];
+        for (int w2 = 1; w2 < NW; ++w2)
+            ms_merge(mm, zz, red[(w2 * MT * 16 + R) * 2], red[(w2 * MT * 16 + R) * 2 + 1]);
+        st[R * 2] = zz > 0.f ? mm : -INFINITY;
+        st[R * 2 + 1] = zz;
+    }
+}
+
 // Merge the splits' (max, sum) pairs of every window row into its
 // log-normaliser; one workgroup per slab, one thread per row, splits folded
 // in order.
@@ -659,15 +805,47 @@ hipError_t launch_score(const ScoreLaunch& p, int dtype, hipStream_t st) {
         hipLaunchKernelGGL(score_f32, grid, dim3(256), 0, st, p, 0);
     } else {
         const int nw = (p.rows + 31) / 32;
-        if (!p.lse_obs) {
-            if (nw <= 8)
-                hipLaunchKernelGGL(score_stats_bf16<1>, grid, dim3(nw * WAVE), 0, st, p);
-            else
-                hipLaunchKernelGGL(score_stats_bf16<0>, grid, dim3(nw * WAVE), 0, st, p);
-            hipLaunchKernelGGL(score_lse_merge, dim3(p.hkv, p.nb), dim3(1024), 0, st, p);
-        }
         const dim3 mgrid(p.main_nsplit, p.hkv, p.nb);
         const size_t lds = score_main_lds_bytes(p.rows);
+        if (!p.lse_obs) {
+            const int mt = (p.rows + 15) / 16;
+            if (score_stats_tiled(p.rows)) {
+                // the statistics pass on the score pass's grid; its staged
+                // queries cover the even block count the kernel is built for
+                ScoreLaunch q = p;
+                q.nsplit = p.main_nsplit;
+                q.tps = p.main_tps;
+                const size_t lds_st = score_main_lds_bytes(((mt + 1) / 2) * 32);
+                hipError_t e = hipErrorInvalidValue;
+                auto go_stats = [&](auto kern) {
+                    if (lds_st > 64 * 1024 &&
+                        hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                                            (int)lds_st) != hipSuccess)
+                        return hipErrorInvalidValue;
+                    hipLaunchKernelGGL(kern, mgrid, dim3(256), lds_st, st, q);
+                    return hipSuccess;
+                };
+                switch ((mt + 1) / 2) {   // MT rounded up to even: padding blocks see nothing
+                    case 1: e = go_stats(score_stats_tiles_bf16<2>); break;
+                    case 2: e = go_stats(score_stats_tiles_bf16<4>); break;
+                    case 3: e = go_stats(score_stats_tiles_bf16<6>); break;
+                    case 4: e = go_stats(score_stats_tiles_bf16<8>); break;
+                    case 5: e = go_stats(score_stats_tiles_bf16<10>); break;
+                    case 6: e = go_stats(score_stats_tiles_bf16<12>); break;
+                    case 7: e = go_stats(score_stats_tiles_bf16<14>); break;
+                    default: e = go_stats(score_stats_tiles_bf16<16>); break;
+                }
+                if (e != hipSuccess) return e;
+                hipLaunchKernelGGL(score_lse_merge, dim3(p.hkv, p.nb), dim3(1024), 0, st, q);
+            } else {
+                if (nw <= 8)
+                    hipLaunchKernelGGL(score_stats_bf16<1>, grid, dim3(nw * WAVE), 0, st, p);
+                else
+                    hipLaunchKernelGGL(score_stats_bf16<0>, grid, dim3(nw * WAVE), 0, st, p);
+                hipLaunchKernelGGL(score_lse_merge, dim3(p.hkv, p.nb), dim3(1024), 0, st, p);
+            }
+        }
         auto go = [&](auto kern) {
             if (lds > 64 * 1024 &&
                 hipFuncSetAttribute(reinterpret_cast<const void*>(kern),

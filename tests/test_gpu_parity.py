@@ -203,6 +203,9 @@ SCORE_CASES = [
     (torch.bfloat16, 1, 16, 8, 300, 5, True),
     (torch.bfloat16, 1, 32, 8, 8448, 32, True),      # Llama-3.1-8B steady pass length
     (torch.bfloat16, 1, 40, 8, 33280, 32, True),     # Qwen3-14B steady pass: g 5, 160 rows
+    (torch.bfloat16, 2, 40, 8, 777, 16, False),      # 80 rows: an odd number of 16-row blocks
+    (torch.bfloat16, 1, 64, 8, 900, 40, False),      # 320 rows: the per-head statistics pass
+    (torch.bfloat16, 1, 40, 8, 40000, 32, False),    # a prompt-sized slab, 160 rows
     (torch.float32, 1, 8, 2, 1024, 32, False),
     (torch.float32, 1, 8, 2, 1024, 32, True),
 ]
