@@ -603,7 +603,7 @@ int kvc_score(const kvc_cache* c, int slot, const void* q_obs, int n_q_heads, in
 int kvc_select_ws_bytes(int nb, int n_kv_heads, int t_len, size_t* bytes) {
     if (!bytes) return KVC_EALIGN;
     if (nb < 0 || n_kv_heads < 1 || t_len < 0) return KVC_EINVAL;
-    *bytes = (size_t)nb * n_kv_heads * t_len * sizeof(uint32_t);
+    *bytes = 2 * (size_t)nb * n_kv_heads * t_len * sizeof(uint32_t);
     return KVC_OK;
 }
 
@@ -627,7 +627,7 @@ int kvc_select_seq(const float* score, const float* range, int nb, int n_kv_head
     if (!aligned4(score) || !aligned4(kept)) return KVC_EALIGN;
     if (n_v > 0 && !aligned4(range)) return KVC_EALIGN;
     if ((seq_len && !aligned4(seq_len)) || (seq_id && !aligned4(seq_id))) return KVC_EALIGN;
-    const size_t need = (size_t)nb * n_kv_heads * t_len * sizeof(uint32_t);
+    const size_t need = 2 * (size_t)nb * n_kv_heads * t_len * sizeof(uint32_t);
     const bool evicts = t_len > budget_k + recent_b;
     if (evicts && (!ws || ws_bytes < need || !aligned4(ws))) return KVC_EWORKSPACE;
     SelectLaunch p;
@@ -645,6 +645,7 @@ int kvc_select_seq(const float* score, const float* range, int nb, int n_kv_head
     p.layer_id = (uint32_t)layer_id;
     p.kept = kept;
     p.keys = static_cast<uint32_t*>(ws);
+    p.kappa = p.keys + (size_t)nb * n_kv_heads * t_len;
     p.len = seq_len;
     p.seq_id = seq_id;
     if (launch_select(p, (hipStream_t)stream) != hipSuccess) return KVC_EHIP;

@@ -166,7 +166,8 @@ struct SelectLaunch {
     uint32_t seed_lo, seed_hi;
     uint32_t layer_id;
     int32_t* kept;
-    uint32_t* keys;         // workspace [slabs][t_len]
+    uint32_t* keys;         // workspace [slabs][t_len]: selection keys of slabs past LDS_KEYS rows
+    uint32_t* kappa;        // workspace [slabs][t_len]: sampling keys of the candidate rows
     const int32_t* len;     // [nb] rows per slab's sequence, or null (t_len)
     const int32_t* seq_id;  // [nb] sequence word of the Philox counter, or null (b)
 };

@@ -11,14 +11,19 @@
 // low, seed high): E_t = -ln((x_t + 1) / 2^32), evaluated in double with
 // log1p so that words near 2^32 keep full relative accuracy.
 //
-// One workgroup of 1024 threads per slab.  Both "k best" decisions are
-// exact radix selections on 32-bit order-preserving keys: four passes of
-// 8-bit digits with LDS histograms find the k-th key; rows strictly before
-// it are in, rows equal to it are taken in ascending row order.  The kept
-// rows are emitted in ascending order with block-wide ordered scans.
+// Two launches.  select_keys_kernel computes the sampling key of every
+// candidate row of every slab (Philox + log1p in double: the only heavy
+// arithmetic, spread over the whole chip) into the workspace.  Then one
+// workgroup of 1024 threads per slab makes both "k best" decisions as exact
+// radix selections on 32-bit order-preserving keys: four passes of 8-bit
+// digits with LDS histograms find the k-th key; rows strictly before it are
+// in, rows equal to it are taken in ascending row order.  The row-ordered
+// steps (which of the rows tied at a threshold are taken, and the ascending
+// emission of the kept rows) give each thread a contiguous run of rows and
+// need one block-wide scan of per-thread counts each, not one per 1024 rows.
 // The keys (first the range keys, then, in place, the sampling keys) live in
 // LDS when the slab has at most LDS_KEYS rows, otherwise in the caller's
-// workspace (one uint32 per row); all accesses stay inside one workgroup.
+// workspace; all accesses stay inside one workgroup.
 #include "common.h"
 #include "kvc_internal.h"
 #include "philox.h"
@@ -30,7 +35,8 @@ namespace {
 
 constexpr int NT = SELECT_THREADS;
 constexpr int NWV = NT / WAVE;
-constexpr uint32_t EXCLUDED = 0xFFFFFFFFu;   // above every float key
+constexpr uint32_t EXCLUDED = 0xFFFFFFFFu;   // above every float key: a protected row
+constexpr uint32_t TIE_R = 0xFFFFFFFEu;      // range key at the threshold, order not yet decided
 constexpr int LDS_KEYS = 36 * 1024;           // 144 KB of keys
 
 using SelectSmem = RadixSmem<NT, 8>;   // 8 histogram copies: range keys share their top digit
@@ -52,18 +58,29 @@ __device__ __forceinline__ uint32_t sample_key(const SelectLaunch& p, int t, int
     return __float_as_uint(kappa);
 }
 
+// Sampling key of every candidate row [0, T - B) of every evicting slab.
+__global__ __launch_bounds__(256) void select_keys_kernel(SelectLaunch p) {
+    const int slab = blockIdx.y;
+    const int b = slab / p.hkv, j = slab % p.hkv;
+    const int T = p.len ? min(max(p.len[b], 0), p.t_len) : p.t_len;
+    if (T <= p.budget_k + p.recent_b) return;       // keeps everything
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= T - p.recent_b) return;
+    const uint32_t seq = p.seq_id ? (uint32_t)p.seq_id[b] : (uint32_t)b;
+    p.kappa[(size_t)slab * p.t_len + t] = sample_key(p, t, j, seq, p.score[(size_t)slab * p.t_len + t]);
+}
+
 template <bool IN_LDS>
 __global__ __launch_bounds__(NT) void select_kernel(SelectLaunch p) {
     __shared__ SelectSmem sm;
     __shared__ uint32_t lds_keys[IN_LDS ? LDS_KEYS : 1];
     const int slab = blockIdx.x;
-    const int b = slab / p.hkv, j = slab % p.hkv;
+    const int b = slab / p.hkv;
     const int tid = threadIdx.x;
     // Ragged batches: the slab's own row count T (at most t_len, which is
     // the row stride of score / range / keys) and kept stride min(t_len, K+B);
     // kept entries past the slab's min(T, K+B) are -1.
     const int T = p.len ? min(max(p.len[b], 0), p.t_len) : p.t_len;
-    const uint32_t seq = p.seq_id ? (uint32_t)p.seq_id[b] : (uint32_t)b;
     const int kb = p.budget_k + p.recent_b;
     const int stride = min(p.t_len, kb);
     int32_t* kept = p.kept + (size_t)slab * stride;
@@ -72,8 +89,8 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectLaunch p) {
         return;
     }
     const int n_keep = kb;
-    const float* score = p.score + (size_t)slab * p.t_len;
     const float* range = p.range + (size_t)slab * p.t_len;
+    const uint32_t* kap = p.kappa + (size_t)slab * p.t_len;
     uint32_t* keys = IN_LDS ? lds_keys : p.keys + (size_t)slab * p.t_len;
     const int ncand = T - p.recent_b;
 
@@ -85,24 +102,29 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectLaunch p) {
         rthr = radix_select<NT>(ncand, (uint32_t)p.n_v, [&](int t) { return keys[t]; }, sm, &rtake);
     }
 
-    // 2. Sampling keys for the remaining candidates, written over the range
-    //    keys; protected rows are marked EXCLUDED.  Ordered pass: equal-range
-    //    rows are protected in row order.
-    uint32_t eq_seen = 0;
-    for (int base = 0; base < ncand; base += NT) {
-        const int t = base + tid;
-        const bool valid = t < ncand;
-        const uint32_t rk = (valid && p.n_v > 0) ? keys[t] : 0xFFFFFFFFu;
-        const bool eq = valid && p.n_v > 0 && rk == rthr;
-        uint32_t tot;
-        const uint32_t rank = eq_seen + block_scan_flag<NT>(eq, sm, &tot);
-        eq_seen += tot;
-        if (valid) {
-            const bool prot = p.n_v > 0 && (rk < rthr || (eq && rank < rtake));
-            keys[t] = prot ? EXCLUDED : sample_key(p, t, j, seq, score[t]);
+    // 2. Sampling keys over the range keys; rows before the range threshold
+    //    are protected (EXCLUDED), rows at it are marked and then protected
+    //    in row order (the first rtake of them), the others get their key.
+    for (int t = tid; t < ncand; t += NT) {
+        uint32_t u = kap[t];
+        if (p.n_v > 0) {
+            const uint32_t rk = keys[t];
+            if (rk < rthr) u = EXCLUDED;
+            else if (rk == rthr) u = TIE_R;
         }
+        keys[t] = u;
     }
     __syncthreads();
+    if (p.n_v > 0) {
+        const int c = (ncand + NT - 1) / NT, lo = min(ncand, tid * c), hi = min(ncand, lo + c);
+        uint32_t n = 0;
+        for (int t = lo; t < hi; ++t) n += keys[t] == TIE_R;
+        uint32_t tot;
+        uint32_t rank = block_scan_u32<NT>(n, sm, &tot);
+        for (int t = lo; t < hi; ++t)
+            if (keys[t] == TIE_R) keys[t] = rank++ < rtake ? EXCLUDED : kap[t];
+        __syncthreads();
+    }
 
     // 3. K - N_v smallest sampling keys.
     const uint32_t ns = (uint32_t)(p.budget_k - p.n_v);
@@ -110,29 +132,39 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectLaunch p) {
     if (ns > 0) kthr = radix_select<NT>(
         ncand, ns, [&](int t) { return keys[t]; }, sm, &ktake);
 
-    // 4. Emit kept rows in ascending order.
-    uint32_t written = 0, keq_seen = 0;
-    for (int base = 0; base < T; base += NT) {
-        const int t = base + tid;
-        const bool valid = t < T;
-        bool keep = false, eq = false;
-        uint32_t u = 0;
-        if (valid) {
+    // 4. Emit the kept rows in ascending order: each thread owns a run of
+    //    rows; its offset is the kept rows before the run (the sure ones, and
+    //    the first ktake rows tied at the sampling threshold, in row order).
+    {
+        const int c = (T + NT - 1) / NT, lo = min(T, tid * c), hi = min(T, lo + c);
+        uint32_t nsure = 0, neq = 0;
+        for (int t = lo; t < hi; ++t) {
             if (t >= ncand) {
-                keep = true;
+                ++nsure;
             } else {
-                u = keys[t];
-                eq = ns > 0 && u == kthr && u != EXCLUDED;
-                keep = (u == EXCLUDED) || (ns > 0 && u < kthr);
+                const uint32_t u = keys[t];
+                if (u == EXCLUDED || (ns > 0 && u < kthr)) ++nsure;
+                else if (ns > 0 && u == kthr) ++neq;
             }
         }
         uint32_t tot;
-        const uint32_t rank = keq_seen + block_scan_flag<NT>(eq, sm, &tot);
-        keq_seen += tot;
-        if (eq && rank < ktake) keep = true;
-        const uint32_t pos = written + block_scan_flag<NT>(keep, sm, &tot);
-        written += tot;
-        if (keep && pos < (uint32_t)n_keep) kept[pos] = t;
+        const uint32_t sure_off = block_scan_u32<NT>(nsure, sm, &tot);
+        uint32_t eq_rank = block_scan_u32<NT>(neq, sm, &tot);
+        uint32_t pos = sure_off + min(eq_rank, ktake);
+        for (int t = lo; t < hi; ++t) {
+            bool keep;
+            if (t >= ncand) {
+                keep = true;
+            } else {
+                const uint32_t u = keys[t];
+                keep = u == EXCLUDED || (ns > 0 && u < kthr);
+                if (ns > 0 && u == kthr) keep = eq_rank++ < ktake;
+            }
+            if (keep) {
+                if (pos < (uint32_t)n_keep) kept[pos] = t;
+                ++pos;
+            }
+        }
     }
 }
 
@@ -148,6 +180,10 @@ __global__ void philox_kernel(int64_t n, uint32_t c1, uint32_t c2, uint32_t c3, 
 }  // namespace
 
 hipError_t launch_select(const SelectLaunch& p, hipStream_t st) {
+    if (p.t_len > p.budget_k + p.recent_b) {
+        const dim3 kgrid((p.t_len - p.recent_b + 255) / 256, p.nb * p.hkv);
+        hipLaunchKernelGGL(select_keys_kernel, kgrid, dim3(256), 0, st, p);
+    }
     if (p.t_len <= LDS_KEYS)
         hipLaunchKernelGGL(select_kernel<true>, dim3(p.nb * p.hkv), dim3(NT), 0, st, p);
     else

@@ -311,7 +311,9 @@ int kvc_score(const kvc_cache* c, int slot, const void* q_obs, int n_q_heads,
               int w, float scale, const float* lse_obs, float* score,
               float* range, void* ws, size_t ws_bytes, kvc_stream_t stream);
 
-/* Workspace bytes kvc_select needs for nb * n_kv_heads slabs of t_len rows. */
+/* Workspace bytes kvc_select needs for nb * n_kv_heads slabs of t_len rows
+ * (two uint32 per row: the sampling key of every candidate row, and the
+ * selection keys of slabs too long for LDS). */
 int kvc_select_ws_bytes(int nb, int n_kv_heads, int t_len, size_t* bytes);
 
 /*

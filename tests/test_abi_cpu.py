@@ -129,7 +129,7 @@ def test_ws_bytes_queries():
     assert n.value > 0
     assert L.kvc_decode_attn_ws_bytes(ctypes.byref(c), 1, 7, ctypes.byref(n)) == kvc.KVC_EINVAL
     assert L.kvc_score_ws_bytes(ctypes.byref(c), 8, 32, ctypes.byref(n)) == 0 and n.value > 0
-    assert L.kvc_select_ws_bytes(2, 8, 1000, ctypes.byref(n)) == 0 and n.value == 2 * 8 * 1000 * 4
+    assert L.kvc_select_ws_bytes(2, 8, 1000, ctypes.byref(n)) == 0 and n.value == 2 * (2 * 8 * 1000 * 4)
     assert L.kvc_select_ws_bytes(2, 0, 1000, ctypes.byref(n)) == kvc.KVC_EINVAL
 
 
