@@ -281,7 +281,7 @@ DkvWs dkv_layout(int rank, int t_len, int slabs) {
     w.y_off = 0;
     w.gram_off = align_up((size_t)slabs * t_len * rank * sizeof(float), 256);
     w.w_off = w.gram_off + align_up((size_t)slabs * w.nsplit * rank * rank * sizeof(double), 256);
-    w.total = w.w_off + (size_t)slabs * rank * rank * sizeof(float);
+    w.total = w.w_off + (size_t)slabs * rank * rank * sizeof(double);
     return w;
 }
 
@@ -856,7 +856,7 @@ int kvc_q8_decode_attn(const kvc_qcache* c, const void* q, int64_t q_layer_strid
 }
 
 int kvc_dkv_ws_bytes(const kvc_cache* c, int rank, size_t* bytes) {
-    int st = check_tiled(c);
+    int st = check_cache(c);
     if (st) return st;
     if (!bytes) return KVC_EALIGN;
     if (rank != 16 && rank != 32) return KVC_EINVAL;
@@ -867,7 +867,7 @@ int kvc_dkv_ws_bytes(const kvc_cache* c, int rank, size_t* bytes) {
 
 int kvc_dkv_score(const kvc_cache* c, int slot, const void* g, int rank, float* score,
                   float* range, void* ws, size_t ws_bytes, kvc_stream_t stream) {
-    int st = check_tiled(c);
+    int st = check_cache(c);
     if (st) return st;
     if (c->dtype != KVC_BF16) return KVC_EDTYPE;
     if (slot < 0 || slot >= c->n_slots) return KVC_EINVAL;
@@ -894,8 +894,9 @@ int kvc_dkv_score(const kvc_cache* c, int slot, const void* g, int rank, float* 
     char* base = static_cast<char*>(ws);
     p.y = reinterpret_cast<float*>(base + lay.y_off);
     p.gram = reinterpret_cast<double*>(base + lay.gram_off);
-    p.w = reinterpret_cast<float*>(base + lay.w_off);
+    p.w = reinterpret_cast<double*>(base + lay.w_off);
     p.sm = seq_map(c);
+    p.v_rows = v_rows(c);
     if (launch_dkv(p, (hipStream_t)stream) != hipSuccess) return KVC_EHIP;
     return hip_status();
 }

@@ -26,8 +26,11 @@
 //     workgroup writes its partial Gram (float64).
 //  2. dkv_factor: one wave per slab sums the partial Grams in split order,
 //     factors them (Cholesky with dropped pivots, float64, in registers) and
-//     writes W = R^{-1} (zero rows for dropped directions) as float32.
-//  3. dkv_leverage: score_t = ||y_t W||^2, one thread per row.
+//     writes W = R^{-1} (zero rows for dropped directions) as float64.
+//  3. dkv_leverage: score_t = ||y_t W||^2 in float64 (the float32 y_t widened
+//     exactly), one thread per row, rounded to float32 once at the end; the
+//     inverse factor and the quadratic form then add only float64 rounding
+//     to what the float32 sketch carries.
 // Ragged batches: sequence b sketches rows [0, T_b) of cache entry phys(b)
 // (splits past its end contribute a zero Gram); Y and the scores keep the
 // launch's t_len as their row stride.
@@ -103,7 +106,37 @@ __device__ __forceinline__ void tile_range(const u32x4 (&x)[8], int t0, int T, f
     }
 }
 
-template <int R, bool RANGE>
+// Range of the 32 rows of a tile whose values were loaded as rows (the
+// operand fragments va[rb][kc]: row t0 + 16*rb + l16, channels 32*kc + 8*lg
+// .. +8): each lane reduces its 32 channels, the four lane groups of a row
+// meet by lane exchanges.
+__device__ __forceinline__ void tile_range_rows(const u32x4 (&va)[2][4], int t0, int T,
+                                                float* range_out, int lane) {
+    const int l16 = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        float mx = -INFINITY, mn = INFINITY;
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+            for (int w2 = 0; w2 < 4; ++w2) {
+                const float a = bf16lo(va[rb][kc][w2]), c = bf16hi(va[rb][kc][w2]);
+                mx = fmaxf(mx, fmaxf(a, c));
+                mn = fminf(mn, fminf(a, c));
+            }
+#pragma unroll
+        for (int m = 16; m < 64; m <<= 1) {
+            mx = fmaxf(mx, __shfl_xor(mx, m));
+            mn = fminf(mn, __shfl_xor(mn, m));
+        }
+        const int t = t0 + 16 * rb + l16;
+        if (lg == 0 && t < T) range_out[t] = mx - mn;
+    }
+}
+
+// VROWS: the slab's values are [t][D] rows (a prefill's layout) and load as
+// operand fragments exactly like the keys, with no transpose.
+template <int R, bool RANGE, bool VROWS>
 __global__ __launch_bounds__(256) void dkv_sketch(DkvLaunch p) {
     constexpr int CB = R / 16;                  // 16-column blocks of Y
     constexpr int NG = CB * (CB + 1) / 2;       // upper-triangle Gram blocks
@@ -149,34 +182,46 @@ __global__ __launch_bounds__(256) void dkv_sketch(DkvLaunch p) {
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc) ka[rb][kc] = load_stream16(kr + 32 * kc);
         }
-        // V block: channels 16*dt + l16, rows 8*lg .. +8.
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-            vt[dt] = load_stream16(vslab + vt_off(t0, 16 * dt + l16) + 8 * lg);
-
-        // V block into the wave's buffer ([channel][row], 68-byte pitch), then
-        // back out one row per lane: the previous tile's reads of the buffer
-        // and these writes, and these writes and the reads below, are ordered
-        // because one wave's LDS instructions execute in issue order.
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            uint32_t* dst = reinterpret_cast<uint32_t*>(vb + (16 * dt + l16) * VPITCH + 8 * lg);
-#pragma unroll
-            for (int w2 = 0; w2 < 4; ++w2) dst[w2] = vt[dt][w2];
-        }
-        __builtin_amdgcn_wave_barrier();
-        if constexpr (RANGE) tile_range(vt, t0, T, range, lane);
         u32x4 va[2][4];
+        if constexpr (VROWS) {
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+            for (int rb = 0; rb < 2; ++rb) {
+                const uint16_t* vr = vslab + (size_t)(t0 + 16 * rb + l16) * D + 8 * lg;
 #pragma unroll
-            for (int kc = 0; kc < 4; ++kc) {
-                u16x8 e;
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) e[jj] = vb[(32 * kc + 8 * lg + jj) * VPITCH + 16 * rb + l16];
-                va[rb][kc] = __builtin_bit_cast(u32x4, e);
+                for (int kc = 0; kc < 4; ++kc) va[rb][kc] = load_stream16(vr + 32 * kc);
             }
+            if constexpr (RANGE) tile_range_rows(va, t0, T, range, lane);
+        } else {
+            // V block: channels 16*dt + l16, rows 8*lg .. +8.
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+                vt[dt] = load_stream16(vslab + vt_off(t0, 16 * dt + l16) + 8 * lg);
+
+            // V block into the wave's buffer ([channel][row], 68-byte pitch),
+            // then back out one row per lane: the previous tile's reads of
+            // the buffer and these writes, and these writes and the reads
+            // below, are ordered because one wave's LDS instructions execute
+            // in issue order.
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                uint32_t* dst = reinterpret_cast<uint32_t*>(vb + (16 * dt + l16) * VPITCH + 8 * lg);
+#pragma unroll
+                for (int w2 = 0; w2 < 4; ++w2) dst[w2] = vt[dt][w2];
+            }
+            __builtin_amdgcn_wave_barrier();
+            if constexpr (RANGE) tile_range(vt, t0, T, range, lane);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int kc = 0; kc < 4; ++kc) {
+                    u16x8 e;
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj)
+                        e[jj] = vb[(32 * kc + 8 * lg + jj) * VPITCH + 16 * rb + l16];
+                    va[rb][kc] = __builtin_bit_cast(u32x4, e);
+                }
+        }
 
         // Y[rb][cb][i]: row t0 + 16*rb + 4*lg + i, sketch column 16*cb + l16.
         f32x4 Y[2][CB];
@@ -330,25 +375,25 @@ __global__ __launch_bounds__(64) void dkv_factor(DkvLaunch p) {
         w[i] = (keep[i] && i <= col) ? acc / uii : 0.0;
     }
     if (lane < R) {
-        float* wo = p.w + (size_t)slab * R * R;
+        double* wo = p.w + (size_t)slab * R * R;
 #pragma unroll
-        for (int i = 0; i < R; ++i) wo[i * R + col] = (float)w[i];
+        for (int i = 0; i < R; ++i) wo[i * R + col] = w[i];
     }
 }
 
 // score_t = ||y_t W||^2, W upper triangular; one thread per row.
 template <int R>
 __global__ __launch_bounds__(256) void dkv_leverage(DkvLaunch p) {
-    __shared__ float ws[R][R];
+    __shared__ double ws[R][R];
     const int slab = blockIdx.z * p.hkv + blockIdx.y;
-    const float* w = p.w + (size_t)slab * R * R;
+    const double* w = p.w + (size_t)slab * R * R;
     for (int x = threadIdx.x; x < R * R; x += blockDim.x) ws[x / R][x % R] = w[x];
     __syncthreads();
     const int t = blockIdx.x * blockDim.x + threadIdx.x;
     const int b = blockIdx.z;
     if (t >= seq_rows(p.sm, b, seq_phys(p.sm, b))) return;
     const float* y = p.y + ((size_t)slab * p.t_len + t) * R;
-    float yv[R];
+    double yv[R];
 #pragma unroll
     for (int c = 0; c < R; c += 4) {
         const f32x4 v = *reinterpret_cast<const f32x4*>(y + c);
@@ -357,15 +402,15 @@ __global__ __launch_bounds__(256) void dkv_leverage(DkvLaunch p) {
         yv[c + 2] = v[2];
         yv[c + 3] = v[3];
     }
-    float l = 0.f;
+    double l = 0.0;
 #pragma unroll
     for (int c = 0; c < R; ++c) {
-        float z = 0.f;
+        double z = 0.0;
 #pragma unroll
-        for (int i = 0; i <= c; ++i) z = fmaf(yv[i], ws[i][c], z);
-        l = fmaf(z, z, l);
+        for (int i = 0; i <= c; ++i) z = fma(yv[i], ws[i][c], z);
+        l = fma(z, z, l);
     }
-    p.score[(size_t)slab * p.t_len + t] = l;
+    p.score[(size_t)slab * p.t_len + t] = (float)l;
 }
 
 // Box-Muller on Philox4x32-10 words; pair q -> elements 2q, 2q+1.
@@ -389,21 +434,26 @@ hipError_t launch_dkv(const DkvLaunch& p, hipStream_t st) {
     const dim3 grid(p.nsplit, p.hkv, p.nb);
     const dim3 sgrid(p.hkv, p.nb);
     const dim3 lgrid((p.t_len + 255) / 256, p.hkv, p.nb);
-    if (p.rank == 16) {
-        if (p.range)
-            hipLaunchKernelGGL((dkv_sketch<16, true>), grid, dim3(256), 0, st, p);
-        else
-            hipLaunchKernelGGL((dkv_sketch<16, false>), grid, dim3(256), 0, st, p);
-        hipLaunchKernelGGL(dkv_factor<16>, sgrid, dim3(64), 0, st, p);
-        hipLaunchKernelGGL(dkv_leverage<16>, lgrid, dim3(256), 0, st, p);
-    } else {
-        if (p.range)
-            hipLaunchKernelGGL((dkv_sketch<32, true>), grid, dim3(256), 0, st, p);
-        else
-            hipLaunchKernelGGL((dkv_sketch<32, false>), grid, dim3(256), 0, st, p);
-        hipLaunchKernelGGL(dkv_factor<32>, sgrid, dim3(64), 0, st, p);
-        hipLaunchKernelGGL(dkv_leverage<32>, lgrid, dim3(256), 0, st, p);
-    }
+    auto sketch = [&](auto rank_tag) {
+        constexpr int RK = decltype(rank_tag)::value;
+        if (p.v_rows) {
+            if (p.range)
+                hipLaunchKernelGGL((dkv_sketch<RK, true, true>), grid, dim3(256), 0, st, p);
+            else
+                hipLaunchKernelGGL((dkv_sketch<RK, false, true>), grid, dim3(256), 0, st, p);
+        } else {
+            if (p.range)
+                hipLaunchKernelGGL((dkv_sketch<RK, true, false>), grid, dim3(256), 0, st, p);
+            else
+                hipLaunchKernelGGL((dkv_sketch<RK, false, false>), grid, dim3(256), 0, st, p);
+        }
+        hipLaunchKernelGGL(dkv_factor<RK>, sgrid, dim3(64), 0, st, p);
+        hipLaunchKernelGGL(dkv_leverage<RK>, lgrid, dim3(256), 0, st, p);
+    };
+    if (p.rank == 16)
+        sketch(std::integral_constant<int, 16>{});
+    else
+        sketch(std::integral_constant<int, 32>{});
     return hipGetLastError();
 }
 

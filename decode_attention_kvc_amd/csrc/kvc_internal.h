@@ -155,8 +155,9 @@ struct DkvLaunch {
     int nsplit, tps;        // sketch pass: splits per slab, tiles per split
     float* y;               // workspace [slabs][t_len][rank]
     double* gram;           // workspace [slabs][nsplit][rank][rank]
-    float* w;               // workspace [slabs][rank][rank]
+    double* w;              // workspace [slabs][rank][rank]: the inverse factor
     SeqMap sm;
+    int v_rows;             // values stored as [t][D] rows (else tiles)
 };
 
 struct SelectLaunch {

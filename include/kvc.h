@@ -94,7 +94,7 @@ typedef enum kvc_dtype {
  *   KVC_V_ROWS (1): v stored like k, [n_slots][nb_cap][n_kv_heads][t_cap]
  *     [head_dim] rows -- the layout a prefill writes.  A rows cache is an
  *     input of the prompt compression: kvc_value_range, kvc_score (with the
- *     fused range) and kvc_compact (as the source) read it, and kvc_compact
+ *     fused range), kvc_dkv_score and kvc_compact (as the source) read it, and kvc_compact
  *     re-lays the rows it gathers into a tiled destination (with kept =
  *     NULL it copies rows [0, n_keep): a bulk ingest).  Every other call
  *     returns KVC_EINVAL for it.

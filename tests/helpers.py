@@ -56,16 +56,14 @@ def band_compare(gpu_kept, detail, rel=1e-6):
     return ties, bad
 
 
-def dkv_tolerance(K, V, G, ref):
-    """Absolute bound on |score_gpu - score_ref| for the VASE-DKV leverage of
-    one slab.  The library forms Y = [K | V] G in float32 and W = R^-1 in
-    float32 (R the float64 Cholesky factor of Y^T Y); a float32 W carries a
-    relative error of order cond(Y) * sqrt(r) * 2^-24 in y_t W, and the
-    score squares it.  cond(Y) is taken over the kept directions
-    (singular values above 1e-6 of the largest: the pivot drop at 1e-12 of
-    the trace); the factor 4 covers the remaining constants."""
-    Y = np.concatenate([K, V], axis=1) @ G
-    s = np.linalg.svd(Y, compute_uv=False)
-    s = s[s > 1e-6 * s.max()] if s.size and s.max() > 0 else np.ones(1)
-    kappa = s.max() / s.min()
-    return 4.0 * kappa * np.sqrt(G.shape[1]) * 2.0 ** -24 * max(float(np.max(ref)), 1e-30)
+def dkv_tolerance(ref):
+    """Bound on |score_gpu - score_ref| for the VASE-DKV leverage of one slab,
+    elementwise: 1e-6 of the row's own score plus 1e-7 of the slab's largest.
+    The library forms Y = [K | V] G in float32 from exact bf16 products (a
+    relative error of a few 2^-24 per entry over 256 terms); the Gram matrix,
+    its factorisation, the inverse factor and the quadratic form are float64,
+    so the score carries the sketch's rounding (measured: at most 3.4e-7 of
+    the row's own score, 1.4e-7 of the slab's largest) and one float32
+    rounding of the result."""
+    ref = np.asarray(ref)
+    return 1e-6 * ref + 1e-7 * max(float(np.max(ref)), 1e-30)

@@ -417,7 +417,7 @@ def test_value_layout_validation():
     out = ctypes.c_size_t()
     assert L.kvc_decode_attn_ws_bytes(ctypes.byref(r), 1, 8, ctypes.byref(out)) == kvc.KVC_EINVAL
     assert L.kvc_append(ctypes.byref(r), 0, FAKE, FAKE, None) == kvc.KVC_EINVAL
-    assert L.kvc_dkv_ws_bytes(ctypes.byref(r), 32, ctypes.byref(out)) == kvc.KVC_EINVAL
+    assert L.kvc_dkv_ws_bytes(ctypes.byref(r), 32, ctypes.byref(out)) == kvc.KVC_OK
     slots = (ctypes.c_int32 * 1)(0)
     assert L.kvc_decode_attn_noalloc(ctypes.byref(r), FAKE, 0, 1, slots, 8, 0.0, None, None, -1,
                                      FAKE, 0, None, 0, None) == kvc.KVC_EINVAL

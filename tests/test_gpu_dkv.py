@@ -3,15 +3,14 @@ against oracle/dkv.py, through the C ABI.
 
 Tolerance of the scores (derived from the arithmetic, not fitted): Y = [K|V] G
 is accumulated in float32 from exact bf16 products over 256 terms, so each
-entry carries a relative error of a few 1e-7; the Gram matrix and its
-factorisation are float64 and add nothing; the float32 inverse factor W and
-the float32 quadratic form add a relative error of order
-cond(Y) * sqrt(r) * 2^-24 to y_t W, which the score squares.  The bound used
-per slab is 4 * cond(Y) * sqrt(r) * 2^-24 * max(l_ref), with cond(Y) taken
-from the float64 sketch (helpers.dkv_tolerance; measured errors: below
-5e-7 * max for well-conditioned slabs, 8e-6 for a 20-row slab whose sketch
-has cond ~ 8.5); the sum of the scores must equal rank(Y) to 1e-4
-relative.  The kept-set band keeps its relative form."""
+entry carries a relative error of a few 2^-24; the Gram matrix, its
+factorisation, the inverse factor W and the quadratic form ||y_t W||^2 are
+float64 and add nothing at this scale.  Bound, elementwise:
+|l - l_ref| <= 1e-6 l_ref + 1e-7 max(l_ref) (helpers.dkv_tolerance; measured:
+at most 3.4e-7 of the row's own score).  Kept sets follow the window-score
+rule: a row kept by one side only must lie within 1e-6 (relative) of the
+oracle's sampling cutoff (a tie, counted); any other difference fails.  The
+sum of the scores must equal rank(Y) to 1e-4 relative."""
 import sys
 
 import numpy as np
@@ -22,7 +21,7 @@ import oracle
 from oracle import dkv as odkv
 import kvc_synth
 import decode_attention_kvc_amd as kvc
-from helpers import make_cache, slab_np, ws_tensor, dkv_tolerance
+from helpers import make_cache, slab_np, ws_tensor, dkv_tolerance, band_compare
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -71,7 +70,9 @@ DKV_CASES = [
 
 def check_scores(got, ref, K, V, G):
     err = np.abs(got - ref)
-    bound = dkv_tolerance(K, V, G, ref)
+    bound = dkv_tolerance(ref)
+    rel = float(np.max(err / np.maximum(ref, 1e-30)))
+    say(f"    max |err| / max(ref) {err.max() / ref.max():.2e}, max |err| / ref {rel:.2e}")
     assert np.all(err <= bound), (float(err.max()), bound)
     return float(err.max() / ref.max())
 
@@ -147,8 +148,8 @@ def test_dkv_workspace_reuse_and_determinism():
 
 def test_dkv_kept_sets_match_oracle():
     """End to end: DKV scores -> VASE selection, against the oracle's own
-    scores and selection.  Rows within the score tolerance of the sampling
-    cutoff may flip; they are counted."""
+    scores and selection.  Rows within 1e-6 of the sampling cutoff may flip
+    (ties, counted); nothing else may."""
     say("dkv select")
     nb, hkv, T, rank = 1, 8, 4352, 32
     Kb, B, Nv = 4096, 128, 64
@@ -166,16 +167,10 @@ def test_dkv_kept_sets_match_oracle():
     for j in range(hkv):
         sc = odkv.dkv_score(K[0, j], V[0, j], g_for_oracle(g))
         d = oracle.select_detail(sc, oracle.value_range(V[0, j]), T, Kb, B, Nv, 99, 3, 0, j)
-        kc = d["kappa_cut"]
-        diff = set(kept[0, j].cpu().numpy().tolist()) ^ set(d["kept"].tolist())
-        for t in diff:
-            # a row may flip when its key and the cutoff's are closer than
-            # the score tolerance (relative to the row's own score) allows
-            eps = 2 * (5e-6 * sc.max() / sc[t] + 1e-6)
-            assert abs(d["kappa"][t] - kc) <= eps * kc, (j, t)
-        ties += len(diff)
-        assert len(diff) <= 8
-    say(f"  rows flipped inside the score tolerance: {ties}")
+        t, bad = band_compare(kept[0, j].cpu().numpy(), d, rel=1e-6)
+        assert bad == 0, j
+        ties += t
+    say(f"  ties within 1e-6 of the cutoff: {ties}")
 
 
 def test_decoder_dkv_initial_pass():
@@ -210,9 +205,7 @@ def test_decoder_dkv_initial_pass():
                 kept = np.array([rows[K1[b, j, i].tobytes()] for i in range(len(K1[b, j]))])
                 assert np.all(np.diff(kept) > 0)
                 assert np.array_equal(V1[b, j], V0[b, j, kept])
-                diff = set(kept.tolist()) ^ set(d["kept"].tolist())
-                for t in diff:
-                    eps = 2 * (5e-6 * sc.max() / sc[t] + 1e-6)
-                    assert abs(d["kappa"][t] - d["kappa_cut"]) <= eps * d["kappa_cut"]
-                flips += len(diff)
-    say(f"  rows flipped inside the score tolerance: {flips}")
+                t, bad = band_compare(kept, d, rel=1e-6)
+                assert bad == 0, (s, b, j)
+                flips += t
+    say(f"  ties within 1e-6 of the cutoff: {flips}")

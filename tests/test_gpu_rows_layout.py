@@ -220,3 +220,22 @@ def test_rows_cache_rejected_by_decode_calls():
     with pytest.raises(kvc.KvcError) as e:
         kvc.kvc_compact(tiles, 0, None, 10, rows)                # rows destination
     assert e.value.status == kvc.KVC_EINVAL
+
+
+@pytest.mark.parametrize("rank", [16, 32])
+def test_dkv_scores_rows_equal_tiles(rank):
+    """VASE-DKV scores and the fused range from a rows cache equal the tiled
+    form's bit for bit (the same sketch, Gram and leverage arithmetic)."""
+    say("dkv rows", rank)
+    nb, hkv, T = 2, 4, 2500
+    tiles = make_cache(1, nb, hkv, T, seed=31)
+    rows = rows_twin(tiles)
+    g = kvc_synth.queries((rank, 256), dtype=torch.bfloat16, device=DEV, seed=5)
+    out = []
+    for c in (tiles, rows):
+        sc = torch.full((nb, hkv, T), float("nan"), device=DEV)
+        rg = torch.full((nb, hkv, T), float("nan"), device=DEV)
+        kvc.kvc_dkv_score(c, 0, g, sc, rg, ws_tensor(kvc.kvc_dkv_ws_bytes(c, rank)))
+        out.append((sc, rg))
+    torch.cuda.synchronize()
+    assert torch.equal(out[0][0], out[1][0]) and torch.equal(out[0][1], out[1][1])
