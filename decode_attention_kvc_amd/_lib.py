@@ -144,6 +144,36 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _arg(t, name, dtype, elems, n=1, stride=0):
+    """Check a device-memory argument before its pointer crosses the ABI (the
+    C side sees only the pointer): element type, an extent of `elems`
+    elements (packed, stride 0: t contiguous with at least that many), or
+    `n` blocks of `elems` elements `stride` elements apart inside t's
+    storage, and a device tensor.  Returns the pointer (None for None)."""
+    if t is None:
+        return None
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if stride == 0:
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: must be contiguous")
+        if t.numel() < n * elems:
+            raise ValueError(f"{name}: {t.numel()} elements, the call uses {n * elems}")
+    else:
+        span = (n - 1) * stride + elems
+        if (t.storage_offset() + span) * t.element_size() > t.untyped_storage().nbytes():
+            raise ValueError(f"{name}: {n} blocks of {elems} elements {stride} apart leave "
+                             f"the tensor's storage")
+    return t.data_ptr()
+
+
+def _on_device(**tensors):
+    """The device arguments of a call, checked after their types and extents."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name}: must be a device tensor")
+
+
 _HAS_GPU = None
 
 
@@ -433,8 +463,23 @@ def kvc_share_map(n_layers, leaders):
 
 def kvc_append(cache, slot, k_new, v_new, stream=None):
     c = cache.desc()
-    _check(lib().kvc_append(ctypes.byref(c), slot, _ptr(k_new), _ptr(v_new), _stream(stream)),
-           "kvc_append")
+    row = cache.nb * cache.n_kv_heads * HEAD_DIM
+    pk, pv = _arg(k_new, "k_new", cache.dtype, row), _arg(v_new, "v_new", cache.dtype, row)
+    _on_device(k_new=k_new, v_new=v_new)
+    _check(lib().kvc_append(ctypes.byref(c), slot, pk, pv, _stream(stream)), "kvc_append")
+
+
+def _attn_args(cache, q, out, lse, k_new, v_new, append_slot, nq, hq, qs, os_, ls):
+    """Pointers of a decode-attention call's device arguments, checked."""
+    per = cache.nb * hq * HEAD_DIM
+    row = cache.nb * cache.n_kv_heads * HEAD_DIM
+    app = append_slot >= 0
+    ptrs = (_arg(q, "q", cache.dtype, per, nq, qs), _arg(out, "out", torch.float32, per, nq, os_),
+            _arg(lse, "lse", torch.float32, cache.nb * hq, nq, ls),
+            _arg(k_new if app else None, "k_new", cache.dtype, row),
+            _arg(v_new if app else None, "v_new", cache.dtype, row))
+    _on_device(q=q, out=out, lse=lse, k_new=k_new if app else None, v_new=v_new if app else None)
+    return ptrs
 
 
 def kvc_decode_attn_ws_bytes(cache, n_q_layers, n_q_heads):
@@ -454,10 +499,13 @@ def kvc_decode_attn(cache, q, q_slot, out, lse=None, ws=None, scale=0.0, k_new=N
     hq = q.shape[-2] if n_q_heads is None else n_q_heads
     slots = (ctypes.c_int32 * max(1, nq))(*[int(s) for s in q_slot])
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().kvc_decode_attn(ctypes.byref(c), _ptr(q), q_layer_stride, nq, slots, hq,
-                                 float(scale), _ptr(k_new), _ptr(v_new), append_slot, _ptr(out),
-                                 out_layer_stride, _ptr(lse), lse_layer_stride, _ptr(ws),
-                                 ws_bytes, _stream(stream)), "kvc_decode_attn")
+    pq, po, pl, pk, pv = _attn_args(cache, q, out, lse, k_new, v_new, append_slot, nq, hq,
+                                    q_layer_stride, out_layer_stride, lse_layer_stride)
+    _on_device(ws=ws)
+    _check(lib().kvc_decode_attn(ctypes.byref(c), pq, q_layer_stride, nq, slots, hq,
+                                 float(scale), pk, pv, append_slot, po, out_layer_stride, pl,
+                                 lse_layer_stride, _arg(ws, "ws", None, 0), ws_bytes,
+                                 _stream(stream)), "kvc_decode_attn")
 
 
 def kvc_decode_attn_noalloc(cache, q, q_slot, out, lse=None, scale=0.0, k_new=None,
@@ -469,17 +517,21 @@ def kvc_decode_attn_noalloc(cache, q, q_slot, out, lse=None, scale=0.0, k_new=No
     nq = len(q_slot) if n_q_layers is None else n_q_layers
     hq = q.shape[-2] if n_q_heads is None else n_q_heads
     slots = (ctypes.c_int32 * max(1, nq))(*[int(s) for s in q_slot])
-    _check(lib().kvc_decode_attn_noalloc(ctypes.byref(c), _ptr(q), q_layer_stride, nq, slots, hq,
-                                         float(scale), _ptr(k_new), _ptr(v_new), append_slot,
-                                         _ptr(out), out_layer_stride, _ptr(lse),
-                                         lse_layer_stride, _stream(stream)),
+    pq, po, pl, pk, pv = _attn_args(cache, q, out, lse, k_new, v_new, append_slot, nq, hq,
+                                    q_layer_stride, out_layer_stride, lse_layer_stride)
+    _check(lib().kvc_decode_attn_noalloc(ctypes.byref(c), pq, q_layer_stride, nq, slots, hq,
+                                         float(scale), pk, pv, append_slot, po,
+                                         out_layer_stride, pl, lse_layer_stride,
+                                         _stream(stream)),
            "kvc_decode_attn_noalloc")
 
 
 def kvc_value_range(cache, slot, rng, stream=None):
     c = cache.desc()
-    _check(lib().kvc_value_range(ctypes.byref(c), slot, _ptr(rng), _stream(stream)),
-           "kvc_value_range")
+    per_row = cache.nb * cache.n_kv_heads * int(cache.t_len)
+    pr = _arg(rng, "range", torch.float32, per_row)
+    _on_device(range=rng)
+    _check(lib().kvc_value_range(ctypes.byref(c), slot, pr, _stream(stream)), "kvc_value_range")
 
 
 def kvc_score_ws_bytes(cache, n_q_heads, w):
@@ -496,9 +548,17 @@ def kvc_score(cache, slot, q_obs, score, rng=None, lse_obs=None, ws=None, scale=
     c = cache.desc()
     w, hq = q_obs.shape[0], q_obs.shape[2]
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().kvc_score(ctypes.byref(c), slot, _ptr(q_obs), hq, w, float(scale),
-                           _ptr(lse_obs), _ptr(score), _ptr(rng), _ptr(ws), ws_bytes,
-                           _stream(stream)), "kvc_score")
+    nb = cache.nb
+    per_row = nb * cache.n_kv_heads * int(cache.t_len)
+    if q_obs.dim() != 4 or q_obs.shape[1] != nb or q_obs.shape[3] != HEAD_DIM:
+        raise ValueError(f"q_obs: shape {tuple(q_obs.shape)}, expected [w][{nb}][Hq][128]")
+    pq = _arg(q_obs, "q_obs", cache.dtype, w * nb * hq * HEAD_DIM)
+    pl = _arg(lse_obs, "lse_obs", torch.float32, w * nb * hq)
+    ps = _arg(score, "score", torch.float32, per_row)
+    pr = _arg(rng, "range", torch.float32, per_row)
+    _on_device(q_obs=q_obs, lse_obs=lse_obs, score=score, range=rng, ws=ws)
+    _check(lib().kvc_score(ctypes.byref(c), slot, pq, hq, w, float(scale), pl, ps, pr,
+                           _arg(ws, "ws", None, 0), ws_bytes, _stream(stream)), "kvc_score")
 
 
 def kvc_select_ws_bytes(nb, n_kv_heads, t_len):
@@ -508,11 +568,22 @@ def kvc_select_ws_bytes(nb, n_kv_heads, t_len):
     return out.value
 
 
+def _select_args(score, rng, kept, nb, n_kv_heads, t_len, budget_k, recent_b):
+    per_row = nb * n_kv_heads * t_len
+    n_keep = nb * n_kv_heads * min(t_len, budget_k + recent_b)
+    ptrs = (_arg(score, "score", torch.float32, per_row),
+            _arg(rng, "range", torch.float32, per_row),
+            _arg(kept, "kept", torch.int32, n_keep))
+    _on_device(score=score, range=rng, kept=kept)
+    return ptrs
+
+
 def kvc_select(score, rng, nb, n_kv_heads, t_len, budget_k, recent_b, n_v, seed, layer_id,
                kept, ws=None, stream=None):
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().kvc_select(_ptr(score), _ptr(rng), nb, n_kv_heads, t_len, budget_k, recent_b,
-                            n_v, int(seed) & (2**64 - 1), layer_id, _ptr(kept), _ptr(ws),
+    ps, pr, pk = _select_args(score, rng, kept, nb, n_kv_heads, t_len, budget_k, recent_b)
+    _check(lib().kvc_select(ps, pr, nb, n_kv_heads, t_len, budget_k, recent_b,
+                            n_v, int(seed) & (2**64 - 1), layer_id, pk, _arg(ws, "ws", None, 0),
                             ws_bytes, _stream(stream)), "kvc_select")
 
 
@@ -520,16 +591,21 @@ def kvc_select_seq(score, rng, nb, n_kv_heads, t_len, seq_len, seq_id, budget_k,
                    seed, layer_id, kept, ws=None, stream=None):
     """seq_len, seq_id: device int32 [nb] or None."""
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().kvc_select_seq(_ptr(score), _ptr(rng), nb, n_kv_heads, t_len, _ptr(seq_len),
-                                _ptr(seq_id), budget_k, recent_b, n_v, int(seed) & (2**64 - 1),
-                                layer_id, _ptr(kept), _ptr(ws), ws_bytes, _stream(stream)),
+    ps, pr, pk = _select_args(score, rng, kept, nb, n_kv_heads, t_len, budget_k, recent_b)
+    _check(lib().kvc_select_seq(ps, pr, nb, n_kv_heads, t_len,
+                                _arg(seq_len, "seq_len", torch.int32, nb),
+                                _arg(seq_id, "seq_id", torch.int32, nb), budget_k, recent_b, n_v,
+                                int(seed) & (2**64 - 1), layer_id, pk, _arg(ws, "ws", None, 0),
+                                ws_bytes, _stream(stream)),
            "kvc_select_seq")
 
 
 def kvc_compact(src, slot, kept, n_keep, dst, stream=None):
     """kept: device int32 [nb][hkv][n_keep], or None for rows [0, n_keep)."""
     cs, cd = src.desc(), dst.desc()
-    _check(lib().kvc_compact(ctypes.byref(cs), slot, _ptr(kept), n_keep, ctypes.byref(cd),
+    pk = _arg(kept, "kept", torch.int32, src.nb * src.n_kv_heads * n_keep)
+    _on_device(kept=kept)
+    _check(lib().kvc_compact(ctypes.byref(cs), slot, pk, n_keep, ctypes.byref(cd),
                              _stream(stream)), "kvc_compact")
 
 
@@ -549,8 +625,14 @@ def kvc_dkv_score(cache, slot, g, score, rng=None, ws=None, stream=None):
     """g: bf16 [rank][2*head_dim] (row n = sketch column n)."""
     c = cache.desc()
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().kvc_dkv_score(ctypes.byref(c), slot, _ptr(g), g.shape[0], _ptr(score), _ptr(rng),
-                               _ptr(ws), ws_bytes, _stream(stream)), "kvc_dkv_score")
+    per_row = cache.nb * cache.n_kv_heads * int(cache.t_len)
+    _on_device(g=g, score=score, range=rng, ws=ws)
+    _check(lib().kvc_dkv_score(ctypes.byref(c), slot,
+                               _arg(g, "g", torch.bfloat16, g.shape[0] * 2 * HEAD_DIM),
+                               g.shape[0], _arg(score, "score", torch.float32, per_row),
+                               _arg(rng, "range", torch.float32, per_row),
+                               _arg(ws, "ws", None, 0), ws_bytes, _stream(stream)),
+           "kvc_dkv_score")
 
 
 def kvc_gaussian_bf16(n, seed, c1, c2, out, stream=None):
@@ -589,9 +671,17 @@ def kvc_q8_decode_attn(cache, q, q_slot, out, lse, ws, n_q_heads=None, scale=0.0
     hq = n_q_heads if n_q_heads is not None else q.shape[-2]
     slots = (ctypes.c_int32 * max(1, nq))(*[int(x) for x in q_slot])
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().kvc_q8_decode_attn(ctypes.byref(c), _ptr(q), q_layer_stride, nq, slots, hq,
-                                    float(scale), _ptr(out), out_layer_stride, _ptr(lse),
-                                    lse_layer_stride, _ptr(ws), ws_bytes, _stream(stream)),
+    per = cache.nb * hq * HEAD_DIM
+    _on_device(q=q, out=out, lse=lse, ws=ws)
+    _check(lib().kvc_q8_decode_attn(ctypes.byref(c),
+                                    _arg(q, "q", torch.bfloat16, per, nq, q_layer_stride),
+                                    q_layer_stride, nq, slots, hq, float(scale),
+                                    _arg(out, "out", torch.float32, per, nq, out_layer_stride),
+                                    out_layer_stride,
+                                    _arg(lse, "lse", torch.float32, cache.nb * hq, nq,
+                                         lse_layer_stride),
+                                    lse_layer_stride, _arg(ws, "ws", None, 0), ws_bytes,
+                                    _stream(stream)),
            "kvc_q8_decode_attn")
 
 
@@ -630,7 +720,16 @@ def kvc_xkv_decode_attn(store, layer, q, out, lse=None, n_select=256, scale=0.0,
     x = store.desc()
     hq = q.shape[-2] if n_q_heads is None else n_q_heads
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().kvc_xkv_decode_attn(ctypes.byref(x), layer, _ptr(q), hq, float(scale), n_select,
-                                     _ptr(o_in), _ptr(lse_in), _ptr(out), _ptr(lse),
-                                     _ptr(selected), _ptr(ws), ws_bytes, _stream(stream)),
+    nb = store.nb
+    per = nb * hq * HEAD_DIM
+    n_sel = store.nb * store.n_kv_heads * n_select
+    _on_device(q=q, o_in=o_in, lse_in=lse_in, out=out, lse=lse, selected=selected, ws=ws)
+    _check(lib().kvc_xkv_decode_attn(ctypes.byref(x), layer, _arg(q, "q", torch.bfloat16, per),
+                                     hq, float(scale), n_select,
+                                     _arg(o_in, "o_in", torch.float32, per),
+                                     _arg(lse_in, "lse_in", torch.float32, nb * hq),
+                                     _arg(out, "out", torch.float32, per),
+                                     _arg(lse, "lse", torch.float32, nb * hq),
+                                     _arg(selected, "selected", torch.int32, n_sel),
+                                     _arg(ws, "ws", None, 0), ws_bytes, _stream(stream)),
            "kvc_xkv_decode_attn")

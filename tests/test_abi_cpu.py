@@ -430,3 +430,50 @@ def test_value_layout_validation():
     assert compact(src, cache(k=0x30000000, v=0x40000000), kept=None, n=0) == kvc.KVC_OK
     # the score's size and argument checks still apply to rows caches
     assert L.kvc_score_ws_bytes(ctypes.byref(r), 8, 32, ctypes.byref(out)) == kvc.KVC_OK
+
+
+def test_wrappers_check_device_arguments():
+    """The binding checks each device argument's element type, extent and
+    layout before its pointer crosses the ABI (the C side sees pointers only);
+    a host tensor is refused last."""
+    import torch
+    c = kvc.Cache.empty(1, 2, 2, 64, device="cpu", t_len=10)
+    f32 = dict(dtype=torch.float32)
+    q = torch.zeros((1, 2, 8, 128), dtype=torch.bfloat16)
+    out = torch.zeros((1, 2, 8, 128), **f32)
+    ws = torch.zeros(1 << 16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="q: dtype"):
+        kvc.kvc_decode_attn(c, q.float(), [0], out, None, ws)
+    with pytest.raises(ValueError, match="out: dtype"):
+        kvc.kvc_decode_attn(c, q, [0], out.bfloat16(), None, ws)
+    with pytest.raises(ValueError, match="out: .* elements"):
+        kvc.kvc_decode_attn(c, q, [0], out[:, :1], None, ws)
+    with pytest.raises(ValueError, match="q: must be contiguous"):
+        kvc.kvc_decode_attn(c, q.transpose(2, 3).contiguous().transpose(2, 3), [0], out, None, ws)
+    with pytest.raises(ValueError, match="lse: .* elements"):
+        kvc.kvc_decode_attn(c, q, [0], out, torch.zeros((1, 2, 7), **f32), ws)
+    with pytest.raises(ValueError, match="k_new: dtype"):
+        kvc.kvc_decode_attn(c, q, [0], out, None, ws, k_new=torch.zeros((2, 2, 128), **f32),
+                            v_new=torch.zeros((2, 2, 128), dtype=torch.bfloat16), append_slot=0)
+    with pytest.raises(ValueError, match="leave the tensor's storage"):
+        kvc.kvc_decode_attn(c, q[0:1], [0, 0], out, None, ws, q_layer_stride=2 * 8 * 128,
+                            out_layer_stride=2 * 8 * 128)
+    with pytest.raises(ValueError, match="must be a device tensor"):
+        kvc.kvc_decode_attn(c, q, [0], out, None, ws)
+    # score, range, selection and compaction
+    sc = torch.zeros((2, 2, 10), **f32)
+    with pytest.raises(ValueError, match="range: .* elements"):
+        kvc.kvc_value_range(c, 0, torch.zeros((2, 2, 5), **f32))
+    with pytest.raises(ValueError, match="q_obs: shape"):
+        kvc.kvc_score(c, 0, torch.zeros((4, 3, 8, 128), dtype=torch.bfloat16), sc)
+    with pytest.raises(ValueError, match="score: dtype"):
+        kvc.kvc_score(c, 0, torch.zeros((4, 2, 8, 128), dtype=torch.bfloat16), sc.double())
+    with pytest.raises(ValueError, match="lse_obs: .* elements"):
+        kvc.kvc_score(c, 0, torch.zeros((4, 2, 8, 128), dtype=torch.bfloat16), sc,
+                      lse_obs=torch.zeros((4, 2, 7), **f32))
+    with pytest.raises(ValueError, match="kept: dtype"):
+        kvc.kvc_select(sc, sc, 2, 2, 10, 4, 2, 1, 0, 0, torch.zeros((2, 2, 6), dtype=torch.int64))
+    with pytest.raises(ValueError, match="kept: .* elements"):
+        kvc.kvc_select(sc, sc, 2, 2, 10, 4, 2, 1, 0, 0, torch.zeros((2, 2, 5), dtype=torch.int32))
+    with pytest.raises(ValueError, match="kept: .* elements"):
+        kvc.kvc_compact(c, 0, torch.zeros((2, 2, 3), dtype=torch.int32), 4, c)
