@@ -284,6 +284,35 @@ def test_select_matches_oracle(case):
     say(f"  ties within the band: {ties}")
 
 
+@pytest.mark.parametrize("case", [
+    # (nb, hkv, T, K, B, N_v): ranges of four values only (thousands of rows
+    # tied at the N_v threshold), half of the weights zero (infinite keys:
+    # the sampling threshold itself is +inf, taken in row order)
+    (1, 2, 5000, 4000, 64, 256),
+    (2, 1, 40000, 32768, 256, 256),      # the same in the workspace path
+    (1, 1, 3000, 2000, 0, 1999),         # N_v = K - 1: one sampled row
+])
+def test_select_heavy_ties(case):
+    nb, hkv, T, K, B, Nv = case
+    say("select ties", case)
+    g = torch.Generator(device=DEV).manual_seed(T)
+    score = torch.rand((nb, hkv, T), generator=g, device=DEV)
+    score[..., 1::2] = 0.0
+    rng = torch.floor(torch.rand((nb, hkv, T), generator=g, device=DEV) * 4)
+    n_keep = min(T, K + B)
+    kept = torch.full((nb, hkv, n_keep), -7, dtype=torch.int32, device=DEV)
+    seed, layer = 77, 9
+    kvc.kvc_select(score, rng, nb, hkv, T, K, B, Nv, seed, layer, kept,
+                   ws_tensor(kvc.kvc_select_ws_bytes(nb, hkv, T)))
+    torch.cuda.synchronize()
+    sc, rg, kp = to_np(score), rng.cpu().numpy(), kept.cpu().numpy()
+    for b in range(nb):
+        for j in range(hkv):
+            d = oracle.select_detail(sc[b, j], rg[b, j], T, K, B, Nv, seed, layer, b, j)
+            assert np.array_equal(kp[b, j], d["kept"]), (b, j)
+    say("  kept sets equal")
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("pattern", ["sparse", "dense", "unordered"])
 def test_compact_bit_exact(dtype, pattern):
