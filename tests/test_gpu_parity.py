@@ -66,6 +66,8 @@ ATTN_CASES = [
     (33, 16, 4, 300, 1, [1]),                 # 132 slabs: part of the last group idle
     (16, 32, 8, 500, 4, [0, 0, 0, 0]),        # grouped, 16 rows
     (16, 32, 8, 400, 8, [1] * 8),             # 32 rows (two column blocks)
+    (256, 32, 8, 300, 1, [0]),                # 2048 slabs: one split each, no merge launch
+    (1, 64, 1, 262145, 1, [1]),               # one 256K-row slab, g = 64: the split cap
 ]
 
 
@@ -206,6 +208,7 @@ SCORE_CASES = [
     (torch.bfloat16, 2, 40, 8, 777, 16, False),      # 80 rows: an odd number of 16-row blocks
     (torch.bfloat16, 1, 64, 8, 900, 40, False),      # 320 rows: the per-head statistics pass
     (torch.bfloat16, 1, 40, 8, 40000, 32, False),    # a prompt-sized slab, 160 rows
+    (torch.bfloat16, 1, 10, 2, 262144, 32, False),   # 256K rows, g 5, statistics pass
     (torch.float32, 1, 8, 2, 1024, 32, False),
     (torch.float32, 1, 8, 2, 1024, 32, True),
 ]
@@ -250,6 +253,7 @@ SELECT_CASES = [
     (1, 2, 33280, 32768, 256, 256),      # Qwen3-14B steady pass
     (1, 1, 36864, 32768, 256, 256),      # the longest slab whose keys stay in LDS
     (1, 1, 36865, 32768, 256, 256),      # one row more: keys in the workspace
+    (1, 2, 262144, 65536, 512, 512),     # 256K rows
     (1, 1, 300, 100, 0, 0),
     (1, 1, 300, 100, 10, 100),
     (1, 2, 200, 250, 32, 16),            # keep everything
