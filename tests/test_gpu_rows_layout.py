@@ -239,3 +239,27 @@ def test_dkv_scores_rows_equal_tiles(rank):
         out.append((sc, rg))
     torch.cuda.synchronize()
     assert torch.equal(out[0][0], out[1][0]) and torch.equal(out[0][1], out[1][1])
+
+
+def test_ragged_score_and_range_rows():
+    """A batch map and per-sequence lengths on a rows cache: scores (two
+    passes: statistics from the keys) and ranges equal the tiled form's."""
+    say("ragged score rows")
+    hkv, hq, w, T = 4, 20, 16, 1500
+    tiles = make_cache(2, 4, hkv, T, seed=41)
+    rows = rows_twin(tiles)
+    idx = torch.tensor([3, 0, 2], dtype=torch.int32, device=DEV)
+    lens = torch.tensor([1500, 40, 777], dtype=torch.int32, device=DEV)
+    q_obs = kvc_synth.queries((w, 3, hq, 128), device=DEV, seed=42)
+    out = []
+    for c in (tiles, rows):
+        v = c.seqs(idx, lens, t_len=T)
+        sc = torch.full((3, hkv, T), float("nan"), device=DEV)
+        rg = torch.full((3, hkv, T), float("nan"), device=DEV)
+        kvc.kvc_score(v, 1, q_obs, sc, rg, None, ws_tensor(kvc.kvc_score_ws_bytes(v, hq, w)))
+        out.append((sc, rg))
+    torch.cuda.synchronize()
+    for b, L in enumerate([1500, 40, 777]):
+        assert torch.equal(out[0][0][b, :, :L], out[1][0][b, :, :L])
+        assert torch.equal(out[0][1][b, :, :L], out[1][1][b, :, :L])
+        assert bool(torch.isnan(out[1][1][b, :, L:]).all())     # rows past the length untouched
