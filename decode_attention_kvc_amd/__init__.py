@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     NOALLOC_SCRATCH_BYTES, lib, strerror,
     kvc_version, kvc_strerror, kvc_share_map, kvc_append, kvc_decode_attn_ws_bytes,
     kvc_decode_attn, kvc_decode_attn_noalloc, kvc_value_range, kvc_score_ws_bytes, kvc_score,
+    kvc_score_seq,
     kvc_select_ws_bytes,
     kvc_select, kvc_select_seq, kvc_compact, kvc_philox_words, kvc_dkv_ws_bytes, kvc_dkv_score,
     kvc_gaussian_bf16, QCache, kvc_q8_quantize, kvc_q8_append, kvc_q8_decode_attn_ws_bytes,

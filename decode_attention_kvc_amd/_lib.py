@@ -29,7 +29,8 @@ V_TILE = 32
 EXPORTS = (
     "kvc_version", "kvc_strerror", "kvc_share_map", "kvc_append",
     "kvc_decode_attn_ws_bytes", "kvc_decode_attn", "kvc_decode_attn_noalloc", "kvc_value_range",
-    "kvc_score_ws_bytes", "kvc_score", "kvc_select_ws_bytes", "kvc_select", "kvc_select_seq",
+    "kvc_score_ws_bytes", "kvc_score", "kvc_score_seq", "kvc_select_ws_bytes", "kvc_select",
+    "kvc_select_seq",
     "kvc_compact", "kvc_philox_words", "kvc_dkv_ws_bytes", "kvc_dkv_score",
     "kvc_gaussian_bf16", "kvc_q8_quantize", "kvc_q8_append", "kvc_q8_decode_attn_ws_bytes",
     "kvc_q8_decode_attn", "kvc_xkv_factor_ws_bytes", "kvc_xkv_factor", "kvc_xkv_decode_ws_bytes",
@@ -100,6 +101,7 @@ def lib():
             "kvc_value_range": ([cp, i32, vp, vp], i32),
             "kvc_score_ws_bytes": ([cp, i32, i32, szp], i32),
             "kvc_score": ([cp, i32, vp, i32, i32, f32, vp, vp, vp, vp, sz, vp], i32),
+            "kvc_score_seq": ([cp, i32, vp, i32, vp, i32, i32, f32, vp, vp, vp, vp, sz, vp], i32),
             "kvc_select_ws_bytes": ([i32, i32, i32, szp], i32),
             "kvc_select": ([vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_uint64, i32, vp, vp,
                             sz, vp], i32),
@@ -559,6 +561,28 @@ def kvc_score(cache, slot, q_obs, score, rng=None, lse_obs=None, ws=None, scale=
     _on_device(q_obs=q_obs, lse_obs=lse_obs, score=score, range=rng, ws=ws)
     _check(lib().kvc_score(ctypes.byref(c), slot, pq, hq, w, float(scale), pl, ps, pr,
                            _arg(ws, "ws", None, 0), ws_bytes, _stream(stream)), "kvc_score")
+
+
+def kvc_score_seq(cache, slot, q_obs, q_idx, score, rng=None, lse_obs=None, ws=None, scale=0.0,
+                  stream=None):
+    """q_obs: [w][q_nb][Hq][d] (the whole batch's window queries); q_idx:
+    device int32 [cache.nb], the q_obs row of each sequence the cache view
+    addresses, or None (row b)."""
+    c = cache.desc()
+    if q_obs.dim() != 4 or q_obs.shape[3] != HEAD_DIM:
+        raise ValueError(f"q_obs: shape {tuple(q_obs.shape)}, expected [w][q_nb][Hq][128]")
+    w, q_nb, hq = q_obs.shape[0], q_obs.shape[1], q_obs.shape[2]
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    per_row = cache.nb * cache.n_kv_heads * int(cache.t_len)
+    pq = _arg(q_obs, "q_obs", cache.dtype, w * q_nb * hq * HEAD_DIM)
+    pi = _arg(q_idx, "q_idx", torch.int32, cache.nb)
+    pl = _arg(lse_obs, "lse_obs", torch.float32, w * q_nb * hq)
+    ps = _arg(score, "score", torch.float32, per_row)
+    pr = _arg(rng, "range", torch.float32, per_row)
+    _on_device(q_obs=q_obs, q_idx=q_idx, lse_obs=lse_obs, score=score, range=rng, ws=ws)
+    _check(lib().kvc_score_seq(ctypes.byref(c), slot, pq, q_nb, pi, hq, w, float(scale), pl, ps,
+                               pr, _arg(ws, "ws", None, 0), ws_bytes, _stream(stream)),
+           "kvc_score_seq")
 
 
 def kvc_select_ws_bytes(nb, n_kv_heads, t_len):

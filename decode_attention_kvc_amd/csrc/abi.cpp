@@ -545,6 +545,13 @@ int kvc_score_ws_bytes(const kvc_cache* c, int n_q_heads, int w, size_t* bytes) 
 int kvc_score(const kvc_cache* c, int slot, const void* q_obs, int n_q_heads, int w, float scale,
               const float* lse_obs, float* score, float* range, void* ws, size_t ws_bytes,
               kvc_stream_t stream) {
+    return kvc_score_seq(c, slot, q_obs, c ? c->nb : 0, nullptr, n_q_heads, w, scale, lse_obs,
+                         score, range, ws, ws_bytes, stream);
+}
+
+int kvc_score_seq(const kvc_cache* c, int slot, const void* q_obs, int q_nb, const int32_t* q_idx,
+                  int n_q_heads, int w, float scale, const float* lse_obs, float* score,
+                  float* range, void* ws, size_t ws_bytes, kvc_stream_t stream) {
     int st = check_cache(c);
     if (st) return st;
     if (slot < 0 || slot >= c->n_slots) return KVC_EINVAL;
@@ -553,9 +560,11 @@ int kvc_score(const kvc_cache* c, int slot, const void* q_obs, int n_q_heads, in
     const int rows = g * w;
     if (rows > (c->dtype == KVC_F32 ? 128 : 512)) return KVC_EINVAL;
     if (!isfinite(scale) || scale < 0.f) return KVC_EINVAL;
+    if (q_nb < 0 || (!q_idx && q_nb < c->nb)) return KVC_EINVAL;
     if (c->nb == 0) return KVC_OK;
     if (w > c->t_len) return KVC_EINVAL;
     if (!aligned16(q_obs) || !aligned4(score)) return KVC_EALIGN;
+    if (q_idx && !aligned4(q_idx)) return KVC_EALIGN;
     if ((lse_obs && !aligned4(lse_obs)) || (range && !aligned4(range))) return KVC_EALIGN;
     const int slabs = c->nb * c->n_kv_heads;
     const ScoreWs lay = score_ws_layout(c->dtype, rows, c->t_len, slabs);
@@ -576,6 +585,8 @@ int kvc_score(const kvc_cache* c, int slot, const void* q_obs, int n_q_heads, in
     p.rows = rows;
     p.q_obs = q_obs;
     p.lse_obs = lse_obs;
+    p.q_idx = q_idx;
+    p.q_nb = q_nb;
     p.scale = scale;
     p.score = score;
     // Values stored as rows: the score pass reads the keys only and the

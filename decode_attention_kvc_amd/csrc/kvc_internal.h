@@ -68,6 +68,11 @@ __device__ __forceinline__ int seq_rows(const SeqMap& m, int b, int phys) {
     return min(max(m.len[b], 0), m.t_len);
 }
 
+// Batch row of q_obs / lse_obs that sequence b of a score launch reads.
+__device__ __forceinline__ int score_qrow(const int32_t* q_idx, int b) {
+    return q_idx ? q_idx[b] : b;
+}
+
 // One attention launch: a set of q-layers that all read one cache slot.
 struct AttnLaunch {
     const void* k;          // slot base of K: [nb][hkv][t_cap][D]
@@ -100,8 +105,10 @@ struct ScoreLaunch {
     int nb, hkv, g, hq, w;
     int t_len, t_cap;
     int rows;               // g * w
-    const void* q_obs;      // [w][nb][hq][D]
-    const float* lse_obs;   // [w][nb][hq] or null (then `lse_ws` is used)
+    const void* q_obs;      // [w][q_nb][hq][D]
+    const float* lse_obs;   // [w][q_nb][hq] or null (then `lse_ws` is used)
+    const int32_t* q_idx;   // [nb]: q_obs / lse_obs batch row of each sequence, or null (b)
+    int q_nb;               // batch rows of q_obs / lse_obs
     float scale;
     float* score;           // [nb][hkv][t_len]
     float* range;           // [nb][hkv][t_len] or null

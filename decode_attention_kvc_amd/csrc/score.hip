@@ -116,7 +116,8 @@ __device__ __forceinline__ void load_qfrag(QFrag& Q, const ScoreLaunch& p, int b
         if (R < p.rows) {
             const int h = j * p.g + R / p.w, iw = R % p.w;
             const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q_obs) +
-                                 (((size_t)iw * p.nb + b) * p.hq + h) * D + 8 * lg;
+                                 (((size_t)iw * p.q_nb + score_qrow(p.q_idx, b)) * p.hq + h) * D +
+                                 8 * lg;
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc) Q.a[mt][kc] = as_bf(load16(qp + 32 * kc));
         } else {
@@ -299,12 +300,13 @@ __global__ __launch_bounds__(256) void score_stats_tiles_bf16(ScoreLaunch p) {
     uint16_t* qs = reinterpret_cast<uint16_t*>(smem);                          // [MT*16][QPITCH]
 
     const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q_obs);
+    const int qb = score_qrow(p.q_idx, b);
     for (int x = tid; x < MT * 16 * (D / 8); x += blockDim.x) {
         const int R = x / (D / 8), c = x % (D / 8);
         u32x4 v = u32x4{0u, 0u, 0u, 0u};
         if (R < p.rows) {
             const int h = j * p.g + R / p.w, iw = R % p.w;
-            v = load16(q + (((size_t)iw * p.nb + b) * p.hq + h) * D + 8 * c);
+            v = load16(q + (((size_t)iw * p.q_nb + qb) * p.hq + h) * D + 8 * c);
         }
         *reinterpret_cast<u32x4*>(qs + R * SCORE_QPITCH + 8 * c) = v;
     }
@@ -498,19 +500,20 @@ __global__ __launch_bounds__(256) void score_main_bf16(ScoreLaunch p) {
     int* lims = reinterpret_cast<int*>(l2s + MT * 16);                          // [MT*16]
 
     const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q_obs);
+    const int qb = score_qrow(p.q_idx, b);
     for (int x = tid; x < MT * 16 * (D / 8); x += blockDim.x) {
         const int R = x / (D / 8), c = x % (D / 8);
         u32x4 v = u32x4{0u, 0u, 0u, 0u};
         if (R < p.rows) {
             const int h = j * p.g + R / p.w, iw = R % p.w;
-            v = load16(q + (((size_t)iw * p.nb + b) * p.hq + h) * D + 8 * c);
+            v = load16(q + (((size_t)iw * p.q_nb + qb) * p.hq + h) * D + 8 * c);
         }
         *reinterpret_cast<u32x4*>(qs + R * QPITCH + 8 * c) = v;
     }
     for (int R = tid; R < MT * 16; R += blockDim.x) {
         if (R < p.rows) {
             const int h = j * p.g + R / p.w, iw = R % p.w;
-            const float l = p.lse_obs ? p.lse_obs[((size_t)iw * p.nb + b) * p.hq + h]
+            const float l = p.lse_obs ? p.lse_obs[((size_t)iw * p.q_nb + qb) * p.hq + h]
                                       : p.lse_ws[(size_t)slab * p.rows_pad + R];
             l2s[R] = EXP_BIAS - l * LOG2E;
             lims[R] = T - p.w + iw;
@@ -609,6 +612,7 @@ __device__ float f32_dot_row(const float* q, const float (*ks)[D + 1], int t) {
 __global__ __launch_bounds__(256) void score_f32(ScoreLaunch p, int stats_pass) {
     const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int slab = b * p.hkv + j;
+    const int qb = score_qrow(p.q_idx, b);
     const int tid = threadIdx.x, tl = tid % FT, rg = tid / FT;
     const int phys = seq_phys(p.sm, b);
     const int T = seq_rows(p.sm, b, phys);
@@ -642,7 +646,7 @@ __global__ __launch_bounds__(256) void score_f32(ScoreLaunch p, int stats_pass) 
             if (R >= p.rows) continue;
             const int h = j * p.g + R / p.w, iw = R % p.w;
             const float* q = reinterpret_cast<const float*>(p.q_obs) +
-                             (((size_t)iw * p.nb + b) * p.hq + h) * D;
+                             (((size_t)iw * p.q_nb + qb) * p.hq + h) * D;
             const float x = f32_dot_row(q, ks, tl) * p.scale;
             const bool vis = t <= T - p.w + iw;
             if (stats_pass) {
@@ -652,7 +656,7 @@ __global__ __launch_bounds__(256) void score_f32(ScoreLaunch p, int stats_pass) 
                     m[k] = mn;
                 }
             } else if (vis) {
-                const float l = p.lse_obs ? p.lse_obs[((size_t)iw * p.nb + b) * p.hq + h]
+                const float l = p.lse_obs ? p.lse_obs[((size_t)iw * p.q_nb + qb) * p.hq + h]
                                           : p.lse_ws[(size_t)slab * p.rows_pad + R];
                 c += expf(x - l);
             }

@@ -295,9 +295,9 @@ class RaggedDecoder:
     row per step, the whole schedule (lengths, due sets, entries) is host
     bookkeeping fixed by the prompt lengths; it is planned here once and its
     per-step device arrays are uploaded once, so a step only launches
-    kernels.  A pass's calls address the whole batch, the sequences that
-    are not due as empty ones, so its window queries are the pools' own
-    [w][nb][Hq][d] slices.
+    kernels.  A pass's calls address the due sequences; their window
+    queries and log-normalisers are read from the pools' own [w][nb] slices
+    through the due sequences' indices (kvc_score_seq).
     """
 
     def __init__(self, n_layers, leaders, cache, n_q_heads, t0, n_steps, evict=None,
@@ -335,20 +335,15 @@ class RaggedDecoder:
         # per-step entries and lengths, one upload
         self.att_idx = torch.tensor(plan["att_idx"], dtype=torch.int32, device=dev)
         self.att_len = torch.tensor(plan["att_len"], dtype=torch.int32, device=dev)
-        # A pass addresses every sequence of the batch: the due ones through
-        # their source / destination entries and lengths, the others
-        # through an entry past the cache's (an empty sequence: the kernels
-        # read and write none of its rows).  So the window queries and
-        # log-normalisers are the pools' plain [w][nb] slices, and no
-        # gather runs between the steps' library calls.
+        # A pass addresses the due sequences only (their entries and
+        # lengths); their window queries and log-normalisers stay in the
+        # pools' [w][nb] slices, which kvc_score_seq reads through the due
+        # sequences' indices: no gather runs between the library calls.
         self.passes = {}
-        off = cache.nb_cap
         for s, p in plan["passes"].items():
-            src, dst, lens = [off] * nb, [off] * nb, [0] * nb
-            for b, e_src, e_dst, t in zip(p["seqs"], p["src"], p["dst"], p["lens"]):
-                src[b], dst[b], lens[b] = e_src, e_dst, t
-            arr = torch.tensor([src, dst, lens], dtype=torch.int32, device=dev)
-            self.passes[s] = dict(p, src_d=arr[0], dst_d=arr[1], lens_d=arr[2])
+            arr = torch.tensor([p["seqs"], p["src"], p["dst"], p["lens"]], dtype=torch.int32,
+                               device=dev)
+            self.passes[s] = dict(p, seqs_d=arr[0], src_d=arr[1], dst_d=arr[2], lens_d=arr[3])
         self.prompt_len = torch.tensor(self.t0, dtype=torch.int32, device=dev)
         self.seq_ids = torch.arange(nb, dtype=torch.int32, device=dev)
         nql = 1 if mode != "grouped" else max(len(g) for g in self.groups)
@@ -406,7 +401,7 @@ class RaggedDecoder:
             windows.append((q_obs, lse))
         src = self.cache.seqs(p["src_d"], p["lens_d"], t_len=p["t_len"])
         dst = self.cache.seqs(p["dst_d"], None, t_len=self.ev["K"] + self.ev["B"])
-        self._pass(src, dst, windows, self.seq_ids, p["round"])
+        self._pass(src, dst, windows, p["seqs_d"], p["round"])
         if ev1 is not None:
             self.pass_events.append((ev1, self._event(), s, len(p["seqs"])))
         return True
@@ -454,7 +449,8 @@ class RaggedDecoder:
         kept = b["kept"][: n * hkv * n_keep]
         for slot, leader in enumerate(self.leaders):
             q_obs, lse = windows[slot]
-            K.kvc_score(src, slot, q_obs, score, rng, lse, None if lse is not None else b["score_ws"])
+            K.kvc_score_seq(src, slot, q_obs, seq_ids, score, rng, lse,
+                            None if lse is not None else b["score_ws"])
             K.kvc_select_seq(score, rng, n, hkv, T, src.seq_len, seq_ids, e["K"], e["B"], e["N_v"],
                              e["seed"] + r, leader, kept, b["sel_ws"])
             K.kvc_compact(src, slot, kept, n_keep, dst)

@@ -311,6 +311,23 @@ int kvc_score(const kvc_cache* c, int slot, const void* q_obs, int n_q_heads,
               int w, float scale, const float* lse_obs, float* score,
               float* range, void* ws, size_t ws_bytes, kvc_stream_t stream);
 
+/*
+ * kvc_score for a pass over some of a batch's sequences (the due ones of a
+ * ragged schedule) whose window queries sit in the whole batch's arrays:
+ * call sequence b reads q_obs[i][q_idx[b]][h] and lse_obs[i][q_idx[b]][h].
+ *   q_obs:   device [w][q_nb][n_q_heads][head_dim]; lse_obs [w][q_nb][n_q_heads]
+ *            or NULL.
+ *   q_idx:   device int32 [c->nb], entries in [0, q_nb) (read on the
+ *            device, not checked), or NULL: sequence b reads row b (then
+ *            q_nb >= c->nb).
+ * Everything else is kvc_score's (which is this call with q_nb = c->nb and
+ * q_idx = NULL).
+ */
+int kvc_score_seq(const kvc_cache* c, int slot, const void* q_obs, int q_nb,
+                  const int32_t* q_idx, int n_q_heads, int w, float scale,
+                  const float* lse_obs, float* score, float* range, void* ws,
+                  size_t ws_bytes, kvc_stream_t stream);
+
 /* Workspace bytes kvc_select needs for nb * n_kv_heads slabs of t_len rows
  * (two uint32 per row: the sampling key of every candidate row, and the
  * selection keys of slabs too long for LDS). */

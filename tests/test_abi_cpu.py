@@ -477,3 +477,17 @@ def test_wrappers_check_device_arguments():
         kvc.kvc_select(sc, sc, 2, 2, 10, 4, 2, 1, 0, 0, torch.zeros((2, 2, 5), dtype=torch.int32))
     with pytest.raises(ValueError, match="kept: .* elements"):
         kvc.kvc_compact(c, 0, torch.zeros((2, 2, 3), dtype=torch.int32), 4, c)
+
+
+def test_score_seq_validation():
+    c = cache(nb=3)
+    q = FAKE
+    sc = FAKE2
+    L_ = L
+    # without an index map the query batch must cover the sequences
+    assert L_.kvc_score_seq(ctypes.byref(c), 0, q, 2, None, 8, 32, 0.0, FAKE, sc, None, None, 0,
+                            None) == kvc.KVC_EINVAL
+    assert L_.kvc_score_seq(ctypes.byref(c), 0, q, -1, FAKE, 8, 32, 0.0, FAKE, sc, None, None, 0,
+                            None) == kvc.KVC_EINVAL
+    assert L_.kvc_score_seq(ctypes.byref(c), 0, q, 5, FAKE + 2, 8, 32, 0.0, FAKE, sc, None, None,
+                            0, None) == kvc.KVC_EALIGN

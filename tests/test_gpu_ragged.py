@@ -310,3 +310,34 @@ def test_uniform_view_equals_plain_cache():
     torch.cuda.synchronize()
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("use_lse", [False, True])
+def test_score_seq_reads_queries_through_the_index(use_lse):
+    """kvc_score_seq over a subset of a batch's sequences, reading their
+    window queries (and log-normalisers) through q_idx from the whole batch's
+    arrays, equals kvc_score on the same queries gathered beforehand, bit for
+    bit."""
+    say("score_seq", use_lse)
+    hkv, hq, w, T = 4, 16, 8, 900
+    cache, view, K, V = ragged_setup(2, 6, hkv, T, [4, 1, 3], [900, 300, 650], seed=31)
+    nb_all = 5
+    q_all = kvc_synth.queries((w, nb_all, hq, 128), device=DEV, seed=32)
+    lse_all = (torch.rand((w, nb_all, hq), device=DEV) * 3 + 5) if use_lse else None
+    q_idx = torch.tensor([2, 0, 4], dtype=torch.int32, device=DEV)
+    outs = []
+    for mode in ("seq", "gathered"):
+        sc = torch.full((3, hkv, T), float("nan"), device=DEV)
+        rg = torch.full((3, hkv, T), float("nan"), device=DEV)
+        ws = None if use_lse else ws_tensor(kvc.kvc_score_ws_bytes(view, hq, w))
+        if mode == "seq":
+            kvc.kvc_score_seq(view, 1, q_all, q_idx, sc, rg, lse_all, ws)
+        else:
+            li = q_idx.long()
+            kvc.kvc_score(view, 1, q_all[:, li].contiguous(), sc, rg,
+                          lse_all[:, li].contiguous() if use_lse else None, ws)
+        outs.append((sc, rg))
+    torch.cuda.synchronize()
+    for b, L in enumerate([900, 300, 650]):
+        assert torch.equal(outs[0][0][b, :, :L], outs[1][0][b, :, :L])
+        assert torch.equal(outs[0][1][b, :, :L], outs[1][1][b, :, :L])
