@@ -391,9 +391,11 @@ class QCache:
 @dataclass
 class XkvStore:
     """One window's cross-layer factorisation in libkvc's layout (see
-    include/kvc.h): token bases ak, av (bf16 [nb][hkv][t_cap][rank]), key
-    landmarks lk (bf16 [nb][hkv][t_cap/8][rank]) and the per-layer matrices,
-    stored transposed in bk, bv (float32 [nb][hkv][window*128][rank])."""
+    include/kvc.h): the key basis ak (bf16 [nb][hkv][t_cap][rank]), the value
+    basis av chunk-transposed (bf16 [nb][hkv][t_cap/8][rank][8]: the 8 rows
+    of a chunk side by side for each rank; av_rows / set_av_rows convert),
+    key landmarks lk (bf16 [nb][hkv][t_cap/8][rank]) and the per-layer
+    matrices, stored transposed in bk, bv (float32 [nb][hkv][window*128][rank])."""
     ak: torch.Tensor
     av: torch.Tensor
     lk: torch.Tensor
@@ -409,7 +411,7 @@ class XkvStore:
         t_cap = int(math.ceil(max(t_cap, 1) / T_ALIGN) * T_ALIGN)
         bf = dict(dtype=torch.bfloat16, device=device)
         ak = torch.empty((nb, n_kv_heads, t_cap, rank), **bf)
-        av = torch.empty_like(ak)
+        av = torch.empty((nb, n_kv_heads, t_cap // XkvStore.CHUNK, rank, XkvStore.CHUNK), **bf)
         lk = torch.empty((nb, n_kv_heads, t_cap // XkvStore.CHUNK, rank), **bf)
         bk = torch.empty((nb, n_kv_heads, window * HEAD_DIM, rank), dtype=torch.float32,
                          device=device)
@@ -431,6 +433,21 @@ class XkvStore:
     @property
     def rank(self):
         return self.ak.shape[3]
+
+    def av_rows(self, b=None, j=None):
+        """The value basis as rows (a copy): bf16 [nb][hkv][t_cap][rank], or
+        [t_cap][rank] for one (b, j)."""
+        if b is not None:
+            return self.av[b, j].transpose(-1, -2).reshape(self.t_cap, self.rank)
+        return self.av.transpose(-1, -2).reshape(self.nb, self.n_kv_heads, self.t_cap, self.rank)
+
+    def set_av_rows(self, b, j, rows):
+        """Rows [0, len(rows)) of the value basis of (b, j) from [n][rank]."""
+        n = rows.shape[0]
+        full = self.av[b, j].transpose(-1, -2).reshape(self.t_cap, self.rank).clone()
+        full[:n] = rows.to(full.dtype)
+        self.av[b, j].copy_(full.reshape(self.t_cap // self.CHUNK, self.CHUNK,
+                                         self.rank).transpose(-1, -2))
 
     def desc(self):
         return kvc_xkv(self.ak.data_ptr(), self.av.data_ptr(), self.lk.data_ptr(),
@@ -740,7 +757,7 @@ def kvc_xkv_decode_attn(store, layer, q, out, lse=None, n_select=256, scale=0.0,
                         lse_in=None, selected=None, n_q_heads=None, ws=None, stream=None):
     """q: bf16 [nb][Hq][d]; out float32 like q (o_in / lse_in: a second part
     to merge, e.g. attention over rows appended after the factorisation);
-    ws: kvc_xkv_decode_ws_bytes bytes of device memory."""
+    ws: kvc_xkv_decode_ws_bytes bytes of device memory (None when that is 0)."""
     x = store.desc()
     hq = q.shape[-2] if n_q_heads is None else n_q_heads
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()

@@ -288,7 +288,9 @@ DkvWs dkv_layout(int rank, int t_len, int slabs) {
 // ---- cross-layer factorisation ---------------------------------------------
 constexpr int XKV_MAXG = 8;          // query heads per KV head on the decode path
 constexpr int XKV_CHUNK = 8;
-constexpr size_t XKV_LDS_LIMIT = LDS_PER_CU - 4096;   // dynamic LDS of one decode workgroup
+// dynamic LDS of one decode workgroup (it also holds ~8.4 KB of static LDS,
+// the selection histograms)
+constexpr size_t XKV_DECODE_LDS_LIMIT = LDS_PER_CU - 12 * 1024;
 
 int check_xkv(const kvc_xkv* x) {
     if (!x) return KVC_EALIGN;
@@ -319,37 +321,25 @@ XkvWs xkv_ws(const kvc_xkv* x) {
     return w;
 }
 
-// Decode launch shape: chunk splits for the score launch and kept-row splits
-// for the attention launch, so that each launch has about XKV_TARGET_WGS
-// workgroups without splits smaller than XKV_MIN_CHUNKS chunks or
-// XKV_MIN_ROWS rows.
-constexpr int XKV_TARGET_WGS = 256;
-constexpr int XKV_MIN_CHUNKS = 128;
-constexpr int XKV_MIN_ROWS = 256;
-
+// Decode plan: one workgroup per (b, j); the chunk keys live in LDS when
+// they fit beside the rest of the work (no workspace), else in the workspace.
 struct XkvDecodePlan {
-    int nch, ksel, nscore, cps, nattend, rpw;
-    size_t keys_off, qt_off, part_off, ws_bytes, lds;
+    int nch, ksel;
+    bool gkeys;
+    size_t ws_bytes, lds;
 };
 
-XkvDecodePlan plan_xkv_decode(const kvc_xkv* x, int g, int n_select) {
+XkvDecodePlan plan_xkv_decode(const kvc_xkv* x, int n_select) {
     XkvDecodePlan pl;
-    const long long slabs = std::max<long long>(1, (long long)x->nb * x->n_kv_heads);
-    const int want = (int)std::max<long long>(1, (XKV_TARGET_WGS + slabs - 1) / slabs);
     pl.nch = (x->t_len + XKV_CHUNK - 1) / XKV_CHUNK;
     pl.ksel = std::min(n_select, pl.nch);
-    const int nrows = pl.ksel * XKV_CHUNK;
-    pl.nscore = std::max(1, std::min(want, (pl.nch + XKV_MIN_CHUNKS - 1) / XKV_MIN_CHUNKS));
-    pl.cps = std::max(1, (pl.nch + pl.nscore - 1) / pl.nscore);
-    pl.nattend = std::max(1, std::min({want, XKV_MAX_ATTEND, (nrows + XKV_MIN_ROWS - 1) / XKV_MIN_ROWS}));
-    pl.rpw = std::max(1, (nrows + pl.nattend - 1) / pl.nattend);
-    const size_t sl = (size_t)x->nb * x->n_kv_heads;
-    pl.keys_off = 0;
-    pl.qt_off = align_up(sl * pl.nch * 4, 256);
-    pl.part_off = pl.qt_off + align_up(sl * XKV_MAXG * x->rank * 4, 256);
-    pl.ws_bytes = pl.part_off + sl * pl.nattend * XKV_MAXG * (x->rank + 2) * 4;
-    // attention launch: keys, kept chunks, logits of its rows, 8 waves' value partials
-    pl.lds = ((size_t)pl.nch + pl.ksel + (size_t)pl.rpw * g + 8 * XKV_MAXG * (x->rank + 1)) * 4;
+    pl.lds = xkv_decode_lds(x->rank, pl.nch, pl.ksel, false);
+    pl.gkeys = pl.lds > XKV_DECODE_LDS_LIMIT;
+    pl.ws_bytes = 0;
+    if (pl.gkeys) {
+        pl.lds = xkv_decode_lds(x->rank, pl.nch, pl.ksel, true);
+        pl.ws_bytes = (size_t)x->nb * x->n_kv_heads * pl.nch * 4;
+    }
     return pl;
 }
 
@@ -975,7 +965,7 @@ int kvc_xkv_decode_ws_bytes(const kvc_xkv* x, int n_q_heads, int n_select, size_
     const int g = n_q_heads / x->n_kv_heads;
     if (g > XKV_MAXG) return KVC_EINVAL;
     if (n_select < 1 || (long long)n_select * XKV_CHUNK * g > 16384) return KVC_EINVAL;
-    *bytes = plan_xkv_decode(x, g, n_select).ws_bytes;
+    *bytes = plan_xkv_decode(x, n_select).ws_bytes;
     return KVC_OK;
 }
 
@@ -997,9 +987,9 @@ int kvc_xkv_decode_attn(const kvc_xkv* x, int layer, const void* q, int n_q_head
     if ((lse && !aligned4(lse)) || (o_in && (!aligned4(o_in) || !aligned4(lse_in))) ||
         (selected && !aligned4(selected)))
         return KVC_EALIGN;
-    const XkvDecodePlan pl = plan_xkv_decode(x, g, n_select);
-    if (pl.lds > XKV_LDS_LIMIT) return KVC_EINVAL;
-    if (!ws || ws_bytes < pl.ws_bytes || !aligned16(ws)) return KVC_EWORKSPACE;
+    const XkvDecodePlan pl = plan_xkv_decode(x, n_select);
+    if (pl.lds > XKV_DECODE_LDS_LIMIT) return KVC_EINVAL;
+    if (pl.ws_bytes && (!ws || ws_bytes < pl.ws_bytes || !aligned16(ws))) return KVC_EWORKSPACE;
     if (scale == 0.f) scale = 1.0f / sqrtf((float)KVC_HEAD_DIM);
     XkvDecodeLaunch p;
     memset(&p, 0, sizeof(p));
@@ -1025,14 +1015,8 @@ int kvc_xkv_decode_attn(const kvc_xkv* x, int layer, const void* q, int n_q_head
     p.out = out;
     p.lse = lse;
     p.selected = selected;
-    p.nscore = pl.nscore;
-    p.cps = pl.cps;
-    p.nattend = pl.nattend;
-    p.rpw = pl.rpw;
-    p.ws_keys = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + pl.keys_off);
-    p.ws_qt = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.qt_off);
-    p.ws_part = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.part_off);
-    if (launch_xkv_decode(p, pl.lds, (hipStream_t)stream) != hipSuccess) return KVC_EHIP;
+    p.ws_keys = pl.gkeys ? static_cast<uint32_t*>(ws) : nullptr;
+    if (launch_xkv_decode(p, pl.gkeys, pl.lds, (hipStream_t)stream) != hipSuccess) return KVC_EHIP;
     return hip_status();
 }
 

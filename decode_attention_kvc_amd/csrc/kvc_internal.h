@@ -19,7 +19,6 @@ constexpr int SCORE_QPITCH = 136;     // bf16 per window-query row staged in LDS
 constexpr int CU_COUNT = 256;         // compute units of the part
 constexpr int XCD_COUNT = 8;          // accelerator dies; workgroups are dealt to them in turn
 constexpr int LDS_PER_CU = 160 * 1024;
-constexpr int XKV_MAX_ATTEND = 16;  // kept-row splits per (b, j) of a cross-layer decode
 
 // LDS of one bf16 score-pass workgroup: the window queries (16-row blocks)
 // plus one float (lse term) and one int (last visible row) per row.
@@ -228,11 +227,7 @@ struct XkvDecodeLaunch {
     float* out;
     float* lse;             // may be null
     int32_t* selected;      // [nb][hkv][n_select] or null
-    int nscore, cps;        // chunk splits per (b, j) and chunks per split
-    int nattend, rpw;       // kept-row splits per (b, j) and rows per split
-    uint32_t* ws_keys;      // [nb][hkv][nch] chunk score keys
-    float* ws_qt;           // [nb][hkv][8][rank] q~
-    float* ws_part;         // [nb][hkv][nattend][8][rank + 2] partials (a~, max, z)
+    uint32_t* ws_keys;      // [nb][hkv][nch] chunk score keys when they do not fit in LDS
 };
 
 // Host-side launchers (defined next to their kernels).  Each returns
@@ -257,7 +252,10 @@ hipError_t launch_gaussian(int64_t n, uint32_t c1, uint32_t c2, uint32_t k0, uin
                            void* out, hipStream_t s);
 hipError_t launch_compact(const CompactLaunch& p, hipStream_t s);
 hipError_t launch_xkv_factor(const XkvLaunch& p, hipStream_t s);
-hipError_t launch_xkv_decode(const XkvDecodeLaunch& p, size_t lds, hipStream_t s);
+// The decode (one workgroup per (b, j)): dynamic LDS bytes for nch chunks
+// and ksel kept ones, with the chunk keys in LDS or (gkeys) in ws_keys.
+size_t xkv_decode_lds(int rank, int nch, int ksel, bool gkeys);
+hipError_t launch_xkv_decode(const XkvDecodeLaunch& p, bool gkeys, size_t lds, hipStream_t s);
 hipError_t launch_philox(int64_t n, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
                          uint32_t k1, uint32_t* out, hipStream_t s);
 

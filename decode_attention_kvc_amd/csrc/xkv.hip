@@ -23,19 +23,17 @@
 //  3. xkv_project: A = X V on MFMA with V^T as bf16 in LDS, stored as bf16,
 //     and for keys the landmark of every 8-row chunk: the mean of its stored
 //     A rows.
-// Decode, three launches so that the whole chip streams the landmarks and
-// the kept rows (one workgroup per (b, j) would leave half the CUs idle):
-//  1. xkv_scores, (chunk split, b, j): q~_h = B_l q_h (r numbers per head)
-//     and the chunk scores max_h q~_h . landmark;
-//  2. xkv_attend, (row split, b, j): exact top-k of the chunks (radix
-//     select, ties to the lower chunk; each split repeats it), then attention
-//     over the split's share of the kept rows in the rank space:
-//     q_h . (A_t B_l) = q~_h . A_t and sum_t p_t A_t B_l = (sum_t p_t A_t)
-//     B_l, so the selected rows are rebuilt implicitly and never written;
-//  3. xkv_output, (b, j): the splits' partials merge with log-sum-exp
-//     weights, the output is projected by B_l^V, and an optional second part
-//     (rows appended after the factorisation, attended separately) is merged
-//     the same way.
+// Decode, one launch with one workgroup per (b, j) (section 4): q~_h = B_l q_h
+// (r numbers per head); the chunk scores max_h q~_h . landmark on MFMA; the
+// exact top-k of the chunks (ties to the lower chunk); attention over the
+// kept rows in the rank space, q_h . (A_t B_l) = q~_h . A_t and
+// sum_t p_t A_t B_l = (sum_t p_t A_t) B_l, so the selected rows are rebuilt
+// implicitly and never written; the output projected by B_l^V and merged
+// with an optional second part (rows appended after the factorisation,
+// attended separately) by log-sum-exp weights.  The value basis is stored
+// chunk-transposed (av_off) for the rank-space P*V product.
+#include <algorithm>
+
 #include "common.h"
 #include "kvc_internal.h"
 #include "philox.h"
@@ -50,9 +48,8 @@ constexpr int GP = 40;          // bf16 per staged channel row of a tile (80 byt
 constexpr int CHUNK = 8;        // rows per landmark chunk
 constexpr int VPITCH = XT + 2;  // bf16 per channel in a wave's value transpose buffer
 constexpr int MAXG = 8;         // query heads per KV head on the decode path
-constexpr int XNT = 512;        // threads of a decode workgroup (two waves per SIMD)
-constexpr int XNW = XNT / WAVE;
-static_assert(XNT == 4 * D, "the output step maps one thread to a (head, channel) pair");
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
 
 __device__ __forceinline__ bf16x8 as_bf(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
@@ -274,6 +271,14 @@ __global__ __launch_bounds__(256) void xkv_subspace(XkvLaunch p) {
     }
 }
 
+// Element of the value basis A_V[t][c] in its chunk-transposed layout
+// [t / 8][c][t % 8]: the 8 rows of a chunk for one rank are 16 contiguous
+// bytes, the operand layout of the decode's a~^T = A_V^T P^T product.
+template <int R>
+__host__ __device__ __forceinline__ size_t av_off(int t, int c) {
+    return (size_t)(t / CHUNK) * (R * CHUNK) + (size_t)c * CHUNK + (t % CHUNK);
+}
+
 // ---------------------------------------------------------------------------
 // 3. Projection A = X V and key landmarks
 // ---------------------------------------------------------------------------
@@ -373,7 +378,7 @@ __global__ __launch_bounds__(256) void xkv_project(XkvLaunch p) {
                 for (int i = 0; i < 4; ++i) {
                     const int t = t0 + 16 * rb + 4 * lg + i;
                     const uint16_t h = f32_to_bf16(t < T ? Y[rb][cb][i] : 0.f);
-                    if (t < T) A[(size_t)t * R + 16 * cb + l16] = h;
+                    if (t < T) A[IS_V ? av_off<R>(t, 16 * cb + l16) : (size_t)t * R + 16 * cb + l16] = h;
                     sum += bf16_to_f32(h);
                 }
                 if constexpr (!IS_V) {
@@ -398,420 +403,471 @@ __device__ __forceinline__ uint32_t desc_key(float s) {
     return ~asc;
 }
 
-// Lane permutations inside a 16-lane row (DPP: plain VALU moves).
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-    return __builtin_bit_cast(
-        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-// Sum over aligned groups of N lanes (N = 4 or 8; every lane gets it): swap
-// neighbours, swap pairs, then (N = 8) mirror the half-row.
-template <int N>
-__device__ __forceinline__ float group_sum(float v) {
-    v += dpp_mov<0xB1>(v);
-    v += dpp_mov<0x4E>(v);
-    if constexpr (N == 8) v += dpp_mov<0x141>(v);
-    return v;
-}
-// Sum over the lanes of a wave whose index agrees modulo N (N = 2 or 4):
-// rotations inside each 16-lane row, then across the four rows.
-template <int N>
-__device__ __forceinline__ float strided_sum(float v) {
-    if constexpr (N == 2) v += dpp_mov<0x122>(v);      // row_ror:2
-    if constexpr (N <= 4) v += dpp_mov<0x124>(v);      // row_ror:4
-    v += dpp_mov<0x128>(v);                             // row_ror:8
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
-}
-
-// Lanes per row of the rank space (8 columns each) and the dot products of
-// one row with the G query vectors q~ held in registers, summed over the
-// row's lanes (every lane of the group gets the sums).
-template <int R, int G>
-__device__ __forceinline__ void rank_dots(const u32x4& w, const float (&qr)[G][8], float (&s)[G]) {
-    constexpr int LPR = R / 8;
+// The k smallest of n keys (ties to the lower index), described as a masked
+// prefix: key u is kept when (u & mask) < prefix, or when (u & mask) ==
+// prefix and it is among the first *take such keys in index order (*cnt of
+// them exist; take == cnt keeps them all).  The first digit is the top 11
+// bits of the key, whose histogram the caller builds in sm.hist (2048 bins,
+// one copy) while it stores the keys; further digits of 8 bits (LDS
+// histograms in NC copies) follow only while the bin holding the k-th key
+// is not kept whole, so score keys usually resolve in one more pass.
+// 1 <= k <= n; every thread of the block must call it.
+constexpr int TOPK_B0 = 11;
+template <int NT, int NC>
+__device__ void topk_prefix(const uint32_t* keys, int n, uint32_t k, RadixSmem<NT, NC>& sm,
+                            uint32_t* prefix_out, uint32_t* mask_out, uint32_t* take_out,
+                            uint32_t* cnt_out) {
+    constexpr int PITCH = RadixSmem<NT, NC>::PITCH;
+    constexpr int BPL = (1 << TOPK_B0) / NT;     // first-digit bins per thread
+    static_assert(BPL >= 1 && NC * PITCH >= (1 << TOPK_B0), "first-digit histogram");
+    const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
+    {
+        uint32_t c[BPL], s = 0;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        float a = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            a = fmaf(qr[h][2 * e], bf16lo(w[e]), a);
-            a = fmaf(qr[h][2 * e + 1], bf16hi(w[e]), a);
+        for (int e = 0; e < BPL; ++e) {
+            c[e] = sm.hist[tid * BPL + e];
+            s += c[e];
         }
-        s[h] = group_sum<LPR>(a);
+        const uint32_t incl = wave_incl_scan(s);
+        if (lane == WAVE - 1) sm.wave_tot[wave] = incl;
+        __syncthreads();
+        uint32_t run = incl - s;
+        for (int w = 0; w < wave; ++w) run += sm.wave_tot[w];
+#pragma unroll
+        for (int e = 0; e < BPL; ++e) {
+            if (run < k && k <= run + c[e]) {
+                sm.bcast[0] = tid * BPL + e;
+                sm.bcast[1] = run;
+                sm.bcast[2] = c[e];
+            }
+            run += c[e];
+        }
+        __syncthreads();
     }
-}
-
-// q~_h = B_l q_h for the g heads of one (b, j) into LDS qt [MAXG][R] (heads
-// past g: zero); qs is scratch for the queries as float [g][D].
-template <int R>
-__device__ __forceinline__ void rank_queries(const XkvDecodeLaunch& p, int slab, int b, int j,
-                                             float* qs, float* qt) {
-    const int tid = threadIdx.x, g = p.g, n = p.window * D;
-    const float* BK = p.bk + (size_t)slab * n * R + (size_t)p.layer * D * R;
-    const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)b * p.hq + j * g) * D;
-    for (int x = tid; x < g * D; x += XNT) qs[x] = bf16_to_f32(q[x]);
-    __syncthreads();
-    for (int x = tid; x < MAXG * R; x += XNT) {
-        const int h = x / R, c = x % R;
-        float a0 = 0.f, a1 = 0.f;
-        if (h < g) {
-            const float* qh = qs + h * D;
-#pragma unroll 16
-            for (int i = 0; i < D; i += 2) {
-                a0 = fmaf(qh[i], BK[i * R + c], a0);
-                a1 = fmaf(qh[i + 1], BK[(i + 1) * R + c], a1);
+    uint32_t cnt = sm.bcast[2];
+    k -= sm.bcast[1];
+    int shift = 32 - TOPK_B0;
+    uint32_t prefix = sm.bcast[0] << shift, mask = ~((1u << shift) - 1u);
+    while (cnt != k && shift > 0) {
+        const int width = min(8, shift);
+        shift -= width;
+        // the first-digit histogram and bcast were read before the last barrier
+        for (int i = tid; i < NC * PITCH; i += NT) sm.hist[i] = 0;
+        __syncthreads();
+        uint32_t* hist = sm.hist + (tid % NC) * PITCH;
+        const uint32_t dmask = (1u << width) - 1u;
+        for (int t = tid; t < n; t += NT) {
+            const uint32_t u = keys[t];
+            if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & dmask], 1u);
+        }
+        __syncthreads();
+        if (tid < WAVE) {
+            // lane owns bins 4*lane .. 4*lane+3 (summed over the copies)
+            uint32_t c[4], s = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                c[e] = 0;
+#pragma unroll
+                for (int cp = 0; cp < NC; ++cp) c[e] += sm.hist[cp * PITCH + 4 * tid + e];
+                s += c[e];
+            }
+            uint32_t run = wave_incl_scan(s) - s;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (run < k && k <= run + c[e]) {
+                    sm.bcast[0] = 4 * tid + e;
+                    sm.bcast[1] = run;
+                    sm.bcast[2] = c[e];
+                }
+                run += c[e];
             }
         }
-        qt[h * R + c] = a0 + a1;
+        __syncthreads();
+        k -= sm.bcast[1];
+        cnt = sm.bcast[2];
+        prefix |= sm.bcast[0] << shift;
+        mask |= dmask << shift;
     }
-    __syncthreads();
+    *prefix_out = prefix;
+    *mask_out = mask;
+    *take_out = k;
+    *cnt_out = cnt;
 }
 
-// Decode, step 1: grid (chunk split, j, b).  q~ (the first split also keeps
-// it in the workspace for step 2) and the score keys of this split's chunks:
-// max over the heads of q~_h . landmark, LPR lanes per chunk, UNR chunks in
-// flight per lane group.
-template <int R, int G>
-__global__ __launch_bounds__(XNT) void xkv_scores(XkvDecodeLaunch p) {
-    __shared__ float qs[MAXG * D];
-    __shared__ float qt[MAXG * R];
-    constexpr int LPR = R / 8;
-    constexpr int NGRP = XNT / LPR;
-    constexpr int UNR = G <= 4 ? 16 : 8;
-    // The chunk splits of a (batch, KV head) pair read the same query
-    // projection inputs: contiguous runs of blocks per XCD share them in L2.
-    const BlockXYZ blk = xcd_run_block(true);
-    const int s = blk.x, j = blk.y, b = blk.z;
-    const int slab = b * p.hkv + j, g = p.g;
-    const int tid = threadIdx.x, lane = tid % WAVE;
-    const int sub = lane % LPR, grp = tid / LPR;
-    const int nch = (p.t_len + CHUNK - 1) / CHUNK;
-    const int c0 = s * p.cps, c1 = min(nch, c0 + p.cps);
-    rank_queries<R>(p, slab, b, j, qs, qt);
-    if (s == 0)
-        for (int x = tid; x < MAXG * R; x += XNT) p.ws_qt[(size_t)slab * MAXG * R + x] = qt[x];
-    float qr[G][8];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qr[h][e] = qt[h * R + 8 * sub + e];
-    const uint16_t* L = reinterpret_cast<const uint16_t*>(p.lk) + (size_t)slab * (p.x_tcap / CHUNK) * R;
-    uint32_t* keys = p.ws_keys + (size_t)slab * nch;
-    for (int base = c0; base < c1; base += UNR * NGRP) {
-        u32x4 w[UNR];
-#pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-            const int ch = base + u * NGRP + grp;
-            w[u] = ch < c1 ? load16(L + (size_t)ch * R + 8 * sub) : u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-            const int ch = base + u * NGRP + grp;
-            float sc[G];
-            rank_dots<R, G>(w[u], qr, sc);
-            float best = -INFINITY;
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-                if (h < g) best = fmaxf(best, sc[h]);
-            if (sub == 0 && ch < c1) keys[ch] = desc_key(best);
-        }
-    }
+constexpr int XF_NT = 1024;            // one decode workgroup per (b, j)
+constexpr int XF_NW = XF_NT / WAVE;
+
+// LDS floats of the decode besides the kept chunks and (when they fit) the
+// chunk keys: B_l^V rows, B_l^K (later the waves' partials), the queries,
+// q~ (later a~) and the partial sums of q~.
+__host__ __device__ constexpr int xf_area_a(int r) {
+    return D * r > XF_NW * MAXG * (r + 2) ? D * r : XF_NW * MAXG * (r + 2);
+}
+__host__ __device__ constexpr int xf_fixed_floats(int r) {
+    return D * (r + 1) + xf_area_a(r) + MAXG * D + MAXG * r + XF_NT;
 }
 
-// Decode, step 2: grid (row split, j, b).  Every workgroup of a (b, j)
-// selects the same ksel chunks from the keys (exact radix select, ties to
-// the lower chunk; the first workgroup reports them), then takes its share
-// [r0, r1) of the kept rows: logits in the rank space, its own maximum per
-// head, and a~_h = sum_t p_t,h A^V_t with z_h = sum_t p_t,h; the partial
-// (a~, max, z) goes to the workspace.
-template <int R, int G>
-__global__ __launch_bounds__(XNT) void xkv_attend(XkvDecodeLaunch p) {
+// x ~ hi + lo with both parts in bf16 (about 16 significant bits).
+__device__ __forceinline__ void split_bf16(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+    u16x8 h, l;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        h[e] = f32_to_bf16(x[e]);
+        l[e] = f32_to_bf16(x[e] - bf16_to_f32(h[e]));
+    }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+}
+
+// Decode in one launch, grid (j, b), one workgroup of 1024 threads per (b, j):
+//  0. B_l^K and the queries are read (every wave's reads queued before the
+//     landmark stream), then the first round of landmark rows and B_l^V;
+//  1. q~_h = B_l q_h (from LDS), held as bf16 hi + lo fragments: for 16x32
+//     operands the A fragment of q~ (heads x ranks) and the B fragment of
+//     q~^T (ranks x heads) are the same registers;
+//  2. chunk scores S = q~ L^T on v_mfma_f32_16x16x32_bf16, 16 chunks per
+//     product (heads padded to 16), max over the heads, order-preserving keys
+//     into LDS (GKEYS: into the workspace, for stores whose keys do not fit);
+//  3. the exact top-k of the keys (topk_prefix, its first digit counted while
+//     the keys are stored), emitted in chunk order;
+//  4. per 32 kept rows (4 chunks): S^T = A_K q~^T with the kept rows loaded
+//     in the order that makes each lane's S^T fragment its P^T operand (the
+//     8 rows of chunk lg), an online softmax whose reference maximum moves
+//     only when a logit exceeds it by more than 8 (log2 units), P split into
+//     bf16 hi + lo, and a~^T += A_V^T P^T, A_V stored chunk-transposed
+//     ([chunk][rank][8 rows]) so that the A operand is one 16-byte load;
+//  5. the waves' (reference, sum, a~) merge through LDS, then
+//     o_h = B_l^V a~_h / z_h per (head, channel), merged with the second part
+//     when one is given.
+template <int R, bool GKEYS>
+__global__ __launch_bounds__(XF_NT) void xkv_decode(XkvDecodeLaunch p) {
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ RadixSmem<XNT, 8> rs;
-    __shared__ float red[XNW][MAXG];
-    __shared__ float hm[MAXG];
-    constexpr int LPR = R / 8;             // lanes per rank-space row
-    constexpr int NGRP = XNT / LPR;        // rows per block pass
-    constexpr int UNR = G <= 4 ? 16 : 8;   // logit rows in flight per lane group
-    constexpr int CW = G <= 4 ? 16 : 8;    // value phase: columns per lane
-    constexpr int CG = R / CW;             //              column groups
-    constexpr int RGW = WAVE / CG;         //              row groups per wave
-    constexpr int RGS = XNW * RGW;         //              row groups per block
-    // The row splits of a pair read the same chunk scores and query
-    // projection: contiguous runs of blocks per XCD share them in L2.
-    const BlockXYZ blk = xcd_run_block(true);
-    const int a = blk.x, j = blk.y, b = blk.z;
+    __shared__ RadixSmem<XF_NT, 8> rs;
+    __shared__ float hz[MAXG], hm[MAXG];
+    constexpr int NT = XF_NT, NW = XF_NW;
+    constexpr int KS = R / 32;           // 32-rank k-steps
+    constexpr int RBK = R / 16;          // 16-rank blocks of a~^T
+    constexpr int UNB = 4;               // 16-chunk landmark blocks per wave and round
+    constexpr int BVP = R + 1;           // float pitch of the staged B_l^V rows
+    constexpr int BPT = D * R / 4 / NT;  // float4 per thread of one B matrix
+    constexpr int NPART = NT / (MAXG * R);
+    static_assert(BPT >= 1 && NPART >= 1 && D % NPART == 0 && MAXG * D == NT, "launch shape");
+    const int j = blockIdx.x, b = blockIdx.y;
     const int slab = b * p.hkv + j, g = p.g;
     const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
-    const int sub = lane % LPR, grp = tid / LPR;
+    const int l16 = lane & 15, lg = lane >> 4;
     const int T = p.t_len, nch = (T + CHUNK - 1) / CHUNK;
-    const int ksel = min(p.n_select, nch), nrows = ksel * CHUNK;
-    const int r0 = min(nrows, a * p.rpw), r1 = min(nrows, r0 + p.rpw);
-    uint32_t* keys = reinterpret_cast<uint32_t*>(smem);          // [nch]
-    int32_t* sel = reinterpret_cast<int32_t*>(keys + nch);       // [ksel]
-    float* lgt = reinterpret_cast<float*>(sel + ksel);           // [rpw][g]
-    float* part = lgt + (size_t)p.rpw * g;                       // [XNW][MAXG][R + 1]
-    float* out_part = p.ws_part + ((size_t)slab * p.nattend + a) * MAXG * (R + 2);
+    const int ksel = min(p.n_select, nch);
+    const int n = p.window * D;
 
-    if (r0 >= r1 && !(a == 0 && p.selected)) {
-        // no rows here and nothing to report: an empty partial
-        for (int h = tid; h < MAXG; h += XNT) {
-            out_part[h * (R + 2) + R] = -INFINITY;
-            out_part[h * (R + 2) + R + 1] = 0.f;
+    float* bvs = reinterpret_cast<float*>(smem);                  // [D][R + 1]
+    float* area = bvs + D * BVP;                                  // B_l^K [D][R], later partials
+    float* qs = area + xf_area_a(R);                              // [MAXG][D] queries
+    float* qt = qs + MAXG * D;                                    // [MAXG][R] q~, later a~
+    float* qpart = qt + MAXG * R;                                 // [NT] partial sums of q~
+    int32_t* sel = reinterpret_cast<int32_t*>(qpart + NT);        // [ksel] kept chunks
+    uint32_t* keys = GKEYS ? p.ws_keys + (size_t)slab * nch       // [nch]
+                           : reinterpret_cast<uint32_t*>(sel + ksel);
+
+    // 0. global reads
+    const float* BK = p.bk + (size_t)slab * n * R + (size_t)p.layer * D * R;
+    const float* BV = p.bv + (size_t)slab * n * R + (size_t)p.layer * D * R;
+    f32x4 bkr[BPT], bvr[BPT];
+#pragma unroll
+    for (int e = 0; e < BPT; ++e) bkr[e] = *reinterpret_cast<const f32x4*>(BK + 4 * (tid + e * NT));
+    const size_t row0 = (size_t)b * p.hq + (size_t)j * g;        // first output row of (b, j)
+    const bool qok = tid < g * D;                                 // (head tid / D, channel tid % D)
+    // loads are unconditional (clamped addresses, results selected after), so
+    // that the compiler's wait counts cover only the older loads
+    const uint16_t qraw = reinterpret_cast<const uint16_t*>(p.q)[row0 * D + (qok ? tid : 0)];
+    for (int i = tid; i < (1 << TOPK_B0); i += NT) rs.hist[i] = 0;   // first selection digit
+    // every wave's reads for q~ are queued ahead of the landmark stream
+    __syncthreads();
+    const uint16_t* L = reinterpret_cast<const uint16_t*>(p.lk) + (size_t)slab * (p.x_tcap / CHUNK) * R;
+    const int nlb = (nch + 15) / 16;                              // 16-chunk blocks
+    const int nlr = (nlb + NW * UNB - 1) / (NW * UNB);            // rounds
+    // B fragment of L^T: chunk 16 blk + l16, ranks 32 ks + 8 lg .. +8
+    auto load_lm = [&](u32x4 (&w)[UNB][KS], int r) {
+#pragma unroll
+        for (int u = 0; u < UNB; ++u) {
+            const int ch = ((r * UNB + u) * NW + wave) * 16 + l16;
+            const int chc = ch < nch ? ch : 0;   // in bounds: lk holds t_cap / 8 >= 8 rows
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) w[u][ks] = load16(L + (size_t)chc * R + 32 * ks + 8 * lg);
         }
-        return;
-    }
-    const float* qtg = p.ws_qt + (size_t)slab * MAXG * R;
-    float qr[G][8];                      // this lane's 8 columns of every q~_h
+    };
+    u32x4 la[UNB][KS], lb[UNB][KS];
+    load_lm(la, 0);
+    // B_l^V and the second part are needed at the end only
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int e = 0; e < BPT; ++e) bvr[e] = *reinterpret_cast<const f32x4*>(BV + 4 * (tid + e * NT));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qr[h][e] = qtg[h * R + 8 * sub + e];
-    const uint32_t* kg = p.ws_keys + (size_t)slab * nch;
-    for (int ch = tid; ch < nch; ch += XNT) keys[ch] = kg[ch];
+    for (int e = 0; e < BPT; ++e) *reinterpret_cast<f32x4*>(area + 4 * (tid + e * NT)) = bkr[e];
+    qs[tid] = qok ? bf16_to_f32(qraw) : 0.f;
     __syncthreads();
 
-    // the ksel best chunks, ascending (all of them when there are fewer):
-    // thread t owns the contiguous chunks [t*per, (t+1)*per), so one block
-    // scan places the equal keys in chunk order and another the kept ones
-    if (ksel < nch) {
-        uint32_t take;
-        const uint32_t thr = radix_select<XNT>(nch, (uint32_t)ksel, [&](int t) { return keys[t]; },
-                                               rs, &take);
-        const int per = (nch + XNT - 1) / XNT;
-        const int c0 = min(nch, tid * per), c1 = min(nch, c0 + per);
-        uint32_t n_eq = 0;
-        for (int ch = c0; ch < c1; ++ch) n_eq += keys[ch] == thr;
-        uint32_t tot;
-        uint32_t eq_rank = block_scan_u32<XNT>(n_eq, rs, &tot);
-        uint32_t n_keep = 0;
-        for (int ch = c0; ch < c1; ++ch) {
-            const uint32_t u = keys[ch];
-            n_keep += (u < thr) || (u == thr && eq_rank++ < take);
+    // 1. q~ (NPART threads per (head, rank), contiguous channel ranges)
+    {
+        const int c = tid % R, h = (tid / R) % MAXG, part = tid / (MAXG * R);
+        constexpr int IPP = D / NPART;
+        float a = 0.f;
+        if (h < g)
+            for (int i = part * IPP; i < (part + 1) * IPP; ++i) a = fmaf(qs[h * D + i], area[i * R + c], a);
+        qpart[tid] = a;
+    }
+    __syncthreads();
+    if (tid < MAXG * R) {
+        float a = 0.f;
+#pragma unroll
+        for (int part = 0; part < NPART; ++part) a += qpart[part * MAXG * R + tid];
+        qt[tid] = a;
+    }
+    __syncthreads();
+    bf16x8 qh[KS], ql[KS];               // head l16, ranks 32 ks + 8 lg .. +8
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = l16 < MAXG ? qt[l16 * R + 32 * ks + 8 * lg + e] : 0.f;
+        split_bf16(x, qh[ks], ql[ks]);
+    }
+
+    load_lm(lb, 1);                     // the second round once q~'s reads are in
+    // 2. chunk score keys
+    auto score_lm = [&](const u32x4 (&w)[UNB][KS], int r) {
+#pragma unroll
+        for (int u = 0; u < UNB; ++u) {
+            f32x4 S = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[ks], as_bf(w[u][ks]), S, 0, 0, 0);
+                S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[ks], as_bf(w[u][ks]), S, 0, 0, 0);
+            }
+            // S[i]: head 4 lg + i, chunk 16 blk + l16
+            float best = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * lg + i < g) best = fmaxf(best, S[i]);
+            best = fmaxf(best, __shfl_xor(best, 16));            // heads 4..7 into lanes lg = 0
+            const int ch = ((r * UNB + u) * NW + wave) * 16 + l16;
+            if (lg == 0 && ch < nch) {
+                const uint32_t key = desc_key(best);
+                keys[ch] = key;
+                atomicAdd(&rs.hist[key >> (32 - TOPK_B0)], 1u);
+            }
         }
-        eq_rank -= n_eq;                           // back to this thread's first equal key
-        uint32_t pos = block_scan_u32<XNT>(n_keep, rs, &tot);
+    };
+    // Branch-free rounds: a round past the last one loads row 0 of the
+    // landmarks in every lane (one cached line) and writes no key, so the
+    // wait counts stay exact and one round is always in flight.
+    for (int r = 0; r < nlr; r += 2) {
+        score_lm(la, r);
+        load_lm(la, r + 2);
+        score_lm(lb, r + 1);
+        load_lm(lb, r + 3);
+    }
+#pragma unroll
+    for (int e = 0; e < BPT; ++e) {
+        const int x = 4 * (tid + e * NT);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) bvs[((x + c) / R) * BVP + (x + c) % R] = bvr[e][c];
+    }
+    __syncthreads();
+
+    // 3. the ksel best chunks in ascending chunk order (all of them when
+    // there are fewer): thread t owns chunks [t*per, (t+1)*per)
+    if (ksel < nch) {
+        uint32_t prefix, mask, take, cnt;
+        topk_prefix<NT, 8>(keys, nch, (uint32_t)ksel, rs, &prefix, &mask, &take, &cnt);
+        const int per = (nch + NT - 1) / NT;
+        const int c0 = min(nch, tid * per), c1 = min(nch, c0 + per);
+        // ranks among the keys equal to the prefix, needed only when some of
+        // them are left out (the condition is the same in every thread)
+        uint32_t eq0 = 0, tot;
+        if (take != cnt) {
+            uint32_t n_eq = 0;
+            for (int ch = c0; ch < c1; ++ch) n_eq += (keys[ch] & mask) == prefix;
+            eq0 = block_scan_u32<NT>(n_eq, rs, &tot);
+        }
+        auto kept = [&](uint32_t u, uint32_t& eq_rank) {
+            const uint32_t um = u & mask;
+            return (um < prefix) || (um == prefix && eq_rank++ < take);
+        };
+        uint32_t eq_rank = eq0, n_keep = 0;
+        for (int ch = c0; ch < c1; ++ch) n_keep += kept(keys[ch], eq_rank);
+        eq_rank = eq0;
+        uint32_t pos = block_scan_u32<NT>(n_keep, rs, &tot);
         for (int ch = c0; ch < c1; ++ch) {
-            const uint32_t u = keys[ch];
-            if ((u < thr) || (u == thr && eq_rank++ < take)) {
+            if (kept(keys[ch], eq_rank)) {
                 if (pos < (uint32_t)ksel) sel[pos] = ch;
                 ++pos;
             }
         }
     } else {
-        for (int ch = tid; ch < nch; ch += XNT) sel[ch] = ch;
+        for (int ch = tid; ch < nch; ch += NT) sel[ch] = ch;
     }
     __syncthreads();
-    if (a == 0 && p.selected)
-        for (int x = tid; x < p.n_select; x += XNT)
+    if (p.selected)
+        for (int x = tid; x < p.n_select; x += NT)
             p.selected[(size_t)slab * p.n_select + x] = x < ksel ? sel[x] : -1;
 
-    // logits of this workgroup's rows in the rank space (LPR lanes per row,
-    // UNR rows in flight) and its maximum per head
+    // 4. kept rows, 32 (4 chunks) per block, blocks wave, wave + NW, ...
     const uint16_t* AK = reinterpret_cast<const uint16_t*>(p.ak) + (size_t)slab * p.x_tcap * R;
     const uint16_t* AV = reinterpret_cast<const uint16_t*>(p.av) + (size_t)slab * p.x_tcap * R;
-    {
-        float mh[G];
+    const float scale2 = p.scale * LOG2E;
+    const int nblk = (ksel + 3) / 4;
+    struct RowRegs {
+        u32x4 k[2][KS];   // A_K rows: MFMA block c, lane row l16
+        u32x4 v[RBK];     // A_V^T: ranks 16 rb + l16, the 8 rows of kept chunk lg
+    };
+    auto load_blk = [&](RowRegs& X, int k) {
+        const int qk = 4 * k + (l16 >> 2);
+        const int ck = qk < ksel ? sel[qk] * CHUNK : T;
 #pragma unroll
-        for (int h = 0; h < G; ++h) mh[h] = -INFINITY;
-        for (int base = r0; base < r1; base += UNR * NGRP) {
-            u32x4 w[UNR];
-            int tr[UNR];
+        for (int c = 0; c < 2; ++c) {
+            const int t = ck + 4 * c + (l16 & 3);
 #pragma unroll
-            for (int u = 0; u < UNR; ++u) {
-                const int r = base + u * NGRP + grp;
-                tr[u] = r < r1 ? sel[r / CHUNK] * CHUNK + r % CHUNK : T;
-                w[u] = tr[u] < T ? load16(AK + (size_t)tr[u] * R + 8 * sub) : u32x4{0u, 0u, 0u, 0u};
+            for (int ks = 0; ks < KS; ++ks)
+                X.k[c][ks] = t < T ? load16(AK + (size_t)t * R + 32 * ks + 8 * lg) : u32x4{0u, 0u, 0u, 0u};
+        }
+        const int qv4 = 4 * k + lg;
+        const int cv = qv4 < ksel ? sel[qv4] : -1;
+#pragma unroll
+        for (int rb = 0; rb < RBK; ++rb)
+            X.v[rb] = cv >= 0 ? load16(AV + (size_t)cv * R * CHUNK + (16 * rb + l16) * CHUNK)
+                              : u32x4{0u, 0u, 0u, 0u};
+    };
+    float mr = -INFINITY, zl = 0.f;      // head l16: reference maximum, this lane's sum
+    f32x4 acc[RBK];                      // a~^T: rank 16 rb + 4 lg + i, head l16
+#pragma unroll
+    for (int rb = 0; rb < RBK; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute_blk = [&](RowRegs& X, int k) {
+        f32x4 S[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            S[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                S[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(X.k[c][ks]), qh[ks], S[c], 0, 0, 0);
+                S[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(X.k[c][ks]), ql[ks], S[c], 0, 0, 0);
             }
+        }
+        // S[c][i]: head l16, row 4 c + i of kept chunk lg of this block
+        const int qv4 = 4 * k + lg;
+        const int cb = qv4 < ksel ? sel[qv4] * CHUNK : T;
+        float sv[8];
+        float mx = -INFINITY;
 #pragma unroll
-            for (int u = 0; u < UNR; ++u) {
-                const int r = base + u * NGRP + grp;
-                float sc[G];
-                rank_dots<R, G>(w[u], qr, sc);
-                if (r < r1) {
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-                    for (int h = 0; h < G; ++h) {
-                        if (h < g) {
-                            const float l = tr[u] < T ? sc[h] * p.scale : -INFINITY;
-                            mh[h] = fmaxf(mh[h], l);
-                            if (sub == 0) lgt[(r - r0) * g + h] = l;
-                        }
-                    }
-                }
+            for (int i = 0; i < 4; ++i) {
+                const float x = cb + 4 * c + i < T ? S[c][i] * scale2 : -INFINITY;
+                sv[4 * c + i] = x;
+                mx = fmaxf(mx, x);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool move = mx > mr + 8.f;            // also the first block with a row
+        const float mnew = move ? mx : mr;
+        const float alpha = move ? exp2f(mr - mnew) : 1.f;   // 0 from -inf
+        const bool any_move = __ballot(move) != 0;
+        mr = mnew;
+        float ps = 0.f;
+        u16x8 hi, lo;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            const float pj = sv[jj] == -INFINITY ? 0.f : exp2f(sv[jj] - mnew);
+            ps += pj;
+            const uint16_t h16 = f32_to_bf16(pj);
+            hi[jj] = h16;
+            lo[jj] = f32_to_bf16(pj - bf16_to_f32(h16));
+        }
+        zl = zl * alpha + ps;
+        if (any_move) {
+#pragma unroll
+            for (int rb = 0; rb < RBK; ++rb) acc[rb] *= alpha;
+        }
+        if (cb + CHUNK > T && cb < T) {
+            // the sequence's last chunk: its rows past T hold arbitrary bits
+#pragma unroll
+            for (int rb = 0; rb < RBK; ++rb) {
+                u16x8 e = __builtin_bit_cast(u16x8, X.v[rb]);
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) e[jj] = cb + jj < T ? e[jj] : (uint16_t)0;
+                X.v[rb] = __builtin_bit_cast(u32x4, e);
             }
         }
+        const bf16x8 pH = __builtin_bit_cast(bf16x8, hi), pL = __builtin_bit_cast(bf16x8, lo);
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float m = wave_max(mh[h]);
-            if (lane == 0) red[wave][h] = m;
+        for (int rb = 0; rb < RBK; ++rb) {
+            acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(X.v[rb]), pH, acc[rb], 0, 0, 0);
+            acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(X.v[rb]), pL, acc[rb], 0, 0, 0);
         }
-        __syncthreads();
-        if (tid < MAXG) {
-            float m = red[0][tid];
-            for (int w2 = 1; w2 < XNW; ++w2) m = fmaxf(m, red[w2][tid]);
-            hm[tid] = m;
-        }
-        __syncthreads();
+    };
+    // the second part, read while the kept rows stream
+    const float o2 = (qok && p.o_in) ? p.o_in[row0 * D + tid] : 0.f;
+    const float l2 = (qok && p.o_in) ? p.lse_in[row0 + tid / D] : -INFINITY;
+    // one block in flight per wave (sixteen waves: 128 KB per workgroup); a
+    // second register set would not fit beside the accumulators
+    for (int k = wave; k < nblk; k += NW) {
+        RowRegs X;
+        load_blk(X, k);
+        compute_blk(X, k);
     }
 
-    // a~ and z over this workgroup's rows: lane (row group, CW-column
-    // group), 16-byte value reads, VR rows in flight; then sums over the row
-    // groups (lanes, then waves)
-    {
-        const int cg = lane % CG, rgl = lane / CG;
-        const int rg = wave * RGW + rgl;
-        float mx[G];
+    // 5. the waves' partials (every lane of head l16 shares its reference)
+    zl += __shfl_xor(zl, 16);
+    zl += __shfl_xor(zl, 32);
+    float* wp = area;                                             // [NW][MAXG][R + 2]
+    if (l16 < g) {
+        float* d = wp + (wave * MAXG + l16) * (R + 2);
 #pragma unroll
-        for (int h = 0; h < G; ++h) mx[h] = hm[h];
-        float acc[G][CW], zs[G];
+        for (int rb = 0; rb < RBK; ++rb)
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            zs[h] = 0.f;
-#pragma unroll
-            for (int e = 0; e < CW; ++e) acc[h][e] = 0.f;
-        }
-        constexpr int VR = 8;
-        constexpr int NL = CW / 8;                 // 16-byte loads per row and lane
-        for (int base = r0 + rg; base < r1; base += VR * RGS) {
-            u32x4 w[VR][NL];
-            int tr[VR];
-#pragma unroll
-            for (int u = 0; u < VR; ++u) {
-                const int r = base + u * RGS;
-                tr[u] = r < r1 ? sel[r / CHUNK] * CHUNK + r % CHUNK : T;
-                const bool ok = tr[u] < T;
-#pragma unroll
-                for (int q2 = 0; q2 < NL; ++q2)
-                    w[u][q2] = ok ? load16(AV + (size_t)tr[u] * R + CW * cg + 8 * q2)
-                                  : u32x4{0u, 0u, 0u, 0u};
-            }
-#pragma unroll
-            for (int u = 0; u < VR; ++u) {
-                const int r = base + u * RGS;
-                if (tr[u] < T) {
-#pragma unroll
-                    for (int h = 0; h < G; ++h) {
-                        if (h < g) {
-                            const float pr = expf(lgt[(r - r0) * g + h] - mx[h]);
-                            zs[h] += pr;
-#pragma unroll
-                            for (int q2 = 0; q2 < NL; ++q2)
-#pragma unroll
-                                for (int e = 0; e < 4; ++e) {
-                                    acc[h][8 * q2 + 2 * e] =
-                                        fmaf(pr, bf16lo(w[u][q2][e]), acc[h][8 * q2 + 2 * e]);
-                                    acc[h][8 * q2 + 2 * e + 1] =
-                                        fmaf(pr, bf16hi(w[u][q2][e]), acc[h][8 * q2 + 2 * e + 1]);
-                                }
-                        }
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            zs[h] = strided_sum<CG>(zs[h]);
-#pragma unroll
-            for (int e = 0; e < CW; ++e) acc[h][e] = strided_sum<CG>(acc[h][e]);
-        }
-        if (rgl == 0) {
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-#pragma unroll
-                for (int e = 0; e < CW; ++e) part[(wave * MAXG + h) * (R + 1) + CW * cg + e] = acc[h][e];
-                if (cg == 0) part[(wave * MAXG + h) * (R + 1) + R] = zs[h];
-            }
+            for (int i = 0; i < 4; ++i) d[16 * rb + 4 * lg + i] = acc[rb][i];
+        if (lg == 0) {
+            d[R] = mr;
+            d[R + 1] = zl;
         }
     }
     __syncthreads();
-    for (int x = tid; x < MAXG * (R + 1); x += XNT) {
+    for (int x = tid; x < g * (R + 1); x += NT) {
         const int h = x / (R + 1), c = x % (R + 1);
-        float s4 = 0.f;
-        for (int w2 = 0; w2 < XNW; ++w2) s4 += part[(w2 * MAXG + h) * (R + 1) + c];
-        out_part[h * (R + 2) + (c < R ? c : R + 1)] = s4;
-        if (c == R) out_part[h * (R + 2) + R] = hm[h];
-    }
-}
-
-// Decode, step 3: grid (j, b).  The row splits' partials merge with
-// log-sum-exp weights; o_h = B_l^V a~_h / z_h, merged with the second part
-// if given.  Thread (h, i) owns output channel i of heads h and h + 4.
-// Every global read (its row of B_l^V, the second part, the partials) is
-// issued before the first barrier, so the kernel waits on one round trip.
-template <int R>
-__global__ __launch_bounds__(XNT) void xkv_output(XkvDecodeLaunch p) {
-    __shared__ float ps[XKV_MAX_ATTEND * MAXG * (R + 2)];
-    __shared__ float at[MAXG * R];
-    __shared__ float hz[MAXG], hmx[MAXG];
-    __shared__ float wts[XKV_MAX_ATTEND * MAXG];
-    constexpr int HPT = MAXG / (XNT / D);      // heads per thread
-    const int j = blockIdx.x, b = blockIdx.y;
-    const int slab = b * p.hkv + j, g = p.g, n = p.window * D, tid = threadIdx.x;
-    const int na = p.nattend;
-    const float* P = p.ws_part + (size_t)slab * na * MAXG * (R + 2);
-    const float* BV = p.bv + (size_t)slab * n * R + (size_t)p.layer * D * R;
-    const int oh = tid / D, i = tid % D;
-    f32x4 bvv[R / 4];
-#pragma unroll
-    for (int c4 = 0; c4 < R / 4; ++c4) bvv[c4] = *reinterpret_cast<const f32x4*>(BV + i * R + 4 * c4);
-    float o2[HPT], l2[HPT];
-#pragma unroll
-    for (int k = 0; k < HPT; ++k) {
-        const int h = oh + k * (XNT / D);
-        const size_t row = (size_t)b * p.hq + j * g + h;
-        o2[k] = (p.o_in && h < g) ? p.o_in[row * D + i] : 0.f;
-        l2[k] = (p.o_in && h < g) ? p.lse_in[row] : -INFINITY;
-    }
-    for (int x = tid; x < na * MAXG * (R + 2); x += XNT) ps[x] = P[x];
-    __syncthreads();
-    if (tid < MAXG) {
         float M = -INFINITY;
-        for (int a = 0; a < na; ++a) M = fmaxf(M, ps[(a * MAXG + tid) * (R + 2) + R]);
-        for (int a = 0; a < na; ++a) {
-            const float ma = ps[(a * MAXG + tid) * (R + 2) + R];
-            wts[a * MAXG + tid] = ma == -INFINITY ? 0.f : expf(ma - M);   // a split without rows
-        }
-        hmx[tid] = M;
-    }
-    __syncthreads();
-    for (int x = tid; x < g * (R + 1); x += XNT) {
-        const int h = x / (R + 1), c = x % (R + 1);
+        for (int w2 = 0; w2 < NW; ++w2) M = fmaxf(M, wp[(w2 * MAXG + h) * (R + 2) + R]);
         float sum = 0.f;
-        for (int a = 0; a < na; ++a) {
-            const float w = wts[a * MAXG + h];
-            const float v = ps[(a * MAXG + h) * (R + 2) + (c < R ? c : R + 1)];
-            sum = w == 0.f ? sum : fmaf(w, v, sum);
+        for (int w2 = 0; w2 < NW; ++w2) {
+            const float* d = wp + (w2 * MAXG + h) * (R + 2);
+            const float f = d[R] == -INFINITY ? 0.f : exp2f(d[R] - M);   // a wave without rows
+            sum = f == 0.f ? sum : fmaf(f, d[c < R ? c : R + 1], sum);
         }
-        if (c < R) at[h * R + c] = sum;
-        else hz[h] = sum;
+        if (c < R) {
+            qt[h * R + c] = sum;
+        } else {
+            hz[h] = sum;
+            hm[h] = M;
+        }
     }
     __syncthreads();
-#pragma unroll
-    for (int k = 0; k < HPT; ++k) {
-        const int h = oh + k * (XNT / D);
-        if (h >= g) break;
+    if (qok) {
+        const int h = tid / D, i = tid % D;
         float o = 0.f;
-#pragma unroll
-        for (int c4 = 0; c4 < R / 4; ++c4)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o = fmaf(bvv[c4][e], at[h * R + 4 * c4 + e], o);
+#pragma unroll 16
+        for (int c = 0; c < R; ++c) o = fmaf(bvs[i * BVP + c], qt[h * R + c], o);
         const float zz = hz[h];
-        float l1 = zz > 0.f ? hmx[h] + logf(zz) : -INFINITY;
+        float l1 = zz > 0.f ? (hm[h] + log2f(zz)) * LN2 : -INFINITY;
         o = zz > 0.f ? o / zz : 0.f;
-        const size_t row = (size_t)b * p.hq + j * g + h;
         if (p.o_in) {
-            const float mm = fmaxf(l1, l2[k]);
+            const float mm = fmaxf(l1, l2);
             if (mm != -INFINITY) {
                 const float w1 = (l1 == -INFINITY) ? 0.f : expf(l1 - mm);
-                const float w2 = (l2[k] == -INFINITY) ? 0.f : expf(l2[k] - mm);
-                o = (o * w1 + o2[k] * w2) / (w1 + w2);
+                const float w2 = (l2 == -INFINITY) ? 0.f : expf(l2 - mm);
+                o = (o * w1 + o2 * w2) / (w1 + w2);
                 l1 = mm + logf(w1 + w2);
             }
         }
-        p.out[row * D + i] = o;
-        if (i == 0 && p.lse) p.lse[row] = l1;
+        p.out[row0 * D + tid] = o;
+        if (i == 0 && p.lse) p.lse[row0 + h] = l1;
     }
 }
 
@@ -850,23 +906,21 @@ hipError_t launch_xkv_factor(const XkvLaunch& p, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_xkv_decode(const XkvDecodeLaunch& p, size_t lds, hipStream_t st) {
-    const dim3 sgrid(p.nscore, p.hkv, p.nb), agrid(p.nattend, p.hkv, p.nb), ogrid(p.hkv, p.nb);
-    auto go = [&](auto score, auto attend, auto output) {
-        if (lds > 64 * 1024 &&
-            hipFuncSetAttribute(reinterpret_cast<const void*>(attend),
+size_t xkv_decode_lds(int rank, int nch, int ksel, bool gkeys) {
+    return ((size_t)xf_fixed_floats(rank) + ksel + (gkeys ? 0 : nch)) * 4;
+}
+
+hipError_t launch_xkv_decode(const XkvDecodeLaunch& p, bool gkeys, size_t lds, hipStream_t st) {
+    const dim3 grid(p.hkv, p.nb);
+    auto go = [&](auto kern) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
             return hipErrorInvalidValue;
-        hipLaunchKernelGGL(score, sgrid, dim3(XNT), 0, st, p);
-        hipLaunchKernelGGL(attend, agrid, dim3(XNT), lds, st, p);
-        hipLaunchKernelGGL(output, ogrid, dim3(XNT), 0, st, p);
+        hipLaunchKernelGGL(kern, grid, dim3(XF_NT), lds, st, p);
         return hipGetLastError();
     };
-    if (p.rank == 32)
-        return p.g <= 4 ? go(xkv_scores<32, 4>, xkv_attend<32, 4>, xkv_output<32>)
-                        : go(xkv_scores<32, 8>, xkv_attend<32, 8>, xkv_output<32>);
-    return p.g <= 4 ? go(xkv_scores<64, 4>, xkv_attend<64, 4>, xkv_output<64>)
-                    : go(xkv_scores<64, 8>, xkv_attend<64, 8>, xkv_output<64>);
+    if (p.rank == 32) return gkeys ? go(xkv_decode<32, true>) : go(xkv_decode<32, false>);
+    return gkeys ? go(xkv_decode<64, true>) : go(xkv_decode<64, false>);
 }
 
 }  // namespace kvc

@@ -488,7 +488,11 @@ int kvc_q8_decode_attn(const kvc_qcache* c, const void* q,
  * [XKV §2.2: the window's caches concatenated side by side, a rank-r SVD,
  * one token basis A shared by the window and one matrix B_l per layer].
  * Per (batch entry b, KV head j), keys and values separately:
- *   ak, av: bf16 [nb][n_kv_heads][t_cap][rank]      token bases A
+ *   ak:     bf16 [nb][n_kv_heads][t_cap][rank]      key token basis A_K
+ *   av:     bf16 [nb][n_kv_heads][t_cap/chunk][rank][chunk]  value token
+ *           basis A_V, chunk-transposed: A_V[t][c] at [t/chunk][c][t%chunk]
+ *           (the chunk's rows side by side for each rank, the operand
+ *           layout of the rank-space value product)
  *   bk, bv: float32 [nb][n_kv_heads][window*head_dim][rank]: rows
  *           l*head_dim .. l*head_dim + head_dim - 1 hold B_l^T, so layer l's
  *           row t is rebuilt as A[t] B_l
@@ -550,11 +554,15 @@ int kvc_xkv_factor(const kvc_cache* c, int slot0, int iters, uint64_t seed,
  * union's log-normaliser.  q: bf16 [nb][n_q_heads][head_dim]; out: float32
  * like o_in; selected: NULL or int32 [nb][n_kv_heads][n_select] (-1 past the
  * kept count).  n_select * chunk * g <= 16384 and the chunk keys of t_len
- * rows must fit one workgroup's LDS (KVC_EINVAL otherwise).  ws:
- * kvc_xkv_decode_ws_bytes bytes for the same store shape, head count and
- * n_select (16-byte aligned, no initialisation needed; KVC_EWORKSPACE if
- * smaller); it holds the chunk keys, q~ and the row splits' partials between
- * the three launches, so calls that share a workspace must be ordered.
+ * rows must fit one workgroup's LDS (KVC_EINVAL otherwise).  When the keys
+ * of every (b, j) fit with the rest of the work (about 18000 chunks at rank
+ * 64, 26000 at rank 32) the whole decode is one launch with one workgroup
+ * per (b, j) and needs no workspace: kvc_xkv_decode_ws_bytes reports 0 and
+ * ws may be NULL.  Longer stores take three launches whose chunk keys, q~
+ * and row-split partials live in ws: kvc_xkv_decode_ws_bytes bytes for the
+ * same store shape, head count and n_select (16-byte aligned, no
+ * initialisation needed; KVC_EWORKSPACE if smaller), so calls that share a
+ * workspace must be ordered.
  */
 int kvc_xkv_decode_attn(const kvc_xkv* x, int layer, const void* q, int n_q_heads, float scale,
                         int n_select, const float* o_in, const float* lse_in, float* out,
@@ -562,7 +570,8 @@ int kvc_xkv_decode_attn(const kvc_xkv* x, int layer, const void* q, int n_q_head
                         kvc_stream_t stream);
 
 /* Workspace bytes kvc_xkv_decode_attn needs for this store shape, query head
- * count and n_select (same argument checks as the call). */
+ * count and n_select (same argument checks as the call); 0 for the
+ * one-launch decode. */
 int kvc_xkv_decode_ws_bytes(const kvc_xkv* x, int n_q_heads, int n_select, size_t* bytes);
 
 /*

@@ -386,17 +386,22 @@ def test_xkv_decode_validation():
     assert d(o_in=FAKE) == kvc.KVC_EINVAL                        # lse_in missing
     assert d(q=FAKE + 2) == kvc.KVC_EALIGN
     assert d(x=xkv_desc(nb=0)) == kvc.KVC_OK
-    # the workspace: keys of 13 chunks, q~ for 8 heads and one row split's
-    # partials per (b, j) at least; checked after the arguments
+    # a store whose chunk keys fit in LDS decodes in one launch without a
+    # workspace (a null one is accepted)
     n = ctypes.c_size_t()
     assert L.kvc_xkv_decode_ws_bytes(ctypes.byref(x), 8, 64, ctypes.byref(n)) == kvc.KVC_OK
-    assert n.value >= 2 * (13 * 4 + 8 * 64 * 4 + 8 * 66 * 4)
+    assert n.value == 0
     assert L.kvc_xkv_decode_ws_bytes(ctypes.byref(x), 7, 64, ctypes.byref(n)) == kvc.KVC_EINVAL
     assert L.kvc_xkv_decode_ws_bytes(ctypes.byref(x), 8, 0, ctypes.byref(n)) == kvc.KVC_EINVAL
-    assert d(wsb=n.value - 1) == kvc.KVC_EWORKSPACE
-    assert d(ws=None) == kvc.KVC_EWORKSPACE
-    assert d(ws=FAKE + 4) == kvc.KVC_EWORKSPACE
-    assert d(ws=None, hq=7) == kvc.KVC_EINVAL
+    # 25000 chunks do not fit: the workspace holds the chunk keys of every
+    # (b, j); checked after the arguments
+    big = xkv_desc(t_len=200000, t_cap=200000)
+    assert L.kvc_xkv_decode_ws_bytes(ctypes.byref(big), 8, 64, ctypes.byref(n)) == kvc.KVC_OK
+    assert n.value == 2 * 25000 * 4
+    assert d(x=big, wsb=n.value - 1) == kvc.KVC_EWORKSPACE
+    assert d(x=big, ws=None) == kvc.KVC_EWORKSPACE
+    assert d(x=big, ws=FAKE + 4) == kvc.KVC_EWORKSPACE
+    assert d(x=big, ws=None, hq=7) == kvc.KVC_EINVAL
 
 
 def rows_cache(**kw):

@@ -63,7 +63,7 @@ def factor(c, slot0, W, rank, iters=12):
 
 
 def gpu_recon(st, b, j, l, kv):
-    A = (st.ak if kv == 0 else st.av)[b, j, :st.t_len].double().cpu().numpy()
+    A = (st.ak[b, j] if kv == 0 else st.av_rows(b, j))[:st.t_len].double().cpu().numpy()
     B = (st.bk if kv == 0 else st.bv)[b, j, l * 128:(l + 1) * 128].double().cpu().numpy().T
     return A @ B
 
@@ -127,7 +127,7 @@ def oracle_store(Ks, Vs, rank, t_cap):
             BKf = [np.asarray(B, dtype=np.float32).astype(np.float64) for B in BK]
             BVf = [np.asarray(B, dtype=np.float32).astype(np.float64) for B in BV]
             st.ak[b, j, :T] = torch.as_tensor(AKr, dtype=torch.bfloat16)
-            st.av[b, j, :T] = torch.as_tensor(AVr, dtype=torch.bfloat16)
+            st.set_av_rows(b, j, torch.as_tensor(AVr, dtype=torch.bfloat16, device=DEV))
             st.lk[b, j, :len(L)] = torch.as_tensor(L, dtype=torch.bfloat16)
             st.bk[b, j] = torch.as_tensor(np.vstack([B.T for B in BKf]), dtype=torch.float32)
             st.bv[b, j] = torch.as_tensor(np.vstack([B.T for B in BVf]), dtype=torch.float32)
@@ -273,7 +273,7 @@ def test_decode_full_size_sampled():
     flips = 0
     for (b, j) in [(0, 0), (7, 3), (15, 7), (9, 5)]:
         AK = st.ak[b, j, :T].double().cpu().numpy()
-        AV = st.av[b, j, :T].double().cpu().numpy()
+        AV = st.av_rows(b, j)[:T].double().cpu().numpy()
         L = st.lk[b, j, :nch].double().cpu().numpy()
         BK = st.bk[b, j, layer * 128:(layer + 1) * 128].double().cpu().numpy().T
         BV = st.bv[b, j, layer * 128:(layer + 1) * 128].double().cpu().numpy().T
@@ -293,3 +293,94 @@ def test_decode_full_size_sampled():
         assert np.abs(to_np(lse[b, j * g:(j + 1) * g]) - rl).max() <= 1e-4, (b, j)
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
     say(f"  sampled pairs with a flipped chunk inside the band: {flips}")
+
+
+def random_store(nb, hkv, T, W, R, seed):
+    """Seeded N(0, 1) store contents (the decode needs no factorisation)."""
+    st = kvc.XkvStore.empty(nb, hkv, W, R, T, device=DEV, t_len=T)
+    st.ak.copy_(kvc_synth.queries(st.ak.shape, device=DEV, seed=seed))
+    st.av.copy_(kvc_synth.queries(st.av.shape, device=DEV, seed=seed + 1))
+    st.lk.copy_(kvc_synth.queries(st.lk.shape, device=DEV, seed=seed + 2))
+    st.bk.copy_(kvc_synth.queries(st.bk.shape, dtype=torch.float32, device=DEV, seed=seed + 3)
+                * 128 ** -0.5)
+    st.bv.copy_(kvc_synth.queries(st.bv.shape, dtype=torch.float32, device=DEV, seed=seed + 4)
+                * 128 ** -0.5)
+    return st
+
+
+def check_pairs(st, q, out, lse, sel, layer, n_sel, pairs, exact_sel=False):
+    """Sampled (b, j) pairs against the oracle's selective reconstruction;
+    chunks kept by one side only must sit within 1e-5 of the cutoff score
+    unless exact_sel.  Returns the number of pairs with such a flip."""
+    T, hkv = st.t_len, st.n_kv_heads
+    g = q.shape[1] // hkv
+    nch = (T + 7) // 8
+    flips = 0
+    for (b, j) in pairs:
+        AK = st.ak[b, j, :T].double().cpu().numpy()
+        AV = st.av_rows(b, j)[:T].double().cpu().numpy()
+        L = st.lk[b, j, :nch].double().cpu().numpy()
+        BK = st.bk[b, j, layer * 128:(layer + 1) * 128].double().cpu().numpy().T
+        BV = st.bv[b, j, layer * 128:(layer + 1) * 128].double().cpu().numpy().T
+        qh = to_np(q[b, j * g:(j + 1) * g])
+        ro, rl, kept = oxkv.sr_attention(qh, AK, AV, BK, BV, L, 8, n_sel)
+        got = sel[b, j].cpu().numpy()
+        k = len(kept)
+        assert np.all(got[k:] == -1)
+        if not np.array_equal(got[:k], kept):
+            assert not exact_sel, (b, j)
+            sc = oxkv.chunk_scores(qh, BK, L)
+            cut = np.sort(sc)[::-1][k - 1]
+            for ch in set(got[:k].tolist()) ^ set(kept.tolist()):
+                assert abs(sc[ch] - cut) <= 1e-5 * np.abs(sc).max(), (b, j, ch)
+            flips += 1
+            continue
+        assert np.abs(to_np(out[b, j * g:(j + 1) * g]) - ro).max() <= 1e-3, (b, j)
+        assert np.abs(to_np(lse[b, j * g:(j + 1) * g]) - rl).max() <= 1e-4, (b, j)
+    return flips
+
+
+def run_decode(st, q, layer, n_sel):
+    nb, hq = q.shape[0], q.shape[1]
+    out = torch.full((nb, hq, 128), float("nan"), device=DEV)
+    lse = torch.full((nb, hq), float("nan"), device=DEV)
+    sel = torch.full((nb, st.n_kv_heads, n_sel), -7, dtype=torch.int32, device=DEV)
+    nbytes = kvc.kvc_xkv_decode_ws_bytes(st, hq, n_sel)
+    kvc.kvc_xkv_decode_attn(st, layer, q, out, lse, n_select=n_sel, selected=sel,
+                            ws=ws_tensor(nbytes) if nbytes else None)
+    torch.cuda.synchronize()
+    return out, lse, sel, nbytes
+
+
+def test_decode_long_store_uses_the_workspace_path():
+    """170000 rows at rank 64 (21250 chunk keys, more than one workgroup's
+    LDS holds): the three-launch decode with keys in the workspace, against
+    the oracle."""
+    say("xkv decode, long store")
+    nb, hkv, hq, T, W, R, n_sel = 1, 2, 8, 170000, 2, 64, 64
+    st = random_store(nb, hkv, T, W, R, seed=301)
+    q = kvc_synth.queries((nb, hq, 128), device=DEV, seed=306)
+    out, lse, sel, nbytes = run_decode(st, q, 1, n_sel)
+    assert nbytes > 0
+    flips = check_pairs(st, q, out, lse, sel, 1, n_sel, [(0, 0), (0, 1)])
+    say(f"  pairs with a flipped chunk inside the band: {flips}")
+
+
+@pytest.mark.parametrize("levels", [1, 3])
+def test_decode_selection_ties(levels):
+    """Landmarks that take only `levels` distinct rows, so most chunk scores
+    tie exactly: the kept chunks must be the oracle's (ties to the lower
+    chunk), in both the one-launch path (4100 chunks) and the workspace
+    path (21250)."""
+    for T, R in [(32800, 64), (170000, 64)]:
+        say("xkv selection ties", levels, T)
+        nb, hkv, hq, W, n_sel = 1, 2, 8, 2, 200
+        st = random_store(nb, hkv, T, W, R, seed=400 + levels)
+        nch = (T + 7) // 8
+        pick = torch.randint(0, levels, (nb, hkv, nch), generator=torch.Generator().manual_seed(levels))
+        rows = kvc_synth.queries((levels, R), device=DEV, seed=410 + levels).to(torch.bfloat16)
+        st.lk[:, :, :nch] = rows[pick.to(DEV)]
+        q = kvc_synth.queries((nb, hq, 128), device=DEV, seed=420 + levels)
+        out, lse, sel, nbytes = run_decode(st, q, 0, n_sel)
+        assert (nbytes > 0) == (T == 170000)
+        check_pairs(st, q, out, lse, sel, 0, n_sel, [(0, 0), (0, 1)], exact_sel=True)
