@@ -509,7 +509,7 @@ def xkv_leg(args, cfg, qpool, knew, vnew, steps, warm=3):
                 sr_bytes_per_call=sr_bytes,
                 full_attention_us_per_layer=round(1e3 * base, 2),
                 full_attention_ms_per_step=round(L * base, 3),
-                kernel="per layer: attn_bf16_kernel over the tail (+ merge), then xkv_fused (one workgroup per (b, j))",
+                kernel="per layer: attn_bf16_kernel over the tail (+ merge), then xkv_decode (one workgroup per (b, j))",
                 data="synthetic cross-layer low-rank caches (rank-48 shared basis + 0.1 noise)")
 
 
