@@ -1,10 +1,12 @@
 // Block-wide exact k-selection on 32-bit keys and ordered flag scans, for a
 // workgroup of NT threads (a multiple of the 64-wide wave).
 //
-// radix_select finds the k-th smallest key with four passes of 8-bit digits
-// (LDS histograms, most significant digit first); rows equal to that key
-// are taken in ascending row order, so "the k smallest, ties to the lower
-// row" is decided exactly.  Keys that share their leading digit (floats of
+// radix_select finds the k smallest keys with passes of 8-bit digits (LDS
+// histograms, most significant digit first, the first one counted by the
+// caller while it stores the keys), stopping as soon as the bin that holds
+// the k-th key is taken whole; rows tied in the last bin are taken in
+// ascending row order, so "the k smallest, ties to the lower row" is decided
+// exactly.  Keys that share their leading digit (floats of
 // one magnitude) all land in a few bins, and LDS atomics on one address are
 // serialised, so the histogram can be held in NC copies (lane l counts in
 // copy l % NC; copies are padded so that one bin of two copies sits in two
@@ -88,24 +90,33 @@ __device__ __forceinline__ uint32_t block_scan_u32(uint32_t v, RadixSmem<NT, NC>
     return off + incl - v;
 }
 
-// k-th smallest (1-based) of key(t), t < n.  Returns the key; *take gets how
-// many rows equal to it belong to the k smallest (lowest rows first).
+// The k smallest (1-based k) of key(t), t < n, ties to the lower row, as a
+// masked prefix: key u is among them when (u & mask) < prefix, or when
+// (u & mask) == prefix and it is among the first *take such rows in row
+// order (*cnt such rows exist; take == cnt keeps them all).  The caller has
+// counted every key's top 8 bits into sm.hist (copy tid % NC) and
+// synchronised; further 8-bit digits are counted here only while the bin
+// holding the k-th key is not kept whole, so keys of spread magnitudes
+// resolve in one or two passes instead of four.  Returns the prefix.
 template <int NT, int NC, typename KeyFn>
 __device__ uint32_t radix_select(int n, uint32_t k, KeyFn key, RadixSmem<NT, NC>& sm,
-                                 uint32_t* take) {
+                                 uint32_t* mask_out, uint32_t* take, uint32_t* cnt_out) {
     constexpr int PITCH = RadixSmem<NT, NC>::PITCH;
     const int tid = threadIdx.x;
     uint32_t* hist = sm.hist + (tid % NC) * PITCH;
-    uint32_t prefix = 0, mask = 0;
+    uint32_t prefix = 0, mask = 0, cnt = 0;
     for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = tid; i < NC * PITCH; i += NT) sm.hist[i] = 0;
-        __syncthreads();
+        if (shift != 24) {
+            // the previous scan read the histogram before the last barrier
+            for (int i = tid; i < NC * PITCH; i += NT) sm.hist[i] = 0;
+            __syncthreads();
 #pragma unroll 4
-        for (int t = tid; t < n; t += NT) {
-            const uint32_t u = key(t);
-            if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+            for (int t = tid; t < n; t += NT) {
+                const uint32_t u = key(t);
+                if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+            }
+            __syncthreads();
         }
-        __syncthreads();
         if (tid < WAVE) {
             // lane owns bins 4*lane .. 4*lane+3 (summed over the copies)
             uint32_t c[4], s = 0;
@@ -124,18 +135,23 @@ __device__ uint32_t radix_select(int n, uint32_t k, KeyFn key, RadixSmem<NT, NC>
                 if (run < k && k <= run + c[e]) {
                     sm.bcast[0] = 4 * tid + e;
                     sm.bcast[1] = run;
+                    sm.bcast[2] = c[e];
                 }
                 run += c[e];
             }
         }
         __syncthreads();
         const uint32_t bin = sm.bcast[0], below = sm.bcast[1];
-        __syncthreads();
+        cnt = sm.bcast[2];
         k -= below;
         prefix |= bin << shift;
         mask |= 255u << shift;
+        // bcast is written again only after two more barriers
+        if (cnt == k) break;
     }
+    *mask_out = mask;
     *take = k;
+    *cnt_out = cnt;
     return prefix;
 }
 

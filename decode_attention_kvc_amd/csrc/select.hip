@@ -15,9 +15,10 @@
 // candidate row of every slab (Philox + log1p in double: the only heavy
 // arithmetic, spread over the whole chip) into the workspace.  Then one
 // workgroup of 1024 threads per slab makes both "k best" decisions as exact
-// radix selections on 32-bit order-preserving keys: four passes of 8-bit
-// digits with LDS histograms find the k-th key; rows strictly before it are
-// in, rows equal to it are taken in ascending row order.  The row-ordered
+// radix selections on 32-bit order-preserving keys: 8-bit digits with LDS
+// histograms (the first counted while the keys are stored, further ones only
+// while the bin holding the k-th key is not taken whole) find the cut; rows
+// strictly before it are in, rows at it are taken in ascending row order.  The row-ordered
 // steps (which of the rows tied at a threshold are taken, and the ascending
 // emission of the kept rows) give each thread a contiguous run of rows and
 // need one block-wide scan of per-thread counts each, not one per 1024 rows.
@@ -94,72 +95,108 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectLaunch p) {
     uint32_t* keys = IN_LDS ? lds_keys : p.keys + (size_t)slab * p.t_len;
     const int ncand = T - p.recent_b;
 
-    // 1. N_v candidates of largest range (ties to the lower row).
-    uint32_t rthr = 0, rtake = 0;
-    if (p.n_v > 0) {
-        for (int t = tid; t < ncand; t += NT) keys[t] = range_key(range[t]);
+    // First-digit histograms are counted while the keys are stored.  Keys of
+    // one magnitude share their top byte, so a wave whose active lanes all
+    // fall in one bin adds them with a single atomic.
+    constexpr int PITCH = SelectSmem::PITCH;
+    uint32_t* hist = sm.hist + (tid % 8) * PITCH;
+    auto count_top8 = [&](uint32_t u, bool add) {
+        const uint32_t bin = u >> 24;
+        const unsigned long long want = __ballot(add);
+        if (want == 0) return;
+        const int first = __ffsll((long long)want) - 1;
+        const uint32_t b0 = (uint32_t)__builtin_amdgcn_readlane((int)bin, first);
+        const unsigned long long same = __ballot(add && bin == b0);
+        if (same == want) {
+            if ((tid % WAVE) == first) atomicAdd(&hist[b0], (uint32_t)__popcll(want));
+        } else if (add) {
+            atomicAdd(&hist[bin], 1u);
+        }
+    };
+    auto clear_hist = [&]() {
+        for (int i = tid; i < 8 * PITCH; i += NT) sm.hist[i] = 0;
         __syncthreads();
-        rthr = radix_select<NT>(ncand, (uint32_t)p.n_v, [&](int t) { return keys[t]; }, sm, &rtake);
-    }
+    };
 
-    // 2. Sampling keys over the range keys; rows before the range threshold
-    //    are protected (EXCLUDED), rows at it are marked and then protected
-    //    in row order (the first rtake of them), the others get their key.
+    // 1. N_v candidates of largest range (ties to the lower row): the range
+    //    keys below rpre under rmask, and the first rtake of those equal to
+    //    it (all rcnt of them when rtake == rcnt).
+    uint32_t rpre = 0, rmask = 0, rtake = 0, rcnt = 0;
+    if (p.n_v > 0) {
+        clear_hist();
+        for (int t = tid; t < ncand; t += NT) {
+            const uint32_t u = range_key(range[t]);
+            keys[t] = u;
+            count_top8(u, true);
+        }
+        __syncthreads();
+        rpre = radix_select<NT>(ncand, (uint32_t)p.n_v, [&](int t) { return keys[t]; }, sm,
+                                &rmask, &rtake, &rcnt);
+    }
+    const bool split_r = p.n_v > 0 && rtake != rcnt;   // some rows at the range cut are left out
+
+    // 2. Sampling keys over the range keys; rows before the range cut are
+    //    protected (EXCLUDED), rows at it too when the cut keeps them all,
+    //    else they are marked and then protected in row order (the first
+    //    rtake of them); the others get their key.
+    clear_hist();
     for (int t = tid; t < ncand; t += NT) {
         uint32_t u = kap[t];
         if (p.n_v > 0) {
-            const uint32_t rk = keys[t];
-            if (rk < rthr) u = EXCLUDED;
-            else if (rk == rthr) u = TIE_R;
+            const uint32_t rm = keys[t] & rmask;
+            if (rm < rpre) u = EXCLUDED;
+            else if (rm == rpre) u = split_r ? TIE_R : EXCLUDED;
         }
         keys[t] = u;
+        count_top8(u, u != TIE_R);        // a marked row is counted once it is resolved
     }
     __syncthreads();
-    if (p.n_v > 0) {
+    if (split_r) {
         const int c = (ncand + NT - 1) / NT, lo = min(ncand, tid * c), hi = min(ncand, lo + c);
         uint32_t n = 0;
         for (int t = lo; t < hi; ++t) n += keys[t] == TIE_R;
         uint32_t tot;
         uint32_t rank = block_scan_u32<NT>(n, sm, &tot);
         for (int t = lo; t < hi; ++t)
-            if (keys[t] == TIE_R) keys[t] = rank++ < rtake ? EXCLUDED : kap[t];
+            if (keys[t] == TIE_R) {
+                const uint32_t u = rank++ < rtake ? EXCLUDED : kap[t];
+                keys[t] = u;
+                atomicAdd(&hist[u >> 24], 1u);
+            }
         __syncthreads();
     }
 
-    // 3. K - N_v smallest sampling keys.
+    // 3. K - N_v smallest sampling keys: below kpre under kmask, and the
+    //    first ktake of those equal to it (all kcnt when ktake == kcnt).
     const uint32_t ns = (uint32_t)(p.budget_k - p.n_v);
-    uint32_t kthr = 0, ktake = 0;
-    if (ns > 0) kthr = radix_select<NT>(
-        ncand, ns, [&](int t) { return keys[t]; }, sm, &ktake);
+    uint32_t kpre = 0, kmask = 0, ktake = 0, kcnt = 0;
+    if (ns > 0)
+        kpre = radix_select<NT>(ncand, ns, [&](int t) { return keys[t]; }, sm, &kmask, &ktake, &kcnt);
 
     // 4. Emit the kept rows in ascending order: each thread owns a run of
     //    rows; its offset is the kept rows before the run (the sure ones, and
-    //    the first ktake rows tied at the sampling threshold, in row order).
+    //    the first ktake rows at the sampling cut, in row order).
     {
         const int c = (T + NT - 1) / NT, lo = min(T, tid * c), hi = min(T, lo + c);
+        auto sure = [&](int t, uint32_t u) {
+            return t >= ncand || u == EXCLUDED || (ns > 0 && (u & kmask) < kpre);
+        };
+        auto at_cut = [&](uint32_t u) { return ns > 0 && u != EXCLUDED && (u & kmask) == kpre; };
+        const bool split_k = ktake != kcnt;   // some rows at the cut are left out
         uint32_t nsure = 0, neq = 0;
         for (int t = lo; t < hi; ++t) {
-            if (t >= ncand) {
-                ++nsure;
-            } else {
-                const uint32_t u = keys[t];
-                if (u == EXCLUDED || (ns > 0 && u < kthr)) ++nsure;
-                else if (ns > 0 && u == kthr) ++neq;
-            }
+            const uint32_t u = t < ncand ? keys[t] : 0u;
+            if (sure(t, u) || (!split_k && at_cut(u))) ++nsure;
+            else if (at_cut(u)) ++neq;
         }
         uint32_t tot;
         const uint32_t sure_off = block_scan_u32<NT>(nsure, sm, &tot);
-        uint32_t eq_rank = block_scan_u32<NT>(neq, sm, &tot);
+        uint32_t eq_rank = split_k ? block_scan_u32<NT>(neq, sm, &tot) : 0u;
         uint32_t pos = sure_off + min(eq_rank, ktake);
         for (int t = lo; t < hi; ++t) {
-            bool keep;
-            if (t >= ncand) {
-                keep = true;
-            } else {
-                const uint32_t u = keys[t];
-                keep = u == EXCLUDED || (ns > 0 && u < kthr);
-                if (ns > 0 && u == kthr) keep = eq_rank++ < ktake;
-            }
+            const uint32_t u = t < ncand ? keys[t] : 0u;
+            bool keep = sure(t, u) || (!split_k && at_cut(u));
+            if (split_k && at_cut(u)) keep = eq_rank++ < ktake;
             if (keep) {
                 if (pos < (uint32_t)n_keep) kept[pos] = t;
                 ++pos;
