@@ -964,7 +964,7 @@ int kvc_xkv_decode_ws_bytes(const kvc_xkv* x, int n_q_heads, int n_select, size_
     if (n_q_heads < 1 || n_q_heads % x->n_kv_heads) return KVC_EINVAL;
     const int g = n_q_heads / x->n_kv_heads;
     if (g > XKV_MAXG) return KVC_EINVAL;
-    if (n_select < 1 || (long long)n_select * XKV_CHUNK * g > 16384) return KVC_EINVAL;
+    if (n_select < 1) return KVC_EINVAL;
     *bytes = plan_xkv_decode(x, n_select).ws_bytes;
     return KVC_OK;
 }
@@ -979,7 +979,7 @@ int kvc_xkv_decode_attn(const kvc_xkv* x, int layer, const void* q, int n_q_head
     if (n_q_heads < 1 || n_q_heads % x->n_kv_heads) return KVC_EINVAL;
     const int g = n_q_heads / x->n_kv_heads;
     if (g > XKV_MAXG) return KVC_EINVAL;
-    if (n_select < 1 || (long long)n_select * XKV_CHUNK * g > 16384) return KVC_EINVAL;
+    if (n_select < 1) return KVC_EINVAL;
     if (!isfinite(scale) || scale < 0.f) return KVC_EINVAL;
     if ((o_in == nullptr) != (lse_in == nullptr)) return KVC_EINVAL;
     if (x->nb == 0) return KVC_OK;

@@ -553,16 +553,14 @@ int kvc_xkv_factor(const kvc_cache* c, int slot0, int iters, uint64_t seed,
  * parts merge into attention over their union; lse (optional) is the
  * union's log-normaliser.  q: bf16 [nb][n_q_heads][head_dim]; out: float32
  * like o_in; selected: NULL or int32 [nb][n_kv_heads][n_select] (-1 past the
- * kept count).  n_select * chunk * g <= 16384 and the chunk keys of t_len
- * rows must fit one workgroup's LDS (KVC_EINVAL otherwise).  When the keys
- * of every (b, j) fit with the rest of the work (about 18000 chunks at rank
- * 64, 26000 at rank 32) the whole decode is one launch with one workgroup
- * per (b, j) and needs no workspace: kvc_xkv_decode_ws_bytes reports 0 and
- * ws may be NULL.  Longer stores take three launches whose chunk keys, q~
- * and row-split partials live in ws: kvc_xkv_decode_ws_bytes bytes for the
- * same store shape, head count and n_select (16-byte aligned, no
- * initialisation needed; KVC_EWORKSPACE if smaller), so calls that share a
- * workspace must be ordered.
+ * kept count).  n_select >= 1 (KVC_EINVAL otherwise).  One launch, one
+ * workgroup per (b, j).  When the chunk keys of a (b, j) fit in its LDS
+ * beside the rest of the work (about 18000 chunks at rank 64, 26000 at rank
+ * 32) no workspace is needed: kvc_xkv_decode_ws_bytes reports 0 and ws may
+ * be NULL.  Longer stores keep the keys in ws: kvc_xkv_decode_ws_bytes bytes
+ * (nb * n_kv_heads * chunks * 4) for the same store shape, head count and
+ * n_select (16-byte aligned, no initialisation needed; KVC_EWORKSPACE if
+ * smaller), so calls that share a workspace must be ordered.
  */
 int kvc_xkv_decode_attn(const kvc_xkv* x, int layer, const void* q, int n_q_heads, float scale,
                         int n_select, const float* o_in, const float* lse_in, float* out,

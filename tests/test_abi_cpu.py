@@ -382,7 +382,7 @@ def test_xkv_decode_validation():
     assert d(hq=7) == kvc.KVC_EINVAL
     assert d(hq=2 * 9) == kvc.KVC_EINVAL                         # group of 9 heads
     assert d(nsel=0) == kvc.KVC_EINVAL
-    assert d(nsel=600) == kvc.KVC_EINVAL                         # 600 * 8 * 4 > 16384
+    assert d(nsel=-3) == kvc.KVC_EINVAL
     assert d(o_in=FAKE) == kvc.KVC_EINVAL                        # lse_in missing
     assert d(q=FAKE + 2) == kvc.KVC_EALIGN
     assert d(x=xkv_desc(nb=0)) == kvc.KVC_OK
@@ -393,6 +393,8 @@ def test_xkv_decode_validation():
     assert n.value == 0
     assert L.kvc_xkv_decode_ws_bytes(ctypes.byref(x), 7, 64, ctypes.byref(n)) == kvc.KVC_EINVAL
     assert L.kvc_xkv_decode_ws_bytes(ctypes.byref(x), 8, 0, ctypes.byref(n)) == kvc.KVC_EINVAL
+    # any n_select >= 1: at most the chunk count is kept
+    assert L.kvc_xkv_decode_ws_bytes(ctypes.byref(x), 8, 600, ctypes.byref(n)) == kvc.KVC_OK
     # 25000 chunks do not fit: the workspace holds the chunk keys of every
     # (b, j); checked after the arguments
     big = xkv_desc(t_len=200000, t_cap=200000)

@@ -354,8 +354,8 @@ def run_decode(st, q, layer, n_sel):
 
 def test_decode_long_store_uses_the_workspace_path():
     """170000 rows at rank 64 (21250 chunk keys, more than one workgroup's
-    LDS holds): the three-launch decode with keys in the workspace, against
-    the oracle."""
+    LDS holds beside the rest): the chunk keys in the workspace, against the
+    oracle."""
     say("xkv decode, long store")
     nb, hkv, hq, T, W, R, n_sel = 1, 2, 8, 170000, 2, 64, 64
     st = random_store(nb, hkv, T, W, R, seed=301)
@@ -384,3 +384,33 @@ def test_decode_selection_ties(levels):
         out, lse, sel, nbytes = run_decode(st, q, 0, n_sel)
         assert (nbytes > 0) == (T == 170000)
         check_pairs(st, q, out, lse, sel, 0, n_sel, [(0, 0), (0, 1)], exact_sel=True)
+
+
+EDGE_CASES = [
+    # (nb, hkv, hq, T, W, R, n_select)
+    (1, 1, 1, 1, 2, 32, 1),          # one row, one head
+    (1, 2, 6, 7, 3, 64, 1),          # one partial chunk
+    (2, 1, 3, 9, 2, 32, 1),          # two chunks, keep one (g = 3)
+    (1, 2, 10, 17, 4, 64, 2),        # g = 5, partial last chunk kept or not
+    (1, 1, 7, 1001, 2, 32, 126),     # g = 7, ~all but a few chunks
+    (1, 2, 16, 4100, 2, 64, 513),    # g = 8, more kept chunks than the old 16384-row cap
+    (3, 2, 4, 260, 1, 64, 40),       # g = 2, window of one layer
+]
+
+
+@pytest.mark.parametrize("case", EDGE_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_decode_edge_shapes(case):
+    """Small, ragged and odd shapes of the one-launch decode (one row, one
+    partial chunk, odd head groups up to 8, every chunk or all but a few kept)
+    against the oracle for every (b, j) and every layer of the window."""
+    nb, hkv, hq, T, W, R, n_sel = case
+    say("xkv decode edge", case)
+    st = random_store(nb, hkv, T, W, R, seed=500 + T)
+    q = kvc_synth.queries((nb, hq, 128), device=DEV, seed=600 + T)
+    flips = 0
+    for layer in range(W):
+        out, lse, sel, nbytes = run_decode(st, q, layer, n_sel)
+        assert nbytes == 0
+        pairs = [(b, j) for b in range(nb) for j in range(hkv)]
+        flips += check_pairs(st, q, out, lse, sel, layer, n_sel, pairs)
+    say(f"  pairs with a flipped chunk inside the band: {flips}")
