@@ -551,6 +551,30 @@ def step_plan(ev, t0, W, S):
         s += 1
 
 
+def copy_ceiling(dev, nbytes=1 << 30, reps=5):
+    """Read + write rate of a plain device copy of nbytes, timed with HIP
+    events (the median of reps copies after one warm-up): the machine's copy
+    ceiling in this run, for comparison with the attention's read rate."""
+    import torch
+    x = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    y.copy_(x)
+    st = torch.cuda.current_stream()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        y.copy_(x)
+        b.record(st)
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    del x, y
+    torch.cuda.empty_cache()
+    ms = sorted(ts)[len(ts) // 2]
+    return dict(GBps=round(2 * nbytes / (ms * 1e-3) / 1e9, 1), bytes=2 * nbytes,
+                kernel="torch device copy: 1 GiB read + 1 GiB written, median of 5")
+
+
 def _leg(name, fn, *a, **k):
     """Run one side leg; a Python exception becomes an "error" entry so that
     the headline line is still printed."""
@@ -859,6 +883,10 @@ def main():
         xkv_res = _leg("xkv", xkv_leg, args, cfg, qpool, knew, vnew, S, warm=W)
         torch.cuda.empty_cache()
 
+    ceiling = _leg("copy_ceiling", copy_ceiling, dev)
+    if isinstance(ceiling, dict) and "GBps" in ceiling:
+        ceiling["attention_over_copy"] = round(att_gbps / ceiling["GBps"], 4)
+
     if args.copy_calibration:
         # Two plain copies of known size for scaling the memory counters:
         # a 1 GiB runtime blit, and a 512 MiB float32 copy done by a
@@ -927,6 +955,7 @@ def main():
             "bytes_per_launch": round(sum(att_bytes) / n_calls),
             "timing": "HIP events around each step's attention calls, on the stream they run on",
         },
+        "copy_ceiling": ceiling,
         "eviction": eviction,
         "eviction_passes_timed": len(passes) if ev else 0,
         "initial_pass_ms": None if initial_ms is None else round(initial_ms, 3),
