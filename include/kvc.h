@@ -34,6 +34,8 @@
  *   - Ownership: the caller allocates and owns all memory.  The library
  *     allocates nothing and keeps no state between calls; calls are
  *     reentrant.  Calls that share a workspace must be ordered on one stream.
+ *     (The one exception, kvc_decode_attn_noalloc, uses a device array the
+ *     library owns; see there.)
  *   - Alignment: cache, query and output pointers must be 16-byte aligned
  *     (KVC_EALIGN otherwise).
  *   - Sizes are element counts unless a name ends in _bytes.
@@ -312,8 +314,10 @@ int kvc_score(const kvc_cache* c, int slot, const void* q_obs, int n_q_heads,
               float* range, void* ws, size_t ws_bytes, kvc_stream_t stream);
 
 /*
- * kvc_score for a pass over some of a batch's sequences (the due ones of a
- * ragged schedule) whose window queries sit in the whole batch's arrays:
+ * Observation-window score [VASE §2.B] for a pass over some of a batch's
+ * sequences [VASE §2: each sequence evicts on its own period, so a pass
+ * covers the sequences due after a step] whose window queries sit in the
+ * whole batch's arrays:
  * call sequence b reads q_obs[i][q_idx[b]][h] and lse_obs[i][q_idx[b]][h].
  *   q_obs:   device [w][q_nb][n_q_heads][head_dim]; lse_obs [w][q_nb][n_q_heads]
  *            or NULL.
