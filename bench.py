@@ -465,8 +465,9 @@ def xkv_leg(args, cfg, qpool, knew, vnew, steps, warm=3):
     o_t = torch.empty((L, nb, hq, 128), device=dev)
     l_t = torch.empty((L, nb, hq), device=dev)
     out = torch.empty((L, nb, hq, 128), device=dev)
-    nbx = kvc.kvc_xkv_decode_ws_bytes(stores[0], hq, n_sel)   # 0: the one-launch decode
-    ws_x = torch.zeros(nbx, dtype=torch.uint8, device=dev) if nbx else None
+    # zeroed: the decode's arrival counters start at zero
+    ws_x = torch.zeros(kvc.kvc_xkv_decode_ws_bytes(stores[0], hq, n_sel), dtype=torch.uint8,
+                       device=dev)
 
     def step(s):
         tail.t_len += 1
@@ -507,7 +508,7 @@ def xkv_leg(args, cfg, qpool, knew, vnew, steps, warm=3):
                 sr_bytes_per_call=sr_bytes,
                 full_attention_us_per_layer=round(1e3 * base, 2),
                 full_attention_ms_per_step=round(L * base, 3),
-                kernel="per layer: attn_bf16_kernel over the tail (+ merge), then xkv_decode (one workgroup per (b, j))",
+                kernel="per layer: attn_bf16_kernel over the tail (+ merge), then xkv_scores + xkv_rows (two workgroups per (b, j))",
                 data="synthetic cross-layer low-rank caches (rank-48 shared basis + 0.1 noise)")
 
 

@@ -757,7 +757,8 @@ def kvc_xkv_decode_attn(store, layer, q, out, lse=None, n_select=256, scale=0.0,
                         lse_in=None, selected=None, n_q_heads=None, ws=None, stream=None):
     """q: bf16 [nb][Hq][d]; out float32 like q (o_in / lse_in: a second part
     to merge, e.g. attention over rows appended after the factorisation);
-    ws: kvc_xkv_decode_ws_bytes bytes of device memory (None when that is 0)."""
+    ws: kvc_xkv_decode_ws_bytes bytes of device memory, allocated zeroed
+    (its arrival counters start at zero; every call leaves them zero)."""
     x = store.desc()
     hq = q.shape[-2] if n_q_heads is None else n_q_heads
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()

@@ -321,25 +321,33 @@ XkvWs xkv_ws(const kvc_xkv* x) {
     return w;
 }
 
-// Decode plan: one workgroup per (b, j); the chunk keys live in LDS when
-// they fit beside the rest of the work (no workspace), else in the workspace.
+// Decode plan: two launches of `ns` workgroups per (b, j) (scores, then
+// top-k and the kept rows), enough to give every compute unit a workgroup.
+// The workspace holds the chunk keys, q~, the splits' partials and one
+// arrival counter per (b, j); the second launch keeps the keys in LDS when
+// they fit beside the rest of its work.
+constexpr int XKV_MAX_SPLIT = 8;
+
 struct XkvDecodePlan {
-    int nch, ksel;
+    int nch, ksel, ns;
     bool gkeys;
-    size_t ws_bytes, lds;
+    size_t keys_off, qt_off, part_off, arrive_off, ws_bytes, lds;
 };
 
 XkvDecodePlan plan_xkv_decode(const kvc_xkv* x, int n_select) {
     XkvDecodePlan pl;
+    const size_t slabs = (size_t)x->nb * x->n_kv_heads;
     pl.nch = (x->t_len + XKV_CHUNK - 1) / XKV_CHUNK;
     pl.ksel = std::min(n_select, pl.nch);
-    pl.lds = xkv_decode_lds(x->rank, pl.nch, pl.ksel, false);
+    pl.ns = (int)std::min<size_t>(XKV_MAX_SPLIT, std::max<size_t>(1, (CU_COUNT + slabs - 1) / std::max<size_t>(slabs, 1)));
+    pl.lds = xkv_rows_lds(x->rank, pl.nch, pl.ksel, false);
     pl.gkeys = pl.lds > XKV_DECODE_LDS_LIMIT;
-    pl.ws_bytes = 0;
-    if (pl.gkeys) {
-        pl.lds = xkv_decode_lds(x->rank, pl.nch, pl.ksel, true);
-        pl.ws_bytes = (size_t)x->nb * x->n_kv_heads * pl.nch * 4;
-    }
+    if (pl.gkeys) pl.lds = xkv_rows_lds(x->rank, pl.nch, pl.ksel, true);
+    pl.keys_off = 0;
+    pl.qt_off = align_up(slabs * pl.nch * 4, 256);
+    pl.part_off = pl.qt_off + align_up(slabs * XKV_MAXG * x->rank * 4, 256);
+    pl.arrive_off = pl.part_off + align_up(slabs * pl.ns * XKV_MAXG * (x->rank + 2) * 4, 256);
+    pl.ws_bytes = pl.arrive_off + slabs * 4;
     return pl;
 }
 
@@ -989,7 +997,7 @@ int kvc_xkv_decode_attn(const kvc_xkv* x, int layer, const void* q, int n_q_head
         return KVC_EALIGN;
     const XkvDecodePlan pl = plan_xkv_decode(x, n_select);
     if (pl.lds > XKV_DECODE_LDS_LIMIT) return KVC_EINVAL;
-    if (pl.ws_bytes && (!ws || ws_bytes < pl.ws_bytes || !aligned16(ws))) return KVC_EWORKSPACE;
+    if (!ws || ws_bytes < pl.ws_bytes || !aligned16(ws)) return KVC_EWORKSPACE;
     if (scale == 0.f) scale = 1.0f / sqrtf((float)KVC_HEAD_DIM);
     XkvDecodeLaunch p;
     memset(&p, 0, sizeof(p));
@@ -1015,7 +1023,12 @@ int kvc_xkv_decode_attn(const kvc_xkv* x, int layer, const void* q, int n_q_head
     p.out = out;
     p.lse = lse;
     p.selected = selected;
-    p.ws_keys = pl.gkeys ? static_cast<uint32_t*>(ws) : nullptr;
+    char* w = static_cast<char*>(ws);
+    p.ns = pl.ns;
+    p.ws_keys = reinterpret_cast<uint32_t*>(w + pl.keys_off);
+    p.ws_qt = reinterpret_cast<float*>(w + pl.qt_off);
+    p.ws_part = reinterpret_cast<float*>(w + pl.part_off);
+    p.ws_arrive = reinterpret_cast<unsigned*>(w + pl.arrive_off);
     if (launch_xkv_decode(p, pl.gkeys, pl.lds, (hipStream_t)stream) != hipSuccess) return KVC_EHIP;
     return hip_status();
 }

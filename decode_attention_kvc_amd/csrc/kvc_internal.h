@@ -227,7 +227,11 @@ struct XkvDecodeLaunch {
     float* out;
     float* lse;             // may be null
     int32_t* selected;      // [nb][hkv][n_select] or null
-    uint32_t* ws_keys;      // [nb][hkv][nch] chunk score keys when they do not fit in LDS
+    int ns;                 // workgroups per (b, j) in each of the two launches
+    uint32_t* ws_keys;      // [nb][hkv][nch] chunk score keys
+    float* ws_qt;           // [nb][hkv][8][rank] q~ of the first launch
+    float* ws_part;         // [nb][hkv][ns][8][rank + 2] the splits' partials
+    unsigned* ws_arrive;    // [nb][hkv] arrival counters, zero between launches
 };
 
 // Host-side launchers (defined next to their kernels).  Each returns
@@ -254,8 +258,10 @@ hipError_t launch_compact(const CompactLaunch& p, hipStream_t s);
 hipError_t launch_xkv_factor(const XkvLaunch& p, hipStream_t s);
 // The decode (one workgroup per (b, j)): dynamic LDS bytes for nch chunks
 // and ksel kept ones, with the chunk keys in LDS or (gkeys) in ws_keys.
-size_t xkv_decode_lds(int rank, int nch, int ksel, bool gkeys);
-hipError_t launch_xkv_decode(const XkvDecodeLaunch& p, bool gkeys, size_t lds, hipStream_t s);
+// LDS bytes of the decode's second launch (the first needs xkv_scores_lds).
+size_t xkv_scores_lds(int rank);
+size_t xkv_rows_lds(int rank, int nch, int ksel, bool gkeys);
+hipError_t launch_xkv_decode(const XkvDecodeLaunch& p, bool gkeys, size_t rows_lds, hipStream_t s);
 hipError_t launch_philox(int64_t n, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
                          uint32_t k1, uint32_t* out, hipStream_t s);
 

@@ -494,18 +494,8 @@ __device__ void topk_prefix(const uint32_t* keys, int n, uint32_t k, RadixSmem<N
     *cnt_out = cnt;
 }
 
-constexpr int XF_NT = 1024;            // one decode workgroup per (b, j)
+constexpr int XF_NT = 1024;            // threads of a decode workgroup
 constexpr int XF_NW = XF_NT / WAVE;
-
-// LDS floats of the decode besides the kept chunks and (when they fit) the
-// chunk keys: B_l^V rows, B_l^K (later the waves' partials), the queries,
-// q~ (later a~) and the partial sums of q~.
-__host__ __device__ constexpr int xf_area_a(int r) {
-    return D * r > XF_NW * MAXG * (r + 2) ? D * r : XF_NW * MAXG * (r + 2);
-}
-__host__ __device__ constexpr int xf_fixed_floats(int r) {
-    return D * (r + 1) + xf_area_a(r) + MAXG * D + MAXG * r + XF_NT;
-}
 
 // x ~ hi + lo with both parts in bf16 (about 16 significant bits).
 __device__ __forceinline__ void split_bf16(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
@@ -519,88 +509,107 @@ __device__ __forceinline__ void split_bf16(const float (&x)[8], bf16x8& hi, bf16
     lo = __builtin_bit_cast(bf16x8, l);
 }
 
-// Decode in one launch, grid (j, b), one workgroup of 1024 threads per (b, j):
+// Hand-off between the workgroups of one launch without a cache writeback:
+// partials are written with agent-scope stores (through to the device's
+// coherence point), every store is complete (vmcnt 0) before the workgroup
+// counts itself in, and the last workgroup to arrive reads the partials with
+// agent-scope loads, which do not hit a stale line of its own XCD's L2.  The
+// last workgroup returns the counter to zero for the next launch.
+__device__ __forceinline__ void st_coh(float* a, float x) {
+    __hip_atomic_store(a, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coh(const float* a) {
+    return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool arrive_last(unsigned* ctr, int n) {
+    __shared__ int last;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned old =
+            __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = old == (unsigned)n - 1;
+        if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    return last;
+}
+
+// LDS floats of the score launch: B_l^K [D][R], the queries [MAXG][D], q~
+// [MAXG][R] and the partial sums of q~ [NT].
+__host__ __device__ constexpr int xs_floats(int r) { return D * r + MAXG * D + MAXG * r + XF_NT; }
+// LDS floats of the row launch besides the kept chunks and (when they fit)
+// the chunk keys: B_l^V rows [D][R + 1], the waves' partials [NW][MAXG][R + 2],
+// a~ [MAXG][R].
+__host__ __device__ constexpr int xr_floats(int r) {
+    return D * (r + 1) + XF_NW * MAXG * (r + 2) + MAXG * r;
+}
+
+// Decode, first launch, grid (split, j, b), 1024 threads: the chunk score
+// keys of split s's share of the (b, j) landmarks (contiguous runs of
+// 16-chunk blocks).
 //  0. B_l^K and the queries are read (every wave's reads queued before the
-//     landmark stream), then the first round of landmark rows and B_l^V;
+//     landmark stream), then the first round of landmark rows;
 //  1. q~_h = B_l q_h (from LDS), held as bf16 hi + lo fragments: for 16x32
 //     operands the A fragment of q~ (heads x ranks) and the B fragment of
-//     q~^T (ranks x heads) are the same registers;
+//     q~^T (ranks x heads) are the same registers; split 0 stores q~ in the
+//     workspace for the second launch;
 //  2. chunk scores S = q~ L^T on v_mfma_f32_16x16x32_bf16, 16 chunks per
 //     product (heads padded to 16), max over the heads, order-preserving keys
-//     into LDS (GKEYS: into the workspace, for stores whose keys do not fit);
-//  3. the exact top-k of the keys (topk_prefix, its first digit counted while
-//     the keys are stored), emitted in chunk order;
-//  4. per 32 kept rows (4 chunks): S^T = A_K q~^T with the kept rows loaded
-//     in the order that makes each lane's S^T fragment its P^T operand (the
-//     8 rows of chunk lg), an online softmax whose reference maximum moves
-//     only when a logit exceeds it by more than 8 (log2 units), P split into
-//     bf16 hi + lo, and a~^T += A_V^T P^T, A_V stored chunk-transposed
-//     ([chunk][rank][8 rows]) so that the A operand is one 16-byte load;
-//  5. the waves' (reference, sum, a~) merge through LDS, then
-//     o_h = B_l^V a~_h / z_h per (head, channel), merged with the second part
-//     when one is given.
-template <int R, bool GKEYS>
-__global__ __launch_bounds__(XF_NT) void xkv_decode(XkvDecodeLaunch p) {
+//     into the workspace.
+template <int R>
+__global__ __launch_bounds__(XF_NT) void xkv_scores(XkvDecodeLaunch p) {
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ RadixSmem<XF_NT, 8> rs;
-    __shared__ float hz[MAXG], hm[MAXG];
     constexpr int NT = XF_NT, NW = XF_NW;
     constexpr int KS = R / 32;           // 32-rank k-steps
-    constexpr int RBK = R / 16;          // 16-rank blocks of a~^T
     constexpr int UNB = 4;               // 16-chunk landmark blocks per wave and round
-    constexpr int BVP = R + 1;           // float pitch of the staged B_l^V rows
     constexpr int BPT = D * R / 4 / NT;  // float4 per thread of one B matrix
     constexpr int NPART = NT / (MAXG * R);
     static_assert(BPT >= 1 && NPART >= 1 && D % NPART == 0 && MAXG * D == NT, "launch shape");
-    const int j = blockIdx.x, b = blockIdx.y;
+    const int sp = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int slab = b * p.hkv + j, g = p.g;
     const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
     const int l16 = lane & 15, lg = lane >> 4;
     const int T = p.t_len, nch = (T + CHUNK - 1) / CHUNK;
-    const int ksel = min(p.n_select, nch);
     const int n = p.window * D;
+    const int nlb = (nch + 15) / 16;                              // 16-chunk blocks
+    const int per = (nlb + p.ns - 1) / p.ns;
+    const int lb0 = sp * per, nl = max(0, min(nlb, lb0 + per) - lb0);   // this split's blocks
+    const int nlr = (nl + NW * UNB - 1) / (NW * UNB);             // rounds
 
-    float* bvs = reinterpret_cast<float*>(smem);                  // [D][R + 1]
-    float* area = bvs + D * BVP;                                  // B_l^K [D][R], later partials
-    float* qs = area + xf_area_a(R);                              // [MAXG][D] queries
-    float* qt = qs + MAXG * D;                                    // [MAXG][R] q~, later a~
+    float* area = reinterpret_cast<float*>(smem);                 // B_l^K [D][R]
+    float* qs = area + D * R;                                     // [MAXG][D] queries
+    float* qt = qs + MAXG * D;                                    // [MAXG][R] q~
     float* qpart = qt + MAXG * R;                                 // [NT] partial sums of q~
-    int32_t* sel = reinterpret_cast<int32_t*>(qpart + NT);        // [ksel] kept chunks
-    uint32_t* keys = GKEYS ? p.ws_keys + (size_t)slab * nch       // [nch]
-                           : reinterpret_cast<uint32_t*>(sel + ksel);
+    uint32_t* keys = p.ws_keys + (size_t)slab * nch;
 
     // 0. global reads
     const float* BK = p.bk + (size_t)slab * n * R + (size_t)p.layer * D * R;
-    const float* BV = p.bv + (size_t)slab * n * R + (size_t)p.layer * D * R;
-    f32x4 bkr[BPT], bvr[BPT];
+    f32x4 bkr[BPT];
 #pragma unroll
     for (int e = 0; e < BPT; ++e) bkr[e] = *reinterpret_cast<const f32x4*>(BK + 4 * (tid + e * NT));
-    const size_t row0 = (size_t)b * p.hq + (size_t)j * g;        // first output row of (b, j)
+    const size_t row0 = (size_t)b * p.hq + (size_t)j * g;        // first query row of (b, j)
     const bool qok = tid < g * D;                                 // (head tid / D, channel tid % D)
     // loads are unconditional (clamped addresses, results selected after), so
     // that the compiler's wait counts cover only the older loads
     const uint16_t qraw = reinterpret_cast<const uint16_t*>(p.q)[row0 * D + (qok ? tid : 0)];
-    for (int i = tid; i < (1 << TOPK_B0); i += NT) rs.hist[i] = 0;   // first selection digit
     // every wave's reads for q~ are queued ahead of the landmark stream
     __syncthreads();
     const uint16_t* L = reinterpret_cast<const uint16_t*>(p.lk) + (size_t)slab * (p.x_tcap / CHUNK) * R;
-    const int nlb = (nch + 15) / 16;                              // 16-chunk blocks
-    const int nlr = (nlb + NW * UNB - 1) / (NW * UNB);            // rounds
     // B fragment of L^T: chunk 16 blk + l16, ranks 32 ks + 8 lg .. +8
+    auto chunk_of = [&](int r, int u) { return (lb0 + (r * UNB + u) * NW + wave) * 16 + l16; };
+    auto in_split = [&](int r, int u) { return (r * UNB + u) * NW + wave < nl; };
     auto load_lm = [&](u32x4 (&w)[UNB][KS], int r) {
 #pragma unroll
         for (int u = 0; u < UNB; ++u) {
-            const int ch = ((r * UNB + u) * NW + wave) * 16 + l16;
-            const int chc = ch < nch ? ch : 0;   // in bounds: lk holds t_cap / 8 >= 8 rows
+            const int ch = chunk_of(r, u);
+            const int chc = in_split(r, u) && ch < nch ? ch : 0;   // lk holds t_cap / 8 >= 8 rows
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) w[u][ks] = load16(L + (size_t)chc * R + 32 * ks + 8 * lg);
         }
     };
     u32x4 la[UNB][KS], lb[UNB][KS];
     load_lm(la, 0);
-    // B_l^V and the second part are needed at the end only
-#pragma unroll
-    for (int e = 0; e < BPT; ++e) bvr[e] = *reinterpret_cast<const f32x4*>(BV + 4 * (tid + e * NT));
 #pragma unroll
     for (int e = 0; e < BPT; ++e) *reinterpret_cast<f32x4*>(area + 4 * (tid + e * NT)) = bkr[e];
     qs[tid] = qok ? bf16_to_f32(qraw) : 0.f;
@@ -621,6 +630,7 @@ __global__ __launch_bounds__(XF_NT) void xkv_decode(XkvDecodeLaunch p) {
 #pragma unroll
         for (int part = 0; part < NPART; ++part) a += qpart[part * MAXG * R + tid];
         qt[tid] = a;
+        if (sp == 0) p.ws_qt[(size_t)slab * MAXG * R + tid] = a;
     }
     __syncthreads();
     bf16x8 qh[KS], ql[KS];               // head l16, ranks 32 ks + 8 lg .. +8
@@ -649,12 +659,8 @@ __global__ __launch_bounds__(XF_NT) void xkv_decode(XkvDecodeLaunch p) {
             for (int i = 0; i < 4; ++i)
                 if (4 * lg + i < g) best = fmaxf(best, S[i]);
             best = fmaxf(best, __shfl_xor(best, 16));            // heads 4..7 into lanes lg = 0
-            const int ch = ((r * UNB + u) * NW + wave) * 16 + l16;
-            if (lg == 0 && ch < nch) {
-                const uint32_t key = desc_key(best);
-                keys[ch] = key;
-                atomicAdd(&rs.hist[key >> (32 - TOPK_B0)], 1u);
-            }
+            const int ch = chunk_of(r, u);
+            if (lg == 0 && in_split(r, u) && ch < nch) keys[ch] = desc_key(best);
         }
     };
     // Branch-free rounds: a round past the last one loads row 0 of the
@@ -666,17 +672,80 @@ __global__ __launch_bounds__(XF_NT) void xkv_decode(XkvDecodeLaunch p) {
         score_lm(lb, r + 1);
         load_lm(lb, r + 3);
     }
+}
+
+// Decode, second launch, grid (split, j, b), 1024 threads:
+//  3. the chunk keys of (b, j) are read (into LDS when they fit) while their
+//     first digit is counted, and the exact top-k of the keys (topk_prefix)
+//     is emitted in chunk order, by every split alike;
+//  4. per 32 kept rows (4 chunks; blocks split, split + ns, ... are this
+//     split's): S^T = A_K q~^T with the kept rows loaded in the order that
+//     makes each lane's S^T fragment its P^T operand (the 8 rows of chunk
+//     lg), an online softmax whose reference maximum moves only when a
+//     logit exceeds it by more than 8 (log2 units), P split into bf16 hi +
+//     lo, and a~^T += A_V^T P^T, A_V stored chunk-transposed
+//     ([chunk][rank][8 rows]) so that the A operand is one 16-byte load;
+//  5. the waves' (reference, sum, a~) merge through LDS into the split's
+//     partial; the last split of (b, j) to finish merges the partials, forms
+//     o_h = B_l^V a~_h / z_h per (head, channel) and merges it with the
+//     second part when one is given.
+template <int R, bool GKEYS>
+__global__ __launch_bounds__(XF_NT) void xkv_rows(XkvDecodeLaunch p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ RadixSmem<XF_NT, 8> rs;
+    __shared__ float hz[MAXG], hm[MAXG];
+    constexpr int NT = XF_NT, NW = XF_NW;
+    constexpr int KS = R / 32;           // 32-rank k-steps
+    constexpr int RBK = R / 16;          // 16-rank blocks of a~^T
+    constexpr int BVP = R + 1;           // float pitch of the staged B_l^V rows
+    constexpr int PP = MAXG * (R + 2);   // floats of one split's partial
+    static_assert(MAXG * D == NT, "launch shape");
+    const int sp = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+    const int slab = b * p.hkv + j, g = p.g, ns = p.ns;
+    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int T = p.t_len, nch = (T + CHUNK - 1) / CHUNK;
+    const int ksel = min(p.n_select, nch);
+    const int n = p.window * D;
+
+    float* bvs = reinterpret_cast<float*>(smem);                  // [D][R + 1]
+    float* wp = bvs + D * BVP;                                    // [NW][MAXG][R + 2]
+    float* qt = wp + NW * PP;                                     // [MAXG][R] a~
+    int32_t* sel = reinterpret_cast<int32_t*>(qt + MAXG * R);     // [ksel] kept chunks
+    const uint32_t* gkeys = p.ws_keys + (size_t)slab * nch;
+    uint32_t* lkeys = reinterpret_cast<uint32_t*>(sel + ksel);    // [nch] when !GKEYS
+    const uint32_t* keys = GKEYS ? gkeys : lkeys;
+
+    // q~ fragments (head l16, ranks 32 ks + 8 lg .. +8) from the first launch
+    bf16x8 qh[KS], ql[KS];
+    {
+        const float* qg = p.ws_qt + (size_t)slab * MAXG * R;
 #pragma unroll
-    for (int e = 0; e < BPT; ++e) {
-        const int x = 4 * (tid + e * NT);
+        for (int ks = 0; ks < KS; ++ks) {
+            float x[8];
+            const int hh = l16 < MAXG ? l16 : 0;
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(qg + hh * R + 32 * ks + 8 * lg);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(qg + hh * R + 32 * ks + 8 * lg + 4);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) bvs[((x + c) / R) * BVP + (x + c) % R] = bvr[e][c];
+            for (int e = 0; e < 4; ++e) {
+                x[e] = l16 < MAXG ? x0[e] : 0.f;
+                x[4 + e] = l16 < MAXG ? x1[e] : 0.f;
+            }
+            split_bf16(x, qh[ks], ql[ks]);
+        }
     }
-    __syncthreads();
 
     // 3. the ksel best chunks in ascending chunk order (all of them when
     // there are fewer): thread t owns chunks [t*per, (t+1)*per)
     if (ksel < nch) {
+        for (int i = tid; i < (1 << TOPK_B0); i += NT) rs.hist[i] = 0;
+        __syncthreads();
+        for (int ch = tid; ch < nch; ch += NT) {
+            const uint32_t key = gkeys[ch];
+            if constexpr (!GKEYS) lkeys[ch] = key;
+            atomicAdd(&rs.hist[key >> (32 - TOPK_B0)], 1u);
+        }
+        __syncthreads();
         uint32_t prefix, mask, take, cnt;
         topk_prefix<NT, 8>(keys, nch, (uint32_t)ksel, rs, &prefix, &mask, &take, &cnt);
         const int per = (nch + NT - 1) / NT;
@@ -707,11 +776,11 @@ __global__ __launch_bounds__(XF_NT) void xkv_decode(XkvDecodeLaunch p) {
         for (int ch = tid; ch < nch; ch += NT) sel[ch] = ch;
     }
     __syncthreads();
-    if (p.selected)
+    if (p.selected && sp == 0)
         for (int x = tid; x < p.n_select; x += NT)
             p.selected[(size_t)slab * p.n_select + x] = x < ksel ? sel[x] : -1;
 
-    // 4. kept rows, 32 (4 chunks) per block, blocks wave, wave + NW, ...
+    // 4. kept rows, 32 (4 chunks) per block; block k is split k % ns's
     const uint16_t* AK = reinterpret_cast<const uint16_t*>(p.ak) + (size_t)slab * p.x_tcap * R;
     const uint16_t* AV = reinterpret_cast<const uint16_t*>(p.av) + (size_t)slab * p.x_tcap * R;
     const float scale2 = p.scale * LOG2E;
@@ -804,12 +873,9 @@ __global__ __launch_bounds__(XF_NT) void xkv_decode(XkvDecodeLaunch p) {
             acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(X.v[rb]), pL, acc[rb], 0, 0, 0);
         }
     };
-    // the second part, read while the kept rows stream
-    const float o2 = (qok && p.o_in) ? p.o_in[row0 * D + tid] : 0.f;
-    const float l2 = (qok && p.o_in) ? p.lse_in[row0 + tid / D] : -INFINITY;
     // one block in flight per wave (sixteen waves: 128 KB per workgroup); a
     // second register set would not fit beside the accumulators
-    for (int k = wave; k < nblk; k += NW) {
+    for (int k = sp + ns * wave; k < nblk; k += ns * NW) {
         RowRegs X;
         load_blk(X, k);
         compute_blk(X, k);
@@ -818,7 +884,6 @@ __global__ __launch_bounds__(XF_NT) void xkv_decode(XkvDecodeLaunch p) {
     // 5. the waves' partials (every lane of head l16 shares its reference)
     zl += __shfl_xor(zl, 16);
     zl += __shfl_xor(zl, 32);
-    float* wp = area;                                             // [NW][MAXG][R + 2]
     if (l16 < g) {
         float* d = wp + (wave * MAXG + l16) * (R + 2);
 #pragma unroll
@@ -831,6 +896,8 @@ __global__ __launch_bounds__(XF_NT) void xkv_decode(XkvDecodeLaunch p) {
         }
     }
     __syncthreads();
+    // this split's partial: [MAXG][R + 2] = (a~ [R], reference, sum) per head
+    float* part = p.ws_part + (size_t)slab * ns * PP;
     for (int x = tid; x < g * (R + 1); x += NT) {
         const int h = x / (R + 1), c = x % (R + 1);
         float M = -INFINITY;
@@ -840,6 +907,35 @@ __global__ __launch_bounds__(XF_NT) void xkv_decode(XkvDecodeLaunch p) {
             const float* d = wp + (w2 * MAXG + h) * (R + 2);
             const float f = d[R] == -INFINITY ? 0.f : exp2f(d[R] - M);   // a wave without rows
             sum = f == 0.f ? sum : fmaf(f, d[c < R ? c : R + 1], sum);
+        }
+        float* dst = part + (size_t)sp * PP + h * (R + 2);
+        if (c < R) {
+            st_coh(dst + c, sum);
+        } else {
+            st_coh(dst + R, M);
+            st_coh(dst + R + 1, sum);
+        }
+    }
+    if (!arrive_last(p.ws_arrive + slab, ns)) return;
+
+    // The last split of (b, j): B_l^V, the splits' partials merged, output.
+    const float* BV = p.bv + (size_t)slab * n * R + (size_t)p.layer * D * R;
+    for (int x = tid; x < D * R; x += NT) bvs[(x / R) * BVP + x % R] = BV[x];
+    const size_t row0 = (size_t)b * p.hq + (size_t)j * g;        // first output row of (b, j)
+    const bool qok = tid < g * D;                                 // (head tid / D, channel tid % D)
+    const float o2 = (qok && p.o_in) ? p.o_in[row0 * D + tid] : 0.f;
+    const float l2 = (qok && p.o_in) ? p.lse_in[row0 + tid / D] : -INFINITY;
+    for (int x = tid; x < g * (R + 1); x += NT) {
+        const int h = x / (R + 1), c = x % (R + 1);
+        float M = -INFINITY;
+        for (int s2 = 0; s2 < ns; ++s2) M = fmaxf(M, ld_coh(part + (size_t)s2 * PP + h * (R + 2) + R));
+        float sum = 0.f;
+        for (int s2 = 0; s2 < ns; ++s2) {
+            const float* d = part + (size_t)s2 * PP + h * (R + 2);
+            const float ms = ld_coh(d + R);
+            const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);       // a split without rows
+            const float v = ld_coh(d + (c < R ? c : R + 1));
+            sum = f == 0.f ? sum : fmaf(f, v, sum);
         }
         if (c < R) {
             qt[h * R + c] = sum;
@@ -906,21 +1002,31 @@ hipError_t launch_xkv_factor(const XkvLaunch& p, hipStream_t st) {
     return hipGetLastError();
 }
 
-size_t xkv_decode_lds(int rank, int nch, int ksel, bool gkeys) {
-    return ((size_t)xf_fixed_floats(rank) + ksel + (gkeys ? 0 : nch)) * 4;
+size_t xkv_scores_lds(int rank) { return (size_t)xs_floats(rank) * 4; }
+
+size_t xkv_rows_lds(int rank, int nch, int ksel, bool gkeys) {
+    return ((size_t)xr_floats(rank) + ksel + (gkeys ? 0 : nch)) * 4;
 }
 
-hipError_t launch_xkv_decode(const XkvDecodeLaunch& p, bool gkeys, size_t lds, hipStream_t st) {
-    const dim3 grid(p.hkv, p.nb);
-    auto go = [&](auto kern) {
+hipError_t launch_xkv_decode(const XkvDecodeLaunch& p, bool gkeys, size_t rows_lds, hipStream_t st) {
+    const dim3 grid(p.ns, p.hkv, p.nb);
+    auto go = [&](auto kern, size_t lds) {
         if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
             return hipErrorInvalidValue;
         hipLaunchKernelGGL(kern, grid, dim3(XF_NT), lds, st, p);
         return hipGetLastError();
     };
-    if (p.rank == 32) return gkeys ? go(xkv_decode<32, true>) : go(xkv_decode<32, false>);
-    return gkeys ? go(xkv_decode<64, true>) : go(xkv_decode<64, false>);
+    const size_t slds = xkv_scores_lds(p.rank);
+    hipError_t e;
+    if (p.rank == 32) {
+        e = go(xkv_scores<32>, slds);
+        if (e == hipSuccess) e = gkeys ? go(xkv_rows<32, true>, rows_lds) : go(xkv_rows<32, false>, rows_lds);
+    } else {
+        e = go(xkv_scores<64>, slds);
+        if (e == hipSuccess) e = gkeys ? go(xkv_rows<64, true>, rows_lds) : go(xkv_rows<64, false>, rows_lds);
+    }
+    return e;
 }
 
 }  // namespace kvc

@@ -557,14 +557,15 @@ int kvc_xkv_factor(const kvc_cache* c, int slot0, int iters, uint64_t seed,
  * parts merge into attention over their union; lse (optional) is the
  * union's log-normaliser.  q: bf16 [nb][n_q_heads][head_dim]; out: float32
  * like o_in; selected: NULL or int32 [nb][n_kv_heads][n_select] (-1 past the
- * kept count).  n_select >= 1 (KVC_EINVAL otherwise).  One launch, one
- * workgroup per (b, j).  When the chunk keys of a (b, j) fit in its LDS
- * beside the rest of the work (about 18000 chunks at rank 64, 26000 at rank
- * 32) no workspace is needed: kvc_xkv_decode_ws_bytes reports 0 and ws may
- * be NULL.  Longer stores keep the keys in ws: kvc_xkv_decode_ws_bytes bytes
- * (nb * n_kv_heads * chunks * 4) for the same store shape, head count and
- * n_select (16-byte aligned, no initialisation needed; KVC_EWORKSPACE if
- * smaller), so calls that share a workspace must be ordered.
+ * kept count).  n_select >= 1 (KVC_EINVAL otherwise).  Two launches of
+ * one to eight workgroups per (b, j): the chunk scores, then the top-k and
+ * the kept rows, whose partials the last workgroup of each (b, j) merges.
+ * ws: kvc_xkv_decode_ws_bytes bytes for the same store shape, head count and
+ * n_select (16-byte aligned; KVC_EWORKSPACE if NULL or smaller).  It holds
+ * the chunk keys, q~, the partials and one arrival counter per (b, j) at its
+ * end: the counters must be zero before the first call that uses the
+ * workspace (allocate it zeroed) and every completed call leaves them zero.
+ * Calls that share a workspace must be ordered (one stream).
  */
 int kvc_xkv_decode_attn(const kvc_xkv* x, int layer, const void* q, int n_q_heads, float scale,
                         int n_select, const float* o_in, const float* lse_in, float* out,
@@ -572,8 +573,7 @@ int kvc_xkv_decode_attn(const kvc_xkv* x, int layer, const void* q, int n_q_head
                         kvc_stream_t stream);
 
 /* Workspace bytes kvc_xkv_decode_attn needs for this store shape, query head
- * count and n_select (same argument checks as the call); 0 for the
- * one-launch decode. */
+ * count and n_select (same argument checks as the call). */
 int kvc_xkv_decode_ws_bytes(const kvc_xkv* x, int n_q_heads, int n_select, size_t* bytes);
 
 /*

@@ -386,23 +386,36 @@ def test_xkv_decode_validation():
     assert d(o_in=FAKE) == kvc.KVC_EINVAL                        # lse_in missing
     assert d(q=FAKE + 2) == kvc.KVC_EALIGN
     assert d(x=xkv_desc(nb=0)) == kvc.KVC_OK
-    # a store whose chunk keys fit in LDS decodes in one launch without a
-    # workspace (a null one is accepted)
+    # the workspace: chunk keys, q~, the splits' partials and one arrival
+    # counter per (b, j), each part 256-byte aligned; ns = min(8, ceil(256 /
+    # slabs)) workgroups per (b, j)
+    def ws_expect(nb, hkv, t_len, rank):
+        al = lambda v: (v + 255) // 256 * 256
+        slabs = nb * hkv
+        ns = min(8, -(-256 // slabs))
+        nch = (t_len + 7) // 8
+        return (al(slabs * nch * 4) + al(slabs * 8 * rank * 4)
+                + al(slabs * ns * 8 * (rank + 2) * 4) + slabs * 4)
     n = ctypes.c_size_t()
     assert L.kvc_xkv_decode_ws_bytes(ctypes.byref(x), 8, 64, ctypes.byref(n)) == kvc.KVC_OK
-    assert n.value == 0
+    assert n.value == ws_expect(1, 2, 100, 64)
+    assert d(wsb=n.value - 1) == kvc.KVC_EWORKSPACE
+    assert d(ws=None) == kvc.KVC_EWORKSPACE
     assert L.kvc_xkv_decode_ws_bytes(ctypes.byref(x), 7, 64, ctypes.byref(n)) == kvc.KVC_EINVAL
     assert L.kvc_xkv_decode_ws_bytes(ctypes.byref(x), 8, 0, ctypes.byref(n)) == kvc.KVC_EINVAL
     # any n_select >= 1: at most the chunk count is kept
     assert L.kvc_xkv_decode_ws_bytes(ctypes.byref(x), 8, 600, ctypes.byref(n)) == kvc.KVC_OK
-    # 25000 chunks do not fit: the workspace holds the chunk keys of every
-    # (b, j); checked after the arguments
+    # 25000 chunks (their keys read from the workspace, not LDS); checked
+    # after the arguments
     big = xkv_desc(t_len=200000, t_cap=200000)
     assert L.kvc_xkv_decode_ws_bytes(ctypes.byref(big), 8, 64, ctypes.byref(n)) == kvc.KVC_OK
-    assert n.value == 2 * 25000 * 4
+    assert n.value == ws_expect(1, 2, 200000, 64)
     assert d(x=big, wsb=n.value - 1) == kvc.KVC_EWORKSPACE
     assert d(x=big, ws=None) == kvc.KVC_EWORKSPACE
     assert d(x=big, ws=FAKE + 4) == kvc.KVC_EWORKSPACE
+    x16 = xkv_desc(nb=16, n_kv_heads=8, rank=32, t_len=32768, t_cap=32768)
+    assert L.kvc_xkv_decode_ws_bytes(ctypes.byref(x16), 32, 256, ctypes.byref(n)) == kvc.KVC_OK
+    assert n.value == ws_expect(16, 8, 32768, 32)
     assert d(x=big, ws=None, hq=7) == kvc.KVC_EINVAL
 
 

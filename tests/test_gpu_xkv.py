@@ -345,23 +345,21 @@ def run_decode(st, q, layer, n_sel):
     out = torch.full((nb, hq, 128), float("nan"), device=DEV)
     lse = torch.full((nb, hq), float("nan"), device=DEV)
     sel = torch.full((nb, st.n_kv_heads, n_sel), -7, dtype=torch.int32, device=DEV)
-    nbytes = kvc.kvc_xkv_decode_ws_bytes(st, hq, n_sel)
-    kvc.kvc_xkv_decode_attn(st, layer, q, out, lse, n_select=n_sel, selected=sel,
-                            ws=ws_tensor(nbytes) if nbytes else None)
+    ws = ws_tensor(kvc.kvc_xkv_decode_ws_bytes(st, hq, n_sel))
+    kvc.kvc_xkv_decode_attn(st, layer, q, out, lse, n_select=n_sel, selected=sel, ws=ws)
     torch.cuda.synchronize()
-    return out, lse, sel, nbytes
+    return out, lse, sel
 
 
 def test_decode_long_store_uses_the_workspace_path():
     """170000 rows at rank 64 (21250 chunk keys, more than one workgroup's
-    LDS holds beside the rest): the chunk keys in the workspace, against the
-    oracle."""
+    LDS holds beside the rest): the top-k reads the chunk keys from the
+    workspace instead of LDS, against the oracle."""
     say("xkv decode, long store")
     nb, hkv, hq, T, W, R, n_sel = 1, 2, 8, 170000, 2, 64, 64
     st = random_store(nb, hkv, T, W, R, seed=301)
     q = kvc_synth.queries((nb, hq, 128), device=DEV, seed=306)
-    out, lse, sel, nbytes = run_decode(st, q, 1, n_sel)
-    assert nbytes > 0
+    out, lse, sel = run_decode(st, q, 1, n_sel)
     flips = check_pairs(st, q, out, lse, sel, 1, n_sel, [(0, 0), (0, 1)])
     say(f"  pairs with a flipped chunk inside the band: {flips}")
 
@@ -370,8 +368,8 @@ def test_decode_long_store_uses_the_workspace_path():
 def test_decode_selection_ties(levels):
     """Landmarks that take only `levels` distinct rows, so most chunk scores
     tie exactly: the kept chunks must be the oracle's (ties to the lower
-    chunk), in both the one-launch path (4100 chunks) and the workspace
-    path (21250)."""
+    chunk), with the keys in LDS (4100 chunks) and read from the workspace
+    (21250)."""
     for T, R in [(32800, 64), (170000, 64)]:
         say("xkv selection ties", levels, T)
         nb, hkv, hq, W, n_sel = 1, 2, 8, 2, 200
@@ -381,8 +379,7 @@ def test_decode_selection_ties(levels):
         rows = kvc_synth.queries((levels, R), device=DEV, seed=410 + levels).to(torch.bfloat16)
         st.lk[:, :, :nch] = rows[pick.to(DEV)]
         q = kvc_synth.queries((nb, hq, 128), device=DEV, seed=420 + levels)
-        out, lse, sel, nbytes = run_decode(st, q, 0, n_sel)
-        assert (nbytes > 0) == (T == 170000)
+        out, lse, sel = run_decode(st, q, 0, n_sel)
         check_pairs(st, q, out, lse, sel, 0, n_sel, [(0, 0), (0, 1)], exact_sel=True)
 
 
@@ -400,7 +397,7 @@ EDGE_CASES = [
 
 @pytest.mark.parametrize("case", EDGE_CASES, ids=lambda c: "x".join(map(str, c)))
 def test_decode_edge_shapes(case):
-    """Small, ragged and odd shapes of the one-launch decode (one row, one
+    """Small, ragged and odd shapes of the decode (one row, one
     partial chunk, odd head groups up to 8, every chunk or all but a few kept)
     against the oracle for every (b, j) and every layer of the window."""
     nb, hkv, hq, T, W, R, n_sel = case
@@ -409,8 +406,7 @@ def test_decode_edge_shapes(case):
     q = kvc_synth.queries((nb, hq, 128), device=DEV, seed=600 + T)
     flips = 0
     for layer in range(W):
-        out, lse, sel, nbytes = run_decode(st, q, layer, n_sel)
-        assert nbytes == 0
+        out, lse, sel = run_decode(st, q, layer, n_sel)
         pairs = [(b, j) for b in range(nb) for j in range(hkv)]
         flips += check_pairs(st, q, out, lse, sel, layer, n_sel, pairs)
     say(f"  pairs with a flipped chunk inside the band: {flips}")
