@@ -34,7 +34,7 @@ EXPORTS = (
     "kvc_compact", "kvc_philox_words", "kvc_dkv_ws_bytes", "kvc_dkv_score",
     "kvc_gaussian_bf16", "kvc_q8_quantize", "kvc_q8_append", "kvc_q8_decode_attn_ws_bytes",
     "kvc_q8_decode_attn", "kvc_xkv_factor_ws_bytes", "kvc_xkv_factor", "kvc_xkv_decode_ws_bytes",
-    "kvc_xkv_decode_attn",
+    "kvc_xkv_decode_attn", "kvc_read_probe",
 )
 
 
@@ -110,6 +110,7 @@ def lib():
             "kvc_compact": ([cp, i32, vp, i32, cp, vp], i32),
             "kvc_philox_words": ([i64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
                                   ctypes.c_uint64, vp, vp], i32),
+            "kvc_read_probe": ([vp, sz, vp, vp], i32),
             "kvc_dkv_ws_bytes": ([cp, i32, szp], i32),
             "kvc_dkv_score": ([cp, i32, vp, i32, vp, vp, vp, sz, vp], i32),
             "kvc_gaussian_bf16": ([i64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, vp,
@@ -653,6 +654,23 @@ def kvc_compact(src, slot, kept, n_keep, dst, stream=None):
 def kvc_philox_words(n, c1, c2, c3, seed, out, stream=None):
     _check(lib().kvc_philox_words(n, c1, c2, c3, int(seed) & (2**64 - 1), _ptr(out),
                                   _stream(stream)), "kvc_philox_words")
+
+
+PROBE_BLOCKS = 256
+
+
+def kvc_read_probe(buf, out, stream=None):
+    """Stream the device tensor buf once (its bytes, a multiple of 16) and
+    write one XOR checksum word per probe workgroup into out (device int32 or
+    uint32, PROBE_BLOCKS elements)."""
+    nbytes = buf.numel() * buf.element_size()
+    _on_device(buf=buf, out=out)
+    if not buf.is_contiguous():
+        raise ValueError("kvc_read_probe: buf must be contiguous")
+    if out.dtype not in (torch.int32, torch.uint32) or not out.is_contiguous() \
+            or out.numel() < PROBE_BLOCKS:
+        raise ValueError(f"kvc_read_probe: out must be {PROBE_BLOCKS} contiguous 32-bit words")
+    _check(lib().kvc_read_probe(_ptr(buf), nbytes, _ptr(out), _stream(stream)), "kvc_read_probe")
 
 
 def kvc_dkv_ws_bytes(cache, rank):

@@ -1044,6 +1044,14 @@ int kvc_gaussian_bf16(int64_t n, uint64_t seed, uint32_t c1, uint32_t c2, void* 
     return hip_status();
 }
 
+int kvc_read_probe(const void* buf, size_t bytes, uint32_t* out, kvc_stream_t stream) {
+    static_assert(KVC_PROBE_BLOCKS == PROBE_BLOCKS, "probe grid");
+    if (bytes % 16) return KVC_EINVAL;
+    if (!aligned4(out) || (bytes && !aligned16(buf))) return KVC_EALIGN;
+    if (launch_read_probe(buf, bytes, out, (hipStream_t)stream) != hipSuccess) return KVC_EHIP;
+    return hip_status();
+}
+
 int kvc_philox_words(int64_t n, uint32_t c1, uint32_t c2, uint32_t c3, uint64_t seed,
                      uint32_t* out, kvc_stream_t stream) {
     if (n < 0 || n > (int64_t)1 << 32) return KVC_EINVAL;

@@ -242,6 +242,10 @@ hipError_t launch_attn(const AttnLaunch& p, int dtype, int nt, hipStream_t s);
 // (KVC_NOALLOC_SCRATCH_BYTES); `stream` (may be NULL) must be on that device.
 hipError_t noalloc_scratch(hipStream_t stream, void** ptr);
 hipError_t launch_attn_combine(const AttnLaunch& p, hipStream_t s);
+// Read-bandwidth probe: PROBE_BLOCKS workgroups stream `bytes` (a multiple of
+// 16) and write one XOR checksum word each to out[PROBE_BLOCKS].
+constexpr int PROBE_BLOCKS = 256;
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* out, hipStream_t s);
 hipError_t launch_attn_q8(const Q8AttnLaunch& p, int nt, hipStream_t s);
 hipError_t launch_q8_quantize(const Q8QuantLaunch& p, hipStream_t s);
 hipError_t launch_append(const void* k, const void* v, int nb, int hkv, int t_cap,

@@ -585,6 +585,19 @@ int kvc_xkv_decode_ws_bytes(const kvc_xkv* x, int n_q_heads, int n_select, size_
 int kvc_philox_words(int64_t n, uint32_t c1, uint32_t c2, uint32_t c3,
                      uint64_t seed, uint32_t* out, kvc_stream_t stream);
 
+/*
+ * Diagnostic: the read rate this device sustains for a pure stream, the
+ * ceiling for the decode kernels (HBM-bound: every cache byte is read once).
+ * Streams buf once with the 16-byte non-temporal loads those kernels use;
+ * out[i] (i < KVC_PROBE_BLOCKS) is the XOR of the 32-bit words that
+ * workgroup i read, so the XOR of all of out is the XOR of every word of
+ * buf.  buf: device, 16-byte aligned, bytes a multiple of 16 (KVC_EALIGN /
+ * KVC_EINVAL otherwise; bytes 0 writes zeros); out: device uint32
+ * [KVC_PROBE_BLOCKS], 4-byte aligned.  Stream-ordered.
+ */
+#define KVC_PROBE_BLOCKS 256
+int kvc_read_probe(const void* buf, size_t bytes, uint32_t* out, kvc_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -8,6 +8,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import oracle
 import decode_attention_kvc_amd as kvc
@@ -219,6 +220,13 @@ def test_append_and_range_and_philox_validation():
     assert L.kvc_philox_words(-1, 0, 0, 0, 0, FAKE, None) == kvc.KVC_EINVAL
     assert L.kvc_philox_words(4, 0, 0, 0, 0, FAKE + 4, None) == kvc.KVC_EALIGN
     assert L.kvc_philox_words(0, 0, 0, 0, 0, FAKE, None) == kvc.KVC_OK
+    # read probe: a whole number of 16-byte words, aligned buffers
+    assert L.kvc_read_probe(FAKE, 17, FAKE, None) == kvc.KVC_EINVAL
+    assert L.kvc_read_probe(FAKE + 4, 32, FAKE, None) == kvc.KVC_EALIGN
+    assert L.kvc_read_probe(FAKE, 32, FAKE + 1, None) == kvc.KVC_EALIGN
+    assert L.kvc_read_probe(FAKE, 32, None, None) == kvc.KVC_EALIGN
+    with pytest.raises(ValueError):
+        kvc.kvc_read_probe(torch.zeros(16), torch.zeros(kvc.PROBE_BLOCKS, dtype=torch.int32))
     assert L.kvc_decode_attn(None, FAKE, 0, 1, (ctypes.c_int32 * 1)(0), 8, 0.0, None, None, -1,
                              FAKE, 0, None, 0, FAKE, 1 << 30, None) == kvc.KVC_EALIGN
 
