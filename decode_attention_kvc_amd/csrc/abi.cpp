@@ -323,8 +323,8 @@ XkvWs xkv_ws(const kvc_xkv* x) {
 
 // Decode plan: two launches of `ns` workgroups per (b, j) (scores, then
 // top-k and the kept rows), enough to give every compute unit a workgroup.
-// The workspace holds the chunk keys, q~, the splits' partials and one
-// arrival counter per (b, j); the second launch keeps the keys in LDS when
+// The workspace holds one arrival counter per (b, j), the chunk keys, q~
+// and the splits' partials; the second launch keeps the keys in LDS when
 // they fit beside the rest of its work.
 constexpr int XKV_MAX_SPLIT = 8;
 
@@ -343,11 +343,13 @@ XkvDecodePlan plan_xkv_decode(const kvc_xkv* x, int n_select) {
     pl.lds = xkv_rows_lds(x->rank, pl.nch, pl.ksel, false);
     pl.gkeys = pl.lds > XKV_DECODE_LDS_LIMIT;
     if (pl.gkeys) pl.lds = xkv_rows_lds(x->rank, pl.nch, pl.ksel, true);
-    pl.keys_off = 0;
-    pl.qt_off = align_up(slabs * pl.nch * 4, 256);
+    // the counters first: a workspace shared by stores of other shapes keeps
+    // them at the same place (every completed call leaves them zero)
+    pl.arrive_off = 0;
+    pl.keys_off = align_up(slabs * 4, 256);
+    pl.qt_off = pl.keys_off + align_up(slabs * pl.nch * 4, 256);
     pl.part_off = pl.qt_off + align_up(slabs * XKV_MAXG * x->rank * 4, 256);
-    pl.arrive_off = pl.part_off + align_up(slabs * pl.ns * XKV_MAXG * (x->rank + 2) * 4, 256);
-    pl.ws_bytes = pl.arrive_off + slabs * 4;
+    pl.ws_bytes = pl.part_off + slabs * pl.ns * XKV_MAXG * (x->rank + 2) * 4;
     return pl;
 }
 

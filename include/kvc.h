@@ -561,11 +561,12 @@ int kvc_xkv_factor(const kvc_cache* c, int slot0, int iters, uint64_t seed,
  * one to eight workgroups per (b, j): the chunk scores, then the top-k and
  * the kept rows, whose partials the last workgroup of each (b, j) merges.
  * ws: kvc_xkv_decode_ws_bytes bytes for the same store shape, head count and
- * n_select (16-byte aligned; KVC_EWORKSPACE if NULL or smaller).  It holds
- * the chunk keys, q~, the partials and one arrival counter per (b, j) at its
- * end: the counters must be zero before the first call that uses the
- * workspace (allocate it zeroed) and every completed call leaves them zero.
- * Calls that share a workspace must be ordered (one stream).
+ * n_select (16-byte aligned; KVC_EWORKSPACE if NULL or smaller).  It starts
+ * with one arrival counter per (b, j), then holds the chunk keys, q~ and the
+ * partials: the counters must be zero before the first call that uses the
+ * workspace (allocate it zeroed) and every completed call leaves them zero,
+ * so one workspace may serve stores of several shapes.  Calls that share a
+ * workspace must be ordered (one stream).
  */
 int kvc_xkv_decode_attn(const kvc_xkv* x, int layer, const void* q, int n_q_heads, float scale,
                         int n_select, const float* o_in, const float* lse_in, float* out,

@@ -394,16 +394,16 @@ def test_xkv_decode_validation():
     assert d(o_in=FAKE) == kvc.KVC_EINVAL                        # lse_in missing
     assert d(q=FAKE + 2) == kvc.KVC_EALIGN
     assert d(x=xkv_desc(nb=0)) == kvc.KVC_OK
-    # the workspace: chunk keys, q~, the splits' partials and one arrival
-    # counter per (b, j), each part 256-byte aligned; ns = min(8, ceil(256 /
+    # the workspace: one arrival counter per (b, j), chunk keys, q~ and the
+    # splits' partials, each part 256-byte aligned; ns = min(8, ceil(256 /
     # slabs)) workgroups per (b, j)
     def ws_expect(nb, hkv, t_len, rank):
         al = lambda v: (v + 255) // 256 * 256
         slabs = nb * hkv
         ns = min(8, -(-256 // slabs))
         nch = (t_len + 7) // 8
-        return (al(slabs * nch * 4) + al(slabs * 8 * rank * 4)
-                + al(slabs * ns * 8 * (rank + 2) * 4) + slabs * 4)
+        return (al(slabs * 4) + al(slabs * nch * 4) + al(slabs * 8 * rank * 4)
+                + slabs * ns * 8 * (rank + 2) * 4)
     n = ctypes.c_size_t()
     assert L.kvc_xkv_decode_ws_bytes(ctypes.byref(x), 8, 64, ctypes.byref(n)) == kvc.KVC_OK
     assert n.value == ws_expect(1, 2, 100, 64)

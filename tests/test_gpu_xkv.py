@@ -410,3 +410,32 @@ def test_decode_edge_shapes(case):
         pairs = [(b, j) for b in range(nb) for j in range(hkv)]
         flips += check_pairs(st, q, out, lse, sel, layer, n_sel, pairs)
     say(f"  pairs with a flipped chunk inside the band: {flips}")
+
+
+def test_decode_one_workspace_for_two_store_shapes():
+    """One zeroed workspace, sized for the larger store, serves calls on two
+    stores of different shapes in turn (40 and 3 (b, j), so seven and eight
+    workgroups per (b, j)): the arrival counters sit at the workspace's start
+    and every call leaves them zero, so each call merges its own splits."""
+    say("xkv decode, one workspace for two shapes")
+    big = random_store(5, 8, 2000, 2, 64, seed=700)
+    small = random_store(1, 3, 900, 3, 32, seed=710)
+    q_big = kvc_synth.queries((5, 32, 128), device=DEV, seed=720)
+    q_small = kvc_synth.queries((1, 6, 128), device=DEV, seed=721)
+    n_sel = 40
+    ws = ws_tensor(max(kvc.kvc_xkv_decode_ws_bytes(big, 32, n_sel),
+                       kvc.kvc_xkv_decode_ws_bytes(small, 6, n_sel)))
+    flips = 0
+    for it, (st, q, layer) in enumerate([(big, q_big, 0), (small, q_small, 2), (big, q_big, 1),
+                                         (small, q_small, 0), (big, q_big, 1)]):
+        nb, hq = q.shape[0], q.shape[1]
+        out = torch.full((nb, hq, 128), float("nan"), device=DEV)
+        lse = torch.full((nb, hq), float("nan"), device=DEV)
+        sel = torch.full((nb, st.n_kv_heads, n_sel), -7, dtype=torch.int32, device=DEV)
+        kvc.kvc_xkv_decode_attn(st, layer, q, out, lse, n_select=n_sel, selected=sel, ws=ws)
+        torch.cuda.synchronize()
+        pairs = [(b, j) for b in range(nb) for j in range(st.n_kv_heads)]
+        flips += check_pairs(st, q, out, lse, sel, layer, n_sel, pairs)
+        assert torch.isfinite(out).all()
+    assert int(ws[:256].view(torch.int32).abs().sum()) == 0       # counters left at zero
+    say(f"  pairs with a flipped chunk inside the band: {flips}")
