@@ -573,18 +573,22 @@ def copy_ceiling(dev, nbytes=1 << 30, reps=5):
                 kernel="torch device copy: 1 GiB read + 1 GiB written, median of 5")
 
 
-def read_ceiling(dev, nbytes=4 << 30, reps=5):
-    """Read rate of the library's read probe (kvc_read_probe: one pass over
-    nbytes with the decode kernels' 16-byte non-temporal loads, a checksum
-    word per workgroup written), timed with HIP events, median of reps after
-    one warm-up: the pure-stream read rate of this part in this run, the
-    ceiling for the HBM-bound decode kernels."""
+def read_ceiling(dev, call_bytes, nbytes=4 << 30, reps=5, n_buf=4, calls=40):
+    """Read rates of the library's read probe (kvc_read_probe: the decode
+    attention's launch shape and loads without its arithmetic), timed with
+    HIP events in the same run: `GBps`, one pass over nbytes (median of reps
+    after a warm-up), the part's streaming read rate; `same_size_GBps`,
+    `calls` back-to-back reads of the attention call's algorithmic bytes,
+    rotating over n_buf buffers as the decode rotates over cache slots (the
+    working set exceeds the 256 MB last-level cache), one event pair around
+    them: the read rate a kernel of the call's size and launch shape reaches,
+    set against the attention call's rate."""
     import torch
     import decode_attention_kvc_amd as kvc
-    x = torch.ones(nbytes, dtype=torch.uint8, device=dev)
     out = torch.empty(kvc.PROBE_BLOCKS, dtype=torch.int32, device=dev)
-    kvc.kvc_read_probe(x, out)
     st = torch.cuda.current_stream()
+    x = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    kvc.kvc_read_probe(x, out)
     ts = []
     for _ in range(reps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -593,10 +597,25 @@ def read_ceiling(dev, nbytes=4 << 30, reps=5):
         b.record(st)
         b.synchronize()
         ts.append(a.elapsed_time(b))
-    del x, out
+    del x
     ms = sorted(ts)[len(ts) // 2]
+    n1 = max(16, int(call_bytes) // 16 * 16)
+    bufs = [torch.ones(n1, dtype=torch.uint8, device=dev) for _ in range(n_buf)]
+    for i in range(n_buf):
+        kvc.kvc_read_probe(bufs[i], out)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(st)
+    for i in range(calls):
+        kvc.kvc_read_probe(bufs[i % n_buf], out)
+    b.record(st)
+    b.synchronize()
+    us_same = a.elapsed_time(b) * 1e3 / calls
+    del bufs, out
     return dict(GBps=round(nbytes / (ms * 1e-3) / 1e9, 1), bytes=nbytes,
-                kernel="read_probe_kernel (kvc_read_probe): 4 GiB read once, median of 5")
+                same_size_GBps=round(n1 / (us_same * 1e-6) / 1e9, 1), same_size_bytes=n1,
+                same_size_us=round(us_same, 2),
+                kernel=f"read_probe_kernel (kvc_read_probe): 4 GiB read once, median of {reps}; "
+                       f"and {calls} back-to-back reads of the call's bytes over {n_buf} buffers")
 
 
 def _leg(name, fn, *a, **k):
@@ -921,9 +940,10 @@ def main():
     ceiling = _leg("copy_ceiling", copy_ceiling, dev)
     if isinstance(ceiling, dict) and "GBps" in ceiling:
         ceiling["attention_over_copy"] = round(att_gbps / ceiling["GBps"], 4)
-    rceiling = _leg("read_ceiling", read_ceiling, dev)
+    rceiling = _leg("read_ceiling", read_ceiling, dev, sum(att_bytes) / n_calls)
     if isinstance(rceiling, dict) and "GBps" in rceiling:
         rceiling["attention_over_read"] = round(att_gbps / rceiling["GBps"], 4)
+        rceiling["attention_over_same_size"] = round(att_gbps / rceiling["same_size_GBps"], 4)
 
     if args.copy_calibration:
         # Two plain copies of known size for scaling the memory counters:
