@@ -16,7 +16,7 @@ from ._lib import (  # noqa: F401
     kvc_select, kvc_select_seq, kvc_compact, kvc_philox_words, kvc_dkv_ws_bytes, kvc_dkv_score,
     kvc_gaussian_bf16, QCache, kvc_q8_quantize, kvc_q8_append, kvc_q8_decode_attn_ws_bytes,
     kvc_q8_decode_attn, XkvStore, kvc_xkv_factor_ws_bytes, kvc_xkv_factor, kvc_xkv_decode_ws_bytes,
-    kvc_xkv_decode_attn, kvc_read_probe, PROBE_BLOCKS,
+    kvc_xkv_decode_attn, kvc_read_probe, PROBE_BLOCKS, ATTN_COUNTERS,
 )
 
 lib()

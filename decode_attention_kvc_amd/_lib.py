@@ -513,7 +513,9 @@ def kvc_decode_attn_ws_bytes(cache, n_q_layers, n_q_heads):
 def kvc_decode_attn(cache, q, q_slot, out, lse=None, ws=None, scale=0.0, k_new=None,
                     v_new=None, append_slot=-1, q_layer_stride=0, out_layer_stride=0,
                     lse_layer_stride=0, n_q_layers=None, n_q_heads=None, stream=None):
-    """q: [nq][nb][Hq][d] (or strided views given explicit strides)."""
+    """q: [nq][nb][Hq][d] (or strided views given explicit strides); ws:
+    kvc_decode_attn_ws_bytes bytes of device memory, allocated zeroed (its
+    head of arrival counters starts at zero; every call leaves it zero)."""
     c = cache.desc()
     nq = len(q_slot) if n_q_layers is None else n_q_layers
     hq = q.shape[-2] if n_q_heads is None else n_q_heads
@@ -657,6 +659,7 @@ def kvc_philox_words(n, c1, c2, c3, seed, out, stream=None):
 
 
 PROBE_BLOCKS = 256
+ATTN_COUNTERS = 16384      # arrival counters at the head of a kvc_decode_attn workspace
 
 
 def kvc_read_probe(buf, out, stream=None):

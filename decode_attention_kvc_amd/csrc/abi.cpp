@@ -131,6 +131,28 @@ size_t attn_ws_total(const kvc_cache* c, int rows) {
     return part;
 }
 
+// The workspace of kvc_decode_attn starts with a fixed head of arrival
+// counters (one per slab of a launch whose last workgroup per slab merges),
+// then holds the split partials.  The head's place and size do not depend on
+// the cache's shape, so a workspace shared by calls of several shapes keeps
+// its counters where every call left them: at zero.
+constexpr size_t ATTN_COUNTER_HEAD = (size_t)KVC_ATTN_COUNTERS * sizeof(unsigned);
+
+size_t attn_ws_with_counters(const kvc_cache* c, int rows) {
+    return ATTN_COUNTER_HEAD + attn_ws_total(c, rows);
+}
+
+// Whether the last workgroup of each slab merges the launch's partials (in
+// place of the merge kernel): 256 threads share a slab's (row, 8 channels)
+// items, split groups sharing an item, so each thread folds at most eight
+// splits; and the launch's slabs have counters in the head.
+bool fuse_merge(int rows, int nsplit, int slabs) {
+    if (nsplit < 2 || slabs > KVC_ATTN_COUNTERS) return false;
+    const int items = rows * (KVC_HEAD_DIM / 8);
+    const int sg = std::max(1, std::min(nsplit, 256 / std::max(items, 1)));
+    return (nsplit + sg - 1) / sg <= 8;
+}
+
 // ---- score planning --------------------------------------------------------
 struct ScorePlan {
     int nsplit, tps, rows_pad;
@@ -414,7 +436,7 @@ int kvc_decode_attn_ws_bytes(const kvc_cache* c, int n_q_layers, int n_q_heads, 
     const int g = n_q_heads / c->n_kv_heads;
     if (g > (c->dtype == KVC_F32 ? 16 : 64)) return KVC_EINVAL;
     const int rows = std::min(n_q_layers * g, max_rows_per_chunk(c->dtype, g));
-    *bytes = (n_q_layers == 0 || c->nb == 0) ? 0 : attn_ws_total(c, std::max(rows, 1));
+    *bytes = (n_q_layers == 0 || c->nb == 0) ? 0 : attn_ws_with_counters(c, std::max(rows, 1));
     return KVC_OK;
 }
 
@@ -452,7 +474,7 @@ int kvc_decode_attn(const kvc_cache* c, const void* q, int64_t q_layer_stride, i
     size_t need = 0;
     if (n_q_layers > 0) {
         const int rows = std::min(n_q_layers * g, max_rows_per_chunk(c->dtype, g));
-        need = attn_ws_total(c, rows);
+        need = attn_ws_with_counters(c, rows);
         if (!ws || ws_bytes < need || !aligned16(ws)) return KVC_EWORKSPACE;
     }
     if (scale == 0.f) scale = 1.0f / sqrtf((float)KVC_HEAD_DIM);
@@ -482,7 +504,9 @@ int kvc_decode_attn(const kvc_cache* c, const void* q, int64_t q_layer_stride, i
         p.nsplit = pl.nsplit;
         p.tps = pl.tps;
         p.xcd_runs = pl.nsplit >= 8;
-        p.part = static_cast<float*>(ws);
+        p.part = reinterpret_cast<float*>(static_cast<char*>(ws) + ATTN_COUNTER_HEAD);
+        if (c->dtype == KVC_BF16 && fuse_merge(p.rows, pl.nsplit, slabs))
+            p.arrive = static_cast<unsigned*>(ws);
         p.sm = seq_map(c);
         if (launch_attn(p, c->dtype, pl.nt, s) != hipSuccess) return (int)KVC_EHIP;
         if (p.append_write) append_done = true;

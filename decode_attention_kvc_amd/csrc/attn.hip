@@ -83,19 +83,48 @@ __device__ __forceinline__ bf16x8 as_bf(u32x4 x) { return __builtin_bit_cast(bf1
 // (one pass of independent reads); the split groups' (max, sum, acc) meet
 // once in LDS, rescaled to the largest maximum and added in a fixed order.
 // Slabs with many splits (few slabs per launch) use 1024 threads.
-template <int NTH>
-__global__ __launch_bounds__(NTH) void attn_combine_kernel(AttnLaunch p) {
-    __shared__ float red[NTH * 10];
-    const int j = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+// Partial stores and loads of the launches whose last workgroup per slab
+// merges (COH): buffer accesses with the agent-scope cache policy (sc1),
+// written through to and read from the device's coherence point.
+constexpr int CPOL_SC1 = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const float* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, 0x7fffffff, 0x00020000);
+}
+
+template <bool COH>
+__device__ __forceinline__ f32x4 ld_part4(const float* a, __amdgpu_buffer_rsrc_t r,
+                                          const float* base) {
+    if constexpr (COH) {
+        const int off = (int)((a - base) * 4);
+        return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL_SC1));
+    } else {
+        return *reinterpret_cast<const f32x4*>(a);
+    }
+}
+
+template <bool COH>
+__device__ __forceinline__ void ld_ml(const float* a, __amdgpu_buffer_rsrc_t r, const float* base,
+                                      float& m, float& l) {
+    if constexpr (COH) {
+        // two word loads (the compiler pairs them into one 8-byte load)
+        const int off = (int)((a - base) * 4);
+        m = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, CPOL_SC1));
+        l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off + 4, 0, CPOL_SC1));
+    } else {
+        m = a[0];
+        l = a[1];
+    }
+}
+
+template <int NTH, bool COH>
+__device__ void combine_rows(const AttnLaunch& p, int j, int b, int r0, int rpb, float* red) {
+    const int tid = threadIdx.x;
     const int slab = b * p.hkv + j;
     const int nsplit = p.nsplit, rp = p.rp;
     const size_t slabs = (size_t)p.nb * p.hkv;
     const float* acc = p.part + (size_t)slab * nsplit * rp * D;
     const float* ml = p.part + slabs * nsplit * rp * D + (size_t)slab * nsplit * rp * 2;
-    // blockIdx.z: a block of the slab's query rows (one block unless the
-    // launch spreads many-split rows over several workgroups).
-    const int rpb = (p.rows + gridDim.z - 1) / gridDim.z;
-    const int r0 = blockIdx.z * rpb;
+    const __amdgpu_buffer_rsrc_t rsrc = part_rsrc(p.part);
     const int items = min(rpb, p.rows - r0) * (D / 8);
     if (items <= 0) return;
     if (nsplit <= 4) {
@@ -106,22 +135,25 @@ __global__ __launch_bounds__(NTH) void attn_combine_kernel(AttnLaunch p) {
             for (int e = 0; e < 8; ++e) o[e] = 0.f;
 #pragma unroll 4
             for (int sp = 0; sp < nsplit; ++sp) {
-                const float ms = ml[((size_t)sp * rp + r) * 2];
-                const float ls = ml[((size_t)sp * rp + r) * 2 + 1];
+                float ms, ls;
+                ld_ml<COH>(ml + ((size_t)sp * rp + r) * 2, rsrc, p.part, ms, ls);
                 const float* a = acc + ((size_t)sp * rp + r) * D + d0;
-                const f32x4 a0 = *reinterpret_cast<const f32x4*>(a);
-                const f32x4 a1 = *reinterpret_cast<const f32x4*>(a + 4);
-                if (ms == -INFINITY) continue;   // a split with no visible row
+                const f32x4 a0 = ld_part4<COH>(a, rsrc, p.part);
+                const f32x4 a1 = ld_part4<COH>(a + 4, rsrc, p.part);
+                // Branch-free, so that the loads of every unrolled split
+                // are issued together: a split with no visible row (its
+                // accumulators unwritten) is passed over by selects.
+                const bool live = ms != -INFINITY;
                 const float mn = fmaxf(M, ms);
-                const float fo = exp2f((M - mn) * LOG2E);   // 0 on the first split
+                const float fo = exp2f((M - mn) * LOG2E);   // 0 on the first live split
                 const float fs = exp2f((ms - mn) * LOG2E);
-                L = L * fo + ls * fs;
+                L = live ? L * fo + ls * fs : L;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    o[e] = o[e] * fo + a0[e] * fs;
-                    o[4 + e] = o[4 + e] * fo + a1[e] * fs;
+                    o[e] = live ? o[e] * fo + a0[e] * fs : o[e];
+                    o[4 + e] = live ? o[4 + e] * fo + a1[e] * fs : o[4 + e];
                 }
-                M = mn;
+                M = live ? mn : M;
             }
             const float inv = L > 0.f ? 1.f / L : 0.f;   // no split saw a row: zeros
             const int qi = r / p.g, h = j * p.g + r % p.g;
@@ -145,24 +177,27 @@ __global__ __launch_bounds__(NTH) void attn_combine_kernel(AttnLaunch p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = 0.f;
         if (act) {
-#pragma unroll 4
+#pragma unroll 8
             for (int sp = sg; sp < nsplit; sp += SG) {
-                const float ms = ml[((size_t)sp * rp + r) * 2];
-                const float ls = ml[((size_t)sp * rp + r) * 2 + 1];
+                float ms, ls;
+                ld_ml<COH>(ml + ((size_t)sp * rp + r) * 2, rsrc, p.part, ms, ls);
                 const float* a = acc + ((size_t)sp * rp + r) * D + d0;
-                const f32x4 a0 = *reinterpret_cast<const f32x4*>(a);
-                const f32x4 a1 = *reinterpret_cast<const f32x4*>(a + 4);
-                if (ms == -INFINITY) continue;   // a split with no visible row
+                const f32x4 a0 = ld_part4<COH>(a, rsrc, p.part);
+                const f32x4 a1 = ld_part4<COH>(a + 4, rsrc, p.part);
+                // Branch-free, so that the loads of every unrolled split
+                // are issued together: a split with no visible row (its
+                // accumulators unwritten) is passed over by selects.
+                const bool live = ms != -INFINITY;
                 const float mn = fmaxf(M, ms);
-                const float fo = exp2f((M - mn) * LOG2E);   // 0 on the first split
+                const float fo = exp2f((M - mn) * LOG2E);   // 0 on the first live split
                 const float fs = exp2f((ms - mn) * LOG2E);
-                L = L * fo + ls * fs;
+                L = live ? L * fo + ls * fs : L;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    o[e] = o[e] * fo + a0[e] * fs;
-                    o[4 + e] = o[4 + e] * fo + a1[e] * fs;
+                    o[e] = live ? o[e] * fo + a0[e] * fs : o[e];
+                    o[4 + e] = live ? o[4 + e] * fo + a1[e] * fs : o[4 + e];
                 }
-                M = mn;
+                M = live ? mn : M;
             }
         }
         if (SG > 1) {
@@ -206,6 +241,36 @@ __global__ __launch_bounds__(NTH) void attn_combine_kernel(AttnLaunch p) {
     }
 }
 
+template <int NTH>
+__global__ __launch_bounds__(NTH) void attn_combine_kernel(AttnLaunch p) {
+    __shared__ float red[NTH * 10];
+    // blockIdx.z: a block of the slab's query rows (one block unless the
+    // launch spreads many-split rows over several workgroups).
+    const int rpb = (p.rows + gridDim.z - 1) / gridDim.z;
+    combine_rows<NTH, false>(p, blockIdx.x, blockIdx.y, blockIdx.z * rpb, rpb, red);
+}
+
+// Counted arrival of a workgroup whose partial is written; true in the last
+// workgroup of the slab to arrive, which then merges every partial.  The
+// partial stores are complete (vmcnt 0) before the workgroup counts itself
+// in, and the last workgroup reads them with agent-scope loads: no L2
+// writeback or invalidation is needed, since no partial passes through a
+// non-coherent cache line.  The last workgroup returns the counter to zero
+// for the next launch on the workspace.
+__device__ __forceinline__ bool arrive_last(unsigned* ctr, int nsplit) {
+    __shared__ int last;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned old =
+            __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = old == (unsigned)nsplit - 1;
+        if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    return last;
+}
+
 // Row t of cache slab cslab <- the new row of sequence slab `slab`.
 template <typename T>
 __device__ void write_append_row(const AttnLaunch& p, size_t slab, size_t cslab, int t) {
@@ -228,6 +293,9 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(AttnLaunch p) {
     // rows (32 splits per slab) every XCD then streams one whole slab,
     // measured 2.5% faster per call; launches with few splits per slab were
     // 0.2-0.5% slower with it and keep the plain order.
+    // Wave merge, then (in the last workgroup of a slab) the split merge.
+    __shared__ float buf[W * 16 * D];
+    static_assert(W * 16 * D >= W * 64 * 10, "LDS of the split merge");
     const BlockXYZ blk = xcd_run_block(p.xcd_runs);
     const int s = blk.x, j = blk.y, b = blk.z;
     const int slab = b * p.hkv + j;
@@ -251,10 +319,18 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(AttnLaunch p) {
                 if (p.lse) p.lse[p.lse_off[qi] + (size_t)b * p.hq + h] = -INFINITY;
             } else {
                 float* ml = p.part + slabs * p.nsplit * RP * D + ((size_t)slab * p.nsplit + s) * RP * 2;
-                ml[r * 2] = -INFINITY;
-                ml[r * 2 + 1] = 0.f;
+                if (p.arrive) {
+                    const auto ml2 = __builtin_bit_cast(u32x2, f32x2{-INFINITY, 0.f});
+                    __builtin_amdgcn_raw_buffer_store_b64(ml2, part_rsrc(p.part),
+                                                          (int)((ml + r * 2 - p.part) * 4), 0, CPOL_SC1);
+                } else {
+                    ml[r * 2] = -INFINITY;
+                    ml[r * 2 + 1] = 0.f;
+                }
             }
         }
+        if (p.nsplit > 1 && p.arrive && arrive_last(p.arrive + slab, p.nsplit))
+            combine_rows<W * 64, true>(p, j, b, 0, p.rows, buf);
         return;
     }
     const size_t cslab = (size_t)phys * p.hkv + j;
@@ -433,7 +509,6 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(AttnLaunch p) {
 
     // Merge the four waves through LDS, one 16-row block at a time, and
     // write this workgroup's partial.
-    __shared__ float buf[W * 16 * D];
     __shared__ float wm[W][16], wl[W][16];
     constexpr int EPT = 2048 / (W * 64);  // merged outputs per thread (16 rows x 128)
     auto store_ept = [](float* dst, const float* o) {
@@ -492,10 +567,24 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(AttnLaunch p) {
                     if (d0 == 0 && p.lse) p.lse[p.lse_off[qi] + (size_t)b * p.hq + h] = M + logf(L);
                 }
             } else if (r < p.rows) {          // padding rows are never merged
-                store_ept(part_acc + (size_t)r * D + d0, o);
-                if (d0 == 0) {
-                    part_ml[r * 2] = M;
-                    part_ml[r * 2 + 1] = L;
+                if (p.arrive) {
+                    const __amdgpu_buffer_rsrc_t rs = part_rsrc(p.part);
+                    const int off = (int)((part_acc + (size_t)r * D + d0 - p.part) * 4);
+#pragma unroll
+                    for (int e = 0; e < EPT; e += 4)
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            __builtin_bit_cast(u32x4, f32x4{o[e], o[e + 1], o[e + 2], o[e + 3]}), rs,
+                            off + 4 * e, 0, CPOL_SC1);
+                    if (d0 == 0)
+                        __builtin_amdgcn_raw_buffer_store_b64(
+                            __builtin_bit_cast(u32x2, f32x2{M, L}), rs,
+                            (int)((part_ml + r * 2 - p.part) * 4), 0, CPOL_SC1);
+                } else {
+                    store_ept(part_acc + (size_t)r * D + d0, o);
+                    if (d0 == 0) {
+                        part_ml[r * 2] = M;
+                        part_ml[r * 2 + 1] = L;
+                    }
                 }
             }
         }
@@ -503,6 +592,8 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(AttnLaunch p) {
     }
 
     if (p.append_write && tile_end == ntiles) write_append_row<uint16_t>(p, slab, cslab, T - 1);
+    if (p.nsplit > 1 && p.arrive && arrive_last(p.arrive + slab, p.nsplit))
+        combine_rows<W * 64, true>(p, j, b, 0, p.rows, buf);
 }
 
 // float32 path: plain VALU arithmetic, up to 16 query rows per launch.
@@ -668,8 +759,9 @@ hipError_t launch_attn(const AttnLaunch& p, int dtype, int nt, hipStream_t st) {
         else
             go(attn_bf16_kernel<4, ATTN_WAVES, 1>);
     }
-    // bf16 launches with one split per slab finish their rows themselves.
-    if (dtype == 0 || p.nsplit > 1) return launch_attn_combine(p, st);
+    // bf16 launches with one split per slab finish their rows themselves, and
+    // so do those whose last workgroup per slab merges.
+    if (dtype == 0 || (p.nsplit > 1 && !p.arrive)) return launch_attn_combine(p, st);
     return hipGetLastError();
 }
 

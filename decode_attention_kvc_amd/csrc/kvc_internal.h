@@ -94,6 +94,8 @@ struct AttnLaunch {
     int nsplit, tps;        // splits per slab, tiles per split
     int xcd_runs;           // workgroups renumbered into contiguous runs per XCD
     float* part;            // partial accumulators, then (m, l) pairs
+    unsigned* arrive;       // per-slab arrival counters (zero between launches), or null:
+                            // then a separate kernel merges the partials
     SeqMap sm;              // cache entry and rows of each sequence
 };
 

@@ -204,7 +204,9 @@ int kvc_append(const kvc_cache* c, int slot, const void* k_new,
                const void* v_new, kvc_stream_t stream);
 
 /* Workspace bytes kvc_decode_attn needs for caches of this shape, for any
- * t_len <= c->t_cap and any n_q_layers up to the given count. */
+ * t_len <= c->t_cap and any n_q_layers up to the given count: a head of
+ * KVC_ATTN_COUNTERS 32-bit arrival counters, then the split partials. */
+#define KVC_ATTN_COUNTERS 16384
 int kvc_decode_attn_ws_bytes(const kvc_cache* c, int n_q_layers,
                              int n_q_heads, size_t* bytes);
 
@@ -230,8 +232,16 @@ int kvc_decode_attn_ws_bytes(const kvc_cache* c, int n_q_layers,
  *        out_layer_stride (0 = packed).
  *   lse: device float32 [n_q_layers][nb][n_q_heads] or NULL, layer stride
  *        lse_layer_stride (0 = packed).
- *   ws:  device workspace of at least kvc_decode_attn_ws_bytes bytes (split
- *        partials; no initialisation needed).
+ *   ws:  device workspace of at least kvc_decode_attn_ws_bytes bytes: a head
+ *        of KVC_ATTN_COUNTERS arrival counters, which must be zero before
+ *        the first call that uses the workspace (allocate it zeroed) and
+ *        which every completed call leaves zero, so that one workspace may
+ *        serve calls of any shape; then the split partials (no
+ *        initialisation needed).  Calls that share a workspace must be
+ *        ordered (one stream).  A launch whose slabs have several splits
+ *        has its partials merged by the last workgroup of each slab to
+ *        finish, counted in the head, or by a second kernel when a slab has
+ *        many splits per query row.
  * Requires t_len >= 1, n_q_heads a multiple of n_kv_heads, head_dim 128.
  */
 int kvc_decode_attn(const kvc_cache* c, const void* q, int64_t q_layer_stride,
@@ -261,8 +271,10 @@ int kvc_decode_attn(const kvc_cache* c, const void* q, int64_t q_layer_stride,
  *   - Every call on one GPU shares that GPU's array and leaves its partials
  *     there; calls that overlap on one GPU (different streams, or different
  *     host threads without ordering) race and may return wrong results.
- *     Calls ordered on one stream are safe.  The partials need no clearing:
- *     every launch writes what it reads.
+ *     Calls ordered on one stream are safe.  The array's counter head is
+ *     zero when the library is loaded (static storage) and every completed
+ *     call leaves it zero; the partials need no clearing: every launch
+ *     writes what it reads.
  */
 #define KVC_NOALLOC_SCRATCH_BYTES (32u << 20)
 int kvc_decode_attn_noalloc(const kvc_cache* c, const void* q,

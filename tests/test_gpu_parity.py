@@ -71,6 +71,42 @@ ATTN_CASES = [
 ]
 
 
+def test_decode_attn_one_workspace_for_many_shapes():
+    """One zeroed workspace serves attention calls of several shapes in turn:
+    launches whose last workgroup per slab merges (2 to 32 splits per slab)
+    and launches merged by the second kernel (16 query rows at 32 splits),
+    different slab counts and lengths.  Each output is checked against the
+    oracle, and the workspace's counter head is zero after every call."""
+    shapes = [
+        # (nb, hq, hkv, T, nq, q_slot)
+        (1, 32, 8, 33000, 1, [1]),          # 8 slabs x 32 splits, 4 rows: merged in the last workgroup
+        (16, 32, 8, 8400, 1, [0]),          # 128 slabs x 2 splits
+        (1, 32, 8, 33000, 4, [0] * 4),      # 16 rows at 32 splits: the merge kernel
+        (4, 40, 8, 9000, 1, [1]),           # 32 slabs x 8 splits, g = 5
+        (8, 32, 8, 4300, 1, [0]),           # 64 slabs x 4 splits
+        (1, 32, 8, 33000, 1, [0]),
+    ]
+    caches = {}
+    need = 0
+    for (nb, hq, hkv, T, nq, _) in shapes:
+        if (nb, hkv, T) not in caches:
+            caches[(nb, hkv, T)] = make_cache(2, nb, hkv, T, seed=nb + T)
+        need = max(need, kvc.kvc_decode_attn_ws_bytes(caches[(nb, hkv, T)], nq, hq))
+    ws = ws_tensor(need)
+    for i, (nb, hq, hkv, T, nq, q_slot) in enumerate(shapes):
+        say("attention, shared workspace", nb, hq, hkv, T, nq)
+        cache = caches[(nb, hkv, T)]
+        q = kvc_synth.queries((nq, nb, hq, 128), device=DEV, seed=50 + i)
+        out = torch.full((nq, nb, hq, 128), float("nan"), device=DEV)
+        lse = torch.full((nq, nb, hq), float("nan"), device=DEV)
+        kvc.kvc_decode_attn(cache, q, q_slot, out, lse, ws)
+        torch.cuda.synchronize()
+        ro, rl = oracle_decode(cache, q, q_slot)
+        assert np.abs(to_np(out) - ro).max() <= 2e-2
+        assert np.abs(to_np(lse) - rl).max() <= 1e-3
+        assert int(ws[:4 * kvc.ATTN_COUNTERS].view(torch.int32).abs().sum()) == 0
+
+
 @pytest.mark.parametrize("case", ATTN_CASES, ids=lambda c: f"nb{c[0]}h{c[1]}/{c[2]}T{c[3]}q{c[4]}")
 def test_decode_attn_bf16(case):
     nb, hq, hkv, T, nq, q_slot = case
