@@ -229,19 +229,30 @@ TRAFFIC_FILES = {
 }
 
 
+ATTN_SOURCES = ("attn.hip", "merge.h")
+
+
+def attn_source_sha256():
+    """sha256 of the decode attention kernel's sources (in order), the key
+    under which its memory counters are recorded."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        h.update(open(os.path.join(ROOT, "decode_attention_kvc_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
 def load_traffic(workload, mode, bytes_per_launch):
     """HBM traffic per attention call from the committed counter summary of
     the same workload and call order, or None when there is none or the
     attention source has changed since the counters were taken."""
-    import hashlib
     name = TRAFFIC_FILES.get(workload)
     if name is None:
         return None, None
     path = os.path.join(ROOT, "profiles", name)
-    src = os.path.join(ROOT, "decode_attention_kvc_amd", "csrc", "attn.hip")
     try:
         t = json.load(open(path))
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        sha = attn_source_sha256()
     except (OSError, ValueError):
         return None, None
     if t.get("attn_source_sha256") != sha or t.get("mode", "per-layer") != mode:

@@ -823,7 +823,7 @@ int kvc_q8_decode_attn_ws_bytes(const kvc_qcache* c, int n_q_layers, int n_q_hea
     size_t part = 0;
     for (int t = ATTN_TILE; t <= std::max(ATTN_TILE, vmax); t += ATTN_TILE)
         part = std::max(part, attn_ws_for(KVC_BF16, rows, t, slabs));
-    *bytes = part;
+    *bytes = ATTN_COUNTER_HEAD + part;
     return KVC_OK;
 }
 
@@ -875,7 +875,8 @@ int kvc_q8_decode_attn(const kvc_qcache* c, const void* q, int64_t q_layer_strid
         p.a.rp = pl.rp;
         p.a.nsplit = pl.nsplit;
         p.a.tps = pl.tps;
-        p.a.part = static_cast<float*>(ws);
+        p.a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + ATTN_COUNTER_HEAD);
+        if (fuse_merge(p.a.rows, pl.nsplit, slabs)) p.a.arrive = static_cast<unsigned*>(ws);
         p.sk = q_sk(c, slot);
         p.sv = q_sv(c, slot);
         p.kp = q_kp(c, slot);

@@ -37,6 +37,7 @@
 
 #include "common.h"
 #include "kvc_internal.h"
+#include "merge.h"
 
 namespace kvc {
 
@@ -590,6 +591,8 @@ __global__ __launch_bounds__(256) void attn_q8_kernel(Q8AttnLaunch P) {
                             f32x4{o[e] * inv, o[e + 1] * inv, o[e + 2] * inv, o[e + 3] * inv};
                     if (d0 == 0 && p.lse) p.lse[p.lse_off[qi] + (size_t)b * p.hq + h] = M + logf(L);
                 }
+            } else if (p.arrive) {
+                if (r < p.rows) store_part_coh<EPT>(p, part_acc, part_ml, r, d0, o, M, L);
             } else {
                 float* dst = part_acc + (size_t)r * D + d0;
 #pragma unroll
@@ -603,6 +606,8 @@ __global__ __launch_bounds__(256) void attn_q8_kernel(Q8AttnLaunch P) {
         }
         __syncthreads();
     }
+    if (p.nsplit > 1 && p.arrive && arrive_last(p.arrive + slab, p.nsplit))
+        combine_rows<W * 64, true>(p, j, b, 0, p.rows, buf);
 }
 
 }  // namespace
@@ -625,7 +630,7 @@ hipError_t launch_attn_q8(const Q8AttnLaunch& p, int nt, hipStream_t st) {
         hipLaunchKernelGGL(attn_q8_kernel<2>, grid, dim3(256), 0, st, p);
     else
         hipLaunchKernelGGL(attn_q8_kernel<4>, grid, dim3(256), 0, st, p);
-    if (p.a.nsplit > 1) return launch_attn_combine(p.a, st);
+    if (p.a.nsplit > 1 && !p.a.arrive) return launch_attn_combine(p.a, st);
     return hipGetLastError();
 }
 

@@ -481,7 +481,9 @@ int kvc_q8_quantize(const kvc_cache* src, int slot, const int32_t* protect,
 int kvc_q8_append(const kvc_qcache* c, int slot, const void* k_new,
                   const void* v_new, kvc_stream_t stream);
 
-/* Workspace bytes kvc_q8_decode_attn needs (any t_len <= t_cap). */
+/* Workspace bytes kvc_q8_decode_attn needs (any t_len <= t_cap): the same
+ * head of KVC_ATTN_COUNTERS arrival counters as kvc_decode_attn's (zero
+ * before the first call, left zero by every call), then the partials. */
 int kvc_q8_decode_attn_ws_bytes(const kvc_qcache* c, int n_q_layers,
                                 int n_q_heads, size_t* bytes);
 
@@ -490,7 +492,8 @@ int kvc_q8_decode_attn_ws_bytes(const kvc_qcache* c, int n_q_layers,
  * kvc_decode_attn's contract (same q / out / lse layouts and strides, GQA,
  * q-layer grouping; no fused append -- use kvc_q8_append first), with each
  * row's key and value taken as code * scale, or as the bf16 protected row.
- * q: bf16.  Requires g = n_q_heads / n_kv_heads <= 64.
+ * q: bf16.  Requires g = n_q_heads / n_kv_heads <= 64.  ws: as for
+ * kvc_decode_attn (allocated zeroed; one workspace may serve both calls).
  */
 int kvc_q8_decode_attn(const kvc_qcache* c, const void* q,
                        int64_t q_layer_stride, int n_q_layers,
