@@ -36,6 +36,7 @@
 
 #include "common.h"
 #include "kvc_internal.h"
+#include "merge.h"
 #include "philox.h"
 #include "radix.h"
 
@@ -513,28 +514,15 @@ __device__ __forceinline__ void split_bf16(const float (&x)[8], bf16x8& hi, bf16
 // partials are written with agent-scope stores (through to the device's
 // coherence point), every store is complete (vmcnt 0) before the workgroup
 // counts itself in, and the last workgroup to arrive reads the partials with
-// agent-scope loads, which do not hit a stale line of its own XCD's L2.  The
-// last workgroup returns the counter to zero for the next launch.
+// agent-scope loads, which do not hit a stale line of its own XCD's L2; the
+// counted arrival (arrive_last) is the one of the split-K attention merge,
+// and the last workgroup returns the counter to zero for the next launch.
 __device__ __forceinline__ void st_coh(float* a, float x) {
     __hip_atomic_store(a, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float ld_coh(const float* a) {
     return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ bool arrive_last(unsigned* ctr, int n) {
-    __shared__ int last;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned old =
-            __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last = old == (unsigned)n - 1;
-        if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    return last;
-}
-
 // LDS floats of the score launch: B_l^K [D][R], the queries [MAXG][D], q~
 // [MAXG][R] and the partial sums of q~ [NT].
 __host__ __device__ constexpr int xs_floats(int r) { return D * r + MAXG * D + MAXG * r + XF_NT; }
