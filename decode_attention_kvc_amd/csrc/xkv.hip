@@ -495,8 +495,9 @@ __device__ void topk_prefix(const uint32_t* keys, int n, uint32_t k, RadixSmem<N
     *cnt_out = cnt;
 }
 
-constexpr int XF_NT = 1024;            // threads of a decode workgroup
+constexpr int XF_NT = 1024;            // threads of a decode row workgroup
 constexpr int XF_NW = XF_NT / WAVE;
+constexpr int XS_NT = 512;             // threads of a decode score workgroup
 
 // x ~ hi + lo with both parts in bf16 (about 16 significant bits).
 __device__ __forceinline__ void split_bf16(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
@@ -525,7 +526,9 @@ __device__ __forceinline__ float ld_coh(const float* a) {
 }
 // LDS floats of the score launch: B_l^K [D][R], the queries [MAXG][D], q~
 // [MAXG][R] and the partial sums of q~ [NT].
-__host__ __device__ constexpr int xs_floats(int r) { return D * r + MAXG * D + MAXG * r + XF_NT; }
+__host__ __device__ constexpr int xs_floats(int r) {
+    return D * r + MAXG * D + MAXG * r + (XS_NT > MAXG * r ? XS_NT : MAXG * r);
+}
 // LDS floats of the row launch besides the kept chunks and (when they fit)
 // the chunk keys: B_l^V rows [D][R + 1], the waves' partials [NW][MAXG][R + 2],
 // a~ [MAXG][R].
@@ -546,14 +549,16 @@ __host__ __device__ constexpr int xr_floats(int r) {
 //     product (heads padded to 16), max over the heads, order-preserving keys
 //     into the workspace.
 template <int R>
-__global__ __launch_bounds__(XF_NT) void xkv_scores(XkvDecodeLaunch p) {
+__global__ __launch_bounds__(XS_NT) void xkv_scores(XkvDecodeLaunch p) {
     extern __shared__ __align__(16) unsigned char smem[];
-    constexpr int NT = XF_NT, NW = XF_NW;
+    constexpr int NT = XS_NT, NW = XS_NT / WAVE;
     constexpr int KS = R / 32;           // 32-rank k-steps
-    constexpr int UNB = 4;               // 16-chunk landmark blocks per wave and round
+    constexpr int UNB = 32 / NW;         // 16-chunk landmark blocks per wave and round
     constexpr int BPT = D * R / 4 / NT;  // float4 per thread of one B matrix
-    constexpr int NPART = NT / (MAXG * R);
-    static_assert(BPT >= 1 && NPART >= 1 && D % NPART == 0 && MAXG * D == NT, "launch shape");
+    constexpr int NPART = NT > MAXG * R ? NT / (MAXG * R) : 1;   // threads per (head, rank)
+    constexpr int QX = MAXG * R * NPART; // (part, head, rank) items of q~
+    constexpr int QPT = MAXG * D / NT;    // query elements per thread
+    static_assert(UNB * NW == 32 && BPT >= 1 && D % NPART == 0 && QPT * NT == MAXG * D, "launch shape");
     const int sp = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int slab = b * p.hkv + j, g = p.g;
     const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
@@ -568,7 +573,7 @@ __global__ __launch_bounds__(XF_NT) void xkv_scores(XkvDecodeLaunch p) {
     float* area = reinterpret_cast<float*>(smem);                 // B_l^K [D][R]
     float* qs = area + D * R;                                     // [MAXG][D] queries
     float* qt = qs + MAXG * D;                                    // [MAXG][R] q~
-    float* qpart = qt + MAXG * R;                                 // [NT] partial sums of q~
+    float* qpart = qt + MAXG * R;                                 // [QX] partial sums of q~
     uint32_t* keys = p.ws_keys + (size_t)slab * nch;
 
     // 0. global reads
@@ -577,10 +582,15 @@ __global__ __launch_bounds__(XF_NT) void xkv_scores(XkvDecodeLaunch p) {
 #pragma unroll
     for (int e = 0; e < BPT; ++e) bkr[e] = *reinterpret_cast<const f32x4*>(BK + 4 * (tid + e * NT));
     const size_t row0 = (size_t)b * p.hq + (size_t)j * g;        // first query row of (b, j)
-    const bool qok = tid < g * D;                                 // (head tid / D, channel tid % D)
-    // loads are unconditional (clamped addresses, results selected after), so
-    // that the compiler's wait counts cover only the older loads
-    const uint16_t qraw = reinterpret_cast<const uint16_t*>(p.q)[row0 * D + (qok ? tid : 0)];
+    // query element tid + e NT is (head / D, channel % D); loads are
+    // unconditional (clamped addresses, results selected after), so that the
+    // compiler's wait counts cover only the older loads
+    uint16_t qraw[QPT];
+#pragma unroll
+    for (int e = 0; e < QPT; ++e) {
+        const int i = tid + e * NT;
+        qraw[e] = reinterpret_cast<const uint16_t*>(p.q)[row0 * D + (i < g * D ? i : 0)];
+    }
     // every wave's reads for q~ are queued ahead of the landmark stream
     __syncthreads();
     const uint16_t* L = reinterpret_cast<const uint16_t*>(p.lk) + (size_t)slab * (p.x_tcap / CHUNK) * R;
@@ -600,25 +610,29 @@ __global__ __launch_bounds__(XF_NT) void xkv_scores(XkvDecodeLaunch p) {
     load_lm(la, 0);
 #pragma unroll
     for (int e = 0; e < BPT; ++e) *reinterpret_cast<f32x4*>(area + 4 * (tid + e * NT)) = bkr[e];
-    qs[tid] = qok ? bf16_to_f32(qraw) : 0.f;
+#pragma unroll
+    for (int e = 0; e < QPT; ++e) {
+        const int i = tid + e * NT;
+        qs[i] = i < g * D ? bf16_to_f32(qraw[e]) : 0.f;
+    }
     __syncthreads();
 
-    // 1. q~ (NPART threads per (head, rank), contiguous channel ranges)
-    {
-        const int c = tid % R, h = (tid / R) % MAXG, part = tid / (MAXG * R);
+    // 1. q~ (NPART parts per (head, rank), contiguous channel ranges)
+    for (int x = tid; x < QX; x += NT) {
+        const int c = x % R, h = (x / R) % MAXG, part = x / (MAXG * R);
         constexpr int IPP = D / NPART;
         float a = 0.f;
         if (h < g)
             for (int i = part * IPP; i < (part + 1) * IPP; ++i) a = fmaf(qs[h * D + i], area[i * R + c], a);
-        qpart[tid] = a;
+        qpart[x] = a;
     }
     __syncthreads();
-    if (tid < MAXG * R) {
+    for (int x = tid; x < MAXG * R; x += NT) {
         float a = 0.f;
 #pragma unroll
-        for (int part = 0; part < NPART; ++part) a += qpart[part * MAXG * R + tid];
-        qt[tid] = a;
-        if (sp == 0) p.ws_qt[(size_t)slab * MAXG * R + tid] = a;
+        for (int part = 0; part < NPART; ++part) a += qpart[part * MAXG * R + x];
+        qt[x] = a;
+        if (sp == 0) p.ws_qt[(size_t)slab * MAXG * R + x] = a;
     }
     __syncthreads();
     bf16x8 qh[KS], ql[KS];               // head l16, ranks 32 ks + 8 lg .. +8
@@ -998,21 +1012,23 @@ size_t xkv_rows_lds(int rank, int nch, int ksel, bool gkeys) {
 
 hipError_t launch_xkv_decode(const XkvDecodeLaunch& p, bool gkeys, size_t rows_lds, hipStream_t st) {
     const dim3 grid(p.ns, p.hkv, p.nb);
-    auto go = [&](auto kern, size_t lds) {
+    auto go = [&](auto kern, size_t lds, int nt) {
         if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
             return hipErrorInvalidValue;
-        hipLaunchKernelGGL(kern, grid, dim3(XF_NT), lds, st, p);
+        hipLaunchKernelGGL(kern, grid, dim3(nt), lds, st, p);
         return hipGetLastError();
     };
     const size_t slds = xkv_scores_lds(p.rank);
     hipError_t e;
     if (p.rank == 32) {
-        e = go(xkv_scores<32>, slds);
-        if (e == hipSuccess) e = gkeys ? go(xkv_rows<32, true>, rows_lds) : go(xkv_rows<32, false>, rows_lds);
+        e = go(xkv_scores<32>, slds, XS_NT);
+        if (e == hipSuccess)
+            e = gkeys ? go(xkv_rows<32, true>, rows_lds, XF_NT) : go(xkv_rows<32, false>, rows_lds, XF_NT);
     } else {
-        e = go(xkv_scores<64>, slds);
-        if (e == hipSuccess) e = gkeys ? go(xkv_rows<64, true>, rows_lds) : go(xkv_rows<64, false>, rows_lds);
+        e = go(xkv_scores<64>, slds, XS_NT);
+        if (e == hipSuccess)
+            e = gkeys ? go(xkv_rows<64, true>, rows_lds, XF_NT) : go(xkv_rows<64, false>, rows_lds, XF_NT);
     }
     return e;
 }
