@@ -687,7 +687,7 @@ def main():
         sys.exit(2)
 
     # A process that freed device memory just before this one (a test run,
-    # say) leaves the driver clearing it in the background: decode attention
+    # say) leaves the GPU kernel driver clearing it in the background: decode attention
     # measured ~10% slower over a whole bench run started right after the GPU
     # test suite's process exited (95.0 against 86.5 us per call at the
     # Qwen3-14B shape), and at its usual rate after an 8 s pause.  So the
@@ -802,8 +802,8 @@ def main():
         log(f"[bench] initial compression {t0} -> {dec.cache.t_len} rows: {initial_ms:.2f} ms")
         dec.spare = spare
         # The prompt's buffers go back to torch's caching allocator, not to
-        # the driver (nothing here calls empty_cache): device memory returned
-        # to the driver is cleared in the background at ~35 GB/s, and that
+        # the GPU kernel driver (nothing here calls empty_cache): device memory
+        # returned to the kernel driver is cleared in the background at ~35 GB/s, and that
         # clear of the 86 GB prompt ran under the timed steps for ~2.4 s,
         # costing 4-5% per attention call (90.7 vs 86.5 us at this shape).
         del big, q_init
